@@ -1,0 +1,385 @@
+"""Pins of the fp64 oracle to facts that do not come from its own code.
+
+Each test checks the oracle against something fixed independently: a
+textbook identity of the Haar transform, a library convolution (torch CPU),
+a hand-worked example, a closed form derived from the layer's definition,
+brute force on tiny inputs, or an exact identity of linear maps (adjoint,
+finite differences). Together they are chosen so that a dropped term, a
+wrong sign or index, or a transposed operand in the oracle fails one of
+them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from wavelet_convolution_amd.inputs import make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(rng, B, C, H, W, L, kb, k):
+    x = rng.standard_normal((B, C, H, W))
+    dy = rng.standard_normal((B, C, H, W))
+    wb = rng.standard_normal((C, kb, kb))
+    wl = rng.standard_normal((L, C, 4, k, k))
+    sc = rng.uniform(0.5, 1.5, (L, C, 4))
+    return x, dy, wb, wl, sc
+
+
+# --------------------------------------------------------------- Haar (P1)
+
+def test_haar_perfect_reconstruction_and_energy():
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((12, 20))
+    bands = oracle.haar_dwt(X)
+    assert bands.shape == (4, 6, 10)
+    np.testing.assert_allclose(oracle.haar_iwt(bands), X, rtol=0, atol=1e-14)
+    assert abs(np.sum(bands ** 2) - np.sum(X ** 2)) < 1e-12 * np.sum(X ** 2)
+    # orthonormality the other way round: DWT(IWT(b)) = b
+    b = rng.standard_normal((4, 3, 5))
+    np.testing.assert_allclose(oracle.haar_dwt(oracle.haar_iwt(b)), b, rtol=0, atol=1e-14)
+
+
+def test_haar_band_semantics_on_textbook_patterns():
+    """The four 2x2 Haar patterns each excite exactly one band (value 2 for
+    unit amplitude, the orthonormal gain of a 4-point Hadamard row / 2)."""
+    H = W = 8
+    i, j = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    patterns = {
+        0: np.ones((H, W)),                   # constant -> LL
+        1: np.where(i % 2 == 0, 1.0, -1.0),   # rows alternate -> top minus bottom
+        2: np.where(j % 2 == 0, 1.0, -1.0),   # columns alternate -> left minus right
+        3: np.where((i + j) % 2 == 0, 1.0, -1.0),  # checkerboard -> diagonal
+    }
+    for s, X in patterns.items():
+        bands = oracle.haar_dwt(X)
+        for t in range(4):
+            expect = 2.0 if t == s else 0.0
+            np.testing.assert_allclose(bands[t], expect, atol=1e-15)
+
+
+# --------------------------------------------------------- golden (hand)
+
+def _golden():
+    with open(os.path.join(GOLDEN, "hand_worked_4x4_l1.json")) as f:
+        return json.load(f)
+
+
+def _golden_params(g):
+    wb = np.array(g["w_base"], float)[None]
+    wl = np.zeros((1, 1, 4, 3, 3))
+    wl[0, 0, 1] = np.array(g["w_lvl_band1"], float)
+    sc = np.array(g["scale"], float)[None, None]
+    return wb, wl, sc
+
+
+def test_golden_hand_worked_forward():
+    g = _golden()
+    x = np.array(g["x"], float)[None, None]
+    wb, wl, sc = _golden_params(g)
+    np.testing.assert_allclose(oracle.fwd(x, wb, wl, sc)[0, 0], np.array(g["y"]), atol=1e-15)
+    np.testing.assert_allclose(oracle.fwd_closed(x, wb, wl, sc)[0, 0], np.array(g["y"]), atol=1e-15)
+
+
+def test_golden_hand_worked_backward():
+    g = _golden()
+    x = np.array(g["x"], float)[None, None]
+    wb, wl, sc = _golden_params(g)
+    case = g["case_dy_impulse_2_0"]
+    dy = np.array(case["dy"], float)[None, None]
+    np.testing.assert_allclose(oracle.bwd_data(dy, wb, wl, sc)[0, 0], np.array(case["dx"]), atol=1e-15)
+    for fn in (oracle.bwd_weight, oracle.bwd_weight_gcorr):
+        dwb, dwl, dsc = fn(x, dy, wb, wl, sc)
+        np.testing.assert_allclose(dwb[0], np.array(case["dw_base"]), atol=1e-15)
+        np.testing.assert_allclose(dwl[0, 0], np.array(case["dw_lvl"]), atol=1e-15)
+        np.testing.assert_allclose(dsc[0, 0], np.array(case["dscale"]), atol=1e-15)
+    case = g["case_dy_impulse_3_2"]
+    dy = np.array(case["dy"], float)[None, None]
+    dwb, _, _ = oracle.bwd_weight(x, dy, wb, wl, sc)
+    np.testing.assert_allclose(dwb[0], np.array(case["dw_base"]), atol=1e-15)
+
+
+# ------------------------------------------------------- linearity (P2)
+
+def test_linearity_in_each_argument():
+    rng = np.random.default_rng(2)
+    x, x2, wb, wl, sc = _rand_problem(rng, 2, 3, 16, 16, 2, 5, 3)
+    a, b = 0.7, -1.3
+    f = oracle.fwd
+    np.testing.assert_allclose(f(a * x + b * x2, wb, wl, sc), a * f(x, wb, wl, sc) + b * f(x2, wb, wl, sc), atol=1e-12)
+    # y = base(w_base) + branch: linear in w_base once the branch is switched off
+    wb2 = rng.standard_normal(wb.shape)
+    zs = np.zeros_like(sc)
+    np.testing.assert_allclose(f(x, a * wb + b * wb2, wl, zs), a * f(x, wb, wl, zs) + b * f(x, wb2, wl, zs), atol=1e-12)
+    # the branch alone (base weights zero) is linear in w_lvl and in scale separately
+    z = np.zeros_like(wb)
+    wl2 = rng.standard_normal(wl.shape)
+    sc2 = rng.standard_normal(sc.shape)
+    np.testing.assert_allclose(f(x, z, a * wl + b * wl2, sc), a * f(x, z, wl, sc) + b * f(x, z, wl2, sc), atol=1e-12)
+    np.testing.assert_allclose(f(x, z, wl, a * sc + b * sc2), a * f(x, z, wl, sc) + b * f(x, z, wl, sc2), atol=1e-12)
+
+
+# ------------------------------------ zero branch = depthwise conv (P3)
+
+@pytest.mark.parametrize("kb", [3, 5, 7])
+def test_zero_branch_is_depthwise_conv_two_library_routes(kb):
+    """With zero level weights, zero scales, or L = 0 the layer is the base
+    depthwise convolution. Checked against torch's grouped conv2d and against
+    one dense conv with a block-diagonal weight, the identity that
+    diagonalwise refactorization rests on (mlsanity.com page,
+    "Diagonalwise Refactorization", Abstract)."""
+    rng = np.random.default_rng(3)
+    B, C, H, W, L, k = 2, 4, 16, 12, 2, 5
+    x, dy, wb, wl, sc = _rand_problem(rng, B, C, H, W, L, kb, k)
+    xt = torch.from_numpy(x)
+    grouped = torch.nn.functional.conv2d(xt, torch.from_numpy(wb)[:, None], padding=kb // 2, groups=C).numpy()
+    dense_w = torch.zeros(C, C, kb, kb, dtype=torch.float64)
+    for c in range(C):
+        dense_w[c, c] = torch.from_numpy(wb[c])
+    dense = torch.nn.functional.conv2d(xt, dense_w, padding=kb // 2).numpy()
+    np.testing.assert_allclose(grouped, dense, atol=1e-12)
+    for y in (oracle.fwd(x, wb, np.zeros_like(wl), sc),
+              oracle.fwd(x, wb, wl, np.zeros_like(sc)),
+              oracle.fwd(x, wb, np.zeros((0, C, 4, k, k)), np.zeros((0, C, 4)))):
+        np.testing.assert_allclose(y, grouped, atol=1e-12)
+    # and the backward of the base conv, through torch autograd
+    xt = torch.from_numpy(x).requires_grad_(True)
+    wt = torch.from_numpy(wb)[:, None].clone().requires_grad_(True)
+    yt = torch.nn.functional.conv2d(xt, wt, padding=kb // 2, groups=C)
+    yt.backward(torch.from_numpy(dy))
+    np.testing.assert_allclose(oracle.bwd_data(dy, wb, np.zeros_like(wl), sc), xt.grad.numpy(), atol=1e-12)
+    dwb, _, _ = oracle.bwd_weight(x, dy, wb, wl, sc)
+    np.testing.assert_allclose(dwb, wt.grad.numpy()[:, 0], atol=1e-10)
+
+
+# ------------------------------------ identity levels = block means (P4)
+
+def _block_mean(x, s):
+    B, C, H, W = x.shape
+    m = x.reshape(B, C, H // s, s, W // s, s).mean(axis=(3, 5))
+    return np.repeat(np.repeat(m, s, axis=2), s, axis=3)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_identity_levels_give_sum_of_block_means(L):
+    """Zero base, centre-delta level kernels and unit scales: each level's
+    branch reproduces its input exactly (perfect reconstruction), and the
+    LL path averages it, so y = sum_{m<L} BlockMean_{2^m}(x) (derived from
+    the cascade by hand; L = 1 gives y = x)."""
+    rng = np.random.default_rng(4)
+    B, C, H, W, k = 2, 3, 32, 16, 3
+    x = rng.standard_normal((B, C, H, W))
+    wl = np.zeros((L, C, 4, k, k))
+    wl[..., k // 2, k // 2] = 1.0
+    sc = np.ones((L, C, 4))
+    y = oracle.fwd(x, np.zeros((C, 5, 5)), wl, sc)
+    expect = sum(_block_mean(x, 1 << m) for m in range(L))
+    np.testing.assert_allclose(y, expect, atol=1e-12)
+
+
+# ---------------------------------- closed form == cascade (P5)
+
+@pytest.mark.parametrize("L,kb,k", [(1, 3, 3), (2, 5, 5), (3, 7, 5), (4, 5, 3), (5, 3, 5)])
+def test_closed_form_equals_cascade(L, kb, k):
+    rng = np.random.default_rng(5)
+    x, _, wb, wl, sc = _rand_problem(rng, 1, 2, 64, 32, L, kb, k)
+    np.testing.assert_allclose(oracle.fwd_closed(x, wb, wl, sc), oracle.fwd(x, wb, wl, sc), atol=1e-12)
+
+
+# ------------------------------------------------ impulse probing (P6)
+
+@pytest.mark.parametrize("L,kb,k", [(1, 3, 3), (2, 5, 3), (3, 3, 5), (4, 7, 3)])
+def test_impulse_probe_support_and_receptive_field(L, kb, k):
+    rng = np.random.default_rng(6)
+    H = W = 16
+    wb = rng.standard_normal((1, kb, kb))
+    wl = rng.standard_normal((L, 1, 4, k, k))
+    sc = rng.uniform(0.5, 1.5, (L, 1, 4))
+    N = H * W
+    cols = oracle.fwd(np.eye(N).reshape(N, 1, H, W), wb, wl, sc)
+    # batch of impulses uses channel 0 for every b: column q of M is cols[q]
+    M = cols.reshape(N, N).T          # M[h, q]
+    x = rng.standard_normal((1, 1, H, W))
+    np.testing.assert_allclose(M @ x.ravel(), oracle.fwd(x, wb, wl, sc).ravel(), atol=1e-12)
+    # support: base box of radius kb//2, plus for each level a box of radius
+    # k//2 on that level's grid
+    hh, ww = np.divmod(np.arange(N), W)
+    dh = np.abs(hh[:, None] - hh[None, :])
+    dw = np.abs(ww[:, None] - ww[None, :])
+    expect = (dh <= kb // 2) & (dw <= kb // 2)
+    for l in range(1, L + 1):
+        dl_h = np.abs((hh[:, None] >> l) - (hh[None, :] >> l))
+        dl_w = np.abs((ww[:, None] >> l) - (ww[None, :] >> l))
+        expect |= (dl_h <= k // 2) & (dl_w <= k // 2)
+    nz = np.abs(M) > 1e-12
+    assert np.array_equal(nz, expect)
+    # receptive-field radius grows like 2^L (exponentially in the level count)
+    radius = max(int(dh[nz].max()), int(dw[nz].max()))
+    assert radius == min(H - 1, max(kb // 2, (k // 2 + 1) * (1 << L) - 1))
+
+
+def test_parameter_count_linear_in_levels():
+    C, kb, k = 3, 5, 5
+    counts = []
+    for L in range(0, 6):
+        dwb, dwl, dsc = oracle.bwd_weight(np.zeros((1, C, 32, 32)), np.zeros((1, C, 32, 32)),
+                                          np.zeros((C, kb, kb)), np.zeros((L, C, 4, k, k)), np.ones((L, C, 4)))
+        counts.append(dwb.size + dwl.size + dsc.size)
+    assert np.all(np.diff(counts) == C * 4 * (k * k + 1))
+
+
+# ------------------------------------------- shift by 2^L (P8)
+
+def test_shift_equivariance_by_multiples_of_2L_only():
+    rng = np.random.default_rng(7)
+    L, kb, k = 2, 5, 3
+    H = W = 48
+    x = np.zeros((1, 1, H, W))
+    x[0, 0, 16:28, 12:24] = rng.standard_normal((12, 12))   # compact support away from borders
+    wb = rng.standard_normal((1, kb, kb))
+    wl = rng.standard_normal((L, 1, 4, k, k))
+    sc = rng.uniform(0.5, 1.5, (L, 1, 4))
+    y = oracle.fwd(x, wb, wl, sc)
+    s = 1 << L
+    ys = oracle.fwd(np.roll(x, (s, 2 * s), axis=(2, 3)), wb, wl, sc)
+    np.testing.assert_allclose(ys, np.roll(y, (s, 2 * s), axis=(2, 3)), atol=1e-12)
+    y1 = oracle.fwd(np.roll(x, (1, 0), axis=(2, 3)), wb, wl, sc)
+    assert np.abs(y1 - np.roll(y, (1, 0), axis=(2, 3))).max() > 1e-3
+
+
+# ---------------------------------------------- adjoint identities (P9)
+
+@pytest.mark.parametrize("L,kb,k", [(1, 5, 5), (2, 5, 5), (3, 7, 5), (4, 3, 3)])
+def test_adjoint_identities(L, kb, k):
+    rng = np.random.default_rng(8)
+    x, v, wb, wl, sc = _rand_problem(rng, 2, 3, 32, 32, L, kb, k)
+    y = oracle.fwd(x, wb, wl, sc)
+    dx = oracle.bwd_data(v, wb, wl, sc)
+    assert abs(np.vdot(y, v) - np.vdot(x, dx)) < 1e-10 * np.abs(y).sum()
+    dwb, dwl, dsc = oracle.bwd_weight(x, v, wb, wl, sc)
+    # y is linear in each parameter group with the others held fixed
+    d = rng.standard_normal(wb.shape)
+    lhs = np.vdot(oracle.fwd(x, d, np.zeros_like(wl), sc), v)
+    assert abs(lhs - np.vdot(d, dwb)) < 1e-10 * (1 + abs(lhs))
+    d = rng.standard_normal(wl.shape)
+    lhs = np.vdot(oracle.fwd(x, np.zeros_like(wb), d, sc), v)
+    assert abs(lhs - np.vdot(d, dwl)) < 1e-10 * (1 + abs(lhs))
+    d = rng.standard_normal(sc.shape)
+    lhs = np.vdot(oracle.fwd(x, np.zeros_like(wb), wl, d), v)
+    assert abs(lhs - np.vdot(d, dsc)) < 1e-10 * (1 + abs(lhs))
+
+
+# ------------------------------------------ rotated kernels (derived)
+
+def test_bwd_data_is_forward_with_rotated_kernels():
+    """The transpose of the layer has the same structure with every kernel
+    turned by 180 degrees (derived: corr^T = corr with the flipped kernel,
+    and the orthonormal Haar analysis and synthesis are each other's
+    transpose)."""
+    rng = np.random.default_rng(9)
+    _, v, wb, wl, sc = _rand_problem(rng, 2, 3, 32, 16, 3, 7, 5)
+    np.testing.assert_allclose(oracle.bwd_data(v, wb, wl, sc),
+                               oracle.fwd(v, wb[:, ::-1, ::-1], wl[..., ::-1, ::-1], sc), atol=1e-12)
+
+
+# ------------------------------------------ finite differences (P10)
+
+def test_central_finite_differences():
+    rng = np.random.default_rng(10)
+    x, v, wb, wl, sc = _rand_problem(rng, 1, 2, 16, 16, 2, 5, 3)
+
+    def loss(x_, wb_, wl_, sc_):
+        return np.vdot(oracle.fwd(x_, wb_, wl_, sc_), v)
+
+    dx = oracle.bwd_data(v, wb, wl, sc)
+    dwb, dwl, dsc = oracle.bwd_weight(x, v, wb, wl, sc)
+    eps = 1e-3
+    for trial in range(3):
+        for name, grad in (("x", dx), ("wb", dwb), ("wl", dwl), ("sc", dsc)):
+            d = rng.standard_normal(grad.shape)
+            args_p = dict(x_=x, wb_=wb, wl_=wl, sc_=sc)
+            args_m = dict(args_p)
+            args_p[name + "_"] = args_p[name + "_"] + eps * d
+            args_m[name + "_"] = args_m[name + "_"] - eps * d
+            fd = (loss(**args_p) - loss(**args_m)) / (2 * eps)
+            assert abs(fd - np.vdot(grad, d)) < 1e-8 * (1 + abs(fd)), name
+
+
+# ------------------------- torch autograd of a library-built layer
+
+def _torch_layer(x, wb, wl, sc):
+    """The layer assembled from torch library ops: strided grouped conv2d
+    for the Haar analysis, conv_transpose2d for synthesis, grouped conv2d
+    for every convolution. Used only to obtain gradients by autograd."""
+    C = x.shape[1]
+    L = wl.shape[0]
+    kb, k = wb.shape[-1], wl.shape[-1]
+    h = torch.tensor([[[1, 1], [1, 1]], [[1, 1], [-1, -1]], [[1, -1], [1, -1]], [[1, -1], [-1, 1]]],
+                     dtype=x.dtype) / 2
+    filt = h[None].repeat(C, 1, 1, 1).reshape(4 * C, 1, 2, 2)
+    y = torch.nn.functional.conv2d(x, wb[:, None], padding=kb // 2, groups=C)
+    lls, zs = [x], []
+    for l in range(L):
+        bands = torch.nn.functional.conv2d(lls[-1], filt, stride=2, groups=C)   # [B, 4C, h, w]
+        z = torch.nn.functional.conv2d(bands, wl[l].reshape(4 * C, 1, k, k), padding=k // 2, groups=4 * C)
+        zs.append(z * sc[l].reshape(1, 4 * C, 1, 1))
+        lls.append(bands[:, 0::4])
+    r = None
+    for l in reversed(range(L)):
+        z = zs[l].clone()
+        if r is not None:
+            z = torch.cat([(z[:, 0::4] + r)[:, :, None], z.reshape(z.shape[0], C, 4, *z.shape[2:])[:, :, 1:]], 2)
+            z = z.reshape(z.shape[0], 4 * C, *z.shape[3:])
+        r = torch.nn.functional.conv_transpose2d(z, filt, stride=2, groups=C)
+    return y + r if r is not None else y
+
+
+def test_against_torch_autograd():
+    rng = np.random.default_rng(11)
+    x, v, wb, wl, sc = _rand_problem(rng, 2, 3, 32, 32, 3, 5, 5)
+    t = [torch.from_numpy(a).clone().requires_grad_(True) for a in (x, wb, wl, sc)]
+    yt = _torch_layer(*t)
+    np.testing.assert_allclose(oracle.fwd(x, wb, wl, sc), yt.detach().numpy(), atol=1e-12)
+    yt.backward(torch.from_numpy(v))
+    dx = oracle.bwd_data(v, wb, wl, sc)
+    dwb, dwl, dsc = oracle.bwd_weight(x, v, wb, wl, sc)
+    np.testing.assert_allclose(dx, t[0].grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dwb, t[1].grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dwl, t[2].grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(dsc, t[3].grad.numpy(), atol=1e-10)
+
+
+# --------------------------------- scale-folded gradient form (P11)
+
+@pytest.mark.parametrize("L,kb,k", [(1, 5, 5), (3, 7, 5), (5, 3, 3)])
+def test_gcorr_gradients_equal_reverse_mode(L, kb, k):
+    rng = np.random.default_rng(12)
+    x, v, wb, wl, sc = _rand_problem(rng, 3, 2, 32, 32, L, kb, k)
+    a = oracle.bwd_weight(x, v, wb, wl, sc)
+    b = oracle.bwd_weight_gcorr(x, v, wb, wl, sc)
+    for ga, gb in zip(a, b):
+        np.testing.assert_allclose(ga, gb, atol=1e-11)
+
+
+# ---------------------------------------------- determinism (P12)
+
+def test_bitwise_stable_across_thread_counts():
+    inp = make_inputs(4, 3, 32, 32, 2, dtype="f32", seed=3)
+    x, dy = inp.act_f64("x"), inp.act_f64("dy")
+    wb, wl, sc = inp.params_f64()
+    n0 = oracle.max_threads()
+    try:
+        outs = []
+        for n in (1, 3, max(2, n0)):
+            oracle.set_threads(n)
+            outs.append((oracle.fwd(x, wb, wl, sc), oracle.bwd_data(dy, wb, wl, sc))
+                        + oracle.bwd_weight(x, dy, wb, wl, sc))
+        for o in outs[1:]:
+            for a, b in zip(outs[0], o):
+                assert np.array_equal(a, b)
+    finally:
+        oracle.set_threads(n0)
