@@ -11,7 +11,7 @@ def test_bf16_round_to_nearest_even():
     # 1+3*2^-8 ties between 1+2^-7 and 1+2^-6: even (1+2^-6) wins
     assert out[0] == 1.0 and out[1] == 1.0 and out[2] == np.float32(1 + 2 ** -6)
     assert out[3] == 1.0 and out[4] == -2.5
-    assert abs(out[5] - 3.0e-3) <= 2 ** -9 * 3.0e-3
+    assert abs(out[5] - 3.0e-3) <= 2 ** -8 * 3.0e-3   # unit roundoff of an 8-bit significand
     # decode is exact and round trip of representable values is the identity
     b = np.arange(0, 0x7F80, 7, dtype=np.uint16)
     assert np.array_equal(I.f32_to_bf16_bits(I.bf16_bits_to_f32(b)), b)

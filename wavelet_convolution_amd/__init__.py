@@ -2,17 +2,24 @@
 
 The compute path is ``libwtconv.so`` (HIP, built from ``csrc/``); the Python
 functions here only marshal arguments to it. Importing the package does not
-load the library; the first call does, and raises if it is missing.
+load the library; the first call of a binding function does, and raises if
+the library is missing.
 """
 from .configs import CONFIGS, WorkloadConfig, get_config  # noqa: F401
 
-__all__ = ["CONFIGS", "WorkloadConfig", "get_config"]
+_BINDING_NAMES = (
+    "wtconv_fwd", "wtconv_bwd_data", "wtconv_bwd_weight",
+    "wtconv_naive_fwd", "wtconv_naive_bwd_data", "wtconv_naive_bwd_weight",
+    "wtconv_workspace_size", "wtconv_status_string", "load_library", "WTConvError",
+)
+
+__all__ = ["CONFIGS", "WorkloadConfig", "get_config", *_BINDING_NAMES]
 
 
 def __getattr__(name):
-    # the binding is loaded on first use so that CPU-only code (configs,
+    # the binding is imported on first use so that CPU-only code (configs,
     # inputs, the I/O model) never needs the HIP runtime
-    from . import binding
-    if hasattr(binding, name):
+    if name in _BINDING_NAMES:
+        from . import binding
         return getattr(binding, name)
     raise AttributeError(name)
