@@ -1,0 +1,156 @@
+/*
+ * wtconv.h - C-ABI of the MI355X (gfx950) WTConv library, libwtconv.so.
+ *
+ * The operation
+ * -------------
+ * A wavelet-convolution (WTConv) layer, as named in the abstract of
+ * "I/O-aware reformulation of wavelet convolution" (arXiv:2608.10805;
+ * tech.sinsc.com page, Abstract, and the layerthelatestinalattice.com
+ * summary): a depthwise base convolution plus an L-level Haar wavelet branch.
+ * Per (b, c) plane:
+ *
+ *   X_0 = x;  for l = 1..L: (LL, B1, B2, B3)_l = DWT(X_{l-1}), X_l = LL_l
+ *   Z_l^s = scale[l][c][s] * corr(band_l^s, w_lvl[l][c][s])        s = 0..3
+ *   R_L = 0;  R_{l-1} = IWT(Z_l^0 + R_l, Z_l^1, Z_l^2, Z_l^3)
+ *   y = corr(x, w_base[c]) + R_0
+ *
+ *   DWT on the 2x2 block (a b / c d): LL = (a+b+c+d)/2, B1 = (a+b-c-d)/2,
+ *   B2 = (a-b+c-d)/2, B3 = (a-b-c+d)/2 (orthonormal); IWT is its inverse.
+ *   corr(u, w)[i][j] = sum_{m,n<k} w[m][n] u[i+m-k/2][j+n-k/2], zero outside
+ *   the level's own band grid (cross-correlation, 'same', stride 1).
+ *
+ * The kernels evaluate this through the three reformulations the abstract
+ * lists: the Haar analysis is recomputed on chip from x (or dy) and never
+ * stored, the synthesis cascade is one closed-form pass indexed by the bits of
+ * the output coordinates, and the scales are folded into the convolution
+ * results. The result equals the cascade up to fp32 rounding order.
+ *
+ * Data layout (all device pointers, caller-owned):
+ *   x, y, dy, dx   [B][C][H][W] contiguous, element type = desc->dtype
+ *   w_base         [C][k_base][k_base]        fp32
+ *   w_lvl          [L][C][4][k_level][k_level] fp32 (level index 0 = level 1)
+ *   scale          [L][C][4]                  fp32
+ *   gradients      fp32, same layouts as the parameters
+ * Band order s: 0 LL, 1 B1 (difference across rows), 2 B2 (difference across
+ * columns), 3 B3.
+ *
+ * Arithmetic: activations are loaded as fp32 (bf16 widened exactly), all
+ * products and sums are fp32, and bf16 outputs are rounded to nearest even.
+ *
+ * Ownership and synchronisation: the library allocates nothing, keeps no
+ * pointer after a call returns, never synchronises the stream, and is
+ * reentrant. Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream). Outputs are overwritten, never accumulated. x and y (dy and dx)
+ * must not overlap.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * launched; on error nothing is enqueued and the status says why. A failed
+ * launch (hipGetLastError) returns WTCONV_ERR_LAUNCH.
+ */
+#ifndef WTCONV_H
+#define WTCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WTCONV_F32 = 0,    /* fp32 activations */
+    WTCONV_BF16 = 1    /* bf16 activations, fp32 arithmetic */
+} wtconv_dtype_t;
+
+typedef enum {
+    WTCONV_OK = 0,
+    WTCONV_ERR_INVALID_ARG = 1,        /* null pointer, overlap, bad dtype, sizes < 1 */
+    WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* H or W not divisible by 2^L, even or
+                                          unsupported k, L out of range, or no
+                                          kernel for this plane size */
+    WTCONV_ERR_WORKSPACE = 3,          /* ws too small or misaligned */
+    WTCONV_ERR_LAUNCH = 4              /* the HIP runtime rejected a launch */
+} wtconv_status_t;
+
+typedef enum {
+    WTCONV_OP_FWD = 0,
+    WTCONV_OP_BWD_DATA = 1,
+    WTCONV_OP_BWD_WEIGHT = 2
+} wtconv_op_t;
+
+typedef struct {
+    int32_t B, C, H, W;   /* activation shape, NCHW */
+    int32_t levels;       /* L, 0..5 */
+    int32_t k_base;       /* base kernel size: 3, 5 or 7 */
+    int32_t k_level;      /* per-level kernel size: 3, 5 or 7 */
+    int32_t dtype;        /* wtconv_dtype_t */
+} wtconv_desc_t;
+
+/* Bytes of device workspace `op` needs for `desc` (0 if none). Returns
+   (size_t)-1 if the descriptor is invalid or unsupported. Workspace pointers
+   must be 256-byte aligned. */
+size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
+
+/* Forward: y = WTConv(x). One fused pass: reads x once, writes y once.
+   Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
+   that fit one workgroup's LDS; ws may then be NULL). */
+wtconv_status_t wtconv_fwd(const wtconv_desc_t *desc, const void *x,
+                           const float *w_base, const float *w_lvl,
+                           const float *scale, void *y, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Backward data: dx = J^T dy. The transpose of the layer is the same layer
+   with every kernel turned by 180 degrees (the orthonormal Haar analysis and
+   synthesis are each other's transpose, and corr^T is corr with the flipped
+   kernel), so this runs the forward kernels with rotated weight indexing. */
+wtconv_status_t wtconv_bwd_data(const wtconv_desc_t *desc, const void *dy,
+                                const float *w_base, const float *w_lvl,
+                                const float *scale, void *dx, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/* Backward weight: with G_l^s = sum_{b,i,j} (A_l^s dy)[i][j] (A_l^s x)[i+m-p][j+n-p]
+   the correlation of the two Haar pyramids (A_l^s = level-l band s analysis),
+     dw_base[c]      = sum_b corr-grad(x, dy)               [C][kb][kb]
+     dw_lvl[l][c][s] = scale[l][c][s] * G_l^s                [L][C][4][k][k]
+     dscale[l][c][s] = sum_{m,n} w_lvl[l][c][s][m][n] * G_l^s[m][n]
+   (the scale-folding reformulation applied to the gradient). The batch sum
+   is a fixed-order two-stage reduction, so results are bitwise
+   reproducible. Workspace: wtconv_workspace_size(desc, WTCONV_OP_BWD_WEIGHT). */
+wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t *desc, const void *x,
+                                  const void *dy, const float *w_lvl,
+                                  const float *scale, float *dw_base,
+                                  float *dw_lvl, float *dscale, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/* Naive unfused baseline (comparator only): the same three operations as a
+   chain of one-kernel-per-step launches (analysis, per-level convolution,
+   scale, LL add, synthesis, base convolution, final add) that keeps every
+   intermediate in device memory, as the abstract describes the reference
+   implementation. Same semantics and layouts as the fused entry points;
+   workspace from wtconv_naive_workspace_size. Any H, W divisible by 2^L. */
+size_t wtconv_naive_workspace_size(const wtconv_desc_t *desc, int32_t op);
+wtconv_status_t wtconv_naive_fwd(const wtconv_desc_t *desc, const void *x,
+                                 const float *w_base, const float *w_lvl,
+                                 const float *scale, void *y, void *ws,
+                                 size_t ws_bytes, void *stream);
+wtconv_status_t wtconv_naive_bwd_data(const wtconv_desc_t *desc, const void *dy,
+                                      const float *w_base, const float *w_lvl,
+                                      const float *scale, void *dx, void *ws,
+                                      size_t ws_bytes, void *stream);
+wtconv_status_t wtconv_naive_bwd_weight(const wtconv_desc_t *desc, const void *x,
+                                        const void *dy, const float *w_lvl,
+                                        const float *scale, float *dw_base,
+                                        float *dw_lvl, float *dscale, void *ws,
+                                        size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *wtconv_status_string(wtconv_status_t status);
+
+/* Library version, e.g. "0.1.0". */
+const char *wtconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WTCONV_H */

@@ -1,0 +1,90 @@
+"""The C-ABI library: it loads, exports every symbol the header declares,
+and rejects bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wtconv.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wtconv_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (load torch's HIP runtime first, as the binding does)
+    from wavelet_convolution_amd import binding
+    if not os.path.exists(binding._LIB_PATH):
+        pytest.skip("libwtconv.so not built")
+    return binding.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("wtconv_fwd", "wtconv_bwd_data", "wtconv_bwd_weight", "wtconv_workspace_size",
+              "wtconv_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _desc(**kw):
+    from wavelet_convolution_amd.binding import WTConvDesc
+    d = dict(B=2, C=4, H=56, W=56, levels=3, k_base=5, k_level=5, dtype=1)
+    d.update(kw)
+    return WTConvDesc(**d)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.wtconv_status_string(s).decode().startswith("WTCONV")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(C=-1), 1), (dict(dtype=7), 1),
+    (dict(levels=6), 2), (dict(k_base=4), 2), (dict(k_level=9), 2), (dict(H=60), 2),
+    (dict(H=56, W=52), 2),  # 52 not divisible by 8
+])
+def test_bad_descriptors_rejected_before_launch(lib, kw, status):
+    d = _desc(**kw)
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    rc = lib.wtconv_fwd(ctypes.byref(d), fake, fake, fake, fake, ctypes.c_void_p(2 << 20), None, 0, None)
+    assert rc == status
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    d = _desc()
+    ok = ctypes.c_void_p(1 << 20)
+    assert lib.wtconv_fwd(ctypes.byref(d), None, ok, ok, ok, ok, None, 0, None) == 1
+    assert lib.wtconv_fwd(ctypes.byref(d), ctypes.c_void_p((1 << 20) + 2), ok, ok, ok,
+                          ctypes.c_void_p(2 << 20), None, 0, None) == 1
+    # input and output overlapping
+    assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ok, None, 0, None) == 1
+
+
+def test_unplanned_plane_is_unsupported(lib):
+    d = _desc(H=40, W=48, levels=3)
+    ok = ctypes.c_void_p(1 << 20)
+    assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ctypes.c_void_p(1 << 30), None, 0, None) == 2
+
+
+def test_bwd_weight_workspace_checked(lib):
+    d = _desc()
+    need = lib.wtconv_workspace_size(ctypes.byref(d), 2)
+    assert 0 < need < (1 << 40)
+    ok = ctypes.c_void_p(1 << 20)
+    # too small
+    assert lib.wtconv_bwd_weight(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ctypes.c_void_p(1 << 24),
+                                 need - 4, None) == 3
+    # misaligned
+    assert lib.wtconv_bwd_weight(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ctypes.c_void_p((1 << 24) + 16),
+                                 need, None) == 3

@@ -1,0 +1,126 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Bar (normwise max relative error per output tensor, max|g-o| / max|o|):
+1e-4 for fp32 activations, 2e-2 for bf16 activations. Every shape is also
+run with fp32 activations, where the kernels are the same templates, so a
+mistake small enough to hide under the bf16 bound still fails at 1e-4.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests._util import TOL, rel_err, to_device, to_f64
+from wavelet_convolution_amd.inputs import make_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines too
+    pytest.skip("no GPU", allow_module_level=True)
+
+from wavelet_convolution_amd import binding as wt  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# (B, C, H, W, L, kb, k): every whole-plane plan, including shapes with a
+# partial last round of work items, other kernel sizes and non-square planes
+SMALL = [
+    (2, 3, 32, 32, 2, 5, 5),
+    (2, 3, 56, 56, 3, 5, 5),
+    (2, 3, 28, 28, 2, 5, 5),
+    (2, 3, 14, 14, 1, 5, 5),
+    (1, 2, 128, 128, 1, 5, 5),
+    (1, 2, 128, 128, 3, 5, 5),
+    (1, 2, 128, 128, 5, 5, 5),
+    (2, 3, 32, 32, 3, 7, 5),
+    (2, 3, 24, 40, 3, 3, 3),
+    (3, 2, 16, 16, 4, 3, 7),
+    (2, 2, 64, 64, 4, 7, 5),
+]
+
+# the fused backward weight kernel keeps whole planes and both pyramids in LDS
+BWDW_OK = {(32, 32, 2, 5, 5), (56, 56, 3, 5, 5), (28, 28, 2, 5, 5), (14, 14, 1, 5, 5),
+           (32, 32, 3, 7, 5), (24, 40, 3, 3, 3), (16, 16, 4, 3, 7), (64, 64, 4, 7, 5)}
+
+
+def _oracle_all(inp):
+    x, dy = inp.act_f64("x"), inp.act_f64("dy")
+    wb, wl, sc = inp.params_f64()
+    return (oracle.fwd(x, wb, wl, sc), oracle.bwd_data(dy, wb, wl, sc), oracle.bwd_weight(x, dy, wb, wl, sc))
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_matches_oracle(shape, dtype):
+    B, C, H, W, L, kb, k = shape
+    _say(f"[parity] fused {dtype} {shape}")
+    inp = make_inputs(B, C, H, W, L, kb, k, dtype=dtype, seed=0)
+    x, dy, wb, wl, sc = to_device(inp)
+    y = wt.wtconv_fwd(x, wb, wl, sc)
+    dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+    torch.cuda.synchronize()
+    oy, odx, (odwb, odwl, odsc) = _oracle_all(inp)
+    tol = TOL[dtype]
+    assert rel_err(to_f64(y), oy) <= tol
+    assert rel_err(to_f64(dx), odx) <= tol
+    if (H, W, L, kb, k) in BWDW_OK:
+        dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, kb, wl, sc)
+        torch.cuda.synchronize()
+        # gradients are fp32 sums over the batch of bf16-exact products
+        assert rel_err(to_f64(dwb), odwb) <= TOL["f32"]
+        assert rel_err(to_f64(dwl), odwl) <= TOL["f32"]
+        assert rel_err(to_f64(dsc), odsc) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("shape", SMALL[:4] + SMALL[7:9], ids=lambda s: "x".join(map(str, s)))
+def test_naive_matches_oracle(shape):
+    B, C, H, W, L, kb, k = shape
+    _say(f"[parity] naive f32 {shape}")
+    inp = make_inputs(B, C, H, W, L, kb, k, dtype="f32", seed=1)
+    x, dy, wb, wl, sc = to_device(inp)
+    y = wt.wtconv_naive_fwd(x, wb, wl, sc)
+    dx = wt.wtconv_naive_bwd_data(dy, wb, wl, sc)
+    dwb, dwl, dsc = wt.wtconv_naive_bwd_weight(x, dy, kb, wl, sc)
+    torch.cuda.synchronize()
+    oy, odx, (odwb, odwl, odsc) = _oracle_all(inp)
+    for g, o in ((y, oy), (dx, odx), (dwb, odwb), (dwl, odwl), (dsc, odsc)):
+        assert rel_err(to_f64(g), o) <= TOL["f32"]
+
+
+def test_adjoint_identity_on_gpu():
+    _say("[parity] adjoint 2x3x56x56 L3")
+    inp = make_inputs(2, 3, 56, 56, 3, dtype="f32", seed=2)
+    x, dy, wb, wl, sc = to_device(inp)
+    y = wt.wtconv_fwd(x, wb, wl, sc)
+    dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+    lhs = float((y.double() * dy.double()).sum())
+    rhs = float((x.double() * dx.double()).sum())
+    assert abs(lhs - rhs) <= 1e-5 * (abs(lhs) + abs(rhs) + 1.0)
+
+
+def test_bwd_weight_bitwise_deterministic():
+    _say("[parity] determinism 8x16x56x56 L3 bf16")
+    inp = make_inputs(8, 16, 56, 56, 3, dtype="bf16", seed=3)
+    x, dy, wb, wl, sc = to_device(inp)
+    a = wt.wtconv_bwd_weight(x, dy, 5, wl, sc)
+    b = wt.wtconv_bwd_weight(x, dy, 5, wl, sc)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_zero_branch_equals_base_only():
+    """Zero scales: the branch contributes exactly nothing (not approximately)."""
+    _say("[parity] zero branch")
+    inp = make_inputs(2, 3, 56, 56, 3, dtype="f32", seed=4)
+    x, dy, wb, wl, sc = to_device(inp)
+    y0 = wt.wtconv_fwd(x, wb, wl, torch.zeros_like(sc))
+    ref = torch.nn.functional.conv2d(x.double().cpu(), wb.double().cpu()[:, None], padding=2, groups=3)
+    assert rel_err(to_f64(y0), ref.numpy()) <= 1e-6

@@ -1,0 +1,187 @@
+"""Thin ctypes binding of libwtconv.so (argument marshalling only).
+
+Every function takes torch tensors on the GPU, checks nothing beyond what is
+needed to build the C descriptor, and calls the C-ABI entry point of the same
+name on the current stream. Validation and every step of the computation
+happen in the library. The library must exist: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwtconv.so")
+_lock = threading.Lock()
+_lib = None
+
+WTCONV_F32, WTCONV_BF16 = 0, 1
+OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2
+
+
+class WTConvError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class WTConvDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("C", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("levels", ctypes.c_int32), ("k_base", ctypes.c_int32),
+                ("k_level", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_V = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_P = ctypes.POINTER(WTConvDesc)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libwtconv.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError(
+                    f"{_LIB_PATH} is missing: build it with `python -m wavelet_convolution_amd.build` "
+                    "(there is no CPU fallback)")
+            lib = ctypes.CDLL(_LIB_PATH)
+            lib.wtconv_workspace_size.argtypes = [_P, ctypes.c_int32]
+            lib.wtconv_workspace_size.restype = _SZ
+            lib.wtconv_naive_workspace_size.argtypes = [_P, ctypes.c_int32]
+            lib.wtconv_naive_workspace_size.restype = _SZ
+            for name in ("wtconv_fwd", "wtconv_bwd_data", "wtconv_naive_fwd", "wtconv_naive_bwd_data"):
+                fn = getattr(lib, name)
+                fn.argtypes = [_P, _V, _V, _V, _V, _V, _V, _SZ, _V]
+                fn.restype = ctypes.c_int
+            for name in ("wtconv_bwd_weight", "wtconv_naive_bwd_weight"):
+                fn = getattr(lib, name)
+                fn.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]
+                fn.restype = ctypes.c_int
+            lib.wtconv_status_string.argtypes = [ctypes.c_int]
+            lib.wtconv_status_string.restype = ctypes.c_char_p
+            lib.wtconv_version.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def wtconv_status_string(status: int) -> str:
+    return load_library().wtconv_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise WTConvError(status, wtconv_status_string(status))
+
+
+def _desc(act: torch.Tensor, levels: int, k_base: int, k_level: int) -> WTConvDesc:
+    B, C, H, W = act.shape
+    dt = {torch.float32: WTCONV_F32, torch.bfloat16: WTCONV_BF16}.get(act.dtype, -1)
+    return WTConvDesc(B, C, H, W, int(levels), int(k_base), int(k_level), dt)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _dims(w_base: torch.Tensor, w_lvl: torch.Tensor):
+    levels = int(w_lvl.shape[0]) if w_lvl is not None else 0
+    k_level = int(w_lvl.shape[-1]) if (w_lvl is not None and w_lvl.dim() == 5) else 3
+    k_base = int(w_base.shape[-1])
+    return levels, k_base, k_level
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def wtconv_workspace_size(act: torch.Tensor, levels: int, k_base: int, k_level: int, op: int,
+                          naive: bool = False) -> int:
+    lib = load_library()
+    d = _desc(act, levels, k_base, k_level)
+    fn = lib.wtconv_naive_workspace_size if naive else lib.wtconv_workspace_size
+    n = fn(ctypes.byref(d), int(op))
+    if n == ctypes.c_size_t(-1).value:
+        raise WTConvError(2, wtconv_status_string(2))
+    return int(n)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+
+
+def _ws_ptr(ws: torch.Tensor | None) -> int:
+    if ws is None:
+        return 0
+    p = ws.data_ptr()
+    return (p + 255) & ~255
+
+
+def _data_pass(name: str, naive: bool, op: int, act, w_base, w_lvl, scale, out, ws, stream):
+    lib = load_library()
+    levels, kb, k = _dims(w_base, w_lvl)
+    d = _desc(act, levels, kb, k)
+    if out is None:
+        out = torch.empty_like(act)
+    if ws is None:
+        ws = _workspace(wtconv_workspace_size(act, levels, kb, k, op, naive), act.device)
+    ws_bytes = 0 if ws is None else ws.numel() - (_ws_ptr(ws) - ws.data_ptr())
+    _check(getattr(lib, name)(ctypes.byref(d), _ptr(act), _ptr(w_base), _ptr(w_lvl), _ptr(scale),
+                              _ptr(out), _ws_ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def wtconv_fwd(x, w_base, w_lvl, scale, y=None, ws=None, stream=None):
+    """y = WTConv(x). x: [B,C,H,W] fp32/bf16 CUDA tensor; w_base [C,kb,kb],
+    w_lvl [L,C,4,k,k], scale [L,C,4] fp32."""
+    return _data_pass("wtconv_fwd", False, OP_FWD, x, w_base, w_lvl, scale, y, ws, stream)
+
+
+def wtconv_bwd_data(dy, w_base, w_lvl, scale, dx=None, ws=None, stream=None):
+    """dx = J^T dy."""
+    return _data_pass("wtconv_bwd_data", False, OP_BWD_DATA, dy, w_base, w_lvl, scale, dx, ws, stream)
+
+
+def wtconv_naive_fwd(x, w_base, w_lvl, scale, y=None, ws=None, stream=None):
+    return _data_pass("wtconv_naive_fwd", True, OP_FWD, x, w_base, w_lvl, scale, y, ws, stream)
+
+
+def wtconv_naive_bwd_data(dy, w_base, w_lvl, scale, dx=None, ws=None, stream=None):
+    return _data_pass("wtconv_naive_bwd_data", True, OP_BWD_DATA, dy, w_base, w_lvl, scale, dx, ws, stream)
+
+
+def _bwd_weight(name: str, naive: bool, x, dy, w_base_shape_kb, w_lvl, scale, out, ws, stream):
+    lib = load_library()
+    levels = int(w_lvl.shape[0])
+    k = int(w_lvl.shape[-1])
+    kb = int(w_base_shape_kb)
+    d = _desc(x, levels, kb, k)
+    C = x.shape[1]
+    if out is None:
+        dev = x.device
+        out = (torch.empty((C, kb, kb), dtype=torch.float32, device=dev),
+               torch.empty((levels, C, 4, k, k), dtype=torch.float32, device=dev),
+               torch.empty((levels, C, 4), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = _workspace(wtconv_workspace_size(x, levels, kb, k, OP_BWD_WEIGHT, naive), x.device)
+    ws_bytes = 0 if ws is None else ws.numel() - (_ws_ptr(ws) - ws.data_ptr())
+    dwb, dwl, dsc = out
+    _check(getattr(lib, name)(ctypes.byref(d), _ptr(x), _ptr(dy), _ptr(w_lvl), _ptr(scale), _ptr(dwb),
+                              _ptr(dwl), _ptr(dsc), _ws_ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def wtconv_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stream=None):
+    """(dW_base, dW_lvl, dscale) for kernels of size k_base (base) and w_lvl's."""
+    return _bwd_weight("wtconv_bwd_weight", False, x, dy, k_base, w_lvl, scale, out, ws, stream)
+
+
+def wtconv_naive_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stream=None):
+    return _bwd_weight("wtconv_naive_bwd_weight", True, x, dy, k_base, w_lvl, scale, out, ws, stream)

@@ -1,0 +1,194 @@
+// C-ABI of libwtconv.so: argument validation on the host, then dispatch to
+// the fused kernels (forward, backward data, backward weight) or to the naive
+// unfused chain. Nothing is launched unless every check passes.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/wtconv.h"
+#include "wtconv_plans.h"
+#include "wtconv_bwdw.h"
+#include "wtconv_naive.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+size_t act_bytes(const wtconv_desc_t* d) {
+    return (size_t)d->B * d->C * d->H * d->W * (d->dtype == WTCONV_BF16 ? 2 : 4);
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Shape checks shared by every entry point.
+wtconv_status_t check_desc(const wtconv_desc_t* d) {
+    if (!d) return WTCONV_ERR_INVALID_ARG;
+    if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1) return WTCONV_ERR_INVALID_ARG;
+    if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_BF16) return WTCONV_ERR_INVALID_ARG;
+    if (d->levels < 0 || d->levels > 5) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    const int kb = d->k_base, k = d->k_level;
+    if (kb != 3 && kb != 5 && kb != 7) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    if (k != 3 && k != 5 && k != 7) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    const int blk = 1 << d->levels;
+    if (d->H % blk != 0 || d->W % blk != 0) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    // every index below is computed in 32 bits per plane and 64 bits across planes
+    if ((int64_t)d->H * d->W > (1ll << 30) || (int64_t)d->B * d->C > (1ll << 31) - 1)
+        return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    return WTCONV_OK;
+}
+
+wtconv_status_t check_params(const wtconv_desc_t* d, const float* w_base, const float* w_lvl,
+                             const float* scale, bool need_base) {
+    if (need_base && !w_base) return WTCONV_ERR_INVALID_ARG;
+    if (d->levels > 0 && (!w_lvl || !scale)) return WTCONV_ERR_INVALID_ARG;
+    if ((w_base && !aligned16(w_base)) || (w_lvl && !aligned16(w_lvl)) || (scale && !aligned16(scale)))
+        return WTCONV_ERR_INVALID_ARG;
+    return WTCONV_OK;
+}
+
+wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const float* w_base,
+                                const float* w_lvl, const float* scale, void* out, void* ws,
+                                size_t ws_bytes, void* stream, bool flip) {
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (!in || !out) return WTCONV_ERR_INVALID_ARG;
+    if (!aligned16(in) || !aligned16(out)) return WTCONV_ERR_INVALID_ARG;
+    if (overlap(in, act_bytes(d), out, act_bytes(d))) return WTCONV_ERR_INVALID_ARG;
+    st = check_params(d, w_base, w_lvl, scale, true);
+    if (st != WTCONV_OK) return st;
+    const wtc::PlaneEntry* e = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level);
+    if (!e) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    (void)ws;
+    (void)ws_bytes;
+    hipError_t err = e->fn[d->dtype == WTCONV_BF16 ? 1 : 0][flip ? 1 : 0](
+        in, w_base, w_lvl, scale, out, d->B, d->C, (hipStream_t)stream);
+    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
+    if (check_desc(d) != WTCONV_OK) return (size_t)-1;
+    switch (op) {
+    case WTCONV_OP_FWD:
+    case WTCONV_OP_BWD_DATA:
+        return wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level) ? 0 : (size_t)-1;
+    case WTCONV_OP_BWD_WEIGHT:
+        return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
+    default:
+        return (size_t)-1;
+    }
+}
+
+wtconv_status_t wtconv_fwd(const wtconv_desc_t* d, const void* x, const float* w_base,
+                           const float* w_lvl, const float* scale, void* y, void* ws,
+                           size_t ws_bytes, void* stream) {
+    return fused_data_pass(d, x, w_base, w_lvl, scale, y, ws, ws_bytes, stream, false);
+}
+
+wtconv_status_t wtconv_bwd_data(const wtconv_desc_t* d, const void* dy, const float* w_base,
+                                const float* w_lvl, const float* scale, void* dx, void* ws,
+                                size_t ws_bytes, void* stream) {
+    return fused_data_pass(d, dy, w_base, w_lvl, scale, dx, ws, ws_bytes, stream, true);
+}
+
+wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const void* dy,
+                                  const float* w_lvl, const float* scale, float* dw_base,
+                                  float* dw_lvl, float* dscale, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (!x || !dy || !dw_base) return WTCONV_ERR_INVALID_ARG;
+    if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dw_base)) return WTCONV_ERR_INVALID_ARG;
+    if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
+    st = check_params(d, nullptr, w_lvl, scale, false);
+    if (st != WTCONV_OK) return st;
+    const size_t need = wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
+                                                  d->k_level);
+    if (need == (size_t)-1) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+    hipError_t err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                      d->dtype == WTCONV_BF16, x, dy, w_lvl, scale, dw_base,
+                                      dw_lvl, dscale, ws, (hipStream_t)stream);
+    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+size_t wtconv_naive_workspace_size(const wtconv_desc_t* d, int32_t op) {
+    if (check_desc(d) != WTCONV_OK) return (size_t)-1;
+    return wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                      op);
+}
+
+static wtconv_status_t naive_data(const wtconv_desc_t* d, const void* in, const float* w_base,
+                                  const float* w_lvl, const float* scale, void* out, void* ws,
+                                  size_t ws_bytes, void* stream, int op) {
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (!in || !out || !aligned16(in) || !aligned16(out)) return WTCONV_ERR_INVALID_ARG;
+    if (overlap(in, act_bytes(d), out, act_bytes(d))) return WTCONV_ERR_INVALID_ARG;
+    st = check_params(d, w_base, w_lvl, scale, true);
+    if (st != WTCONV_OK) return st;
+    const size_t need = wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
+                                                   d->k_level, op);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+    hipError_t err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base,
+                                            d->k_level, d->dtype == WTCONV_BF16,
+                                            op == WTCONV_OP_BWD_DATA, in, w_base, w_lvl, scale,
+                                            out, ws, (hipStream_t)stream);
+    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+wtconv_status_t wtconv_naive_fwd(const wtconv_desc_t* d, const void* x, const float* w_base,
+                                 const float* w_lvl, const float* scale, void* y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    return naive_data(d, x, w_base, w_lvl, scale, y, ws, ws_bytes, stream, WTCONV_OP_FWD);
+}
+
+wtconv_status_t wtconv_naive_bwd_data(const wtconv_desc_t* d, const void* dy, const float* w_base,
+                                      const float* w_lvl, const float* scale, void* dx, void* ws,
+                                      size_t ws_bytes, void* stream) {
+    return naive_data(d, dy, w_base, w_lvl, scale, dx, ws, ws_bytes, stream, WTCONV_OP_BWD_DATA);
+}
+
+wtconv_status_t wtconv_naive_bwd_weight(const wtconv_desc_t* d, const void* x, const void* dy,
+                                        const float* w_lvl, const float* scale, float* dw_base,
+                                        float* dw_lvl, float* dscale, void* ws, size_t ws_bytes,
+                                        void* stream) {
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (!x || !dy || !dw_base || !aligned16(x) || !aligned16(dy)) return WTCONV_ERR_INVALID_ARG;
+    if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
+    st = check_params(d, nullptr, w_lvl, scale, false);
+    if (st != WTCONV_OK) return st;
+    const size_t need = wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
+                                                   d->k_level, WTCONV_OP_BWD_WEIGHT);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+    hipError_t err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base,
+                                            d->k_level, d->dtype == WTCONV_BF16, x, dy, w_lvl,
+                                            scale, dw_base, dw_lvl, dscale, ws,
+                                            (hipStream_t)stream);
+    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+const char* wtconv_status_string(wtconv_status_t s) {
+    switch (s) {
+    case WTCONV_OK: return "WTCONV_OK";
+    case WTCONV_ERR_INVALID_ARG: return "WTCONV_ERR_INVALID_ARG: null, misaligned or overlapping pointer, or bad size/dtype";
+    case WTCONV_ERR_UNSUPPORTED_SHAPE: return "WTCONV_ERR_UNSUPPORTED_SHAPE: H, W not divisible by 2^L, unsupported kernel size or levels, or no kernel for this plane";
+    case WTCONV_ERR_WORKSPACE: return "WTCONV_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case WTCONV_ERR_LAUNCH: return "WTCONV_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    default: return "WTCONV: unknown status";
+    }
+}
+
+const char* wtconv_version(void) { return "0.1.0"; }
+
+}  // extern "C"

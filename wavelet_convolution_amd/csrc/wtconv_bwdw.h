@@ -1,0 +1,18 @@
+// Backward-weight launchers (fused kernel + fixed-order second stage).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace wtc {
+
+// Workspace bytes for the per-chunk partial sums, or (size_t)-1 if no fused
+// plan covers this shape.
+size_t bwdw_workspace_bytes(int B, int C, int H, int W, int L, int KB, int K);
+
+hipError_t bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16,
+                       const void* x, const void* dy, const float* w_lvl, const float* scale,
+                       float* dw_base, float* dw_lvl, float* dscale, void* ws,
+                       hipStream_t stream);
+
+}  // namespace wtc

@@ -1,0 +1,184 @@
+// Device-side helpers shared by the WTConv HIP kernels (gfx950).
+//
+// Activation storage is fp32 or bf16; every product and sum is fp32. bf16 is
+// widened exactly (a 16-bit shift) and narrowed with round-to-nearest-even,
+// written from the IEEE definition.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wtc {
+
+typedef uint16_t bf16_t;
+
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Row strides of LDS planes are made odd so that lanes reading the same
+// column of different rows fall into different banks.
+constexpr int odd_stride(int w) { return (w % 2 == 0) ? w + 1 : w; }
+
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+__device__ __forceinline__ bf16_t narrow_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // keep NaN quiet
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Act;
+template <> struct Act<float> {
+    static constexpr int BYTES = 4;
+};
+template <> struct Act<bf16_t> {
+    static constexpr int BYTES = 2;
+};
+
+// Largest vector (elements) that divides a row and keeps every plane aligned.
+template <typename T>
+constexpr int vec_elems(int W, int HW) {
+    const int cands[4] = {16 / Act<T>::BYTES, 8 / Act<T>::BYTES, 4 / Act<T>::BYTES, 1};
+    for (int i = 0; i < 4; ++i) {
+        int v = cands[i];
+        if (v >= 1 && W % v == 0 && (HW * Act<T>::BYTES) % (v * Act<T>::BYTES) == 0) return v;
+    }
+    return 1;
+}
+
+// Load V consecutive activations (V * sizeof(T) bytes, naturally aligned)
+// and widen them to fp32.
+template <typename T, int V>
+__device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&out)[V]) {
+    constexpr int BYTES = V * Act<T>::BYTES;
+    if constexpr (BYTES == 16) {
+        uint4 q = *reinterpret_cast<const uint4*>(p);
+        uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                out[2 * i] = __uint_as_float(w[i] << 16);
+                out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+        }
+    } else if constexpr (BYTES == 8) {
+        uint2 q = *reinterpret_cast<const uint2*>(p);
+        uint32_t w[2] = {q.x, q.y};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                out[2 * i] = __uint_as_float(w[i] << 16);
+                out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        } else {
+            out[0] = __uint_as_float(w[0]);
+            out[1] = __uint_as_float(w[1]);
+        }
+    } else if constexpr (BYTES == 4 && sizeof(T) == 2) {
+        uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+        out[0] = __uint_as_float(w << 16);
+        out[1] = __uint_as_float(w & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) out[i] = widen(p[i]);
+    }
+}
+
+// Store a row segment of N fp32 values (N even for bf16; the segment start
+// is 4-byte aligned for bf16 and 8-byte aligned for fp32 pairs).
+template <int N>
+__device__ __forceinline__ void store_row(float* __restrict__ p, const float (&v)[N]) {
+    if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) *reinterpret_cast<float2*>(p + i) = make_float2(v[i], v[i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) p[i] = v[i];
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_row(bf16_t* __restrict__ p, const float (&v)[N]) {
+    static_assert(N % 2 == 0, "bf16 rows are stored as pairs");
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+        uint32_t lo = narrow_bf16(v[i]), hi = narrow_bf16(v[i + 1]);
+        *reinterpret_cast<uint32_t*>(p + i) = lo | (hi << 16);
+    }
+}
+
+// Tap (m, n) of a k x k kernel; FLIP turns the kernel by 180 degrees (the
+// transpose of a 'same' cross-correlation with odd k).
+template <int K, bool FLIP>
+__device__ __forceinline__ float tap(const float* __restrict__ w, int m, int n) {
+    return FLIP ? w[(K - 1 - m) * K + (K - 1 - n)] : w[m * K + n];
+}
+
+// acc[o][q] += sum_{m,n} w[m][n] * s[(o+m)*S + q+n]: an OR x OC tile of a
+// 'same' cross-correlation read from a zero-bordered LDS plane (s points at
+// the window's top-left corner, S is the plane's row stride). Window rows are
+// streamed through registers; every loaded value feeds up to K*K FMAs.
+template <int K, int OR, int OC, int S, bool FLIP>
+__device__ __forceinline__ void conv_tile(const float* s, const float* __restrict__ w,
+                                          float (&acc)[OR][OC]) {
+    float wr[K * K];
+#pragma unroll
+    for (int t = 0; t < K * K; ++t) wr[t] = tap<K, FLIP>(w, t / K, t % K);
+#pragma unroll
+    for (int r = 0; r < OR + K - 1; ++r) {
+        float win[OC + K - 1];
+#pragma unroll
+        for (int q = 0; q < OC + K - 1; ++q) win[q] = s[r * S + q];
+#pragma unroll
+        for (int o = 0; o < OR; ++o) {
+            const int m = r - o;
+            if (m < 0 || m >= K) continue;
+#pragma unroll
+            for (int n = 0; n < K; ++n) {
+#pragma unroll
+                for (int q = 0; q < OC; ++q) acc[o][q] = __builtin_fmaf(wr[m * K + n], win[q + n], acc[o][q]);
+            }
+        }
+    }
+}
+
+// Zero the border cells of NB bordered planes of interior h x w, border B,
+// row stride S (everything outside rows [B, B+h) x cols [B, B+w)).
+template <int NB, int h, int w, int B, int S>
+__device__ __forceinline__ void zero_border(float* base, int tid, int nt) {
+    constexpr int ROWS = h + 2 * B;
+    constexpr int TOPBOT = 2 * B * S;
+    constexpr int SIDE = S - w;
+    constexpr int PER = TOPBOT + h * SIDE;
+    for (int i = tid; i < NB * PER; i += nt) {
+        const int b = i / PER;
+        int j = i - b * PER, r, c;
+        if (j < TOPBOT) {
+            r = j / S;
+            c = j - r * S;
+            if (r >= B) r += h;
+        } else {
+            j -= TOPBOT;
+            r = B + j / SIDE;
+            c = j % SIDE;
+            if (c >= B) c += w;
+        }
+        base[b * ROWS * S + r * S + c] = 0.f;
+    }
+}
+
+// Butterfly of one 2x2 block (a b / c d), unnormalised: the four Haar bands
+// times 2 (the 1/2 factors are folded into the convolution weights).
+__device__ __forceinline__ void haar4(float a, float b, float c, float d, float& ll, float& b1,
+                                      float& b2, float& b3) {
+    const float s0 = a + b, d0 = a - b, s1 = c + d, d1 = c - d;
+    ll = s0 + s1;
+    b1 = s0 - s1;
+    b2 = d0 + d1;
+    b3 = d0 - d1;
+}
+
+}  // namespace wtc

@@ -1,0 +1,120 @@
+// Compile-time plans of the whole-plane fused kernel: the LDS layout and the
+// work split of one (b, c) plane over a workgroup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "wtconv_device.h"
+
+namespace wtc {
+
+struct Tile {
+    int r, c;
+};
+
+// Tile (positions per work item) for a coarse level grid of h x w on nt
+// threads: the shortest critical path (items per thread x tile size), ties
+// going to the larger tile (fewer LDS reads per FMA).
+constexpr Tile pick_tile(int h, int w, int nt) {
+    const int cand[7][2] = {{4, 4}, {4, 2}, {2, 4}, {2, 2}, {2, 1}, {1, 2}, {1, 1}};
+    Tile best{1, 1};
+    int best_cost = 1 << 30, best_size = 0;
+    for (int i = 0; i < 7; ++i) {
+        const int r = cand[i][0], c = cand[i][1];
+        if (h % r != 0 || w % c != 0) continue;
+        const int items = (h / r) * (w / c);
+        const int cost = cdiv(items, nt) * r * c;
+        if (cost < best_cost || (cost == best_cost && r * c > best_size)) {
+            best = Tile{r, c};
+            best_cost = cost;
+            best_size = r * c;
+        }
+    }
+    return best;
+}
+
+// H x W plane, L levels, base kernel KB, level kernel K, NT threads; a main
+// work item is a TR x TC tile of level-1 positions (a 2TR x 2TC output tile).
+//
+// LDS: region A holds x with a zero border of KB/2 (row stride SX); after the
+// base convolution it is reused for the bordered subbands of levels 2..L.
+// Region B holds the four bordered level-1 subbands. Bordered planes have a
+// zero border of K/2 and an odd row stride.
+template <int H_, int W_, int L_, int KB_, int K_, int NT_, int TR_, int TC_>
+struct PlanePlan {
+    static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, NT = NT_, TR = TR_, TC = TC_;
+    static constexpr int PB = KB / 2, PK = K / 2;
+    static_assert(L >= 1, "the whole-plane kernel needs at least one level");
+    static_assert(H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
+    static_assert((H / 2) % TR == 0 && (W / 2) % TC == 0, "main tile must divide the level-1 grid");
+    static_assert(KB % 2 == 1 && K % 2 == 1, "odd kernels only");
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole wavefronts");
+
+    static constexpr int SX = odd_stride(W + 2 * PB);
+    static constexpr int XSIZE = (H + 2 * PB) * SX;
+    static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
+    static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
+    static constexpr int uoff(int l) {
+        int o = 0;
+        for (int q = 2; q < l; ++q) o += 4 * bandsz(q);
+        return o;
+    }
+    static constexpr int UDEEP = uoff(L + 1);
+    static constexpr int ASIZE = XSIZE > UDEEP ? XSIZE : UDEEP;
+    static constexpr int BSIZE = 4 * bandsz(1);
+    static constexpr int LDS_FLOATS = ASIZE + BSIZE;
+    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
+    static constexpr int NI = ((H / 2) / TR) * ((W / 2) / TC);
+    static constexpr int MI = cdiv(NI, NT);
+
+    static constexpr Tile deep_tile(int l) { return pick_tile(H >> l, W >> l, NT); }
+
+    // f(std::integral_constant<int, l>) for l = 2..L, unrolled at compile time
+    template <class F>
+    __device__ static __forceinline__ void for_deep_levels(F&& f) {
+        deep_impl(f, std::make_integer_sequence<int, (L >= 2 ? L - 1 : 0)>{});
+    }
+    template <class F, int... I>
+    __device__ static __forceinline__ void deep_impl(F& f, std::integer_sequence<int, I...>) {
+        (f(std::integral_constant<int, I + 2>{}), ...);
+    }
+};
+
+typedef hipError_t (*plane_launch_fn)(const void* in, const float* w_base, const float* w_lvl,
+                                      const float* scale, void* out, int B, int C,
+                                      hipStream_t stream);
+
+struct PlaneEntry {
+    int H, W, L, KB, K;
+    plane_launch_fn fn[2][2];  // [dtype: 0 fp32, 1 bf16][flip: 0 fwd, 1 bwd_data]
+    int lds_bytes;
+    int nt;
+};
+
+const PlaneEntry* find_plane_entry(int H, int W, int L, int KB, int K);
+
+// ------------------------------------------------------------ the plans
+// ConvNeXt-stage and sweep shapes first, then small shapes that exercise
+// other kernel sizes, odd tile counts and non-square planes.
+typedef PlanePlan<32, 32, 2, 5, 5, 64, 2, 2> PP_32_L2_k55;
+typedef PlanePlan<56, 56, 3, 5, 5, 64, 2, 7> PP_56_L3_k55;
+typedef PlanePlan<28, 28, 2, 5, 5, 64, 2, 2> PP_28_L2_k55;
+typedef PlanePlan<14, 14, 1, 5, 5, 64, 1, 1> PP_14_L1_k55;
+typedef PlanePlan<128, 128, 1, 5, 5, 256, 4, 4> PP_128_L1_k55;
+typedef PlanePlan<128, 128, 2, 5, 5, 256, 4, 4> PP_128_L2_k55;
+typedef PlanePlan<128, 128, 3, 5, 5, 256, 4, 4> PP_128_L3_k55;
+typedef PlanePlan<128, 128, 4, 5, 5, 256, 4, 4> PP_128_L4_k55;
+typedef PlanePlan<128, 128, 5, 5, 5, 256, 4, 4> PP_128_L5_k55;
+typedef PlanePlan<32, 32, 3, 7, 5, 64, 2, 2> PP_32_L3_k75;
+typedef PlanePlan<24, 40, 3, 3, 3, 64, 2, 2> PP_24x40_L3_k33;
+typedef PlanePlan<16, 16, 4, 3, 7, 64, 1, 1> PP_16_L4_k37;
+typedef PlanePlan<64, 64, 4, 7, 5, 64, 4, 4> PP_64_L4_k75;
+
+#define WTC_PLANE_ENTRIES(X)                                                                 \
+    X(PP_32_L2_k55), X(PP_56_L3_k55), X(PP_28_L2_k55), X(PP_14_L1_k55), X(PP_128_L1_k55),   \
+        X(PP_128_L2_k55), X(PP_128_L3_k55), X(PP_128_L4_k55), X(PP_128_L5_k55),            \
+        X(PP_32_L3_k75), X(PP_24x40_L3_k33), X(PP_16_L4_k37), X(PP_64_L4_k75)
+
+}  // namespace wtc
