@@ -124,3 +124,24 @@ def test_zero_branch_equals_base_only():
     y0 = wt.wtconv_fwd(x, wb, wl, torch.zeros_like(sc))
     ref = torch.nn.functional.conv2d(x.double().cpu(), wb.double().cpu()[:, None], padding=2, groups=3)
     assert rel_err(to_f64(y0), ref.numpy()) <= 1e-6
+
+
+def test_bf16_store_rounding_is_round_to_nearest_even():
+    """Pin the fp32 -> bf16 narrowing of the stores bit-exactly: with zero
+    scales and a base kernel c * delta, y = c * x is exact in fp32 (8-bit
+    times 8-bit significands), so the store's rounding is the only one.
+    Expected bits: numpy round-to-nearest-even of the exact product."""
+    from wavelet_convolution_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    _say("[parity] bf16 RNE store")
+    inp = make_inputs(2, 3, 56, 56, 3, dtype="bf16", seed=5)
+    x, dy, wb, wl, sc = to_device(inp)
+    c = 1.0 + 2.0 ** -8 + 2.0 ** -7   # many products land exactly on bf16 ties
+    wdelta = torch.zeros_like(wb)
+    wdelta[:, 2, 2] = c
+    y = wt.wtconv_fwd(x, wdelta, wl, torch.zeros_like(sc))
+    torch.cuda.synchronize()
+    exact = bf16_bits_to_f32(inp.x).astype(np.float64) * c
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)   # exact in fp32
+    expect = f32_to_bf16_bits(exact.astype(np.float32))
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, expect)

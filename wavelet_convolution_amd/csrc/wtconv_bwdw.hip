@@ -9,12 +9,14 @@
 // with U_l, V_l the unnormalised level-l bands of x and dy (2^l times the
 // orthonormal ones). Then dw_lvl = scale * G and dscale = sum(w_lvl * G).
 //
-// Stage 1: one workgroup per (channel, chunk of the batch), 4 wavefronts.
-// Each plane of the chunk is streamed into LDS once; both Haar pyramids are
-// built on chip; wavefront s owns band s at every level. Every lane keeps its
-// tap sums in registers across the whole chunk; at the end they are reduced
-// across the wavefront with shuffles, across wavefronts through LDS, and one
-// partial per (chunk, channel, tap) goes to the workspace.
+// Stage 1: one workgroup per (channel, chunk of the batch), 8 wavefronts.
+// Each plane of the chunk is streamed into LDS once (the next plane's loads
+// are issued while the current one's level taps run); both Haar pyramids are
+// built on chip; every wavefront owns one band of some levels (see BwPlan).
+// Every lane keeps its tap sums in registers across the whole chunk; at the
+// end they are reduced across the wavefront with shuffles, across
+// wavefronts through LDS, and one partial per (chunk, channel, tap) goes to
+// the workspace.
 // Stage 2: one workgroup per channel sums the chunks in a fixed order and
 // applies the scale and normalisation. No atomics: results are bitwise
 // reproducible.
@@ -27,8 +29,12 @@ namespace wtc {
 // acc[m*K+n] += sum_{o,q} v[o*SV+q] * u[(o+m)*SU + q+n]: tap sums of an
 // OR x OC tile of dy-side values v against the matching window of the
 // bordered x-side plane u (u points at the window's top-left corner).
-template <int K, int OR, int OC, int SU, int SV>
-__device__ __forceinline__ void taps_tile(const float* u, const float* v, float (&acc)[K * K]) {
+// Scheduling barriers keep each call's tile and window rows live only
+// during the call.
+template <int K, int OR, int OC, int SU, int SV, int NA>
+__device__ __forceinline__ void taps_tile(const float* u, const float* v, float (&acc)[NA]) {
+    static_assert(NA >= K * K, "accumulator slot too small");
+    __builtin_amdgcn_sched_barrier(0);
     float vt[OR][OC];
 #pragma unroll
     for (int o = 0; o < OR; ++o)
@@ -49,6 +55,7 @@ __device__ __forceinline__ void taps_tile(const float* u, const float* v, float 
                 for (int q = 0; q < OC; ++q) acc[m * K + n] = __builtin_fmaf(vt[o][q], win[q + n], acc[m * K + n]);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -60,12 +67,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 // H x W plane, L >= 1 levels; BR x BC dy positions per base work item.
 // LDS: x (border KB/2), dy, the bordered x bands U_1..U_L (border K/2) and
 // the unbordered dy bands V_1..V_L all stay resident.
+//
+// Work split, 8 wavefronts in two groups of four; wavefront w owns band
+// s = w % 4 and keeps its tap sums for the whole chunk in registers:
+//   group A (w < 4): a quarter of the base taps (slot 0), levels 3, 5 (slots 1, 2)
+//   group B (w >= 4): level 1 (slot 0), levels 2, 4 (slots 1, 2)
+// which balances the multiply-adds (level 1 alone equals the base work) and
+// keeps every lane at about two or three slots of taps.
 template <int H_, int W_, int L_, int KB_, int K_, int BR_, int BC_>
 struct BwPlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, BR = BR_, BC = BC_;
-    static constexpr int NT = 256, NW = 4;
+    static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2;
-    static_assert(L >= 1 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
+    static_assert(L >= 1 && L <= 5 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
     static_assert(H % BR == 0 && W % BC == 0, "base tile must divide the plane");
     static constexpr int SX = odd_stride(W + 2 * PB);
     static constexpr int XSIZE = (H + 2 * PB) * SX;
@@ -84,14 +98,28 @@ struct BwPlan {
         return o;
     }
     static constexpr int UTOT = uoff(L + 1), VTOT = voff(L + 1);
-    static constexpr int RED = NW * (KB * KB + L * K * K);   // reduction scratch at the end
+    // role slots: group A = base, 3, 5; group B = 1, 2, 4
+    static constexpr int NSLOT = 1 + (L >= 2 ? 1 : 0) + (L >= 4 ? 1 : 0);
+    static constexpr int SLOT0 = KB * KB > K * K ? KB * KB : K * K;   // base or level-1 taps
+    static constexpr int RED = NW * SLOT0 + NW * (NSLOT - 1) * K * K;   // reduction scratch
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
     static constexpr int NI = (H / BR) * (W / BC);
-    static constexpr int MI = cdiv(NI, NT);
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
     static constexpr Tile band_tile(int l) { return pick_tile(H >> l, W >> l, 64); }
+    static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
+    static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
+    // registers bound the occupancy too: each lane holds its tap slots plus
+    // about 48 registers of tiles and addresses (512 VGPRs per SIMD lane)
+    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 48;
+    static constexpr int WAVES_PER_EU_REG = 512 / (REGS <= 128 ? 128 : (REGS <= 168 ? 168 : 256));
+    static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
+    static constexpr int WAVES_PER_EU = WAVES_PER_EU_MIN < 1 ? 1 : WAVES_PER_EU_MIN;
+
+    // group and slot of level l (1..5)
+    static constexpr int group_of(int l) { return (l == 3 || l == 5) ? 0 : 1; }
+    static constexpr int slot_of(int l) { return l == 1 ? 0 : (l == 2 || l == 3) ? 1 : 2; }
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -104,19 +132,25 @@ struct BwPlan {
 };
 
 template <class P, typename T>
-__global__ __launch_bounds__(256) void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy,
-                                                   float* __restrict__ part, int B, int C, int bpc) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
+void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part, int B,
+                 int C, int bpc) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
-    constexpr int BR = P::BR, BC = P::BC, NI = P::NI, MI = P::MI, TPR = W / BC;
+    constexpr int BR = P::BR, BC = P::BC, NI = P::NI, TPR = W / BC;
+    constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
+    constexpr int V = vec_elems<T>(W, H * W);
+    constexpr int NV = H * W / V;
+    constexpr int NL = cdiv(NV, NT);
 
-    __shared__ float lds[P::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS];
     float* X = lds;
     float* DY = X + P::XSIZE;
     float* U = DY + P::DSIZE;
     float* Vb = U + P::UTOT;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int grp = wave >> 2, band = wave & 3, gtid = tid & 255;
     const int c = blockIdx.x % C, chunk = blockIdx.x / C;
     const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
 
@@ -127,55 +161,53 @@ __global__ __launch_bounds__(256) void bwdw_kernel(const T* __restrict__ x, cons
         zero_border<4, (H >> l), (W >> l), PK, P::su(l)>(U + P::uoff(l), tid, NT);
     });
 
-    float accb[KB * KB];
-    float accl[L][K * K];
+    float acc0[SLOT0];
+    float accl[NSLOT > 1 ? NSLOT - 1 : 1][K * K];
 #pragma unroll
-    for (int t = 0; t < KB * KB; ++t) accb[t] = 0.f;
+    for (int t = 0; t < SLOT0; ++t) acc0[t] = 0.f;
 #pragma unroll
-    for (int l = 0; l < L; ++l)
+    for (int j = 0; j < (NSLOT > 1 ? NSLOT - 1 : 1); ++j)
 #pragma unroll
-        for (int t = 0; t < K * K; ++t) accl[l][t] = 0.f;
+        for (int t = 0; t < K * K; ++t) accl[j][t] = 0.f;
 
-    for (int b = b0; b < b1; ++b) {
+    // raw global loads of the next plane, issued ahead of the level taps
+    float vx[NL][V], vd[NL][V];
+    auto issue_loads = [&](int b) {
         const size_t plane = (size_t)b * C + c;
         const T* __restrict__ xs = x + plane * H * W;
         const T* __restrict__ ds = dy + plane * H * W;
-        // ------------------------------------------------ P0: stream in
-        {
-            constexpr int V = vec_elems<T>(W, H * W);
-            constexpr int NV = H * W / V;
-            constexpr int NL = cdiv(NV, NT);
-            float vx[NL][V], vd[NL][V];
 #pragma unroll
-            for (int k = 0; k < NL; ++k) {
-                const int q = tid + k * NT;
-                if (NV % NT == 0 || q < NV) {
-                    load_vec<T, V>(xs + q * V, vx[k]);
-                    load_vec<T, V>(ds + q * V, vd[k]);
-                }
+        for (int k = 0; k < NL; ++k) {
+            const int q = tid + k * NT;
+            if (NV % NT == 0 || q < NV) {
+                load_vec<T, V>(xs + q * V, vx[k]);
+                load_vec<T, V>(ds + q * V, vd[k]);
             }
+        }
+    };
+    if (b0 < b1) issue_loads(b0);
+
+    for (int b = b0; b < b1; ++b) {
+        // ------------------------------------------------ P0: stream in
 #pragma unroll
-            for (int k = 0; k < NL; ++k) {
-                const int q = tid + k * NT;
-                if (NV % NT == 0 || q < NV) {
-                    const int e = q * V, r = e / W, col = e - r * W;
+        for (int k = 0; k < NL; ++k) {
+            const int q = tid + k * NT;
+            if (NV % NT == 0 || q < NV) {
+                const int e = q * V, r = e / W, col = e - r * W;
 #pragma unroll
-                    for (int i = 0; i < V; ++i) {
-                        X[(r + PB) * SX + col + PB + i] = vx[k][i];
-                        DY[e + i] = vd[k][i];
-                    }
+                for (int i = 0; i < V; ++i) {
+                    X[(r + PB) * SX + col + PB + i] = vx[k][i];
+                    DY[e + i] = vd[k][i];
                 }
             }
         }
         __syncthreads();
         // ------------------------------------- P1: base taps, level 1 bands
-#pragma unroll
-        for (int it = 0; it < MI; ++it) {
-            const int item = tid + it * NT;
-            if (NI % NT == 0 || item < NI) {
+        if (grp == 0) {
+            for (int item = gtid; item < NI; item += 256) {
                 const int ti = item / TPR, tj = item - ti * TPR;
                 const int h0 = BR * ti, w0 = BC * tj;
-                taps_tile<KB, BR, BC, SX, W>(X + h0 * SX + w0, DY + h0 * W + w0, accb);
+                taps_tile<KB, BR, BC, SX, W>(X + h0 * SX + w0, DY + h0 * W + w0, acc0);
             }
         }
         {
@@ -221,58 +253,61 @@ __global__ __launch_bounds__(256) void bwdw_kernel(const T* __restrict__ x, cons
                 __syncthreads();
             }
         });
-        // --------------------------- P3: level taps, wavefront s = band s
+        // the next plane's loads fly while the level taps run; P0 of the
+        // next plane writes only x and dy, which the level taps do not read
+        if (b + 1 < b1) issue_loads(b + 1);
+        // --------------------------- P3: level taps, one band per wavefront
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
             constexpr Tile tl = P::band_tile(l);
             constexpr int RR = tl.r, CC = tl.c, TPRl = wl / CC, NIl = (hl / RR) * TPRl;
-            constexpr int MIl = cdiv(NIl, 64);
-            const float* Us = U + P::uoff(l) + wave * BSl;
-            const float* Vs = Vb + P::voff(l) + wave * VSl;
-#pragma unroll
-            for (int it = 0; it < MIl; ++it) {
-                const int item = lane + it * 64;
-                if (NIl % 64 == 0 || item < NIl) {
+            if (grp == P::group_of(l)) {
+                const float* Us = U + P::uoff(l) + band * BSl;
+                const float* Vs = Vb + P::voff(l) + band * VSl;
+                for (int item = lane; item < NIl; item += 64) {
                     const int ti = item / TPRl, tj = item - ti * TPRl;
-                    taps_tile<K, RR, CC, Sl, wl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * wl + CC * tj,
-                                                 accl[l - 1]);
+                    if constexpr (P::slot_of(l) == 0)
+                        taps_tile<K, RR, CC, Sl, wl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * wl + CC * tj, acc0);
+                    else
+                        taps_tile<K, RR, CC, Sl, wl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * wl + CC * tj,
+                                                     accl[P::slot_of(l) - 1]);
                 }
             }
         });
-        // the next plane's P0 writes only x and dy, which P3 does not read;
-        // its P1 comes after P0's barrier
     }
 
     // ------------------------------------------------------ reduction
 #pragma unroll
-    for (int t = 0; t < KB * KB; ++t) accb[t] = wave_sum(accb[t]);
+    for (int t = 0; t < SLOT0; ++t) acc0[t] = wave_sum(acc0[t]);
 #pragma unroll
-    for (int l = 0; l < L; ++l)
+    for (int j = 0; j < NSLOT - 1; ++j)
 #pragma unroll
-        for (int t = 0; t < K * K; ++t) accl[l][t] = wave_sum(accl[l][t]);
+        for (int t = 0; t < K * K; ++t) accl[j][t] = wave_sum(accl[j][t]);
     __syncthreads();  // all of LDS becomes reduction scratch
-    float* red = lds;
+    float* red0 = lds;                     // [NW][SLOT0]
+    float* redl = lds + P::NW * SLOT0;     // [NW][NSLOT-1][K*K]
     if (lane == 0) {
 #pragma unroll
-        for (int t = 0; t < KB * KB; ++t) red[wave * KB * KB + t] = accb[t];
+        for (int t = 0; t < SLOT0; ++t) red0[wave * SLOT0 + t] = acc0[t];
 #pragma unroll
-        for (int l = 0; l < L; ++l)
+        for (int j = 0; j < NSLOT - 1; ++j)
 #pragma unroll
-            for (int t = 0; t < K * K; ++t) red[P::NW * KB * KB + (wave * L + l) * K * K + t] = accl[l][t];
+            for (int t = 0; t < K * K; ++t) redl[(wave * (NSLOT - 1) + j) * K * K + t] = accl[j][t];
     }
     __syncthreads();
     float* dst = part + ((size_t)chunk * C + c) * P::TAPS;
     for (int t = tid; t < P::TAPS; t += NT) {
         float v;
         if (t < KB * KB) {
-            v = red[t];
+            v = red0[t];   // group A, waves 0..3 in order
 #pragma unroll
-            for (int w = 1; w < P::NW; ++w) v += red[w * KB * KB + t];
+            for (int w = 1; w < 4; ++w) v += red0[w * SLOT0 + t];
         } else {
             const int r = t - KB * KB, ls = r / (K * K), tap = r - ls * (K * K);
-            const int l = ls / 4, s = ls - l * 4;   // taps are ordered [L][4][K*K]
-            v = red[P::NW * KB * KB + (s * L + l) * K * K + tap];
+            const int l = ls / 4 + 1, s = ls - (l - 1) * 4;   // taps are ordered [L][4][K*K]
+            const int w = P::group_of(l) * 4 + s, slot = P::slot_of(l);
+            v = slot == 0 ? red0[w * SLOT0 + tap] : redl[(w * (NSLOT - 1) + slot - 1) * K * K + tap];
         }
         dst[t] = v;
     }
@@ -359,9 +394,10 @@ static const BwEntry* find_bw(int H, int W, int L, int KB, int K) {
     return nullptr;
 }
 
-// batches per chunk: enough workgroups to fill the chip several times over
+// batches per chunk: about three rounds of workgroups over the chip, so the
+// per-chunk reduction is amortised over several planes
 static int chunk_batches(int B, int C) {
-    const int want_chunks = cdiv(2048, C);
+    const int want_chunks = cdiv(1536, C);
     const int nchunk = want_chunks < B ? want_chunks : B;
     return cdiv(B, nchunk < 1 ? 1 : nchunk);
 }

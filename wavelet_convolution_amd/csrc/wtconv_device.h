@@ -1,8 +1,7 @@
 // Device-side helpers shared by the WTConv HIP kernels (gfx950).
 //
 // Activation storage is fp32 or bf16; every product and sum is fp32. bf16 is
-// widened exactly (a 16-bit shift) and narrowed with round-to-nearest-even,
-// written from the IEEE definition.
+// widened exactly (a 16-bit shift) and narrowed with round-to-nearest-even.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,11 +20,17 @@ constexpr int odd_stride(int w) { return (w % 2 == 0) ? w + 1 : w; }
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 converts
+// two values per instruction without branches (NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t narrow_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ bf16_t narrow_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // keep NaN quiet
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+    return (bf16_t)(narrow_bf16x2(f, 0.f) & 0xffffu);
 }
 
 template <typename T> struct Act;
@@ -105,28 +110,36 @@ __device__ __forceinline__ void store_row(bf16_t* __restrict__ p, const float (&
     static_assert(N % 2 == 0, "bf16 rows are stored as pairs");
 #pragma unroll
     for (int i = 0; i < N; i += 2) {
-        uint32_t lo = narrow_bf16(v[i]), hi = narrow_bf16(v[i + 1]);
-        *reinterpret_cast<uint32_t*>(p + i) = lo | (hi << 16);
+        *reinterpret_cast<uint32_t*>(p + i) = narrow_bf16x2(v[i], v[i + 1]);
     }
-}
-
-// Tap (m, n) of a k x k kernel; FLIP turns the kernel by 180 degrees (the
-// transpose of a 'same' cross-correlation with odd k).
-template <int K, bool FLIP>
-__device__ __forceinline__ float tap(const float* __restrict__ w, int m, int n) {
-    return FLIP ? w[(K - 1 - m) * K + (K - 1 - n)] : w[m * K + n];
 }
 
 // acc[o][q] += sum_{m,n} w[m][n] * s[(o+m)*S + q+n]: an OR x OC tile of a
 // 'same' cross-correlation read from a zero-bordered LDS plane (s points at
-// the window's top-left corner, S is the plane's row stride). Window rows are
-// streamed through registers; every loaded value feeds up to K*K FMAs.
-template <int K, int OR, int OC, int S, bool FLIP>
-__device__ __forceinline__ void conv_tile(const float* s, const float* __restrict__ w,
-                                          float (&acc)[OR][OC]) {
-    float wr[K * K];
+// the window's top-left corner, S is the plane's row stride). The K*K taps
+// come from LDS too (every lane reads the same address: a broadcast). Window
+// rows are streamed through registers; every loaded value feeds up to K*K
+// FMAs. The first tap of each output initialises it (no separate zeroing).
+//
+// The taps block starts 16-byte aligned and is padded to a multiple of four
+// floats (kpad4), so it is read with 128-bit broadcasts. Scheduling barriers
+// on both ends keep one call's taps and window rows live only during that
+// call: without them the scheduler hoists the taps of every band of a phase
+// at once, or sinks the FMA chains into the store loop, and spills.
+constexpr int kpad4(int k) { return (k * k + 3) / 4 * 4; }
+
+template <int K, int OR, int OC, int S>
+__device__ __forceinline__ void conv_tile(const float* s, const float* w, float (&acc)[OR][OC]) {
+    __builtin_amdgcn_sched_barrier(0);
+    float wr[kpad4(K)];
 #pragma unroll
-    for (int t = 0; t < K * K; ++t) wr[t] = tap<K, FLIP>(w, t / K, t % K);
+    for (int t = 0; t < kpad4(K); t += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(w + t);
+        wr[t] = q.x;
+        wr[t + 1] = q.y;
+        wr[t + 2] = q.z;
+        wr[t + 3] = q.w;
+    }
 #pragma unroll
     for (int r = 0; r < OR + K - 1; ++r) {
         float win[OC + K - 1];
@@ -139,10 +152,14 @@ __device__ __forceinline__ void conv_tile(const float* s, const float* __restric
 #pragma unroll
             for (int n = 0; n < K; ++n) {
 #pragma unroll
-                for (int q = 0; q < OC; ++q) acc[o][q] = __builtin_fmaf(wr[m * K + n], win[q + n], acc[o][q]);
+                for (int q = 0; q < OC; ++q) {
+                    if (m == 0 && n == 0) acc[o][q] = wr[0] * win[q];
+                    else acc[o][q] = __builtin_fmaf(wr[m * K + n], win[q + n], acc[o][q]);
+                }
             }
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Zero the border cells of NB bordered planes of interior h x w, border B,

@@ -30,7 +30,7 @@
 namespace wtc {
 
 template <class P, typename T, bool FLIP>
-__global__ __launch_bounds__(P::NT) void plane_kernel(const T* __restrict__ in,
+__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU))) void plane_kernel(const T* __restrict__ in,
                                                       const float* __restrict__ w_base,
                                                       const float* __restrict__ w_lvl,
                                                       const float* __restrict__ scale,
@@ -41,18 +41,30 @@ __global__ __launch_bounds__(P::NT) void plane_kernel(const T* __restrict__ in,
     constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
     constexpr int NI = P::NI, MI = P::MI, TPR = W1 / TC;
 
-    __shared__ float lds[P::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
     float* A = lds;               // x (bordered), later U_2..U_L and Z'_2..Z'_L
     float* Bq = lds + P::ASIZE;   // U_1 (4 bordered bands)
+    float* WB = lds + P::LDS_FLOATS;   // base taps (turned for FLIP), padded to KB2P
+    float* WL = WB + P::KB2P;          // level taps x scale x 4^-l, [L][4][K2P]
 
     const int tid = threadIdx.x;
     const int plane = blockIdx.x;
     const int c = plane % C;
     const T* __restrict__ src = in + (size_t)plane * H * W;
     T* __restrict__ dst = out + (size_t)plane * H * W;
-    const float* __restrict__ wb = w_base + (size_t)c * KB * KB;
 
     // ---------------------------------------------------------------- P0
+    // stage the taps: turned by 180 degrees for the transpose, and the level
+    // taps scaled by scale * 4^-l (reformulation (3)); padding taps are zero
+    constexpr int KB2P = P::KB2P, K2P = P::K2P;
+    for (int t = tid; t < KB2P; t += NT)
+        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
+    for (int t = tid; t < 4 * L * K2P; t += NT) {
+        const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
+        const size_t pi = ((size_t)l * C + c) * 4 + s;
+        const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
+        WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
+    }
     zero_border<1, H, W, PB, SX>(A, tid, NT);
     zero_border<4, H1, W1, PK, S1>(Bq, tid, NT);
     {
@@ -91,7 +103,7 @@ __global__ __launch_bounds__(P::NT) void plane_kernel(const T* __restrict__ in,
         if (item < NI) {
             const int ti = item / TPR, tj = item - ti * TPR;
             const int h0 = 2 * TR * ti, w0 = 2 * TC * tj;
-            conv_tile<KB, 2 * TR, 2 * TC, SX, FLIP>(A + h0 * SX + w0, wb, yb[it]);
+            conv_tile<KB, 2 * TR, 2 * TC, SX>(A + h0 * SX + w0, WB, yb[it]);
             const int i0 = TR * ti, j0 = TC * tj;
 #pragma unroll
             for (int r = 0; r < TR; ++r)
@@ -136,7 +148,6 @@ __global__ __launch_bounds__(P::NT) void plane_kernel(const T* __restrict__ in,
         constexpr Tile tl = P::deep_tile(l);
         constexpr int RR = tl.r, CC = tl.c, TPRl = wl / CC, NIl = (hl / RR) * TPRl;
         constexpr int MIl = cdiv(NIl, NT);
-        constexpr float fold = 1.0f / (float)(1 << (2 * l));
         float* Ul = A + P::uoff(l);
         float z[MIl][4][RR][CC];
 #pragma unroll
@@ -149,16 +160,9 @@ __global__ __launch_bounds__(P::NT) void plane_kernel(const T* __restrict__ in,
                 for (int r = 0; r < RR; ++r)
 #pragma unroll
                     for (int q = 0; q < CC; ++q) z[it][s][r][q] = 0.f;
-                if (item < NIl) {
-                    const size_t wo = (((size_t)(l - 1) * C + c) * 4 + s);
-                    conv_tile<K, RR, CC, Sl, FLIP>(Ul + s * BSl + RR * ti * Sl + CC * tj,
-                                                   w_lvl + wo * K * K, z[it][s]);
-                    const float f = scale[wo] * fold;
-#pragma unroll
-                    for (int r = 0; r < RR; ++r)
-#pragma unroll
-                        for (int q = 0; q < CC; ++q) z[it][s][r][q] *= f;
-                }
+                if (item < NIl)
+                    conv_tile<K, RR, CC, Sl>(Ul + s * BSl + RR * ti * Sl + CC * tj,
+                                             WL + ((l - 1) * 4 + s) * K2P, z[it][s]);
             }
         }
         __syncthreads();
@@ -193,13 +197,7 @@ __global__ __launch_bounds__(P::NT) void plane_kernel(const T* __restrict__ in,
             for (int r = 0; r < TR; ++r)
 #pragma unroll
                 for (int q = 0; q < TC; ++q) z1[s][r][q] = 0.f;
-            const size_t wo = ((size_t)c * 4 + s);
-            conv_tile<K, TR, TC, S1, FLIP>(Bq + s * BS1 + i0 * S1 + j0, w_lvl + wo * K * K, z1[s]);
-            const float f = scale[wo] * 0.25f;
-#pragma unroll
-            for (int r = 0; r < TR; ++r)
-#pragma unroll
-                for (int q = 0; q < TC; ++q) z1[s][r][q] *= f;
+            conv_tile<K, TR, TC, S1>(Bq + s * BS1 + i0 * S1 + j0, WL + s * K2P, z1[s]);
         }
 #pragma unroll
         for (int r = 0; r < TR; ++r) {
@@ -245,7 +243,7 @@ static hipError_t launch_plane(const void* in, const float* wb, const float* wl,
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \
      {{launch_plane<PLAN, float, false>, launch_plane<PLAN, float, true>},                   \
       {launch_plane<PLAN, bf16_t, false>, launch_plane<PLAN, bf16_t, true>}},                \
-     PLAN::LDS_FLOATS * 4, PLAN::NT}
+     (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT}
 
 static const PlaneEntry kPlaneEntries[] = {
     WTC_PLANE_ENTRIES(WTC_PLANE_ENTRY)

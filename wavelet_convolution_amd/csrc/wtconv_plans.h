@@ -64,12 +64,22 @@ struct PlanePlan {
     static constexpr int UDEEP = uoff(L + 1);
     static constexpr int ASIZE = XSIZE > UDEEP ? XSIZE : UDEEP;
     static constexpr int BSIZE = 4 * bandsz(1);
-    static constexpr int LDS_FLOATS = ASIZE + BSIZE;
-    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
+    static constexpr int LDS_FLOATS = (ASIZE + BSIZE + 3) / 4 * 4;   // taps start 16-byte aligned
+    static constexpr int KB2P = kpad4(KB), K2P = kpad4(K);
+    static constexpr int WFLOATS = KB2P + 4 * L * K2P;   // staged taps
+    static_assert((LDS_FLOATS + WFLOATS) * 4 <= 160 * 1024, "plane does not fit in LDS");
     static constexpr int NI = ((H / 2) / TR) * ((W / 2) / TC);
     static constexpr int MI = cdiv(NI, NT);
 
     static constexpr Tile deep_tile(int l) { return pick_tile(H >> l, W >> l, NT); }
+
+    // occupancy the LDS footprint allows (waves per SIMD, at most 8): the
+    // register allocator is held to it so that registers never become the
+    // tighter limit
+    static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
+    static constexpr int WAVES_PER_EU_LDS = (WG_PER_CU * (NT / 64)) / 4;
+    static constexpr int WAVES_PER_EU =
+        WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > 8 ? 8 : WAVES_PER_EU_LDS);
 
     // f(std::integral_constant<int, l>) for l = 2..L, unrolled at compile time
     template <class F>
@@ -99,19 +109,27 @@ const PlaneEntry* find_plane_entry(int H, int W, int L, int KB, int K);
 // ConvNeXt-stage and sweep shapes first, then small shapes that exercise
 // other kernel sizes, odd tile counts and non-square planes.
 typedef PlanePlan<32, 32, 2, 5, 5, 64, 2, 2> PP_32_L2_k55;
-typedef PlanePlan<56, 56, 3, 5, 5, 64, 2, 7> PP_56_L3_k55;
+#ifndef WTC_PLAN_56
+#define WTC_PLAN_56 256, 1, 4
+#endif
+#ifndef WTC_PLAN_128
+#define WTC_PLAN_128 1024, 2, 2
+#endif
+typedef PlanePlan<56, 56, 3, 5, 5, WTC_PLAN_56> PP_56_L3_k55;
 typedef PlanePlan<28, 28, 2, 5, 5, 64, 2, 2> PP_28_L2_k55;
 typedef PlanePlan<14, 14, 1, 5, 5, 64, 1, 1> PP_14_L1_k55;
-typedef PlanePlan<128, 128, 1, 5, 5, 256, 4, 4> PP_128_L1_k55;
-typedef PlanePlan<128, 128, 2, 5, 5, 256, 4, 4> PP_128_L2_k55;
-typedef PlanePlan<128, 128, 3, 5, 5, 256, 4, 4> PP_128_L3_k55;
-typedef PlanePlan<128, 128, 4, 5, 5, 256, 4, 4> PP_128_L4_k55;
-typedef PlanePlan<128, 128, 5, 5, 5, 256, 4, 4> PP_128_L5_k55;
+typedef PlanePlan<128, 128, 1, 5, 5, WTC_PLAN_128> PP_128_L1_k55;
+typedef PlanePlan<128, 128, 2, 5, 5, WTC_PLAN_128> PP_128_L2_k55;
+typedef PlanePlan<128, 128, 3, 5, 5, WTC_PLAN_128> PP_128_L3_k55;
+typedef PlanePlan<128, 128, 4, 5, 5, WTC_PLAN_128> PP_128_L4_k55;
+typedef PlanePlan<128, 128, 5, 5, 5, WTC_PLAN_128> PP_128_L5_k55;
 typedef PlanePlan<32, 32, 3, 7, 5, 64, 2, 2> PP_32_L3_k75;
 typedef PlanePlan<24, 40, 3, 3, 3, 64, 2, 2> PP_24x40_L3_k33;
 typedef PlanePlan<16, 16, 4, 3, 7, 64, 1, 1> PP_16_L4_k37;
 typedef PlanePlan<64, 64, 4, 7, 5, 64, 4, 4> PP_64_L4_k75;
 
+// NT, TR, TC of the ConvNeXt stage-1 and 128x128 plans can be set at build
+// time (-DWTC_PLAN_56=...) for tuning sweeps.
 #define WTC_PLANE_ENTRIES(X)                                                                 \
     X(PP_32_L2_k55), X(PP_56_L3_k55), X(PP_28_L2_k55), X(PP_14_L1_k55), X(PP_128_L1_k55),   \
         X(PP_128_L2_k55), X(PP_128_L3_k55), X(PP_128_L4_k55), X(PP_128_L5_k55),            \
