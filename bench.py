@@ -27,7 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "WTConv fwd+bwd images/sec and achieved HBM TB/s (% of MI355X peak)"
-KERNEL_SOURCES = ("wtconv_device.h", "wtconv_plans.h", "wtconv_fused.hip", "wtconv_bwdw.hip")
+KERNEL_SOURCES = ("wtconv_device.h", "wtconv_plans.h", "wtconv_plane.h", "wtconv_fused.hip", "wtconv_tiled.hip",
+                  "wtconv_bwdw.hip")
 
 
 def kernel_source_hash() -> str:
@@ -141,17 +142,19 @@ def main() -> int:
     dx = torch.empty_like(sets[0][0])
     grads = (torch.empty((cfg.C, cfg.kb, cfg.kb), device=dev), torch.empty(tuple(wl.shape), device=dev),
              torch.empty(tuple(sc.shape), device=dev))
-    ws_bytes = wt.wtconv_workspace_size(sets[0][0], cfg.L, cfg.kb, cfg.k, wt.OP_BWD_WEIGHT)
+    # one workspace for every call of a step, allocated before timing
+    ws_bytes = max(wt.wtconv_workspace_size(sets[0][0], cfg.L, cfg.kb, cfg.k, op)
+                   for op in (wt.OP_FWD, wt.OP_BWD_DATA, wt.OP_BWD_WEIGHT))
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
 
     def step(i, ev=None):
         x, dy = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        wt.wtconv_fwd(x, wb, wl, sc, y=y)
+        wt.wtconv_fwd(x, wb, wl, sc, y=y, ws=ws)
         if ev is not None:
             ev[1].record()
-        wt.wtconv_bwd_data(dy, wb, wl, sc, dx=dx)
+        wt.wtconv_bwd_data(dy, wb, wl, sc, dx=dx, ws=ws)
         if ev is not None:
             ev[2].record()
         wt.wtconv_bwd_weight(x, dy, cfg.kb, wl, sc, out=grads, ws=ws)

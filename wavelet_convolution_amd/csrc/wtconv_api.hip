@@ -10,6 +10,7 @@
 #include "wtconv_plans.h"
 #include "wtconv_bwdw.h"
 #include "wtconv_naive.h"
+#include "wtconv_tiled.h"
 
 namespace {
 
@@ -61,12 +62,19 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     if (overlap(in, act_bytes(d), out, act_bytes(d))) return WTCONV_ERR_INVALID_ARG;
     st = check_params(d, w_base, w_lvl, scale, true);
     if (st != WTCONV_OK) return st;
-    const wtc::PlaneEntry* e = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level);
-    if (!e) return WTCONV_ERR_UNSUPPORTED_SHAPE;
-    (void)ws;
-    (void)ws_bytes;
-    hipError_t err = e->fn[d->dtype == WTCONV_BF16 ? 1 : 0][flip ? 1 : 0](
-        in, w_base, w_lvl, scale, out, d->B, d->C, (hipStream_t)stream);
+    const int dt = d->dtype == WTCONV_BF16 ? 1 : 0;
+    hipError_t err;
+    if (const wtc::PlaneEntry* e = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) {
+        // the whole plane fits one workgroup: one kernel, no workspace
+        err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, d->B, d->C, (hipStream_t)stream);
+    } else if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) {
+        // coarse pass on the LL band at level L0, then the fine tiles
+        const size_t need = e->ws_bytes(d->B, d->C);
+        if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+        err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, (float*)ws, d->B, d->C, (hipStream_t)stream);
+    } else {
+        return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    }
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
@@ -79,7 +87,10 @@ size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
     switch (op) {
     case WTCONV_OP_FWD:
     case WTCONV_OP_BWD_DATA:
-        return wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level) ? 0 : (size_t)-1;
+        if (wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) return 0;
+        if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))
+            return e->ws_bytes(d->B, d->C);
+        return (size_t)-1;
     case WTCONV_OP_BWD_WEIGHT:
         return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
     default:

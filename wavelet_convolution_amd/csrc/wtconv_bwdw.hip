@@ -55,6 +55,7 @@ __device__ __forceinline__ void taps_tile(const float* u, const float* v, float 
                 for (int q = 0; q < OC; ++q) acc[m * K + n] = __builtin_fmaf(vt[o][q], win[q + n], acc[m * K + n]);
         }
     }
+    pin_regs(acc);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -111,8 +112,8 @@ struct BwPlan {
     static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
     static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
     // registers bound the occupancy too: each lane holds its tap slots plus
-    // about 48 registers of tiles and addresses (512 VGPRs per SIMD lane)
-    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 48;
+    // about 64 registers of tiles and addresses (512 VGPRs per SIMD lane)
+    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 64;
     static constexpr int WAVES_PER_EU_REG = 512 / (REGS <= 128 ? 128 : (REGS <= 168 ? 168 : 256));
     static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
     static constexpr int WAVES_PER_EU = WAVES_PER_EU_MIN < 1 ? 1 : WAVES_PER_EU_MIN;
@@ -131,7 +132,11 @@ struct BwPlan {
     }
 };
 
-template <class P, typename T>
+// BASE = false is the coarse pass of the split path: x and dy are the fp32
+// planes P_x, P_dy of unnormalised level-L0 LL sums written by the fine pass,
+// the kernel's levels are L0+1.. of the layer, and only level taps are
+// produced (ordered [L][4][K*K], relative levels).
+template <class P, typename T, bool BASE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
 void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part, int B,
                  int C, int bpc) {
@@ -203,7 +208,7 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
         }
         __syncthreads();
         // ------------------------------------- P1: base taps, level 1 bands
-        if (grp == 0) {
+        if (BASE && grp == 0) {
             for (int item = gtid; item < NI; item += 256) {
                 const int ti = item / TPR, tj = item - ti * TPR;
                 const int h0 = BR * ti, w0 = BC * tj;
@@ -296,15 +301,17 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             for (int t = 0; t < K * K; ++t) redl[(wave * (NSLOT - 1) + j) * K * K + t] = accl[j][t];
     }
     __syncthreads();
-    float* dst = part + ((size_t)chunk * C + c) * P::TAPS;
-    for (int t = tid; t < P::TAPS; t += NT) {
+    constexpr int NB = BASE ? KB * KB : 0;   // base taps written by this kernel
+    constexpr int TOUT = NB + 4 * L * K * K;
+    float* dst = part + ((size_t)chunk * C + c) * TOUT;
+    for (int t = tid; t < TOUT; t += NT) {
         float v;
-        if (t < KB * KB) {
+        if (t < NB) {
             v = red0[t];   // group A, waves 0..3 in order
 #pragma unroll
             for (int w = 1; w < 4; ++w) v += red0[w * SLOT0 + t];
         } else {
-            const int r = t - KB * KB, ls = r / (K * K), tap = r - ls * (K * K);
+            const int r = t - NB, ls = r / (K * K), tap = r - ls * (K * K);
             const int l = ls / 4 + 1, s = ls - (l - 1) * 4;   // taps are ordered [L][4][K*K]
             const int w = P::group_of(l) * 4 + s, slot = P::slot_of(l);
             v = slot == 0 ? red0[w * SLOT0 + tap] : redl[(w * (NSLOT - 1) + slot - 1) * K * K + tap];
@@ -313,8 +320,11 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     }
 }
 
-// Stage 2: fixed-order sum over chunks, then scale and normalisation.
-__global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ part, int nchunk, int C,
+// Stage 2: fixed-order sum over chunks, then scale and normalisation. Taps
+// [0, TA) (base, levels 1..LA) come from partA, the rest (levels LA+1..L)
+// from partB when the plane was split.
+__global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ partA, int nA, int LA,
+                                                     const float* __restrict__ partB, int nB, int C,
                                                      int L, int KB, int K,
                                                      const float* __restrict__ w_lvl,
                                                      const float* __restrict__ scale,
@@ -324,9 +334,13 @@ __global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ p
     __shared__ float G[49 + 4 * 5 * 49];
     const int c = blockIdx.x, tid = threadIdx.x;
     const int kb2 = KB * KB, k2 = K * K, taps = kb2 + 4 * L * k2;
+    const int TA = kb2 + 4 * LA * k2, TB = taps - TA;
     for (int t = tid; t < taps; t += blockDim.x) {
         float a = 0.f;
-        for (int ch = 0; ch < nchunk; ++ch) a += part[((size_t)ch * C + c) * taps + t];
+        if (t < TA)
+            for (int ch = 0; ch < nA; ++ch) a += partA[((size_t)ch * C + c) * TA + t];
+        else
+            for (int ch = 0; ch < nB; ++ch) a += partB[((size_t)ch * C + c) * TB + (t - TA)];
         if (t >= kb2) {
             const int l = (t - kb2) / (4 * k2);   // 0-based level
             a *= 1.0f / (float)(1 << (2 * (l + 1)));
@@ -352,22 +366,394 @@ __global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ p
     }
 }
 
-// ------------------------------------------------------------ registry
+// ---------------------------------------------------- split fine pass
 
-typedef hipError_t (*bwdw_fn)(const void*, const void*, float*, int, int, int, hipStream_t);
+// Fine pass of the backward weight for planes too large for one workgroup:
+// full-width tiles of TH rows of dy, the rows of x they reach plus a halo of
+// G rows (as in the forward fine pass), base taps and the taps of levels
+// 1..L0, and the tile's unnormalised level-L0 LL sums of x and dy, which the
+// coarse pass (bwdw_kernel with BASE = false) correlates for levels L0+1..L.
+// One workgroup per (channel, chunk of (b, tile) units); the units of a chunk
+// follow each other down the plane, so the halo rows of consecutive tiles
+// are read from L2.
+template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int BR_, int BC_>
+struct TileBwPlan {
+    static constexpr int H = H_, W = W_, L0 = L0_, LT = LT_, KB = KB_, K = K_, TH = TH_, BR = BR_, BC = BC_;
+    static constexpr int L = L0;   // levels handled here (role helpers below)
+    static constexpr int NT = 512, NW = 8;
+    static constexpr int PB = KB / 2, PK = K / 2, BLK = 1 << L0;
+    static_assert(L0 >= 1 && L0 <= 5 && L0 <= LT, "fine levels 1..L0");
+    static_assert(H % (1 << LT) == 0 && W % (1 << LT) == 0, "plane must divide into 2^L blocks");
+    static_assert(TH % BLK == 0 && H % TH == 0 && TH % BR == 0 && W % BC == 0, "tile shapes");
+    static constexpr int G0 = PB > (PK << L0) ? PB : (PK << L0);
+    static constexpr int G = cdiv(G0, BLK) * BLK;
+    static constexpr int RH0 = TH + 2 * G;
+    static constexpr int SX = odd_stride(W + 2 * PB);
+    static constexpr int XSIZE = RH0 * SX;
+    static constexpr int DSIZE = TH * W;
+    static constexpr int rh(int l) { return RH0 >> l; }
+    static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
+    static constexpr int bandsz(int l) { return rh(l) * su(l); }
+    static constexpr int vsz(int l) { return (TH >> l) * (W >> l); }
+    static constexpr int uoff(int l) {
+        int o = 0;
+        for (int q = 1; q < l; ++q) o += 4 * bandsz(q);
+        return o;
+    }
+    static constexpr int voff(int l) {
+        int o = 0;
+        for (int q = 1; q < l; ++q) o += 4 * vsz(q);
+        return o;
+    }
+    static constexpr int UTOT = uoff(L0 + 1), VTOT = voff(L0 + 1);
+    static constexpr int NSLOT = 1 + (L0 >= 2 ? 1 : 0) + (L0 >= 4 ? 1 : 0);
+    static constexpr int SLOT0 = KB * KB > K * K ? KB * KB : K * K;
+    static constexpr int RED = NW * SLOT0 + NW * (NSLOT - 1) * K * K;
+    static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
+    static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
+    static_assert(LDS_FLOATS * 4 <= 160 * 1024, "tile does not fit in LDS");
+    static constexpr int NI = (TH / BR) * (W / BC);
+    static constexpr int NTILE = H / TH;
+    static constexpr int TAPS = KB * KB + 4 * L0 * K * K;
+    static constexpr Tile band_tile(int l) { return pick_tile(TH >> l, W >> l, 64); }
+    static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
+    static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
+    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 64;
+    static constexpr int WAVES_PER_EU_REG = 512 / (REGS <= 128 ? 128 : (REGS <= 168 ? 168 : 256));
+    static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
+    static constexpr int WAVES_PER_EU = WAVES_PER_EU_MIN < 1 ? 1 : WAVES_PER_EU_MIN;
+    static constexpr int group_of(int l) { return (l == 3 || l == 5) ? 0 : 1; }
+    static constexpr int slot_of(int l) { return l == 1 ? 0 : (l == 2 || l == 3) ? 1 : 2; }
+
+    template <class F>
+    __device__ static __forceinline__ void for_levels(F&& f) {
+        lv_impl(f, std::make_integer_sequence<int, L0>{});
+    }
+    template <class F, int... I>
+    __device__ static __forceinline__ void lv_impl(F& f, std::integer_sequence<int, I...>) {
+        (f(std::integral_constant<int, I + 1>{}), ...);
+    }
+};
 
 template <class P, typename T>
-static hipError_t launch_bwdw(const void* x, const void* dy, float* part, int B, int C, int bpc,
-                              hipStream_t stream) {
-    const int nchunk = cdiv(B, bpc);
-    hipLaunchKernelGGL((bwdw_kernel<P, T>), dim3((unsigned)(nchunk * C)), dim3(P::NT), 0, stream,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
+void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part,
+                      float* __restrict__ px, float* __restrict__ pdy, int B, int C, int upc) {
+    constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH;
+    constexpr int PB = P::PB, PK = P::PK, SX = P::SX, G = P::G, RH0 = P::RH0, W1 = W / 2;
+    constexpr int BR = P::BR, BC = P::BC, NI = P::NI, TPR = W / BC;
+    constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
+    constexpr int V = vec_elems<T>(W, H * W);
+    constexpr int NVX = RH0 * W / V, NVD = TH * W / V;
+    constexpr int NLX = cdiv(NVX, NT), NLD = cdiv(NVD, NT);
+
+    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS];
+    float* X = lds;
+    float* DY = X + P::XSIZE;
+    float* U = DY + P::DSIZE;
+    float* Vb = U + P::UTOT;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int grp = wave >> 2, band = wave & 3, gtid = tid & 255;
+    const int c = blockIdx.x % C, chunk = blockIdx.x / C;
+    const int nunits = B * P::NTILE;
+    const int u0 = chunk * upc, u1 = min(nunits, u0 + upc);
+
+    // border columns stay zero: loads and analyses write interior columns only
+    for (int i = tid; i < RH0 * (SX - W); i += NT) {
+        const int r = i / (SX - W), q = i - r * (SX - W);
+        X[r * SX + (q < PB ? q : q + W)] = 0.f;
+    }
+    P::for_levels([&](auto lc) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
+        float* Ul = U + P::uoff(l);
+        for (int i = tid; i < 4 * rl * (Sl - wl); i += NT) {
+            const int b = i / (rl * (Sl - wl)), j = i - b * (rl * (Sl - wl));
+            const int r = j / (Sl - wl), q = j - r * (Sl - wl);
+            Ul[b * BSl + r * Sl + (q < PK ? q : q + wl)] = 0.f;
+        }
+    });
+
+    float acc0[SLOT0];
+    float accl[NSLOT > 1 ? NSLOT - 1 : 1][K * K];
+#pragma unroll
+    for (int t = 0; t < SLOT0; ++t) acc0[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < (NSLOT > 1 ? NSLOT - 1 : 1); ++j)
+#pragma unroll
+        for (int t = 0; t < K * K; ++t) accl[j][t] = 0.f;
+
+    float vx[NLX][V], vd[NLD][V];
+    auto issue_loads = [&](int u) {
+        const int b = u / P::NTILE, r0 = (u - b * P::NTILE) * TH;
+        const size_t plane = (size_t)b * C + c;
+        const T* __restrict__ xs = x + plane * H * W;
+        const T* __restrict__ ds = dy + plane * H * W;
+#pragma unroll
+        for (int k = 0; k < NLX; ++k) {
+            const int q = tid + k * NT;
+            const int e = q * V, rr = e / W, pr = r0 - G + rr;
+            if ((NVX % NT == 0 || q < NVX) && pr >= 0 && pr < H)
+                load_vec<T, V>(xs + (size_t)pr * W + (e - rr * W), vx[k]);
+            else
+#pragma unroll
+                for (int i = 0; i < V; ++i) vx[k][i] = 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const int q = tid + k * NT;
+            if (NVD % NT == 0 || q < NVD) load_vec<T, V>(ds + (size_t)r0 * W + q * V, vd[k]);
+        }
+    };
+    if (u0 < u1) issue_loads(u0);
+
+    for (int u = u0; u < u1; ++u) {
+        const int b = u / P::NTILE, r0 = (u - b * P::NTILE) * TH;
+        const size_t plane = (size_t)b * C + c;
+        // ------------------------------------------------ P0: stream in
+#pragma unroll
+        for (int k = 0; k < NLX; ++k) {
+            const int q = tid + k * NT;
+            if (NVX % NT == 0 || q < NVX) {
+                const int e = q * V, rr = e / W, col = e - rr * W;
+#pragma unroll
+                for (int i = 0; i < V; ++i) X[rr * SX + col + PB + i] = vx[k][i];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const int q = tid + k * NT;
+            if (NVD % NT == 0 || q < NVD)
+#pragma unroll
+                for (int i = 0; i < V; ++i) DY[q * V + i] = vd[k][i];
+        }
+        __syncthreads();
+        // ------------------------------------- P1: base taps, level 1 bands
+        if (grp == 0) {
+            for (int item = gtid; item < NI; item += 256) {
+                const int ti = item / TPR, tj = item - ti * TPR;
+                const int h0 = BR * ti, w0 = BC * tj;
+                taps_tile<KB, BR, BC, SX, W>(X + (G + h0 - PB) * SX + w0, DY + h0 * W + w0, acc0);
+            }
+        }
+        {
+            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1);
+            for (int q = tid; q < P::rh(1) * W1; q += NT) {
+                const int i = q / W1, j = q - i * W1;
+                const float* x2 = X + (2 * i) * SX + PB + 2 * j;
+                float uu[4];
+                haar4(x2[0], x2[1], x2[SX], x2[SX + 1], uu[0], uu[1], uu[2], uu[3]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) U[s * BS1 + i * S1 + PK + j] = uu[s];
+            }
+            for (int q = tid; q < (TH / 2) * W1; q += NT) {
+                const int i = q / W1, j = q - i * W1;
+                const float* d2 = DY + 2 * i * W + 2 * j;
+                float vv[4];
+                haar4(d2[0], d2[1], d2[W], d2[W + 1], vv[0], vv[1], vv[2], vv[3]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Vb[s * VS1 + q] = vv[s];
+            }
+        }
+        __syncthreads();
+        // ----------------------------------------- P2: levels 2..L0 analysis
+        P::for_levels([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            if constexpr (l >= 2) {
+                constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
+                constexpr int Sp = P::su(l - 1), wp = W >> (l - 1);
+                const float* LLu = U + P::uoff(l - 1) + PK;
+                const float* LLv = Vb + P::voff(l - 1);
+                float* Ul = U + P::uoff(l);
+                float* Vl = Vb + P::voff(l);
+                for (int q = tid; q < rl * wl; q += NT) {
+                    const int i = q / wl, j = q - i * wl;
+                    const float* x2 = LLu + 2 * i * Sp + 2 * j;
+                    float uu[4];
+                    haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], uu[0], uu[1], uu[2], uu[3]);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) Ul[s * BSl + i * Sl + PK + j] = uu[s];
+                }
+                for (int q = tid; q < (TH >> l) * wl; q += NT) {
+                    const int i = q / wl, j = q - i * wl;
+                    const float* d2 = LLv + 2 * i * wp + 2 * j;
+                    float vv[4];
+                    haar4(d2[0], d2[1], d2[wp], d2[wp + 1], vv[0], vv[1], vv[2], vv[3]);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) Vl[s * VSl + q] = vv[s];
+                }
+                __syncthreads();
+            }
+        });
+        // the coarse pass's inputs: the tile's level-L0 LL sums of x and dy
+        if (P::LT > L0) {
+            constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GL = G >> L0;
+            const float* LLu = U + P::uoff(L0) + PK;
+            const float* LLv = Vb + P::voff(L0);
+            float* pxo = px + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            float* pdo = pdy + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            for (int q = tid; q < hl * wl; q += NT) {
+                const int i = q / wl, j = q - i * wl;
+                pxo[q] = LLu[(GL + i) * Sl + j];
+                pdo[q] = LLv[q];
+            }
+        }
+        if (u + 1 < u1) issue_loads(u + 1);
+        // --------------------------- P3: level taps, one band per wavefront
+        P::for_levels([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
+            constexpr int Gl = G >> l;
+            constexpr Tile tl = P::band_tile(l);
+            constexpr int RR = tl.r, CC = tl.c, TPRl = wl / CC, NIl = (hl / RR) * TPRl;
+            if (grp == P::group_of(l)) {
+                const float* Us = U + P::uoff(l) + band * BSl;
+                const float* Vs = Vb + P::voff(l) + band * VSl;
+                for (int item = lane; item < NIl; item += 64) {
+                    const int ti = item / TPRl, tj = item - ti * TPRl;
+                    if constexpr (P::slot_of(l) == 0)
+                        taps_tile<K, RR, CC, Sl, wl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
+                                                     Vs + RR * ti * wl + CC * tj, acc0);
+                    else
+                        taps_tile<K, RR, CC, Sl, wl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
+                                                     Vs + RR * ti * wl + CC * tj, accl[P::slot_of(l) - 1]);
+                }
+            }
+        });
+        // the next unit's P0 overwrites x, dy, U and V: wait for every reader
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int t = 0; t < SLOT0; ++t) acc0[t] = wave_sum(acc0[t]);
+#pragma unroll
+    for (int j = 0; j < NSLOT - 1; ++j)
+#pragma unroll
+        for (int t = 0; t < K * K; ++t) accl[j][t] = wave_sum(accl[j][t]);
+    __syncthreads();
+    float* red0 = lds;
+    float* redl = lds + P::NW * SLOT0;
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < SLOT0; ++t) red0[wave * SLOT0 + t] = acc0[t];
+#pragma unroll
+        for (int j = 0; j < NSLOT - 1; ++j)
+#pragma unroll
+            for (int t = 0; t < K * K; ++t) redl[(wave * (NSLOT - 1) + j) * K * K + t] = accl[j][t];
+    }
+    __syncthreads();
+    float* dst = part + ((size_t)chunk * C + c) * P::TAPS;
+    for (int t = tid; t < P::TAPS; t += NT) {
+        float v;
+        if (t < KB * KB) {
+            v = red0[t];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) v += red0[w * SLOT0 + t];
+        } else {
+            const int r = t - KB * KB, ls = r / (K * K), tap = r - ls * (K * K);
+            const int l = ls / 4 + 1, s = ls - (l - 1) * 4;
+            const int w = P::group_of(l) * 4 + s, slot = P::slot_of(l);
+            v = slot == 0 ? red0[w * SLOT0 + tap] : redl[(w * (NSLOT - 1) + slot - 1) * K * K + tap];
+        }
+        dst[t] = v;
+    }
+}
+
+// ------------------------------------------------------------ registry
+
+// batches (or tile units) per chunk: about three rounds of workgroups over
+// the chip, so the per-chunk reduction is amortised over several planes
+static int chunk_units(int units, int C) {
+    const int want_chunks = cdiv(1536, C);
+    const int nchunk = want_chunks < units ? want_chunks : units;
+    return cdiv(units, nchunk < 1 ? 1 : nchunk);
+}
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// whole planes: one kernel and the finalize
+template <class P>
+static size_t whole_ws(int B, int C) {
+    const int nchunk = cdiv(B, chunk_units(B, C));
+    return (size_t)nchunk * C * P::TAPS * sizeof(float);
+}
+
+template <class P, typename T>
+static hipError_t whole_launch(const void* x, const void* dy, const float* w_lvl, const float* scale,
+                               float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
+                               hipStream_t stream) {
+    const int bpc = chunk_units(B, C), nchunk = cdiv(B, bpc);
+    float* part = (float*)ws;
+    hipLaunchKernelGGL((bwdw_kernel<P, T, true>), dim3((unsigned)(nchunk * C)), dim3(P::NT), 0, stream,
                        (const T*)x, (const T*)dy, part, B, C, bpc);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(256), 0, stream, (const float*)part, nchunk,
+                       P::L, (const float*)nullptr, 0, C, P::L, P::KB, P::K, w_lvl, scale, dw_base, dw_lvl,
+                       dscale);
     return hipGetLastError();
 }
+
+// split planes: the fine tiles (base and levels 1..L0, plus the LL sums),
+// the coarse pass on the LL sums (levels L0+1..L), then the finalize
+template <class FP, class CP>
+static size_t split_bw_ws(int B, int C) {
+    const int units = B * FP::NTILE;
+    const int nA = cdiv(units, chunk_units(units, C));
+    size_t n = align256((size_t)nA * C * FP::TAPS * sizeof(float));
+    if (FP::LT > FP::L0) {
+        const int nB = cdiv(B, chunk_units(B, C));
+        n += align256((size_t)nB * C * 4 * (FP::LT - FP::L0) * FP::K * FP::K * sizeof(float));
+        n += 2 * align256((size_t)B * C * (FP::H >> FP::L0) * (FP::W >> FP::L0) * sizeof(float));
+    }
+    return n;
+}
+
+template <class FP, class CP, typename T>
+static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_lvl, const float* scale,
+                                  float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
+                                  hipStream_t stream) {
+    const int units = B * FP::NTILE;
+    const int upc = chunk_units(units, C), nA = cdiv(units, upc);
+    char* cur = (char*)ws;
+    float* partA = (float*)cur;
+    cur += align256((size_t)nA * C * FP::TAPS * sizeof(float));
+    float *partB = nullptr, *px = nullptr, *pdy = nullptr;
+    int nB = 0;
+    if constexpr (FP::LT > FP::L0) {
+        nB = cdiv(B, chunk_units(B, C));
+        partB = (float*)cur;
+        cur += align256((size_t)nB * C * 4 * (FP::LT - FP::L0) * FP::K * FP::K * sizeof(float));
+        const size_t pl = (size_t)B * C * (FP::H >> FP::L0) * (FP::W >> FP::L0) * sizeof(float);
+        px = (float*)cur;
+        cur += align256(pl);
+        pdy = (float*)cur;
+    }
+    hipLaunchKernelGGL((tile_bwdw_kernel<FP, T>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
+                       (const T*)x, (const T*)dy, partA, px, pdy, B, C, upc);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if constexpr (FP::LT > FP::L0) {
+        const int bpc = chunk_units(B, C);
+        hipLaunchKernelGGL((bwdw_kernel<CP, float, false>), dim3((unsigned)(nB * C)), dim3(CP::NT), 0, stream,
+                           (const float*)px, (const float*)pdy, partB, B, C, bpc);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(256), 0, stream, (const float*)partA, nA, FP::L0,
+                       (const float*)partB, nB, C, FP::LT, FP::KB, FP::K, w_lvl, scale, dw_base, dw_lvl,
+                       dscale);
+    return hipGetLastError();
+}
+
+typedef hipError_t (*bwdw_fn)(const void*, const void*, const float*, const float*, float*, float*, float*,
+                              void*, int, int, hipStream_t);
 
 struct BwEntry {
     int H, W, L, KB, K;
     bwdw_fn fn[2];
+    size_t (*ws)(int B, int C);
 };
 
 typedef BwPlan<32, 32, 2, 5, 5, 2, 2> BP_32_L2_k55;
@@ -379,13 +765,36 @@ typedef BwPlan<24, 40, 3, 3, 3, 2, 2> BP_24x40_L3_k33;
 typedef BwPlan<16, 16, 4, 3, 7, 1, 1> BP_16_L4_k37;
 typedef BwPlan<64, 64, 4, 7, 5, 4, 4> BP_64_L4_k75;
 
-#define WTC_BW_ENTRY(PLAN) \
-    { PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K, {launch_bwdw<PLAN, float>, launch_bwdw<PLAN, bf16_t>} }
+// split plans: fine tiles + coarse planes of LL_{L0} sums (no base taps)
+typedef TileBwPlan<128, 128, 1, 1, 5, 5, 16, 2, 4> TB_128_L1_k55;
+typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16, 2, 4> TB_128_L2_k55;
+typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16, 2, 4> TB_128_L2of3_k55;
+typedef TileBwPlan<128, 128, 2, 4, 5, 5, 16, 2, 4> TB_128_L2of4_k55;
+typedef TileBwPlan<128, 128, 2, 5, 5, 5, 16, 2, 4> TB_128_L2of5_k55;
+typedef BwPlan<32, 32, 1, 1, 5, 1, 1> CB_32_L1_k5;
+typedef BwPlan<32, 32, 2, 1, 5, 1, 1> CB_32_L2_k5;
+typedef BwPlan<32, 32, 3, 1, 5, 1, 1> CB_32_L3_k5;
+typedef TileBwPlan<256, 256, 2, 4, 7, 5, 8, 2, 4> TB_256_L2of4_k75;
+typedef BwPlan<64, 64, 2, 1, 5, 1, 1> CB_64_L2_k5;
+typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8, 2, 2> TB_64_L2of4_k33;
+typedef BwPlan<16, 16, 2, 1, 3, 1, 1> CB_16_L2_k3;
+typedef TileBwPlan<64, 64, 1, 2, 5, 5, 16, 2, 2> TB_64_L1of2_k55;
+typedef BwPlan<32, 32, 1, 1, 5, 1, 1> CB_32_L1_k5b;
+
+#define WTC_BW_WHOLE(PLAN) \
+    {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K, {whole_launch<PLAN, float>, whole_launch<PLAN, bf16_t>}, whole_ws<PLAN>}
+#define WTC_BW_SPLIT(FPL, CPL)                                                                    \
+    {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K,                                                   \
+     {split_bw_launch<FPL, CPL, float>, split_bw_launch<FPL, CPL, bf16_t>}, split_bw_ws<FPL, CPL>}
 
 static const BwEntry kBwEntries[] = {
-    WTC_BW_ENTRY(BP_32_L2_k55), WTC_BW_ENTRY(BP_56_L3_k55),    WTC_BW_ENTRY(BP_28_L2_k55),
-    WTC_BW_ENTRY(BP_14_L1_k55), WTC_BW_ENTRY(BP_32_L3_k75),    WTC_BW_ENTRY(BP_24x40_L3_k33),
-    WTC_BW_ENTRY(BP_16_L4_k37), WTC_BW_ENTRY(BP_64_L4_k75),
+    WTC_BW_WHOLE(BP_32_L2_k55), WTC_BW_WHOLE(BP_56_L3_k55),    WTC_BW_WHOLE(BP_28_L2_k55),
+    WTC_BW_WHOLE(BP_14_L1_k55), WTC_BW_WHOLE(BP_32_L3_k75),    WTC_BW_WHOLE(BP_24x40_L3_k33),
+    WTC_BW_WHOLE(BP_16_L4_k37), WTC_BW_WHOLE(BP_64_L4_k75),
+    WTC_BW_SPLIT(TB_128_L1_k55, CB_32_L1_k5),      WTC_BW_SPLIT(TB_128_L2_k55, CB_32_L1_k5),
+    WTC_BW_SPLIT(TB_128_L2of3_k55, CB_32_L1_k5),   WTC_BW_SPLIT(TB_128_L2of4_k55, CB_32_L2_k5),
+    WTC_BW_SPLIT(TB_128_L2of5_k55, CB_32_L3_k5),   WTC_BW_SPLIT(TB_256_L2of4_k75, CB_64_L2_k5),
+    WTC_BW_SPLIT(TB_64_L2of4_k33, CB_16_L2_k3),    WTC_BW_SPLIT(TB_64_L1of2_k55, CB_32_L1_k5b),
 };
 
 static const BwEntry* find_bw(int H, int W, int L, int KB, int K) {
@@ -394,18 +803,9 @@ static const BwEntry* find_bw(int H, int W, int L, int KB, int K) {
     return nullptr;
 }
 
-// batches per chunk: about three rounds of workgroups over the chip, so the
-// per-chunk reduction is amortised over several planes
-static int chunk_batches(int B, int C) {
-    const int want_chunks = cdiv(1536, C);
-    const int nchunk = want_chunks < B ? want_chunks : B;
-    return cdiv(B, nchunk < 1 ? 1 : nchunk);
-}
-
 size_t bwdw_workspace_bytes(int B, int C, int H, int W, int L, int KB, int K) {
-    if (!find_bw(H, W, L, KB, K)) return (size_t)-1;
-    const int nchunk = cdiv(B, chunk_batches(B, C));
-    return (size_t)nchunk * C * (KB * KB + 4 * L * K * K) * sizeof(float);
+    const BwEntry* e = find_bw(H, W, L, KB, K);
+    return e ? e->ws(B, C) : (size_t)-1;
 }
 
 hipError_t bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16, const void* x,
@@ -413,13 +813,7 @@ hipError_t bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf
                        float* dw_lvl, float* dscale, void* ws, hipStream_t stream) {
     const BwEntry* e = find_bw(H, W, L, KB, K);
     if (!e) return hipErrorInvalidValue;
-    const int bpc = chunk_batches(B, C), nchunk = cdiv(B, bpc);
-    float* part = (float*)ws;
-    hipError_t err = e->fn[bf16 ? 1 : 0](x, dy, part, B, C, bpc, stream);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(256), 0, stream, (const float*)part,
-                       nchunk, C, L, KB, K, w_lvl, scale, dw_base, dw_lvl, dscale);
-    return hipGetLastError();
+    return e->fn[bf16 ? 1 : 0](x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, B, C, stream);
 }
 
 }  // namespace wtc

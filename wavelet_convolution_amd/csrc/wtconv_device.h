@@ -114,6 +114,21 @@ __device__ __forceinline__ void store_row(bf16_t* __restrict__ p, const float (&
     }
 }
 
+// Materialise values in registers at this point: an empty asm that reads and
+// writes each one. Compiler passes may otherwise sink a convolution's FMAs
+// down to the first use of its result, phases later, keeping every loaded
+// window value live across the barriers in between (and spilling them).
+template <int N>
+__device__ __forceinline__ void pin_regs(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+template <int R, int N>
+__device__ __forceinline__ void pin_regs(float (&v)[R][N]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) pin_regs(v[r]);
+}
+
 // acc[o][q] += sum_{m,n} w[m][n] * s[(o+m)*S + q+n]: an OR x OC tile of a
 // 'same' cross-correlation read from a zero-bordered LDS plane (s points at
 // the window's top-left corner, S is the plane's row stride). The K*K taps
@@ -123,9 +138,10 @@ __device__ __forceinline__ void store_row(bf16_t* __restrict__ p, const float (&
 //
 // The taps block starts 16-byte aligned and is padded to a multiple of four
 // floats (kpad4), so it is read with 128-bit broadcasts. Scheduling barriers
-// on both ends keep one call's taps and window rows live only during that
-// call: without them the scheduler hoists the taps of every band of a phase
-// at once, or sinks the FMA chains into the store loop, and spills.
+// on both ends and the pinned results keep one call's taps and window rows
+// live only during that call: without them the taps of every band of a phase
+// are hoisted at once, or the FMA chains sink to the results' use, and
+// registers spill.
 constexpr int kpad4(int k) { return (k * k + 3) / 4 * 4; }
 
 template <int K, int OR, int OC, int S>
@@ -159,6 +175,7 @@ __device__ __forceinline__ void conv_tile(const float* s, const float* w, float 
             }
         }
     }
+    pin_regs(acc);
     __builtin_amdgcn_sched_barrier(0);
 }
 

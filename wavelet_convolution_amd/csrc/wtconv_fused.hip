@@ -1,240 +1,14 @@
-// Fused WTConv forward / backward-data kernel for gfx950: one workgroup owns
-// one (b, c) plane, which lives in LDS together with its Haar pyramid.
-//
-// The abstract of arXiv:2608.10805 ("I/O-aware reformulation of wavelet
-// convolution", Abstract) names three reformulations; all three are used:
-//  (1) the Haar analysis butterfly is recomputed on chip from x: x is read
-//      from HBM once and no subband ever leaves LDS;
-//  (2) the synthesis cascade is one closed-form pass: level l adds
-//        sum_s sign_s(bit_{l-1} h, bit_{l-1} w) * Z'_l^s[h >> l][w >> l]
-//      to output pixel (h, w), where sign_s is the band's +-1 pattern;
-//  (3) the per-(level, channel, band) scale and the Haar normalisation
-//      4^-l are folded into each band's convolution result, so
-//      Z'_l^s = 4^-l * scale * corr(U_l^s, w) with U_l the unnormalised band.
-// y is written to HBM once. Backward data runs the same kernel with every
-// kernel turned by 180 degrees (the layer's transpose).
-//
-// Phases (barriers between them):
-//  P0  zero LDS borders, stream x into LDS (fp32, zero border k_base/2)
-//  P1  per main item (a TR x TC tile of level-1 positions = a 2TR x 2TC
-//      output tile): base convolution into registers, level-1 analysis into
-//      LDS region B
-//  P2  levels 2..L: analysis from the LL band below, into region A (x is dead)
-//  P3  levels 2..L: per-band convolution into registers, then written over
-//      their own subbands in LDS
-//  P4  per main item: level-1 convolution of the four bands in registers,
-//      closed-form synthesis of all levels, one store of y.
-#include "wtconv_device.h"
-#include "wtconv_plans.h"
+// Registry of the whole-plane forward / backward-data kernels (the kernel
+// itself is in wtconv_plane.h).
+#include "wtconv_plane.h"
 
 namespace wtc {
-
-template <class P, typename T, bool FLIP>
-__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU))) void plane_kernel(const T* __restrict__ in,
-                                                      const float* __restrict__ w_base,
-                                                      const float* __restrict__ w_lvl,
-                                                      const float* __restrict__ scale,
-                                                      T* __restrict__ out, int C) {
-    constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
-    constexpr int TR = P::TR, TC = P::TC, PB = P::PB, PK = P::PK;
-    constexpr int SX = P::SX, H1 = H / 2, W1 = W / 2;
-    constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
-    constexpr int NI = P::NI, MI = P::MI, TPR = W1 / TC;
-
-    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
-    float* A = lds;               // x (bordered), later U_2..U_L and Z'_2..Z'_L
-    float* Bq = lds + P::ASIZE;   // U_1 (4 bordered bands)
-    float* WB = lds + P::LDS_FLOATS;   // base taps (turned for FLIP), padded to KB2P
-    float* WL = WB + P::KB2P;          // level taps x scale x 4^-l, [L][4][K2P]
-
-    const int tid = threadIdx.x;
-    const int plane = blockIdx.x;
-    const int c = plane % C;
-    const T* __restrict__ src = in + (size_t)plane * H * W;
-    T* __restrict__ dst = out + (size_t)plane * H * W;
-
-    // ---------------------------------------------------------------- P0
-    // stage the taps: turned by 180 degrees for the transpose, and the level
-    // taps scaled by scale * 4^-l (reformulation (3)); padding taps are zero
-    constexpr int KB2P = P::KB2P, K2P = P::K2P;
-    for (int t = tid; t < KB2P; t += NT)
-        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
-    for (int t = tid; t < 4 * L * K2P; t += NT) {
-        const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
-        const size_t pi = ((size_t)l * C + c) * 4 + s;
-        const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
-        WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
-    }
-    zero_border<1, H, W, PB, SX>(A, tid, NT);
-    zero_border<4, H1, W1, PK, S1>(Bq, tid, NT);
-    {
-        // every global load of the plane is issued before the first LDS
-        // write, so the HBM latency is paid once per plane
-        constexpr int V = vec_elems<T>(W, H * W);
-        constexpr int NV = H * W / V;
-        constexpr int NL = cdiv(NV, NT);
-        float v[NL][V];
-#pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) load_vec<T, V>(src + q * V, v[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) {
-                const int e = q * V, r = e / W, col = e - r * W;
-#pragma unroll
-                for (int i = 0; i < V; ++i) A[(r + PB) * SX + col + PB + i] = v[k][i];
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------------- P1
-    float yb[MI][2 * TR][2 * TC];
-#pragma unroll
-    for (int it = 0; it < MI; ++it) {
-        const int item = tid + it * NT;
-#pragma unroll
-        for (int r = 0; r < 2 * TR; ++r)
-#pragma unroll
-            for (int q = 0; q < 2 * TC; ++q) yb[it][r][q] = 0.f;
-        if (item < NI) {
-            const int ti = item / TPR, tj = item - ti * TPR;
-            const int h0 = 2 * TR * ti, w0 = 2 * TC * tj;
-            conv_tile<KB, 2 * TR, 2 * TC, SX>(A + h0 * SX + w0, WB, yb[it]);
-            const int i0 = TR * ti, j0 = TC * tj;
-#pragma unroll
-            for (int r = 0; r < TR; ++r)
-#pragma unroll
-                for (int q = 0; q < TC; ++q) {
-                    const float* x2 = A + (PB + 2 * (i0 + r)) * SX + PB + 2 * (j0 + q);
-                    float b[4];
-                    haar4(x2[0], x2[1], x2[SX], x2[SX + 1], b[0], b[1], b[2], b[3]);
-                    const int o = (PK + i0 + r) * S1 + PK + j0 + q;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) Bq[s * BS1 + o] = b[s];
-                }
-        }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------------- P2
-    P::for_deep_levels([&](auto lc) {
-        constexpr int l = decltype(lc)::value;
-        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
-        constexpr int Sp = P::su(l - 1), BSp = P::bandsz(l - 1);
-        float* Ul = A + P::uoff(l);
-        const float* LLp = (l == 2) ? (Bq + PK * Sp + PK) : (A + P::uoff(l - 1) + PK * Sp + PK);
-        (void)BSp;
-        zero_border<4, hl, wl, PK, Sl>(Ul, tid, NT);
-        for (int q = tid; q < hl * wl; q += NT) {
-            const int i = q / wl, j = q - i * wl;
-            const float* x2 = LLp + 2 * i * Sp + 2 * j;
-            float b[4];
-            haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], b[0], b[1], b[2], b[3]);
-            const int o = (PK + i) * Sl + PK + j;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Ul[s * BSl + o] = b[s];
-        }
-        __syncthreads();
-    });
-
-    // ---------------------------------------------------------------- P3
-    P::for_deep_levels([&](auto lc) {
-        constexpr int l = decltype(lc)::value;
-        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
-        constexpr Tile tl = P::deep_tile(l);
-        constexpr int RR = tl.r, CC = tl.c, TPRl = wl / CC, NIl = (hl / RR) * TPRl;
-        constexpr int MIl = cdiv(NIl, NT);
-        float* Ul = A + P::uoff(l);
-        float z[MIl][4][RR][CC];
-#pragma unroll
-        for (int it = 0; it < MIl; ++it) {
-            const int item = tid + it * NT;
-            const int ti = item / TPRl, tj = item - ti * TPRl;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                for (int r = 0; r < RR; ++r)
-#pragma unroll
-                    for (int q = 0; q < CC; ++q) z[it][s][r][q] = 0.f;
-                if (item < NIl)
-                    conv_tile<K, RR, CC, Sl>(Ul + s * BSl + RR * ti * Sl + CC * tj,
-                                             WL + ((l - 1) * 4 + s) * K2P, z[it][s]);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < MIl; ++it) {
-            const int item = tid + it * NT;
-            if (item < NIl) {
-                const int ti = item / TPRl, tj = item - ti * TPRl;
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int r = 0; r < RR; ++r)
-#pragma unroll
-                        for (int q = 0; q < CC; ++q)
-                            Ul[s * BSl + (PK + RR * ti + r) * Sl + PK + CC * tj + q] = z[it][s][r][q];
-            }
-        }
-    });
-    if constexpr (L >= 2) __syncthreads();
-
-    // ---------------------------------------------------------------- P4
-#pragma unroll
-    for (int it = 0; it < MI; ++it) {
-        const int item = tid + it * NT;
-        if (item >= NI) continue;
-        const int ti = item / TPR, tj = item - ti * TPR;
-        const int i0 = TR * ti, j0 = TC * tj;
-        float z1[4][TR][TC];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int r = 0; r < TR; ++r)
-#pragma unroll
-                for (int q = 0; q < TC; ++q) z1[s][r][q] = 0.f;
-            conv_tile<K, TR, TC, S1>(Bq + s * BS1 + i0 * S1 + j0, WL + s * K2P, z1[s]);
-        }
-#pragma unroll
-        for (int r = 0; r < TR; ++r) {
-            float row0[2 * TC], row1[2 * TC];
-#pragma unroll
-            for (int q = 0; q < TC; ++q) {
-                const int i = i0 + r, j = j0 + q;
-                // coarser levels: constant over the 2x2 output block of (i, j)
-                float e = 0.f;
-                P::for_deep_levels([&](auto lc) {
-                    constexpr int l = decltype(lc)::value;
-                    constexpr int Sl = P::su(l), BSl = P::bandsz(l);
-                    const float* Zl = A + P::uoff(l) + (PK + (i >> (l - 1))) * Sl + PK + (j >> (l - 1));
-                    const bool bi = (i >> (l - 2)) & 1, bj = (j >> (l - 2)) & 1;
-                    const float a0 = Zl[0], a1 = Zl[BSl], a2 = Zl[2 * BSl], a3 = Zl[3 * BSl];
-                    e += a0 + (bi ? -a1 : a1) + (bj ? -a2 : a2) + ((bi != bj) ? -a3 : a3);
-                });
-                const float p0 = z1[0][r][q], p1 = z1[1][r][q], p2 = z1[2][r][q], p3 = z1[3][r][q];
-                row0[2 * q] = yb[it][2 * r][2 * q] + (p0 + p1 + p2 + p3) + e;
-                row0[2 * q + 1] = yb[it][2 * r][2 * q + 1] + (p0 + p1 - p2 - p3) + e;
-                row1[2 * q] = yb[it][2 * r + 1][2 * q] + (p0 - p1 + p2 - p3) + e;
-                row1[2 * q + 1] = yb[it][2 * r + 1][2 * q + 1] + (p0 - p1 - p2 + p3) + e;
-            }
-            const int h = 2 * (i0 + r), w0 = 2 * j0;
-            store_row<2 * TC>(dst + (size_t)h * W + w0, row0);
-            store_row<2 * TC>(dst + (size_t)(h + 1) * W + w0, row1);
-        }
-    }
-}
-
-// ------------------------------------------------------------ registry
 
 template <class P, typename T, bool FLIP>
 static hipError_t launch_plane(const void* in, const float* wb, const float* wl, const float* sc,
                                void* out, int B, int C, hipStream_t stream) {
     const unsigned planes = (unsigned)B * (unsigned)C;
-    hipLaunchKernelGGL((plane_kernel<P, T, FLIP>), dim3(planes), dim3(P::NT), 0, stream,
+    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, 0, T>), dim3(planes), dim3(P::NT), 0, stream,
                        (const T*)in, wb, wl, sc, (T*)out, C);
     return hipGetLastError();
 }
