@@ -101,6 +101,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the 256 MB MALL)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the steps, copy one 1 GiB buffer (known HBM bytes) so that a counter "
+                         "run can scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -211,6 +214,14 @@ def main() -> int:
         naive = {"ms_per_step": round(nms, 4), "images_per_s": round(cfg.B / (nms * 1e-3), 1),
                  "fused_speedup": round(nms / ms_per_step, 3)}
         del nws
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)   # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     step_s = ms_per_step * 1e-3
     hbm_tbs = model.step_bytes / step_s / 1e12
