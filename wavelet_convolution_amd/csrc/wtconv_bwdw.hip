@@ -84,10 +84,12 @@ struct BwPlan {
     static_assert(H % BR == 0 && W % BC == 0, "base tile must divide the plane");
     static constexpr int SX = odd_stride(W + 2 * PB);
     static constexpr int XSIZE = (H + 2 * PB) * SX;
-    static constexpr int DSIZE = H * W;
+    static constexpr int SD = odd_stride(W);   // dy rows: odd stride, fewer bank conflicts
+    static constexpr int DSIZE = H * SD;
     static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
     static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
-    static constexpr int vsz(int l) { return (H >> l) * (W >> l); }
+    static constexpr int sv(int l) { return odd_stride(W >> l); }
+    static constexpr int vsz(int l) { return (H >> l) * sv(l); }
     static constexpr int uoff(int l) {
         int o = 0;
         for (int q = 1; q < l; ++q) o += 4 * bandsz(q);
@@ -202,7 +204,7 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
 #pragma unroll
                 for (int i = 0; i < V; ++i) {
                     X[(r + PB) * SX + col + PB + i] = vx[k][i];
-                    DY[e + i] = vd[k][i];
+                    DY[r * P::SD + col + i] = vd[k][i];
                 }
             }
         }
@@ -212,22 +214,22 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             for (int item = gtid; item < NI; item += 256) {
                 const int ti = item / TPR, tj = item - ti * TPR;
                 const int h0 = BR * ti, w0 = BC * tj;
-                taps_tile<KB, BR, BC, SX, W>(X + h0 * SX + w0, DY + h0 * W + w0, acc0);
+                taps_tile<KB, BR, BC, SX, P::SD>(X + h0 * SX + w0, DY + h0 * P::SD + w0, acc0);
             }
         }
         {
-            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1);
+            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1), SD = P::SD;
             for (int q = tid; q < H1 * W1; q += NT) {
                 const int i = q / W1, j = q - i * W1;
                 const float* x2 = X + (PB + 2 * i) * SX + PB + 2 * j;
-                const float* d2 = DY + 2 * i * W + 2 * j;
+                const float* d2 = DY + 2 * i * SD + 2 * j;
                 float u[4], v[4];
                 haar4(x2[0], x2[1], x2[SX], x2[SX + 1], u[0], u[1], u[2], u[3]);
-                haar4(d2[0], d2[1], d2[W], d2[W + 1], v[0], v[1], v[2], v[3]);
+                haar4(d2[0], d2[1], d2[SD], d2[SD + 1], v[0], v[1], v[2], v[3]);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     U[s * BS1 + (PK + i) * S1 + PK + j] = u[s];
-                    Vb[s * VS1 + q] = v[s];
+                    Vb[s * VS1 + i * SV1 + j] = v[s];
                 }
             }
         }
@@ -237,7 +239,7 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             constexpr int l = decltype(lc)::value;
             if constexpr (l >= 2) {
                 constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-                constexpr int Sp = P::su(l - 1), wp = W >> (l - 1);
+                constexpr int Sp = P::su(l - 1), SVp = P::sv(l - 1), SVl = P::sv(l);
                 const float* LLu = U + P::uoff(l - 1) + PK * Sp + PK;
                 const float* LLv = Vb + P::voff(l - 1);
                 float* Ul = U + P::uoff(l);
@@ -245,14 +247,14 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                 for (int q = tid; q < hl * wl; q += NT) {
                     const int i = q / wl, j = q - i * wl;
                     const float* x2 = LLu + 2 * i * Sp + 2 * j;
-                    const float* d2 = LLv + 2 * i * wp + 2 * j;
+                    const float* d2 = LLv + 2 * i * SVp + 2 * j;
                     float u[4], v[4];
                     haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], u[0], u[1], u[2], u[3]);
-                    haar4(d2[0], d2[1], d2[wp], d2[wp + 1], v[0], v[1], v[2], v[3]);
+                    haar4(d2[0], d2[1], d2[SVp], d2[SVp + 1], v[0], v[1], v[2], v[3]);
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         Ul[s * BSl + (PK + i) * Sl + PK + j] = u[s];
-                        Vl[s * VSl + q] = v[s];
+                        Vl[s * VSl + i * SVl + j] = v[s];
                     }
                 }
                 __syncthreads();
@@ -270,13 +272,14 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
+                constexpr int SVl = P::sv(l);
                 for (int item = lane; item < NIl; item += 64) {
                     const int ti = item / TPRl, tj = item - ti * TPRl;
                     if constexpr (P::slot_of(l) == 0)
-                        taps_tile<K, RR, CC, Sl, wl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * wl + CC * tj, acc0);
+                        taps_tile<K, RR, CC, Sl, SVl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * SVl + CC * tj, acc0);
                     else
-                        taps_tile<K, RR, CC, Sl, wl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * wl + CC * tj,
-                                                     accl[P::slot_of(l) - 1]);
+                        taps_tile<K, RR, CC, Sl, SVl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * SVl + CC * tj,
+                                                      accl[P::slot_of(l) - 1]);
                 }
             }
         });
@@ -337,10 +340,14 @@ __global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ p
     const int TA = kb2 + 4 * LA * k2, TB = taps - TA;
     for (int t = tid; t < taps; t += blockDim.x) {
         float a = 0.f;
-        if (t < TA)
+        // independent loads, issued eight at a time; the sum stays in chunk order
+        if (t < TA) {
+#pragma unroll 8
             for (int ch = 0; ch < nA; ++ch) a += partA[((size_t)ch * C + c) * TA + t];
-        else
+        } else {
+#pragma unroll 8
             for (int ch = 0; ch < nB; ++ch) a += partB[((size_t)ch * C + c) * TB + (t - TA)];
+        }
         if (t >= kb2) {
             const int l = (t - kb2) / (4 * k2);   // 0-based level
             a *= 1.0f / (float)(1 << (2 * (l + 1)));
@@ -390,11 +397,13 @@ struct TileBwPlan {
     static constexpr int RH0 = TH + 2 * G;
     static constexpr int SX = odd_stride(W + 2 * PB);
     static constexpr int XSIZE = RH0 * SX;
-    static constexpr int DSIZE = TH * W;
+    static constexpr int SD = odd_stride(W);
+    static constexpr int DSIZE = TH * SD;
     static constexpr int rh(int l) { return RH0 >> l; }
     static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
     static constexpr int bandsz(int l) { return rh(l) * su(l); }
-    static constexpr int vsz(int l) { return (TH >> l) * (W >> l); }
+    static constexpr int sv(int l) { return odd_stride(W >> l); }
+    static constexpr int vsz(int l) { return (TH >> l) * sv(l); }
     static constexpr int uoff(int l) {
         int o = 0;
         for (int q = 1; q < l; ++q) o += 4 * bandsz(q);
@@ -524,9 +533,11 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int q = tid + k * NT;
-            if (NVD % NT == 0 || q < NVD)
+            if (NVD % NT == 0 || q < NVD) {
+                const int e = q * V, rr = e / W, col = e - rr * W;
 #pragma unroll
-                for (int i = 0; i < V; ++i) DY[q * V + i] = vd[k][i];
+                for (int i = 0; i < V; ++i) DY[rr * P::SD + col + i] = vd[k][i];
+            }
         }
         __syncthreads();
         // ------------------------------------- P1: base taps, level 1 bands
@@ -534,7 +545,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             for (int item = gtid; item < NI; item += 256) {
                 const int ti = item / TPR, tj = item - ti * TPR;
                 const int h0 = BR * ti, w0 = BC * tj;
-                taps_tile<KB, BR, BC, SX, W>(X + (G + h0 - PB) * SX + w0, DY + h0 * W + w0, acc0);
+                taps_tile<KB, BR, BC, SX, P::SD>(X + (G + h0 - PB) * SX + w0, DY + h0 * P::SD + w0, acc0);
             }
         }
         {
@@ -547,13 +558,14 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 #pragma unroll
                 for (int s = 0; s < 4; ++s) U[s * BS1 + i * S1 + PK + j] = uu[s];
             }
+            constexpr int SD = P::SD, SV1 = P::sv(1);
             for (int q = tid; q < (TH / 2) * W1; q += NT) {
                 const int i = q / W1, j = q - i * W1;
-                const float* d2 = DY + 2 * i * W + 2 * j;
+                const float* d2 = DY + 2 * i * SD + 2 * j;
                 float vv[4];
-                haar4(d2[0], d2[1], d2[W], d2[W + 1], vv[0], vv[1], vv[2], vv[3]);
+                haar4(d2[0], d2[1], d2[SD], d2[SD + 1], vv[0], vv[1], vv[2], vv[3]);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) Vb[s * VS1 + q] = vv[s];
+                for (int s = 0; s < 4; ++s) Vb[s * VS1 + i * SV1 + j] = vv[s];
             }
         }
         __syncthreads();
@@ -562,7 +574,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             constexpr int l = decltype(lc)::value;
             if constexpr (l >= 2) {
                 constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-                constexpr int Sp = P::su(l - 1), wp = W >> (l - 1);
+                constexpr int Sp = P::su(l - 1), SVp = P::sv(l - 1), SVl = P::sv(l);
                 const float* LLu = U + P::uoff(l - 1) + PK;
                 const float* LLv = Vb + P::voff(l - 1);
                 float* Ul = U + P::uoff(l);
@@ -577,11 +589,11 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
                 }
                 for (int q = tid; q < (TH >> l) * wl; q += NT) {
                     const int i = q / wl, j = q - i * wl;
-                    const float* d2 = LLv + 2 * i * wp + 2 * j;
+                    const float* d2 = LLv + 2 * i * SVp + 2 * j;
                     float vv[4];
-                    haar4(d2[0], d2[1], d2[wp], d2[wp + 1], vv[0], vv[1], vv[2], vv[3]);
+                    haar4(d2[0], d2[1], d2[SVp], d2[SVp + 1], vv[0], vv[1], vv[2], vv[3]);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) Vl[s * VSl + q] = vv[s];
+                    for (int s = 0; s < 4; ++s) Vl[s * VSl + i * SVl + j] = vv[s];
                 }
                 __syncthreads();
             }
@@ -593,10 +605,11 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             const float* LLv = Vb + P::voff(L0);
             float* pxo = px + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
             float* pdo = pdy + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            constexpr int SVL = P::sv(L0);
             for (int q = tid; q < hl * wl; q += NT) {
                 const int i = q / wl, j = q - i * wl;
                 pxo[q] = LLu[(GL + i) * Sl + j];
-                pdo[q] = LLv[q];
+                pdo[q] = LLv[i * SVL + j];
             }
         }
         if (u + 1 < u1) issue_loads(u + 1);
@@ -610,14 +623,15 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
+                constexpr int SVl = P::sv(l);
                 for (int item = lane; item < NIl; item += 64) {
                     const int ti = item / TPRl, tj = item - ti * TPRl;
                     if constexpr (P::slot_of(l) == 0)
-                        taps_tile<K, RR, CC, Sl, wl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
-                                                     Vs + RR * ti * wl + CC * tj, acc0);
+                        taps_tile<K, RR, CC, Sl, SVl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
+                                                      Vs + RR * ti * SVl + CC * tj, acc0);
                     else
-                        taps_tile<K, RR, CC, Sl, wl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
-                                                     Vs + RR * ti * wl + CC * tj, accl[P::slot_of(l) - 1]);
+                        taps_tile<K, RR, CC, Sl, SVl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
+                                                      Vs + RR * ti * SVl + CC * tj, accl[P::slot_of(l) - 1]);
                 }
             }
         });
@@ -662,12 +676,16 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 
 // ------------------------------------------------------------ registry
 
-// batches (or tile units) per chunk: about three rounds of workgroups over
-// the chip, so the per-chunk reduction is amortised over several planes
+// batches (or tile units) per chunk: about one workgroup per slot of the
+// chip (256 CUs x 2 resident workgroups of 8 wavefronts), so the per-chunk
+// reduction is amortised over as many planes as the parallelism allows
+// (rounded down: a second, mostly empty round of workgroups would double
+// the kernel's tail)
 static int chunk_units(int units, int C) {
-    const int want_chunks = cdiv(1536, C);
-    const int nchunk = want_chunks < units ? want_chunks : units;
-    return cdiv(units, nchunk < 1 ? 1 : nchunk);
+    int nchunk = 512 / C;
+    if (nchunk > units) nchunk = units;
+    if (nchunk < 1) nchunk = 1;
+    return cdiv(units, nchunk);
 }
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
