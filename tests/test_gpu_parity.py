@@ -145,3 +145,58 @@ def test_bf16_store_rounding_is_round_to_nearest_even():
     expect = f32_to_bf16_bits(exact.astype(np.float32))
     got = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 56, 56, 3), (1, 2, 128, 128, 5), (1, 2, 64, 64, 4)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_identity_levels_closed_form_on_gpu(shape):
+    """No oracle involved: with zero base taps, centre-delta level taps and
+    unit scales every level reproduces its input, so the layer returns
+    sum_{m<L} BlockMean_{2^m}(x) (derived by hand from the cascade). Covers the
+    whole-plane and the split path (64x64, L=4, 3x3 taps)."""
+    B, C, H, W, L = shape
+    k = 3 if H == 64 else 5
+    _say(f"[parity] identity levels {shape}")
+    inp = make_inputs(B, C, H, W, L, 5 if H != 64 else 3, k, dtype="f32", seed=6)
+    x, dy, wb, wl, sc = to_device(inp)
+    wl = torch.zeros_like(wl)
+    wl[..., k // 2, k // 2] = 1.0
+    y = wt.wtconv_fwd(x, torch.zeros_like(wb), wl, torch.ones_like(sc))
+    torch.cuda.synchronize()
+    xn = inp.x.astype(np.float64)
+    expect = np.zeros_like(xn)
+    for m in range(L):
+        s = 1 << m
+        bm = xn.reshape(B, C, H // s, s, W // s, s).mean(axis=(3, 5))
+        expect += np.repeat(np.repeat(bm, s, axis=2), s, axis=3)
+    assert rel_err(to_f64(y), expect) <= 1e-6
+
+
+def test_level_zero_and_unplanned_shapes():
+    """L = 0 is the plain depthwise convolution: the naive chain computes it;
+    the fused entry points have no plan for it and say so."""
+    _say("[parity] L = 0")
+    inp = make_inputs(2, 3, 20, 12, 0, 5, 5, dtype="f32", seed=7)
+    x, dy, wb, wl, sc = to_device(inp)
+    y = wt.wtconv_naive_fwd(x, wb, wl, sc)
+    torch.cuda.synchronize()
+    ref = torch.nn.functional.conv2d(x.double().cpu(), wb.double().cpu()[:, None], padding=2, groups=3)
+    assert rel_err(to_f64(y), ref.numpy()) <= 1e-6
+    with pytest.raises(wt.WTConvError) as ei:
+        wt.wtconv_fwd(x, wb, wl, sc)
+    assert ei.value.status == 2
+
+
+def test_repeated_calls_with_changing_batch():
+    """Two calls in a row, the second with a smaller batch: no state is kept
+    between calls."""
+    _say("[parity] changing batch")
+    for B in (4, 1):
+        inp = make_inputs(B, 3, 56, 56, 3, dtype="f32", seed=8 + B)
+        x, dy, wb, wl, sc = to_device(inp)
+        y = wt.wtconv_fwd(x, wb, wl, sc)
+        dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, 5, wl, sc)
+        torch.cuda.synchronize()
+        oy, _, (odwb, odwl, odsc) = _oracle_all(inp)
+        assert rel_err(to_f64(y), oy) <= 1e-4
+        assert rel_err(to_f64(dwl), odwl) <= 1e-4 and rel_err(to_f64(dsc), odsc) <= 1e-4

@@ -179,6 +179,44 @@ __device__ __forceinline__ void conv_tile(const float* s, const float* w, float 
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// acc[o] += sum_{m,n} w[m][n] * s[(o+m)*S + n] for o < R: a column strip of R
+// outputs of a 'same' cross-correlation from a zero-bordered LDS plane
+// (s points at the window's top-left corner). Lanes of a wavefront take
+// consecutive columns, so every window load is a run of consecutive words
+// across the wavefront: no LDS bank conflicts. Each loaded value feeds up to
+// K FMAs (the K taps of its column). Same pinning as conv_tile.
+template <int K, int R, int S>
+__device__ __forceinline__ void conv_col(const float* s, const float* w, float (&acc)[R]) {
+    __builtin_amdgcn_sched_barrier(0);
+    float wr[kpad4(K)];
+#pragma unroll
+    for (int t = 0; t < kpad4(K); t += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(w + t);
+        wr[t] = q.x;
+        wr[t + 1] = q.y;
+        wr[t + 2] = q.z;
+        wr[t + 3] = q.w;
+    }
+#pragma unroll
+    for (int r = 0; r < R + K - 1; ++r) {
+        float win[K];
+#pragma unroll
+        for (int n = 0; n < K; ++n) win[n] = s[r * S + n];
+#pragma unroll
+        for (int o = 0; o < R; ++o) {
+            const int m = r - o;
+            if (m < 0 || m >= K) continue;
+#pragma unroll
+            for (int n = 0; n < K; ++n) {
+                if (m == 0 && n == 0) acc[o] = wr[0] * win[0];
+                else acc[o] = __builtin_fmaf(wr[m * K + n], win[n], acc[o]);
+            }
+        }
+    }
+    pin_regs(acc);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Zero the border cells of NB bordered planes of interior h x w, border B,
 // row stride S (everything outside rows [B, B+h) x cols [B, B+w)).
 template <int NB, int h, int w, int B, int S>

@@ -13,6 +13,21 @@ static hipError_t launch_plane(const void* in, const float* wb, const float* wl,
     return hipGetLastError();
 }
 
+template <class P, typename T, bool FLIP>
+static hipError_t launch_col(const void* in, const float* wb, const float* wl, const float* sc, void* out,
+                             int B, int C, hipStream_t stream) {
+    const unsigned planes = (unsigned)B * (unsigned)C;
+    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(planes), dim3(P::NT), 0, stream, (const T*)in, wb, wl, sc,
+                       (T*)out, C);
+    return hipGetLastError();
+}
+
+#define WTC_COL_ENTRY(PLAN)                                                                   \
+    {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \
+     {{launch_col<PLAN, float, false>, launch_col<PLAN, float, true>},                       \
+      {launch_col<PLAN, bf16_t, false>, launch_col<PLAN, bf16_t, true>}},                    \
+     (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT}
+
 #define WTC_PLANE_ENTRY(PLAN)                                                                 \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \
      {{launch_plane<PLAN, float, false>, launch_plane<PLAN, float, true>},                   \
@@ -20,6 +35,9 @@ static hipError_t launch_plane(const void* in, const float* wb, const float* wl,
      (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT}
 
 static const PlaneEntry kPlaneEntries[] = {
+#if WTC_COL56
+    WTC_COL_ENTRY(CP_56_L3_k55),
+#endif
     WTC_PLANE_ENTRIES(WTC_PLANE_ENTRY)
 };
 

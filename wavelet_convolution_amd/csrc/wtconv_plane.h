@@ -264,3 +264,201 @@ hipError_t launch_coarse(const void* in, const float* wl, const float* sc, float
 }
 
 }  // namespace wtc
+
+namespace wtc {
+
+// Whole-plane forward / backward-data kernel, column-strip work split (see
+// ColPlan). Same phases and LDS regions as plane_kernel; P3 convolves every
+// level (level 1 included) into registers and writes the results over their
+// own subbands, P4 synthesises each output column strip in closed form.
+template <class P, typename T, bool FLIP>
+__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
+void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, const float* __restrict__ w_lvl,
+                const float* __restrict__ scale, T* __restrict__ out, int C) {
+    constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT, RB = P::RB;
+    constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
+    constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
+    constexpr int NIB = P::NIB, MB = P::MB;
+    constexpr int KB2P = P::KB2P, K2P = P::K2P;
+
+    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
+    float* A = lds;
+    float* Bq = lds + P::ASIZE;
+    float* WB = lds + P::LDS_FLOATS;
+    float* WL = WB + KB2P;
+
+    const int tid = threadIdx.x;
+    const int plane = blockIdx.x;
+    const int c = plane % C;
+    const T* __restrict__ src = in + (size_t)plane * H * W;
+    T* __restrict__ dst = out + (size_t)plane * H * W;
+    // U_l (and then Z'_l) of level l: level 1 in region B, the others in A
+    auto ubase = [&](auto lc) -> float* {
+        constexpr int l = decltype(lc)::value;
+        if constexpr (l == 1) return Bq;
+        else return A + P::uoff(l);
+    };
+
+    // ---------------------------------------------------------------- P0
+    for (int t = tid; t < KB2P; t += NT)
+        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
+    for (int t = tid; t < 4 * L * K2P; t += NT) {
+        const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
+        const size_t pi = ((size_t)l * C + c) * 4 + s;
+        const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
+        WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
+    }
+    zero_border<1, H, W, PB, SX>(A, tid, NT);
+    zero_border<4, H1, W1, PK, S1>(Bq, tid, NT);
+    {
+        constexpr int V = vec_elems<T>(W, H * W);
+        constexpr int NV = H * W / V;
+        constexpr int NL = cdiv(NV, NT);
+        float v[NL][V];
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int q = tid + k * NT;
+            if (NV % NT == 0 || q < NV) load_vec<T, V>(src + q * V, v[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int q = tid + k * NT;
+            if (NV % NT == 0 || q < NV) {
+                const int e = q * V, r = e / W, col = e - r * W;
+#pragma unroll
+                for (int i = 0; i < V; ++i) A[(r + PB) * SX + col + PB + i] = v[k][i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- P1
+    float yb[MB][RB];
+#pragma unroll
+    for (int it = 0; it < MB; ++it) {
+        const int item = tid + it * NT;
+        if (NIB % NT == 0 || item < NIB) {
+            const int rb = item / W, w = item - rb * W;
+            conv_col<KB, RB, SX>(A + (rb * RB) * SX + w, WB, yb[it]);
+        }
+    }
+    for (int q = tid; q < H1 * W1; q += NT) {
+        const int i = q / W1, j = q - i * W1;
+        const float* x2 = A + (PB + 2 * i) * SX + PB + 2 * j;
+        float b[4];
+        haar4(x2[0], x2[1], x2[SX], x2[SX + 1], b[0], b[1], b[2], b[3]);
+        const int o = (PK + i) * S1 + PK + j;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Bq[s * BS1 + o] = b[s];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- P2
+    P::for_deep_levels([&](auto lc) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
+        constexpr int Sp = P::su(l - 1);
+        float* Ul = A + P::uoff(l);
+        const float* LLp = (l == 2) ? (Bq + PK * Sp + PK) : (A + P::uoff(l - 1) + PK * Sp + PK);
+        zero_border<4, hl, wl, PK, Sl>(Ul, tid, NT);
+        for (int q = tid; q < hl * wl; q += NT) {
+            const int i = q / wl, j = q - i * wl;
+            const float* x2 = LLp + 2 * i * Sp + 2 * j;
+            float b[4];
+            haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], b[0], b[1], b[2], b[3]);
+            const int o = (PK + i) * Sl + PK + j;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Ul[s * BSl + o] = b[s];
+        }
+        __syncthreads();
+    });
+
+    // ---------------------------------------------------------------- P3
+    // every level: strips of rl(l) rows x 1 column of one band, into registers
+    auto level_conv = [&](auto lc, auto& z) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
+        constexpr int NS = hl / R, NIl = P::nil(l), MIl = cdiv(NIl, NT);
+        float* Ul = ubase(lc);
+#pragma unroll
+        for (int it = 0; it < MIl; ++it) {
+            const int item = tid + it * NT;
+            if (NIl % NT == 0 || item < NIl) {
+                const int s = item / (NS * wl), rem = item - s * (NS * wl);
+                const int rs = rem / wl, j = rem - rs * wl;
+                conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z[it]);
+            }
+        }
+    };
+    auto level_store = [&](auto lc, auto& z) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
+        constexpr int NS = hl / R, NIl = P::nil(l), MIl = cdiv(NIl, NT);
+        float* Ul = ubase(lc);
+#pragma unroll
+        for (int it = 0; it < MIl; ++it) {
+            const int item = tid + it * NT;
+            if (NIl % NT == 0 || item < NIl) {
+                const int s = item / (NS * wl), rem = item - s * (NS * wl);
+                const int rs = rem / wl, j = rem - rs * wl;
+#pragma unroll
+                for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = z[it][o];
+            }
+        }
+    };
+    // results of all levels stay in registers across one barrier
+    float z1[cdiv(P::nil(1), NT)][P::rl(1)];
+    level_conv(std::integral_constant<int, 1>{}, z1);
+    float z2[L >= 2 ? cdiv(P::nil(L >= 2 ? 2 : 1), NT) : 1][P::rl(L >= 2 ? 2 : 1)];
+    float z3[L >= 3 ? cdiv(P::nil(L >= 3 ? 3 : 1), NT) : 1][P::rl(L >= 3 ? 3 : 1)];
+    float z4[L >= 4 ? cdiv(P::nil(L >= 4 ? 4 : 1), NT) : 1][P::rl(L >= 4 ? 4 : 1)];
+    float z5[L >= 5 ? cdiv(P::nil(L >= 5 ? 5 : 1), NT) : 1][P::rl(L >= 5 ? 5 : 1)];
+    if constexpr (L >= 2) level_conv(std::integral_constant<int, 2>{}, z2);
+    if constexpr (L >= 3) level_conv(std::integral_constant<int, 3>{}, z3);
+    if constexpr (L >= 4) level_conv(std::integral_constant<int, 4>{}, z4);
+    if constexpr (L >= 5) level_conv(std::integral_constant<int, 5>{}, z5);
+    __syncthreads();
+    level_store(std::integral_constant<int, 1>{}, z1);
+    if constexpr (L >= 2) level_store(std::integral_constant<int, 2>{}, z2);
+    if constexpr (L >= 3) level_store(std::integral_constant<int, 3>{}, z3);
+    if constexpr (L >= 4) level_store(std::integral_constant<int, 4>{}, z4);
+    if constexpr (L >= 5) level_store(std::integral_constant<int, 5>{}, z5);
+    __syncthreads();
+
+    // ---------------------------------------------------------------- P4
+    // y[h][w] = base + sum_l A_l + sign(bit_{l-1} h) B_l with
+    // A_l = Z0 + sign(bit_{l-1} w) Z2, B_l = Z1 + sign(bit_{l-1} w) Z3 at (h >> l, w >> l)
+#pragma unroll
+    for (int it = 0; it < MB; ++it) {
+        const int item = tid + it * NT;
+        if (!(NIB % NT == 0 || item < NIB)) continue;
+        const int rb = item / W, w = item - rb * W, h0 = rb * RB;
+        float y[RB];
+#pragma unroll
+        for (int o = 0; o < RB; ++o) y[o] = yb[it][o];
+        P::for_levels([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            constexpr int Sl = P::su(l), BSl = P::bandsz(l), NP = RB >> l;
+            // strips start on a 2^L row boundary: the row bits below L are the
+            // strip-relative ones, known at compile time
+            const float* Zl = ubase(lc) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
+            const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const float* z = Zl + p * Sl;
+                const float a = __builtin_fmaf(sw, z[2 * BSl], z[0]);
+                const float b = __builtin_fmaf(sw, z[3 * BSl], z[BSl]);
+                const float plus = a + b, minus = a - b;
+#pragma unroll
+                for (int o = p << l; o < (p + 1) << l; ++o) y[o] += ((o >> (l - 1)) & 1) ? minus : plus;
+            }
+        });
+#pragma unroll
+        for (int o = 0; o < RB; ++o) {
+            if constexpr (sizeof(T) == 2) dst[(size_t)(h0 + o) * W + w] = narrow_bf16(y[o]);
+            else dst[(size_t)(h0 + o) * W + w] = y[o];
+        }
+    }
+}
+
+}  // namespace wtc

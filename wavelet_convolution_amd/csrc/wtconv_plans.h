@@ -136,3 +136,72 @@ typedef PlanePlan<64, 64, 4, 7, 5, 64, 4, 4> PP_64_L4_k75;
         X(PP_32_L3_k75), X(PP_24x40_L3_k33), X(PP_16_L4_k37), X(PP_64_L4_k75)
 
 }  // namespace wtc
+
+namespace wtc {
+
+// Column-strip variant of the whole-plane plan: a lane computes RB rows x 1
+// column of the base convolution, and RL rows x 1 column of one band at each
+// level, so the lanes of a wavefront read consecutive LDS words (no bank
+// conflicts) and write consecutive output columns. The level results go
+// through LDS and one closed-form pass synthesises every output.
+template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_>
+struct ColPlan {
+    static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, NT = NT_, RB = RB_, RL = RL_;
+    static constexpr int PB = KB / 2, PK = K / 2;
+    static_assert(L >= 1 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
+    static_assert(H % RB == 0, "base strips must divide the plane");
+    static_assert(RB % (1 << L) == 0, "base strips start on 2^L row boundaries");
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole wavefronts");
+    static constexpr int SX = odd_stride(W + 2 * PB);
+    static constexpr int XSIZE = (H + 2 * PB) * SX;
+    static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
+    static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
+    static constexpr int uoff(int l) {
+        int o = 0;
+        for (int q = 2; q < l; ++q) o += 4 * bandsz(q);
+        return o;
+    }
+    static constexpr int UDEEP = uoff(L + 1);
+    static constexpr int ASIZE = XSIZE > UDEEP ? XSIZE : UDEEP;
+    static constexpr int BSIZE = 4 * bandsz(1);
+    static constexpr int LDS_FLOATS = (ASIZE + BSIZE + 3) / 4 * 4;
+    static constexpr int KB2P = kpad4(KB), K2P = kpad4(K);
+    static constexpr int WFLOATS = KB2P + 4 * L * K2P;
+    static_assert((LDS_FLOATS + WFLOATS) * 4 <= 160 * 1024, "plane does not fit in LDS");
+    static constexpr int NIB = (H / RB) * W;       // base strips
+    static constexpr int MB = cdiv(NIB, NT);
+    // rows per strip at level l
+    static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
+    static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * (W >> l); }
+    static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
+    static constexpr int WAVES_PER_EU_LDS = (WG_PER_CU * (NT / 64)) / 4;
+    static constexpr int WAVES_PER_EU =
+        WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > 8 ? 8 : WAVES_PER_EU_LDS);
+
+    template <class F>
+    __device__ static __forceinline__ void for_levels(F&& f) {
+        lv_impl(f, std::make_integer_sequence<int, L>{});
+    }
+    template <class F, int... I>
+    __device__ static __forceinline__ void lv_impl(F& f, std::integer_sequence<int, I...>) {
+        (f(std::integral_constant<int, I + 1>{}), ...);
+    }
+    template <class F>
+    __device__ static __forceinline__ void for_deep_levels(F&& f) {
+        deep_impl(f, std::make_integer_sequence<int, (L >= 2 ? L - 1 : 0)>{});
+    }
+    template <class F, int... I>
+    __device__ static __forceinline__ void deep_impl(F& f, std::integer_sequence<int, I...>) {
+        (f(std::integral_constant<int, I + 2>{}), ...);
+    }
+};
+
+}  // namespace wtc
+
+namespace wtc {
+// column-strip plans (listed ahead of the tile plans of the same shape)
+#ifndef WTC_COL56
+#define WTC_COL56 1
+#endif
+typedef ColPlan<56, 56, 3, 5, 5, 448, 8, 7> CP_56_L3_k55;
+}  // namespace wtc
