@@ -26,37 +26,50 @@
 
 namespace wtc {
 
-// acc[m*K+n] += sum_{o,q} v[o*SV+q] * u[(o+m)*SU + q+n]: tap sums of an
-// OR x OC tile of dy-side values v against the matching window of the
-// bordered x-side plane u (u points at the window's top-left corner).
-// Scheduling barriers keep each call's tile and window rows live only
-// during the call.
-template <int K, int OR, int OC, int SU, int SV, int NA>
-__device__ __forceinline__ void taps_tile(const float* u, const float* v, float (&acc)[NA]) {
+// acc[m*K+n] += sum_{o<R} v[o*SV] * u[(o+m)*SU + n]: tap sums of an R x 1
+// column strip of dy-side values against its window of x-side values. Lanes
+// of a wavefront take consecutive columns: every load is a run of
+// consecutive LDS words across the wavefront, free of bank conflicts.
+template <int K, int R, int SU, int SV, int NA>
+__device__ __forceinline__ void taps_col(const float* u, const float* v, float (&acc)[NA]) {
     static_assert(NA >= K * K, "accumulator slot too small");
     __builtin_amdgcn_sched_barrier(0);
-    float vt[OR][OC];
+    float vt[R];
 #pragma unroll
-    for (int o = 0; o < OR; ++o)
+    for (int o = 0; o < R; ++o) vt[o] = v[o * SV];
 #pragma unroll
-        for (int q = 0; q < OC; ++q) vt[o][q] = v[o * SV + q];
+    for (int r = 0; r < R + K - 1; ++r) {
+        float win[K];
 #pragma unroll
-    for (int r = 0; r < OR + K - 1; ++r) {
-        float win[OC + K - 1];
+        for (int n = 0; n < K; ++n) win[n] = u[r * SU + n];
 #pragma unroll
-        for (int q = 0; q < OC + K - 1; ++q) win[q] = u[r * SU + q];
-#pragma unroll
-        for (int o = 0; o < OR; ++o) {
+        for (int o = 0; o < R; ++o) {
             const int m = r - o;
             if (m < 0 || m >= K) continue;
 #pragma unroll
-            for (int n = 0; n < K; ++n)
-#pragma unroll
-                for (int q = 0; q < OC; ++q) acc[m * K + n] = __builtin_fmaf(vt[o][q], win[q + n], acc[m * K + n]);
+            for (int n = 0; n < K; ++n) acc[m * K + n] = __builtin_fmaf(vt[o], win[n], acc[m * K + n]);
         }
     }
     pin_regs(acc);
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// Rows per column strip for an h x w grid on `lanes` lanes with k x k taps:
+// the fewest cycles on the busiest lane, counting each strip's R*k*k
+// multiply-adds plus its (R+k-1)*k + R LDS reads at two multiply-adds each
+// (a CU issues one wavefront multiply-add per clock across its four SIMDs
+// but moves only half a wavefront's worth of LDS words per clock).
+constexpr int pick_rows(int h, int w, int lanes, int k) {
+    int best = 1, best_cost = 1 << 30;
+    for (int r = 1; r <= 16 && r <= h; ++r) {
+        if (h % r != 0) continue;
+        const int cost = cdiv((h / r) * w, lanes) * (r * k * k + 2 * ((r + k - 1) * k + r));
+        if (cost < best_cost) {
+            best = r;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -75,13 +88,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 //   group B (w >= 4): level 1 (slot 0), levels 2, 4 (slots 1, 2)
 // which balances the multiply-adds (level 1 alone equals the base work) and
 // keeps every lane at about two or three slots of taps.
-template <int H_, int W_, int L_, int KB_, int K_, int BR_, int BC_>
+template <int H_, int W_, int L_, int KB_, int K_>
 struct BwPlan {
-    static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, BR = BR_, BC = BC_;
+    static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_;
+    static constexpr int RB = pick_rows(H, W, 256, KB);   // base strips on group A's lanes
     static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && L <= 5 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
-    static_assert(H % BR == 0 && W % BC == 0, "base tile must divide the plane");
     static constexpr int SX = odd_stride(W + 2 * PB);
     static constexpr int XSIZE = (H + 2 * PB) * SX;
     static constexpr int SD = odd_stride(W);   // dy rows: odd stride, fewer bank conflicts
@@ -108,9 +121,9 @@ struct BwPlan {
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
-    static constexpr int NI = (H / BR) * (W / BC);
+    static constexpr int NI = (H / RB) * W;   // base strips
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
-    static constexpr Tile band_tile(int l) { return pick_tile(H >> l, W >> l, 64); }
+    static constexpr int band_rows(int l) { return pick_rows(H >> l, W >> l, 64, K); }
     static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
     static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
     // registers bound the occupancy too: each lane holds its tap slots plus
@@ -144,7 +157,7 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                  int C, int bpc) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
-    constexpr int BR = P::BR, BC = P::BC, NI = P::NI, TPR = W / BC;
+    constexpr int RB = P::RB, NI = P::NI;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
     constexpr int V = vec_elems<T>(W, H * W);
     constexpr int NV = H * W / V;
@@ -195,6 +208,8 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     if (b0 < b1) issue_loads(b0);
 
     for (int b = b0; b < b1; ++b) {
+        // the previous plane's taps read x, dy and the bands: all done first
+        if (b > b0) __syncthreads();
         // ------------------------------------------------ P0: stream in
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
@@ -209,14 +224,9 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             }
         }
         __syncthreads();
-        // ------------------------------------- P1: base taps, level 1 bands
-        if (BASE && grp == 0) {
-            for (int item = gtid; item < NI; item += 256) {
-                const int ti = item / TPR, tj = item - ti * TPR;
-                const int h0 = BR * ti, w0 = BC * tj;
-                taps_tile<KB, BR, BC, SX, P::SD>(X + h0 * SX + w0, DY + h0 * P::SD + w0, acc0);
-            }
-        }
+        // the next plane's loads fly during the analysis and the taps
+        if (b + 1 < b1) issue_loads(b + 1);
+        // ----------------------------------------- P1: level 1 analysis
         {
             constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1), SD = P::SD;
             for (int q = tid; q < H1 * W1; q += NT) {
@@ -260,26 +270,27 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                 __syncthreads();
             }
         });
-        // the next plane's loads fly while the level taps run; P0 of the
-        // next plane writes only x and dy, which the level taps do not read
-        if (b + 1 < b1) issue_loads(b + 1);
-        // --------------------------- P3: level taps, one band per wavefront
+        // ------------------- P3: all taps at once, base taps and one band per wavefront
+        if (BASE && grp == 0) {
+            for (int item = gtid; item < NI; item += 256) {
+                const int rb = item / W, w = item - rb * W, h0 = rb * RB;
+                taps_col<KB, RB, SX, P::SD>(X + h0 * SX + w, DY + h0 * P::SD + w, acc0);
+            }
+        }
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-            constexpr Tile tl = P::band_tile(l);
-            constexpr int RR = tl.r, CC = tl.c, TPRl = wl / CC, NIl = (hl / RR) * TPRl;
+            constexpr int R = P::band_rows(l), NIl = (hl / R) * wl;
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
                 constexpr int SVl = P::sv(l);
                 for (int item = lane; item < NIl; item += 64) {
-                    const int ti = item / TPRl, tj = item - ti * TPRl;
+                    const int rs = item / wl, j = item - rs * wl;
                     if constexpr (P::slot_of(l) == 0)
-                        taps_tile<K, RR, CC, Sl, SVl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * SVl + CC * tj, acc0);
+                        taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, acc0);
                     else
-                        taps_tile<K, RR, CC, Sl, SVl>(Us + RR * ti * Sl + CC * tj, Vs + RR * ti * SVl + CC * tj,
-                                                      accl[P::slot_of(l) - 1]);
+                        taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, accl[P::slot_of(l) - 1]);
                 }
             }
         });
@@ -383,15 +394,16 @@ __global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ p
 // One workgroup per (channel, chunk of (b, tile) units); the units of a chunk
 // follow each other down the plane, so the halo rows of consecutive tiles
 // are read from L2.
-template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int BR_, int BC_>
+template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_>
 struct TileBwPlan {
-    static constexpr int H = H_, W = W_, L0 = L0_, LT = LT_, KB = KB_, K = K_, TH = TH_, BR = BR_, BC = BC_;
+    static constexpr int H = H_, W = W_, L0 = L0_, LT = LT_, KB = KB_, K = K_, TH = TH_;
+    static constexpr int RB = pick_rows(TH, W, 256, KB);
     static constexpr int L = L0;   // levels handled here (role helpers below)
     static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2, BLK = 1 << L0;
     static_assert(L0 >= 1 && L0 <= 5 && L0 <= LT, "fine levels 1..L0");
     static_assert(H % (1 << LT) == 0 && W % (1 << LT) == 0, "plane must divide into 2^L blocks");
-    static_assert(TH % BLK == 0 && H % TH == 0 && TH % BR == 0 && W % BC == 0, "tile shapes");
+    static_assert(TH % BLK == 0 && H % TH == 0, "tile shapes");
     static constexpr int G0 = PB > (PK << L0) ? PB : (PK << L0);
     static constexpr int G = cdiv(G0, BLK) * BLK;
     static constexpr int RH0 = TH + 2 * G;
@@ -421,10 +433,10 @@ struct TileBwPlan {
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "tile does not fit in LDS");
-    static constexpr int NI = (TH / BR) * (W / BC);
+    static constexpr int NI = (TH / RB) * W;
     static constexpr int NTILE = H / TH;
     static constexpr int TAPS = KB * KB + 4 * L0 * K * K;
-    static constexpr Tile band_tile(int l) { return pick_tile(TH >> l, W >> l, 64); }
+    static constexpr int band_rows(int l) { return pick_rows(TH >> l, W >> l, 64, K); }
     static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
     static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
     static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 64;
@@ -450,7 +462,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
                       float* __restrict__ px, float* __restrict__ pdy, int B, int C, int upc) {
     constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, G = P::G, RH0 = P::RH0, W1 = W / 2;
-    constexpr int BR = P::BR, BC = P::BC, NI = P::NI, TPR = W / BC;
+    constexpr int RB = P::RB, NI = P::NI;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
     constexpr int V = vec_elems<T>(W, H * W);
     constexpr int NVX = RH0 * W / V, NVD = TH * W / V;
@@ -540,14 +552,8 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             }
         }
         __syncthreads();
-        // ------------------------------------- P1: base taps, level 1 bands
-        if (grp == 0) {
-            for (int item = gtid; item < NI; item += 256) {
-                const int ti = item / TPR, tj = item - ti * TPR;
-                const int h0 = BR * ti, w0 = BC * tj;
-                taps_tile<KB, BR, BC, SX, P::SD>(X + (G + h0 - PB) * SX + w0, DY + h0 * P::SD + w0, acc0);
-            }
-        }
+        if (u + 1 < u1) issue_loads(u + 1);
+        // ----------------------------------------- P1: level 1 analysis
         {
             constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1);
             for (int q = tid; q < P::rh(1) * W1; q += NT) {
@@ -612,26 +618,29 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
                 pdo[q] = LLv[i * SVL + j];
             }
         }
-        if (u + 1 < u1) issue_loads(u + 1);
-        // --------------------------- P3: level taps, one band per wavefront
+        // ------------------- P3: all taps at once, base taps and one band per wavefront
+        if (grp == 0) {
+            for (int item = gtid; item < NI; item += 256) {
+                const int rb = item / W, w = item - rb * W, h0 = rb * RB;
+                taps_col<KB, RB, SX, P::SD>(X + (G + h0 - PB) * SX + w, DY + h0 * P::SD + w, acc0);
+            }
+        }
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
             constexpr int Gl = G >> l;
-            constexpr Tile tl = P::band_tile(l);
-            constexpr int RR = tl.r, CC = tl.c, TPRl = wl / CC, NIl = (hl / RR) * TPRl;
+            constexpr int R = P::band_rows(l), NIl = (hl / R) * wl;
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
                 constexpr int SVl = P::sv(l);
                 for (int item = lane; item < NIl; item += 64) {
-                    const int ti = item / TPRl, tj = item - ti * TPRl;
+                    const int rs = item / wl, j = item - rs * wl;
                     if constexpr (P::slot_of(l) == 0)
-                        taps_tile<K, RR, CC, Sl, SVl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
-                                                      Vs + RR * ti * SVl + CC * tj, acc0);
+                        taps_col<K, R, Sl, SVl>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j, acc0);
                     else
-                        taps_tile<K, RR, CC, Sl, SVl>(Us + (Gl + RR * ti - PK) * Sl + CC * tj,
-                                                      Vs + RR * ti * SVl + CC * tj, accl[P::slot_of(l) - 1]);
+                        taps_col<K, R, Sl, SVl>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j,
+                                                accl[P::slot_of(l) - 1]);
                 }
             }
         });
@@ -774,30 +783,30 @@ struct BwEntry {
     size_t (*ws)(int B, int C);
 };
 
-typedef BwPlan<32, 32, 2, 5, 5, 2, 2> BP_32_L2_k55;
-typedef BwPlan<56, 56, 3, 5, 5, 4, 4> BP_56_L3_k55;
-typedef BwPlan<28, 28, 2, 5, 5, 2, 2> BP_28_L2_k55;
-typedef BwPlan<14, 14, 1, 5, 5, 1, 1> BP_14_L1_k55;
-typedef BwPlan<32, 32, 3, 7, 5, 2, 2> BP_32_L3_k75;
-typedef BwPlan<24, 40, 3, 3, 3, 2, 2> BP_24x40_L3_k33;
-typedef BwPlan<16, 16, 4, 3, 7, 1, 1> BP_16_L4_k37;
-typedef BwPlan<64, 64, 4, 7, 5, 4, 4> BP_64_L4_k75;
+typedef BwPlan<32, 32, 2, 5, 5> BP_32_L2_k55;
+typedef BwPlan<56, 56, 3, 5, 5> BP_56_L3_k55;
+typedef BwPlan<28, 28, 2, 5, 5> BP_28_L2_k55;
+typedef BwPlan<14, 14, 1, 5, 5> BP_14_L1_k55;
+typedef BwPlan<32, 32, 3, 7, 5> BP_32_L3_k75;
+typedef BwPlan<24, 40, 3, 3, 3> BP_24x40_L3_k33;
+typedef BwPlan<16, 16, 4, 3, 7> BP_16_L4_k37;
+typedef BwPlan<64, 64, 4, 7, 5> BP_64_L4_k75;
 
 // split plans: fine tiles + coarse planes of LL_{L0} sums (no base taps)
-typedef TileBwPlan<128, 128, 1, 1, 5, 5, 16, 2, 4> TB_128_L1_k55;
-typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16, 2, 4> TB_128_L2_k55;
-typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16, 2, 4> TB_128_L2of3_k55;
-typedef TileBwPlan<128, 128, 2, 4, 5, 5, 16, 2, 4> TB_128_L2of4_k55;
-typedef TileBwPlan<128, 128, 2, 5, 5, 5, 16, 2, 4> TB_128_L2of5_k55;
-typedef BwPlan<32, 32, 1, 1, 5, 1, 1> CB_32_L1_k5;
-typedef BwPlan<32, 32, 2, 1, 5, 1, 1> CB_32_L2_k5;
-typedef BwPlan<32, 32, 3, 1, 5, 1, 1> CB_32_L3_k5;
-typedef TileBwPlan<256, 256, 2, 4, 7, 5, 8, 2, 4> TB_256_L2of4_k75;
-typedef BwPlan<64, 64, 2, 1, 5, 1, 1> CB_64_L2_k5;
-typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8, 2, 2> TB_64_L2of4_k33;
-typedef BwPlan<16, 16, 2, 1, 3, 1, 1> CB_16_L2_k3;
-typedef TileBwPlan<64, 64, 1, 2, 5, 5, 16, 2, 2> TB_64_L1of2_k55;
-typedef BwPlan<32, 32, 1, 1, 5, 1, 1> CB_32_L1_k5b;
+typedef TileBwPlan<128, 128, 1, 1, 5, 5, 16> TB_128_L1_k55;
+typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16> TB_128_L2_k55;
+typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16> TB_128_L2of3_k55;
+typedef TileBwPlan<128, 128, 2, 4, 5, 5, 16> TB_128_L2of4_k55;
+typedef TileBwPlan<128, 128, 2, 5, 5, 5, 16> TB_128_L2of5_k55;
+typedef BwPlan<32, 32, 1, 1, 5> CB_32_L1_k5;
+typedef BwPlan<32, 32, 2, 1, 5> CB_32_L2_k5;
+typedef BwPlan<32, 32, 3, 1, 5> CB_32_L3_k5;
+typedef TileBwPlan<256, 256, 2, 4, 7, 5, 8> TB_256_L2of4_k75;
+typedef BwPlan<64, 64, 2, 1, 5> CB_64_L2_k5;
+typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8> TB_64_L2of4_k33;
+typedef BwPlan<16, 16, 2, 1, 3> CB_16_L2_k3;
+typedef TileBwPlan<64, 64, 1, 2, 5, 5, 16> TB_64_L1of2_k55;
+typedef BwPlan<32, 32, 1, 1, 5> CB_32_L1_k5b;
 
 #define WTC_BW_WHOLE(PLAN) \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K, {whole_launch<PLAN, float>, whole_launch<PLAN, bf16_t>}, whole_ws<PLAN>}
