@@ -54,8 +54,8 @@ __device__ __forceinline__ void taps_col(const float* u, const float* v, float (
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Rows per column strip for an h x w grid on `lanes` lanes with k x k taps:
-// the fewest cycles on the busiest lane, counting each strip's R*k*k
+// Rows per column strip for an h x w grid on `lanes` lanes with k x k taps
+// (strip_lanes(w) lanes per row block): the fewest cycles on the busiest lane, counting each strip's R*k*k
 // multiply-adds plus its (R+k-1)*k + R LDS reads at two multiply-adds each
 // (a CU issues one wavefront multiply-add per clock across its four SIMDs
 // but moves only half a wavefront's worth of LDS words per clock).
@@ -63,7 +63,7 @@ constexpr int pick_rows(int h, int w, int lanes, int k) {
     int best = 1, best_cost = 1 << 30;
     for (int r = 1; r <= 16 && r <= h; ++r) {
         if (h % r != 0) continue;
-        const int cost = cdiv((h / r) * w, lanes) * (r * k * k + 2 * ((r + k - 1) * k + r));
+        const int cost = cdiv((h / r) * strip_lanes(w), lanes) * (r * k * k + 2 * ((r + k - 1) * k + r));
         if (cost < best_cost) {
             best = r;
             best_cost = cost;
@@ -78,7 +78,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// H x W plane, L >= 1 levels; BR x BC dy positions per base work item.
+// H x W plane, L >= 1 levels; base strips of RB rows.
 // LDS: x (border KB/2), dy, the bordered x bands U_1..U_L (border K/2) and
 // the unbordered dy bands V_1..V_L all stay resident.
 //
@@ -95,9 +95,14 @@ struct BwPlan {
     static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && L <= 5 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
-    static constexpr int SX = odd_stride(W + 2 * PB);
+    // x rows: interior from column XO (a multiple of 4, at least KB/2), row
+    // stride a multiple of 4, so that streamed rows take aligned 128-bit
+    // stores and 2x2 blocks aligned 64-bit reads; dy rows likewise
+    static constexpr int VL = lds_vec(W);
+    static constexpr int XO = round_up(PB, 4);
+    static constexpr int SX = round_up(XO + W + PB, 4);
     static constexpr int XSIZE = (H + 2 * PB) * SX;
-    static constexpr int SD = odd_stride(W);   // dy rows: odd stride, fewer bank conflicts
+    static constexpr int SD = round_up(W, 4);
     static constexpr int DSIZE = H * SD;
     static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
     static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
@@ -121,7 +126,8 @@ struct BwPlan {
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
-    static constexpr int NI = (H / RB) * W;   // base strips
+    static constexpr int LPB = strip_lanes(W);
+    static constexpr int NI = (H / RB) * LPB;   // base strip slots
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
     static constexpr int band_rows(int l) { return pick_rows(H >> l, W >> l, 64, K); }
     static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
@@ -157,14 +163,15 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                  int C, int bpc) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
-    constexpr int RB = P::RB, NI = P::NI;
+    constexpr int RB = P::RB, NI = P::NI, LPB = P::LPB, XO = P::XO, SD = P::SD;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
-    constexpr int V = vec_elems<T>(W, H * W);
-    constexpr int NV = H * W / V;
+    constexpr int VL = P::VL;
+    constexpr int NV = H * W / VL;
     constexpr int NL = cdiv(NV, NT);
 
     __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS];
     float* X = lds;
+    const float* X0 = X + XO - PB;   // origin of the bordered x plane
     float* DY = X + P::XSIZE;
     float* U = DY + P::DSIZE;
     float* Vb = U + P::UTOT;
@@ -175,7 +182,7 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
 
     // borders stay zero for the whole chunk: nothing writes them
-    zero_border<1, H, W, PB, SX>(X, tid, NT);
+    zero_border<1, H, W, PB, SX, XO>(X, tid, NT);
     P::for_levels([&](auto lc) {
         constexpr int l = decltype(lc)::value;
         zero_border<4, (H >> l), (W >> l), PK, P::su(l)>(U + P::uoff(l), tid, NT);
@@ -190,8 +197,8 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
 #pragma unroll
         for (int t = 0; t < K * K; ++t) accl[j][t] = 0.f;
 
-    // raw global loads of the next plane, issued ahead of the level taps
-    float vx[NL][V], vd[NL][V];
+    // global loads of the next plane, in flight during the current taps
+    RawVec<T, VL> vx[NL], vd[NL];
     auto issue_loads = [&](int b) {
         const size_t plane = (size_t)b * C + c;
         const T* __restrict__ xs = x + plane * H * W;
@@ -200,8 +207,8 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
             if (NV % NT == 0 || q < NV) {
-                load_vec<T, V>(xs + q * V, vx[k]);
-                load_vec<T, V>(ds + q * V, vd[k]);
+                load_raw<T, VL>(xs + q * VL, vx[k]);
+                load_raw<T, VL>(ds + q * VL, vd[k]);
             }
         }
     };
@@ -215,12 +222,9 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
             if (NV % NT == 0 || q < NV) {
-                const int e = q * V, r = e / W, col = e - r * W;
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                    X[(r + PB) * SX + col + PB + i] = vx[k][i];
-                    DY[r * P::SD + col + i] = vd[k][i];
-                }
+                const int e = q * VL, r = e / W, col = e - r * W;
+                store_lds<T, VL>(X + (r + PB) * SX + XO + col, vx[k]);
+                store_lds<T, VL>(DY + r * SD + col, vd[k]);
             }
         }
         __syncthreads();
@@ -228,14 +232,17 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
         if (b + 1 < b1) issue_loads(b + 1);
         // ----------------------------------------- P1: level 1 analysis
         {
-            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1), SD = P::SD;
+            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1);
             for (int q = tid; q < H1 * W1; q += NT) {
                 const int i = q / W1, j = q - i * W1;
-                const float* x2 = X + (PB + 2 * i) * SX + PB + 2 * j;
-                const float* d2 = DY + 2 * i * SD + 2 * j;
+                // 2x2 blocks start on even columns of 8-byte aligned rows
+                const float2 x01 = *reinterpret_cast<const float2*>(X + (PB + 2 * i) * SX + XO + 2 * j);
+                const float2 x23 = *reinterpret_cast<const float2*>(X + (PB + 2 * i + 1) * SX + XO + 2 * j);
+                const float2 d01 = *reinterpret_cast<const float2*>(DY + 2 * i * SD + 2 * j);
+                const float2 d23 = *reinterpret_cast<const float2*>(DY + (2 * i + 1) * SD + 2 * j);
                 float u[4], v[4];
-                haar4(x2[0], x2[1], x2[SX], x2[SX + 1], u[0], u[1], u[2], u[3]);
-                haar4(d2[0], d2[1], d2[SD], d2[SD + 1], v[0], v[1], v[2], v[3]);
+                haar4(x01.x, x01.y, x23.x, x23.y, u[0], u[1], u[2], u[3]);
+                haar4(d01.x, d01.y, d23.x, d23.y, v[0], v[1], v[2], v[3]);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     U[s * BS1 + (PK + i) * S1 + PK + j] = u[s];
@@ -273,20 +280,21 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
         // ------------------- P3: all taps at once, base taps and one band per wavefront
         if (BASE && grp == 0) {
             for (int item = gtid; item < NI; item += 256) {
-                const int rb = item / W, w = item - rb * W, h0 = rb * RB;
-                taps_col<KB, RB, SX, P::SD>(X + h0 * SX + w, DY + h0 * P::SD + w, acc0);
+                const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
+                if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + h0 * SX + w, DY + h0 * SD + w, acc0);
             }
         }
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-            constexpr int R = P::band_rows(l), NIl = (hl / R) * wl;
+            constexpr int R = P::band_rows(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
                 constexpr int SVl = P::sv(l);
                 for (int item = lane; item < NIl; item += 64) {
-                    const int rs = item / wl, j = item - rs * wl;
+                    const int rs = item / LPl, j = item - rs * LPl;
+                    if (!(LPl == wl || j < wl)) continue;
                     if constexpr (P::slot_of(l) == 0)
                         taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, acc0);
                     else
@@ -407,9 +415,12 @@ struct TileBwPlan {
     static constexpr int G0 = PB > (PK << L0) ? PB : (PK << L0);
     static constexpr int G = cdiv(G0, BLK) * BLK;
     static constexpr int RH0 = TH + 2 * G;
-    static constexpr int SX = odd_stride(W + 2 * PB);
+    // row layout as in BwPlan: aligned interiors for vector stores and reads
+    static constexpr int VL = lds_vec(W);
+    static constexpr int XO = round_up(PB, 4);
+    static constexpr int SX = round_up(XO + W + PB, 4);
     static constexpr int XSIZE = RH0 * SX;
-    static constexpr int SD = odd_stride(W);
+    static constexpr int SD = round_up(W, 4);
     static constexpr int DSIZE = TH * SD;
     static constexpr int rh(int l) { return RH0 >> l; }
     static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
@@ -433,7 +444,8 @@ struct TileBwPlan {
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "tile does not fit in LDS");
-    static constexpr int NI = (TH / RB) * W;
+    static constexpr int LPB = strip_lanes(W);
+    static constexpr int NI = (TH / RB) * LPB;
     static constexpr int NTILE = H / TH;
     static constexpr int TAPS = KB * KB + 4 * L0 * K * K;
     static constexpr int band_rows(int l) { return pick_rows(TH >> l, W >> l, 64, K); }
@@ -462,14 +474,15 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
                       float* __restrict__ px, float* __restrict__ pdy, int B, int C, int upc) {
     constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, G = P::G, RH0 = P::RH0, W1 = W / 2;
-    constexpr int RB = P::RB, NI = P::NI;
+    constexpr int RB = P::RB, NI = P::NI, LPB = P::LPB, XO = P::XO, SD = P::SD;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
-    constexpr int V = vec_elems<T>(W, H * W);
-    constexpr int NVX = RH0 * W / V, NVD = TH * W / V;
+    constexpr int VL = P::VL;
+    constexpr int NVX = RH0 * W / VL, NVD = TH * W / VL;
     constexpr int NLX = cdiv(NVX, NT), NLD = cdiv(NVD, NT);
 
     __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS];
     float* X = lds;
+    const float* X0 = X + XO - PB;   // origin of the bordered x rows
     float* DY = X + P::XSIZE;
     float* U = DY + P::DSIZE;
     float* Vb = U + P::UTOT;
@@ -483,7 +496,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
     // border columns stay zero: loads and analyses write interior columns only
     for (int i = tid; i < RH0 * (SX - W); i += NT) {
         const int r = i / (SX - W), q = i - r * (SX - W);
-        X[r * SX + (q < PB ? q : q + W)] = 0.f;
+        X[r * SX + (q < XO ? q : q + W)] = 0.f;
     }
     P::for_levels([&](auto lc) {
         constexpr int l = decltype(lc)::value;
@@ -505,7 +518,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 #pragma unroll
         for (int t = 0; t < K * K; ++t) accl[j][t] = 0.f;
 
-    float vx[NLX][V], vd[NLD][V];
+    RawVec<T, VL> vx[NLX], vd[NLD];
     auto issue_loads = [&](int u) {
         const int b = u / P::NTILE, r0 = (u - b * P::NTILE) * TH;
         const size_t plane = (size_t)b * C + c;
@@ -514,17 +527,17 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 #pragma unroll
         for (int k = 0; k < NLX; ++k) {
             const int q = tid + k * NT;
-            const int e = q * V, rr = e / W, pr = r0 - G + rr;
+            const int e = q * VL, rr = e / W, pr = r0 - G + rr;
             if ((NVX % NT == 0 || q < NVX) && pr >= 0 && pr < H)
-                load_vec<T, V>(xs + (size_t)pr * W + (e - rr * W), vx[k]);
+                load_raw<T, VL>(xs + (size_t)pr * W + (e - rr * W), vx[k]);
             else
 #pragma unroll
-                for (int i = 0; i < V; ++i) vx[k][i] = 0.f;
+                for (int i = 0; i < RawVec<T, VL>::N; ++i) vx[k].w[i] = 0u;   // rows outside the plane: zeros
         }
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int q = tid + k * NT;
-            if (NVD % NT == 0 || q < NVD) load_vec<T, V>(ds + (size_t)r0 * W + q * V, vd[k]);
+            if (NVD % NT == 0 || q < NVD) load_raw<T, VL>(ds + (size_t)r0 * W + q * VL, vd[k]);
         }
     };
     if (u0 < u1) issue_loads(u0);
@@ -537,18 +550,16 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
         for (int k = 0; k < NLX; ++k) {
             const int q = tid + k * NT;
             if (NVX % NT == 0 || q < NVX) {
-                const int e = q * V, rr = e / W, col = e - rr * W;
-#pragma unroll
-                for (int i = 0; i < V; ++i) X[rr * SX + col + PB + i] = vx[k][i];
+                const int e = q * VL, rr = e / W, col = e - rr * W;
+                store_lds<T, VL>(X + rr * SX + XO + col, vx[k]);
             }
         }
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int q = tid + k * NT;
             if (NVD % NT == 0 || q < NVD) {
-                const int e = q * V, rr = e / W, col = e - rr * W;
-#pragma unroll
-                for (int i = 0; i < V; ++i) DY[rr * P::SD + col + i] = vd[k][i];
+                const int e = q * VL, rr = e / W, col = e - rr * W;
+                store_lds<T, VL>(DY + rr * SD + col, vd[k]);
             }
         }
         __syncthreads();
@@ -558,18 +569,20 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1);
             for (int q = tid; q < P::rh(1) * W1; q += NT) {
                 const int i = q / W1, j = q - i * W1;
-                const float* x2 = X + (2 * i) * SX + PB + 2 * j;
+                const float2 a = *reinterpret_cast<const float2*>(X + (2 * i) * SX + XO + 2 * j);
+                const float2 c2 = *reinterpret_cast<const float2*>(X + (2 * i + 1) * SX + XO + 2 * j);
                 float uu[4];
-                haar4(x2[0], x2[1], x2[SX], x2[SX + 1], uu[0], uu[1], uu[2], uu[3]);
+                haar4(a.x, a.y, c2.x, c2.y, uu[0], uu[1], uu[2], uu[3]);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) U[s * BS1 + i * S1 + PK + j] = uu[s];
             }
-            constexpr int SD = P::SD, SV1 = P::sv(1);
+            constexpr int SV1 = P::sv(1);
             for (int q = tid; q < (TH / 2) * W1; q += NT) {
                 const int i = q / W1, j = q - i * W1;
-                const float* d2 = DY + 2 * i * SD + 2 * j;
+                const float2 a = *reinterpret_cast<const float2*>(DY + 2 * i * SD + 2 * j);
+                const float2 c2 = *reinterpret_cast<const float2*>(DY + (2 * i + 1) * SD + 2 * j);
                 float vv[4];
-                haar4(d2[0], d2[1], d2[SD], d2[SD + 1], vv[0], vv[1], vv[2], vv[3]);
+                haar4(a.x, a.y, c2.x, c2.y, vv[0], vv[1], vv[2], vv[3]);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) Vb[s * VS1 + i * SV1 + j] = vv[s];
             }
@@ -621,21 +634,22 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
         // ------------------- P3: all taps at once, base taps and one band per wavefront
         if (grp == 0) {
             for (int item = gtid; item < NI; item += 256) {
-                const int rb = item / W, w = item - rb * W, h0 = rb * RB;
-                taps_col<KB, RB, SX, P::SD>(X + (G + h0 - PB) * SX + w, DY + h0 * P::SD + w, acc0);
+                const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
+                if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + (G + h0 - PB) * SX + w, DY + h0 * SD + w, acc0);
             }
         }
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
             constexpr int Gl = G >> l;
-            constexpr int R = P::band_rows(l), NIl = (hl / R) * wl;
+            constexpr int R = P::band_rows(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
                 constexpr int SVl = P::sv(l);
                 for (int item = lane; item < NIl; item += 64) {
-                    const int rs = item / wl, j = item - rs * wl;
+                    const int rs = item / LPl, j = item - rs * LPl;
+                    if (!(LPl == wl || j < wl)) continue;
                     if constexpr (P::slot_of(l) == 0)
                         taps_col<K, R, Sl, SVl>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j, acc0);
                     else

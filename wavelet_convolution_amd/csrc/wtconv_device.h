@@ -93,6 +93,69 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&out)[V
     }
 }
 
+// Elements per lane when a plane is streamed into LDS: 4 when rows hold
+// whole groups of four (one 128-bit LDS store per lane; consecutive lanes
+// fill consecutive 16-byte words, which no two lanes of a pass share a bank
+// in), else 2, else 1.
+constexpr int lds_vec(int W) { return W % 4 == 0 ? 4 : (W % 2 == 0 ? 2 : 1); }
+
+constexpr int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// V activations as loaded from HBM, still in their storage format (bf16
+// pairs stay packed: half the registers while a load is in flight).
+template <typename T, int V>
+struct RawVec {
+    static constexpr int N = (V * Act<T>::BYTES + 3) / 4;
+    uint32_t w[N];
+};
+
+template <typename T, int V>
+__device__ __forceinline__ void load_raw(const T* __restrict__ p, RawVec<T, V>& r) {
+    constexpr int BYTES = V * Act<T>::BYTES;
+    if constexpr (BYTES == 16) {
+        const uint4 q = *reinterpret_cast<const uint4*>(p);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+        r.w[2] = q.z;
+        r.w[3] = q.w;
+    } else if constexpr (BYTES == 8) {
+        const uint2 q = *reinterpret_cast<const uint2*>(p);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+    } else if constexpr (BYTES == 4) {
+        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+        r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+}
+
+// Widen to fp32 and store at p (aligned to 4 * V bytes).
+template <typename T, int V>
+__device__ __forceinline__ void store_lds(float* p, const RawVec<T, V>& r) {
+    float f[V];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) f[i] = __uint_as_float(i % 2 == 0 ? r.w[i / 2] << 16 : r.w[i / 2] & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) f[i] = __uint_as_float(r.w[i]);
+    }
+    if constexpr (V == 4) *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    else if constexpr (V == 2) *reinterpret_cast<float2*>(p) = make_float2(f[0], f[1]);
+    else p[0] = f[0];
+}
+
+// Lanes given to one row block of column strips over a row of w columns:
+// whole wavefronts when w > 32, else the next power of two, so that the 32
+// lanes of one LDS pass never straddle two row blocks (w >= 32) or cover
+// whole aligned groups of them (w < 32). Lanes past w idle.
+constexpr int strip_lanes(int w) {
+    if (w > 32) return round_up(w, 64);
+    int p = 1;
+    while (p < w) p *= 2;
+    return p;
+}
+
 // Store a row segment of N fp32 values (N even for bf16; the segment start
 // is 4-byte aligned for bf16 and 8-byte aligned for fp32 pairs).
 template <int N>
@@ -218,13 +281,21 @@ __device__ __forceinline__ void conv_col(const float* s, const float* w, float (
 }
 
 // Zero the border cells of NB bordered planes of interior h x w, border B,
-// row stride S (everything outside rows [B, B+h) x cols [B, B+w)).
-template <int NB, int h, int w, int B, int S>
+// row stride S (everything outside rows [B, B+h) x cols [CO, CO+w); the
+// interior starts at column CO, B by default).
+template <int NB, int h, int w, int B, int S, int CO = B>
 __device__ __forceinline__ void zero_border(float* base, int tid, int nt) {
     constexpr int ROWS = h + 2 * B;
     constexpr int TOPBOT = 2 * B * S;
     constexpr int SIDE = S - w;
     constexpr int PER = TOPBOT + h * SIDE;
+    if constexpr (PER == 0 || SIDE == 0) {   // no border columns
+        for (int i = tid; i < NB * TOPBOT; i += nt) {
+            const int b = i / (TOPBOT > 0 ? TOPBOT : 1), j = i - b * TOPBOT, r0 = j / S;
+            base[b * ROWS * S + (r0 >= B ? r0 + h : r0) * S + (j - r0 * S)] = 0.f;
+        }
+        return;
+    }
     for (int i = tid; i < NB * PER; i += nt) {
         const int b = i / PER;
         int j = i - b * PER, r, c;
@@ -236,7 +307,7 @@ __device__ __forceinline__ void zero_border(float* base, int tid, int nt) {
             j -= TOPBOT;
             r = B + j / SIDE;
             c = j % SIDE;
-            if (c >= B) c += w;
+            if (c >= CO) c += w;
         }
         base[b * ROWS * S + r * S + c] = 0.f;
     }
