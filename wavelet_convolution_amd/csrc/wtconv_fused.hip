@@ -35,8 +35,8 @@ static hipError_t launch_col(const void* in, const float* wb, const float* wl, c
      (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT}
 
 static const PlaneEntry kPlaneEntries[] = {
-#if WTC_COL56
-    WTC_COL_ENTRY(CP_56_L3_k55),
+#if WTC_COLS
+    WTC_COL_ENTRIES(WTC_COL_ENTRY),
 #endif
     WTC_PLANE_ENTRIES(WTC_PLANE_ENTRY)
 };

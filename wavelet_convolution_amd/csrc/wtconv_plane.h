@@ -278,7 +278,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT, RB = P::RB;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
     constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
-    constexpr int NIB = P::NIB, MB = P::MB;
+    constexpr int NIB = P::NIB, MB = P::MB, LPB = P::LPB, XO = P::XO, VL = P::VL;
     constexpr int KB2P = P::KB2P, K2P = P::K2P;
 
     __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
@@ -308,29 +308,29 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
         WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
     }
-    zero_border<1, H, W, PB, SX>(A, tid, NT);
+    zero_border<1, H, W, PB, SX, XO>(A, tid, NT);
     zero_border<4, H1, W1, PK, S1>(Bq, tid, NT);
     {
-        constexpr int V = vec_elems<T>(W, H * W);
-        constexpr int NV = H * W / V;
+        // VL elements per lane, one aligned vector store each
+        constexpr int NV = H * W / VL;
         constexpr int NL = cdiv(NV, NT);
-        float v[NL][V];
+        RawVec<T, VL> v[NL];
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) load_vec<T, V>(src + q * V, v[k]);
+            if (NV % NT == 0 || q < NV) load_raw<T, VL>(src + q * VL, v[k]);
         }
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
             if (NV % NT == 0 || q < NV) {
-                const int e = q * V, r = e / W, col = e - r * W;
-#pragma unroll
-                for (int i = 0; i < V; ++i) A[(r + PB) * SX + col + PB + i] = v[k][i];
+                const int e = q * VL, r = e / W, col = e - r * W;
+                store_lds<T, VL>(A + (r + PB) * SX + XO + col, v[k]);
             }
         }
     }
     __syncthreads();
+    const float* X0 = A + XO - PB;   // origin of the bordered x plane
 
     // ---------------------------------------------------------------- P1
     float yb[MB][RB];
@@ -338,15 +338,17 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     for (int it = 0; it < MB; ++it) {
         const int item = tid + it * NT;
         if (NIB % NT == 0 || item < NIB) {
-            const int rb = item / W, w = item - rb * W;
-            conv_col<KB, RB, SX>(A + (rb * RB) * SX + w, WB, yb[it]);
+            const int rb = item / LPB, w = item - rb * LPB;
+            if (LPB == W || w < W) conv_col<KB, RB, SX>(X0 + (rb * RB) * SX + w, WB, yb[it]);
         }
     }
     for (int q = tid; q < H1 * W1; q += NT) {
         const int i = q / W1, j = q - i * W1;
-        const float* x2 = A + (PB + 2 * i) * SX + PB + 2 * j;
+        // 2x2 blocks start on even columns of 8-byte aligned rows
+        const float2 x01 = *reinterpret_cast<const float2*>(A + (PB + 2 * i) * SX + XO + 2 * j);
+        const float2 x23 = *reinterpret_cast<const float2*>(A + (PB + 2 * i + 1) * SX + XO + 2 * j);
         float b[4];
-        haar4(x2[0], x2[1], x2[SX], x2[SX + 1], b[0], b[1], b[2], b[3]);
+        haar4(x01.x, x01.y, x23.x, x23.y, b[0], b[1], b[2], b[3]);
         const int o = (PK + i) * S1 + PK + j;
 #pragma unroll
         for (int s = 0; s < 4; ++s) Bq[s * BS1 + o] = b[s];
@@ -378,29 +380,31 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     auto level_conv = [&](auto lc, auto& z) {
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
-        constexpr int NS = hl / R, NIl = P::nil(l), MIl = cdiv(NIl, NT);
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NIl, NT);
         float* Ul = ubase(lc);
 #pragma unroll
         for (int it = 0; it < MIl; ++it) {
             const int item = tid + it * NT;
             if (NIl % NT == 0 || item < NIl) {
-                const int s = item / (NS * wl), rem = item - s * (NS * wl);
-                const int rs = rem / wl, j = rem - rs * wl;
-                conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z[it]);
+                const int s = item / (NS * LP), rem = item - s * (NS * LP);
+                const int rs = rem / LP, j = rem - rs * LP;
+                if (LP == wl || j < wl)
+                    conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z[it]);
             }
         }
     };
     auto level_store = [&](auto lc, auto& z) {
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
-        constexpr int NS = hl / R, NIl = P::nil(l), MIl = cdiv(NIl, NT);
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NIl, NT);
         float* Ul = ubase(lc);
 #pragma unroll
         for (int it = 0; it < MIl; ++it) {
             const int item = tid + it * NT;
             if (NIl % NT == 0 || item < NIl) {
-                const int s = item / (NS * wl), rem = item - s * (NS * wl);
-                const int rs = rem / wl, j = rem - rs * wl;
+                const int s = item / (NS * LP), rem = item - s * (NS * LP);
+                const int rs = rem / LP, j = rem - rs * LP;
+                if (!(LP == wl || j < wl)) continue;
 #pragma unroll
                 for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = z[it][o];
             }
@@ -432,25 +436,36 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     for (int it = 0; it < MB; ++it) {
         const int item = tid + it * NT;
         if (!(NIB % NT == 0 || item < NIB)) continue;
-        const int rb = item / W, w = item - rb * W, h0 = rb * RB;
+        const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
+        if (!(LPB == W || w < W)) continue;
         float y[RB];
 #pragma unroll
         for (int o = 0; o < RB; ++o) y[o] = yb[it][o];
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
-            constexpr int Sl = P::su(l), BSl = P::bandsz(l), NP = RB >> l;
-            // strips start on a 2^L row boundary: the row bits below L are the
-            // strip-relative ones, known at compile time
+            constexpr int Sl = P::su(l), BSl = P::bandsz(l);
             const float* Zl = ubase(lc) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
             const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
+            if constexpr (RB % (1 << l) == 0) {
+                // whole 2^l-row blocks: the row bits below l are strip-relative
+                // and known at compile time
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const float* z = Zl + p * Sl;
-                const float a = __builtin_fmaf(sw, z[2 * BSl], z[0]);
-                const float b = __builtin_fmaf(sw, z[3 * BSl], z[BSl]);
-                const float plus = a + b, minus = a - b;
+                for (int p = 0; p < (RB >> l); ++p) {
+                    const float* z = Zl + p * Sl;
+                    const float a = __builtin_fmaf(sw, z[2 * BSl], z[0]);
+                    const float b = __builtin_fmaf(sw, z[3 * BSl], z[BSl]);
+                    const float plus = a + b, minus = a - b;
 #pragma unroll
-                for (int o = p << l; o < (p + 1) << l; ++o) y[o] += ((o >> (l - 1)) & 1) ? minus : plus;
+                    for (int o = p << l; o < (p + 1) << l; ++o) y[o] += ((o >> (l - 1)) & 1) ? minus : plus;
+                }
+            } else {
+                // the strip lies inside one 2^l-row block and shares its row
+                // bit l-1 (RB is a power of two below 2^l)
+                const float a = __builtin_fmaf(sw, Zl[2 * BSl], Zl[0]);
+                const float b = __builtin_fmaf(sw, Zl[3 * BSl], Zl[BSl]);
+                const float v = ((h0 >> (l - 1)) & 1) ? a - b : a + b;
+#pragma unroll
+                for (int o = 0; o < RB; ++o) y[o] += v;
             }
         });
 #pragma unroll

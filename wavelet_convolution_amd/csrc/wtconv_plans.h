@@ -143,16 +143,27 @@ namespace wtc {
 // column of the base convolution, and RL rows x 1 column of one band at each
 // level, so the lanes of a wavefront read consecutive LDS words (no bank
 // conflicts) and write consecutive output columns. The level results go
-// through LDS and one closed-form pass synthesises every output.
-template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_>
+// through LDS and one closed-form pass synthesises every output. Strips of
+// a row block get strip_lanes(width) lanes (whole half-wavefronts or
+// aligned groups), the rest idle.
+//
+// Base strips start on RB-row boundaries. The synthesis needs, for each
+// level l, either whole 2^l-row blocks per strip (RB a multiple of 2^l) or a
+// strip inside one block whose row bit l-1 is constant (RB a power of two
+// below 2^l): RB is a multiple of 2^L or a power of two.
+template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_, int WMAX_ = 8>
 struct ColPlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, NT = NT_, RB = RB_, RL = RL_;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
     static_assert(H % RB == 0, "base strips must divide the plane");
-    static_assert(RB % (1 << L) == 0, "base strips start on 2^L row boundaries");
+    static_assert(RB % (1 << L) == 0 || (RB & (RB - 1)) == 0, "base strips: a multiple of 2^L rows or a power of two");
     static_assert(NT % 64 == 0 && NT <= 1024, "whole wavefronts");
-    static constexpr int SX = odd_stride(W + 2 * PB);
+    // x rows: interior from column XO (a multiple of 4, at least KB/2), row
+    // stride a multiple of 4: streamed rows take aligned 128-bit stores
+    static constexpr int VL = lds_vec(W);
+    static constexpr int XO = round_up(PB, 4);
+    static constexpr int SX = round_up(XO + W + PB, 4);
     static constexpr int XSIZE = (H + 2 * PB) * SX;
     static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
     static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
@@ -168,15 +179,19 @@ struct ColPlan {
     static constexpr int KB2P = kpad4(KB), K2P = kpad4(K);
     static constexpr int WFLOATS = KB2P + 4 * L * K2P;
     static_assert((LDS_FLOATS + WFLOATS) * 4 <= 160 * 1024, "plane does not fit in LDS");
-    static constexpr int NIB = (H / RB) * W;       // base strips
+    static constexpr int LPB = strip_lanes(W);
+    static constexpr int NIB = (H / RB) * LPB;   // base strip slots
     static constexpr int MB = cdiv(NIB, NT);
-    // rows per strip at level l
+    // rows per strip at level l, lanes per row block, strip slots (4 bands)
     static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
-    static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * (W >> l); }
+    static constexpr int lpl(int l) { return strip_lanes(W >> l); }
+    static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * lpl(l); }
+    // occupancy the LDS footprint allows, at most WMAX waves per SIMD (a
+    // plan whose registers need more than 512 / WMAX lowers WMAX)
     static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
     static constexpr int WAVES_PER_EU_LDS = (WG_PER_CU * (NT / 64)) / 4;
     static constexpr int WAVES_PER_EU =
-        WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > 8 ? 8 : WAVES_PER_EU_LDS);
+        WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > WMAX_ ? WMAX_ : WAVES_PER_EU_LDS);
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -200,8 +215,21 @@ struct ColPlan {
 
 namespace wtc {
 // column-strip plans (listed ahead of the tile plans of the same shape)
-#ifndef WTC_COL56
-#define WTC_COL56 1
+#ifndef WTC_COLS
+#define WTC_COLS 1
 #endif
-typedef ColPlan<56, 56, 3, 5, 5, 448, 8, 7> CP_56_L3_k55;
+#ifndef WTC_COL56_NT
+#define WTC_COL56_NT 512
+#endif
+typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, 7> CP_56_L3_k55;
+typedef ColPlan<28, 28, 2, 5, 5, 256, 4, 7> CP_28_L2_k55;
+typedef ColPlan<14, 14, 1, 5, 5, 128, 2, 7> CP_14_L1_k55;
+typedef ColPlan<128, 128, 1, 5, 5, 1024, 8, 8> CP_128_L1_k55;
+typedef ColPlan<128, 128, 2, 5, 5, 1024, 8, 8> CP_128_L2_k55;
+typedef ColPlan<128, 128, 3, 5, 5, 1024, 8, 8> CP_128_L3_k55;
+typedef ColPlan<128, 128, 4, 5, 5, 1024, 8, 8> CP_128_L4_k55;
+typedef ColPlan<128, 128, 5, 5, 5, 1024, 8, 8> CP_128_L5_k55;
+#define WTC_COL_ENTRIES(X)                                                                     \
+    X(CP_56_L3_k55), X(CP_28_L2_k55), X(CP_14_L1_k55), X(CP_128_L1_k55), X(CP_128_L2_k55),     \
+        X(CP_128_L3_k55), X(CP_128_L4_k55), X(CP_128_L5_k55)
 }  // namespace wtc
