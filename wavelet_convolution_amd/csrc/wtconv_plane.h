@@ -308,25 +308,31 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
         WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
     }
-    zero_border<1, H, W, PB, SX, XO>(A, tid, NT);
-    zero_border<4, H1, W1, PK, S1>(Bq, tid, NT);
     {
-        // VL elements per lane, one aligned vector store each
-        constexpr int NV = H * W / VL;
-        constexpr int NL = cdiv(NV, NT);
+        // The whole bordered x plane in VL-element units, one aligned vector
+        // store each: units inside the plane carry x, the rest zeros (the
+        // border the base convolution reads).
+        constexpr int UPR = SX / VL, NU = (H + 2 * PB) * UPR;
+        constexpr int NL = cdiv(NU, NT);
         RawVec<T, VL> v[NL];
+        auto inside = [&](int q, int& e) {
+            const int r = q / UPR, col = (q - r * UPR) * VL - XO, h = r - PB;
+            e = h * W + col;
+            return h >= 0 && h < H && col >= 0 && col < W;
+        };
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) load_raw<T, VL>(src + q * VL, v[k]);
+            int e;
+            if ((NU % NT == 0 || q < NU) && inside(q, e)) load_raw<T, VL>(src + e, v[k]);
+            else
+#pragma unroll
+                for (int i = 0; i < RawVec<T, VL>::N; ++i) v[k].w[i] = 0u;
         }
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) {
-                const int e = q * VL, r = e / W, col = e - r * W;
-                store_lds<T, VL>(A + (r + PB) * SX + XO + col, v[k]);
-            }
+            if (NU % NT == 0 || q < NU) store_lds<T, VL>(A + q * VL, v[k]);
         }
     }
     __syncthreads();
@@ -342,16 +348,22 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             if (LPB == W || w < W) conv_col<KB, RB, SX>(X0 + (rb * RB) * SX + w, WB, yb[it]);
         }
     }
-    for (int q = tid; q < H1 * W1; q += NT) {
-        const int i = q / W1, j = q - i * W1;
-        // 2x2 blocks start on even columns of 8-byte aligned rows
-        const float2 x01 = *reinterpret_cast<const float2*>(A + (PB + 2 * i) * SX + XO + 2 * j);
-        const float2 x23 = *reinterpret_cast<const float2*>(A + (PB + 2 * i + 1) * SX + XO + 2 * j);
-        float b[4];
-        haar4(x01.x, x01.y, x23.x, x23.y, b[0], b[1], b[2], b[3]);
-        const int o = (PK + i) * S1 + PK + j;
+    // level-1 bands over their bordered grid: zeros on the border
+    {
+        constexpr int GW = W1 + 2 * PK, GN = (H1 + 2 * PK) * GW;
+        for (int q = tid; q < GN; q += NT) {
+            const int ii = q / GW, jj = q - ii * GW, i = ii - PK, j = jj - PK;
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            if (i >= 0 && i < H1 && j >= 0 && j < W1) {
+                // 2x2 blocks start on even columns of 8-byte aligned rows
+                const float2 x01 = *reinterpret_cast<const float2*>(A + (PB + 2 * i) * SX + XO + 2 * j);
+                const float2 x23 = *reinterpret_cast<const float2*>(A + (PB + 2 * i + 1) * SX + XO + 2 * j);
+                haar4(x01.x, x01.y, x23.x, x23.y, b[0], b[1], b[2], b[3]);
+            }
+            const int o = ii * S1 + jj;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Bq[s * BS1 + o] = b[s];
+            for (int s = 0; s < 4; ++s) Bq[s * BS1 + o] = b[s];
+        }
     }
     __syncthreads();
 
@@ -362,13 +374,16 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         constexpr int Sp = P::su(l - 1);
         float* Ul = A + P::uoff(l);
         const float* LLp = (l == 2) ? (Bq + PK * Sp + PK) : (A + P::uoff(l - 1) + PK * Sp + PK);
-        zero_border<4, hl, wl, PK, Sl>(Ul, tid, NT);
-        for (int q = tid; q < hl * wl; q += NT) {
-            const int i = q / wl, j = q - i * wl;
-            const float* x2 = LLp + 2 * i * Sp + 2 * j;
-            float b[4];
-            haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], b[0], b[1], b[2], b[3]);
-            const int o = (PK + i) * Sl + PK + j;
+        // over the bordered grid: zeros on the border
+        constexpr int GW = wl + 2 * PK, GN = (hl + 2 * PK) * GW;
+        for (int q = tid; q < GN; q += NT) {
+            const int ii = q / GW, jj = q - ii * GW, i = ii - PK, j = jj - PK;
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            if (i >= 0 && i < hl && j >= 0 && j < wl) {
+                const float* x2 = LLp + 2 * i * Sp + 2 * j;
+                haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], b[0], b[1], b[2], b[3]);
+            }
+            const int o = ii * Sl + jj;
 #pragma unroll
             for (int s = 0; s < 4; ++s) Ul[s * BSl + o] = b[s];
         }
