@@ -30,24 +30,37 @@ namespace wtc {
 // column strip of dy-side values against its window of x-side values. Lanes
 // of a wavefront take consecutive columns: every load is a run of
 // consecutive LDS words across the wavefront, free of bank conflicts.
+#ifndef WTC_TAPS_AHEAD
+#define WTC_TAPS_AHEAD 1
+#endif
 template <int K, int R, int SU, int SV, int NA>
 __device__ __forceinline__ void taps_col(const float* u, const float* v, float (&acc)[NA]) {
     static_assert(NA >= K * K, "accumulator slot too small");
+    constexpr int NR = R + K - 1;       // window rows
+    constexpr int D = WTC_TAPS_AHEAD;   // rows requested ahead of their use
     __builtin_amdgcn_sched_barrier(0);
     float vt[R];
 #pragma unroll
     for (int o = 0; o < R; ++o) vt[o] = v[o * SV];
+    // a ring of D + 1 window rows: row r + D is requested before row r's
+    // multiply-adds, so LDS latency hides behind D rows of them
+    float win[D + 1][K];
 #pragma unroll
-    for (int r = 0; r < R + K - 1; ++r) {
-        float win[K];
+    for (int r = 0; r < D && r < NR; ++r)
 #pragma unroll
-        for (int n = 0; n < K; ++n) win[n] = u[r * SU + n];
+        for (int n = 0; n < K; ++n) win[r][n] = u[r * SU + n];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (r + D < NR) {
+#pragma unroll
+            for (int n = 0; n < K; ++n) win[(r + D) % (D + 1)][n] = u[(r + D) * SU + n];
+        }
 #pragma unroll
         for (int o = 0; o < R; ++o) {
             const int m = r - o;
             if (m < 0 || m >= K) continue;
 #pragma unroll
-            for (int n = 0; n < K; ++n) acc[m * K + n] = __builtin_fmaf(vt[o], win[n], acc[m * K + n]);
+            for (int n = 0; n < K; ++n) acc[m * K + n] = __builtin_fmaf(vt[o], win[r % (D + 1)][n], acc[m * K + n]);
         }
     }
     pin_regs(acc);
@@ -70,6 +83,13 @@ constexpr int pick_rows(int h, int w, int lanes, int k) {
         }
     }
     return best;
+}
+
+// One butterfly stage across lanes: the pair (lane, lane ^ mask) holding
+// (a, b) ends with a + b on the first lane and a - b on the second.
+__device__ __forceinline__ float haar_pair(float own, int mask, bool second) {
+    const float p = __shfl_xor(own, mask, 64);
+    return second ? p - own : own + p;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -130,6 +150,16 @@ struct BwPlan {
     static constexpr int NI = (H / RB) * LPB;   // base strip slots
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
     static constexpr int band_rows(int l) { return pick_rows(H >> l, W >> l, 64, K); }
+    // Analysis lanes: each owns 2 rows x CW columns of x and dy. The lanes
+    // of one 2^L x 2^L block form a group of GS = BR x BC (BR row pairs,
+    // BC column slices, row pair fastest) inside one wavefront.
+    static constexpr int CW = W % 4 == 0 ? 4 : 2;
+    static constexpr int NC = W / CW, NA = (H / 2) * NC;
+    static constexpr int BR = L >= 2 ? 1 << (L - 1) : 1;
+    static constexpr int BC = L >= 2 ? (CW == 4 ? 1 << (L - 2) : 1 << (L - 1)) : 1;
+    static constexpr int GS = BR * BC, NBC = NC / BC;
+    static_assert(NA <= NT, "one analysis lane per 2 x CW block of the plane");
+    static_assert(64 % GS == 0, "a block's analysis lanes share a wavefront");
     static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
     static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
     // registers bound the occupancy too: each lane holds its tap slots plus
@@ -162,12 +192,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::WAVES_PE
 void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part, int B,
                  int C, int bpc) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
-    constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
+    constexpr int PB = P::PB, PK = P::PK, SX = P::SX;
     constexpr int RB = P::RB, NI = P::NI, LPB = P::LPB, XO = P::XO, SD = P::SD;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
-    constexpr int VL = P::VL;
-    constexpr int NV = H * W / VL;
-    constexpr int NL = cdiv(NV, NT);
 
     __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS];
     float* X = lds;
@@ -197,19 +224,24 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
 #pragma unroll
         for (int t = 0; t < K * K; ++t) accl[j][t] = 0.f;
 
+    // Stream-in and the whole Haar analysis in registers: analysis lane
+    // a < NA owns rows 2r, 2r+1 and columns CW q .. CW q + CW-1 of x and dy.
+    // Level 1 comes from its own values; each deeper level combines the
+    // 2x2 blocks of the level above across lanes with xor shuffles.
+    constexpr int CW = P::CW, NA = P::NA, BR = P::BR, BC = P::BC, GS = P::GS, NBC = P::NBC, NP = CW / 2;
+    const int a_lb = tid % GS, a_blk = tid / GS;
+    const int a_rb = a_lb % BR, a_cb = a_lb / BR;
+    const int a_r = (a_blk / NBC) * BR + a_rb, a_q = (a_blk % NBC) * BC + a_cb;
+
     // global loads of the next plane, in flight during the current taps
-    RawVec<T, VL> vx[NL], vd[NL];
+    RawVec<T, CW> vx[2], vd[2];
     auto issue_loads = [&](int b) {
-        const size_t plane = (size_t)b * C + c;
-        const T* __restrict__ xs = x + plane * H * W;
-        const T* __restrict__ ds = dy + plane * H * W;
-#pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) {
-                load_raw<T, VL>(xs + q * VL, vx[k]);
-                load_raw<T, VL>(ds + q * VL, vd[k]);
-            }
+        if (tid < NA) {
+            const size_t off = ((size_t)b * C + c) * H * W + (size_t)(2 * a_r) * W + CW * a_q;
+            load_raw<T, CW>(x + off, vx[0]);
+            load_raw<T, CW>(x + off + W, vx[1]);
+            load_raw<T, CW>(dy + off, vd[0]);
+            load_raw<T, CW>(dy + off + W, vd[1]);
         }
     };
     if (b0 < b1) issue_loads(b0);
@@ -217,66 +249,78 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     for (int b = b0; b < b1; ++b) {
         // the previous plane's taps read x, dy and the bands: all done first
         if (b > b0) __syncthreads();
-        // ------------------------------------------------ P0: stream in
-#pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            const int q = tid + k * NT;
-            if (NV % NT == 0 || q < NV) {
-                const int e = q * VL, r = e / W, col = e - r * W;
-                store_lds<T, VL>(X + (r + PB) * SX + XO + col, vx[k]);
-                store_lds<T, VL>(DY + r * SD + col, vd[k]);
+        // ------------------------------------ P0: stream in and analyse
+        if (tid < NA) {
+            float xv[2][CW], dv[2][CW];
+            widen_raw(vx[0], xv[0]);
+            widen_raw(vx[1], xv[1]);
+            widen_raw(vd[0], dv[0]);
+            widen_raw(vd[1], dv[1]);
+            // the next plane's loads fly during the analysis and the taps
+            if (b + 1 < b1) issue_loads(b + 1);
+            if constexpr (BASE) {
+                store_vec<CW>(X + (2 * a_r + PB) * SX + XO + CW * a_q, xv[0]);
+                store_vec<CW>(X + (2 * a_r + 1 + PB) * SX + XO + CW * a_q, xv[1]);
+                store_vec<CW>(DY + (2 * a_r) * SD + CW * a_q, dv[0]);
+                store_vec<CW>(DY + (2 * a_r + 1) * SD + CW * a_q, dv[1]);
             }
-        }
-        __syncthreads();
-        // the next plane's loads fly during the analysis and the taps
-        if (b + 1 < b1) issue_loads(b + 1);
-        // ----------------------------------------- P1: level 1 analysis
-        {
-            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1);
-            for (int q = tid; q < H1 * W1; q += NT) {
-                const int i = q / W1, j = q - i * W1;
-                // 2x2 blocks start on even columns of 8-byte aligned rows
-                const float2 x01 = *reinterpret_cast<const float2*>(X + (PB + 2 * i) * SX + XO + 2 * j);
-                const float2 x23 = *reinterpret_cast<const float2*>(X + (PB + 2 * i + 1) * SX + XO + 2 * j);
-                const float2 d01 = *reinterpret_cast<const float2*>(DY + 2 * i * SD + 2 * j);
-                const float2 d23 = *reinterpret_cast<const float2*>(DY + (2 * i + 1) * SD + 2 * j);
-                float u[4], v[4];
-                haar4(x01.x, x01.y, x23.x, x23.y, u[0], u[1], u[2], u[3]);
-                haar4(d01.x, d01.y, d23.x, d23.y, v[0], v[1], v[2], v[3]);
+            // level 1: NP horizontally adjacent positions per lane
+            float u[NP][4], v[NP][4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    U[s * BS1 + (PK + i) * S1 + PK + j] = u[s];
-                    Vb[s * VS1 + i * SV1 + j] = v[s];
-                }
+            for (int k = 0; k < NP; ++k) {
+                haar4(xv[0][2 * k], xv[0][2 * k + 1], xv[1][2 * k], xv[1][2 * k + 1], u[k][0], u[k][1], u[k][2], u[k][3]);
+                haar4(dv[0][2 * k], dv[0][2 * k + 1], dv[1][2 * k], dv[1][2 * k + 1], v[k][0], v[k][1], v[k][2], v[k][3]);
             }
-        }
-        __syncthreads();
-        // ----------------------------------------- P2: levels 2..L analysis
-        P::for_levels([&](auto lc) {
-            constexpr int l = decltype(lc)::value;
-            if constexpr (l >= 2) {
-                constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-                constexpr int Sp = P::su(l - 1), SVp = P::sv(l - 1), SVl = P::sv(l);
-                const float* LLu = U + P::uoff(l - 1) + PK * Sp + PK;
-                const float* LLv = Vb + P::voff(l - 1);
-                float* Ul = U + P::uoff(l);
-                float* Vl = Vb + P::voff(l);
-                for (int q = tid; q < hl * wl; q += NT) {
-                    const int i = q / wl, j = q - i * wl;
-                    const float* x2 = LLu + 2 * i * Sp + 2 * j;
-                    const float* d2 = LLv + 2 * i * SVp + 2 * j;
-                    float u[4], v[4];
-                    haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], u[0], u[1], u[2], u[3]);
-                    haar4(d2[0], d2[1], d2[SVp], d2[SVp + 1], v[0], v[1], v[2], v[3]);
+            {
+                constexpr int S1 = P::su(1), BS1 = P::bandsz(1), SV1 = P::sv(1), VS1 = P::vsz(1);
+#pragma unroll
+                for (int k = 0; k < NP; ++k)
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        Ul[s * BSl + (PK + i) * Sl + PK + j] = u[s];
-                        Vl[s * VSl + i * SVl + j] = v[s];
+                        U[s * BS1 + (PK + a_r) * S1 + PK + NP * a_q + k] = u[k][s];
+                        Vb[s * VS1 + a_r * SV1 + NP * a_q + k] = v[k][s];
                     }
-                }
-                __syncthreads();
             }
-        });
+            // levels 2..L: the LL of the level above, where this lane holds one
+            float llu = u[0][0], llv = v[0][0];
+            if constexpr (L >= 2 && CW == 4) {
+                // level 2: the lane's two level-1 positions are a horizontal
+                // pair, its row-pair partner (lane ^ 1) holds the other row
+                constexpr int S2 = P::su(2), BS2 = P::bandsz(2), SV2 = P::sv(2), VS2 = P::vsz(2);
+                const bool lower = a_rb & 1;
+                const float su0 = u[0][0] + u[1][0], du0 = u[0][0] - u[1][0];
+                const float sv0 = v[0][0] + v[1][0], dv0 = v[0][0] - v[1][0];
+                const float bu0 = haar_pair(su0, 1, lower), bu2 = haar_pair(du0, 1, lower);
+                const float bv0 = haar_pair(sv0, 1, lower), bv2 = haar_pair(dv0, 1, lower);
+                const int s0 = lower ? 1 : 0, r2 = a_r >> 1;
+                U[P::uoff(2) + s0 * BS2 + (PK + r2) * S2 + PK + a_q] = bu0;
+                U[P::uoff(2) + (s0 + 2) * BS2 + (PK + r2) * S2 + PK + a_q] = bu2;
+                Vb[P::voff(2) + s0 * VS2 + r2 * SV2 + a_q] = bv0;
+                Vb[P::voff(2) + (s0 + 2) * VS2 + r2 * SV2 + a_q] = bv2;
+                llu = bu0;
+                llv = bv0;
+            }
+            P::for_levels([&](auto lc) {
+                constexpr int l = decltype(lc)::value;
+                if constexpr (l >= (CW == 4 ? 3 : 2)) {
+                    constexpr int Sl = P::su(l), BSl = P::bandsz(l), SVl = P::sv(l), VSl = P::vsz(l);
+                    constexpr int MV = 1 << (l - 2), HB = CW == 4 ? 1 << (l - 3) : 1 << (l - 2), MH = BR * HB;
+                    const bool right = a_lb & MH, lower = a_lb & MV;
+                    // 2x2 butterfly: horizontal pairs, then vertical pairs
+                    const float bu = haar_pair(haar_pair(llu, MH, right), MV, lower);
+                    const float bv = haar_pair(haar_pair(llv, MH, right), MV, lower);
+                    if ((a_rb & (MV - 1)) == 0 && (a_cb & (HB - 1)) == 0) {
+                        const int s = (lower ? 1 : 0) + (right ? 2 : 0);
+                        const int rl = a_r >> (l - 1), cl = (NP * a_q) >> (l - 1);
+                        U[P::uoff(l) + s * BSl + (PK + rl) * Sl + PK + cl] = bu;
+                        Vb[P::voff(l) + s * VSl + rl * SVl + cl] = bv;
+                    }
+                    llu = bu;
+                    llv = bv;
+                }
+            });
+        }
+        __syncthreads();
         // ------------------- P3: all taps at once, base taps and one band per wavefront
         if (BASE && grp == 0) {
             for (int item = gtid; item < NI; item += 256) {

@@ -129,10 +129,9 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ p, RawVec<T, V>& 
     }
 }
 
-// Widen to fp32 and store at p (aligned to 4 * V bytes).
+// Widen to fp32 (exact for bf16).
 template <typename T, int V>
-__device__ __forceinline__ void store_lds(float* p, const RawVec<T, V>& r) {
-    float f[V];
+__device__ __forceinline__ void widen_raw(const RawVec<T, V>& r, float (&f)[V]) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int i = 0; i < V; ++i) f[i] = __uint_as_float(i % 2 == 0 ? r.w[i / 2] << 16 : r.w[i / 2] & 0xffff0000u);
@@ -140,9 +139,22 @@ __device__ __forceinline__ void store_lds(float* p, const RawVec<T, V>& r) {
 #pragma unroll
         for (int i = 0; i < V; ++i) f[i] = __uint_as_float(r.w[i]);
     }
+}
+
+// Store V floats at p (aligned to 4 * V bytes) with one vector store.
+template <int V>
+__device__ __forceinline__ void store_vec(float* p, const float (&f)[V]) {
     if constexpr (V == 4) *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
     else if constexpr (V == 2) *reinterpret_cast<float2*>(p) = make_float2(f[0], f[1]);
     else p[0] = f[0];
+}
+
+// Widen to fp32 and store at p (aligned to 4 * V bytes).
+template <typename T, int V>
+__device__ __forceinline__ void store_lds(float* p, const RawVec<T, V>& r) {
+    float f[V];
+    widen_raw(r, f);
+    store_vec<V>(p, f);
 }
 
 // Lanes given to one row block of column strips over a row of w columns:
@@ -260,19 +272,25 @@ __device__ __forceinline__ void conv_col(const float* s, const float* w, float (
         wr[t + 2] = q.z;
         wr[t + 3] = q.w;
     }
+    // window rows double-buffered: row r+1 is requested before row r's
+    // multiply-adds, so its LDS latency hides behind them
+    float win[2][K];
+#pragma unroll
+    for (int n = 0; n < K; ++n) win[0][n] = s[n];
 #pragma unroll
     for (int r = 0; r < R + K - 1; ++r) {
-        float win[K];
+        if (r + 1 < R + K - 1) {
 #pragma unroll
-        for (int n = 0; n < K; ++n) win[n] = s[r * S + n];
+            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = s[(r + 1) * S + n];
+        }
 #pragma unroll
         for (int o = 0; o < R; ++o) {
             const int m = r - o;
             if (m < 0 || m >= K) continue;
 #pragma unroll
             for (int n = 0; n < K; ++n) {
-                if (m == 0 && n == 0) acc[o] = wr[0] * win[0];
-                else acc[o] = __builtin_fmaf(wr[m * K + n], win[n], acc[o]);
+                if (m == 0 && n == 0) acc[o] = wr[0] * win[r & 1][0];
+                else acc[o] = __builtin_fmaf(wr[m * K + n], win[r & 1][n], acc[o]);
             }
         }
     }
