@@ -85,6 +85,78 @@ constexpr int pick_rows(int h, int w, int lanes, int k) {
     return best;
 }
 
+// Lane i takes lane i+1's value (the last lane takes 0): a DPP wave shift.
+__device__ __forceinline__ float shl1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xf, 0xf, true));
+}
+
+// Column-pair tap sums: acc[m*K+n] += sum_o v0[o] * u[o+m][n] + v1[o] * u[o+m][n+1]
+// for a strip of R rows x 2 columns (the lane's dy pair v0, v1 per row).
+// Each lane loads one aligned 64-bit pair per window row; the K-1 columns
+// to its right come from the next (K-1)/2 lanes through DPP wave shifts, so
+// a row block of w columns takes w/2 + (K-1)/2 lanes (the last ones only
+// feed their neighbours: pass live = false and their dy counts as zero).
+// Every lane of the wavefront must execute the call (no divergence): the
+// shifts read the neighbours' registers.
+template <int K, int R, int SU, int SV, int NA>
+__device__ __forceinline__ void taps_pair(const float* u, const float* v, bool live, float (&acc)[NA]) {
+    static_assert(NA >= K * K && K % 2 == 1, "accumulator slot too small / odd kernels only");
+    constexpr int NR = R + K - 1, NS = (K - 1) / 2;
+    __builtin_amdgcn_sched_barrier(0);
+    float v0[R], v1[R];
+#pragma unroll
+    for (int o = 0; o < R; ++o) {
+        const float2 q = *reinterpret_cast<const float2*>(v + o * SV);
+        v0[o] = live ? q.x : 0.f;
+        v1[o] = live ? q.y : 0.f;
+    }
+    float2 row[2];
+    row[0] = *reinterpret_cast<const float2*>(u);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (r + 1 < NR) row[(r + 1) & 1] = *reinterpret_cast<const float2*>(u + (r + 1) * SU);
+        float w[K + 1];
+        w[0] = row[r & 1].x;
+        w[1] = row[r & 1].y;
+#pragma unroll
+        for (int q = 1; q <= NS; ++q) {
+            w[2 * q] = shl1(w[2 * q - 2]);
+            w[2 * q + 1] = shl1(w[2 * q - 1]);
+        }
+#pragma unroll
+        for (int o = 0; o < R; ++o) {
+            const int m = r - o;
+            if (m < 0 || m >= K) continue;
+#pragma unroll
+            for (int n = 0; n < K; ++n) {
+                acc[m * K + n] = __builtin_fmaf(v0[o], w[n], acc[m * K + n]);
+                acc[m * K + n] = __builtin_fmaf(v1[o], w[n + 1], acc[m * K + n]);
+            }
+        }
+    }
+    pin_regs(acc);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Lanes per row block of column-pair strips over w columns with k x k taps.
+constexpr int pair_lanes(int w, int k) { return strip_lanes(w / 2 + (k - 1) / 2); }
+
+// Rows per column-pair strip: as pick_rows, counting the DPP shifts and
+// the pair loads.
+constexpr int pick_rows2(int h, int w, int lanes, int k) {
+    int best = 1, best_cost = 1 << 30;
+    for (int r = 1; r <= 16 && r <= h; ++r) {
+        if (h % r != 0) continue;
+        const int per = 2 * r * k * k + (r + k - 1) * (k - 1) + 2 * (2 * (r + k - 1) + 2 * r);
+        const int cost = cdiv((h / r) * pair_lanes(w, k), lanes) * per;
+        if (cost < best_cost) {
+            best = r;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 // One butterfly stage across lanes: the pair (lane, lane ^ mask) holding
 // (a, b) ends with a + b on the first lane and a - b on the second.
 __device__ __forceinline__ float haar_pair(float own, int mask, bool second) {
@@ -111,10 +183,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int H_, int W_, int L_, int KB_, int K_>
 struct BwPlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_;
-    static constexpr int RB = pick_rows(H, W, 256, KB);   // base strips on group A's lanes
     static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && L <= 5 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
+    // Column-pair strips (windows shared through DPP shifts) pay where the
+    // one-column strips read more than a third of an LDS word per
+    // multiply-add, and the pair strips keep 3/4 of their lanes busy.
+    static constexpr bool pair_worth(int h, int w, int k, int lanes) {
+        const int r = pick_rows(h, w, lanes, k);
+        return w % 2 == 0 && w / 2 + (k - 1) / 2 <= 64 && 4 * (w / 2) >= 3 * pair_lanes(w, k) &&
+               3 * ((r + k - 1) * k + r) > r * k * k;
+    }
+    static constexpr bool BASE_PAIR = PB % 2 == 0 && pair_worth(H, W, KB, 256);
+    static constexpr bool level_pair(int l) { return pair_worth(H >> l, W >> l, K, 64); }
     // x rows: interior from column XO (a multiple of 4, at least KB/2), row
     // stride a multiple of 4, so that streamed rows take aligned 128-bit
     // stores and 2x2 blocks aligned 64-bit reads; dy rows likewise
@@ -124,9 +205,14 @@ struct BwPlan {
     static constexpr int XSIZE = (H + 2 * PB) * SX;
     static constexpr int SD = round_up(W, 4);
     static constexpr int DSIZE = H * SD;
-    static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
+    // band rows: even strides where column pairs are read (8-byte aligned
+    // pairs), odd ones elsewhere (the analysis stores of lanes on
+    // consecutive rows then fall into different banks)
+    static constexpr int su(int l) {
+        return level_pair(l) ? round_up((W >> l) + 2 * PK, 2) : odd_stride((W >> l) + 2 * PK);
+    }
     static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
-    static constexpr int sv(int l) { return odd_stride(W >> l); }
+    static constexpr int sv(int l) { return level_pair(l) ? round_up(W >> l, 2) : odd_stride(W >> l); }
     static constexpr int vsz(int l) { return (H >> l) * sv(l); }
     static constexpr int uoff(int l) {
         int o = 0;
@@ -139,6 +225,9 @@ struct BwPlan {
         return o;
     }
     static constexpr int UTOT = uoff(L + 1), VTOT = voff(L + 1);
+    // Column-pair strips (DPP-shared windows) where a grid is wide and even:
+    // the base when its window starts on an even column, and each level
+    // whose pair strips keep at least 3/4 of a wavefront's lanes busy.
     // role slots: group A = base, 3, 5; group B = 1, 2, 4
     static constexpr int NSLOT = 1 + (L >= 2 ? 1 : 0) + (L >= 4 ? 1 : 0);
     static constexpr int SLOT0 = KB * KB > K * K ? KB * KB : K * K;   // base or level-1 taps
@@ -146,10 +235,14 @@ struct BwPlan {
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
-    static constexpr int LPB = strip_lanes(W);
-    static constexpr int NI = (H / RB) * LPB;   // base strip slots
+    // base strips on group A's 256 lanes: rows, lanes per row block, slots
+    static constexpr int RB = BASE_PAIR ? pick_rows2(H, W, 256, KB) : pick_rows(H, W, 256, KB);
+    static constexpr int LPB = BASE_PAIR ? pair_lanes(W, KB) : strip_lanes(W);
+    static constexpr int NI = (H / RB) * LPB;
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
-    static constexpr int band_rows(int l) { return pick_rows(H >> l, W >> l, 64, K); }
+    static constexpr int band_rows(int l) {
+        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K) : pick_rows(H >> l, W >> l, 64, K);
+    }
     // Analysis lanes: each owns 2 rows x CW columns of x and dy. The lanes
     // of one 2^L x 2^L block form a group of GS = BR x BC (BR row pairs,
     // BC column slices, row pair fastest) inside one wavefront.
@@ -323,26 +416,54 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
         __syncthreads();
         // ------------------- P3: all taps at once, base taps and one band per wavefront
         if (BASE && grp == 0) {
-            for (int item = gtid; item < NI; item += 256) {
-                const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
-                if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + h0 * SX + w, DY + h0 * SD + w, acc0);
+            if constexpr (P::BASE_PAIR) {
+                // column-pair strips; every lane of group A runs every pass
+                constexpr int NB = H / RB, WP = (W + KB - 1) / 2;
+#pragma unroll
+                for (int it = 0; it < cdiv(NI, 256); ++it) {
+                    const int item = gtid + 256 * it;
+                    const int rb = min(item / LPB, NB - 1), cq = item % LPB;
+                    const bool live = item < NI && cq < W / 2;
+                    const int cl = min(cq, WP - 1), cv = min(cq, W / 2 - 1);
+                    taps_pair<KB, RB, SX, SD>(X0 + rb * RB * SX + 2 * cl, DY + rb * RB * SD + 2 * cv, live, acc0);
+                }
+            } else {
+                for (int item = gtid; item < NI; item += 256) {
+                    const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
+                    if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + h0 * SX + w, DY + h0 * SD + w, acc0);
+                }
             }
         }
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-            constexpr int R = P::band_rows(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
+            constexpr int R = P::band_rows(l);
             if (grp == P::group_of(l)) {
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
                 constexpr int SVl = P::sv(l);
-                for (int item = lane; item < NIl; item += 64) {
-                    const int rs = item / LPl, j = item - rs * LPl;
-                    if (!(LPl == wl || j < wl)) continue;
-                    if constexpr (P::slot_of(l) == 0)
-                        taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, acc0);
-                    else
-                        taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, accl[P::slot_of(l) - 1]);
+                auto& slot = [&]() -> auto& {
+                    if constexpr (P::slot_of(l) == 0) return acc0;
+                    else return accl[P::slot_of(l) - 1];
+                }();
+                if constexpr (P::level_pair(l)) {
+                    // column-pair strips; every lane of the wavefront runs every pass
+                    constexpr int LP = pair_lanes(wl, K), NS = hl / R, NIl = NS * LP, WP = (wl + K - 1) / 2;
+#pragma unroll
+                    for (int it = 0; it < cdiv(NIl, 64); ++it) {
+                        const int item = lane + 64 * it;
+                        const int rs = min(item / LP, NS - 1), cq = item % LP;
+                        const bool live = item < NIl && cq < wl / 2;
+                        const int cl = min(cq, WP - 1), cv = min(cq, wl / 2 - 1);
+                        taps_pair<K, R, Sl, SVl>(Us + R * rs * Sl + 2 * cl, Vs + R * rs * SVl + 2 * cv, live, slot);
+                    }
+                } else {
+                    constexpr int LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
+                    for (int item = lane; item < NIl; item += 64) {
+                        const int rs = item / LPl, j = item - rs * LPl;
+                        if (!(LPl == wl || j < wl)) continue;
+                        taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, slot);
+                    }
                 }
             }
         });
