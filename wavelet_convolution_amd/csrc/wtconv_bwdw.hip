@@ -507,24 +507,41 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     }
 }
 
+// Threads of the finalize kernel: one per tap, whole wavefronts.
+static inline unsigned finalize_threads(int KB, int K, int L) {
+    const int taps = KB * KB + 4 * L * K * K;
+    return (unsigned)(((taps + 63) / 64) * 64 > 1024 ? 1024 : ((taps + 63) / 64) * 64);
+}
+
 // Stage 2: fixed-order sum over chunks, then scale and normalisation. Taps
 // [0, TA) (base, levels 1..LA) come from partA, the rest (levels LA+1..L)
 // from partB when the plane was split.
-__global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ partA, int nA, int LA,
-                                                     const float* __restrict__ partB, int nB, int C,
-                                                     int L, int KB, int K,
-                                                     const float* __restrict__ w_lvl,
-                                                     const float* __restrict__ scale,
-                                                     float* __restrict__ dw_base,
-                                                     float* __restrict__ dw_lvl,
-                                                     float* __restrict__ dscale) {
-    __shared__ float G[49 + 4 * 5 * 49];
+__global__ __launch_bounds__(1024) void bwdw_finalize(const float* __restrict__ partA, int nA, int LA,
+                                                      const float* __restrict__ partB, int nB, int C,
+                                                      int L, int KB, int K,
+                                                      const float* __restrict__ w_lvl,
+                                                      const float* __restrict__ scale,
+                                                      float* __restrict__ dw_base,
+                                                      float* __restrict__ dw_lvl,
+                                                      float* __restrict__ dscale) {
+    __shared__ float WG[4 * 5 * 49];   // w_lvl * G per level tap
     const int c = blockIdx.x, tid = threadIdx.x;
     const int kb2 = KB * KB, k2 = K * K, taps = kb2 + 4 * L * k2;
     const int TA = kb2 + 4 * LA * k2, TB = taps - TA;
+    // one tap per thread (blockDim covers every tap): the partial sums, the
+    // scale and the level tap are all requested before any is used
     for (int t = tid; t < taps; t += blockDim.x) {
-        float a = 0.f;
-        // independent loads, issued eight at a time; the sum stays in chunk order
+        float sc = 1.f, wv = 0.f;
+        size_t pi = 0;
+        int tap = 0;
+        if (t >= kb2) {
+            const int r = t - kb2, ls = r / k2, l = ls / 4, s = ls - 4 * l;
+            tap = r - ls * k2;
+            pi = ((size_t)l * C + c) * 4 + s;
+            sc = scale[pi];
+            wv = w_lvl[pi * k2 + tap];
+        }
+        float a = 0.f;   // the sum stays in chunk order
         if (t < TA) {
 #pragma unroll 8
             for (int ch = 0; ch < nA; ++ch) a += partA[((size_t)ch * C + c) * TA + t];
@@ -532,28 +549,21 @@ __global__ __launch_bounds__(256) void bwdw_finalize(const float* __restrict__ p
 #pragma unroll 8
             for (int ch = 0; ch < nB; ++ch) a += partB[((size_t)ch * C + c) * TB + (t - TA)];
         }
-        if (t >= kb2) {
+        if (t < kb2) {
+            dw_base[(size_t)c * kb2 + t] = a;
+        } else {
             const int l = (t - kb2) / (4 * k2);   // 0-based level
             a *= 1.0f / (float)(1 << (2 * (l + 1)));
+            dw_lvl[pi * k2 + tap] = sc * a;
+            WG[t - kb2] = wv * a;
         }
-        G[t] = a;
     }
     __syncthreads();
-    for (int t = tid; t < taps; t += blockDim.x) {
-        if (t < kb2) {
-            dw_base[(size_t)c * kb2 + t] = G[t];
-        } else {
-            const int r = t - kb2, ls = r / k2, tap = r - ls * k2, l = ls / 4, s = ls - 4 * l;
-            const size_t pi = ((size_t)l * C + c) * 4 + s;
-            dw_lvl[pi * k2 + tap] = scale[pi] * G[t];
-        }
-    }
     for (int ls = tid; ls < 4 * L; ls += blockDim.x) {
         const int l = ls / 4, s = ls - 4 * l;
-        const size_t pi = ((size_t)l * C + c) * 4 + s;
         float a = 0.f;
-        for (int tap = 0; tap < k2; ++tap) a += w_lvl[pi * k2 + tap] * G[kb2 + ls * k2 + tap];
-        dscale[pi] = a;
+        for (int tap = 0; tap < k2; ++tap) a += WG[ls * k2 + tap];
+        dscale[((size_t)l * C + c) * 4 + s] = a;
     }
 }
 
@@ -895,7 +905,8 @@ static hipError_t whole_launch(const void* x, const void* dy, const float* w_lvl
                        (const T*)x, (const T*)dy, part, B, C, bpc);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(256), 0, stream, (const float*)part, nchunk,
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(P::KB, P::K, P::L)), 0, stream,
+                       (const float*)part, nchunk,
                        P::L, (const float*)nullptr, 0, C, P::L, P::KB, P::K, w_lvl, scale, dw_base, dw_lvl,
                        dscale);
     return hipGetLastError();
@@ -947,7 +958,8 @@ static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(256), 0, stream, (const float*)partA, nA, FP::L0,
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(FP::KB, FP::K, FP::LT)), 0,
+                       stream, (const float*)partA, nA, FP::L0,
                        (const float*)partB, nB, C, FP::LT, FP::KB, FP::K, w_lvl, scale, dw_base, dw_lvl,
                        dscale);
     return hipGetLastError();
