@@ -33,15 +33,15 @@ namespace wtc {
 #ifndef WTC_TAPS_AHEAD
 #define WTC_TAPS_AHEAD 1
 #endif
-template <int K, int R, int SU, int SV, int NA>
-__device__ __forceinline__ void taps_col(const float* u, const float* v, float (&acc)[NA]) {
+template <int K, int R, int SU, int SV, int NA, typename VT>
+__device__ __forceinline__ void taps_col(const float* u, const VT* v, float (&acc)[NA]) {
     static_assert(NA >= K * K, "accumulator slot too small");
     constexpr int NR = R + K - 1;       // window rows
     constexpr int D = WTC_TAPS_AHEAD;   // rows requested ahead of their use
     __builtin_amdgcn_sched_barrier(0);
     float vt[R];
 #pragma unroll
-    for (int o = 0; o < R; ++o) vt[o] = v[o * SV];
+    for (int o = 0; o < R; ++o) vt[o] = widen(v[o * SV]);
     // a ring of D + 1 window rows: row r + D is requested before row r's
     // multiply-adds, so LDS latency hides behind D rows of them
     float win[D + 1][K];
@@ -72,11 +72,11 @@ __device__ __forceinline__ void taps_col(const float* u, const float* v, float (
 // multiply-adds plus its (R+k-1)*k + R LDS reads at two multiply-adds each
 // (a CU issues one wavefront multiply-add per clock across its four SIMDs
 // but moves only half a wavefront's worth of LDS words per clock).
-constexpr int pick_rows(int h, int w, int lanes, int k) {
+constexpr int pick_rows(int h, int w, int lanes, int k, int npb = 1) {
     int best = 1, best_cost = 1 << 30;
     for (int r = 1; r <= 16 && r <= h; ++r) {
         if (h % r != 0) continue;
-        const int cost = cdiv((h / r) * strip_lanes(w), lanes) * (r * k * k + 2 * ((r + k - 1) * k + r));
+        const int cost = cdiv(npb * (h / r) * strip_lanes(w), lanes) * (r * k * k + 2 * ((r + k - 1) * k + r));
         if (cost < best_cost) {
             best = r;
             best_cost = cost;
@@ -98,15 +98,21 @@ __device__ __forceinline__ float shl1(float v) {
 // feed their neighbours: pass live = false and their dy counts as zero).
 // Every lane of the wavefront must execute the call (no divergence): the
 // shifts read the neighbours' registers.
-template <int K, int R, int SU, int SV, int NA>
-__device__ __forceinline__ void taps_pair(const float* u, const float* v, bool live, float (&acc)[NA]) {
+template <int K, int R, int SU, int SV, int NA, typename VT>
+__device__ __forceinline__ void taps_pair(const float* u, const VT* v, bool live, float (&acc)[NA]) {
     static_assert(NA >= K * K && K % 2 == 1, "accumulator slot too small / odd kernels only");
     constexpr int NR = R + K - 1, NS = (K - 1) / 2;
     __builtin_amdgcn_sched_barrier(0);
     float v0[R], v1[R];
 #pragma unroll
     for (int o = 0; o < R; ++o) {
-        const float2 q = *reinterpret_cast<const float2*>(v + o * SV);
+        float2 q;
+        if constexpr (sizeof(VT) == 2) {   // a bf16 pair in one 32-bit word
+            const uint32_t w2 = *reinterpret_cast<const uint32_t*>(v + o * SV);
+            q = make_float2(__uint_as_float(w2 << 16), __uint_as_float(w2 & 0xffff0000u));
+        } else {
+            q = *reinterpret_cast<const float2*>(v + o * SV);
+        }
         v0[o] = live ? q.x : 0.f;
         v1[o] = live ? q.y : 0.f;
     }
@@ -143,12 +149,12 @@ constexpr int pair_lanes(int w, int k) { return strip_lanes(w / 2 + (k - 1) / 2)
 
 // Rows per column-pair strip: as pick_rows, counting the DPP shifts and
 // the pair loads.
-constexpr int pick_rows2(int h, int w, int lanes, int k) {
+constexpr int pick_rows2(int h, int w, int lanes, int k, int npb = 1) {
     int best = 1, best_cost = 1 << 30;
     for (int r = 1; r <= 16 && r <= h; ++r) {
         if (h % r != 0) continue;
         const int per = 2 * r * k * k + (r + k - 1) * (k - 1) + 2 * (2 * (r + k - 1) + 2 * r);
-        const int cost = cdiv((h / r) * pair_lanes(w, k), lanes) * per;
+        const int cost = cdiv(npb * (h / r) * pair_lanes(w, k), lanes) * per;
         if (cost < best_cost) {
             best = r;
             best_cost = cost;
@@ -164,10 +170,24 @@ __device__ __forceinline__ float haar_pair(float own, int mask, bool second) {
     return second ? p - own : own + p;
 }
 
+// Sum over the wavefront, in a fixed order: DPP row rotations give every
+// lane its 16-lane row's sum on the vector ALU (no LDS traffic), then the
+// four row sums are read out and added. Valid in every lane.
+template <int N>
+__device__ __forceinline__ float ror_row(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += ror_row<8>(v);
+    v += ror_row<4>(v);
+    v += ror_row<2>(v);
+    v += ror_row<1>(v);
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // H x W plane, L >= 1 levels; base strips of RB rows.
@@ -180,9 +200,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 //   group B (w >= 4): level 1 (slot 0), levels 2, 4 (slots 1, 2)
 // which balances the multiply-adds (level 1 alone equals the base work) and
 // keeps every lane at about two or three slots of taps.
-template <int H_, int W_, int L_, int KB_, int K_>
+template <int H_, int W_, int L_, int KB_, int K_, int LT_ = L_, int NPB_ = 1>
 struct BwPlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_;
+    // LT > L: levels L+1..LT of the layer go to a coarse pass, which gets
+    // the planes of level-L LL sums of x and dy from this one
+    static constexpr int LT = LT_;
+    // planes per step: NPB planes of the chunk share each barrier interval
+    static constexpr int NPB = NPB_;
+    // a coarse plan (1x1 "base", only level taps): no x or dy plane in LDS
+    static constexpr bool COARSE = KB == 1;
     static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && L <= 5 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
@@ -190,7 +217,7 @@ struct BwPlan {
     // one-column strips read more than a third of an LDS word per
     // multiply-add, and the pair strips keep 3/4 of their lanes busy.
     static constexpr bool pair_worth(int h, int w, int k, int lanes) {
-        const int r = pick_rows(h, w, lanes, k);
+        const int r = pick_rows(h, w, lanes, k, NPB);
         return w % 2 == 0 && w / 2 + (k - 1) / 2 <= 64 && 4 * (w / 2) >= 3 * pair_lanes(w, k) &&
                3 * ((r + k - 1) * k + r) > r * k * k;
     }
@@ -202,9 +229,9 @@ struct BwPlan {
     static constexpr int VL = lds_vec(W);
     static constexpr int XO = round_up(PB, 4);
     static constexpr int SX = round_up(XO + W + PB, 4);
-    static constexpr int XSIZE = (H + 2 * PB) * SX;
+    static constexpr int XSIZE = COARSE ? 0 : (H + 2 * PB) * SX;
     static constexpr int SD = round_up(W, 4);
-    static constexpr int DSIZE = H * SD;
+    static constexpr int DSIZE = COARSE ? 0 : H * SD;
     // band rows: even strides where column pairs are read (8-byte aligned
     // pairs), odd ones elsewhere (the analysis stores of lanes on
     // consecutive rows then fall into different banks)
@@ -228,20 +255,29 @@ struct BwPlan {
     // Column-pair strips (DPP-shared windows) where a grid is wide and even:
     // the base when its window starts on an even column, and each level
     // whose pair strips keep at least 3/4 of a wavefront's lanes busy.
-    // role slots: group A = base, 3, 5; group B = 1, 2, 4
-    static constexpr int NSLOT = 1 + (L >= 2 ? 1 : 0) + (L >= 4 ? 1 : 0);
+    // role slots: group A = base, 3, 5; group B = 1, 2, 4; in a coarse
+    // plan group A = 2, 4 and group B = 1, 3, 5
+    static constexpr int NSLOT = COARSE ? (L + 1) / 2 : 1 + (L >= 2 ? 1 : 0) + (L >= 4 ? 1 : 0);
     static constexpr int SLOT0 = KB * KB > K * K ? KB * KB : K * K;   // base or level-1 taps
     static constexpr int RED = NW * SLOT0 + NW * (NSLOT - 1) * K * K;   // reduction scratch
-    static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
-    static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
+    // dy stays in its 16-bit storage format in LDS when the activations are
+    // bf16 (only the base taps read it): half the region
+    template <typename T>
+    static constexpr int dsize() { return sizeof(T) == 2 ? DSIZE / 2 : DSIZE; }
+    // one plane's regions (x, dy, U, V); NPB of them side by side
+    template <typename T>
+    static constexpr int pstride() { return round_up(XSIZE + dsize<T>() + UTOT + VTOT, 4); }
+    template <typename T>
+    static constexpr int lds_floats() { return NPB * pstride<T>() > RED ? NPB * pstride<T>() : RED; }
+    static constexpr int LDS_FLOATS = lds_floats<float>();
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "plane does not fit in LDS");
     // base strips on group A's 256 lanes: rows, lanes per row block, slots
-    static constexpr int RB = BASE_PAIR ? pick_rows2(H, W, 256, KB) : pick_rows(H, W, 256, KB);
+    static constexpr int RB = BASE_PAIR ? pick_rows2(H, W, 256, KB, NPB) : pick_rows(H, W, 256, KB, NPB);
     static constexpr int LPB = BASE_PAIR ? pair_lanes(W, KB) : strip_lanes(W);
     static constexpr int NI = (H / RB) * LPB;
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
     static constexpr int band_rows(int l) {
-        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K) : pick_rows(H >> l, W >> l, 64, K);
+        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K, NPB) : pick_rows(H >> l, W >> l, 64, K, NPB);
     }
     // Analysis lanes: each owns 2 rows x CW columns of x and dy. The lanes
     // of one 2^L x 2^L block form a group of GS = BR x BC (BR row pairs,
@@ -251,20 +287,29 @@ struct BwPlan {
     static constexpr int BR = L >= 2 ? 1 << (L - 1) : 1;
     static constexpr int BC = L >= 2 ? (CW == 4 ? 1 << (L - 2) : 1 << (L - 1)) : 1;
     static constexpr int GS = BR * BC, NBC = NC / BC;
-    static_assert(NA <= NT, "one analysis lane per 2 x CW block of the plane");
+    static_assert(NPB * NA <= NT, "one analysis lane per 2 x CW block of each plane of a step");
     static_assert(64 % GS == 0, "a block's analysis lanes share a wavefront");
-    static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
-    static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
-    // registers bound the occupancy too: each lane holds its tap slots plus
-    // about 64 registers of tiles and addresses (512 VGPRs per SIMD lane)
-    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 64;
-    static constexpr int WAVES_PER_EU_REG = 512 / (REGS <= 128 ? 128 : (REGS <= 168 ? 168 : 256));
-    static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
-    static constexpr int WAVES_PER_EU = WAVES_PER_EU_MIN < 1 ? 1 : WAVES_PER_EU_MIN;
+    // Occupancy (waves per SIMD): what LDS allows, and what registers allow
+    // at about 48 registers of strips and addresses beside the tap slots
+    // (512 per SIMD lane, granted in blocks of 8).
+    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + (COARSE ? 56 : 48);
+    static constexpr int waves_reg() {
+        int w = 8;
+        while (w > 1 && (512 / w) / 8 * 8 < REGS) --w;
+        return w;
+    }
+    template <typename T>
+    static constexpr int waves_per_eu() {
+        const int lds = (160 * 1024) / (lds_floats<T>() * 4) * NW / 4;
+        const int w = lds < waves_reg() ? lds : waves_reg();
+        return w < 1 ? 1 : w;
+    }
 
     // group and slot of level l (1..5)
-    static constexpr int group_of(int l) { return (l == 3 || l == 5) ? 0 : 1; }
-    static constexpr int slot_of(int l) { return l == 1 ? 0 : (l == 2 || l == 3) ? 1 : 2; }
+    static constexpr int group_of(int l) { return COARSE ? (l % 2 == 0 ? 0 : 1) : ((l == 3 || l == 5) ? 0 : 1); }
+    static constexpr int slot_of(int l) {
+        return COARSE ? (l - 1) / 2 : (l == 1 ? 0 : (l == 2 || l == 3) ? 1 : 2);
+    }
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -281,20 +326,21 @@ struct BwPlan {
 // the kernel's levels are L0+1.. of the layer, and only level taps are
 // produced (ordered [L][4][K*K], relative levels).
 template <class P, typename T, bool BASE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
-void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part, int B,
-                 int C, int bpc) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::template waves_per_eu<T>())))
+void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part,
+                 float* __restrict__ px, float* __restrict__ pdy, int B, int C, int bpc) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX;
     constexpr int RB = P::RB, NI = P::NI, LPB = P::LPB, XO = P::XO, SD = P::SD;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
 
-    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS];
-    float* X = lds;
-    const float* X0 = X + XO - PB;   // origin of the bordered x plane
-    float* DY = X + P::XSIZE;
-    float* U = DY + P::DSIZE;
-    float* Vb = U + P::UTOT;
+    constexpr int NPB = P::NPB, PS = P::template pstride<T>();
+    __shared__ __attribute__((aligned(16))) float lds[P::template lds_floats<T>()];
+    // plane p of a step: x (bordered), dy (storage format), U bands, V bands
+    auto Xp = [&](int p) { return lds + p * PS; };
+    auto DYp = [&](int p) { return reinterpret_cast<T*>(lds + p * PS + P::XSIZE); };
+    auto Up = [&](int p) { return lds + p * PS + P::XSIZE + P::template dsize<T>(); };
+    auto Vp = [&](int p) { return lds + p * PS + P::XSIZE + P::template dsize<T>() + P::UTOT; };
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int grp = wave >> 2, band = wave & 3, gtid = tid & 255;
@@ -302,11 +348,13 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
 
     // borders stay zero for the whole chunk: nothing writes them
-    zero_border<1, H, W, PB, SX, XO>(X, tid, NT);
-    P::for_levels([&](auto lc) {
-        constexpr int l = decltype(lc)::value;
-        zero_border<4, (H >> l), (W >> l), PK, P::su(l)>(U + P::uoff(l), tid, NT);
-    });
+    for (int p = 0; p < NPB; ++p) {
+        if constexpr (!P::COARSE) zero_border<1, H, W, PB, SX, XO>(Xp(p), tid, NT);
+        P::for_levels([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            zero_border<4, (H >> l), (W >> l), PK, P::su(l)>(Up(p) + P::uoff(l), tid, NT);
+        });
+    }
 
     float acc0[SLOT0];
     float accl[NSLOT > 1 ? NSLOT - 1 : 1][K * K];
@@ -321,42 +369,54 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     // a < NA owns rows 2r, 2r+1 and columns CW q .. CW q + CW-1 of x and dy.
     // Level 1 comes from its own values; each deeper level combines the
     // 2x2 blocks of the level above across lanes with xor shuffles.
+    // Analysis lane tid < NPB * NA belongs to plane a_p of the step.
     constexpr int CW = P::CW, NA = P::NA, BR = P::BR, BC = P::BC, GS = P::GS, NBC = P::NBC, NP = CW / 2;
-    const int a_lb = tid % GS, a_blk = tid / GS;
+    const int a_p = NPB == 1 ? 0 : tid / NA, a_i = tid - a_p * NA;
+    const int a_lb = a_i % GS, a_blk = a_i / GS;
     const int a_rb = a_lb % BR, a_cb = a_lb / BR;
     const int a_r = (a_blk / NBC) * BR + a_rb, a_q = (a_blk % NBC) * BC + a_cb;
+    float* const X = Xp(a_p < NPB ? a_p : 0);
+    T* const DY = DYp(a_p < NPB ? a_p : 0);
+    float* const U = Up(a_p < NPB ? a_p : 0);
+    float* const Vb = Vp(a_p < NPB ? a_p : 0);
 
-    // global loads of the next plane, in flight during the current taps
+    // global loads of the next step's planes, in flight during the current
+    // taps; a plane past the chunk's end reads as zeros (it adds nothing)
     RawVec<T, CW> vx[2], vd[2];
     auto issue_loads = [&](int b) {
-        if (tid < NA) {
-            const size_t off = ((size_t)b * C + c) * H * W + (size_t)(2 * a_r) * W + CW * a_q;
-            load_raw<T, CW>(x + off, vx[0]);
-            load_raw<T, CW>(x + off + W, vx[1]);
-            load_raw<T, CW>(dy + off, vd[0]);
-            load_raw<T, CW>(dy + off + W, vd[1]);
+        if (tid < NPB * NA) {
+            if (b + a_p < b1) {
+                const size_t off = ((size_t)(b + a_p) * C + c) * H * W + (size_t)(2 * a_r) * W + CW * a_q;
+                load_raw<T, CW>(x + off, vx[0]);
+                load_raw<T, CW>(x + off + W, vx[1]);
+                load_raw<T, CW>(dy + off, vd[0]);
+                load_raw<T, CW>(dy + off + W, vd[1]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < RawVec<T, CW>::N; ++i) vx[0].w[i] = vx[1].w[i] = vd[0].w[i] = vd[1].w[i] = 0u;
+            }
         }
     };
     if (b0 < b1) issue_loads(b0);
 
-    for (int b = b0; b < b1; ++b) {
-        // the previous plane's taps read x, dy and the bands: all done first
+    for (int b = b0; b < b1; b += NPB) {
+        // the previous step's taps read x, dy and the bands: all done first
         if (b > b0) __syncthreads();
         // ------------------------------------ P0: stream in and analyse
-        if (tid < NA) {
+        if (tid < NPB * NA) {
             float xv[2][CW], dv[2][CW];
             widen_raw(vx[0], xv[0]);
             widen_raw(vx[1], xv[1]);
             widen_raw(vd[0], dv[0]);
             widen_raw(vd[1], dv[1]);
-            // the next plane's loads fly during the analysis and the taps
-            if (b + 1 < b1) issue_loads(b + 1);
             if constexpr (BASE) {
                 store_vec<CW>(X + (2 * a_r + PB) * SX + XO + CW * a_q, xv[0]);
                 store_vec<CW>(X + (2 * a_r + 1 + PB) * SX + XO + CW * a_q, xv[1]);
-                store_vec<CW>(DY + (2 * a_r) * SD + CW * a_q, dv[0]);
-                store_vec<CW>(DY + (2 * a_r + 1) * SD + CW * a_q, dv[1]);
+                store_raw<T, CW>(DY + (2 * a_r) * SD + CW * a_q, vd[0]);
+                store_raw<T, CW>(DY + (2 * a_r + 1) * SD + CW * a_q, vd[1]);
             }
+            // the next step's loads fly during the analysis and the taps
+            if (b + NPB < b1) issue_loads(b + NPB);
             // level 1: NP horizontally adjacent positions per lane
             float u[NP][4], v[NP][4];
 #pragma unroll
@@ -412,6 +472,25 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                     llv = bv;
                 }
             });
+            if (P::LT > L && b + a_p < b1) {
+                // level-L LL sums for the coarse pass, from the lanes holding them
+                constexpr int HL = H >> L, WL = W >> L;
+                const size_t po = ((size_t)(b + a_p) * C + c) * HL * WL;
+                if constexpr (L == 1) {
+#pragma unroll
+                    for (int k = 0; k < NP; ++k) {
+                        px[po + a_r * WL + NP * a_q + k] = u[k][0];
+                        pdy[po + a_r * WL + NP * a_q + k] = v[k][0];
+                    }
+                } else {
+                    constexpr int MV = 1 << (L - 1), HB = CW == 4 ? 1 << (L - 2) : 1 << (L - 1);
+                    if ((a_rb & (MV - 1)) == 0 && (a_cb & (HB - 1)) == 0) {
+                        const int rl = a_r >> (L - 1), cl = (NP * a_q) >> (L - 1);
+                        px[po + rl * WL + cl] = llu;
+                        pdy[po + rl * WL + cl] = llv;
+                    }
+                }
+            }
         }
         __syncthreads();
         // ------------------- P3: all taps at once, base taps and one band per wavefront
@@ -420,17 +499,20 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                 // column-pair strips; every lane of group A runs every pass
                 constexpr int NB = H / RB, WP = (W + KB - 1) / 2;
 #pragma unroll
-                for (int it = 0; it < cdiv(NI, 256); ++it) {
-                    const int item = gtid + 256 * it;
-                    const int rb = min(item / LPB, NB - 1), cq = item % LPB;
-                    const bool live = item < NI && cq < W / 2;
+                for (int it = 0; it < cdiv(NPB * NI, 256); ++it) {
+                    const int item = gtid + 256 * it, pl = min(item / NI, NPB - 1), r = item - pl * NI;
+                    const int rb = min(r / LPB, NB - 1), cq = r % LPB;
+                    const bool live = item < NPB * NI && cq < W / 2;
                     const int cl = min(cq, WP - 1), cv = min(cq, W / 2 - 1);
-                    taps_pair<KB, RB, SX, SD>(X0 + rb * RB * SX + 2 * cl, DY + rb * RB * SD + 2 * cv, live, acc0);
+                    taps_pair<KB, RB, SX, SD>(Xp(pl) + XO - PB + rb * RB * SX + 2 * cl, DYp(pl) + rb * RB * SD + 2 * cv,
+                                              live, acc0);
                 }
             } else {
-                for (int item = gtid; item < NI; item += 256) {
-                    const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
-                    if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + h0 * SX + w, DY + h0 * SD + w, acc0);
+                for (int item = gtid; item < NPB * NI; item += 256) {
+                    const int pl = item / NI, r = item - pl * NI;
+                    const int rb = r / LPB, w = r - rb * LPB, h0 = rb * RB;
+                    if (LPB == W || w < W)
+                        taps_col<KB, RB, SX, SD>(Xp(pl) + XO - PB + h0 * SX + w, DYp(pl) + h0 * SD + w, acc0);
                 }
             }
         }
@@ -439,9 +521,10 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
             constexpr int R = P::band_rows(l);
             if (grp == P::group_of(l)) {
-                const float* Us = U + P::uoff(l) + band * BSl;
-                const float* Vs = Vb + P::voff(l) + band * VSl;
                 constexpr int SVl = P::sv(l);
+                // band `band` of level l in plane pl of the step
+                auto Us = [&](int pl) -> const float* { return Up(pl) + P::uoff(l) + band * BSl; };
+                auto Vs = [&](int pl) -> const float* { return Vp(pl) + P::voff(l) + band * VSl; };
                 auto& slot = [&]() -> auto& {
                     if constexpr (P::slot_of(l) == 0) return acc0;
                     else return accl[P::slot_of(l) - 1];
@@ -450,19 +533,21 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                     // column-pair strips; every lane of the wavefront runs every pass
                     constexpr int LP = pair_lanes(wl, K), NS = hl / R, NIl = NS * LP, WP = (wl + K - 1) / 2;
 #pragma unroll
-                    for (int it = 0; it < cdiv(NIl, 64); ++it) {
-                        const int item = lane + 64 * it;
-                        const int rs = min(item / LP, NS - 1), cq = item % LP;
-                        const bool live = item < NIl && cq < wl / 2;
+                    for (int it = 0; it < cdiv(NPB * NIl, 64); ++it) {
+                        const int item = lane + 64 * it, pl = min(item / NIl, NPB - 1), r = item - pl * NIl;
+                        const int rs = min(r / LP, NS - 1), cq = r % LP;
+                        const bool live = item < NPB * NIl && cq < wl / 2;
                         const int cl = min(cq, WP - 1), cv = min(cq, wl / 2 - 1);
-                        taps_pair<K, R, Sl, SVl>(Us + R * rs * Sl + 2 * cl, Vs + R * rs * SVl + 2 * cv, live, slot);
+                        taps_pair<K, R, Sl, SVl>(Us(pl) + R * rs * Sl + 2 * cl, Vs(pl) + R * rs * SVl + 2 * cv, live,
+                                                 slot);
                     }
                 } else {
                     constexpr int LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
-                    for (int item = lane; item < NIl; item += 64) {
-                        const int rs = item / LPl, j = item - rs * LPl;
+                    for (int item = lane; item < NPB * NIl; item += 64) {
+                        const int pl = item / NIl, r = item - pl * NIl;
+                        const int rs = r / LPl, j = r - rs * LPl;
                         if (!(LPl == wl || j < wl)) continue;
-                        taps_col<K, R, Sl, SVl>(Us + R * rs * Sl + j, Vs + R * rs * SVl + j, slot);
+                        taps_col<K, R, Sl, SVl>(Us(pl) + R * rs * Sl + j, Vs(pl) + R * rs * SVl + j, slot);
                     }
                 }
             }
@@ -879,11 +964,32 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 // reduction is amortised over as many planes as the parallelism allows
 // (rounded down: a second, mostly empty round of workgroups would double
 // the kernel's tail)
-static int chunk_units(int units, int C) {
-    int nchunk = 512 / C;
+static int chunk_units(int units, int C, int slots = 512) {
+    int nchunk = slots / C;
     if (nchunk > units) nchunk = units;
     if (nchunk < 1) nchunk = 1;
     return cdiv(units, nchunk);
+}
+
+// Compute units of the current device (queried once per device).
+static int cu_count() {
+    constexpr int MAXDEV = 64;
+    static int cache[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < MAXDEV && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    if (dev < MAXDEV) cache[dev] = n;
+    return n;
+}
+
+// Resident workgroups of a whole-plane weight-gradient plan with activations
+// of type T: CUs x the workgroups per CU its register and LDS budget allows.
+template <class P, typename T>
+static int bw_slots() {
+    const int per_cu = P::template waves_per_eu<T>() * 4 / P::NW;
+    return cu_count() * (per_cu < 1 ? 1 : per_cu);
 }
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -902,7 +1008,7 @@ static hipError_t whole_launch(const void* x, const void* dy, const float* w_lvl
     const int bpc = chunk_units(B, C), nchunk = cdiv(B, bpc);
     float* part = (float*)ws;
     hipLaunchKernelGGL((bwdw_kernel<P, T, true>), dim3((unsigned)(nchunk * C)), dim3(P::NT), 0, stream,
-                       (const T*)x, (const T*)dy, part, B, C, bpc);
+                       (const T*)x, (const T*)dy, part, (float*)nullptr, (float*)nullptr, B, C, bpc);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(P::KB, P::K, P::L)), 0, stream,
@@ -954,7 +1060,8 @@ static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_
     if constexpr (FP::LT > FP::L0) {
         const int bpc = chunk_units(B, C);
         hipLaunchKernelGGL((bwdw_kernel<CP, float, false>), dim3((unsigned)(nB * C)), dim3(CP::NT), 0, stream,
-                           (const float*)px, (const float*)pdy, partB, B, C, bpc);
+                           (const float*)px, (const float*)pdy, partB, (float*)nullptr, (float*)nullptr, B, C,
+                           bpc);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -962,6 +1069,54 @@ static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_
                        stream, (const float*)partA, nA, FP::L0,
                        (const float*)partB, nB, C, FP::LT, FP::KB, FP::K, w_lvl, scale, dw_base, dw_lvl,
                        dscale);
+    return hipGetLastError();
+}
+
+// whole planes split by level: the whole-plane kernel does the base and
+// levels 1..L (one or two tap slots per lane, so more workgroups fit a CU)
+// and writes the level-L LL sums; the coarse pass does levels L+1..LT
+template <class FP, class CP>
+static size_t plane_split_ws(int B, int C) {
+    const int slots = bw_slots<FP, bf16_t>() > bw_slots<FP, float>() ? bw_slots<FP, bf16_t>() : bw_slots<FP, float>();
+    const int nA = cdiv(B, chunk_units(B, C, slots));
+    const int nB = cdiv(B, chunk_units(B, C, bw_slots<CP, float>()));
+    size_t n = align256((size_t)nA * C * FP::TAPS * sizeof(float));
+    n += align256((size_t)nB * C * 4 * (FP::LT - FP::L) * FP::K * FP::K * sizeof(float));
+    n += 2 * align256((size_t)B * C * (FP::H >> FP::L) * (FP::W >> FP::L) * sizeof(float));
+    return n;
+}
+
+template <class FP, class CP, typename T>
+static hipError_t plane_split_launch(const void* x, const void* dy, const float* w_lvl, const float* scale,
+                                     float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
+                                     hipStream_t stream) {
+    static_assert(FP::LT > FP::L && CP::LT == CP::L && CP::KB == 1 && CP::K == FP::K &&
+                      CP::L == FP::LT - FP::L && CP::H == (FP::H >> FP::L) && CP::W == (FP::W >> FP::L),
+                  "coarse plan: levels L+1..LT of the fine plan on its LL planes");
+    const int slots = bw_slots<FP, bf16_t>() > bw_slots<FP, float>() ? bw_slots<FP, bf16_t>() : bw_slots<FP, float>();
+    const int nA_ws = cdiv(B, chunk_units(B, C, slots));
+    const int bpcA = chunk_units(B, C, bw_slots<FP, T>()), nA = cdiv(B, bpcA);
+    const int bpcB = chunk_units(B, C, bw_slots<CP, float>()), nB = cdiv(B, bpcB);
+    char* cur = (char*)ws;
+    float* partA = (float*)cur;
+    cur += align256((size_t)nA_ws * C * FP::TAPS * sizeof(float));
+    float* partB = (float*)cur;
+    cur += align256((size_t)nB * C * 4 * (FP::LT - FP::L) * FP::K * FP::K * sizeof(float));
+    const size_t pl = (size_t)B * C * (FP::H >> FP::L) * (FP::W >> FP::L) * sizeof(float);
+    float* px = (float*)cur;
+    cur += align256(pl);
+    float* pdy = (float*)cur;
+    hipLaunchKernelGGL((bwdw_kernel<FP, T, true>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
+                       (const T*)x, (const T*)dy, partA, px, pdy, B, C, bpcA);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((bwdw_kernel<CP, float, false>), dim3((unsigned)(nB * C)), dim3(CP::NT), 0, stream,
+                       (const float*)px, (const float*)pdy, partB, (float*)nullptr, (float*)nullptr, B, C, bpcB);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(FP::KB, FP::K, FP::LT)), 0,
+                       stream, (const float*)partA, nA, FP::L, (const float*)partB, nB, C, FP::LT, FP::KB, FP::K,
+                       w_lvl, scale, dw_base, dw_lvl, dscale);
     return hipGetLastError();
 }
 
@@ -999,13 +1154,26 @@ typedef BwPlan<16, 16, 2, 1, 3> CB_16_L2_k3;
 typedef TileBwPlan<64, 64, 1, 2, 5, 5, 16> TB_64_L1of2_k55;
 typedef BwPlan<32, 32, 1, 1, 5> CB_32_L1_k5b;
 
+// whole planes split by level (fine: base + level 1; coarse: the rest)
+typedef BwPlan<56, 56, 1, 5, 5, 3> WP_56_L1of3_k55;
+typedef BwPlan<28, 28, 2, 1, 5, 2, 4> CB_28_L2_k5;
+
 #define WTC_BW_WHOLE(PLAN) \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K, {whole_launch<PLAN, float>, whole_launch<PLAN, bf16_t>}, whole_ws<PLAN>}
+#define WTC_BW_PLANESPLIT(FPL, CPL)                                                               \
+    {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K,                                                   \
+     {plane_split_launch<FPL, CPL, float>, plane_split_launch<FPL, CPL, bf16_t>}, plane_split_ws<FPL, CPL>}
 #define WTC_BW_SPLIT(FPL, CPL)                                                                    \
     {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K,                                                   \
      {split_bw_launch<FPL, CPL, float>, split_bw_launch<FPL, CPL, bf16_t>}, split_bw_ws<FPL, CPL>}
 
+#ifndef WTC_BW56_SPLIT
+#define WTC_BW56_SPLIT 1
+#endif
 static const BwEntry kBwEntries[] = {
+#if WTC_BW56_SPLIT
+    WTC_BW_PLANESPLIT(WP_56_L1of3_k55, CB_28_L2_k5),
+#endif
     WTC_BW_WHOLE(BP_32_L2_k55), WTC_BW_WHOLE(BP_56_L3_k55),    WTC_BW_WHOLE(BP_28_L2_k55),
     WTC_BW_WHOLE(BP_14_L1_k55), WTC_BW_WHOLE(BP_32_L3_k75),    WTC_BW_WHOLE(BP_24x40_L3_k33),
     WTC_BW_WHOLE(BP_16_L4_k37), WTC_BW_WHOLE(BP_64_L4_k75),

@@ -149,6 +149,16 @@ __device__ __forceinline__ void store_vec(float* p, const float (&f)[V]) {
     else p[0] = f[0];
 }
 
+// Store V activations in their storage format at p (aligned to the vector).
+template <typename T, int V>
+__device__ __forceinline__ void store_raw(T* p, const RawVec<T, V>& r) {
+    constexpr int N = RawVec<T, V>::N;
+    static_assert(V * sizeof(T) == 4 * N, "whole 32-bit words");
+    if constexpr (N == 4) *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+    else if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(r.w[0], r.w[1]);
+    else *reinterpret_cast<uint32_t*>(p) = r.w[0];
+}
+
 // Widen to fp32 and store at p (aligned to 4 * V bytes).
 template <typename T, int V>
 __device__ __forceinline__ void store_lds(float* p, const RawVec<T, V>& r) {
