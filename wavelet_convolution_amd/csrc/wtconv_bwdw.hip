@@ -170,18 +170,24 @@ __device__ __forceinline__ float haar_pair(float own, int mask, bool second) {
     return second ? p - own : own + p;
 }
 
-// Sum over the wavefront, in a fixed order: DPP row rotations give every
-// lane its 16-lane row's sum on the vector ALU (no LDS traffic), then the
-// four row sums are read out and added. Valid in every lane.
+// Sum over each 16-lane row of the wavefront, in a fixed order: DPP row
+// rotations on the vector ALU (no LDS traffic); every lane of a row ends
+// with its row's sum.
 template <int N>
 __device__ __forceinline__ float ror_row(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, true));
 }
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ float row_sum(float v) {
     v += ror_row<8>(v);
     v += ror_row<4>(v);
     v += ror_row<2>(v);
     v += ror_row<1>(v);
+    return v;
+}
+
+// Sum over the wavefront (row sums, then the four rows), valid in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row_sum(v);
     const int b = __builtin_bit_cast(int, v);
     const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
     const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
@@ -208,8 +214,11 @@ struct BwPlan {
     static constexpr int LT = LT_;
     // planes per step: NPB planes of the chunk share each barrier interval
     static constexpr int NPB = NPB_;
-    // a coarse plan (1x1 "base", only level taps): no x or dy plane in LDS
+    // a coarse plan (1x1 "base", only level taps): no x or dy plane in LDS;
+    // its input planes were just written (L2 hits), so a step's loads are
+    // issued at the step's start rather than a step ahead (fewer registers)
     static constexpr bool COARSE = KB == 1;
+    static constexpr bool PREFETCH = !COARSE;
     static constexpr int NT = 512, NW = 8;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && L <= 5 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
@@ -259,7 +268,7 @@ struct BwPlan {
     // plan group A = 2, 4 and group B = 1, 3, 5
     static constexpr int NSLOT = COARSE ? (L + 1) / 2 : 1 + (L >= 2 ? 1 : 0) + (L >= 4 ? 1 : 0);
     static constexpr int SLOT0 = KB * KB > K * K ? KB * KB : K * K;   // base or level-1 taps
-    static constexpr int RED = NW * SLOT0 + NW * (NSLOT - 1) * K * K;   // reduction scratch
+    static constexpr int RED = 4 * (NW * SLOT0 + NW * (NSLOT - 1) * K * K);   // reduction scratch (4 rows)
     // dy stays in its 16-bit storage format in LDS when the activations are
     // bf16 (only the base taps read it): half the region
     template <typename T>
@@ -292,7 +301,7 @@ struct BwPlan {
     // Occupancy (waves per SIMD): what LDS allows, and what registers allow
     // at about 48 registers of strips and addresses beside the tap slots
     // (512 per SIMD lane, granted in blocks of 8).
-    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + (COARSE ? 56 : 48);
+    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 48;
     static constexpr int waves_reg() {
         int w = 8;
         while (w > 1 && (512 / w) / 8 * 8 < REGS) --w;
@@ -326,16 +335,15 @@ struct BwPlan {
 // the kernel's levels are L0+1.. of the layer, and only level taps are
 // produced (ordered [L][4][K*K], relative levels).
 template <class P, typename T, bool BASE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::template waves_per_eu<T>())))
-void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part,
-                 float* __restrict__ px, float* __restrict__ pdy, int B, int C, int bpc) {
+__device__ __forceinline__ void bwdw_body(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part,
+                                          float* __restrict__ px, float* __restrict__ pdy, int B, int C, int bpc,
+                                          float* __restrict__ lds) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX;
     constexpr int RB = P::RB, NI = P::NI, LPB = P::LPB, XO = P::XO, SD = P::SD;
     constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
 
     constexpr int NPB = P::NPB, PS = P::template pstride<T>();
-    __shared__ __attribute__((aligned(16))) float lds[P::template lds_floats<T>()];
     // plane p of a step: x (bordered), dy (storage format), U bands, V bands
     auto Xp = [&](int p) { return lds + p * PS; };
     auto DYp = [&](int p) { return reinterpret_cast<T*>(lds + p * PS + P::XSIZE); };
@@ -397,9 +405,10 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
             }
         }
     };
-    if (b0 < b1) issue_loads(b0);
+    if (P::PREFETCH && b0 < b1) issue_loads(b0);
 
     for (int b = b0; b < b1; b += NPB) {
+        if (!P::PREFETCH) issue_loads(b);
         // the previous step's taps read x, dy and the bands: all done first
         if (b > b0) __syncthreads();
         // ------------------------------------ P0: stream in and analyse
@@ -416,7 +425,7 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
                 store_raw<T, CW>(DY + (2 * a_r + 1) * SD + CW * a_q, vd[1]);
             }
             // the next step's loads fly during the analysis and the taps
-            if (b + NPB < b1) issue_loads(b + NPB);
+            if (P::PREFETCH && b + NPB < b1) issue_loads(b + NPB);
             // level 1: NP horizontally adjacent positions per lane
             float u[NP][4], v[NP][4];
 #pragma unroll
@@ -555,41 +564,79 @@ void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __res
     }
 
     // ------------------------------------------------------ reduction
+    // each 16-lane row's sum (DPP), the four rows of each wavefront through
+    // LDS, then a fixed-order sum per tap
 #pragma unroll
-    for (int t = 0; t < SLOT0; ++t) acc0[t] = wave_sum(acc0[t]);
+    for (int t = 0; t < SLOT0; ++t) acc0[t] = row_sum(acc0[t]);
 #pragma unroll
     for (int j = 0; j < NSLOT - 1; ++j)
 #pragma unroll
-        for (int t = 0; t < K * K; ++t) accl[j][t] = wave_sum(accl[j][t]);
+        for (int t = 0; t < K * K; ++t) accl[j][t] = row_sum(accl[j][t]);
     __syncthreads();  // all of LDS becomes reduction scratch
-    float* red0 = lds;                     // [NW][SLOT0]
-    float* redl = lds + P::NW * SLOT0;     // [NW][NSLOT-1][K*K]
-    if (lane == 0) {
+    float* red0 = lds;                         // [NW][4 rows][SLOT0]
+    float* redl = lds + P::NW * 4 * SLOT0;     // [NW][4 rows][NSLOT-1][K*K]
+    if ((lane & 15) == 0) {
+        const int wr = wave * 4 + (lane >> 4);
 #pragma unroll
-        for (int t = 0; t < SLOT0; ++t) red0[wave * SLOT0 + t] = acc0[t];
+        for (int t = 0; t < SLOT0; ++t) red0[wr * SLOT0 + t] = acc0[t];
 #pragma unroll
         for (int j = 0; j < NSLOT - 1; ++j)
 #pragma unroll
-            for (int t = 0; t < K * K; ++t) redl[(wave * (NSLOT - 1) + j) * K * K + t] = accl[j][t];
+            for (int t = 0; t < K * K; ++t) redl[(wr * (NSLOT - 1) + j) * K * K + t] = accl[j][t];
     }
     __syncthreads();
     constexpr int NB = BASE ? KB * KB : 0;   // base taps written by this kernel
     constexpr int TOUT = NB + 4 * L * K * K;
     float* dst = part + ((size_t)chunk * C + c) * TOUT;
     for (int t = tid; t < TOUT; t += NT) {
-        float v;
+        float v = 0.f;
         if (t < NB) {
-            v = red0[t];   // group A, waves 0..3 in order
 #pragma unroll
-            for (int w = 1; w < 4; ++w) v += red0[w * SLOT0 + t];
+            for (int wr = 0; wr < 16; ++wr) v += red0[wr * SLOT0 + t];   // group A: waves 0..3, rows in order
         } else {
             const int r = t - NB, ls = r / (K * K), tap = r - ls * (K * K);
             const int l = ls / 4 + 1, s = ls - (l - 1) * 4;   // taps are ordered [L][4][K*K]
             const int w = P::group_of(l) * 4 + s, slot = P::slot_of(l);
-            v = slot == 0 ? red0[w * SLOT0 + tap] : redl[(w * (NSLOT - 1) + slot - 1) * K * K + tap];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v += slot == 0 ? red0[(w * 4 + q) * SLOT0 + tap]
+                               : redl[((w * 4 + q) * (NSLOT - 1) + slot - 1) * K * K + tap];
         }
         dst[t] = v;
     }
+}
+
+template <class P, typename T, bool BASE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::template waves_per_eu<T>())))
+void bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part,
+                 float* __restrict__ px, float* __restrict__ pdy, int B, int C, int bpc) {
+    __shared__ __attribute__((aligned(16))) float lds[P::template lds_floats<T>()];
+    bwdw_body<P, T, BASE>(x, dy, part, px, pdy, B, C, bpc, lds);
+}
+
+// A level split in one workgroup: the fine pass over the chunk (base and
+// levels 1..L, writing the chunk's level-L LL planes), then the coarse pass
+// over the same planes (levels L+1..LT), read back from L2, with the same LDS.
+template <class FP, class CP, typename T>
+constexpr int split_waves() {
+    const int a = FP::template waves_per_eu<T>(), b = CP::template waves_per_eu<float>();
+    return a < b ? a : b;
+}
+template <class FP, class CP, typename T>
+constexpr int split_lds() {
+    const int a = FP::template lds_floats<T>(), b = CP::template lds_floats<float>();
+    return a > b ? a : b;
+}
+template <class FP, class CP, typename T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(split_waves<FP, CP, T>())))
+void bwdw_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ partA,
+                       float* __restrict__ partB, float* __restrict__ px, float* __restrict__ pdy, int B, int C,
+                       int bpc) {
+    __shared__ __attribute__((aligned(16))) float lds[split_lds<FP, CP, T>()];
+    bwdw_body<FP, T, true>(x, dy, partA, px, pdy, B, C, bpc, lds);
+    // the LL planes this workgroup wrote become visible to it; LDS is free
+    __syncthreads();
+    bwdw_body<CP, float, false>(px, pdy, partB, nullptr, nullptr, B, C, bpc, lds);
 }
 
 // Threads of the finalize kernel: one per tap, whole wavefronts.
@@ -1076,12 +1123,17 @@ static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_
 // levels 1..L (one or two tap slots per lane, so more workgroups fit a CU)
 // and writes the level-L LL sums; the coarse pass does levels L+1..LT
 template <class FP, class CP>
+static int plane_split_slots() {
+    const int a = cu_count() * (split_waves<FP, CP, bf16_t>() * 4 / FP::NW);
+    const int b = cu_count() * (split_waves<FP, CP, float>() * 4 / FP::NW);
+    return (a > b ? a : b) < 1 ? 1 : (a > b ? a : b);
+}
+
+template <class FP, class CP>
 static size_t plane_split_ws(int B, int C) {
-    const int slots = bw_slots<FP, bf16_t>() > bw_slots<FP, float>() ? bw_slots<FP, bf16_t>() : bw_slots<FP, float>();
-    const int nA = cdiv(B, chunk_units(B, C, slots));
-    const int nB = cdiv(B, chunk_units(B, C, bw_slots<CP, float>()));
-    size_t n = align256((size_t)nA * C * FP::TAPS * sizeof(float));
-    n += align256((size_t)nB * C * 4 * (FP::LT - FP::L) * FP::K * FP::K * sizeof(float));
+    const int nch = cdiv(B, chunk_units(B, C, plane_split_slots<FP, CP>()));
+    size_t n = align256((size_t)nch * C * FP::TAPS * sizeof(float));
+    n += align256((size_t)nch * C * 4 * (FP::LT - FP::L) * FP::K * FP::K * sizeof(float));
     n += 2 * align256((size_t)B * C * (FP::H >> FP::L) * (FP::W >> FP::L) * sizeof(float));
     return n;
 }
@@ -1091,31 +1143,27 @@ static hipError_t plane_split_launch(const void* x, const void* dy, const float*
                                      float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
                                      hipStream_t stream) {
     static_assert(FP::LT > FP::L && CP::LT == CP::L && CP::KB == 1 && CP::K == FP::K &&
-                      CP::L == FP::LT - FP::L && CP::H == (FP::H >> FP::L) && CP::W == (FP::W >> FP::L),
+                      CP::L == FP::LT - FP::L && CP::H == (FP::H >> FP::L) && CP::W == (FP::W >> FP::L) &&
+                      FP::NT == CP::NT,
                   "coarse plan: levels L+1..LT of the fine plan on its LL planes");
-    const int slots = bw_slots<FP, bf16_t>() > bw_slots<FP, float>() ? bw_slots<FP, bf16_t>() : bw_slots<FP, float>();
-    const int nA_ws = cdiv(B, chunk_units(B, C, slots));
-    const int bpcA = chunk_units(B, C, bw_slots<FP, T>()), nA = cdiv(B, bpcA);
-    const int bpcB = chunk_units(B, C, bw_slots<CP, float>()), nB = cdiv(B, bpcB);
+    const int nch_ws = cdiv(B, chunk_units(B, C, plane_split_slots<FP, CP>()));
+    const int slots = cu_count() * (split_waves<FP, CP, T>() * 4 / FP::NW);
+    const int bpc = chunk_units(B, C, slots < 1 ? 1 : slots), nch = cdiv(B, bpc);
     char* cur = (char*)ws;
     float* partA = (float*)cur;
-    cur += align256((size_t)nA_ws * C * FP::TAPS * sizeof(float));
+    cur += align256((size_t)nch_ws * C * FP::TAPS * sizeof(float));
     float* partB = (float*)cur;
-    cur += align256((size_t)nB * C * 4 * (FP::LT - FP::L) * FP::K * FP::K * sizeof(float));
+    cur += align256((size_t)nch_ws * C * 4 * (FP::LT - FP::L) * FP::K * FP::K * sizeof(float));
     const size_t pl = (size_t)B * C * (FP::H >> FP::L) * (FP::W >> FP::L) * sizeof(float);
     float* px = (float*)cur;
     cur += align256(pl);
     float* pdy = (float*)cur;
-    hipLaunchKernelGGL((bwdw_kernel<FP, T, true>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
-                       (const T*)x, (const T*)dy, partA, px, pdy, B, C, bpcA);
+    hipLaunchKernelGGL((bwdw_split_kernel<FP, CP, T>), dim3((unsigned)(nch * C)), dim3(FP::NT), 0, stream,
+                       (const T*)x, (const T*)dy, partA, partB, px, pdy, B, C, bpc);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((bwdw_kernel<CP, float, false>), dim3((unsigned)(nB * C)), dim3(CP::NT), 0, stream,
-                       (const float*)px, (const float*)pdy, partB, (float*)nullptr, (float*)nullptr, B, C, bpcB);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(FP::KB, FP::K, FP::LT)), 0,
-                       stream, (const float*)partA, nA, FP::L, (const float*)partB, nB, C, FP::LT, FP::KB, FP::K,
+                       stream, (const float*)partA, nch, FP::L, (const float*)partB, nch, C, FP::LT, FP::KB, FP::K,
                        w_lvl, scale, dw_base, dw_lvl, dscale);
     return hipGetLastError();
 }
