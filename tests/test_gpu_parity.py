@@ -47,6 +47,11 @@ SMALL = [
     # then full-width fine tiles with a halo)
     (2, 3, 64, 64, 4, 3, 3),
     (2, 3, 64, 64, 2, 5, 5),
+    # batches that leave the last multi-plane step of a weight-gradient chunk
+    # partly empty (the whole-plane plans take several planes per step)
+    (11, 2, 14, 14, 1, 5, 5),
+    (7, 3, 28, 28, 2, 5, 5),
+    (5, 2, 56, 56, 3, 5, 5),
 ]
 
 

@@ -1044,7 +1044,8 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // whole planes: one kernel and the finalize
 template <class P>
 static size_t whole_ws(int B, int C) {
-    const int nchunk = cdiv(B, chunk_units(B, C));
+    const int slots = bw_slots<P, bf16_t>() > bw_slots<P, float>() ? bw_slots<P, bf16_t>() : bw_slots<P, float>();
+    const int nchunk = cdiv(B, chunk_units(B, C, slots));
     return (size_t)nchunk * C * P::TAPS * sizeof(float);
 }
 
@@ -1052,7 +1053,7 @@ template <class P, typename T>
 static hipError_t whole_launch(const void* x, const void* dy, const float* w_lvl, const float* scale,
                                float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
                                hipStream_t stream) {
-    const int bpc = chunk_units(B, C), nchunk = cdiv(B, bpc);
+    const int bpc = chunk_units(B, C, bw_slots<P, T>()), nchunk = cdiv(B, bpc);
     float* part = (float*)ws;
     hipLaunchKernelGGL((bwdw_kernel<P, T, true>), dim3((unsigned)(nchunk * C)), dim3(P::NT), 0, stream,
                        (const T*)x, (const T*)dy, part, (float*)nullptr, (float*)nullptr, B, C, bpc);
@@ -1179,8 +1180,8 @@ struct BwEntry {
 
 typedef BwPlan<32, 32, 2, 5, 5> BP_32_L2_k55;
 typedef BwPlan<56, 56, 3, 5, 5> BP_56_L3_k55;
-typedef BwPlan<28, 28, 2, 5, 5> BP_28_L2_k55;
-typedef BwPlan<14, 14, 1, 5, 5> BP_14_L1_k55;
+typedef BwPlan<28, 28, 2, 5, 5, 2, 4> BP_28_L2_k55;
+typedef BwPlan<14, 14, 1, 5, 5, 1, 8> BP_14_L1_k55;
 typedef BwPlan<32, 32, 3, 7, 5> BP_32_L3_k75;
 typedef BwPlan<24, 40, 3, 3, 3> BP_24x40_L3_k33;
 typedef BwPlan<16, 16, 4, 3, 7> BP_16_L4_k37;
@@ -1192,15 +1193,15 @@ typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16> TB_128_L2_k55;
 typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16> TB_128_L2of3_k55;
 typedef TileBwPlan<128, 128, 2, 4, 5, 5, 16> TB_128_L2of4_k55;
 typedef TileBwPlan<128, 128, 2, 5, 5, 5, 16> TB_128_L2of5_k55;
-typedef BwPlan<32, 32, 1, 1, 5> CB_32_L1_k5;
-typedef BwPlan<32, 32, 2, 1, 5> CB_32_L2_k5;
-typedef BwPlan<32, 32, 3, 1, 5> CB_32_L3_k5;
+typedef BwPlan<32, 32, 1, 1, 5, 1, 4> CB_32_L1_k5;
+typedef BwPlan<32, 32, 2, 1, 5, 2, 4> CB_32_L2_k5;
+typedef BwPlan<32, 32, 3, 1, 5, 3, 4> CB_32_L3_k5;
 typedef TileBwPlan<256, 256, 2, 4, 7, 5, 8> TB_256_L2of4_k75;
 typedef BwPlan<64, 64, 2, 1, 5> CB_64_L2_k5;
 typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8> TB_64_L2of4_k33;
-typedef BwPlan<16, 16, 2, 1, 3> CB_16_L2_k3;
+typedef BwPlan<16, 16, 2, 1, 3, 2, 8> CB_16_L2_k3;
 typedef TileBwPlan<64, 64, 1, 2, 5, 5, 16> TB_64_L1of2_k55;
-typedef BwPlan<32, 32, 1, 1, 5> CB_32_L1_k5b;
+typedef BwPlan<32, 32, 1, 1, 5, 1, 4> CB_32_L1_k5b;
 
 // whole planes split by level (fine: base + level 1; coarse: the rest)
 typedef BwPlan<56, 56, 1, 5, 5, 3> WP_56_L1of3_k55;
