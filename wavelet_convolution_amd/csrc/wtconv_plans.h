@@ -221,7 +221,10 @@ namespace wtc {
 #ifndef WTC_COL56_NT
 #define WTC_COL56_NT 512
 #endif
-typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, 7> CP_56_L3_k55;
+#ifndef WTC_COL56_WMAX
+#define WTC_COL56_WMAX 8
+#endif
+typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, WTC_COL56_WMAX> CP_56_L3_k55;
 typedef ColPlan<28, 28, 2, 5, 5, 256, 4, 7> CP_28_L2_k55;
 typedef ColPlan<14, 14, 1, 5, 5, 128, 2, 7> CP_14_L1_k55;
 typedef ColPlan<128, 128, 1, 5, 5, 1024, 8, 8> CP_128_L1_k55;
