@@ -295,8 +295,9 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     // U_l (and then Z'_l) of level l: level 1 in region B, the others in A
     auto ubase = [&](auto lc) -> float* {
         constexpr int l = decltype(lc)::value;
+        constexpr int off = P::uoff(l);   // evaluated at compile time
         if constexpr (l == 1) return Bq;
-        else return A + P::uoff(l);
+        else return A + off;
     };
 
     // ---------------------------------------------------------------- P0
@@ -309,30 +310,47 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
     }
     {
-        // The whole bordered x plane in VL-element units, one aligned vector
-        // store each: units inside the plane carry x, the rest zeros (the
-        // border the base convolution reads).
-        constexpr int UPR = SX / VL, NU = (H + 2 * PB) * UPR;
-        constexpr int NL = cdiv(NU, NT);
-        RawVec<T, VL> v[NL];
-        auto inside = [&](int q, int& e) {
-            const int r = q / UPR, col = (q - r * UPR) * VL - XO, h = r - PB;
-            e = h * W + col;
-            return h >= 0 && h < H && col >= 0 && col < W;
-        };
+        // The whole bordered x plane and the bordered level-1 bands in one
+        // pass. An item owns x rows 2i, 2i+1 and VA columns from 2*j0 (one
+        // or two Haar blocks, band cells j0.. of row i): inside the plane it
+        // loads them, stores them widened and stores their four bands; on
+        // the border it stores zeros to both (the padding of the base
+        // convolution and of the level-1 convolutions).
+        constexpr int NQ = P::NQ, IPR = P::IPR, CPI = P::CPI, VA = P::VA, MQ = cdiv(NQ, NT);
+        RawVec<T, VA> r0[MQ], r1[MQ];
 #pragma unroll
-        for (int k = 0; k < NL; ++k) {
+        for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
-            int e;
-            if ((NU % NT == 0 || q < NU) && inside(q, e)) load_raw<T, VL>(src + e, v[k]);
-            else
+            const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
+            if ((NQ % NT == 0 || q < NQ) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1) {
+                const T* s0 = src + (size_t)(2 * i) * W + 2 * j0;
+                load_raw<T, VA>(s0, r0[k]);
+                load_raw<T, VA>(s0 + W, r1[k]);
+            } else {
 #pragma unroll
-                for (int i = 0; i < RawVec<T, VL>::N; ++i) v[k].w[i] = 0u;
+                for (int e = 0; e < RawVec<T, VA>::N; ++e) r0[k].w[e] = r1[k].w[e] = 0u;
+            }
         }
 #pragma unroll
-        for (int k = 0; k < NL; ++k) {
+        for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
-            if (NU % NT == 0 || q < NU) store_lds<T, VL>(A + q * VL, v[k]);
+            if (!(NQ % NT == 0 || q < NQ)) continue;
+            const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
+            float f0[VA], f1[VA];
+            widen_raw<T, VA>(r0[k], f0);
+            widen_raw<T, VA>(r1[k], f1);
+            const int xr = PB + 2 * i, xc = XO + 2 * j0;
+            if (xc >= 0 && xc + VA <= SX) {
+                if (xr >= 0 && xr < H + 2 * PB) store_vec<VA>(A + xr * SX + xc, f0);
+                if (xr + 1 >= 0 && xr + 1 < H + 2 * PB) store_vec<VA>(A + (xr + 1) * SX + xc, f1);
+            }
+            float b[4][CPI];
+#pragma unroll
+            for (int m = 0; m < CPI; ++m)
+                haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], b[0][m], b[1][m], b[2][m], b[3][m]);
+            float* o = Bq + ii * S1 + uu * CPI;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) store_vec<CPI>(o + s * BS1, b[s]);
         }
     }
     __syncthreads();
@@ -348,23 +366,6 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             if (LPB == W || w < W) conv_col<KB, RB, SX>(X0 + (rb * RB) * SX + w, WB, yb[it]);
         }
     }
-    // level-1 bands over their bordered grid: zeros on the border
-    {
-        constexpr int GW = W1 + 2 * PK, GN = (H1 + 2 * PK) * GW;
-        for (int q = tid; q < GN; q += NT) {
-            const int ii = q / GW, jj = q - ii * GW, i = ii - PK, j = jj - PK;
-            float b[4] = {0.f, 0.f, 0.f, 0.f};
-            if (i >= 0 && i < H1 && j >= 0 && j < W1) {
-                // 2x2 blocks start on even columns of 8-byte aligned rows
-                const float2 x01 = *reinterpret_cast<const float2*>(A + (PB + 2 * i) * SX + XO + 2 * j);
-                const float2 x23 = *reinterpret_cast<const float2*>(A + (PB + 2 * i + 1) * SX + XO + 2 * j);
-                haar4(x01.x, x01.y, x23.x, x23.y, b[0], b[1], b[2], b[3]);
-            }
-            const int o = ii * S1 + jj;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Bq[s * BS1 + o] = b[s];
-        }
-    }
     __syncthreads();
 
     // ---------------------------------------------------------------- P2
@@ -372,8 +373,9 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
         constexpr int Sp = P::su(l - 1);
-        float* Ul = A + P::uoff(l);
-        const float* LLp = (l == 2) ? (Bq + PK * Sp + PK) : (A + P::uoff(l - 1) + PK * Sp + PK);
+        constexpr int UO = P::uoff(l), UP = P::uoff(l - 1);
+        float* Ul = A + UO;
+        const float* LLp = (l == 2) ? (Bq + PK * Sp + PK) : (A + UP + PK * Sp + PK);
         // over the bordered grid: zeros on the border
         constexpr int GW = wl + 2 * PK, GN = (hl + 2 * PK) * GW;
         for (int q = tid; q < GN; q += NT) {
@@ -425,23 +427,64 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             }
         }
     };
+    // one level-2..L strip per thread when they all fit (fewer live registers)
+    auto deep_conv = [&](auto lc, float (&zd)[P::RLD]) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), O = P::doff(l);
+        float* Ul = ubase(lc);
+        const int item = tid - O;
+        if (item >= 0 && item < NIl) {
+            const int s = item / (NS * LP), rem = item - s * (NS * LP);
+            const int rs = rem / LP, j = rem - rs * LP;
+            if (LP == wl || j < wl) {
+                float z[R];
+                conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z);
+#pragma unroll
+                for (int o = 0; o < R; ++o) zd[o] = z[o];
+            }
+        }
+    };
+    auto deep_store = [&](auto lc, const float (&zd)[P::RLD]) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), O = P::doff(l);
+        float* Ul = ubase(lc);
+        const int item = tid - O;
+        if (item >= 0 && item < NIl) {
+            const int s = item / (NS * LP), rem = item - s * (NS * LP);
+            const int rs = rem / LP, j = rem - rs * LP;
+            if (LP == wl || j < wl) {
+#pragma unroll
+                for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = zd[o];
+            }
+        }
+    };
     // results of all levels stay in registers across one barrier
     float z1[cdiv(P::nil(1), NT)][P::rl(1)];
     level_conv(std::integral_constant<int, 1>{}, z1);
-    float z2[L >= 2 ? cdiv(P::nil(L >= 2 ? 2 : 1), NT) : 1][P::rl(L >= 2 ? 2 : 1)];
-    float z3[L >= 3 ? cdiv(P::nil(L >= 3 ? 3 : 1), NT) : 1][P::rl(L >= 3 ? 3 : 1)];
-    float z4[L >= 4 ? cdiv(P::nil(L >= 4 ? 4 : 1), NT) : 1][P::rl(L >= 4 ? 4 : 1)];
-    float z5[L >= 5 ? cdiv(P::nil(L >= 5 ? 5 : 1), NT) : 1][P::rl(L >= 5 ? 5 : 1)];
-    if constexpr (L >= 2) level_conv(std::integral_constant<int, 2>{}, z2);
-    if constexpr (L >= 3) level_conv(std::integral_constant<int, 3>{}, z3);
-    if constexpr (L >= 4) level_conv(std::integral_constant<int, 4>{}, z4);
-    if constexpr (L >= 5) level_conv(std::integral_constant<int, 5>{}, z5);
-    __syncthreads();
-    level_store(std::integral_constant<int, 1>{}, z1);
-    if constexpr (L >= 2) level_store(std::integral_constant<int, 2>{}, z2);
-    if constexpr (L >= 3) level_store(std::integral_constant<int, 3>{}, z3);
-    if constexpr (L >= 4) level_store(std::integral_constant<int, 4>{}, z4);
-    if constexpr (L >= 5) level_store(std::integral_constant<int, 5>{}, z5);
+    if constexpr (P::DSHARE) {
+        float zd[P::RLD];
+        P::for_deep_levels([&](auto lc) { deep_conv(lc, zd); });
+        __syncthreads();
+        level_store(std::integral_constant<int, 1>{}, z1);
+        P::for_deep_levels([&](auto lc) { deep_store(lc, zd); });
+    } else {
+        float z2[L >= 2 ? cdiv(P::nil(L >= 2 ? 2 : 1), NT) : 1][P::rl(L >= 2 ? 2 : 1)];
+        float z3[L >= 3 ? cdiv(P::nil(L >= 3 ? 3 : 1), NT) : 1][P::rl(L >= 3 ? 3 : 1)];
+        float z4[L >= 4 ? cdiv(P::nil(L >= 4 ? 4 : 1), NT) : 1][P::rl(L >= 4 ? 4 : 1)];
+        float z5[L >= 5 ? cdiv(P::nil(L >= 5 ? 5 : 1), NT) : 1][P::rl(L >= 5 ? 5 : 1)];
+        if constexpr (L >= 2) level_conv(std::integral_constant<int, 2>{}, z2);
+        if constexpr (L >= 3) level_conv(std::integral_constant<int, 3>{}, z3);
+        if constexpr (L >= 4) level_conv(std::integral_constant<int, 4>{}, z4);
+        if constexpr (L >= 5) level_conv(std::integral_constant<int, 5>{}, z5);
+        __syncthreads();
+        level_store(std::integral_constant<int, 1>{}, z1);
+        if constexpr (L >= 2) level_store(std::integral_constant<int, 2>{}, z2);
+        if constexpr (L >= 3) level_store(std::integral_constant<int, 3>{}, z3);
+        if constexpr (L >= 4) level_store(std::integral_constant<int, 4>{}, z4);
+        if constexpr (L >= 5) level_store(std::integral_constant<int, 5>{}, z5);
+    }
     __syncthreads();
 
     // ---------------------------------------------------------------- P4

@@ -139,6 +139,41 @@ typedef PlanePlan<64, 64, 4, 7, 5, 64, 4, 4> PP_64_L4_k75;
 
 namespace wtc {
 
+// Row stride of a bordered band grid (hl x wl, border pk) for the
+// column-strip level convolution. The lanes of one 32-lane LDS pass read one
+// row of each strip they hold: several strips (rows r apart, or other bands)
+// when the band is narrower than 32 columns. The stride is the smallest, at
+// least the bordered width (and even when asked), with the fewest bank
+// conflicts summed over the passes.
+constexpr int band_stride(int hl, int wl, int pk, int r, bool even) {
+    const int w0 = wl + 2 * pk;
+    const int base = even ? round_up(w0, 2) : w0;
+    const int lp = strip_lanes(wl);
+    if (lp >= 32) return base;
+    const int ns = hl / r, items = 4 * ns * lp;
+    int best = base, best_cost = 1 << 30;
+    for (int S = base; S < base + 64; S += (even ? 2 : 1)) {
+        const int bs = (hl + 2 * pk) * S;
+        int cost = 0;
+        for (int h0 = 0; h0 < items; h0 += 32) {
+            int cnt[32] = {};
+            int worst = 0;
+            for (int t = h0; t < h0 + 32 && t < items; ++t) {
+                const int s = t / (ns * lp), rem = t - s * (ns * lp), rs = rem / lp, j = rem - rs * lp;
+                if (j >= wl) continue;
+                const int b = (s * bs + rs * r * S + j) % 32;
+                if (++cnt[b] > worst) worst = cnt[b];
+            }
+            cost += worst;
+        }
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = S;
+        }
+    }
+    return best;
+}
+
 // Column-strip variant of the whole-plane plan: a lane computes RB rows x 1
 // column of the base convolution, and RL rows x 1 column of one band at each
 // level, so the lanes of a wavefront read consecutive LDS words (no bank
@@ -165,8 +200,21 @@ struct ColPlan {
     static constexpr int XO = round_up(PB, 4);
     static constexpr int SX = round_up(XO + W + PB, 4);
     static constexpr int XSIZE = (H + 2 * PB) * SX;
-    static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
+    // level-1 analysis items: 2 x rows by VA columns (VA / 2 Haar blocks),
+    // over the bordered level-1 grid; the items on the border write the
+    // zeros of the band border and of the x border
+    static constexpr int VA = VL >= 4 ? 4 : 2;
+    static constexpr int CPI = VA / 2;
+    static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
+    // band rows: level-1 cell pairs are stored as aligned 64-bit words
+    // (an even stride); see band_stride for the rest
+    static constexpr int su(int l) { return band_stride(H >> l, W >> l, PK, rl(l), l == 1 && CPI == 2); }
     static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
+    static constexpr int IPR = ((W >> 1) + 2 * PK) / CPI;
+    static constexpr int NQ = ((H >> 1) + 2 * PK) * IPR;
+    static_assert(VL % 2 == 0, "rows of whole Haar blocks");
+    static_assert(PK % CPI == 0 && (XO - 2 * PK) % VA == 0 && PB <= 2 * PK && XO + W + 2 * PK >= SX,
+                  "analysis items cover the bordered x plane in whole vectors");
     static constexpr int uoff(int l) {
         int o = 0;
         for (int q = 2; q < l; ++q) o += 4 * bandsz(q);
@@ -183,9 +231,17 @@ struct ColPlan {
     static constexpr int NIB = (H / RB) * LPB;   // base strip slots
     static constexpr int MB = cdiv(NIB, NT);
     // rows per strip at level l, lanes per row block, strip slots (4 bands)
-    static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
     static constexpr int lpl(int l) { return strip_lanes(W >> l); }
     static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * lpl(l); }
+    // levels 2..L share one register strip per thread when all their strip
+    // slots fit the workgroup: level l takes threads [doff(l), doff(l) + nil(l))
+    static constexpr int doff(int l) {
+        int o = 0;
+        for (int q = 2; q < l; ++q) o += nil(q);
+        return o;
+    }
+    static constexpr bool DSHARE = L >= 2 && doff(L + 1) <= NT;
+    static constexpr int RLD = L >= 2 ? rl(2) : 1;
     // occupancy the LDS footprint allows, at most WMAX waves per SIMD (a
     // plan whose registers need more than 512 / WMAX lowers WMAX)
     static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
