@@ -139,36 +139,61 @@ typedef PlanePlan<64, 64, 4, 7, 5, 64, 4, 4> PP_64_L4_k75;
 
 namespace wtc {
 
-// Row stride of a bordered band grid (hl x wl, border pk) for the
-// column-strip level convolution. The lanes of one 32-lane LDS pass read one
-// row of each strip they hold: several strips (rows r apart, or other bands)
-// when the band is narrower than 32 columns. The stride is the smallest, at
-// least the bordered width (and even when asked), with the fewest bank
-// conflicts summed over the passes.
-constexpr int band_stride(int hl, int wl, int pk, int r, bool even) {
-    const int w0 = wl + 2 * pk;
-    const int base = even ? round_up(w0, 2) : w0;
-    const int lp = strip_lanes(wl);
-    if (lp >= 32) return base;
+// Bank conflicts of the column-strip level convolution over a bordered band
+// grid (hl x wl, border pk, 4 bands `pitch` floats apart, rows `S` floats
+// apart): strip slot t holds band s, strip rs (r rows) and column j, with lp
+// slots per strip (the slots past wl idle). The lanes of one 32-lane LDS pass
+// read one row of each strip they hold; the cost sums, over the passes, the
+// largest number of lanes that read the same bank.
+constexpr int strip_conflicts(int hl, int wl, int r, int lp, int S, int pitch) {
     const int ns = hl / r, items = 4 * ns * lp;
-    int best = base, best_cost = 1 << 30;
-    for (int S = base; S < base + 64; S += (even ? 2 : 1)) {
-        const int bs = (hl + 2 * pk) * S;
-        int cost = 0;
-        for (int h0 = 0; h0 < items; h0 += 32) {
-            int cnt[32] = {};
-            int worst = 0;
-            for (int t = h0; t < h0 + 32 && t < items; ++t) {
-                const int s = t / (ns * lp), rem = t - s * (ns * lp), rs = rem / lp, j = rem - rs * lp;
-                if (j >= wl) continue;
-                const int b = (s * bs + rs * r * S + j) % 32;
-                if (++cnt[b] > worst) worst = cnt[b];
-            }
-            cost += worst;
+    int cost = 0;
+    for (int h0 = 0; h0 < items; h0 += 32) {
+        int cnt[32] = {};
+        int worst = 0;
+        for (int t = h0; t < h0 + 32 && t < items; ++t) {
+            const int s = t / (ns * lp), rem = t - s * (ns * lp), rs = rem / lp, j = rem - rs * lp;
+            if (j >= wl) continue;
+            const int b = (s * pitch + rs * r * S + j) % 32;
+            if (++cnt[b] > worst) worst = cnt[b];
         }
+        cost += worst;
+    }
+    return cost;
+}
+
+// Layout of a level's bands for the column-strip convolution: row stride s
+// (at least the bordered width, even when asked), band pitch, and strip
+// slots per strip lp.
+//  - Strips narrower than 32 columns normally get a power of two of lanes
+//    (strip_lanes), the rest idle. If dropping that padding saves whole
+//    wavefronts, strips are packed back to back instead, with a stride and
+//    pitch that put slot t on bank t + const (mod 32): r * s = wl and
+//    pitch = (hl / r) * wl (mod 32), so no pass has a conflict.
+//  - Otherwise the stride is the smallest with the fewest conflicts.
+struct BandLayout {
+    int s, pitch, lp;
+};
+constexpr BandLayout band_layout(int hl, int wl, int pk, int r, bool even) {
+    const int w0 = wl + 2 * pk, base = even ? round_up(w0, 2) : w0, rows = hl + 2 * pk;
+    const int lpad = strip_lanes(wl), ns = hl / r;
+    if (lpad > wl && cdiv(4 * ns * wl, 64) < cdiv(4 * ns * lpad, 64)) {
+        for (int S = base; S < base + 64; S += (even ? 2 : 1)) {
+            if ((r * S - wl) % 32 != 0) continue;
+            int pitch = rows * S;
+            while ((pitch - ns * wl) % 32 != 0) ++pitch;
+            if (even && pitch % 2 != 0) break;
+            return BandLayout{S, pitch, wl};
+        }
+    }
+    if (lpad >= 32) return BandLayout{base, rows * base, lpad};
+    BandLayout best{base, rows * base, lpad};
+    int best_cost = 1 << 30;
+    for (int S = base; S < base + 64; S += (even ? 2 : 1)) {
+        const int cost = strip_conflicts(hl, wl, r, lpad, S, rows * S);
         if (cost < best_cost) {
             best_cost = cost;
-            best = S;
+            best = BandLayout{S, rows * S, lpad};
         }
     }
     return best;
@@ -207,9 +232,10 @@ struct ColPlan {
     static constexpr int CPI = VA / 2;
     static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
     // band rows: level-1 cell pairs are stored as aligned 64-bit words
-    // (an even stride); see band_stride for the rest
-    static constexpr int su(int l) { return band_stride(H >> l, W >> l, PK, rl(l), l == 1 && CPI == 2); }
-    static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
+    // (an even stride); see band_layout for the rest
+    static constexpr BandLayout lay(int l) { return band_layout(H >> l, W >> l, PK, rl(l), l == 1 && CPI == 2); }
+    static constexpr int su(int l) { return lay(l).s; }
+    static constexpr int bandsz(int l) { return lay(l).pitch; }   // band pitch
     static constexpr int IPR = ((W >> 1) + 2 * PK) / CPI;
     static constexpr int NQ = ((H >> 1) + 2 * PK) * IPR;
     static_assert(VL % 2 == 0, "rows of whole Haar blocks");
@@ -231,7 +257,7 @@ struct ColPlan {
     static constexpr int NIB = (H / RB) * LPB;   // base strip slots
     static constexpr int MB = cdiv(NIB, NT);
     // rows per strip at level l, lanes per row block, strip slots (4 bands)
-    static constexpr int lpl(int l) { return strip_lanes(W >> l); }
+    static constexpr int lpl(int l) { return lay(l).lp; }
     static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * lpl(l); }
     // levels 2..L share one register strip per thread when all their strip
     // slots fit the workgroup: level l takes threads [doff(l), doff(l) + nil(l))
