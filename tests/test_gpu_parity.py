@@ -47,6 +47,8 @@ SMALL = [
     # then full-width fine tiles with a halo)
     (2, 3, 64, 64, 4, 3, 3),
     (2, 3, 64, 64, 2, 5, 5),
+    # the large-plane column tiles (7x7 base, coarse pass on the level-2 sums)
+    (1, 2, 256, 256, 4, 7, 5),
     # batches that leave the last multi-plane step of a weight-gradient chunk
     # partly empty (the whole-plane plans take several planes per step)
     (11, 2, 14, 14, 1, 5, 5),
