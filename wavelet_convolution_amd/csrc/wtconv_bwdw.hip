@@ -44,16 +44,17 @@ __device__ __forceinline__ void taps_col(const float* u, const VT* v, float (&ac
     for (int o = 0; o < R; ++o) vt[o] = widen(v[o * SV]);
     // a ring of D + 1 window rows: row r + D is requested before row r's
     // multiply-adds, so LDS latency hides behind D rows of them
+    const RowAddr<SU, NR> row(u);
     float win[D + 1][K];
 #pragma unroll
     for (int r = 0; r < D && r < NR; ++r)
 #pragma unroll
-        for (int n = 0; n < K; ++n) win[r][n] = u[r * SU + n];
+        for (int n = 0; n < K; ++n) win[r][n] = row(r, n);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         if (r + D < NR) {
 #pragma unroll
-            for (int n = 0; n < K; ++n) win[(r + D) % (D + 1)][n] = u[(r + D) * SU + n];
+            for (int n = 0; n < K; ++n) win[(r + D) % (D + 1)][n] = row(r + D, n);
         }
 #pragma unroll
         for (int o = 0; o < R; ++o) {

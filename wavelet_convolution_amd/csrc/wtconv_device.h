@@ -214,6 +214,42 @@ __device__ __forceinline__ void pin_regs(float (&v)[R][N]) {
     for (int r = 0; r < R; ++r) pin_regs(v[r]);
 }
 
+// LDS row addressing for window loads. The backend pairs dword loads that
+// share a base into one two-address load whose offsets reach 1 KB; beyond
+// that it makes a fresh base register for each pair (one VALU add per two
+// loads). Window rows are therefore read from a base the compiler cannot see
+// through (an empty asm), renewed every GROUP rows so that every pair's
+// offsets stay in range: one add per GROUP rows.
+typedef const float __attribute__((address_space(3)))* lds_cfp;
+__device__ __forceinline__ lds_cfp opaque_lds(const float* p) {
+    uint32_t a = (uint32_t)(uintptr_t)(lds_cfp)p;
+    asm volatile("" : "+v"(a));
+    return (lds_cfp)(uintptr_t)a;
+}
+template <int S>
+struct RowBases {
+    // rows per base: the farthest pair offset (GROUP-1 rows + 7 words) under
+    // 1 KB; rows too long for two in one group keep the compiler's addressing
+    static constexpr int GROUP = (1020 / 4 - 8) / S + 1;
+    static constexpr bool USE = GROUP >= 2;
+};
+template <int S, int NR>
+struct RowAddr {
+    static constexpr int GR = RowBases<S>::USE ? RowBases<S>::GROUP : NR;
+    lds_cfp rb[cdiv(NR, GR)];
+    const float* p;
+    __device__ __forceinline__ explicit RowAddr(const float* base) : p(base) {
+        if constexpr (RowBases<S>::USE) {
+#pragma unroll
+            for (int g = 0; g < cdiv(NR, GR); ++g) rb[g] = opaque_lds(base + g * GR * S);
+        }
+    }
+    __device__ __forceinline__ float operator()(int r, int n) const {
+        if constexpr (RowBases<S>::USE) return rb[r / GR][(r % GR) * S + n];
+        else return p[r * S + n];
+    }
+};
+
 // acc[o][q] += sum_{m,n} w[m][n] * s[(o+m)*S + q+n]: an OR x OC tile of a
 // 'same' cross-correlation read from a zero-bordered LDS plane (s points at
 // the window's top-left corner, S is the plane's row stride). The K*K taps
@@ -284,14 +320,16 @@ __device__ __forceinline__ void conv_col(const float* s, const float* w, float (
     }
     // window rows double-buffered: row r+1 is requested before row r's
     // multiply-adds, so its LDS latency hides behind them
+    constexpr int NR = R + K - 1;
+    const RowAddr<S, NR> row(s);
     float win[2][K];
 #pragma unroll
-    for (int n = 0; n < K; ++n) win[0][n] = s[n];
+    for (int n = 0; n < K; ++n) win[0][n] = row(0, n);
 #pragma unroll
-    for (int r = 0; r < R + K - 1; ++r) {
-        if (r + 1 < R + K - 1) {
+    for (int r = 0; r < NR; ++r) {
+        if (r + 1 < NR) {
 #pragma unroll
-            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = s[(r + 1) * S + n];
+            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = row(r + 1, n);
         }
 #pragma unroll
         for (int o = 0; o < R; ++o) {

@@ -322,13 +322,16 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
             const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
-            if ((NQ % NT == 0 || q < NQ) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1) {
-                const T* s0 = src + (size_t)(2 * i) * W + 2 * j0;
-                load_raw<T, VA>(s0, r0[k]);
-                load_raw<T, VA>(s0 + W, r1[k]);
-            } else {
+            const bool inside = (NQ % NT == 0 || q < NQ) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1;
+            // every lane loads (border items the plane's first words) and
+            // then selects zeros: no branch, so the registers stay registers
+            const T* s0 = src + (inside ? (2 * i) * W + 2 * j0 : 0);
+            load_raw<T, VA>(s0, r0[k]);
+            load_raw<T, VA>(s0 + (inside ? W : 0), r1[k]);
 #pragma unroll
-                for (int e = 0; e < RawVec<T, VA>::N; ++e) r0[k].w[e] = r1[k].w[e] = 0u;
+            for (int e = 0; e < RawVec<T, VA>::N; ++e) {
+                r0[k].w[e] = inside ? r0[k].w[e] : 0u;
+                r1[k].w[e] = inside ? r1[k].w[e] : 0u;
             }
         }
 #pragma unroll
