@@ -319,7 +319,7 @@ def _torch_layer(x, wb, wl, sc):
     L = wl.shape[0]
     kb, k = wb.shape[-1], wl.shape[-1]
     h = torch.tensor([[[1, 1], [1, 1]], [[1, 1], [-1, -1]], [[1, -1], [1, -1]], [[1, -1], [-1, 1]]],
-                     dtype=x.dtype) / 2
+                     dtype=x.dtype, device=x.device) / 2
     filt = h[None].repeat(C, 1, 1, 1).reshape(4 * C, 1, 2, 2)
     y = torch.nn.functional.conv2d(x, wb[:, None], padding=kb // 2, groups=C)
     lls, zs = [x], []

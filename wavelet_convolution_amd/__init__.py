@@ -13,7 +13,9 @@ _BINDING_NAMES = (
     "wtconv_workspace_size", "wtconv_status_string", "load_library", "WTConvError",
 )
 
-__all__ = ["CONFIGS", "WorkloadConfig", "get_config", *_BINDING_NAMES]
+_MODULE_NAMES = ("WTConv2d", "WTConvFunction", "wtconv")
+
+__all__ = ["CONFIGS", "WorkloadConfig", "get_config", *_BINDING_NAMES, *_MODULE_NAMES]
 
 
 def __getattr__(name):
@@ -22,4 +24,7 @@ def __getattr__(name):
     if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)
+    if name in _MODULE_NAMES:
+        from . import module
+        return getattr(module, name)
     raise AttributeError(name)

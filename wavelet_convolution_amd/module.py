@@ -1,0 +1,100 @@
+"""Drop-in WTConv layer for PyTorch: an autograd Function and an nn.Module
+over the C-ABI entry points.
+
+The forward pass keeps only x (and the parameters) for the backward pass:
+``wtconv_bwd_data`` and ``wtconv_bwd_weight`` rebuild the Haar pyramid of x
+and dy on chip, so no band tensor is stored between the passes. Every step
+of the computation runs in libwtconv.so; this file allocates outputs and
+marshals arguments only. Tensors must be on the GPU: there is no CPU path.
+
+Layer (abstract of arXiv:2608.10805, the tech.sinsc.com page): a depthwise
+k_base x k_base convolution plus an L-level Haar branch, each level's four
+subbands convolved depthwise (k_level x k_level) and scaled per channel and
+band, the results synthesised back in one closed-form pass.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as _b
+
+
+def _check_device(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise RuntimeError("WTConv runs on the GPU only (libwtconv.so); got a tensor on "
+                               f"{t.device} - there is no CPU implementation")
+
+
+class WTConvFunction(torch.autograd.Function):
+    """y = WTConv(x; w_base, w_lvl, scale).
+
+    x: [B, C, H, W] fp32 or bf16 (contiguous NCHW), w_base: [C, kb, kb],
+    w_lvl: [L, C, 4, k, k], scale: [L, C, 4], all fp32. Gradients of the
+    parameters are fp32; the gradient of x has x's dtype.
+    """
+
+    @staticmethod
+    def forward(ctx, x, w_base, w_lvl, scale):
+        _check_device(x, w_base, w_lvl, scale)
+        x = x.contiguous()
+        y = _b.wtconv_fwd(x, w_base, w_lvl, scale)
+        ctx.save_for_backward(x, w_base, w_lvl, scale)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w_base, w_lvl, scale = ctx.saved_tensors
+        dy = dy.to(x.dtype).contiguous()
+        dx = dwb = dwl = dsc = None
+        if ctx.needs_input_grad[0]:
+            dx = _b.wtconv_bwd_data(dy, w_base, w_lvl, scale)
+        if any(ctx.needs_input_grad[1:]):
+            dwb, dwl, dsc = _b.wtconv_bwd_weight(x, dy, int(w_base.shape[-1]), w_lvl, scale)
+        return dx, dwb, dwl, dsc
+
+
+def wtconv(x, w_base, w_lvl, scale):
+    """Functional form of the layer (differentiable)."""
+    return WTConvFunction.apply(x, w_base, w_lvl, scale)
+
+
+class WTConv2d(torch.nn.Module):
+    """Depthwise WTConv with `channels` channels and `levels` Haar levels.
+
+    Parameters (fp32): ``w_base`` [C, k_base, k_base], ``w_lvl``
+    [L, C, 4, k_level, k_level], ``scale`` [L, C, 4]. Initialisation: both
+    kernels like a depthwise ``nn.Conv2d`` (uniform, bound 1/sqrt(k*k)), and
+    unit scales. The pages fix no initialisation; this is the plainest one.
+    Input and output: [B, C, H, W], fp32 or bf16, with H and W divisible by
+    2^levels ('same' zero padding, stride 1).
+    """
+
+    def __init__(self, channels: int, levels: int, k_base: int = 5, k_level: int = 5,
+                 device=None):
+        super().__init__()
+        if channels < 1 or levels < 0 or k_base % 2 == 0 or k_level % 2 == 0:
+            raise ValueError("channels >= 1, levels >= 0 and odd kernel sizes are required")
+        self.channels, self.levels, self.k_base, self.k_level = channels, levels, k_base, k_level
+        f32 = dict(dtype=torch.float32, device=device)
+        self.w_base = torch.nn.Parameter(torch.empty(channels, k_base, k_base, **f32))
+        self.w_lvl = torch.nn.Parameter(torch.empty(levels, channels, 4, k_level, k_level, **f32))
+        self.scale = torch.nn.Parameter(torch.ones(levels, channels, 4, **f32))
+        self.reset_parameters()
+
+    def reset_parameters(self) -> None:
+        with torch.no_grad():
+            self.w_base.uniform_(-1.0 / math.sqrt(self.k_base ** 2), 1.0 / math.sqrt(self.k_base ** 2))
+            self.w_lvl.uniform_(-1.0 / math.sqrt(self.k_level ** 2), 1.0 / math.sqrt(self.k_level ** 2))
+            self.scale.fill_(1.0)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dim() != 4 or x.shape[1] != self.channels:
+            raise ValueError(f"expected [B, {self.channels}, H, W], got {tuple(x.shape)}")
+        return WTConvFunction.apply(x, self.w_base, self.w_lvl, self.scale)
+
+    def extra_repr(self) -> str:
+        return (f"channels={self.channels}, levels={self.levels}, k_base={self.k_base}, "
+                f"k_level={self.k_level}")
