@@ -66,8 +66,7 @@ typedef enum {
     WTCONV_OK = 0,
     WTCONV_ERR_INVALID_ARG = 1,        /* null pointer, overlap, bad dtype, sizes < 1 */
     WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* H or W not divisible by 2^L, even or
-                                          unsupported k, L out of range, or no
-                                          kernel for this plane size */
+                                          unsupported k, or L out of range */
     WTCONV_ERR_WORKSPACE = 3,          /* ws too small or misaligned */
     WTCONV_ERR_LAUNCH = 4              /* the HIP runtime rejected a launch */
 } wtconv_status_t;
@@ -93,7 +92,13 @@ size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
 
 /* Forward: y = WTConv(x). One fused pass: reads x once, writes y once.
    Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
-   that fit one workgroup's LDS; ws may then be NULL). */
+   that fit one workgroup's LDS; ws may then be NULL).
+   Plane sizes without a fused kernel (any other H, W divisible by 2^L, any
+   L in 0..5, k in {3,5,7}; e.g. L = 0, the plain depthwise convolution) run
+   the generic one-kernel-per-step chain of the naive entry points below:
+   the same results and semantics, with the intermediates in the workspace,
+   which wtconv_workspace_size then reports. The same holds for
+   wtconv_bwd_data and wtconv_bwd_weight. */
 wtconv_status_t wtconv_fwd(const wtconv_desc_t *desc, const void *x,
                            const float *w_base, const float *w_lvl,
                            const float *scale, void *y, void *ws,

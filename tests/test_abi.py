@@ -71,9 +71,18 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ok, None, 0, None) == 1
 
 
-def test_unplanned_plane_is_unsupported(lib):
+def test_unplanned_plane_takes_the_generic_chain(lib):
+    """A plane size without a fused kernel runs the generic chain, which
+    needs a workspace: its size is reported, and a call without one is
+    refused before anything launches. A plane not divisible by 2^L stays
+    unsupported."""
     d = _desc(H=40, W=48, levels=3)
     ok = ctypes.c_void_p(1 << 20)
+    for op in (0, 1, 2):
+        assert 0 < lib.wtconv_workspace_size(ctypes.byref(d), op) < (1 << 40)
+    assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ctypes.c_void_p(1 << 30), None, 0, None) == 3
+    d = _desc(H=40, W=44, levels=3)
+    assert lib.wtconv_workspace_size(ctypes.byref(d), 0) == ctypes.c_size_t(-1).value
     assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ctypes.c_void_p(1 << 30), None, 0, None) == 2
 
 

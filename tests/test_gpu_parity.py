@@ -180,15 +180,30 @@ def test_identity_levels_closed_form_on_gpu(shape):
 
 
 def test_level_zero_and_unplanned_shapes():
-    """L = 0 is the plain depthwise convolution: the naive chain computes it;
-    the fused entry points have no plan for it and say so."""
-    _say("[parity] L = 0")
+    """L = 0 is the plain depthwise convolution. Plane sizes without a fused
+    kernel (here 20 x 12) run the generic chain through the same entry
+    points; a plane not divisible by 2^L is refused."""
+    _say("[parity] L = 0 and unplanned shapes")
     inp = make_inputs(2, 3, 20, 12, 0, 5, 5, dtype="f32", seed=7)
     x, dy, wb, wl, sc = to_device(inp)
-    y = wt.wtconv_naive_fwd(x, wb, wl, sc)
-    torch.cuda.synchronize()
     ref = torch.nn.functional.conv2d(x.double().cpu(), wb.double().cpu()[:, None], padding=2, groups=3)
-    assert rel_err(to_f64(y), ref.numpy()) <= 1e-6
+    for fn in (wt.wtconv_naive_fwd, wt.wtconv_fwd):
+        y = fn(x, wb, wl, sc)
+        torch.cuda.synchronize()
+        assert rel_err(to_f64(y), ref.numpy()) <= 1e-6
+    for dtype in ("f32", "bf16"):
+        inp = make_inputs(2, 3, 24, 20, 2, 3, 5, dtype=dtype, seed=7)
+        x, dy, wb, wl, sc = to_device(inp)
+        y = wt.wtconv_fwd(x, wb, wl, sc)
+        dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+        dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, 3, wl, sc)
+        torch.cuda.synchronize()
+        oy, odx, (odwb, odwl, odsc) = _oracle_all(inp)
+        assert rel_err(to_f64(y), oy) <= TOL[dtype] and rel_err(to_f64(dx), odx) <= TOL[dtype]
+        for g, o in ((dwb, odwb), (dwl, odwl), (dsc, odsc)):
+            assert rel_err(to_f64(g), o) <= TOL["f32"]
+    inp = make_inputs(1, 2, 20, 12, 3, 5, 5, dtype="f32", seed=7)
+    x, dy, wb, wl, sc = to_device(inp)
     with pytest.raises(wt.WTConvError) as ei:
         wt.wtconv_fwd(x, wb, wl, sc)
     assert ei.value.status == 2

@@ -73,9 +73,23 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
         if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
         err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, (float*)ws, d->B, d->C, (hipStream_t)stream);
     } else {
-        return WTCONV_ERR_UNSUPPORTED_SHAPE;
+        // no fused kernel for this plane size: the generic one-kernel-per-step
+        // chain (same results, intermediates in device memory)
+        const int op = flip ? WTCONV_OP_BWD_DATA : WTCONV_OP_FWD;
+        const size_t need = wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
+                                                       d->k_level, op);
+        if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+        err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                     d->dtype == WTCONV_BF16, flip, in, w_base, w_lvl, scale, out, ws,
+                                     (hipStream_t)stream);
     }
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+// Whether the fused weight-gradient kernels have a plan for this shape.
+bool fused_bwdw_planned(const wtconv_desc_t* d) {
+    return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level) !=
+           (size_t)-1;
 }
 
 }  // namespace
@@ -90,9 +104,11 @@ size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
         if (wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) return 0;
         if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))
             return e->ws_bytes(d->B, d->C);
-        return (size_t)-1;
+        return wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, op);
     case WTCONV_OP_BWD_WEIGHT:
-        return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
+        if (fused_bwdw_planned(d))
+            return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
+        return wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, op);
     default:
         return (size_t)-1;
     }
@@ -122,13 +138,20 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const v
     if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
     st = check_params(d, nullptr, w_lvl, scale, false);
     if (st != WTCONV_OK) return st;
-    const size_t need = wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
-                                                  d->k_level);
-    if (need == (size_t)-1) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    const bool fused = fused_bwdw_planned(d);
+    const size_t need =
+        fused ? wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level)
+              : wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                           WTCONV_OP_BWD_WEIGHT);
     if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
-    hipError_t err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
-                                      d->dtype == WTCONV_BF16, x, dy, w_lvl, scale, dw_base,
-                                      dw_lvl, dscale, ws, (hipStream_t)stream);
+    hipError_t err;
+    if (fused)
+        err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, d->dtype == WTCONV_BF16, x,
+                               dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
+    else   // no fused plan for this shape: the generic chain
+        err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                     d->dtype == WTCONV_BF16, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws,
+                                     (hipStream_t)stream);
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
