@@ -274,9 +274,51 @@ struct BwPlan {
     // bf16 (only the base taps read it): half the region
     template <typename T>
     static constexpr int dsize() { return sizeof(T) == 2 ? DSIZE / 2 : DSIZE; }
-    // one plane's regions (x, dy, U, V); NPB of them side by side
+    static constexpr int band_rows(int l) {
+        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K, NPB) : pick_rows(H >> l, W >> l, 64, K, NPB);
+    }
+    // Bank conflicts of the level taps of a step at plane pitch ps: the
+    // lanes of a pass may hold strips of several planes (narrow bands, NPB
+    // planes per step). Cost: over the passes of U and V reads, the largest
+    // number of lanes on one bank, summed.
+    static constexpr int pitch_conflicts(int ps) {
+        int cost = 0;
+        for (int l = 1; l <= L; ++l) {
+            const int hl = H >> l, wl = W >> l, R = band_rows(l), LP = strip_lanes(wl), NI = (hl / R) * LP;
+            if (level_pair(l)) continue;
+            for (int pass = 0; pass < 2; ++pass) {
+                const int stride = pass == 0 ? su(l) : sv(l);
+                for (int h0 = 0; h0 < NPB * NI; h0 += 32) {
+                    int cnt[32] = {};
+                    int worst = 0;
+                    for (int t = h0; t < h0 + 32 && t < NPB * NI; ++t) {
+                        const int pl = t / NI, r = t - pl * NI, rs = r / LP, j = r - rs * LP;
+                        if (j >= wl) continue;
+                        const int b = (pl * ps + rs * R * stride + j) % 32;
+                        if (++cnt[b] > worst) worst = cnt[b];
+                    }
+                    cost += worst;
+                }
+            }
+        }
+        return cost;
+    }
+    // one plane's regions (x, dy, U, V); NPB of them side by side, at the
+    // pitch within 32 floats above the minimum with the fewest conflicts (a
+    // multiple of 4 where x and dy take 128-bit stores)
+    static constexpr int best_pitch(int base) {
+        if (NPB == 1) return base;
+        const int step = COARSE ? 1 : 4;
+        int best = base, best_cost = pitch_conflicts(base);
+        for (int ps = base + step; ps < base + 32; ps += step)
+            if (pitch_conflicts(ps) < best_cost) {
+                best_cost = pitch_conflicts(ps);
+                best = ps;
+            }
+        return best;
+    }
     template <typename T>
-    static constexpr int pstride() { return round_up(XSIZE + dsize<T>() + UTOT + VTOT, 4); }
+    static constexpr int pstride() { return best_pitch(round_up(XSIZE + dsize<T>() + UTOT + VTOT, 4)); }
     template <typename T>
     static constexpr int lds_floats() { return NPB * pstride<T>() > RED ? NPB * pstride<T>() : RED; }
     static constexpr int LDS_FLOATS = lds_floats<float>();
@@ -286,9 +328,6 @@ struct BwPlan {
     static constexpr int LPB = BASE_PAIR ? pair_lanes(W, KB) : strip_lanes(W);
     static constexpr int NI = (H / RB) * LPB;
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
-    static constexpr int band_rows(int l) {
-        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K, NPB) : pick_rows(H >> l, W >> l, 64, K, NPB);
-    }
     // Analysis lanes: each owns 2 rows x CW columns of x and dy. The lanes
     // of one 2^L x 2^L block form a group of GS = BR x BC (BR row pairs,
     // BC column slices, row pair fastest) inside one wavefront.
