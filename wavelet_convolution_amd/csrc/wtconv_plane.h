@@ -502,6 +502,33 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         float y[RB];
 #pragma unroll
         for (int o = 0; o < RB; ++o) y[o] = yb[it][o];
+        if constexpr (RB % (1 << L) == 0) {
+            // whole 2^L-row blocks. From the coarsest level down, carry[p] is
+            // what the coarser levels add to every row of level-l block p
+            // (constant over it: row bit l is); level l splits it into its
+            // two half-blocks as carry + a +- b.
+            float carry[RB];
+            P::for_levels([&](auto lc) {
+                constexpr int l = L + 1 - decltype(lc)::value;   // L, L-1, ..., 1
+                constexpr int Sl = P::su(l), BSl = P::bandsz(l);
+                const float* Zl = ubase(std::integral_constant<int, l>{}) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
+                const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
+                float next[RB >> (l - 1)];
+#pragma unroll
+                for (int p = 0; p < (RB >> l); ++p) {
+                    const float* z = Zl + p * Sl;
+                    float a = __builtin_fmaf(sw, z[2 * BSl], z[0]);
+                    const float b = __builtin_fmaf(sw, z[3 * BSl], z[BSl]);
+                    if constexpr (l < L) a += carry[p];
+                    next[2 * p] = a + b;
+                    next[2 * p + 1] = a - b;
+                }
+#pragma unroll
+                for (int q = 0; q < (RB >> (l - 1)); ++q) carry[q] = next[q];
+            });
+#pragma unroll
+            for (int o = 0; o < RB; ++o) y[o] += carry[o];
+        } else {
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
@@ -529,10 +556,22 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
                 for (int o = 0; o < RB; ++o) y[o] += v;
             }
         });
+        }
+        if constexpr (sizeof(T) == 2 && RB % 2 == 0) {
+            // two rows per conversion: the low half to row o, the high half
+            // to row o + 1
 #pragma unroll
-        for (int o = 0; o < RB; ++o) {
-            if constexpr (sizeof(T) == 2) dst[(size_t)(h0 + o) * W + w] = narrow_bf16(y[o]);
-            else dst[(size_t)(h0 + o) * W + w] = y[o];
+            for (int o = 0; o < RB; o += 2) {
+                const uint32_t pr = narrow_bf16x2(y[o], y[o + 1]);
+                dst[(size_t)(h0 + o) * W + w] = (bf16_t)(pr & 0xffffu);
+                dst[(size_t)(h0 + o + 1) * W + w] = (bf16_t)(pr >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int o = 0; o < RB; ++o) {
+                if constexpr (sizeof(T) == 2) dst[(size_t)(h0 + o) * W + w] = narrow_bf16(y[o]);
+                else dst[(size_t)(h0 + o) * W + w] = y[o];
+            }
         }
     }
 }

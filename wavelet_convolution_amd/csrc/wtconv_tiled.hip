@@ -522,36 +522,44 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
         if (!(NIB % NT == 0 || item < NIB)) continue;
         const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
         if (!(LPB == W || w < W)) continue;
-        float y[RB];
+        // From the coarse image down to level 1, carry[p] is what the
+        // coarser levels add to every row of level-l block p; level l splits
+        // it into its two half-blocks as carry + a +- b.
+        float carry[RB];
 #pragma unroll
-        for (int o = 0; o < RB; ++o) y[o] = yb[it][o];
-        if (cpl) {
-#pragma unroll
-            for (int p = 0; p < (RB >> L0); ++p) {
-                const float e = cpl[(size_t)(((r0 + h0) >> L0) + p) * CW + (w >> L0)];
-#pragma unroll
-                for (int o = p << L0; o < (p + 1) << L0; ++o) y[o] += e;
-            }
-        }
+        for (int p = 0; p < (RB >> L0); ++p)
+            carry[p] = cpl ? cpl[(size_t)(((r0 + h0) >> L0) + p) * CW + (w >> L0)] : 0.f;
         P::for_levels([&](auto lc) {
-            constexpr int l = decltype(lc)::value;
+            constexpr int l = L0 + 1 - decltype(lc)::value;   // L0, ..., 1
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
-            const float* Zl = ubase(lc) + ((G >> l) + (h0 >> l)) * Sl + PK + (w >> l);
+            const float* Zl = ubase(std::integral_constant<int, l>{}) + ((G >> l) + (h0 >> l)) * Sl + PK + (w >> l);
             const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
+            float next[RB >> (l - 1)];
 #pragma unroll
             for (int p = 0; p < (RB >> l); ++p) {
                 const float* z = Zl + p * Sl;
-                const float a = __builtin_fmaf(sw, z[2 * BSl], z[0]);
+                const float a = __builtin_fmaf(sw, z[2 * BSl], z[0]) + carry[p];
                 const float b = __builtin_fmaf(sw, z[3 * BSl], z[BSl]);
-                const float plus = a + b, minus = a - b;
-#pragma unroll
-                for (int o = p << l; o < (p + 1) << l; ++o) y[o] += ((o >> (l - 1)) & 1) ? minus : plus;
+                next[2 * p] = a + b;
+                next[2 * p + 1] = a - b;
             }
-        });
 #pragma unroll
-        for (int o = 0; o < RB; ++o) {
-            if constexpr (sizeof(T) == 2) dst[(size_t)(r0 + h0 + o) * W + w] = narrow_bf16(y[o]);
-            else dst[(size_t)(r0 + h0 + o) * W + w] = y[o];
+            for (int q = 0; q < (RB >> (l - 1)); ++q) carry[q] = next[q];
+        });
+        float y[RB];
+#pragma unroll
+        for (int o = 0; o < RB; ++o) y[o] = yb[it][o] + carry[o];
+        if constexpr (sizeof(T) == 2) {
+            // two rows per conversion: the low half to row o, the high half to o + 1
+#pragma unroll
+            for (int o = 0; o < RB; o += 2) {
+                const uint32_t pr = narrow_bf16x2(y[o], y[o + 1]);
+                dst[(size_t)(r0 + h0 + o) * W + w] = (bf16_t)(pr & 0xffffu);
+                dst[(size_t)(r0 + h0 + o + 1) * W + w] = (bf16_t)(pr >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int o = 0; o < RB; ++o) dst[(size_t)(r0 + h0 + o) * W + w] = y[o];
         }
     }
 }
