@@ -1246,6 +1246,14 @@ typedef BwPlan<32, 32, 1, 1, 5, 1, 4> CB_32_L1_k5b;
 // whole planes split by level (fine: base + level 1; coarse: the rest)
 typedef BwPlan<56, 56, 1, 5, 5, 3> WP_56_L1of3_k55;
 typedef BwPlan<28, 28, 2, 1, 5, 2, 4> CB_28_L2_k5;
+#ifndef WTC_BW28_NPB
+#define WTC_BW28_NPB 2
+#endif
+#ifndef WTC_BW14C_NPB
+#define WTC_BW14C_NPB 8
+#endif
+typedef BwPlan<28, 28, 1, 5, 5, 2, WTC_BW28_NPB> WP_28_L1of2_k55;
+typedef BwPlan<14, 14, 1, 1, 5, 1, WTC_BW14C_NPB> CB_14_L1_k5;
 
 #define WTC_BW_WHOLE(PLAN) \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K, {whole_launch<PLAN, float>, whole_launch<PLAN, bf16_t>}, whole_ws<PLAN>}
@@ -1259,9 +1267,15 @@ typedef BwPlan<28, 28, 2, 1, 5, 2, 4> CB_28_L2_k5;
 #ifndef WTC_BW56_SPLIT
 #define WTC_BW56_SPLIT 1
 #endif
+#ifndef WTC_BW28_SPLIT
+#define WTC_BW28_SPLIT 1
+#endif
 static const BwEntry kBwEntries[] = {
 #if WTC_BW56_SPLIT
     WTC_BW_PLANESPLIT(WP_56_L1of3_k55, CB_28_L2_k5),
+#endif
+#if WTC_BW28_SPLIT
+    WTC_BW_PLANESPLIT(WP_28_L1of2_k55, CB_14_L1_k5),
 #endif
     WTC_BW_WHOLE(BP_32_L2_k55), WTC_BW_WHOLE(BP_56_L3_k55),    WTC_BW_WHOLE(BP_28_L2_k55),
     WTC_BW_WHOLE(BP_14_L1_k55), WTC_BW_WHOLE(BP_32_L3_k75),    WTC_BW_WHOLE(BP_24x40_L3_k33),
