@@ -1245,7 +1245,10 @@ typedef BwPlan<32, 32, 1, 1, 5, 1, 4> CB_32_L1_k5b;
 
 // whole planes split by level (fine: base + level 1; coarse: the rest)
 typedef BwPlan<56, 56, 1, 5, 5, 3> WP_56_L1of3_k55;
-typedef BwPlan<28, 28, 2, 1, 5, 2, 4> CB_28_L2_k5;
+#ifndef WTC_CB28_NPB
+#define WTC_CB28_NPB 4
+#endif
+typedef BwPlan<28, 28, 2, 1, 5, 2, WTC_CB28_NPB> CB_28_L2_k5;
 #ifndef WTC_BW28_NPB
 #define WTC_BW28_NPB 2
 #endif

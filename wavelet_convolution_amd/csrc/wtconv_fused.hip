@@ -16,9 +16,10 @@ static hipError_t launch_plane(const void* in, const float* wb, const float* wl,
 template <class P, typename T, bool FLIP>
 static hipError_t launch_col(const void* in, const float* wb, const float* wl, const float* sc, void* out,
                              int B, int C, hipStream_t stream) {
-    const unsigned planes = (unsigned)B * (unsigned)C;
-    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(planes), dim3(P::NT), 0, stream, (const T*)in, wb, wl, sc,
-                       (T*)out, C);
+    // one workgroup per channel and group of NPW images
+    const unsigned groups = (unsigned)cdiv(B, P::NPW) * (unsigned)C;
+    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(groups), dim3(P::NT), 0, stream, (const T*)in, wb, wl, sc,
+                       (T*)out, B, C);
     return hipGetLastError();
 }
 
@@ -26,7 +27,7 @@ static hipError_t launch_col(const void* in, const float* wb, const float* wl, c
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \
      {{launch_col<PLAN, float, false>, launch_col<PLAN, float, true>},                       \
       {launch_col<PLAN, bf16_t, false>, launch_col<PLAN, bf16_t, true>}},                    \
-     (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT}
+     PLAN::TOTAL_FLOATS * 4, PLAN::NT}
 
 #define WTC_PLANE_ENTRY(PLAN)                                                                 \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \

@@ -274,30 +274,36 @@ namespace wtc {
 template <class P, typename T, bool FLIP>
 __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
 void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, const float* __restrict__ w_lvl,
-                const float* __restrict__ scale, T* __restrict__ out, int C) {
+                const float* __restrict__ scale, T* __restrict__ out, int B, int C) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT, RB = P::RB;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
     constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
     constexpr int NIB = P::NIB, MB = P::MB, LPB = P::LPB, XO = P::XO, VL = P::VL;
-    constexpr int KB2P = P::KB2P, K2P = P::K2P;
+    constexpr int KB2P = P::KB2P, K2P = P::K2P, NPW = P::NPW, PL = P::PL;
 
-    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
-    float* A = lds;
-    float* Bq = lds + P::ASIZE;
-    float* WB = lds + P::LDS_FLOATS;
+    __shared__ __attribute__((aligned(16))) float lds[P::TOTAL_FLOATS];
+    float* WB = lds + NPW * PL;
     float* WL = WB + KB2P;
 
     const int tid = threadIdx.x;
-    const int plane = blockIdx.x;
-    const int c = plane % C;
-    const T* __restrict__ src = in + (size_t)plane * H * W;
-    T* __restrict__ dst = out + (size_t)plane * H * W;
-    // U_l (and then Z'_l) of level l: level 1 in region B, the others in A
-    auto ubase = [&](auto lc) -> float* {
+    // this workgroup: channel c of images g*NPW .. g*NPW + NPW-1 (those < B)
+    const int c = blockIdx.x % C, g = blockIdx.x / C;
+    auto live = [&](int p) { return NPW == 1 || g * NPW + p < B; };
+    auto plane_off = [&](int p) { return ((size_t)(g * NPW + p) * C + c) * H * W; };
+    // plane p of an item index over all NPW planes, and the index within it
+    auto split = [&](int item, int n, int& r) {
+        const int p = NPW == 1 ? 0 : item / n;
+        r = item - p * n;
+        return p;
+    };
+    // plane p's regions: x (A), level-1 bands (B); U_l (and then Z'_l) of
+    // level l >= 2 in region A
+    auto Ap = [&](int p) { return lds + p * PL; };
+    auto ubase = [&](auto lc, int p) -> float* {
         constexpr int l = decltype(lc)::value;
         constexpr int off = P::uoff(l);   // evaluated at compile time
-        if constexpr (l == 1) return Bq;
-        else return A + off;
+        if constexpr (l == 1) return lds + p * PL + P::ASIZE;
+        else return lds + p * PL + off;
     };
 
     // ---------------------------------------------------------------- P0
@@ -316,16 +322,19 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         // loads them, stores them widened and stores their four bands; on
         // the border it stores zeros to both (the padding of the base
         // convolution and of the level-1 convolutions).
-        constexpr int NQ = P::NQ, IPR = P::IPR, CPI = P::CPI, VA = P::VA, MQ = cdiv(NQ, NT);
+        constexpr int NQ = P::NQ, IPR = P::IPR, CPI = P::CPI, VA = P::VA, NQA = NPW * NQ, MQ = cdiv(NQA, NT);
         RawVec<T, VA> r0[MQ], r1[MQ];
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
-            const int q = tid + k * NT;
+            const int qa = tid + k * NT;
+            int q;
+            const int p = split(qa < NQA ? qa : 0, NQ, q);
             const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
-            const bool inside = (NQ % NT == 0 || q < NQ) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1;
+            const bool inside =
+                (NQA % NT == 0 || qa < NQA) && live(p) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1;
             // every lane loads (border items the plane's first words) and
             // then selects zeros: no branch, so the registers stay registers
-            const T* s0 = src + (inside ? (2 * i) * W + 2 * j0 : 0);
+            const T* s0 = in + plane_off(inside ? p : 0) + (inside ? (2 * i) * W + 2 * j0 : 0);
             load_raw<T, VA>(s0, r0[k]);
             load_raw<T, VA>(s0 + (inside ? W : 0), r1[k]);
 #pragma unroll
@@ -336,8 +345,12 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         }
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
-            const int q = tid + k * NT;
-            if (!(NQ % NT == 0 || q < NQ)) continue;
+            const int qa = tid + k * NT;
+            if (!(NQA % NT == 0 || qa < NQA)) continue;
+            int q;
+            const int p = split(qa, NQ, q);
+            float* const A = Ap(p);
+            float* const Bq = A + P::ASIZE;
             const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
             float f0[VA], f1[VA];
             widen_raw<T, VA>(r0[k], f0);
@@ -357,15 +370,17 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         }
     }
     __syncthreads();
-    const float* X0 = A + XO - PB;   // origin of the bordered x plane
 
     // ---------------------------------------------------------------- P1
     float yb[MB][RB];
 #pragma unroll
     for (int it = 0; it < MB; ++it) {
         const int item = tid + it * NT;
-        if (NIB % NT == 0 || item < NIB) {
-            const int rb = item / LPB, w = item - rb * LPB;
+        if ((NPW * NIB) % NT == 0 || item < NPW * NIB) {
+            int r;
+            const int p = split(item, NIB, r);
+            const int rb = r / LPB, w = r - rb * LPB;
+            const float* X0 = Ap(p) + XO - PB;   // origin of the bordered x plane
             if (LPB == W || w < W) conv_col<KB, RB, SX>(X0 + (rb * RB) * SX + w, WB, yb[it]);
         }
     }
@@ -377,11 +392,13 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
         constexpr int Sp = P::su(l - 1);
         constexpr int UO = P::uoff(l), UP = P::uoff(l - 1);
-        float* Ul = A + UO;
-        const float* LLp = (l == 2) ? (Bq + PK * Sp + PK) : (A + UP + PK * Sp + PK);
         // over the bordered grid: zeros on the border
         constexpr int GW = wl + 2 * PK, GN = (hl + 2 * PK) * GW;
-        for (int q = tid; q < GN; q += NT) {
+        for (int qa = tid; qa < NPW * GN; qa += NT) {
+            int q;
+            const int p = split(qa, GN, q);
+            float* const Ul = Ap(p) + UO;
+            const float* LLp = (l == 2) ? (Ap(p) + P::ASIZE + PK * Sp + PK) : (Ap(p) + UP + PK * Sp + PK);
             const int ii = q / GW, jj = q - ii * GW, i = ii - PK, j = jj - PK;
             float b[4] = {0.f, 0.f, 0.f, 0.f};
             if (i >= 0 && i < hl && j >= 0 && j < wl) {
@@ -400,12 +417,13 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     auto level_conv = [&](auto lc, auto& z) {
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
-        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NIl, NT);
-        float* Ul = ubase(lc);
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NPW * NIl, NT);
 #pragma unroll
         for (int it = 0; it < MIl; ++it) {
-            const int item = tid + it * NT;
-            if (NIl % NT == 0 || item < NIl) {
+            const int ia = tid + it * NT;
+            if ((NPW * NIl) % NT == 0 || ia < NPW * NIl) {
+                int item;
+                float* const Ul = ubase(lc, split(ia, NIl, item));
                 const int s = item / (NS * LP), rem = item - s * (NS * LP);
                 const int rs = rem / LP, j = rem - rs * LP;
                 if (LP == wl || j < wl)
@@ -416,12 +434,13 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     auto level_store = [&](auto lc, auto& z) {
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
-        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NIl, NT);
-        float* Ul = ubase(lc);
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NPW * NIl, NT);
 #pragma unroll
         for (int it = 0; it < MIl; ++it) {
-            const int item = tid + it * NT;
-            if (NIl % NT == 0 || item < NIl) {
+            const int ia = tid + it * NT;
+            if ((NPW * NIl) % NT == 0 || ia < NPW * NIl) {
+                int item;
+                float* const Ul = ubase(lc, split(ia, NIl, item));
                 const int s = item / (NS * LP), rem = item - s * (NS * LP);
                 const int rs = rem / LP, j = rem - rs * LP;
                 if (!(LP == wl || j < wl)) continue;
@@ -435,9 +454,10 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
         constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), O = P::doff(l);
-        float* Ul = ubase(lc);
-        const int item = tid - O;
-        if (item >= 0 && item < NIl) {
+        const int ia = tid - O;
+        if (ia >= 0 && ia < NPW * NIl) {
+            int item;
+            float* const Ul = ubase(lc, split(ia, NIl, item));
             const int s = item / (NS * LP), rem = item - s * (NS * LP);
             const int rs = rem / LP, j = rem - rs * LP;
             if (LP == wl || j < wl) {
@@ -452,9 +472,10 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         constexpr int l = decltype(lc)::value;
         constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
         constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), O = P::doff(l);
-        float* Ul = ubase(lc);
-        const int item = tid - O;
-        if (item >= 0 && item < NIl) {
+        const int ia = tid - O;
+        if (ia >= 0 && ia < NPW * NIl) {
+            int item;
+            float* const Ul = ubase(lc, split(ia, NIl, item));
             const int s = item / (NS * LP), rem = item - s * (NS * LP);
             const int rs = rem / LP, j = rem - rs * LP;
             if (LP == wl || j < wl) {
@@ -464,7 +485,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         }
     };
     // results of all levels stay in registers across one barrier
-    float z1[cdiv(P::nil(1), NT)][P::rl(1)];
+    float z1[cdiv(NPW * P::nil(1), NT)][P::rl(1)];
     level_conv(std::integral_constant<int, 1>{}, z1);
     if constexpr (P::DSHARE) {
         float zd[P::RLD];
@@ -473,10 +494,10 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         level_store(std::integral_constant<int, 1>{}, z1);
         P::for_deep_levels([&](auto lc) { deep_store(lc, zd); });
     } else {
-        float z2[L >= 2 ? cdiv(P::nil(L >= 2 ? 2 : 1), NT) : 1][P::rl(L >= 2 ? 2 : 1)];
-        float z3[L >= 3 ? cdiv(P::nil(L >= 3 ? 3 : 1), NT) : 1][P::rl(L >= 3 ? 3 : 1)];
-        float z4[L >= 4 ? cdiv(P::nil(L >= 4 ? 4 : 1), NT) : 1][P::rl(L >= 4 ? 4 : 1)];
-        float z5[L >= 5 ? cdiv(P::nil(L >= 5 ? 5 : 1), NT) : 1][P::rl(L >= 5 ? 5 : 1)];
+        float z2[L >= 2 ? cdiv(NPW * P::nil(L >= 2 ? 2 : 1), NT) : 1][P::rl(L >= 2 ? 2 : 1)];
+        float z3[L >= 3 ? cdiv(NPW * P::nil(L >= 3 ? 3 : 1), NT) : 1][P::rl(L >= 3 ? 3 : 1)];
+        float z4[L >= 4 ? cdiv(NPW * P::nil(L >= 4 ? 4 : 1), NT) : 1][P::rl(L >= 4 ? 4 : 1)];
+        float z5[L >= 5 ? cdiv(NPW * P::nil(L >= 5 ? 5 : 1), NT) : 1][P::rl(L >= 5 ? 5 : 1)];
         if constexpr (L >= 2) level_conv(std::integral_constant<int, 2>{}, z2);
         if constexpr (L >= 3) level_conv(std::integral_constant<int, 3>{}, z3);
         if constexpr (L >= 4) level_conv(std::integral_constant<int, 4>{}, z4);
@@ -496,9 +517,12 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
 #pragma unroll
     for (int it = 0; it < MB; ++it) {
         const int item = tid + it * NT;
-        if (!(NIB % NT == 0 || item < NIB)) continue;
-        const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
-        if (!(LPB == W || w < W)) continue;
+        if (!((NPW * NIB) % NT == 0 || item < NPW * NIB)) continue;
+        int r;
+        const int p = split(item, NIB, r);
+        const int rb = r / LPB, w = r - rb * LPB, h0 = rb * RB;
+        if (!(LPB == W || w < W) || !live(p)) continue;
+        T* __restrict__ dst = out + plane_off(p);
         float y[RB];
 #pragma unroll
         for (int o = 0; o < RB; ++o) y[o] = yb[it][o];
@@ -511,7 +535,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             P::for_levels([&](auto lc) {
                 constexpr int l = L + 1 - decltype(lc)::value;   // L, L-1, ..., 1
                 constexpr int Sl = P::su(l), BSl = P::bandsz(l);
-                const float* Zl = ubase(std::integral_constant<int, l>{}) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
+                const float* Zl = ubase(std::integral_constant<int, l>{}, p) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
                 const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
                 float next[RB >> (l - 1)];
 #pragma unroll
@@ -532,7 +556,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
-            const float* Zl = ubase(lc) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
+            const float* Zl = ubase(lc, p) + (PK + (h0 >> l)) * Sl + PK + (w >> l);
             const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
             if constexpr (RB % (1 << l) == 0) {
                 // whole 2^l-row blocks: the row bits below l are strip-relative

@@ -211,9 +211,13 @@ constexpr BandLayout band_layout(int hl, int wl, int pk, int r, bool even) {
 // level l, either whole 2^l-row blocks per strip (RB a multiple of 2^l) or a
 // strip inside one block whose row bit l-1 is constant (RB a power of two
 // below 2^l): RB is a multiple of 2^L or a power of two.
-template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_, int WMAX_ = 8>
+template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_, int WMAX_ = 8, int NPW_ = 1>
 struct ColPlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, NT = NT_, RB = RB_, RL = RL_;
+    // planes per workgroup: NPW planes of one channel (consecutive images)
+    // share the staged taps, and every phase packs its strips of all of
+    // them onto the lanes (small planes otherwise leave lanes idle)
+    static constexpr int NPW = NPW_;
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1 && H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
     static_assert(H % RB == 0, "base strips must divide the plane");
@@ -233,7 +237,13 @@ struct ColPlan {
     static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
     // band rows: level-1 cell pairs are stored as aligned 64-bit words
     // (an even stride); see band_layout for the rest
-    static constexpr BandLayout lay(int l) { return band_layout(H >> l, W >> l, PK, rl(l), l == 1 && CPI == 2); }
+    static constexpr BandLayout lay_calc(int l) {
+        return l <= L ? band_layout(H >> l, W >> l, PK, rl(l), l == 1 && CPI == 2) : BandLayout{1, 1, 1};
+    }
+    // computed once per plan (each is a search)
+    static constexpr BandLayout LAYS[6] = {BandLayout{1, 1, 1}, lay_calc(1), lay_calc(2),
+                                           lay_calc(3), lay_calc(4), lay_calc(5)};
+    static constexpr BandLayout lay(int l) { return LAYS[l]; }
     static constexpr int su(int l) { return lay(l).s; }
     static constexpr int bandsz(int l) { return lay(l).pitch; }   // band pitch
     static constexpr int IPR = ((W >> 1) + 2 * PK) / CPI;
@@ -249,13 +259,12 @@ struct ColPlan {
     static constexpr int UDEEP = uoff(L + 1);
     static constexpr int ASIZE = XSIZE > UDEEP ? XSIZE : UDEEP;
     static constexpr int BSIZE = 4 * bandsz(1);
-    static constexpr int LDS_FLOATS = (ASIZE + BSIZE + 3) / 4 * 4;
+    static constexpr int LDS_FLOATS = (ASIZE + BSIZE + 3) / 4 * 4;   // one plane
     static constexpr int KB2P = kpad4(KB), K2P = kpad4(K);
     static constexpr int WFLOATS = KB2P + 4 * L * K2P;
-    static_assert((LDS_FLOATS + WFLOATS) * 4 <= 160 * 1024, "plane does not fit in LDS");
     static constexpr int LPB = strip_lanes(W);
-    static constexpr int NIB = (H / RB) * LPB;   // base strip slots
-    static constexpr int MB = cdiv(NIB, NT);
+    static constexpr int NIB = (H / RB) * LPB;   // base strip slots of one plane
+    static constexpr int MB = cdiv(NPW * NIB, NT);
     // rows per strip at level l, lanes per row block, strip slots (4 bands)
     static constexpr int lpl(int l) { return lay(l).lp; }
     static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * lpl(l); }
@@ -263,14 +272,59 @@ struct ColPlan {
     // slots fit the workgroup: level l takes threads [doff(l), doff(l) + nil(l))
     static constexpr int doff(int l) {
         int o = 0;
-        for (int q = 2; q < l; ++q) o += nil(q);
+        for (int q = 2; q < l; ++q) o += NPW * nil(q);
         return o;
     }
     static constexpr bool DSHARE = L >= 2 && doff(L + 1) <= NT;
     static constexpr int RLD = L >= 2 ? rl(2) : 1;
     // occupancy the LDS footprint allows, at most WMAX waves per SIMD (a
     // plan whose registers need more than 512 / WMAX lowers WMAX)
-    static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
+    // planes of a workgroup lie PL floats apart: a multiple of 4 (128-bit
+    // stores) at most 28 above one plane's size, placed so that the base and
+    // level-1 strips of neighbouring planes sharing a 32-lane pass fall on
+    // different banks
+    static constexpr int pass_conflicts(int pl) {
+        int cost = 0;
+        for (int h0 = 0; h0 < NPW * NIB; h0 += 32) {   // base strips, first window row
+            int cnt[32] = {};
+            int worst = 0;
+            for (int t = h0; t < h0 + 32 && t < NPW * NIB; ++t) {
+                const int p = t / NIB, r = t - p * NIB, rb = r / LPB, w = r - rb * LPB;
+                if (w >= W) continue;
+                const int b = (p * pl + rb * RB * SX + w) % 32;
+                if (++cnt[b] > worst) worst = cnt[b];
+            }
+            cost += worst;
+        }
+        const int n1 = nil(1), ns = (H >> 1) / rl(1), lp = lpl(1);
+        for (int h0 = 0; h0 < NPW * n1; h0 += 32) {   // level-1 strips
+            int cnt[32] = {};
+            int worst = 0;
+            for (int t = h0; t < h0 + 32 && t < NPW * n1; ++t) {
+                const int p = t / n1, r = t - p * n1, s = r / (ns * lp), rem = r - s * (ns * lp);
+                const int rs = rem / lp, j = rem - rs * lp;
+                if (j >= (W >> 1)) continue;
+                const int b = (p * pl + ASIZE + s * bandsz(1) + rs * rl(1) * su(1) + j) % 32;
+                if (++cnt[b] > worst) worst = cnt[b];
+            }
+            cost += worst;
+        }
+        return cost;
+    }
+    static constexpr int plane_pitch() {
+        if (NPW == 1) return LDS_FLOATS;
+        int best = LDS_FLOATS, best_cost = pass_conflicts(LDS_FLOATS);
+        for (int pl = LDS_FLOATS + 4; pl < LDS_FLOATS + 32; pl += 4)
+            if (pass_conflicts(pl) < best_cost) {
+                best_cost = pass_conflicts(pl);
+                best = pl;
+            }
+        return best;
+    }
+    static constexpr int PL = plane_pitch();
+    static constexpr int TOTAL_FLOATS = NPW * PL + WFLOATS;   // planes, then the taps
+    static_assert(TOTAL_FLOATS * 4 <= 160 * 1024, "planes do not fit in LDS");
+    static constexpr int WG_PER_CU = (160 * 1024) / (TOTAL_FLOATS * 4);
     static constexpr int WAVES_PER_EU_LDS = (WG_PER_CU * (NT / 64)) / 4;
     static constexpr int WAVES_PER_EU =
         WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > WMAX_ ? WMAX_ : WAVES_PER_EU_LDS);
@@ -307,8 +361,15 @@ namespace wtc {
 #define WTC_COL56_WMAX 8
 #endif
 typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, WTC_COL56_WMAX> CP_56_L3_k55;
-typedef ColPlan<28, 28, 2, 5, 5, 256, 4, 7> CP_28_L2_k55;
-typedef ColPlan<14, 14, 1, 5, 5, 128, 2, 7> CP_14_L1_k55;
+// small planes: several images of one channel per workgroup
+#ifndef WTC_COL28
+#define WTC_COL28 256, 4, 7, 8, 1
+#endif
+#ifndef WTC_COL14
+#define WTC_COL14 512, 2, 7, 8, 4
+#endif
+typedef ColPlan<28, 28, 2, 5, 5, WTC_COL28> CP_28_L2_k55;
+typedef ColPlan<14, 14, 1, 5, 5, WTC_COL14> CP_14_L1_k55;
 typedef ColPlan<128, 128, 1, 5, 5, 1024, 8, 8> CP_128_L1_k55;
 typedef ColPlan<128, 128, 2, 5, 5, 1024, 8, 8> CP_128_L2_k55;
 typedef ColPlan<128, 128, 3, 5, 5, 1024, 8, 8> CP_128_L3_k55;
