@@ -1,9 +1,8 @@
 """The WTConv workloads this library is measured and parity-tested on.
 
-Shapes follow the evaluation named in the abstract of arXiv:2608.10805
-("the WTConvNeXt configuration across decomposition levels and a broad range
-of tensor shapes"): ConvNeXt stage-like shapes, a level sweep and a large
-plane. All use x, dy ~ N(0,1), kernels ~ N(0, 0.02^2), scales ~ U(0.5, 1.5),
+Shapes follow the evaluation that the abstract of arXiv:2608.10805 describes
+(the WTConvNeXt setting, over several decomposition levels and many tensor
+shapes): ConvNeXt stage-like shapes, a level sweep and a large plane. All use x, dy ~ N(0,1), kernels ~ N(0, 0.02^2), scales ~ U(0.5, 1.5),
 zero 'same' padding, seed 0.
 """
 from __future__ import annotations

@@ -2,8 +2,8 @@
 // every intermediate (each level's subbands, convolution outputs, scaled
 // outputs, the synthesis carry and the base-convolution output) written to
 // and read back from device memory. This is the shape of implementation the
-// abstract of arXiv:2608.10805 calls memory-bound ("excessive data movement
-// through HBM"); it exists as the comparator for the fused kernels and as a
+// abstract of arXiv:2608.10805 describes as memory-bound (it moves too much
+// data through HBM); it exists as the comparator for the fused kernels and as a
 // second, independently written GPU implementation for parity checks. It
 // uses the orthonormal Haar normalisation (1/2 per butterfly) literally.
 #include "wtconv_device.h"

@@ -1,7 +1,7 @@
 """Analytic I/O and arithmetic model of one WTConv training step.
 
-The abstract of arXiv:2608.10805 builds "an I/O model of WTConv" to locate
-its HBM bottleneck; this is this library's own model of the same kind, for
+The abstract of arXiv:2608.10805 models WTConv's I/O to locate its HBM
+bottleneck; this is this library's own model of the same kind, for
 the three-call step (forward, backward data, backward weight).
 
 Minimum HBM bytes: what the method must move if every intermediate stays on
