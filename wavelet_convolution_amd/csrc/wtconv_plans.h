@@ -363,10 +363,10 @@ namespace wtc {
 typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, WTC_COL56_WMAX> CP_56_L3_k55;
 // small planes: several images of one channel per workgroup
 #ifndef WTC_COL28
-#define WTC_COL28 256, 4, 7, 8, 1
+#define WTC_COL28 256, 4, 7, 8, 2
 #endif
 #ifndef WTC_COL14
-#define WTC_COL14 512, 2, 7, 8, 4
+#define WTC_COL14 256, 14, 7, 8, 8
 #endif
 typedef ColPlan<28, 28, 2, 5, 5, WTC_COL28> CP_28_L2_k55;
 typedef ColPlan<14, 14, 1, 5, 5, WTC_COL14> CP_14_L1_k55;
