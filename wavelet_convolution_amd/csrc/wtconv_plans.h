@@ -370,11 +370,14 @@ typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, WTC_COL56_WMAX> CP_56_L3_k5
 #endif
 typedef ColPlan<28, 28, 2, 5, 5, WTC_COL28> CP_28_L2_k55;
 typedef ColPlan<14, 14, 1, 5, 5, WTC_COL14> CP_14_L1_k55;
-typedef ColPlan<128, 128, 1, 5, 5, 1024, 8, 8> CP_128_L1_k55;
-typedef ColPlan<128, 128, 2, 5, 5, 1024, 8, 8> CP_128_L2_k55;
-typedef ColPlan<128, 128, 3, 5, 5, 1024, 8, 8> CP_128_L3_k55;
-typedef ColPlan<128, 128, 4, 5, 5, 1024, 8, 8> CP_128_L4_k55;
-typedef ColPlan<128, 128, 5, 5, 5, 1024, 8, 8> CP_128_L5_k55;
+#ifndef WTC_COL128
+#define WTC_COL128 1024, 16, 16
+#endif
+typedef ColPlan<128, 128, 1, 5, 5, WTC_COL128> CP_128_L1_k55;
+typedef ColPlan<128, 128, 2, 5, 5, WTC_COL128> CP_128_L2_k55;
+typedef ColPlan<128, 128, 3, 5, 5, WTC_COL128> CP_128_L3_k55;
+typedef ColPlan<128, 128, 4, 5, 5, WTC_COL128> CP_128_L4_k55;
+typedef ColPlan<128, 128, 5, 5, 5, WTC_COL128> CP_128_L5_k55;
 #define WTC_COL_ENTRIES(X)                                                                     \
     X(CP_56_L3_k55), X(CP_28_L2_k55), X(CP_14_L1_k55), X(CP_128_L1_k55), X(CP_128_L2_k55),     \
         X(CP_128_L3_k55), X(CP_128_L4_k55), X(CP_128_L5_k55)
