@@ -363,7 +363,7 @@ namespace wtc {
 typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, WTC_COL56_WMAX> CP_56_L3_k55;
 // small planes: several images of one channel per workgroup
 #ifndef WTC_COL28
-#define WTC_COL28 256, 4, 7, 8, 2
+#define WTC_COL28 256, 4, 14, 8, 2
 #endif
 #ifndef WTC_COL14
 #define WTC_COL14 256, 14, 7, 8, 8
