@@ -87,7 +87,7 @@ def _dims(x, w_base, w_lvl, scale):
     assert w_lvl.shape[:3] == (L, C, 4) or L == 0, w_lvl.shape
     assert scale.shape == (L, C, 4), scale.shape
     assert kb % 2 == 1 and k % 2 == 1
-    assert L <= 32 and H % (1 << L) == 0 and W % (1 << L) == 0
+    assert 0 <= L <= 32 and H >= 1 and W >= 1
     return B, C, H, W, L, kb, k
 
 

@@ -33,7 +33,14 @@
  *       corr(u, w)[i][j] = sum_{m,n<k} w[m][n] * u[i+m-k/2][j+n-k/2].
  *   - level l+1 analyses the raw LL_l, not the convolved one;
  *   - the coarser result R_l is added to the processed LL band Z_l^0;
- *   - no bias and no scale on the base path.
+ *   - no bias and no scale on the base path;
+ *   - an image of odd height or width is zero-padded by one row at the
+ *     bottom or one column at the right before its analysis, and the
+ *     synthesis output is cropped back to the image's size: level l has a
+ *     band grid of ceil(h_{l-1} / 2) x ceil(w_{l-1} / 2). (The pages do not
+ *     cover sizes that 2^L does not divide; this is the plainest extension,
+ *     and equals running the layer on x zero-padded to multiples of 2^L and
+ *     cropping the result.)
  *
  * Layouts (all row-major, fp64 here):
  *   x, y, dy, dx    [B][C][H][W]
@@ -147,15 +154,21 @@ static void corr_same_wgrad_acc(const double *u, const double *v, int h, int w,
         }
 }
 
-/* one-level Haar analysis of an h x w image (h, w even) into 4 bands of
-   (h/2) x (w/2), band-major: bands[s][i][j] */
+static int half_up(int v) { return (v + 1) / 2; }
+
+/* one-level Haar analysis of an h x w image into 4 bands of ceil(h/2) x
+   ceil(w/2), band-major: bands[s][i][j]; an odd last row or column is
+   paired with a zero one */
 static void dwt2(const double *X, int h, int w, double *bands)
 {
-    int h2 = h / 2, w2 = w / 2, n2 = h2 * w2;
+    int h2 = half_up(h), w2 = half_up(w), n2 = h2 * w2;
     for (int i = 0; i < h2; i++)
         for (int j = 0; j < w2; j++) {
-            double a = X[(2 * i) * w + 2 * j], b = X[(2 * i) * w + 2 * j + 1];
-            double c = X[(2 * i + 1) * w + 2 * j], d = X[(2 * i + 1) * w + 2 * j + 1];
+            int r0 = 2 * i, r1 = 2 * i + 1, c0 = 2 * j, c1 = 2 * j + 1;
+            double a = X[r0 * w + c0];
+            double b = c1 < w ? X[r0 * w + c1] : 0.0;
+            double c = r1 < h ? X[r1 * w + c0] : 0.0;
+            double d = (r1 < h && c1 < w) ? X[r1 * w + c1] : 0.0;
             bands[0 * n2 + i * w2 + j] = (a + b + c + d) / 2.0;
             bands[1 * n2 + i * w2 + j] = (a + b - c - d) / 2.0;
             bands[2 * n2 + i * w2 + j] = (a - b + c - d) / 2.0;
@@ -163,19 +176,26 @@ static void dwt2(const double *X, int h, int w, double *bands)
         }
 }
 
-/* inverse of dwt2: 4 bands of h2 x w2 -> image of 2h2 x 2w2 */
-static void iwt2(const double *bands, int h2, int w2, double *X)
+/* inverse of dwt2: 4 bands of h2 x w2 -> the image of 2h2 x 2w2, of which
+   the top-left h x w (h <= 2h2, w <= 2w2) is written to X (row stride w) */
+static void iwt2_crop(const double *bands, int h2, int w2, double *X, int h, int w)
 {
-    int n2 = h2 * w2, w = 2 * w2;
+    int n2 = h2 * w2;
     for (int i = 0; i < h2; i++)
         for (int j = 0; j < w2; j++) {
             double b0 = bands[0 * n2 + i * w2 + j], b1 = bands[1 * n2 + i * w2 + j];
             double b2 = bands[2 * n2 + i * w2 + j], b3 = bands[3 * n2 + i * w2 + j];
-            X[(2 * i) * w + 2 * j]         = (b0 + b1 + b2 + b3) / 2.0;
-            X[(2 * i) * w + 2 * j + 1]     = (b0 + b1 - b2 - b3) / 2.0;
-            X[(2 * i + 1) * w + 2 * j]     = (b0 - b1 + b2 - b3) / 2.0;
-            X[(2 * i + 1) * w + 2 * j + 1] = (b0 - b1 - b2 + b3) / 2.0;
+            int r0 = 2 * i, r1 = 2 * i + 1, c0 = 2 * j, c1 = 2 * j + 1;
+            if (r0 < h && c0 < w) X[r0 * w + c0] = (b0 + b1 + b2 + b3) / 2.0;
+            if (r0 < h && c1 < w) X[r0 * w + c1] = (b0 + b1 - b2 - b3) / 2.0;
+            if (r1 < h && c0 < w) X[r1 * w + c0] = (b0 - b1 + b2 - b3) / 2.0;
+            if (r1 < h && c1 < w) X[r1 * w + c1] = (b0 - b1 - b2 + b3) / 2.0;
         }
+}
+
+static void iwt2(const double *bands, int h2, int w2, double *X)
+{
+    iwt2_crop(bands, h2, w2, X, 2 * h2, 2 * w2);
 }
 
 /* offsets of the parameter blocks of channel c */
@@ -189,22 +209,33 @@ static double sc_val(const double *scale, int C, int l1, int c, int s)
     return scale[((size_t)(l1 - 1) * C + c) * 4 + s];
 }
 
-/* Haar pyramid of one plane: pyr[l] holds the 4 bands of level l (1-based),
-   each (H>>l) x (W>>l). pyr[0] is unused. */
+/* Haar pyramid of one plane: lvl[l] holds the 4 bands of level l (1-based),
+   each h[l] x w[l] = ceil(h[l-1] / 2) x ceil(w[l-1] / 2), h[0] x w[0] the
+   plane. lvl[0] is unused. */
 typedef struct {
     int L, H, W;
+    int h[33], w[33];
     double *lvl[33];
 } pyramid;
 
-static void pyramid_build(pyramid *P, const double *plane, int H, int W, int L)
+static void pyramid_sizes(pyramid *P, int H, int W, int L)
 {
     P->L = L; P->H = H; P->W = W;
+    P->h[0] = H; P->w[0] = W;
+    for (int l = 1; l <= L; l++) {
+        P->h[l] = half_up(P->h[l - 1]);
+        P->w[l] = half_up(P->w[l - 1]);
+    }
+}
+
+static void pyramid_build(pyramid *P, const double *plane, int H, int W, int L)
+{
+    pyramid_sizes(P, H, W, L);
     const double *prev = plane;
     for (int l = 1; l <= L; l++) {
-        int h = H >> (l - 1), w = W >> (l - 1);
-        P->lvl[l] = xmalloc(sizeof(double) * (size_t)h * w);  /* 4 * (h/2)(w/2) */
-        dwt2(prev, h, w, P->lvl[l]);
-        prev = P->lvl[l];   /* band 0 (LL) is the first (h/2)(w/2) block */
+        P->lvl[l] = xmalloc(sizeof(double) * 4 * (size_t)P->h[l] * P->w[l]);
+        dwt2(prev, P->h[l - 1], P->w[l - 1], P->lvl[l]);
+        prev = P->lvl[l];   /* band 0 (LL) is the first h[l] x w[l] block */
     }
 }
 
@@ -250,10 +281,11 @@ static void fwd_plane(const double *x, int H, int W, int L, int C, int c,
     pyramid P;
     pyramid_build(&P, x, H, W, L);
 
-    /* R holds the result carried up from the coarser levels */
+    /* R holds the result carried up from the coarser levels, at the size
+       of the level-l band grid (the synthesis output cropped) */
     double *R = NULL;
     for (int l = L; l >= 1; l--) {
-        int h = H >> l, w = W >> l, n = h * w;
+        int h = P.h[l], w = P.w[l], n = h * w;
         double *Z = xmalloc(sizeof(double) * 4 * (size_t)n);
         for (int s = 0; s < 4; s++) {
             corr_same(P.lvl[l] + (size_t)s * n, h, w, wl_ptr(w_lvl, C, k, l, c, s), k,
@@ -265,8 +297,8 @@ static void fwd_plane(const double *x, int H, int W, int L, int C, int c,
             for (int t = 0; t < n; t++) Z[t] += R[t];
             free(R);
         }
-        R = xmalloc(sizeof(double) * 4 * (size_t)n);
-        iwt2(Z, h, w, R);
+        R = xmalloc(sizeof(double) * (size_t)P.h[l - 1] * P.w[l - 1]);
+        iwt2_crop(Z, h, w, R, P.h[l - 1], P.w[l - 1]);
         free(Z);
     }
     for (size_t t = 0; t < (size_t)H * W; t++) y[t] += R[t];
@@ -291,14 +323,16 @@ void wto_fwd(int B, int C, int H, int W, int L, int kb, int k,
 
 /* band s of level l at (i, j) straight from its 2^l x 2^l block of x:
    2^-l * sum_{u,v < 2^l} sign_s(bit_{l-1} u, bit_{l-1} v) x[i 2^l + u][j 2^l + v] */
-static double band_direct(const double *x, int W, int l, int s, int i, int j)
+static double band_direct(const double *x, int H, int W, int l, int s, int i, int j)
 {
     int side = 1 << l;
     double acc = 0.0;
     for (int u = 0; u < side; u++)
-        for (int v = 0; v < side; v++)
-            acc += band_sign(s, (u >> (l - 1)) & 1, (v >> (l - 1)) & 1) *
-                   x[(size_t)(i * side + u) * W + (j * side + v)];
+        for (int v = 0; v < side; v++) {
+            int r = i * side + u, q = j * side + v;
+            if (r >= H || q >= W) continue;   /* x is zero beyond the plane */
+            acc += band_sign(s, (u >> (l - 1)) & 1, (v >> (l - 1)) & 1) * x[(size_t)r * W + q];
+        }
     return acc / (double)side;
 }
 
@@ -307,13 +341,15 @@ static void fwd_closed_plane(const double *x, int H, int W, int L, int C, int c,
                              const double *w_lvl, const double *scale, double *y)
 {
     corr_same(x, H, W, w_base + (size_t)c * kb * kb, kb, y);
+    pyramid S;
+    pyramid_sizes(&S, H, W, L);   /* band grid sizes only */
     for (int l = 1; l <= L; l++) {
-        int h = H >> l, w = W >> l, n = h * w;
+        int h = S.h[l], w = S.w[l], n = h * w;
         double *band = xmalloc(sizeof(double) * (size_t)n);
         double *Z = xmalloc(sizeof(double) * 4 * (size_t)n);
         for (int s = 0; s < 4; s++) {
             for (int i = 0; i < h; i++)
-                for (int j = 0; j < w; j++) band[i * w + j] = band_direct(x, W, l, s, i, j);
+                for (int j = 0; j < w; j++) band[i * w + j] = band_direct(x, H, W, l, s, i, j);
             corr_same(band, h, w, wl_ptr(w_lvl, C, k, l, c, s), k, Z + (size_t)s * n);
             double sc = sc_val(scale, C, l, c, s);
             for (int t = 0; t < n; t++) Z[(size_t)s * n + t] *= sc;
@@ -368,7 +404,7 @@ static void bwd_data_plane(const double *dy, int H, int W, int L, int C, int c,
        dX_l flowing back from level l+1 into the LL band. */
     double *dXl = NULL;   /* gradient w.r.t. X_l (level-l resolution) */
     for (int l = L; l >= 1; l--) {
-        int h = H >> l, w = W >> l, n = h * w;
+        int h = dZ.h[l], w = dZ.w[l], n = h * w;
         double *dband = xmalloc(sizeof(double) * 4 * (size_t)n);
         for (int s = 0; s < 4; s++) {
             double sc = sc_val(scale, C, l, c, s);
@@ -382,8 +418,9 @@ static void bwd_data_plane(const double *dy, int H, int W, int L, int C, int c,
             for (int t = 0; t < n; t++) dband[t] += dXl[t];
             free(dXl);
         }
-        dXl = xmalloc(sizeof(double) * 4 * (size_t)n);   /* level l-1 size */
-        iwt2(dband, h, w, dXl);
+        /* adjoint of "pad, then analyse": synthesise, then crop */
+        dXl = xmalloc(sizeof(double) * (size_t)dZ.h[l - 1] * dZ.w[l - 1]);
+        iwt2_crop(dband, h, w, dXl, dZ.h[l - 1], dZ.w[l - 1]);
         free(dband);
     }
     for (size_t t = 0; t < hw; t++) dx[t] += dXl[t];
@@ -427,7 +464,7 @@ static void bwd_weight_plane(const double *x, const double *dy, int H, int W,
     double *gw = g + (size_t)kb * kb;
     double *gs = gw + (size_t)L * 4 * k * k;
     for (int l = 1; l <= L; l++) {
-        int h = H >> l, w = W >> l, n = h * w;
+        int h = Px.h[l], w = Px.w[l], n = h * w;
         double *T = xmalloc(sizeof(double) * (size_t)n);
         double *tmp = xmalloc(sizeof(double) * (size_t)k * k);
         for (int s = 0; s < 4; s++) {
@@ -465,7 +502,7 @@ static void bwd_weight_plane_gcorr(const double *x, const double *dy, int H, int
     pyramid_build(&Pd, dy, H, W, L);
     double *gw = g + (size_t)kb * kb;
     for (int l = 1; l <= L; l++) {
-        int h = H >> l, w = W >> l, n = h * w;
+        int h = Px.h[l], w = Px.w[l], n = h * w;
         for (int s = 0; s < 4; s++)
             corr_same_wgrad_acc(Px.lvl[l] + (size_t)s * n, Pd.lvl[l] + (size_t)s * n,
                                 h, w, k, gw + ((size_t)(l - 1) * 4 + s) * k * k);

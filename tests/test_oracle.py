@@ -324,7 +324,10 @@ def _torch_layer(x, wb, wl, sc):
     y = torch.nn.functional.conv2d(x, wb[:, None], padding=kb // 2, groups=C)
     lls, zs = [x], []
     for l in range(L):
-        bands = torch.nn.functional.conv2d(lls[-1], filt, stride=2, groups=C)   # [B, 4C, h, w]
+        # an odd last row or column is paired with a zero one (torch's pad)
+        ll = lls[-1]
+        ll = torch.nn.functional.pad(ll, (0, ll.shape[3] % 2, 0, ll.shape[2] % 2))
+        bands = torch.nn.functional.conv2d(ll, filt, stride=2, groups=C)   # [B, 4C, h, w]
         z = torch.nn.functional.conv2d(bands, wl[l].reshape(4 * C, 1, k, k), padding=k // 2, groups=4 * C)
         zs.append(z * sc[l].reshape(1, 4 * C, 1, 1))
         lls.append(bands[:, 0::4])
@@ -335,6 +338,7 @@ def _torch_layer(x, wb, wl, sc):
             z = torch.cat([(z[:, 0::4] + r)[:, :, None], z.reshape(z.shape[0], C, 4, *z.shape[2:])[:, :, 1:]], 2)
             z = z.reshape(z.shape[0], 4 * C, *z.shape[3:])
         r = torch.nn.functional.conv_transpose2d(z, filt, stride=2, groups=C)
+        r = r[:, :, :lls[l].shape[2], :lls[l].shape[3]]   # cropped to the analysed image
     return y + r if r is not None else y
 
 
@@ -383,3 +387,71 @@ def test_bitwise_stable_across_thread_counts():
                 assert np.array_equal(a, b)
     finally:
         oracle.set_threads(n0)
+
+
+# ------------------------------- planes that 2^L does not divide (R9)
+
+ODD = [(2, 3, 13, 11, 2, 5, 3), (1, 2, 7, 9, 3, 3, 5), (1, 2, 5, 6, 2, 5, 5), (2, 1, 9, 1, 1, 3, 3),
+       (1, 1, 3, 5, 4, 3, 3)]
+
+
+def _pad_to(a, m):
+    """Zero-pad the last two axes to multiples of m."""
+    H, W = a.shape[-2:]
+    out = np.zeros(a.shape[:-2] + (-(-H // m) * m, -(-W // m) * m))
+    out[..., :H, :W] = a
+    return out
+
+
+@pytest.mark.parametrize("shape", ODD, ids=lambda s: "x".join(map(str, s)))
+def test_odd_planes_embed_in_the_zero_padded_plane(shape):
+    """Derived from the reading (zero-pad an odd row or column before each
+    analysis, crop after each synthesis): every band grid of x zero-padded to
+    multiples of 2^L is x's grid extended by zeros, so the per-level
+    convolutions agree on x's grid and the layer on x is the layer on the
+    padded plane, cropped. Its transpose and its weight gradients are then
+    those of the padded plane with dy zero-padded. The padded plane is a
+    divisible shape, pinned by every other test."""
+    B, C, H, W, L, kb, k = shape
+    rng = np.random.default_rng(13)
+    x, v, wb, wl, sc = _rand_problem(rng, B, C, H, W, L, kb, k)
+    xp, vp = _pad_to(x, 1 << L), _pad_to(v, 1 << L)
+    np.testing.assert_allclose(oracle.fwd(x, wb, wl, sc), oracle.fwd(xp, wb, wl, sc)[..., :H, :W], atol=1e-12)
+    np.testing.assert_allclose(oracle.bwd_data(v, wb, wl, sc), oracle.bwd_data(vp, wb, wl, sc)[..., :H, :W],
+                               atol=1e-12)
+    for g, gp in zip(oracle.bwd_weight(x, v, wb, wl, sc), oracle.bwd_weight(xp, vp, wb, wl, sc)):
+        np.testing.assert_allclose(g, gp, atol=1e-10)
+
+
+@pytest.mark.parametrize("shape", ODD, ids=lambda s: "x".join(map(str, s)))
+def test_odd_planes_closed_form_adjoint_rotation_and_gcorr(shape):
+    """On planes that 2^L does not divide: the closed form (x zero beyond the
+    plane) equals the cascade; forward and backward data are adjoint;
+    backward data is the forward with rotated kernels; the scale-folded
+    gradient equals reverse mode."""
+    B, C, H, W, L, kb, k = shape
+    rng = np.random.default_rng(14)
+    x, v, wb, wl, sc = _rand_problem(rng, B, C, H, W, L, kb, k)
+    y = oracle.fwd(x, wb, wl, sc)
+    np.testing.assert_allclose(oracle.fwd_closed(x, wb, wl, sc), y, atol=1e-12)
+    dx = oracle.bwd_data(v, wb, wl, sc)
+    assert abs(np.vdot(y, v) - np.vdot(x, dx)) < 1e-10 * np.abs(y).sum()
+    np.testing.assert_allclose(dx, oracle.fwd(v, wb[:, ::-1, ::-1], wl[..., ::-1, ::-1], sc), atol=1e-12)
+    for a, b in zip(oracle.bwd_weight(x, v, wb, wl, sc), oracle.bwd_weight_gcorr(x, v, wb, wl, sc)):
+        np.testing.assert_allclose(a, b, atol=1e-10)
+
+
+@pytest.mark.parametrize("shape", ODD[:3], ids=lambda s: "x".join(map(str, s)))
+def test_odd_planes_against_torch_autograd(shape):
+    """torch's own pad, strided conv, transposed conv and crop, with
+    gradients by autograd, on planes that 2^L does not divide."""
+    B, C, H, W, L, kb, k = shape
+    rng = np.random.default_rng(15)
+    x, v, wb, wl, sc = _rand_problem(rng, B, C, H, W, L, kb, k)
+    t = [torch.from_numpy(a).clone().requires_grad_(True) for a in (x, wb, wl, sc)]
+    yt = _torch_layer(*t)
+    np.testing.assert_allclose(oracle.fwd(x, wb, wl, sc), yt.detach().numpy(), atol=1e-12)
+    yt.backward(torch.from_numpy(v))
+    np.testing.assert_allclose(oracle.bwd_data(v, wb, wl, sc), t[0].grad.numpy(), atol=1e-11)
+    for g, tg in zip(oracle.bwd_weight(x, v, wb, wl, sc), t[1:]):
+        np.testing.assert_allclose(g, tg.grad.numpy(), atol=1e-10)
