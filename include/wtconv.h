@@ -18,6 +18,10 @@
  *   B2 = (a-b+c-d)/2, B3 = (a-b-c+d)/2 (orthonormal); IWT is its inverse.
  *   corr(u, w)[i][j] = sum_{m,n<k} w[m][n] u[i+m-k/2][j+n-k/2], zero outside
  *   the level's own band grid (cross-correlation, 'same', stride 1).
+ *   An h x w image with odd h (w) is analysed as if it had one more, zero,
+ *   row (column): its bands are ceil(h/2) x ceil(w/2); IWT returns the
+ *   h x w image and drops the extra row (column). Where 2^L divides H and W
+ *   this is the plain halving of the pages' workloads.
  *
  * The kernels evaluate this through the three reformulations the abstract
  * lists: the Haar analysis is recomputed on chip from x (or dy) and never
@@ -65,8 +69,8 @@ typedef enum {
 typedef enum {
     WTCONV_OK = 0,
     WTCONV_ERR_INVALID_ARG = 1,        /* null pointer, overlap, bad dtype, sizes < 1 */
-    WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* H or W not divisible by 2^L, even or
-                                          unsupported k, or L out of range */
+    WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* even or unsupported k, L out of
+                                          range, or H*W above 2^30 */
     WTCONV_ERR_WORKSPACE = 3,          /* ws too small or misaligned */
     WTCONV_ERR_LAUNCH = 4              /* the HIP runtime rejected a launch */
 } wtconv_status_t;
@@ -93,8 +97,8 @@ size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
 /* Forward: y = WTConv(x). One fused pass: reads x once, writes y once.
    Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
    that fit one workgroup's LDS; ws may then be NULL).
-   Plane sizes without a fused kernel (any other H, W divisible by 2^L, any
-   L in 0..5, k in {3,5,7}; e.g. L = 0, the plain depthwise convolution) run
+   Plane sizes without a fused kernel (any other H, W >= 1, any L in 0..5,
+   k in {3,5,7}; e.g. L = 0, the plain depthwise convolution) run
    the generic one-kernel-per-step chain of the naive entry points below:
    the same results and semantics, with the intermediates in the workspace,
    which wtconv_workspace_size then reports. The same holds for
@@ -132,7 +136,7 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t *desc, const void *x,
    scale, LL add, synthesis, base convolution, final add) that keeps every
    intermediate in device memory, as the abstract describes the reference
    implementation. Same semantics and layouts as the fused entry points;
-   workspace from wtconv_naive_workspace_size. Any H, W divisible by 2^L. */
+   workspace from wtconv_naive_workspace_size. Any H, W >= 1. */
 size_t wtconv_naive_workspace_size(const wtconv_desc_t *desc, int32_t op);
 wtconv_status_t wtconv_naive_fwd(const wtconv_desc_t *desc, const void *x,
                                  const float *w_base, const float *w_lvl,

@@ -51,8 +51,8 @@ def test_status_strings(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(C=-1), 1), (dict(dtype=7), 1),
-    (dict(levels=6), 2), (dict(k_base=4), 2), (dict(k_level=9), 2), (dict(H=60), 2),
-    (dict(H=56, W=52), 2),  # 52 not divisible by 8
+    (dict(levels=6), 2), (dict(levels=-1), 2), (dict(k_base=4), 2), (dict(k_level=9), 2),
+    (dict(H=1 << 16, W=1 << 15), 2),  # a plane above 2^30 elements
 ])
 def test_bad_descriptors_rejected_before_launch(lib, kw, status):
     d = _desc(**kw)
@@ -74,16 +74,18 @@ def test_null_and_misaligned_pointers_rejected(lib):
 def test_unplanned_plane_takes_the_generic_chain(lib):
     """A plane size without a fused kernel runs the generic chain, which
     needs a workspace: its size is reported, and a call without one is
-    refused before anything launches. A plane not divisible by 2^L stays
-    unsupported."""
+    refused before anything launches. Planes that 2^L does not divide (odd
+    band grids) take it too."""
     d = _desc(H=40, W=48, levels=3)
     ok = ctypes.c_void_p(1 << 20)
     for op in (0, 1, 2):
         assert 0 < lib.wtconv_workspace_size(ctypes.byref(d), op) < (1 << 40)
     assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ctypes.c_void_p(1 << 30), None, 0, None) == 3
-    d = _desc(H=40, W=44, levels=3)
-    assert lib.wtconv_workspace_size(ctypes.byref(d), 0) == ctypes.c_size_t(-1).value
-    assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ctypes.c_void_p(1 << 30), None, 0, None) == 2
+    for H, W in ((40, 44), (13, 11), (1, 1)):
+        d = _desc(H=H, W=W, levels=3)
+        for op in (0, 1, 2):
+            assert 0 < lib.wtconv_workspace_size(ctypes.byref(d), op) < (1 << 40)
+        assert lib.wtconv_fwd(ctypes.byref(d), ok, ok, ok, ok, ctypes.c_void_p(1 << 30), None, 0, None) == 3
 
 
 def test_bwd_weight_workspace_checked(lib):

@@ -181,8 +181,8 @@ def test_identity_levels_closed_form_on_gpu(shape):
 
 def test_level_zero_and_unplanned_shapes():
     """L = 0 is the plain depthwise convolution. Plane sizes without a fused
-    kernel (here 20 x 12) run the generic chain through the same entry
-    points; a plane not divisible by 2^L is refused."""
+    kernel (here 20 x 12 and 24 x 20) run the generic chain through the same
+    entry points."""
     _say("[parity] L = 0 and unplanned shapes")
     inp = make_inputs(2, 3, 20, 12, 0, 5, 5, dtype="f32", seed=7)
     x, dy, wb, wl, sc = to_device(inp)
@@ -191,22 +191,35 @@ def test_level_zero_and_unplanned_shapes():
         y = fn(x, wb, wl, sc)
         torch.cuda.synchronize()
         assert rel_err(to_f64(y), ref.numpy()) <= 1e-6
+    _check_all_three(2, 3, 24, 20, 2, 3, 5)
+
+
+def _check_all_three(B, C, H, W, L, kb, k, seed=7):
     for dtype in ("f32", "bf16"):
-        inp = make_inputs(2, 3, 24, 20, 2, 3, 5, dtype=dtype, seed=7)
+        inp = make_inputs(B, C, H, W, L, kb, k, dtype=dtype, seed=seed)
         x, dy, wb, wl, sc = to_device(inp)
         y = wt.wtconv_fwd(x, wb, wl, sc)
         dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
-        dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, 3, wl, sc)
+        dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, kb, wl, sc)
         torch.cuda.synchronize()
         oy, odx, (odwb, odwl, odsc) = _oracle_all(inp)
         assert rel_err(to_f64(y), oy) <= TOL[dtype] and rel_err(to_f64(dx), odx) <= TOL[dtype]
         for g, o in ((dwb, odwb), (dwl, odwl), (dsc, odsc)):
             assert rel_err(to_f64(g), o) <= TOL["f32"]
-    inp = make_inputs(1, 2, 20, 12, 3, 5, 5, dtype="f32", seed=7)
-    x, dy, wb, wl, sc = to_device(inp)
-    with pytest.raises(wt.WTConvError) as ei:
-        wt.wtconv_fwd(x, wb, wl, sc)
-    assert ei.value.status == 2
+
+
+# planes that 2^L does not divide: odd band grids at one or more levels,
+# down to a 1 x 1 plane analysed five times
+ODD = [(2, 3, 13, 11, 2, 5, 3), (1, 2, 7, 9, 3, 3, 5), (2, 4, 57, 45, 3, 5, 5), (1, 3, 1, 1, 5, 3, 3),
+       (1, 2, 100, 3, 4, 7, 7), (1, 2, 129, 255, 5, 5, 5)]
+
+
+@pytest.mark.parametrize("shape", ODD, ids=lambda s: "x".join(map(str, s)))
+def test_odd_planes_match_oracle(shape):
+    """Forward, backward data and backward weight on planes that 2^L does
+    not divide, fp32 and bf16, against the oracle."""
+    _say(f"[parity] odd plane {shape}")
+    _check_all_three(*shape, seed=17)
 
 
 def test_repeated_calls_with_changing_batch():

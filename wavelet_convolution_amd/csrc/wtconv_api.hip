@@ -35,8 +35,6 @@ wtconv_status_t check_desc(const wtconv_desc_t* d) {
     const int kb = d->k_base, k = d->k_level;
     if (kb != 3 && kb != 5 && kb != 7) return WTCONV_ERR_UNSUPPORTED_SHAPE;
     if (k != 3 && k != 5 && k != 7) return WTCONV_ERR_UNSUPPORTED_SHAPE;
-    const int blk = 1 << d->levels;
-    if (d->H % blk != 0 || d->W % blk != 0) return WTCONV_ERR_UNSUPPORTED_SHAPE;
     // every index below is computed in 32 bits per plane and 64 bits across planes
     if ((int64_t)d->H * d->W > (1ll << 30) || (int64_t)d->B * d->C > (1ll << 31) - 1)
         return WTCONV_ERR_UNSUPPORTED_SHAPE;

@@ -6,6 +6,11 @@
 // data through HBM); it exists as the comparator for the fused kernels and as a
 // second, independently written GPU implementation for parity checks. It
 // uses the orthonormal Haar normalisation (1/2 per butterfly) literally.
+//
+// Band grids: level l holds ceil(h/2) x ceil(w/2) coefficients of the h x w
+// image it analyses; an odd last row or column is paired with a zero one, and
+// each synthesis writes back only the h x w image it came from. For planes
+// that 2^L divides this is the plain halving.
 #include "wtconv_device.h"
 #include "wtconv_naive.h"
 
@@ -21,17 +26,23 @@ inline unsigned grid_for(size_t n) {
     return (unsigned)(g > 65535u * 16u ? 65535u * 16u : (g ? g : 1));
 }
 
+// h x w image (row stride w, plane stride in_stride) -> four bands of
+// ceil(h/2) x ceil(w/2); taps beyond the image read as zero.
 template <typename TI>
 __global__ void k_dwt(const TI* __restrict__ in, size_t in_stride, float* __restrict__ out,
                       int planes, int h, int w) {
-    const int h2 = h / 2, w2 = w / 2;
+    const int h2 = (h + 1) / 2, w2 = (w + 1) / 2;
     const size_t n = (size_t)planes * h2 * w2;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
         const int j = (int)(e % w2);
         const int i = (int)((e / w2) % h2);
         const size_t p = e / ((size_t)h2 * w2);
         const TI* src = in + p * in_stride + (size_t)(2 * i) * w + 2 * j;
-        const float a = widen(src[0]), b = widen(src[1]), c = widen(src[w]), d = widen(src[w + 1]);
+        const bool r1 = 2 * i + 1 < h, c1 = 2 * j + 1 < w;
+        const float a = widen(src[0]);
+        const float b = c1 ? widen(src[1]) : 0.f;
+        const float c = r1 ? widen(src[w]) : 0.f;
+        const float d = (r1 && c1) ? widen(src[w + 1]) : 0.f;
         float* o = out + p * 4 * h2 * w2 + (size_t)i * w2 + j;
         const size_t bs = (size_t)h2 * w2;
         o[0] = 0.5f * (a + b + c + d);
@@ -84,8 +95,10 @@ __global__ void k_lladd(float* __restrict__ bands, const float* __restrict__ r, 
     }
 }
 
+// four bands of h2 x w2 -> the h x w image they were analysed from
+// (h2 = ceil(h/2), w2 = ceil(w/2)); samples beyond it are dropped.
 __global__ void k_iwt(const float* __restrict__ bands, float* __restrict__ out, int planes, int h2,
-                      int w2) {
+                      int w2, int h, int w) {
     const size_t n = (size_t)planes * h2 * w2;
     const size_t bs = (size_t)h2 * w2;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
@@ -94,11 +107,12 @@ __global__ void k_iwt(const float* __restrict__ bands, float* __restrict__ out, 
         const size_t p = e / bs;
         const float* b = bands + p * 4 * bs + (size_t)i * w2 + j;
         const float b0 = b[0], b1 = b[bs], b2 = b[2 * bs], b3 = b[3 * bs];
-        float* o = out + p * 4 * bs + (size_t)(2 * i) * (2 * w2) + 2 * j;
+        const bool r1 = 2 * i + 1 < h, c1 = 2 * j + 1 < w;
+        float* o = out + p * h * w + (size_t)(2 * i) * w + 2 * j;
         o[0] = 0.5f * (b0 + b1 + b2 + b3);
-        o[1] = 0.5f * (b0 + b1 - b2 - b3);
-        o[2 * w2] = 0.5f * (b0 - b1 + b2 - b3);
-        o[2 * w2 + 1] = 0.5f * (b0 - b1 - b2 + b3);
+        if (c1) o[1] = 0.5f * (b0 + b1 - b2 - b3);
+        if (r1) o[w] = 0.5f * (b0 - b1 + b2 - b3);
+        if (r1 && c1) o[w + 1] = 0.5f * (b0 - b1 - b2 + b3);
     }
 }
 
@@ -159,7 +173,17 @@ __global__ void k_wfinal(const float* __restrict__ gb, const float* __restrict__
     }
 }
 
-size_t level_floats(int P, int H, int W, int l) { return (size_t)P * (H >> (l - 1)) * (W >> (l - 1)); }
+// side of level l's band grid (level 0: the plane itself)
+inline int side(int n, int l) {
+    for (int i = 0; i < l; ++i) n = (n + 1) / 2;
+    return n;
+}
+
+// floats of level l's four bands over all P planes
+size_t level_floats(int P, int H, int W, int l) { return (size_t)P * 4 * side(H, l) * side(W, l); }
+
+// floats of the synthesis output of level l (an image of level l-1's size)
+size_t carry_floats(int P, int H, int W, int l) { return (size_t)P * side(H, l - 1) * side(W, l - 1); }
 
 }  // namespace
 
@@ -171,7 +195,7 @@ size_t naive_workspace_bytes(int B, int C, int H, int W, int L, int KB, int K, i
         for (int l = 1; l <= L; ++l) f += 2 * level_floats(P, H, W, l);
         f += (size_t)C * KB * KB + (size_t)L * 4 * C * K * K;
     } else {
-        for (int l = 1; l <= L; ++l) f += 2 * level_floats(P, H, W, l) + level_floats(P, H, W, l);
+        for (int l = 1; l <= L; ++l) f += 2 * level_floats(P, H, W, l) + carry_floats(P, H, W, l);
         f += (size_t)P * H * W;   // base output
     }
     return f * sizeof(float) + 256 * (3 * L + 4);
@@ -195,13 +219,13 @@ static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, b
     for (int l = 1; l <= L; ++l) {
         bands[l] = carve(cur, level_floats(P, H, W, l));
         conv[l] = carve(cur, level_floats(P, H, W, l));
-        carry[l - 1] = carve(cur, level_floats(P, H, W, l));
+        carry[l - 1] = carve(cur, carry_floats(P, H, W, l));
     }
     float* ybase = carve(cur, (size_t)P * H * W);
 
     for (int l = 1; l <= L; ++l) {
-        const int h = H >> (l - 1), w = W >> (l - 1);
-        const size_t n = (size_t)P * (h / 2) * (w / 2);
+        const int h = side(H, l - 1), w = side(W, l - 1);
+        const size_t n = (size_t)P * side(H, l) * side(W, l);
         if (l == 1)
             hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, in, (size_t)H * W, bands[1], P, h, w);
         else
@@ -209,7 +233,7 @@ static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, b
                                (size_t)4 * h * w, bands[l], P, h, w);
     }
     for (int l = 1; l <= L; ++l) {
-        const int h = H >> l, w = W >> l;
+        const int h = side(H, l), w = side(W, l);
         const size_t n = (size_t)P * 4 * h * w;
         hipLaunchKernelGGL(k_dwconv<float>, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)bands[l], conv[l],
                            4 * P, 4 * C, h, w, w_lvl + (size_t)(l - 1) * C * 4 * K * K, K, (int)flip);
@@ -217,11 +241,12 @@ static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, b
                            4 * P, 4 * C, h * w);
     }
     for (int l = L; l >= 1; --l) {
-        const int h = H >> l, w = W >> l;
+        const int h = side(H, l), w = side(W, l);
         const size_t n = (size_t)P * h * w;
         if (l < L)
             hipLaunchKernelGGL(k_lladd, dim3(grid_for(n)), dim3(NB), 0, st, conv[l], (const float*)carry[l], P, h * w);
-        hipLaunchKernelGGL(k_iwt, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)conv[l], carry[l - 1], P, h, w);
+        hipLaunchKernelGGL(k_iwt, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)conv[l], carry[l - 1], P, h, w,
+                           side(H, l - 1), side(W, l - 1));
     }
     const size_t n = (size_t)P * H * W;
     hipLaunchKernelGGL(k_dwconv<T>, dim3(grid_for(n)), dim3(NB), 0, st, in, ybase, P, C, H, W, w_base, KB,
@@ -256,8 +281,8 @@ static hipError_t wgrad_chain(int B, int C, int H, int W, int L, int KB, int K, 
     float* gb = carve(cur, (size_t)C * KB * KB);
     float* gl = carve(cur, (size_t)L * 4 * C * K * K);
     for (int l = 1; l <= L; ++l) {
-        const int h = H >> (l - 1), w = W >> (l - 1);
-        const size_t n = (size_t)P * (h / 2) * (w / 2);
+        const int h = side(H, l - 1), w = side(W, l - 1);
+        const size_t n = (size_t)P * side(H, l) * side(W, l);
         if (l == 1) {
             hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, x, (size_t)H * W, bx[1], P, h, w);
             hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, dy, (size_t)H * W, bd[1], P, h, w);
@@ -272,7 +297,7 @@ static hipError_t wgrad_chain(int B, int C, int H, int W, int L, int KB, int K, 
     for (int l = 1; l <= L; ++l)
         hipLaunchKernelGGL((k_wgrad<float, float>), dim3((unsigned)(4 * C * K * K)), dim3(NB), 0, st,
                            (const float*)bx[l], (const float*)bd[l], gl + (size_t)(l - 1) * 4 * C * K * K, B,
-                           4 * C, H >> l, W >> l, K);
+                           4 * C, side(H, l), side(W, l), K);
     hipLaunchKernelGGL(k_wfinal, dim3((unsigned)C), dim3(64), 0, st, (const float*)gb, (const float*)gl, C, L,
                        KB, K, w_lvl, scale, dw_base, dw_lvl, dscale);
     return hipGetLastError();

@@ -68,8 +68,9 @@ class WTConv2d(torch.nn.Module):
     [L, C, 4, k_level, k_level], ``scale`` [L, C, 4]. Initialisation: both
     kernels like a depthwise ``nn.Conv2d`` (uniform, bound 1/sqrt(k*k)), and
     unit scales. The pages fix no initialisation; this is the plainest one.
-    Input and output: [B, C, H, W], fp32 or bf16, with H and W divisible by
-    2^levels ('same' zero padding, stride 1).
+    Input and output: [B, C, H, W], fp32 or bf16, any H, W >= 1 ('same'
+    zero padding, stride 1; an odd band grid is analysed with one extra zero
+    row or column and its synthesis is cropped back).
     """
 
     def __init__(self, channels: int, levels: int, k_base: int = 5, k_level: int = 5,
