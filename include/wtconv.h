@@ -30,7 +30,8 @@
  * results. The result equals the cascade up to fp32 rounding order.
  *
  * Data layout (all device pointers, caller-owned):
- *   x, y, dy, dx   [B][C][H][W] contiguous, element type = desc->dtype
+ *   x, y, dy, dx   [B][C][H][W] contiguous (desc->layout WTCONV_NCHW) or
+ *                  [B][H][W][C] (WTCONV_NHWC), element type = desc->dtype
  *   w_base         [C][k_base][k_base]        fp32
  *   w_lvl          [L][C][4][k_level][k_level] fp32 (level index 0 = level 1)
  *   scale          [L][C][4]                  fp32
@@ -67,8 +68,14 @@ typedef enum {
 } wtconv_dtype_t;
 
 typedef enum {
+    WTCONV_NCHW = 0,   /* [B][C][H][W] contiguous */
+    WTCONV_NHWC = 1    /* channels last: [B][H][W][C] contiguous */
+} wtconv_layout_t;
+
+typedef enum {
     WTCONV_OK = 0,
-    WTCONV_ERR_INVALID_ARG = 1,        /* null pointer, overlap, bad dtype, sizes < 1 */
+    WTCONV_ERR_INVALID_ARG = 1,        /* null pointer, overlap, bad dtype or
+                                          layout, sizes < 1 */
     WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* even or unsupported k, L out of
                                           range, or H*W above 2^30 */
     WTCONV_ERR_WORKSPACE = 3,          /* ws too small or misaligned */
@@ -84,9 +91,10 @@ typedef enum {
 typedef struct {
     int32_t B, C, H, W;   /* activation shape, NCHW */
     int32_t levels;       /* L, 0..5 */
-    int32_t k_base;       /* base kernel size: 3, 5 or 7 */
-    int32_t k_level;      /* per-level kernel size: 3, 5 or 7 */
+    int32_t k_base;       /* base kernel size: odd, 1..15 */
+    int32_t k_level;      /* per-level kernel size: odd, 1..15 */
     int32_t dtype;        /* wtconv_dtype_t */
+    int32_t layout;       /* wtconv_layout_t of x, y, dy, dx (all four alike) */
 } wtconv_desc_t;
 
 /* Bytes of device workspace `op` needs for `desc` (0 if none). Returns
@@ -97,8 +105,9 @@ size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
 /* Forward: y = WTConv(x). One fused pass: reads x once, writes y once.
    Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
    that fit one workgroup's LDS; ws may then be NULL).
-   Plane sizes without a fused kernel (any other H, W >= 1, any L in 0..5,
-   k in {3,5,7}; e.g. L = 0, the plain depthwise convolution) run
+   Shapes without a fused kernel (any other H, W >= 1, L in 0..5, odd k up
+   to 15; e.g. L = 0, the plain depthwise convolution), and every shape in
+   the channels-last layout, run
    the generic one-kernel-per-step chain of the naive entry points below:
    the same results and semantics, with the intermediates in the workspace,
    which wtconv_workspace_size then reports. The same holds for
@@ -155,7 +164,7 @@ wtconv_status_t wtconv_naive_bwd_weight(const wtconv_desc_t *desc, const void *x
 /* Static description of a status code. */
 const char *wtconv_status_string(wtconv_status_t status);
 
-/* Library version, e.g. "0.1.0". */
+/* Library version, e.g. "0.2.0". */
 const char *wtconv_version(void);
 
 #ifdef __cplusplus

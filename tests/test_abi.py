@@ -50,8 +50,8 @@ def test_status_strings(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(B=0), 1), (dict(C=-1), 1), (dict(dtype=7), 1),
-    (dict(levels=6), 2), (dict(levels=-1), 2), (dict(k_base=4), 2), (dict(k_level=9), 2),
+    (dict(B=0), 1), (dict(C=-1), 1), (dict(dtype=7), 1), (dict(layout=2), 1), (dict(layout=-1), 1),
+    (dict(levels=6), 2), (dict(levels=-1), 2), (dict(k_base=4), 2), (dict(k_level=17), 2), (dict(k_base=-1), 2),
     (dict(H=1 << 16, W=1 << 15), 2),  # a plane above 2^30 elements
 ])
 def test_bad_descriptors_rejected_before_launch(lib, kw, status):
@@ -99,3 +99,26 @@ def test_bwd_weight_workspace_checked(lib):
     # misaligned
     assert lib.wtconv_bwd_weight(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ctypes.c_void_p((1 << 24) + 16),
                                  need, None) == 3
+
+
+def test_channels_last_takes_the_generic_chain(lib):
+    """The fused kernels are planar; a channels-last descriptor of a planned
+    plane is served by the generic chain, so it needs that chain's workspace."""
+    planar, nhwc = _desc(layout=0), _desc(layout=1)
+    assert lib.wtconv_workspace_size(ctypes.byref(planar), 0) == 0
+    for op in (0, 1, 2):
+        assert lib.wtconv_workspace_size(ctypes.byref(nhwc), op) == lib.wtconv_naive_workspace_size(
+            ctypes.byref(nhwc), op) > 0
+
+
+def test_binding_reads_the_memory_order():
+    """The binding's layout code follows the tensor's strides and refuses any
+    other order (a transposed view would otherwise be read as planar)."""
+    import torch
+    from wavelet_convolution_amd.binding import layout_of
+    x = torch.zeros(2, 3, 8, 6)
+    assert layout_of(x) == 0
+    assert layout_of(x.to(memory_format=torch.channels_last)) == 1
+    assert layout_of(torch.zeros(1, 1, 8, 6).to(memory_format=torch.channels_last)) == 0
+    with pytest.raises(ValueError):
+        layout_of(x.transpose(2, 3))

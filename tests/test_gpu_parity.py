@@ -214,12 +214,38 @@ ODD = [(2, 3, 13, 11, 2, 5, 3), (1, 2, 7, 9, 3, 3, 5), (2, 4, 57, 45, 3, 5, 5), 
        (1, 2, 100, 3, 4, 7, 7), (1, 2, 129, 255, 5, 5, 5)]
 
 
-@pytest.mark.parametrize("shape", ODD, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", ODD + [(2, 3, 28, 28, 2, 9, 9), (1, 4, 20, 24, 2, 1, 3), (1, 2, 33, 30, 3, 3, 15)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_odd_planes_match_oracle(shape):
     """Forward, backward data and backward weight on planes that 2^L does
-    not divide, fp32 and bf16, against the oracle."""
+    not divide, and with kernels the fused plans do not cover (1, 9, 15),
+    fp32 and bf16, against the oracle."""
     _say(f"[parity] odd plane {shape}")
     _check_all_three(*shape, seed=17)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 56, 56, 3, 5, 5), (1, 4, 13, 11, 2, 3, 5), (2, 2, 28, 28, 0, 7, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_channels_last_matches_oracle(shape):
+    """Channels-last activations (the generic chain) give the oracle's
+    results, and y and dx come back channels last."""
+    _say(f"[parity] channels last {shape}")
+    cl = torch.channels_last
+    for dtype in ("f32", "bf16"):
+        inp = make_inputs(*shape, dtype=dtype, seed=19)
+        x, dy, wb, wl, sc = to_device(inp)
+        x, dy = x.contiguous(memory_format=cl), dy.contiguous(memory_format=cl)
+        assert not x.is_contiguous()
+        y = wt.wtconv_fwd(x, wb, wl, sc)
+        dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+        dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, shape[5], wl, sc)
+        torch.cuda.synchronize()
+        assert y.is_contiguous(memory_format=cl) and dx.is_contiguous(memory_format=cl)
+        oy, odx, (odwb, odwl, odsc) = _oracle_all(inp)
+        assert rel_err(to_f64(y), oy) <= TOL[dtype] and rel_err(to_f64(dx), odx) <= TOL[dtype]
+        for g, o in ((dwb, odwb), (dwl, odwl), (dsc, odsc)):
+            if g.numel():
+                assert rel_err(to_f64(g), o) <= TOL["f32"]
 
 
 def test_repeated_calls_with_changing_batch():

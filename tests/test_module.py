@@ -106,6 +106,28 @@ def test_module_matches_oracle(shape, dtype):
 
 @pytest.mark.gpu
 @torch_gpu
+def test_module_channels_last():
+    """A channels-last input gives the same results as the planar one, and y
+    and dx keep its memory order."""
+    print("[module] channels last 2x3x28x28 L2 f32", flush=True)
+    inp = make_inputs(2, 3, 28, 28, 2, 5, 5, dtype="f32", seed=21)
+    x, dy, wb, wl, sc = to_device(inp)
+    m = WTConv2d(3, 2, 5, 5, device="cuda")
+    outs = []
+    for fmt in (torch.contiguous_format, torch.channels_last):
+        xi = x.detach().contiguous(memory_format=fmt).requires_grad_(True)
+        m.zero_grad()
+        y = m(xi)
+        y.backward(dy.contiguous(memory_format=fmt))
+        torch.cuda.synchronize()
+        assert y.is_contiguous(memory_format=fmt) and xi.grad.is_contiguous(memory_format=fmt)
+        outs.append([to_f64(t) for t in (y, xi.grad, m.w_base.grad, m.w_lvl.grad, m.scale.grad)])
+    for a, b in zip(*outs):
+        assert rel_err(b, a) <= 1e-5
+
+
+@pytest.mark.gpu
+@torch_gpu
 def test_module_keeps_only_x_and_its_peak_memory():
     """The backward pass rebuilds the pyramid on chip: autograd holds x (and
     the parameters), nothing else. Peak memory of a training step stays

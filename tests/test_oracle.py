@@ -441,10 +441,12 @@ def test_odd_planes_closed_form_adjoint_rotation_and_gcorr(shape):
         np.testing.assert_allclose(a, b, atol=1e-10)
 
 
-@pytest.mark.parametrize("shape", ODD[:3], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", ODD[:3] + [(1, 2, 12, 10, 2, 9, 1), (1, 1, 9, 9, 1, 15, 11)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_odd_planes_against_torch_autograd(shape):
     """torch's own pad, strided conv, transposed conv and crop, with
-    gradients by autograd, on planes that 2^L does not divide."""
+    gradients by autograd, on planes that 2^L does not divide and with
+    kernel sizes 1, 9, 11 and 15."""
     B, C, H, W, L, kb, k = shape
     rng = np.random.default_rng(15)
     x, v, wb, wl, sc = _rand_problem(rng, B, C, H, W, L, kb, k)

@@ -18,6 +18,7 @@ _lock = threading.Lock()
 _lib = None
 
 WTCONV_F32, WTCONV_BF16 = 0, 1
+WTCONV_NCHW, WTCONV_NHWC = 0, 1
 OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2
 
 
@@ -32,7 +33,7 @@ class WTConvError(RuntimeError):
 class WTConvDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("C", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("W", ctypes.c_int32), ("levels", ctypes.c_int32), ("k_base", ctypes.c_int32),
-                ("k_level", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("k_level", ctypes.c_int32), ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _V = ctypes.c_void_p
@@ -78,10 +79,25 @@ def _check(status: int) -> None:
         raise WTConvError(status, wtconv_status_string(status))
 
 
+def layout_of(act: torch.Tensor) -> int:
+    """The library's layout code for a [B, C, H, W] tensor's memory order:
+    planar (contiguous) or channels last. Any other strides are an error."""
+    if act.is_contiguous():
+        return WTCONV_NCHW
+    if act.dim() == 4 and act.is_contiguous(memory_format=torch.channels_last):
+        return WTCONV_NHWC
+    raise ValueError("activations must be contiguous in NCHW or channels-last order")
+
+
 def _desc(act: torch.Tensor, levels: int, k_base: int, k_level: int) -> WTConvDesc:
     B, C, H, W = act.shape
     dt = {torch.float32: WTCONV_F32, torch.bfloat16: WTCONV_BF16}.get(act.dtype, -1)
-    return WTConvDesc(B, C, H, W, int(levels), int(k_base), int(k_level), dt)
+    return WTConvDesc(B, C, H, W, int(levels), int(k_base), int(k_level), dt, layout_of(act))
+
+
+def _same_layout(a: torch.Tensor, b: torch.Tensor) -> None:
+    if b.shape != a.shape or b.dtype != a.dtype or layout_of(b) != layout_of(a):
+        raise ValueError("activation tensors of one call must share shape, dtype and memory order")
 
 
 def _ptr(t) -> int:
@@ -129,7 +145,8 @@ def _data_pass(name: str, naive: bool, op: int, act, w_base, w_lvl, scale, out, 
     levels, kb, k = _dims(w_base, w_lvl)
     d = _desc(act, levels, kb, k)
     if out is None:
-        out = torch.empty_like(act)
+        out = torch.empty_like(act)   # same memory order as act
+    _same_layout(act, out)
     if ws is None:
         ws = _workspace(wtconv_workspace_size(act, levels, kb, k, op, naive), act.device)
     ws_bytes = 0 if ws is None else ws.numel() - (_ws_ptr(ws) - ws.data_ptr())
@@ -163,6 +180,7 @@ def _bwd_weight(name: str, naive: bool, x, dy, w_base_shape_kb, w_lvl, scale, ou
     k = int(w_lvl.shape[-1])
     kb = int(w_base_shape_kb)
     d = _desc(x, levels, kb, k)
+    _same_layout(x, dy)
     C = x.shape[1]
     if out is None:
         dev = x.device

@@ -31,10 +31,12 @@ wtconv_status_t check_desc(const wtconv_desc_t* d) {
     if (!d) return WTCONV_ERR_INVALID_ARG;
     if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1) return WTCONV_ERR_INVALID_ARG;
     if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_BF16) return WTCONV_ERR_INVALID_ARG;
+    if (d->layout != WTCONV_NCHW && d->layout != WTCONV_NHWC) return WTCONV_ERR_INVALID_ARG;
     if (d->levels < 0 || d->levels > 5) return WTCONV_ERR_UNSUPPORTED_SHAPE;
     const int kb = d->k_base, k = d->k_level;
-    if (kb != 3 && kb != 5 && kb != 7) return WTCONV_ERR_UNSUPPORTED_SHAPE;
-    if (k != 3 && k != 5 && k != 7) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    // odd kernels up to 15; the fused plans cover 3, 5 and 7, the generic chain any of them
+    if (kb < 1 || kb > 15 || kb % 2 == 0) return WTCONV_ERR_UNSUPPORTED_SHAPE;
+    if (k < 1 || k > 15 || k % 2 == 0) return WTCONV_ERR_UNSUPPORTED_SHAPE;
     // every index below is computed in 32 bits per plane and 64 bits across planes
     if ((int64_t)d->H * d->W > (1ll << 30) || (int64_t)d->B * d->C > (1ll << 31) - 1)
         return WTCONV_ERR_UNSUPPORTED_SHAPE;
@@ -61,24 +63,27 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     st = check_params(d, w_base, w_lvl, scale, true);
     if (st != WTCONV_OK) return st;
     const int dt = d->dtype == WTCONV_BF16 ? 1 : 0;
+    const bool nchw = d->layout == WTCONV_NCHW;
     hipError_t err;
-    if (const wtc::PlaneEntry* e = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) {
+    const wtc::PlaneEntry* pe = nchw ? wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level) : nullptr;
+    const wtc::SplitEntry* se = nchw ? wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level) : nullptr;
+    if (const wtc::PlaneEntry* e = pe) {
         // the whole plane fits one workgroup: one kernel, no workspace
         err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, d->B, d->C, (hipStream_t)stream);
-    } else if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) {
+    } else if (const wtc::SplitEntry* e = se) {
         // coarse pass on the LL band at level L0, then the fine tiles
         const size_t need = e->ws_bytes(d->B, d->C);
         if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
         err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, (float*)ws, d->B, d->C, (hipStream_t)stream);
     } else {
-        // no fused kernel for this plane size: the generic one-kernel-per-step
-        // chain (same results, intermediates in device memory)
+        // no fused kernel for this shape or layout: the generic
+        // one-kernel-per-step chain (same results, intermediates in device memory)
         const int op = flip ? WTCONV_OP_BWD_DATA : WTCONV_OP_FWD;
         const size_t need = wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
                                                        d->k_level, op);
         if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
         err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
-                                     d->dtype == WTCONV_BF16, flip, in, w_base, w_lvl, scale, out, ws,
+                                     d->dtype == WTCONV_BF16, flip, !nchw, in, w_base, w_lvl, scale, out, ws,
                                      (hipStream_t)stream);
     }
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
@@ -86,7 +91,8 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
 
 // Whether the fused weight-gradient kernels have a plan for this shape.
 bool fused_bwdw_planned(const wtconv_desc_t* d) {
-    return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level) !=
+    return d->layout == WTCONV_NCHW &&
+           wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level) !=
            (size_t)-1;
 }
 
@@ -99,9 +105,11 @@ size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
     switch (op) {
     case WTCONV_OP_FWD:
     case WTCONV_OP_BWD_DATA:
-        if (wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) return 0;
-        if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))
-            return e->ws_bytes(d->B, d->C);
+        if (d->layout == WTCONV_NCHW) {
+            if (wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) return 0;
+            if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))
+                return e->ws_bytes(d->B, d->C);
+        }
         return wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, op);
     case WTCONV_OP_BWD_WEIGHT:
         if (fused_bwdw_planned(d))
@@ -148,8 +156,8 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const v
                                dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
     else   // no fused plan for this shape: the generic chain
         err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
-                                     d->dtype == WTCONV_BF16, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws,
-                                     (hipStream_t)stream);
+                                     d->dtype == WTCONV_BF16, d->layout == WTCONV_NHWC, x, dy, w_lvl, scale,
+                                     dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
@@ -173,8 +181,8 @@ static wtconv_status_t naive_data(const wtconv_desc_t* d, const void* in, const 
     if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
     hipError_t err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base,
                                             d->k_level, d->dtype == WTCONV_BF16,
-                                            op == WTCONV_OP_BWD_DATA, in, w_base, w_lvl, scale,
-                                            out, ws, (hipStream_t)stream);
+                                            op == WTCONV_OP_BWD_DATA, d->layout == WTCONV_NHWC, in,
+                                            w_base, w_lvl, scale, out, ws, (hipStream_t)stream);
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
@@ -204,23 +212,23 @@ wtconv_status_t wtconv_naive_bwd_weight(const wtconv_desc_t* d, const void* x, c
                                                    d->k_level, WTCONV_OP_BWD_WEIGHT);
     if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
     hipError_t err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base,
-                                            d->k_level, d->dtype == WTCONV_BF16, x, dy, w_lvl,
-                                            scale, dw_base, dw_lvl, dscale, ws,
-                                            (hipStream_t)stream);
+                                            d->k_level, d->dtype == WTCONV_BF16,
+                                            d->layout == WTCONV_NHWC, x, dy, w_lvl, scale, dw_base,
+                                            dw_lvl, dscale, ws, (hipStream_t)stream);
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
 const char* wtconv_status_string(wtconv_status_t s) {
     switch (s) {
     case WTCONV_OK: return "WTCONV_OK";
-    case WTCONV_ERR_INVALID_ARG: return "WTCONV_ERR_INVALID_ARG: null, misaligned or overlapping pointer, or bad size/dtype";
-    case WTCONV_ERR_UNSUPPORTED_SHAPE: return "WTCONV_ERR_UNSUPPORTED_SHAPE: H, W not divisible by 2^L, unsupported kernel size or levels, or no kernel for this plane";
+    case WTCONV_ERR_INVALID_ARG: return "WTCONV_ERR_INVALID_ARG: null, misaligned or overlapping pointer, or bad size, dtype or layout";
+    case WTCONV_ERR_UNSUPPORTED_SHAPE: return "WTCONV_ERR_UNSUPPORTED_SHAPE: unsupported kernel size or levels, or a plane above 2^30 elements";
     case WTCONV_ERR_WORKSPACE: return "WTCONV_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
     case WTCONV_ERR_LAUNCH: return "WTCONV_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     default: return "WTCONV: unknown status";
     }
 }
 
-const char* wtconv_version(void) { return "0.1.0"; }
+const char* wtconv_version(void) { return "0.2.0"; }
 
 }  // extern "C"

@@ -21,6 +21,14 @@ namespace {
 
 constexpr int NB = 256;
 
+// Offset of element (plane p = b*nch + c, row i, column j) of an h x w
+// activation: planar ([B][C][H][W], plane stride ps) or, with nhwc set,
+// channels-last ([B][H][W][C]). Band buffers are always planar.
+__device__ inline size_t act_at(size_t p, int i, int j, int h, int w, size_t ps, int nch, int nhwc) {
+    if (!nhwc) return p * ps + (size_t)i * w + j;
+    return (((p / nch) * h + i) * (size_t)w + j) * nch + p % nch;
+}
+
 inline unsigned grid_for(size_t n) {
     size_t g = (n + NB - 1) / NB;
     return (unsigned)(g > 65535u * 16u ? 65535u * 16u : (g ? g : 1));
@@ -30,19 +38,18 @@ inline unsigned grid_for(size_t n) {
 // ceil(h/2) x ceil(w/2); taps beyond the image read as zero.
 template <typename TI>
 __global__ void k_dwt(const TI* __restrict__ in, size_t in_stride, float* __restrict__ out,
-                      int planes, int h, int w) {
+                      int planes, int h, int w, int nch, int nhwc) {
     const int h2 = (h + 1) / 2, w2 = (w + 1) / 2;
     const size_t n = (size_t)planes * h2 * w2;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
         const int j = (int)(e % w2);
         const int i = (int)((e / w2) % h2);
         const size_t p = e / ((size_t)h2 * w2);
-        const TI* src = in + p * in_stride + (size_t)(2 * i) * w + 2 * j;
         const bool r1 = 2 * i + 1 < h, c1 = 2 * j + 1 < w;
-        const float a = widen(src[0]);
-        const float b = c1 ? widen(src[1]) : 0.f;
-        const float c = r1 ? widen(src[w]) : 0.f;
-        const float d = (r1 && c1) ? widen(src[w + 1]) : 0.f;
+        const float a = widen(in[act_at(p, 2 * i, 2 * j, h, w, in_stride, nch, nhwc)]);
+        const float b = c1 ? widen(in[act_at(p, 2 * i, 2 * j + 1, h, w, in_stride, nch, nhwc)]) : 0.f;
+        const float c = r1 ? widen(in[act_at(p, 2 * i + 1, 2 * j, h, w, in_stride, nch, nhwc)]) : 0.f;
+        const float d = (r1 && c1) ? widen(in[act_at(p, 2 * i + 1, 2 * j + 1, h, w, in_stride, nch, nhwc)]) : 0.f;
         float* o = out + p * 4 * h2 * w2 + (size_t)i * w2 + j;
         const size_t bs = (size_t)h2 * w2;
         o[0] = 0.5f * (a + b + c + d);
@@ -56,7 +63,7 @@ __global__ void k_dwt(const TI* __restrict__ in, size_t in_stride, float* __rest
 // p % nch; flip turns every kernel by 180 degrees.
 template <typename TI>
 __global__ void k_dwconv(const TI* __restrict__ in, float* __restrict__ out, int planes, int nch,
-                         int h, int w, const float* __restrict__ wts, int k, int flip) {
+                         int h, int w, const float* __restrict__ wts, int k, int flip, int nhwc) {
     const size_t n = (size_t)planes * h * w;
     const int p2 = k / 2;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
@@ -64,7 +71,6 @@ __global__ void k_dwconv(const TI* __restrict__ in, float* __restrict__ out, int
         const int i = (int)((e / w) % h);
         const size_t p = e / ((size_t)h * w);
         const float* wk = wts + (size_t)(p % nch) * k * k;
-        const TI* src = in + p * h * w;
         float acc = 0.f;
         for (int m = 0; m < k; ++m) {
             const int ii = i + m - p2;
@@ -73,7 +79,7 @@ __global__ void k_dwconv(const TI* __restrict__ in, float* __restrict__ out, int
                 const int jj = j + q - p2;
                 if (jj < 0 || jj >= w) continue;
                 const float wv = flip ? wk[(k - 1 - m) * k + (k - 1 - q)] : wk[m * k + q];
-                acc += wv * widen(src[(size_t)ii * w + jj]);
+                acc += wv * widen(in[act_at(p, ii, jj, h, w, (size_t)h * w, nch, nhwc)]);
             }
         }
         out[e] = acc;
@@ -116,13 +122,17 @@ __global__ void k_iwt(const float* __restrict__ bands, float* __restrict__ out, 
     }
 }
 
+// out = a + b (planar fp32 buffers) in the activation layout
 template <typename T>
 __global__ void k_final(const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ out,
-                        size_t n) {
+                        size_t n, int nch, int h, int w, int nhwc) {
+    const size_t hw = (size_t)h * w;
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
         const float v = a[e] + (b ? b[e] : 0.f);
-        if constexpr (sizeof(T) == 2) out[e] = narrow_bf16(v);
-        else out[e] = v;
+        const size_t t = e % hw;
+        const size_t o = act_at(e / hw, (int)(t / w), (int)(t % w), h, w, hw, nch, nhwc);
+        if constexpr (sizeof(T) == 2) out[o] = narrow_bf16(v);
+        else out[o] = v;
     }
 }
 
@@ -130,7 +140,7 @@ __global__ void k_final(const float* __restrict__ a, const float* __restrict__ b
 // block per (channel, tap), fixed-order tree reduction.
 template <typename TU, typename TV>
 __global__ void k_wgrad(const TU* __restrict__ u, const TV* __restrict__ v, float* __restrict__ g,
-                        int B, int nch, int h, int w, int k) {
+                        int B, int nch, int h, int w, int k, int nhwc) {
     __shared__ float red[NB];
     const int ch = blockIdx.x / (k * k), tap = blockIdx.x % (k * k);
     const int m = tap / k, q = tap % k, p2 = k / 2;
@@ -143,7 +153,8 @@ __global__ void k_wgrad(const TU* __restrict__ u, const TV* __restrict__ v, floa
         const int ii = i + m - p2, jj = j + q - p2;
         if (ii < 0 || ii >= h || jj < 0 || jj >= w) continue;
         const size_t plane = b * nch + ch;
-        acc += widen(v[plane * h * w + (size_t)i * w + j]) * widen(u[plane * h * w + (size_t)ii * w + jj]);
+        const size_t ps = (size_t)h * w;
+        acc += widen(v[act_at(plane, i, j, h, w, ps, nch, nhwc)]) * widen(u[act_at(plane, ii, jj, h, w, ps, nch, nhwc)]);
     }
     red[threadIdx.x] = acc;
     __syncthreads();
@@ -208,7 +219,7 @@ static float* carve(char*& p, size_t floats) {
 }
 
 template <typename T>
-static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, bool flip,
+static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, bool flip, int nhwc,
                              const T* in, const float* w_base, const float* w_lvl, const float* scale,
                              T* out, void* ws, hipStream_t st) {
     const int P = B * C;
@@ -227,16 +238,17 @@ static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, b
         const int h = side(H, l - 1), w = side(W, l - 1);
         const size_t n = (size_t)P * side(H, l) * side(W, l);
         if (l == 1)
-            hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, in, (size_t)H * W, bands[1], P, h, w);
+            hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, in, (size_t)H * W, bands[1], P, h, w,
+                               C, nhwc);
         else
             hipLaunchKernelGGL(k_dwt<float>, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)bands[l - 1],
-                               (size_t)4 * h * w, bands[l], P, h, w);
+                               (size_t)4 * h * w, bands[l], P, h, w, C, 0);
     }
     for (int l = 1; l <= L; ++l) {
         const int h = side(H, l), w = side(W, l);
         const size_t n = (size_t)P * 4 * h * w;
         hipLaunchKernelGGL(k_dwconv<float>, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)bands[l], conv[l],
-                           4 * P, 4 * C, h, w, w_lvl + (size_t)(l - 1) * C * 4 * K * K, K, (int)flip);
+                           4 * P, 4 * C, h, w, w_lvl + (size_t)(l - 1) * C * 4 * K * K, K, (int)flip, 0);
         hipLaunchKernelGGL(k_scale, dim3(grid_for(n)), dim3(NB), 0, st, conv[l], scale + (size_t)(l - 1) * C * 4,
                            4 * P, 4 * C, h * w);
     }
@@ -250,24 +262,25 @@ static hipError_t data_chain(int B, int C, int H, int W, int L, int KB, int K, b
     }
     const size_t n = (size_t)P * H * W;
     hipLaunchKernelGGL(k_dwconv<T>, dim3(grid_for(n)), dim3(NB), 0, st, in, ybase, P, C, H, W, w_base, KB,
-                       (int)flip);
+                       (int)flip, nhwc);
     hipLaunchKernelGGL(k_final<T>, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)ybase,
-                       (const float*)(L > 0 ? carry[0] : nullptr), out, n);
+                       (const float*)(L > 0 ? carry[0] : nullptr), out, n, C, H, W, nhwc);
     return hipGetLastError();
 }
 
 hipError_t naive_data_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16, bool flip,
-                             const void* in, const float* w_base, const float* w_lvl,
+                             bool nhwc, const void* in, const float* w_base, const float* w_lvl,
                              const float* scale, void* out, void* ws, hipStream_t stream) {
     if (bf16)
-        return data_chain<bf16_t>(B, C, H, W, L, KB, K, flip, (const bf16_t*)in, w_base, w_lvl, scale,
-                                  (bf16_t*)out, ws, stream);
-    return data_chain<float>(B, C, H, W, L, KB, K, flip, (const float*)in, w_base, w_lvl, scale, (float*)out,
-                             ws, stream);
+        return data_chain<bf16_t>(B, C, H, W, L, KB, K, flip, (int)nhwc, (const bf16_t*)in, w_base, w_lvl,
+                                  scale, (bf16_t*)out, ws, stream);
+    return data_chain<float>(B, C, H, W, L, KB, K, flip, (int)nhwc, (const float*)in, w_base, w_lvl, scale,
+                             (float*)out, ws, stream);
 }
 
 template <typename T>
-static hipError_t wgrad_chain(int B, int C, int H, int W, int L, int KB, int K, const T* x, const T* dy,
+static hipError_t wgrad_chain(int B, int C, int H, int W, int L, int KB, int K, int nhwc, const T* x,
+                              const T* dy,
                               const float* w_lvl, const float* scale, float* dw_base, float* dw_lvl,
                               float* dscale, void* ws, hipStream_t st) {
     const int P = B * C;
@@ -284,33 +297,36 @@ static hipError_t wgrad_chain(int B, int C, int H, int W, int L, int KB, int K, 
         const int h = side(H, l - 1), w = side(W, l - 1);
         const size_t n = (size_t)P * side(H, l) * side(W, l);
         if (l == 1) {
-            hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, x, (size_t)H * W, bx[1], P, h, w);
-            hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, dy, (size_t)H * W, bd[1], P, h, w);
+            hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, x, (size_t)H * W, bx[1], P, h, w, C,
+                               nhwc);
+            hipLaunchKernelGGL(k_dwt<T>, dim3(grid_for(n)), dim3(NB), 0, st, dy, (size_t)H * W, bd[1], P, h, w, C,
+                               nhwc);
         } else {
             hipLaunchKernelGGL(k_dwt<float>, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)bx[l - 1],
-                               (size_t)4 * h * w, bx[l], P, h, w);
+                               (size_t)4 * h * w, bx[l], P, h, w, C, 0);
             hipLaunchKernelGGL(k_dwt<float>, dim3(grid_for(n)), dim3(NB), 0, st, (const float*)bd[l - 1],
-                               (size_t)4 * h * w, bd[l], P, h, w);
+                               (size_t)4 * h * w, bd[l], P, h, w, C, 0);
         }
     }
-    hipLaunchKernelGGL((k_wgrad<T, T>), dim3((unsigned)(C * KB * KB)), dim3(NB), 0, st, x, dy, gb, B, C, H, W, KB);
+    hipLaunchKernelGGL((k_wgrad<T, T>), dim3((unsigned)(C * KB * KB)), dim3(NB), 0, st, x, dy, gb, B, C, H, W, KB,
+                       nhwc);
     for (int l = 1; l <= L; ++l)
         hipLaunchKernelGGL((k_wgrad<float, float>), dim3((unsigned)(4 * C * K * K)), dim3(NB), 0, st,
                            (const float*)bx[l], (const float*)bd[l], gl + (size_t)(l - 1) * 4 * C * K * K, B,
-                           4 * C, side(H, l), side(W, l), K);
+                           4 * C, side(H, l), side(W, l), K, 0);
     hipLaunchKernelGGL(k_wfinal, dim3((unsigned)C), dim3(64), 0, st, (const float*)gb, (const float*)gl, C, L,
                        KB, K, w_lvl, scale, dw_base, dw_lvl, dscale);
     return hipGetLastError();
 }
 
-hipError_t naive_bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16, const void* x,
-                             const void* dy, const float* w_lvl, const float* scale, float* dw_base,
-                             float* dw_lvl, float* dscale, void* ws, hipStream_t stream) {
+hipError_t naive_bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16, bool nhwc,
+                             const void* x, const void* dy, const float* w_lvl, const float* scale,
+                             float* dw_base, float* dw_lvl, float* dscale, void* ws, hipStream_t stream) {
     if (bf16)
-        return wgrad_chain<bf16_t>(B, C, H, W, L, KB, K, (const bf16_t*)x, (const bf16_t*)dy, w_lvl, scale,
-                                   dw_base, dw_lvl, dscale, ws, stream);
-    return wgrad_chain<float>(B, C, H, W, L, KB, K, (const float*)x, (const float*)dy, w_lvl, scale, dw_base,
-                              dw_lvl, dscale, ws, stream);
+        return wgrad_chain<bf16_t>(B, C, H, W, L, KB, K, (int)nhwc, (const bf16_t*)x, (const bf16_t*)dy, w_lvl,
+                                   scale, dw_base, dw_lvl, dscale, ws, stream);
+    return wgrad_chain<float>(B, C, H, W, L, KB, K, (int)nhwc, (const float*)x, (const float*)dy, w_lvl, scale,
+                              dw_base, dw_lvl, dscale, ws, stream);
 }
 
 }  // namespace wtc

@@ -28,18 +28,27 @@ def _check_device(*ts: torch.Tensor) -> None:
                                f"{t.device} - there is no CPU implementation")
 
 
+def _order(x: torch.Tensor):
+    """channels_last if x is stored that way (and not also planar), else planar."""
+    if not x.is_contiguous() and x.dim() == 4 and x.is_contiguous(memory_format=torch.channels_last):
+        return torch.channels_last
+    return torch.contiguous_format
+
+
 class WTConvFunction(torch.autograd.Function):
     """y = WTConv(x; w_base, w_lvl, scale).
 
-    x: [B, C, H, W] fp32 or bf16 (contiguous NCHW), w_base: [C, kb, kb],
-    w_lvl: [L, C, 4, k, k], scale: [L, C, 4], all fp32. Gradients of the
-    parameters are fp32; the gradient of x has x's dtype.
+    x: [B, C, H, W] fp32 or bf16, w_base: [C, kb, kb], w_lvl:
+    [L, C, 4, k, k], scale: [L, C, 4], all fp32. Gradients of the
+    parameters are fp32; the gradient of x has x's dtype. A channels-last x
+    keeps its memory order (y and dx are channels last too); the library runs
+    that layout through its generic chain, the fused kernels are planar only.
     """
 
     @staticmethod
     def forward(ctx, x, w_base, w_lvl, scale):
         _check_device(x, w_base, w_lvl, scale)
-        x = x.contiguous()
+        x = x.contiguous(memory_format=_order(x))
         y = _b.wtconv_fwd(x, w_base, w_lvl, scale)
         ctx.save_for_backward(x, w_base, w_lvl, scale)
         return y
@@ -47,7 +56,7 @@ class WTConvFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         x, w_base, w_lvl, scale = ctx.saved_tensors
-        dy = dy.to(x.dtype).contiguous()
+        dy = dy.to(x.dtype).contiguous(memory_format=_order(x))
         dx = dwb = dwl = dsc = None
         if ctx.needs_input_grad[0]:
             dx = _b.wtconv_bwd_data(dy, w_base, w_lvl, scale)
