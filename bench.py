@@ -10,7 +10,8 @@ already resident in HBM. The default workload is the ConvNeXt stage-1 shape
 Prints one JSON line: images/s, the achieved HBM rate against the I/O-model
 minimum bytes, the roofline of the dominant kernel (measured with HIP events
 on the stream the kernels run on), the naive unfused chain timed in the same
-run, and the fp64 CPU oracle timed on a bounded sample on the host.
+run, torch's own depthwise convolution of the same shape as context, and the
+fp64 CPU oracle timed on a bounded sample on the host.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -91,6 +92,34 @@ def cpu_baseline(cfg, seconds: float):
     }
 
 
+def depthwise_context(torch, cfg, sets, steps: int):
+    """The layer WTConv stands in for: a k_base x k_base depthwise convolution
+    of the same activations, one step = forward + input gradient + weight
+    gradient through torch (MIOpen), with weights in the activations' dtype as
+    torch requires. Context only: a library's kernels, not this package's."""
+    F = torch.nn.functional
+    wdt = sets[0][0].dtype
+    w = torch.randn(cfg.C, 1, cfg.kb, cfg.kb, device=sets[0][0].device).to(wdt)
+    pad = cfg.kb // 2
+
+    def one(i):
+        x, dy = sets[i % len(sets)]
+        F.conv2d(x, w, padding=pad, groups=cfg.C)
+        torch.ops.aten.convolution_backward(dy, x, w, None, [1, 1], [pad, pad], [1, 1], False, [0, 0], cfg.C,
+                                            [True, True, False])
+
+    for i in range(2):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    return {"what": f"torch depthwise conv {cfg.kb}x{cfg.kb}, fwd + input grad + weight grad", "ms_per_step": round(ms, 4),
+            "images_per_s": round(cfg.B / (ms * 1e-3), 1), "steps": steps}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +129,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context line: torch's own depthwise convolution on the same shape")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the 256 MB MALL)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy one 1 GiB buffer (known HBM bytes) so that a counter "
@@ -215,6 +246,11 @@ def main() -> int:
                  "fused_speedup": round(nms / ms_per_step, 3)}
         del nws
 
+    context = None
+    if not args.no_context:
+        context = depthwise_context(torch, cfg, sets, max(5, args.steps // 5))
+        context["wtconv_over_depthwise"] = round(ms_per_step / context["ms_per_step"], 3)
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -251,6 +287,7 @@ def main() -> int:
                      "flops_per_launch": model.flops_per_call,
                      "unpacked_fma_ceiling_TFLOPs": iomodel.FP32_UNPACKED_FMA_TFLOPS},
         "naive_baseline": naive,
+        "context": context,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
