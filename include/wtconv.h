@@ -75,7 +75,7 @@ typedef enum {
 typedef enum {
     WTCONV_OK = 0,
     WTCONV_ERR_INVALID_ARG = 1,        /* null pointer, overlap, bad dtype or
-                                          layout, sizes < 1 */
+                                          layout, B < 0, C, H or W < 1 */
     WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* even or unsupported k, L out of
                                           range, or H*W above 2^30 */
     WTCONV_ERR_WORKSPACE = 3,          /* ws too small or misaligned */
@@ -89,7 +89,10 @@ typedef enum {
 } wtconv_op_t;
 
 typedef struct {
-    int32_t B, C, H, W;   /* activation shape, NCHW */
+    int32_t B, C, H, W;   /* activation shape, NCHW; B = 0 is an empty batch:
+                             the data passes write nothing (activation
+                             pointers may be NULL), the weight gradients
+                             are zero */
     int32_t levels;       /* L, 0..5 */
     int32_t k_base;       /* base kernel size: odd, 1..15 */
     int32_t k_level;      /* per-level kernel size: odd, 1..15 */

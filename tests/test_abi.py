@@ -50,7 +50,7 @@ def test_status_strings(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(B=0), 1), (dict(C=-1), 1), (dict(dtype=7), 1), (dict(layout=2), 1), (dict(layout=-1), 1),
+    (dict(B=-1), 1), (dict(C=0), 1), (dict(C=-1), 1), (dict(W=0), 1), (dict(dtype=7), 1), (dict(layout=2), 1), (dict(layout=-1), 1),
     (dict(levels=6), 2), (dict(levels=-1), 2), (dict(k_base=4), 2), (dict(k_level=17), 2), (dict(k_base=-1), 2),
     (dict(H=1 << 16, W=1 << 15), 2),  # a plane above 2^30 elements
 ])
@@ -122,3 +122,16 @@ def test_binding_reads_the_memory_order():
     assert layout_of(torch.zeros(1, 1, 8, 6).to(memory_format=torch.channels_last)) == 0
     with pytest.raises(ValueError):
         layout_of(x.transpose(2, 3))
+
+
+def test_empty_batch_is_a_no_op_for_the_data_passes(lib):
+    """B = 0: the data passes validate and return without launching (the
+    activation pointers may be NULL); they need no workspace. The weight
+    gradient of an empty batch (zeros) runs on the GPU and is tested there."""
+    d = _desc(B=0)
+    ok = ctypes.c_void_p(1 << 20)
+    assert lib.wtconv_workspace_size(ctypes.byref(d), 0) == 0
+    assert lib.wtconv_workspace_size(ctypes.byref(d), 2) > 0
+    for fn in (lib.wtconv_fwd, lib.wtconv_bwd_data, lib.wtconv_naive_fwd):
+        assert fn(ctypes.byref(d), None, ok, ok, ok, None, None, 0, None) == 0
+        assert fn(ctypes.byref(d), None, None, ok, ok, None, None, 0, None) == 1   # parameters still checked

@@ -248,6 +248,21 @@ def test_channels_last_matches_oracle(shape):
                 assert rel_err(to_f64(g), o) <= TOL["f32"]
 
 
+def test_empty_batch():
+    """B = 0: empty outputs from the data passes and zero weight gradients
+    (every output element overwritten)."""
+    _say("[parity] empty batch")
+    inp = make_inputs(1, 3, 56, 56, 3, 5, 5, dtype="bf16", seed=3)
+    x, dy, wb, wl, sc = to_device(inp)
+    x0, dy0 = x[:0], dy[:0]
+    assert wt.wtconv_fwd(x0, wb, wl, sc).shape == (0, 3, 56, 56)
+    assert wt.wtconv_bwd_data(dy0, wb, wl, sc).shape == (0, 3, 56, 56)
+    out = tuple(torch.full(s, float("nan"), device="cuda") for s in ((3, 5, 5), tuple(wl.shape), tuple(sc.shape)))
+    wt.wtconv_bwd_weight(x0, dy0, 5, wl, sc, out=out)
+    torch.cuda.synchronize()
+    assert all(bool((g == 0).all()) for g in out)
+
+
 def test_repeated_calls_with_changing_batch():
     """Two calls in a row, the second with a smaller batch: no state is kept
     between calls."""

@@ -29,7 +29,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 // Shape checks shared by every entry point.
 wtconv_status_t check_desc(const wtconv_desc_t* d) {
     if (!d) return WTCONV_ERR_INVALID_ARG;
-    if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1) return WTCONV_ERR_INVALID_ARG;
+    // B = 0 (an empty batch) is valid: nothing to write for the data passes,
+    // zero weight gradients
+    if (d->B < 0 || d->C < 1 || d->H < 1 || d->W < 1) return WTCONV_ERR_INVALID_ARG;
     if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_BF16) return WTCONV_ERR_INVALID_ARG;
     if (d->layout != WTCONV_NCHW && d->layout != WTCONV_NHWC) return WTCONV_ERR_INVALID_ARG;
     if (d->levels < 0 || d->levels > 5) return WTCONV_ERR_UNSUPPORTED_SHAPE;
@@ -57,6 +59,7 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
                                 size_t ws_bytes, void* stream, bool flip) {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
+    if (d->B == 0) return check_params(d, w_base, w_lvl, scale, true);   // empty batch: nothing to write
     if (!in || !out) return WTCONV_ERR_INVALID_ARG;
     if (!aligned16(in) || !aligned16(out)) return WTCONV_ERR_INVALID_ARG;
     if (overlap(in, act_bytes(d), out, act_bytes(d))) return WTCONV_ERR_INVALID_ARG;
@@ -89,9 +92,10 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
-// Whether the fused weight-gradient kernels have a plan for this shape.
+// Whether the fused weight-gradient kernels have a plan for this shape (an
+// empty batch takes the generic chain, which writes zero gradients).
 bool fused_bwdw_planned(const wtconv_desc_t* d) {
-    return d->layout == WTCONV_NCHW &&
+    return d->layout == WTCONV_NCHW && d->B > 0 &&
            wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level) !=
            (size_t)-1;
 }
@@ -105,6 +109,7 @@ size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
     switch (op) {
     case WTCONV_OP_FWD:
     case WTCONV_OP_BWD_DATA:
+        if (d->B == 0) return 0;
         if (d->layout == WTCONV_NCHW) {
             if (wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) return 0;
             if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))
@@ -138,7 +143,8 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const v
                                   void* stream) {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
-    if (!x || !dy || !dw_base) return WTCONV_ERR_INVALID_ARG;
+    if (d->B > 0 && (!x || !dy)) return WTCONV_ERR_INVALID_ARG;   // never read for an empty batch
+    if (!dw_base) return WTCONV_ERR_INVALID_ARG;
     if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(dy) || !aligned16(dw_base)) return WTCONV_ERR_INVALID_ARG;
     if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
@@ -172,6 +178,7 @@ static wtconv_status_t naive_data(const wtconv_desc_t* d, const void* in, const 
                                   size_t ws_bytes, void* stream, int op) {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
+    if (d->B == 0) return check_params(d, w_base, w_lvl, scale, true);   // empty batch: nothing to write
     if (!in || !out || !aligned16(in) || !aligned16(out)) return WTCONV_ERR_INVALID_ARG;
     if (overlap(in, act_bytes(d), out, act_bytes(d))) return WTCONV_ERR_INVALID_ARG;
     st = check_params(d, w_base, w_lvl, scale, true);
@@ -204,7 +211,7 @@ wtconv_status_t wtconv_naive_bwd_weight(const wtconv_desc_t* d, const void* x, c
                                         void* stream) {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
-    if (!x || !dy || !dw_base || !aligned16(x) || !aligned16(dy)) return WTCONV_ERR_INVALID_ARG;
+    if ((d->B > 0 && (!x || !dy)) || !dw_base || !aligned16(x) || !aligned16(dy)) return WTCONV_ERR_INVALID_ARG;
     if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
     st = check_params(d, nullptr, w_lvl, scale, false);
     if (st != WTCONV_OK) return st;
