@@ -263,6 +263,49 @@ def test_empty_batch():
     assert all(bool((g == 0).all()) for g in out)
 
 
+@pytest.mark.parametrize("shape", [(4, 3, 56, 56, 3, 5, 5), (2, 3, 64, 64, 4, 3, 3), (2, 3, 13, 11, 2, 5, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_graph_replay_matches_eager(shape):
+    """The three calls captured in one HIP graph (whole-plane, split and
+    generic-chain shapes): every replay, with other eager work and
+    synchronisation between replays, equals the eager results bit for bit
+    (the kernels are deterministic and the library records no memset)."""
+    _say(f"[parity] graph replay {shape}")
+    B, C, H, W, L, kb, k = shape
+    inp = make_inputs(*shape, dtype="bf16", seed=23)
+    x, dy, wb, wl, sc = to_device(inp)
+    ws = torch.empty(max(wt.wtconv_workspace_size(x, L, kb, k, op) for op in range(3)) + 256, dtype=torch.uint8,
+                     device="cuda")
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    gr = (torch.empty(C, kb, kb, device="cuda"), torch.empty(tuple(wl.shape), device="cuda"),
+          torch.empty(tuple(sc.shape), device="cuda"))
+
+    def step():
+        wt.wtconv_fwd(x, wb, wl, sc, y=y, ws=ws)
+        wt.wtconv_bwd_data(dy, wb, wl, sc, dx=dx, ws=ws)
+        wt.wtconv_bwd_weight(x, dy, kb, wl, sc, out=gr, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (y, dx, *gr)]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in (y, dx, *gr):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip((y, dx, *gr), eager):
+            assert torch.equal(t, e), f"replay {r}"
+        (x.float() * 2).sum().item()   # eager work between replays
+
+
 def test_repeated_calls_with_changing_batch():
     """Two calls in a row, the second with a smaller batch: no state is kept
     between calls."""
