@@ -10,8 +10,9 @@ already resident in HBM. The default workload is the ConvNeXt stage-1 shape
 Prints one JSON line: images/s, the achieved HBM rate against the I/O-model
 minimum bytes, the roofline of the dominant kernel (measured with HIP events
 on the stream the kernels run on), the naive unfused chain timed in the same
-run, torch's own depthwise convolution of the same shape as context, and the
-fp64 CPU oracle timed on a bounded sample on the host.
+run, torch's own depthwise convolution of the same shape as context, the
+device's measured FMA and copy rates, and the fp64 CPU oracle timed on a
+bounded sample on the host.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -120,6 +121,34 @@ def depthwise_context(torch, cfg, sets, steps: int):
             "images_per_s": round(cfg.B / (ms * 1e-3), 1), "steps": steps}
 
 
+def measure_peaks(torch, wt, reps: int = 5):
+    """The two ceilings on this device: unpacked fp32 FMA rate (probe kernel,
+    16 independent chains per lane) and plain copy rate (1 GiB to 1 GiB).
+    Best of `reps` timed launches each, HIP events on the current stream."""
+    dev = torch.device("cuda:0")
+
+    def best(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            work = fn()
+            b.record()
+            b.synchronize()
+            ts.append((a.elapsed_time(b) * 1e-3, work))
+        return min(ts)
+
+    blocks, iters = 256 * 32, 2048
+    out = torch.empty(blocks * 256, device=dev)
+    t, flops = best(lambda: wt.wtconv_peak_fma(out, blocks, iters))
+    src = torch.empty(1 << 28, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    tc, nbytes = best(lambda: wt.wtconv_peak_copy(src, dst))
+    del out, src, dst
+    return {"fma_f32_unpacked_TFLOPs": round(flops / t / 1e12, 2), "copy_TBs": round(nbytes / tc / 1e12, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +161,7 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="replay a HIP graph of each step instead of launching it from Python (measured "
                          "slower on this path: 0.19 vs 0.18 ms per stage-1 step)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the FMA-rate and copy-rate probes")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context line: torch's own depthwise convolution on the same shape")
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets (defeats the 256 MB MALL)")
@@ -277,6 +307,8 @@ def main() -> int:
         context = depthwise_context(torch, cfg, sets, max(5, args.steps // 5))
         context["wtconv_over_depthwise"] = round(ms_per_step / context["ms_per_step"], 3)
 
+    peaks = None if args.no_peaks else measure_peaks(torch, wt)
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -314,6 +346,7 @@ def main() -> int:
                      "unpacked_fma_ceiling_TFLOPs": iomodel.FP32_UNPACKED_FMA_TFLOPS},
         "naive_baseline": naive,
         "context": context,
+        "peaks_measured": peaks,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -170,6 +170,18 @@ const char *wtconv_status_string(wtconv_status_t status);
 /* Library version, e.g. "0.2.0". */
 const char *wtconv_version(void);
 
+/* Measurement probes (not operations of the layer). They measure on the
+   device the two ceilings the kernels above are compared with.
+   wtconv_peak_fma: `blocks` workgroups of 256 lanes; every lane runs 16
+   independent chains of `iters` unpacked fp32 FMAs and writes one float to
+   out[blocks * 256] (16-byte aligned): 2 * 16 * iters * 256 * blocks flops.
+   blocks and iters in 1..2^20, else WTCONV_ERR_INVALID_ARG.
+   wtconv_peak_copy: copies `bytes` (a multiple of 16) from src to dst, both
+   16-byte aligned and not overlapping: 2 * bytes of HBM traffic.
+   Both only enqueue on `stream`; time them with events. */
+wtconv_status_t wtconv_peak_fma(float *out, int32_t blocks, int32_t iters, void *stream);
+wtconv_status_t wtconv_peak_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -306,6 +306,23 @@ def test_graph_replay_matches_eager(shape):
         (x.float() * 2).sum().item()   # eager work between replays
 
 
+def test_measurement_probes():
+    """The copy probe copies exactly; the FMA probe writes finite values to
+    every lane's slot; bad arguments are refused before any launch."""
+    _say("[probes] copy and fma")
+    src = torch.randn(1 << 20, device="cuda")
+    dst = torch.full_like(src, float("nan"))
+    assert wt.wtconv_peak_copy(src, dst) == 2 * src.numel() * 4
+    out = torch.full((4 * 256,), float("nan"), device="cuda")
+    assert wt.wtconv_peak_fma(out, 4, 100) == 2 * 16 * 100 * 256 * 4
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst) and bool(torch.isfinite(out).all())
+    with pytest.raises(wt.WTConvError):
+        wt.wtconv_peak_fma(out, 0, 10)
+    with pytest.raises(wt.WTConvError):
+        wt.wtconv_peak_copy(src[1:5], dst[:4])   # 4-byte offset: misaligned
+
+
 def test_repeated_calls_with_changing_batch():
     """Two calls in a row, the second with a smaller batch: no state is kept
     between calls."""

@@ -63,6 +63,10 @@ def load_library() -> ctypes.CDLL:
                 fn = getattr(lib, name)
                 fn.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]
                 fn.restype = ctypes.c_int
+            lib.wtconv_peak_fma.argtypes = [_V, ctypes.c_int32, ctypes.c_int32, _V]
+            lib.wtconv_peak_fma.restype = ctypes.c_int
+            lib.wtconv_peak_copy.argtypes = [_V, _V, _SZ, _V]
+            lib.wtconv_peak_copy.restype = ctypes.c_int
             lib.wtconv_status_string.argtypes = [ctypes.c_int]
             lib.wtconv_status_string.restype = ctypes.c_char_p
             lib.wtconv_version.restype = ctypes.c_char_p
@@ -203,3 +207,18 @@ def wtconv_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stream=Non
 
 def wtconv_naive_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stream=None):
     return _bwd_weight("wtconv_naive_bwd_weight", True, x, dy, k_base, w_lvl, scale, out, ws, stream)
+
+
+def wtconv_peak_fma(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """Enqueue the FMA-rate probe; returns the flops it performs."""
+    _check(load_library().wtconv_peak_fma(_ptr(out), int(blocks), int(iters), _stream(stream)))
+    return 2 * 16 * int(iters) * 256 * int(blocks)
+
+
+def wtconv_peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
+    """Enqueue the copy probe over src's bytes; returns the HBM bytes moved."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(load_library().wtconv_peak_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
+    return 2 * n

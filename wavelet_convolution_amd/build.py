@@ -18,7 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwtconv.so")
-SOURCES = ["wtconv_fused.hip", "wtconv_tiled.hip", "wtconv_bwdw.hip", "wtconv_naive.hip", "wtconv_api.hip"]
+SOURCES = ["wtconv_fused.hip", "wtconv_tiled.hip", "wtconv_bwdw.hip", "wtconv_naive.hip", "wtconv_api.hip",
+           "wtconv_peaks.hip"]
 ARCH = os.environ.get("WTCONV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
