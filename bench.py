@@ -268,12 +268,13 @@ def main() -> int:
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    dur = {"fwd": 0.0, "bwd_data": 0.0, "bwd_weight": 0.0}
+    per = {"fwd": [], "bwd_data": [], "bwd_weight": []}
     for e in evs:
-        dur["fwd"] += e[0].elapsed_time(e[1])
-        dur["bwd_data"] += e[1].elapsed_time(e[2])
-        dur["bwd_weight"] += e[2].elapsed_time(e[3])
-    dur = {k: v / args.steps for k, v in dur.items()}   # ms per launch
+        per["fwd"].append(e[0].elapsed_time(e[1]))
+        per["bwd_data"].append(e[1].elapsed_time(e[2]))
+        per["bwd_weight"].append(e[2].elapsed_time(e[3]))
+    dur = {k: sum(v) / len(v) for k, v in per.items()}   # mean ms per launch (the roofline's figure)
+    med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
     dominant = max(dur, key=dur.get)
     achieved = model.flops_per_call / (dur[dominant] * 1e-3) / 1e12
     src_hash = kernel_source_hash()
@@ -338,6 +339,7 @@ def main() -> int:
         "hbm": {"min_bytes_per_step": model.step_bytes, "achieved_TBs": round(hbm_tbs, 4),
                 "frac_of_8TBs": round(hbm_tbs / iomodel.HBM_PEAK_TBS, 4)},
         "kernel_ms": {k: round(v, 5) for k, v in dur.items()},
+        "kernel_ms_median": {k: round(v, 5) for k, v in med.items()},
         "roofline": {"bound": "alu", "kernel": dominant, "achieved": round(achieved, 3),
                      "peak": iomodel.FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / iomodel.FP32_VECTOR_PEAK_TFLOPS, 4),
