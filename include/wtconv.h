@@ -109,12 +109,14 @@ size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
    Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
    that fit one workgroup's LDS; ws may then be NULL).
    Shapes without a fused kernel (any other H, W >= 1, L in 0..5, odd k up
-   to 15; e.g. L = 0, the plain depthwise convolution), and every shape in
-   the channels-last layout, run
-   the generic one-kernel-per-step chain of the naive entry points below:
-   the same results and semantics, with the intermediates in the workspace,
-   which wtconv_workspace_size then reports. The same holds for
-   wtconv_bwd_data and wtconv_bwd_weight. */
+   to 15; e.g. L = 0, the plain depthwise convolution) run the generic
+   one-kernel-per-step chain of the naive entry points below: the same
+   results and semantics, with the intermediates in the workspace, which
+   wtconv_workspace_size then reports. A channels-last call of a planned
+   shape converts its activations to planar copies in the workspace (after
+   the kernels' own part), runs the fused kernels on them and converts the
+   result back: bit for bit the planar results, two extra passes over the
+   activations. The same holds for wtconv_bwd_data and wtconv_bwd_weight. */
 wtconv_status_t wtconv_fwd(const wtconv_desc_t *desc, const void *x,
                            const float *w_base, const float *w_lvl,
                            const float *scale, void *y, void *ws,

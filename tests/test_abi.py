@@ -101,14 +101,23 @@ def test_bwd_weight_workspace_checked(lib):
                                  need, None) == 3
 
 
-def test_channels_last_takes_the_generic_chain(lib):
-    """The fused kernels are planar; a channels-last descriptor of a planned
-    plane is served by the generic chain, so it needs that chain's workspace."""
+def test_channels_last_workspace(lib):
+    """A channels-last call of a planned shape runs the planar kernels on
+    planar copies of its activations, which live in the workspace after the
+    kernels' own part; a shape without a plan takes the generic chain."""
+    def a256(n):
+        return (n + 255) // 256 * 256
+
     planar, nhwc = _desc(layout=0), _desc(layout=1)
+    act = 2 * 4 * 56 * 56 * 2   # B C H W, bf16
     assert lib.wtconv_workspace_size(ctypes.byref(planar), 0) == 0
     for op in (0, 1, 2):
-        assert lib.wtconv_workspace_size(ctypes.byref(nhwc), op) == lib.wtconv_naive_workspace_size(
-            ctypes.byref(nhwc), op) > 0
+        own = lib.wtconv_workspace_size(ctypes.byref(planar), op)
+        assert lib.wtconv_workspace_size(ctypes.byref(nhwc), op) == a256(own) + 2 * a256(act)
+    odd = _desc(H=13, W=11, layout=1)
+    for op in (0, 1, 2):
+        assert lib.wtconv_workspace_size(ctypes.byref(odd), op) == lib.wtconv_naive_workspace_size(
+            ctypes.byref(odd), op) > 0
 
 
 def test_binding_reads_the_memory_order():

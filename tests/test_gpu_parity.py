@@ -224,11 +224,15 @@ def test_odd_planes_match_oracle(shape):
     _check_all_three(*shape, seed=17)
 
 
-@pytest.mark.parametrize("shape", [(2, 3, 56, 56, 3, 5, 5), (1, 4, 13, 11, 2, 3, 5), (2, 2, 28, 28, 0, 7, 3)],
+@pytest.mark.parametrize("shape", [(2, 3, 56, 56, 3, 5, 5), (2, 3, 64, 64, 4, 3, 3), (1, 2, 256, 256, 4, 7, 5),
+                                   (3, 70, 14, 14, 1, 5, 5), (1, 4, 13, 11, 2, 3, 5), (2, 2, 28, 28, 0, 7, 3)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_channels_last_matches_oracle(shape):
-    """Channels-last activations (the generic chain) give the oracle's
-    results, and y and dx come back channels last."""
+    """Channels-last activations give the oracle's results, and y and dx come
+    back channels last. Planned shapes (whole-plane, split, large-plane
+    tiles; 70 channels leave a partial 64-channel tile) run the planar
+    kernels on converted copies and must equal the planar call bit for bit;
+    the others run the generic chain."""
     _say(f"[parity] channels last {shape}")
     cl = torch.channels_last
     for dtype in ("f32", "bf16"):
@@ -246,6 +250,13 @@ def test_channels_last_matches_oracle(shape):
         for g, o in ((dwb, odwb), (dwl, odwl), (dsc, odsc)):
             if g.numel():
                 assert rel_err(to_f64(g), o) <= TOL["f32"]
+        if shape[4] > 0 and shape[2] % (1 << shape[4]) == 0:
+            xp, dyp = x.contiguous(), dy.contiguous()
+            planar = (wt.wtconv_fwd(xp, wb, wl, sc), wt.wtconv_bwd_data(dyp, wb, wl, sc),
+                      *wt.wtconv_bwd_weight(xp, dyp, shape[5], wl, sc))
+            torch.cuda.synchronize()
+            for a, b in zip((y, dx, dwb, dwl, dsc), planar):
+                assert torch.equal(a.contiguous(), b)
 
 
 def test_empty_batch():

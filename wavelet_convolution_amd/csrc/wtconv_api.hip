@@ -9,6 +9,7 @@
 #include "../../include/wtconv.h"
 #include "wtconv_plans.h"
 #include "wtconv_bwdw.h"
+#include "wtconv_layout.h"
 #include "wtconv_naive.h"
 #include "wtconv_tiled.h"
 
@@ -54,6 +55,58 @@ wtconv_status_t check_params(const wtconv_desc_t* d, const float* w_base, const 
     return WTCONV_OK;
 }
 
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// How a call is served. Planned shapes run the fused kernels; a channels-last
+// call of a planned shape runs them on planar copies of its activations kept
+// in the workspace (after the kernels' own part); everything else runs the
+// generic chain, which reads either layout directly.
+struct Route {
+    const wtc::PlaneEntry* pe = nullptr;   // whole-plane data kernels
+    const wtc::SplitEntry* se = nullptr;   // coarse + fine data kernels
+    bool bw = false;                       // fused weight-gradient kernels
+    bool copies = false;                   // channels last through planar copies
+    size_t own = 0;                        // the kernels' own workspace bytes
+    size_t need = 0;                       // total workspace bytes
+};
+
+Route route(const wtconv_desc_t* d, int op) {
+    Route r;
+    const bool nhwc = d->layout == WTCONV_NHWC;
+    const bool convertible = !nhwc || wtc::transpose_fits(d->B, d->C, d->H, d->W);
+    if (d->B > 0 && convertible) {
+        if (op == WTCONV_OP_BWD_WEIGHT) {
+            const size_t b = wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
+            if (b != (size_t)-1) {
+                r.bw = true;
+                r.own = b;
+            }
+        } else if ((r.pe = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level))) {
+            r.own = 0;
+        } else if ((r.se = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))) {
+            r.own = r.se->ws_bytes(d->B, d->C);
+        }
+    }
+    if (r.pe || r.se || r.bw) {
+        r.copies = nhwc;
+        r.need = r.copies ? align256(r.own) + 2 * align256(act_bytes(d)) : r.own;
+    } else if (d->B == 0 && op != WTCONV_OP_BWD_WEIGHT) {
+        r.need = 0;   // nothing to compute
+    } else {
+        r.need = wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, op);
+    }
+    return r;
+}
+
+bool ws_ok(const Route& r, const void* ws, size_t ws_bytes) {
+    return r.need == 0 || (ws && ws_bytes >= r.need && aligned256(ws));
+}
+
+// The two planar copies of a channels-last call, after the kernels' workspace.
+void* copy_slot(const Route& r, const wtconv_desc_t* d, void* ws, int i) {
+    return (char*)ws + align256(r.own) + (size_t)i * align256(act_bytes(d));
+}
+
 wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const float* w_base,
                                 const float* w_lvl, const float* scale, void* out, void* ws,
                                 size_t ws_bytes, void* stream, bool flip) {
@@ -65,39 +118,34 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     if (overlap(in, act_bytes(d), out, act_bytes(d))) return WTCONV_ERR_INVALID_ARG;
     st = check_params(d, w_base, w_lvl, scale, true);
     if (st != WTCONV_OK) return st;
+    const int op = flip ? WTCONV_OP_BWD_DATA : WTCONV_OP_FWD;
+    const Route r = route(d, op);
+    if (!ws_ok(r, ws, ws_bytes)) return WTCONV_ERR_WORKSPACE;
     const int dt = d->dtype == WTCONV_BF16 ? 1 : 0;
-    const bool nchw = d->layout == WTCONV_NCHW;
-    hipError_t err;
-    const wtc::PlaneEntry* pe = nchw ? wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level) : nullptr;
-    const wtc::SplitEntry* se = nchw ? wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level) : nullptr;
-    if (const wtc::PlaneEntry* e = pe) {
-        // the whole plane fits one workgroup: one kernel, no workspace
-        err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, d->B, d->C, (hipStream_t)stream);
-    } else if (const wtc::SplitEntry* e = se) {
-        // coarse pass on the LL band at level L0, then the fine tiles
-        const size_t need = e->ws_bytes(d->B, d->C);
-        if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
-        err = e->fn[dt][flip ? 1 : 0](in, w_base, w_lvl, scale, out, (float*)ws, d->B, d->C, (hipStream_t)stream);
-    } else {
-        // no fused kernel for this shape or layout: the generic
-        // one-kernel-per-step chain (same results, intermediates in device memory)
-        const int op = flip ? WTCONV_OP_BWD_DATA : WTCONV_OP_FWD;
-        const size_t need = wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base,
-                                                       d->k_level, op);
-        if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
-        err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
-                                     d->dtype == WTCONV_BF16, flip, !nchw, in, w_base, w_lvl, scale, out, ws,
-                                     (hipStream_t)stream);
+    const hipStream_t s = (hipStream_t)stream;
+    if (!r.pe && !r.se) {
+        // no fused kernel for this shape: the generic one-kernel-per-step
+        // chain (same results, intermediates in device memory)
+        const hipError_t err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                                      dt == 1, flip, d->layout == WTCONV_NHWC, in, w_base, w_lvl,
+                                                      scale, out, ws, s);
+        return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
     }
+    const void* kin = in;
+    void* kout = out;
+    if (r.copies) {
+        kin = copy_slot(r, d, ws, 0);
+        kout = copy_slot(r, d, ws, 1);
+        if (wtc::nhwc_to_nchw(in, (void*)kin, d->B, d->C, d->H, d->W, dt == 1, s) != hipSuccess)
+            return WTCONV_ERR_LAUNCH;
+    }
+    hipError_t err;
+    if (r.pe)   // the whole plane fits one workgroup: one kernel, no workspace of its own
+        err = r.pe->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, d->B, d->C, s);
+    else        // coarse pass on the LL band at level L0, then the fine tiles
+        err = r.se->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, (float*)ws, d->B, d->C, s);
+    if (err == hipSuccess && r.copies) err = wtc::nchw_to_nhwc(kout, out, d->B, d->C, d->H, d->W, dt == 1, s);
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
-}
-
-// Whether the fused weight-gradient kernels have a plan for this shape (an
-// empty batch takes the generic chain, which writes zero gradients).
-bool fused_bwdw_planned(const wtconv_desc_t* d) {
-    return d->layout == WTCONV_NCHW && d->B > 0 &&
-           wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level) !=
-           (size_t)-1;
 }
 
 }  // namespace
@@ -106,23 +154,8 @@ extern "C" {
 
 size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
     if (check_desc(d) != WTCONV_OK) return (size_t)-1;
-    switch (op) {
-    case WTCONV_OP_FWD:
-    case WTCONV_OP_BWD_DATA:
-        if (d->B == 0) return 0;
-        if (d->layout == WTCONV_NCHW) {
-            if (wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level)) return 0;
-            if (const wtc::SplitEntry* e = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))
-                return e->ws_bytes(d->B, d->C);
-        }
-        return wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, op);
-    case WTCONV_OP_BWD_WEIGHT:
-        if (fused_bwdw_planned(d))
-            return wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
-        return wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, op);
-    default:
-        return (size_t)-1;
-    }
+    if (op != WTCONV_OP_FWD && op != WTCONV_OP_BWD_DATA && op != WTCONV_OP_BWD_WEIGHT) return (size_t)-1;
+    return route(d, op).need;
 }
 
 wtconv_status_t wtconv_fwd(const wtconv_desc_t* d, const void* x, const float* w_base,
@@ -150,17 +183,23 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const v
     if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
     st = check_params(d, nullptr, w_lvl, scale, false);
     if (st != WTCONV_OK) return st;
-    const bool fused = fused_bwdw_planned(d);
-    const size_t need =
-        fused ? wtc::bwdw_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level)
-              : wtc::naive_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
-                                           WTCONV_OP_BWD_WEIGHT);
-    if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+    const Route r = route(d, WTCONV_OP_BWD_WEIGHT);
+    if (!ws_ok(r, ws, ws_bytes)) return WTCONV_ERR_WORKSPACE;
+    const bool bf16 = d->dtype == WTCONV_BF16;
+    const hipStream_t s = (hipStream_t)stream;
     hipError_t err;
-    if (fused)
-        err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, d->dtype == WTCONV_BF16, x,
-                               dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
-    else   // no fused plan for this shape: the generic chain
+    if (r.bw) {
+        const void *kx = x, *kdy = dy;
+        if (r.copies) {   // planar copies of x and dy, after the kernels' partial sums
+            kx = copy_slot(r, d, ws, 0);
+            kdy = copy_slot(r, d, ws, 1);
+            err = wtc::nhwc_to_nchw(x, (void*)kx, d->B, d->C, d->H, d->W, bf16, s);
+            if (err == hipSuccess) err = wtc::nhwc_to_nchw(dy, (void*)kdy, d->B, d->C, d->H, d->W, bf16, s);
+            if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
+        }
+        err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, bf16, kx, kdy, w_lvl,
+                               scale, dw_base, dw_lvl, dscale, ws, s);
+    } else   // no fused plan for this shape (or an empty batch): the generic chain
         err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
                                      d->dtype == WTCONV_BF16, d->layout == WTCONV_NHWC, x, dy, w_lvl, scale,
                                      dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);

@@ -42,7 +42,7 @@ class WTConvFunction(torch.autograd.Function):
     [L, C, 4, k, k], scale: [L, C, 4], all fp32. Gradients of the
     parameters are fp32; the gradient of x has x's dtype. A channels-last x
     keeps its memory order (y and dx are channels last too); the library runs
-    that layout through its generic chain, the fused kernels are planar only.
+    the planar kernels on converted copies of it.
     """
 
     @staticmethod
