@@ -259,6 +259,34 @@ def test_channels_last_matches_oracle(shape):
                 assert torch.equal(a.contiguous(), b)
 
 
+def test_hand_worked_odd_plane_on_gpu():
+    """The hand-worked 3x3 example (tests/golden) through the C-ABI: values
+    fixed by hand, not by the oracle."""
+    import json
+    import os
+    _say("[parity] hand-worked 3x3 odd plane")
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_3x3_odd_l1.json")) as f:
+        g = json.load(f)
+    dev = "cuda"
+    x = torch.tensor(g["x"], dtype=torch.float32, device=dev)[None, None].contiguous()
+    wb = torch.ones(1, 1, 1, device=dev)
+    wl = torch.ones(1, 1, 4, 1, 1, device=dev)
+    for key in ("case_ll_only", "case_band3"):
+        sc = torch.tensor(g[key]["scale"], dtype=torch.float32, device=dev)[None, None].contiguous()
+        y = wt.wtconv_fwd(x, wb, wl, sc)
+        torch.cuda.synchronize()
+        assert rel_err(to_f64(y[0, 0]), np.array(g[key]["y"])) <= 1e-6, key
+    imp = g["case_band3"]["dy_impulse_2_2"]
+    dy = torch.tensor(imp["dy"], dtype=torch.float32, device=dev)[None, None].contiguous()
+    dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+    dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, 1, wl, sc)
+    torch.cuda.synchronize()
+    assert rel_err(to_f64(dx[0, 0]), np.array(imp["dx"])) <= 1e-6
+    assert abs(float(dwb.flatten()[0]) - imp["dw_base"]) <= 1e-5
+    assert rel_err(to_f64(dwl[0, 0, :, 0, 0]), np.array(imp["dw_lvl"])) <= 1e-6
+    assert rel_err(to_f64(dsc[0, 0]), np.array(imp["dscale"])) <= 1e-6
+
+
 def test_empty_batch():
     """B = 0: empty outputs from the data passes and zero weight gradients
     (every output element overwritten)."""

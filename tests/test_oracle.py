@@ -103,6 +103,32 @@ def test_golden_hand_worked_backward():
     np.testing.assert_allclose(dwb[0], np.array(case["dw_base"]), atol=1e-15)
 
 
+def test_golden_hand_worked_odd_plane():
+    """A 3x3 plane at one level (hand-worked, tests/golden): the zero row and
+    column added before the analysis and the crop after the synthesis,
+    forward, backward data and weight gradients."""
+    with open(os.path.join(GOLDEN, "hand_worked_3x3_odd_l1.json")) as f:
+        g = json.load(f)
+    x = np.array(g["x"], float)[None, None]
+    wb = np.ones((1, 1, 1))
+    wl = np.ones((1, 1, 4, 1, 1))
+    for key in ("case_ll_only", "case_band3"):
+        case = g[key]
+        sc = np.array(case["scale"], float)[None, None]
+        np.testing.assert_allclose(oracle.fwd(x, wb, wl, sc)[0, 0], np.array(case["y"]), atol=1e-15)
+        np.testing.assert_allclose(oracle.fwd_closed(x, wb, wl, sc)[0, 0], np.array(case["y"]), atol=1e-15)
+    case = g["case_band3"]
+    sc = np.array(case["scale"], float)[None, None]
+    imp = case["dy_impulse_2_2"]
+    dy = np.array(imp["dy"], float)[None, None]
+    np.testing.assert_allclose(oracle.bwd_data(dy, wb, wl, sc)[0, 0], np.array(imp["dx"]), atol=1e-15)
+    for fn in (oracle.bwd_weight, oracle.bwd_weight_gcorr):
+        dwb, dwl, dsc = fn(x, dy, wb, wl, sc)
+        assert abs(dwb[0, 0, 0] - imp["dw_base"]) < 1e-15
+        np.testing.assert_allclose(dwl[0, 0, :, 0, 0], np.array(imp["dw_lvl"]), atol=1e-15)
+        np.testing.assert_allclose(dsc[0, 0], np.array(imp["dscale"]), atol=1e-15)
+
+
 # ------------------------------------------------------- linearity (P2)
 
 def test_linearity_in_each_argument():
