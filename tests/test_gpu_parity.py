@@ -287,6 +287,45 @@ def test_hand_worked_odd_plane_on_gpu():
     assert rel_err(to_f64(dsc[0, 0]), np.array(imp["dscale"])) <= 1e-6
 
 
+def _random_cases(n, seed=2024):
+    """Seeded small shapes over every route: planned and unplanned planes,
+    odd band grids, L 0..5, odd kernels 1..9, both layouts."""
+    rng = np.random.default_rng(seed)
+    planned = [(56, 56, 3, 5, 5), (28, 28, 2, 5, 5), (14, 14, 1, 5, 5), (32, 32, 2, 5, 5), (64, 64, 4, 3, 3),
+               (128, 128, 2, 5, 5), (24, 40, 3, 3, 3)]
+    out = []
+    for i in range(n):
+        B, C = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        if i % 3 == 0:
+            H, W, L, kb, k = planned[int(rng.integers(len(planned)))]
+        else:
+            H, W = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+            L, kb, k = int(rng.integers(0, 6)), int(rng.choice([1, 3, 5, 7, 9])), int(rng.choice([1, 3, 5, 7, 9]))
+        out.append((B, C, H, W, L, kb, k, bool(rng.integers(2)), ("f32", "bf16")[int(rng.integers(2))]))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(40), ids=lambda c: "x".join(map(str, c)))
+def test_random_shapes_match_oracle(case):
+    """Forty seeded random shapes through the three entry points against the
+    oracle (layouts, odd grids, every level count and kernel size)."""
+    B, C, H, W, L, kb, k, cl, dtype = case
+    _say(f"[parity] random {case}")
+    inp = make_inputs(B, C, H, W, L, kb, k, dtype=dtype, seed=31)
+    x, dy, wb, wl, sc = to_device(inp)
+    if cl:
+        x, dy = x.contiguous(memory_format=torch.channels_last), dy.contiguous(memory_format=torch.channels_last)
+    y = wt.wtconv_fwd(x, wb, wl, sc)
+    dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+    dwb, dwl, dsc = wt.wtconv_bwd_weight(x, dy, kb, wl, sc)
+    torch.cuda.synchronize()
+    oy, odx, (odwb, odwl, odsc) = _oracle_all(inp)
+    assert rel_err(to_f64(y), oy) <= TOL[dtype] and rel_err(to_f64(dx), odx) <= TOL[dtype]
+    for g, o in ((dwb, odwb), (dwl, odwl), (dsc, odsc)):
+        if g.numel():
+            assert rel_err(to_f64(g), o) <= TOL["f32"]
+
+
 def test_empty_batch():
     """B = 0: empty outputs from the data passes and zero weight gradients
     (every output element overwritten)."""
