@@ -81,10 +81,12 @@ Route route(const wtconv_desc_t* d, int op) {
                 r.bw = true;
                 r.own = b;
             }
-        } else if ((r.pe = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level))) {
-            r.own = 0;
-        } else if ((r.se = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level))) {
-            r.own = r.se->ws_bytes(d->B, d->C);
+        } else {
+            r.pe = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level);
+            // the whole-plane kernels address a workgroup's planes with 32-bit offsets
+            if (r.pe && (uint64_t)r.pe->npw * d->C * d->H * d->W >= (1ull << 32)) r.pe = nullptr;
+            if (!r.pe && (r.se = wtc::find_split_entry(d->H, d->W, d->levels, d->k_base, d->k_level)))
+                r.own = r.se->ws_bytes(d->B, d->C);
         }
     }
     if (r.pe || r.se || r.bw) {

@@ -27,13 +27,13 @@ static hipError_t launch_col(const void* in, const float* wb, const float* wl, c
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \
      {{launch_col<PLAN, float, false>, launch_col<PLAN, float, true>},                       \
       {launch_col<PLAN, bf16_t, false>, launch_col<PLAN, bf16_t, true>}},                    \
-     PLAN::TOTAL_FLOATS * 4, PLAN::NT}
+     PLAN::TOTAL_FLOATS * 4, PLAN::NT, PLAN::NPW}
 
 #define WTC_PLANE_ENTRY(PLAN)                                                                 \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K,                                           \
      {{launch_plane<PLAN, float, false>, launch_plane<PLAN, float, true>},                   \
       {launch_plane<PLAN, bf16_t, false>, launch_plane<PLAN, bf16_t, true>}},                \
-     (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT}
+     (PLAN::LDS_FLOATS + PLAN::WFLOATS) * 4, PLAN::NT, 1}
 
 static const PlaneEntry kPlaneEntries[] = {
 #if WTC_COLS

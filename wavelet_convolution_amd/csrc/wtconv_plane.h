@@ -289,7 +289,14 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     // this workgroup: channel c of images g*NPW .. g*NPW + NPW-1 (those < B)
     const int c = blockIdx.x % C, g = blockIdx.x / C;
     auto live = [&](int p) { return NPW == 1 || g * NPW + p < B; };
-    auto plane_off = [&](int p) { return ((size_t)(g * NPW + p) * C + c) * H * W; };
+    // The workgroup's first plane, a uniform base; plane p lies p*C*H*W
+    // elements further on. The host routes shapes whose NPW*C*H*W reaches
+    // 2^32 elsewhere, so per-lane offsets stay 32-bit and the loads and
+    // stores take the scalar-base, vector-offset form.
+    const size_t g0 = ((size_t)g * NPW * C + c) * H * W;
+    const T* __restrict__ in_g = in + g0;
+    T* __restrict__ out_g = out + g0;
+    auto plane_rel = [&](int p) -> uint32_t { return NPW == 1 ? 0u : (uint32_t)p * ((uint32_t)C * (H * W)); };
     // plane p of an item index over all NPW planes, and the index within it
     auto split = [&](int item, int n, int& r) {
         const int p = NPW == 1 ? 0 : item / n;
@@ -334,7 +341,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
                 (NQA % NT == 0 || qa < NQA) && live(p) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1;
             // every lane loads (border items the plane's first words) and
             // then selects zeros: no branch, so the registers stay registers
-            const T* s0 = in + plane_off(inside ? p : 0) + (inside ? (2 * i) * W + 2 * j0 : 0);
+            const T* s0 = in_g + (inside ? plane_rel(p) + (uint32_t)((2 * i) * W + 2 * j0) : 0u);
             load_raw<T, VA>(s0, r0[k]);
             load_raw<T, VA>(s0 + (inside ? W : 0), r1[k]);
 #pragma unroll
@@ -522,7 +529,8 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         const int p = split(item, NIB, r);
         const int rb = r / LPB, w = r - rb * LPB, h0 = rb * RB;
         if (!(LPB == W || w < W) || !live(p)) continue;
-        T* __restrict__ dst = out + plane_off(p);
+        // this strip's column in its plane: rows at constant offsets from it
+        T* __restrict__ dst = out_g + (plane_rel(p) + (uint32_t)(h0 * W + w));
         float y[RB];
 #pragma unroll
         for (int o = 0; o < RB; ++o) y[o] = yb[it][o];
@@ -587,14 +595,14 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
 #pragma unroll
             for (int o = 0; o < RB; o += 2) {
                 const uint32_t pr = narrow_bf16x2(y[o], y[o + 1]);
-                dst[(size_t)(h0 + o) * W + w] = (bf16_t)(pr & 0xffffu);
-                dst[(size_t)(h0 + o + 1) * W + w] = (bf16_t)(pr >> 16);
+                dst[o * W] = (bf16_t)(pr & 0xffffu);
+                dst[(o + 1) * W] = (bf16_t)(pr >> 16);
             }
         } else {
 #pragma unroll
             for (int o = 0; o < RB; ++o) {
-                if constexpr (sizeof(T) == 2) dst[(size_t)(h0 + o) * W + w] = narrow_bf16(y[o]);
-                else dst[(size_t)(h0 + o) * W + w] = y[o];
+                if constexpr (sizeof(T) == 2) dst[o * W] = narrow_bf16(y[o]);
+                else dst[o * W] = y[o];
             }
         }
     }

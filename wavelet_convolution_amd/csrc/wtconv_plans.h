@@ -101,6 +101,7 @@ struct PlaneEntry {
     plane_launch_fn fn[2][2];  // [dtype: 0 fp32, 1 bf16][flip: 0 fwd, 1 bwd_data]
     int lds_bytes;
     int nt;
+    int npw;   // images per workgroup: the kernel needs npw*C*H*W < 2^32
 };
 
 const PlaneEntry* find_plane_entry(int H, int W, int L, int KB, int K);
