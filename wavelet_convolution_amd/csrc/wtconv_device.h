@@ -17,6 +17,9 @@ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 // column of different rows fall into different banks.
 constexpr int odd_stride(int w) { return (w % 2 == 0) ? w + 1 : w; }
 
+// a / b for a >= 0 and b > 0, in unsigned arithmetic: no sign fix-up
+__device__ __forceinline__ int udiv(int a, int b) { return (int)((unsigned)a / (unsigned)b); }
+
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 

@@ -299,7 +299,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     auto plane_rel = [&](int p) -> uint32_t { return NPW == 1 ? 0u : (uint32_t)p * ((uint32_t)C * (H * W)); };
     // plane p of an item index over all NPW planes, and the index within it
     auto split = [&](int item, int n, int& r) {
-        const int p = NPW == 1 ? 0 : item / n;
+        const int p = NPW == 1 ? 0 : udiv(item, n);
         r = item - p * n;
         return p;
     };
@@ -336,7 +336,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             const int qa = tid + k * NT;
             int q;
             const int p = split(qa < NQA ? qa : 0, NQ, q);
-            const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
+            const int ii = udiv(q, IPR), uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
             const bool inside =
                 (NQA % NT == 0 || qa < NQA) && live(p) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1;
             // every lane loads (border items the plane's first words) and
@@ -358,7 +358,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             const int p = split(qa, NQ, q);
             float* const A = Ap(p);
             float* const Bq = A + P::ASIZE;
-            const int ii = q / IPR, uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
+            const int ii = udiv(q, IPR), uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
             float f0[VA], f1[VA];
             widen_raw<T, VA>(r0[k], f0);
             widen_raw<T, VA>(r1[k], f1);
@@ -386,7 +386,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         if ((NPW * NIB) % NT == 0 || item < NPW * NIB) {
             int r;
             const int p = split(item, NIB, r);
-            const int rb = r / LPB, w = r - rb * LPB;
+            const int rb = udiv(r, LPB), w = r - rb * LPB;
             const float* X0 = Ap(p) + XO - PB;   // origin of the bordered x plane
             if (LPB == W || w < W) conv_col<KB, RB, SX>(X0 + (rb * RB) * SX + w, WB, yb[it]);
         }
@@ -406,7 +406,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             const int p = split(qa, GN, q);
             float* const Ul = Ap(p) + UO;
             const float* LLp = (l == 2) ? (Ap(p) + P::ASIZE + PK * Sp + PK) : (Ap(p) + UP + PK * Sp + PK);
-            const int ii = q / GW, jj = q - ii * GW, i = ii - PK, j = jj - PK;
+            const int ii = udiv(q, GW), jj = q - ii * GW, i = ii - PK, j = jj - PK;
             float b[4] = {0.f, 0.f, 0.f, 0.f};
             if (i >= 0 && i < hl && j >= 0 && j < wl) {
                 const float* x2 = LLp + 2 * i * Sp + 2 * j;
@@ -431,8 +431,8 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             if ((NPW * NIl) % NT == 0 || ia < NPW * NIl) {
                 int item;
                 float* const Ul = ubase(lc, split(ia, NIl, item));
-                const int s = item / (NS * LP), rem = item - s * (NS * LP);
-                const int rs = rem / LP, j = rem - rs * LP;
+                const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
+                const int rs = udiv(rem, LP), j = rem - rs * LP;
                 if (LP == wl || j < wl)
                     conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z[it]);
             }
@@ -448,8 +448,8 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             if ((NPW * NIl) % NT == 0 || ia < NPW * NIl) {
                 int item;
                 float* const Ul = ubase(lc, split(ia, NIl, item));
-                const int s = item / (NS * LP), rem = item - s * (NS * LP);
-                const int rs = rem / LP, j = rem - rs * LP;
+                const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
+                const int rs = udiv(rem, LP), j = rem - rs * LP;
                 if (!(LP == wl || j < wl)) continue;
 #pragma unroll
                 for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = z[it][o];
@@ -465,8 +465,8 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         if (ia >= 0 && ia < NPW * NIl) {
             int item;
             float* const Ul = ubase(lc, split(ia, NIl, item));
-            const int s = item / (NS * LP), rem = item - s * (NS * LP);
-            const int rs = rem / LP, j = rem - rs * LP;
+            const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
+            const int rs = udiv(rem, LP), j = rem - rs * LP;
             if (LP == wl || j < wl) {
                 float z[R];
                 conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z);
@@ -483,8 +483,8 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         if (ia >= 0 && ia < NPW * NIl) {
             int item;
             float* const Ul = ubase(lc, split(ia, NIl, item));
-            const int s = item / (NS * LP), rem = item - s * (NS * LP);
-            const int rs = rem / LP, j = rem - rs * LP;
+            const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
+            const int rs = udiv(rem, LP), j = rem - rs * LP;
             if (LP == wl || j < wl) {
 #pragma unroll
                 for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = zd[o];
@@ -527,7 +527,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         if (!((NPW * NIB) % NT == 0 || item < NPW * NIB)) continue;
         int r;
         const int p = split(item, NIB, r);
-        const int rb = r / LPB, w = r - rb * LPB, h0 = rb * RB;
+        const int rb = udiv(r, LPB), w = r - rb * LPB, h0 = rb * RB;
         if (!(LPB == W || w < W) || !live(p)) continue;
         // this strip's column in its plane: rows at constant offsets from it
         T* __restrict__ dst = out_g + (plane_rel(p) + (uint32_t)(h0 * W + w));
