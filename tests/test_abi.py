@@ -144,3 +144,14 @@ def test_empty_batch_is_a_no_op_for_the_data_passes(lib):
     for fn in (lib.wtconv_fwd, lib.wtconv_bwd_data, lib.wtconv_naive_fwd):
         assert fn(ctypes.byref(d), None, ok, ok, ok, None, None, 0, None) == 0
         assert fn(ctypes.byref(d), None, None, ok, ok, None, None, 0, None) == 1   # parameters still checked
+
+
+def test_huge_channel_counts_leave_the_multi_image_kernels(lib):
+    """The 14x14 kernel packs eight images of a channel per workgroup and
+    addresses them with 32-bit offsets: with 8*C*H*W at or past 2^32 elements
+    the shape takes the generic chain instead (sizes only: nothing runs)."""
+    small = _desc(B=8, C=1000, H=14, W=14, levels=1)
+    huge = _desc(B=8, C=1 << 22, H=14, W=14, levels=1)   # 8 * 2^22 * 196 > 2^32
+    assert lib.wtconv_workspace_size(ctypes.byref(small), 0) == 0
+    assert lib.wtconv_workspace_size(ctypes.byref(huge), 0) == lib.wtconv_naive_workspace_size(
+        ctypes.byref(huge), 0) > 0
