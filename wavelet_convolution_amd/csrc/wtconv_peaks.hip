@@ -1,6 +1,6 @@
 // Two measurement probes exported next to the layer's entry points. They are
 // not part of the layer: they measure, on the device at hand, the two
-// ceilings the layer's kernels are judged against - the rate of unpacked fp32
+// ceilings the layer's kernels are compared with - the rate of unpacked fp32
 // fused multiply-adds on the vector ALU and the rate of a plain HBM copy.
 #include <hip/hip_runtime.h>
 
