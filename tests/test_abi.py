@@ -155,3 +155,22 @@ def test_huge_channel_counts_leave_the_multi_image_kernels(lib):
     assert lib.wtconv_workspace_size(ctypes.byref(small), 0) == 0
     assert lib.wtconv_workspace_size(ctypes.byref(huge), 0) == lib.wtconv_naive_workspace_size(
         ctypes.byref(huge), 0) > 0
+
+
+def test_binding_checks_parameter_buffers():
+    """The library takes plain pointers, so the binding refuses parameter and
+    gradient buffers of the wrong shape, dtype or order before calling it."""
+    import torch
+    from wavelet_convolution_amd import binding as wt
+    x = torch.zeros(1, 4, 8, 8)
+    wb, wl, sc = torch.zeros(4, 5, 5), torch.zeros(1, 4, 4, 3, 3), torch.zeros(1, 4, 4)
+    bad = [(torch.zeros(3, 5, 5), wl, sc), (wb.double(), wl, sc), (wb, torch.zeros(1, 4, 4, 3, 3)[..., ::2, :], sc),
+           (wb, wl, torch.zeros(2, 4, 4))]
+    for args in bad:
+        with pytest.raises(ValueError):
+            wt.wtconv_fwd(x, *args)
+    with pytest.raises(ValueError):
+        wt.wtconv_bwd_weight(x, x, 5, wl, sc, out=(torch.zeros(4, 5, 5), torch.zeros(1, 4, 4, 3, 3),
+                                                     torch.zeros(1, 4, 5)))
+    with pytest.raises(ValueError):
+        wt.wtconv_fwd(x, wb, wl, sc, y=torch.zeros(1, 4, 8, 8, dtype=torch.bfloat16))

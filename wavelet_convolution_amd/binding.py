@@ -108,6 +108,26 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _check_f32(name: str, t, shape, like: torch.Tensor) -> None:
+    """The library reads and writes parameter-shaped buffers through plain
+    pointers: their shape, dtype, order and device are checked here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous() \
+            or t.device != like.device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} on {like.device}; "
+                         f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+
+
+def _check_params(act: torch.Tensor, w_base, w_lvl, scale, levels: int, kb: int, k: int) -> None:
+    C = act.shape[1]
+    if w_base is not None:
+        _check_f32("w_base", w_base, (C, kb, kb), act)
+    if levels > 0:
+        _check_f32("w_lvl", w_lvl, (levels, C, 4, k, k), act)
+        _check_f32("scale", scale, (levels, C, 4), act)
+
+
 def _dims(w_base: torch.Tensor, w_lvl: torch.Tensor):
     levels = int(w_lvl.shape[0]) if w_lvl is not None else 0
     k_level = int(w_lvl.shape[-1]) if (w_lvl is not None and w_lvl.dim() == 5) else 3
@@ -137,6 +157,13 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
     return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
 
 
+def _ws_bytes(ws: torch.Tensor | None) -> int:
+    """Usable bytes of a workspace tensor after aligning its start to 256."""
+    if ws is None:
+        return 0
+    return max(0, ws.numel() * ws.element_size() - (_ws_ptr(ws) - ws.data_ptr()))
+
+
 def _ws_ptr(ws: torch.Tensor | None) -> int:
     if ws is None:
         return 0
@@ -148,12 +175,13 @@ def _data_pass(name: str, naive: bool, op: int, act, w_base, w_lvl, scale, out, 
     lib = load_library()
     levels, kb, k = _dims(w_base, w_lvl)
     d = _desc(act, levels, kb, k)
+    _check_params(act, w_base, w_lvl, scale, levels, kb, k)
     if out is None:
         out = torch.empty_like(act)   # same memory order as act
     _same_layout(act, out)
     if ws is None:
         ws = _workspace(wtconv_workspace_size(act, levels, kb, k, op, naive), act.device)
-    ws_bytes = 0 if ws is None else ws.numel() - (_ws_ptr(ws) - ws.data_ptr())
+    ws_bytes = _ws_bytes(ws)
     _check(getattr(lib, name)(ctypes.byref(d), _ptr(act), _ptr(w_base), _ptr(w_lvl), _ptr(scale),
                               _ptr(out), _ws_ptr(ws), ws_bytes, _stream(stream)))
     return out
@@ -185,6 +213,7 @@ def _bwd_weight(name: str, naive: bool, x, dy, w_base_shape_kb, w_lvl, scale, ou
     kb = int(w_base_shape_kb)
     d = _desc(x, levels, kb, k)
     _same_layout(x, dy)
+    _check_params(x, None, w_lvl, scale, levels, kb, k)
     C = x.shape[1]
     if out is None:
         dev = x.device
@@ -193,8 +222,11 @@ def _bwd_weight(name: str, naive: bool, x, dy, w_base_shape_kb, w_lvl, scale, ou
                torch.empty((levels, C, 4), dtype=torch.float32, device=dev))
     if ws is None:
         ws = _workspace(wtconv_workspace_size(x, levels, kb, k, OP_BWD_WEIGHT, naive), x.device)
-    ws_bytes = 0 if ws is None else ws.numel() - (_ws_ptr(ws) - ws.data_ptr())
+    ws_bytes = _ws_bytes(ws)
     dwb, dwl, dsc = out
+    _check_f32("dw_base", dwb, (C, kb, kb), x)
+    _check_f32("dw_lvl", dwl, (levels, C, 4, k, k), x)
+    _check_f32("dscale", dsc, (levels, C, 4), x)
     _check(getattr(lib, name)(ctypes.byref(d), _ptr(x), _ptr(dy), _ptr(w_lvl), _ptr(scale), _ptr(dwb),
                               _ptr(dwl), _ptr(dsc), _ws_ptr(ws), ws_bytes, _stream(stream)))
     return out
