@@ -329,16 +329,29 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         // loads them, stores them widened and stores their four bands; on
         // the border it stores zeros to both (the padding of the base
         // convolution and of the level-1 convolutions).
-        constexpr int NQ = P::NQ, IPR = P::IPR, CPI = P::CPI, VA = P::VA, NQA = NPW * NQ, MQ = cdiv(NQA, NT);
+        // With ZFILL the regions are zeroed first and the items cover the
+        // interior cells only (row ii, item uu of the bordered grid, offset
+        // by the border).
+        constexpr bool ZF = P::ZFILL;
+        constexpr int CPI = P::CPI, VA = P::VA;
+        constexpr int NQ = ZF ? P::NQI : P::NQ, IPR = ZF ? P::IPRI : P::IPR;
+        constexpr int R0 = ZF ? PK : 0, U0 = ZF ? PK / CPI : 0;
+        constexpr int NQA = NPW * NQ, MQ = cdiv(NQA, NT);
+        if constexpr (ZF) {
+            static_assert((NPW * PL) % 4 == 0, "planes span whole 128-bit words");
+            float4* const z = reinterpret_cast<float4*>(lds);
+            for (int t = tid; t < NPW * PL / 4; t += NT) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+            __syncthreads();
+        }
         RawVec<T, VA> r0[MQ], r1[MQ];
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int qa = tid + k * NT;
             int q;
             const int p = split(qa < NQA ? qa : 0, NQ, q);
-            const int ii = udiv(q, IPR), uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
-            const bool inside =
-                (NQA % NT == 0 || qa < NQA) && live(p) && i >= 0 && i < H1 && j0 >= 0 && j0 < W1;
+            const int ri = udiv(q, IPR), ii = ri + R0, uu = q - ri * IPR + U0, i = ii - PK, j0 = uu * CPI - PK;
+            const bool inside = (NQA % NT == 0 || qa < NQA) && live(p) &&
+                                (ZF || (i >= 0 && i < H1 && j0 >= 0 && j0 < W1));
             // every lane loads (border items the plane's first words) and
             // then selects zeros: no branch, so the registers stay registers
             const T* s0 = in_g + (inside ? plane_rel(p) + (uint32_t)((2 * i) * W + 2 * j0) : 0u);
@@ -358,7 +371,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             const int p = split(qa, NQ, q);
             float* const A = Ap(p);
             float* const Bq = A + P::ASIZE;
-            const int ii = udiv(q, IPR), uu = q - ii * IPR, i = ii - PK, j0 = uu * CPI - PK;
+            const int ri = udiv(q, IPR), ii = ri + R0, uu = q - ri * IPR + U0, i = ii - PK, j0 = uu * CPI - PK;
             float f0[VA], f1[VA];
             widen_raw<T, VA>(r0[k], f0);
             widen_raw<T, VA>(r1[k], f1);
