@@ -93,32 +93,53 @@ def cpu_baseline(cfg, seconds: float):
     }
 
 
-def depthwise_context(torch, cfg, sets, steps: int):
+def depthwise_context(torch, wt, cfg, sets, steps: int):
     """The layer WTConv stands in for: a k_base x k_base depthwise convolution
     of the same activations, one step = forward + input gradient + weight
-    gradient through torch (MIOpen), with weights in the activations' dtype as
-    torch requires. Context only: a library's kernels, not this package's."""
+    gradient, timed two ways: through torch (MIOpen), with weights in the
+    activations' dtype as torch requires (a library's kernels, not this
+    package's), and through this library at L = 0 (its own depthwise kernels,
+    the same three entry points with no levels)."""
     F = torch.nn.functional
+    dev = sets[0][0].device
     wdt = sets[0][0].dtype
-    w = torch.randn(cfg.C, 1, cfg.kb, cfg.kb, device=sets[0][0].device).to(wdt)
+    w = torch.randn(cfg.C, 1, cfg.kb, cfg.kb, device=dev).to(wdt)
     pad = cfg.kb // 2
 
-    def one(i):
+    def torch_step(i):
         x, dy = sets[i % len(sets)]
         F.conv2d(x, w, padding=pad, groups=cfg.C)
         torch.ops.aten.convolution_backward(dy, x, w, None, [1, 1], [pad, pad], [1, 1], False, [0, 0], cfg.C,
                                             [True, True, False])
 
-    for i in range(2):
-        one(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        one(i)
-    torch.cuda.synchronize()
-    ms = 1e3 * (time.perf_counter() - t0) / steps
-    return {"what": f"torch depthwise conv {cfg.kb}x{cfg.kb}, fwd + input grad + weight grad", "ms_per_step": round(ms, 4),
-            "images_per_s": round(cfg.B / (ms * 1e-3), 1), "steps": steps}
+    wb = w.float().reshape(cfg.C, cfg.kb, cfg.kb).contiguous()
+    wl0 = torch.empty(0, cfg.C, 4, cfg.k, cfg.k, device=dev)
+    sc0 = torch.empty(0, cfg.C, 4, device=dev)
+    y, dx = torch.empty_like(sets[0][0]), torch.empty_like(sets[0][0])
+    grads = (torch.empty(cfg.C, cfg.kb, cfg.kb, device=dev), wl0, sc0)
+    ws = torch.empty(max(wt.wtconv_workspace_size(sets[0][0], 0, cfg.kb, cfg.k, op) for op in range(3)) + 256,
+                     dtype=torch.uint8, device=dev)
+
+    def own_step(i):
+        x, dy = sets[i % len(sets)]
+        wt.wtconv_fwd(x, wb, wl0, sc0, y=y, ws=ws)
+        wt.wtconv_bwd_data(dy, wb, wl0, sc0, dx=dx, ws=ws)
+        wt.wtconv_bwd_weight(x, dy, cfg.kb, wl0, sc0, out=grads, ws=ws)
+
+    def timed(step):
+        for i in range(2):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / steps
+
+    ms, own = timed(torch_step), timed(own_step)
+    return {"what": f"depthwise conv {cfg.kb}x{cfg.kb}, fwd + input grad + weight grad", "ms_per_step": round(ms, 4),
+            "images_per_s": round(cfg.B / (ms * 1e-3), 1), "steps": steps,
+            "this_library_L0_ms_per_step": round(own, 4)}
 
 
 def measure_peaks(torch, wt, reps: int = 5):
@@ -311,8 +332,9 @@ def main() -> int:
 
     context = None
     if not args.no_context:
-        context = depthwise_context(torch, cfg, sets, max(5, args.steps // 5))
+        context = depthwise_context(torch, wt, cfg, sets, max(5, args.steps // 5))
         context["wtconv_over_depthwise"] = round(ms_per_step / context["ms_per_step"], 3)
+        context["wtconv_over_this_library_L0"] = round(ms_per_step / context["this_library_L0_ms_per_step"], 3)
 
     peaks = None if args.no_peaks else measure_peaks(torch, wt)
 

@@ -326,6 +326,34 @@ def test_random_shapes_match_oracle(case):
             assert rel_err(to_f64(g), o) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("shape", [(3, 4, 56, 56, 0, 5, 5), (2, 3, 56, 56, 0, 7, 5), (3, 5, 28, 28, 0, 5, 3),
+                                   (1, 3, 28, 28, 0, 7, 7), (17, 3, 14, 14, 0, 5, 5), (5, 2, 14, 14, 0, 7, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_level_zero_fused_kernels(shape):
+    """L = 0 (the plain depthwise correlation) on the planes its fused
+    kernels cover, with batches that leave the last group of images partial:
+    against the oracle and against torch's own grouped convolution (fp64 on
+    the CPU), both layouts."""
+    _say(f"[parity] L = 0 fused {shape}")
+    B, C, H, W, L, kb, k = shape
+    for dtype in ("f32", "bf16"):
+        inp = make_inputs(*shape, dtype=dtype, seed=41)
+        x, dy, wb, wl, sc = to_device(inp)
+        oy, odx, (odwb, _, _) = _oracle_all(inp)
+        xd = torch.from_numpy(inp.act_f64("x"))
+        ref = torch.nn.functional.conv2d(xd, torch.from_numpy(inp.params_f64()[0])[:, None], padding=kb // 2,
+                                         groups=C).numpy()
+        for fmt in (torch.contiguous_format, torch.channels_last):
+            xi, dyi = x.contiguous(memory_format=fmt), dy.contiguous(memory_format=fmt)
+            y = wt.wtconv_fwd(xi, wb, wl, sc)
+            dx = wt.wtconv_bwd_data(dyi, wb, wl, sc)
+            dwb, _, _ = wt.wtconv_bwd_weight(xi, dyi, kb, wl, sc)
+            torch.cuda.synchronize()
+            assert rel_err(to_f64(y), oy) <= TOL[dtype] and rel_err(to_f64(y), ref) <= TOL[dtype]
+            assert rel_err(to_f64(dx), odx) <= TOL[dtype]
+            assert rel_err(to_f64(dwb), odwb) <= TOL["f32"]
+
+
 def test_empty_batch():
     """B = 0: empty outputs from the data passes and zero weight gradients
     (every output element overwritten)."""

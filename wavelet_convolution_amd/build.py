@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwtconv.so")
 SOURCES = ["wtconv_fused.hip", "wtconv_tiled.hip", "wtconv_bwdw.hip", "wtconv_naive.hip", "wtconv_api.hip",
-           "wtconv_peaks.hip", "wtconv_layout.hip"]
+           "wtconv_peaks.hip", "wtconv_layout.hip", "wtconv_dw.hip"]
 ARCH = os.environ.get("WTCONV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

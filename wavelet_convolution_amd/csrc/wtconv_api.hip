@@ -9,6 +9,7 @@
 #include "../../include/wtconv.h"
 #include "wtconv_plans.h"
 #include "wtconv_bwdw.h"
+#include "wtconv_dw.h"
 #include "wtconv_layout.h"
 #include "wtconv_naive.h"
 #include "wtconv_tiled.h"
@@ -62,6 +63,7 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // in the workspace (after the kernels' own part); everything else runs the
 // generic chain, which reads either layout directly.
 struct Route {
+    const wtc::DwEntry* de = nullptr;      // L = 0 data kernels (plain depthwise correlation)
     const wtc::PlaneEntry* pe = nullptr;   // whole-plane data kernels
     const wtc::SplitEntry* se = nullptr;   // coarse + fine data kernels
     bool bw = false;                       // fused weight-gradient kernels
@@ -81,6 +83,10 @@ Route route(const wtconv_desc_t* d, int op) {
                 r.bw = true;
                 r.own = b;
             }
+        } else if (d->levels == 0) {
+            r.de = wtc::find_dw_entry(d->H, d->W, d->k_base);
+            // the kernel addresses a workgroup's planes with 32-bit offsets
+            if (r.de && (uint64_t)r.de->npw * d->C * d->H * d->W >= (1ull << 32)) r.de = nullptr;
         } else {
             r.pe = wtc::find_plane_entry(d->H, d->W, d->levels, d->k_base, d->k_level);
             // the whole-plane kernels address a workgroup's planes with 32-bit offsets
@@ -89,7 +95,7 @@ Route route(const wtconv_desc_t* d, int op) {
                 r.own = r.se->ws_bytes(d->B, d->C);
         }
     }
-    if (r.pe || r.se || r.bw) {
+    if (r.de || r.pe || r.se || r.bw) {
         r.copies = nhwc;
         r.need = r.copies ? align256(r.own) + 2 * align256(act_bytes(d)) : r.own;
     } else if (d->B == 0 && op != WTCONV_OP_BWD_WEIGHT) {
@@ -125,7 +131,7 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     if (!ws_ok(r, ws, ws_bytes)) return WTCONV_ERR_WORKSPACE;
     const int dt = d->dtype == WTCONV_BF16 ? 1 : 0;
     const hipStream_t s = (hipStream_t)stream;
-    if (!r.pe && !r.se) {
+    if (!r.de && !r.pe && !r.se) {
         // no fused kernel for this shape: the generic one-kernel-per-step
         // chain (same results, intermediates in device memory)
         const hipError_t err = wtc::naive_data_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
@@ -142,7 +148,9 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
             return WTCONV_ERR_LAUNCH;
     }
     hipError_t err;
-    if (r.pe)   // the whole plane fits one workgroup: one kernel, no workspace of its own
+    if (r.de)   // L = 0: the plain depthwise correlation
+        err = r.de->fn[dt][flip ? 1 : 0](kin, w_base, kout, d->B, d->C, s);
+    else if (r.pe)   // the whole plane fits one workgroup: one kernel, no workspace of its own
         err = r.pe->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, d->B, d->C, s);
     else        // coarse pass on the LL band at level L0, then the fine tiles
         err = r.se->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, (float*)ws, d->B, d->C, s);

@@ -22,6 +22,7 @@
 // reproducible.
 #include "wtconv_bwdw.h"
 #include "wtconv_device.h"
+#include "wtconv_dw.h"
 #include "wtconv_plans.h"
 
 namespace wtc {
@@ -1209,6 +1210,105 @@ static hipError_t plane_split_launch(const void* x, const void* dy, const float*
     return hipGetLastError();
 }
 
+// L = 0: the base taps alone, G[m][n] = sum_{b,h,w} dy[h][w] x[h+m-kb/2][w+n-kb/2].
+// One workgroup per (channel, chunk of the batch); NPW planes per step: their
+// x interiors (bordered, zero borders written once) and dy stream into LDS,
+// every lane correlates one RB-row column strip (taps_col) into kb*kb sums
+// kept in registers across the chunk; the end of the chunk reduces them as
+// the general kernel does (16-lane rows by DPP, rows and waves through LDS
+// in a fixed order).
+template <class P, typename T>
+__global__ __launch_bounds__(P::NT) void dw_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy,
+                                                        float* __restrict__ part, int B, int C, int bpc) {
+    constexpr int H = P::H, W = P::W, KB = P::KB, NT = P::NT, RB = P::RB, NPB = P::NPW, NW = NT / 64;
+    constexpr int PB = P::PB, XO = P::XO, SX = P::SX, SD = P::SD, VA = P::VA, NQ = P::NQ, LPB = P::LPB;
+    constexpr int NIB = P::NIB, KB2 = KB * KB;
+    constexpr int PL = round_up(P::XSIZE + P::DSIZE, 4), RED = NW * 4 * KB2;
+    __shared__ __attribute__((aligned(16))) float lds[NPB * PL > RED ? NPB * PL : RED];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = blockIdx.x % C, chunk = blockIdx.x / C;
+    const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
+    {
+        float4* const z = reinterpret_cast<float4*>(lds);
+        for (int t = tid; t < NPB * PL / 4; t += NT) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float acc[KB2];
+#pragma unroll
+    for (int t = 0; t < KB2; ++t) acc[t] = 0.f;
+    for (int b = b0; b < b1; b += NPB) {
+        __syncthreads();   // the zeros, or the previous step's taps, are done
+        for (int q = tid; q < NPB * NQ; q += NT) {
+            const int p = udiv(q, NQ), r = q - p * NQ, row = udiv(r, W / VA), col = (r - row * (W / VA)) * VA;
+            float* const X = lds + p * PL + (PB + row) * SX + XO + col;
+            float* const D = lds + p * PL + P::XSIZE + row * SD + col;
+            if (b + p < b1) {   // planes past the chunk's end hold zeros and add nothing
+                const size_t off = ((size_t)(b + p) * C + c) * H * W + (size_t)row * W + col;
+                RawVec<T, VA> vx, vd;
+                load_raw<T, VA>(x + off, vx);
+                load_raw<T, VA>(dy + off, vd);
+                store_lds<T, VA>(X, vx);
+                store_lds<T, VA>(D, vd);
+            } else {
+                float zero[VA] = {};
+                store_vec<VA>(X, zero);
+                store_vec<VA>(D, zero);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < P::MB; ++it) {
+            const int item = tid + it * NT;
+            if (!((NPB * NIB) % NT == 0 || item < NPB * NIB)) continue;
+            const int p = NPB == 1 ? 0 : udiv(item, NIB), r = item - p * NIB;
+            const int rb = udiv(r, LPB), w = r - rb * LPB, h0 = rb * RB;
+            if (LPB == W || w < W)
+                taps_col<KB, RB, SX, SD>(lds + p * PL + XO - PB + h0 * SX + w, lds + p * PL + P::XSIZE + h0 * SD + w,
+                                         acc);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < KB2; ++t) acc[t] = row_sum(acc[t]);
+    __syncthreads();   // LDS becomes reduction scratch
+    float* const red = lds;   // [NW * 4 rows][KB2]
+    if ((lane & 15) == 0) {
+        const int wr = wave * 4 + (lane >> 4);
+#pragma unroll
+        for (int t = 0; t < KB2; ++t) red[wr * KB2 + t] = acc[t];
+    }
+    __syncthreads();
+    for (int t = tid; t < KB2; t += NT) {
+        float v = 0.f;
+        for (int wr = 0; wr < NW * 4; ++wr) v += red[wr * KB2 + t];
+        part[((size_t)chunk * C + c) * KB2 + t] = v;
+    }
+}
+
+// planes per chunk: about four workgroups per CU in all
+static int dw_bw_bpc(int B, int C) { return chunk_units(B, C, cu_count() * 4); }
+
+template <class P>
+static size_t dw_bw_ws(int B, int C) {
+    return (size_t)cdiv(B, dw_bw_bpc(B, C)) * C * P::KB * P::KB * sizeof(float);
+}
+
+template <class P, typename T>
+static hipError_t dw_bw_launch(const void* x, const void* dy, const float* w_lvl, const float* scale,
+                               float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
+                               hipStream_t stream) {
+    (void)w_lvl; (void)scale; (void)dw_lvl; (void)dscale;
+    const int bpc = dw_bw_bpc(B, C), nch = cdiv(B, bpc);
+    float* part = (float*)ws;
+    hipLaunchKernelGGL((dw_bwdw_kernel<P, T>), dim3((unsigned)(nch * C)), dim3(P::NT), 0, stream, (const T*)x,
+                       (const T*)dy, part, B, C, bpc);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // the finalize with no levels: the fixed-order chunk sum of the base taps
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(P::KB, 1, 0)), 0, stream,
+                       (const float*)part, nch, 0, (const float*)nullptr, 0, C, 0, P::KB, 1, (const float*)nullptr,
+                       (const float*)nullptr, dw_base, (float*)nullptr, (float*)nullptr);
+    return hipGetLastError();
+}
+
 typedef hipError_t (*bwdw_fn)(const void*, const void*, const float*, const float*, float*, float*, float*,
                               void*, int, int, hipStream_t);
 
@@ -1258,6 +1358,15 @@ typedef BwPlan<28, 28, 2, 1, 5, 2, WTC_CB28_NPB> CB_28_L2_k5;
 typedef BwPlan<28, 28, 1, 5, 5, 2, WTC_BW28_NPB> WP_28_L1of2_k55;
 typedef BwPlan<14, 14, 1, 1, 5, 1, WTC_BW14C_NPB> CB_14_L1_k5;
 
+typedef DwPlan<56, 56, 5, 256, 14, 1> DB_56_k5;
+typedef DwPlan<56, 56, 7, 256, 14, 1> DB_56_k7;
+typedef DwPlan<28, 28, 5, 256, 7, 2> DB_28_k5;
+typedef DwPlan<28, 28, 7, 256, 7, 2> DB_28_k7;
+typedef DwPlan<14, 14, 5, 256, 14, 16> DB_14_k5;
+typedef DwPlan<14, 14, 7, 256, 14, 16> DB_14_k7;
+// L = 0 entries match any k_level (no level kernels)
+#define WTC_BW_DW(PLAN) {PLAN::H, PLAN::W, 0, PLAN::KB, 0, {dw_bw_launch<PLAN, float>, dw_bw_launch<PLAN, bf16_t>}, dw_bw_ws<PLAN>}
+
 #define WTC_BW_WHOLE(PLAN) \
     {PLAN::H, PLAN::W, PLAN::L, PLAN::KB, PLAN::K, {whole_launch<PLAN, float>, whole_launch<PLAN, bf16_t>}, whole_ws<PLAN>}
 #define WTC_BW_PLANESPLIT(FPL, CPL)                                                               \
@@ -1287,11 +1396,13 @@ static const BwEntry kBwEntries[] = {
     WTC_BW_SPLIT(TB_128_L2of3_k55, CB_32_L1_k5),   WTC_BW_SPLIT(TB_128_L2of4_k55, CB_32_L2_k5),
     WTC_BW_SPLIT(TB_128_L2of5_k55, CB_32_L3_k5),   WTC_BW_SPLIT(TB_256_L2of4_k75, CB_64_L2_k5),
     WTC_BW_SPLIT(TB_64_L2of4_k33, CB_16_L2_k3),    WTC_BW_SPLIT(TB_64_L1of2_k55, CB_32_L1_k5b),
+    WTC_BW_DW(DB_56_k5), WTC_BW_DW(DB_56_k7), WTC_BW_DW(DB_28_k5), WTC_BW_DW(DB_28_k7), WTC_BW_DW(DB_14_k5),
+    WTC_BW_DW(DB_14_k7),
 };
 
 static const BwEntry* find_bw(int H, int W, int L, int KB, int K) {
     for (const BwEntry& e : kBwEntries)
-        if (e.H == H && e.W == W && e.L == L && e.KB == KB && e.K == K) return &e;
+        if (e.H == H && e.W == W && e.L == L && e.KB == KB && (L == 0 || e.K == K)) return &e;
     return nullptr;
 }
 
