@@ -108,8 +108,10 @@ size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
 /* Forward: y = WTConv(x). One fused pass: reads x once, writes y once.
    Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
    that fit one workgroup's LDS; ws may then be NULL).
+   L = 0 is the plain depthwise correlation; it has its own fused kernels
+   on 56x56, 28x28 and 14x14 planes with k_base 5 or 7.
    Shapes without a fused kernel (any other H, W >= 1, L in 0..5, odd k up
-   to 15; e.g. L = 0, the plain depthwise convolution) run the generic
+   to 15) run the generic
    one-kernel-per-step chain of the naive entry points below: the same
    results and semantics, with the intermediates in the workspace, which
    wtconv_workspace_size then reports. A channels-last call of a planned
