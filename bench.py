@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "WTConv fwd+bwd images/sec and achieved HBM TB/s (% of MI355X peak)"
 KERNEL_SOURCES = ("wtconv_device.h", "wtconv_plans.h", "wtconv_plane.h", "wtconv_fused.hip", "wtconv_tiled.hip",
-                  "wtconv_bwdw.hip")
+                  "wtconv_bwdw.hip", "wtconv_dw.h", "wtconv_dw.hip")
 
 
 def kernel_source_hash() -> str:

@@ -52,6 +52,8 @@ def test_full_size_sampled(name):
         o = oracle.bwd_weight(xw[:, c:c + 1], dyw[:, c:c + 1], *pw)
         for key, got, ref in (("dw_base", dwb[c:c + 1], o[0]), ("dw_lvl", dwl[:, c:c + 1], o[1]),
                               ("dscale", dsc[:, c:c + 1], o[2])):
+            if ref.size == 0:   # no levels
+                continue
             e = rel_err(got, ref)
             worst[key] = max(worst[key], e)
             assert e <= TOL["f32"], (c, key, e)

@@ -39,6 +39,9 @@ CONFIGS = {
     **{f"sweep128_L{L}": WorkloadConfig(f"sweep128_L{L}", 32, 128, 128, 128, L, 5, 5, "bf16")
        for L in range(1, 6)},
     "large256": WorkloadConfig("large256", 16, 256, 256, 256, 4, 7, 5, "bf16"),
+    # context: the stage-1 activations through the plain depthwise 5x5
+    # convolution WTConv stands in for (the layer at L = 0)
+    "depthwise56": WorkloadConfig("depthwise56", 64, 96, 56, 56, 0, 5, 5, "bf16"),
 }
 
 # the workload the headline images/s figure is quoted on

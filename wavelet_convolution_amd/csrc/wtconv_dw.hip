@@ -86,7 +86,10 @@ hipError_t launch_dw(const void* in, const float* wb, void* out, int B, int C, h
      PLAN::NPW}
 
 // the ConvNeXt-stage planes with the base kernels of the pages' workloads
-typedef DwPlan<56, 56, 5, 256, 14, 1> DP_56_k5;
+#ifndef WTC_DW56
+#define WTC_DW56 256, 14, 1
+#endif
+typedef DwPlan<56, 56, 5, WTC_DW56> DP_56_k5;
 typedef DwPlan<56, 56, 7, 256, 14, 1> DP_56_k7;
 typedef DwPlan<28, 28, 5, 256, 7, 2> DP_28_k5;
 typedef DwPlan<28, 28, 7, 256, 7, 2> DP_28_k7;
