@@ -158,3 +158,29 @@ def test_module_keeps_only_x_and_its_peak_memory():
     print(f"backward peak above the live tensors: {peak / act:.2f} x the bytes of x", flush=True)
     # dx, the three gradients, the weight-gradient workspace and allocator rounding
     assert peak <= 2.5 * act + 16 * 2 ** 20
+
+
+@pytest.mark.gpu
+@torch_gpu
+def test_module_trains():
+    """A few plain SGD steps fitting the layer to a target made by another
+    instance of it: the loss falls steadily (autograd wiring, gradient
+    accumulation into .grad, parameter updates between calls)."""
+    print("[module] training 4x8x28x28 L2 f32", flush=True)
+    torch.manual_seed(0)
+    teacher = WTConv2d(8, 2, 5, 5, device="cuda")
+    student = WTConv2d(8, 2, 5, 5, device="cuda")
+    x = torch.randn(4, 8, 28, 28, device="cuda")
+    with torch.no_grad():
+        target = teacher(x)
+    opt = torch.optim.SGD(student.parameters(), lr=0.5)
+    losses = []
+    for _ in range(30):
+        opt.zero_grad()
+        loss = torch.nn.functional.mse_loss(student(x), target)
+        loss.backward()
+        opt.step()
+        losses.append(float(loss.detach()))
+    print(f"loss {losses[0]:.4g} -> {losses[-1]:.4g}", flush=True)
+    assert losses[-1] < 0.25 * losses[0]
+    assert all(b <= a * 1.0001 for a, b in zip(losses, losses[1:]))
