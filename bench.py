@@ -117,7 +117,7 @@ def depthwise_context(torch, wt, cfg, sets, steps: int):
     sc0 = torch.empty(0, cfg.C, 4, device=dev)
     y, dx = torch.empty_like(sets[0][0]), torch.empty_like(sets[0][0])
     grads = (torch.empty(cfg.C, cfg.kb, cfg.kb, device=dev), wl0, sc0)
-    ws = torch.empty(max(wt.wtconv_workspace_size(sets[0][0], 0, cfg.kb, cfg.k, op) for op in range(3)) + 256,
+    ws = torch.empty(max(wt.wtconv_workspace_size(sets[0][0], 0, cfg.kb, cfg.k, op) for op in range(4)) + 256,
                      dtype=torch.uint8, device=dev)
 
     def own_step(i):
@@ -125,6 +125,11 @@ def depthwise_context(torch, wt, cfg, sets, steps: int):
         wt.wtconv_fwd(x, wb, wl0, sc0, y=y, ws=ws)
         wt.wtconv_bwd_data(dy, wb, wl0, sc0, dx=dx, ws=ws)
         wt.wtconv_bwd_weight(x, dy, cfg.kb, wl0, sc0, out=grads, ws=ws)
+
+    def own_single_pass(i):
+        x, dy = sets[i % len(sets)]
+        wt.wtconv_fwd(x, wb, wl0, sc0, y=y, ws=ws)
+        wt.wtconv_bwd(x, dy, wb, wl0, sc0, dx=dx, out=grads, ws=ws)
 
     def timed(step):
         for i in range(2):
@@ -136,10 +141,11 @@ def depthwise_context(torch, wt, cfg, sets, steps: int):
         torch.cuda.synchronize()
         return 1e3 * (time.perf_counter() - t0) / steps
 
-    ms, own = timed(torch_step), timed(own_step)
+    ms, own, own1 = timed(torch_step), timed(own_step), timed(own_single_pass)
     return {"what": f"depthwise conv {cfg.kb}x{cfg.kb}, fwd + input grad + weight grad", "ms_per_step": round(ms, 4),
             "images_per_s": round(cfg.B / (ms * 1e-3), 1), "steps": steps,
-            "this_library_L0_ms_per_step": round(own, 4)}
+            "this_library_L0_ms_per_step": round(own, 4),
+            "this_library_L0_single_pass_bwd_ms_per_step": round(own1, 4)}
 
 
 def measure_peaks(torch, wt, reps: int = 5):
@@ -183,6 +189,9 @@ def main() -> int:
                     help="replay a HIP graph of each step instead of launching it from Python (measured "
                          "slower on this path: 0.19 vs 0.18 ms per stage-1 step)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the FMA-rate and copy-rate probes")
+    ap.add_argument("--single-pass-bwd", action="store_true",
+                    help="run the backward as one wtconv_bwd call (a single pass over x and dy where the "
+                         "library has one: L = 0 on its planned planes)")
     ap.add_argument("--channels-last", action="store_true",
                     help="channels-last activations (planar kernels on converted copies)")
     ap.add_argument("--no-context", action="store_true",
@@ -237,7 +246,7 @@ def main() -> int:
              torch.empty(tuple(sc.shape), device=dev))
     # one workspace for every call of a step, allocated before timing
     ws_bytes = max(wt.wtconv_workspace_size(sets[0][0], cfg.L, cfg.kb, cfg.k, op)
-                   for op in (wt.OP_FWD, wt.OP_BWD_DATA, wt.OP_BWD_WEIGHT))
+                   for op in (wt.OP_FWD, wt.OP_BWD_DATA, wt.OP_BWD_WEIGHT, wt.OP_BWD))
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
 
     def step(i, ev=None):
@@ -247,10 +256,16 @@ def main() -> int:
         wt.wtconv_fwd(x, wb, wl, sc, y=y, ws=ws)
         if ev is not None:
             ev[1].record()
-        wt.wtconv_bwd_data(dy, wb, wl, sc, dx=dx, ws=ws)
-        if ev is not None:
-            ev[2].record()
-        wt.wtconv_bwd_weight(x, dy, cfg.kb, wl, sc, out=grads, ws=ws)
+        if args.single_pass_bwd:
+            # the whole backward in one call (events 1 -> 2 span it)
+            wt.wtconv_bwd(x, dy, wb, wl, sc, dx=dx, out=grads, ws=ws)
+            if ev is not None:
+                ev[2].record()
+        else:
+            wt.wtconv_bwd_data(dy, wb, wl, sc, dx=dx, ws=ws)
+            if ev is not None:
+                ev[2].record()
+            wt.wtconv_bwd_weight(x, dy, cfg.kb, wl, sc, out=grads, ws=ws)
         if ev is not None:
             ev[3].record()
 
@@ -294,18 +309,22 @@ def main() -> int:
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    per = {"fwd": [], "bwd_data": [], "bwd_weight": []}
+    per = {"fwd": [], "bwd": []} if args.single_pass_bwd else {"fwd": [], "bwd_data": [], "bwd_weight": []}
     for e in evs:
         per["fwd"].append(e[0].elapsed_time(e[1]))
-        per["bwd_data"].append(e[1].elapsed_time(e[2]))
-        per["bwd_weight"].append(e[2].elapsed_time(e[3]))
+        if args.single_pass_bwd:
+            per["bwd"].append(e[1].elapsed_time(e[2]))
+        else:
+            per["bwd_data"].append(e[1].elapsed_time(e[2]))
+            per["bwd_weight"].append(e[2].elapsed_time(e[3]))
     dur = {k: sum(v) / len(v) for k, v in per.items()}   # mean ms per launch (the roofline's figure)
     med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
     dominant = max(dur, key=dur.get)
-    achieved = model.flops_per_call / (dur[dominant] * 1e-3) / 1e12
+    calls = 2 if dominant == "bwd" else 1   # the whole backward does two calls' multiply-adds
+    achieved = calls * model.flops_per_call / (dur[dominant] * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     # the stored counter summaries are of planar runs
-    traffic = None if args.channels_last else read_traffic(cfg.name, dominant, src_hash)
+    traffic = None if (args.channels_last or args.single_pass_bwd) else read_traffic(cfg.name, dominant, src_hash)
 
     naive = None
     if not args.no_naive:
@@ -364,7 +383,8 @@ def main() -> int:
         "config": {"workload": cfg.name, "B": cfg.B, "C": cfg.C, "H": cfg.H, "W": cfg.W, "levels": cfg.L,
                    "k_base": cfg.kb, "k_level": cfg.k, "activations": cfg.dtype, "accumulate": "f32",
                    "input_sets_rotated": len(sets), "launch": "hip graph per step" if args.graph else "eager",
-                   "layout": "channels_last" if args.channels_last else "nchw"},
+                   "layout": "channels_last" if args.channels_last else "nchw",
+                   "backward": "wtconv_bwd" if args.single_pass_bwd else "wtconv_bwd_data + wtconv_bwd_weight"},
         "hbm": {"min_bytes_per_step": model.step_bytes, "achieved_TBs": round(hbm_tbs, 4),
                 "frac_of_8TBs": round(hbm_tbs / iomodel.HBM_PEAK_TBS, 4)},
         "kernel_ms": {k: round(v, 5) for k, v in dur.items()},
@@ -373,7 +393,7 @@ def main() -> int:
                      "peak": iomodel.FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / iomodel.FP32_VECTOR_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "flops_per_launch": model.flops_per_call,
+                     "flops_per_launch": calls * model.flops_per_call,
                      "unpacked_fma_ceiling_TFLOPs": iomodel.FP32_UNPACKED_FMA_TFLOPS},
         "naive_baseline": naive,
         "context": context,

@@ -85,7 +85,8 @@ typedef enum {
 typedef enum {
     WTCONV_OP_FWD = 0,
     WTCONV_OP_BWD_DATA = 1,
-    WTCONV_OP_BWD_WEIGHT = 2
+    WTCONV_OP_BWD_WEIGHT = 2,
+    WTCONV_OP_BWD = 3          /* wtconv_bwd: both backward results */
 } wtconv_op_t;
 
 typedef struct {
@@ -146,6 +147,21 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t *desc, const void *x,
                                   const float *scale, float *dw_base,
                                   float *dw_lvl, float *dscale, void *ws,
                                   size_t ws_bytes, void *stream);
+
+/* Whole backward pass: dx (as wtconv_bwd_data) and the weight gradients (as
+   wtconv_bwd_weight) in one call. For L = 0 on the planes its kernel covers
+   (56x56, 28x28, 14x14; k_base 5 or 7; planar layout) it is a single pass
+   that reads x and dy once, the fused backward the I/O model counts at
+   5*N*e instead of 6*N*e bytes per step. Other shapes run the two backward
+   calls in stream order on one workspace. Results equal those of the two
+   calls bit for bit (the same multiply-adds in the same order). x and dy
+   must not overlap dx. Workspace:
+   wtconv_workspace_size(desc, WTCONV_OP_BWD). */
+wtconv_status_t wtconv_bwd(const wtconv_desc_t *desc, const void *x,
+                           const void *dy, const float *w_base,
+                           const float *w_lvl, const float *scale, void *dx,
+                           float *dw_base, float *dw_lvl, float *dscale,
+                           void *ws, size_t ws_bytes, void *stream);
 
 /* Naive unfused baseline (comparator only): the same three operations as a
    chain of one-kernel-per-step launches (analysis, per-level convolution,

@@ -174,3 +174,22 @@ def test_binding_checks_parameter_buffers():
                                                      torch.zeros(1, 4, 5)))
     with pytest.raises(ValueError):
         wt.wtconv_fwd(x, wb, wl, sc, y=torch.zeros(1, 4, 8, 8, dtype=torch.bfloat16))
+
+
+def test_whole_backward_workspace(lib):
+    """wtconv_bwd: the single-pass kernel's workspace where it exists (L = 0 on
+    a planned plane, planar), else enough for the two backward calls."""
+    for kw in (dict(levels=0), dict(levels=0, layout=1), dict(levels=3), dict(levels=2, H=13, W=11)):
+        d = _desc(**kw)
+        need = lib.wtconv_workspace_size(ctypes.byref(d), 3)
+        parts = [lib.wtconv_workspace_size(ctypes.byref(d), op) for op in (1, 2)]
+        assert 0 < need < (1 << 40)
+        if kw.get("levels") == 0 and kw.get("layout", 0) == 0:
+            assert need == parts[1]   # the same partial sums as the weight kernel
+        else:
+            assert need == max(parts)
+    d = _desc(levels=0)
+    ok = ctypes.c_void_p(1 << 20)
+    # dx overlapping dy is refused before anything launches
+    assert lib.wtconv_bwd(ctypes.byref(d), ok, ctypes.c_void_p(1 << 24), ok, ok, ok, ctypes.c_void_p(1 << 24), ok,
+                          ok, ok, ctypes.c_void_p(1 << 28), 1 << 30, None) == 1

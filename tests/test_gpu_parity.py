@@ -354,6 +354,28 @@ def test_level_zero_fused_kernels(shape):
             assert rel_err(to_f64(dwb), odwb) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("shape", [(3, 4, 56, 56, 0, 5, 5), (5, 3, 28, 28, 0, 7, 5), (17, 3, 14, 14, 0, 5, 5),
+                                   (2, 3, 56, 56, 3, 5, 5), (2, 3, 13, 11, 2, 5, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_whole_backward_equals_the_two_calls(shape):
+    """wtconv_bwd (a single pass over x and dy at L = 0 on planned planes,
+    the two calls elsewhere) equals wtconv_bwd_data + wtconv_bwd_weight bit
+    for bit, and the oracle within the bars."""
+    _say(f"[parity] whole backward {shape}")
+    kb = shape[5]
+    for dtype in ("f32", "bf16"):
+        inp = make_inputs(*shape, dtype=dtype, seed=43)
+        x, dy, wb, wl, sc = to_device(inp)
+        dx, (dwb, dwl, dsc) = wt.wtconv_bwd(x, dy, wb, wl, sc)
+        dx2 = wt.wtconv_bwd_data(dy, wb, wl, sc)
+        dwb2, dwl2, dsc2 = wt.wtconv_bwd_weight(x, dy, kb, wl, sc)
+        torch.cuda.synchronize()
+        for a, b in ((dx, dx2), (dwb, dwb2), (dwl, dwl2), (dsc, dsc2)):
+            assert torch.equal(a, b)
+        _, odx, (odwb, _, _) = _oracle_all(inp)
+        assert rel_err(to_f64(dx), odx) <= TOL[dtype] and rel_err(to_f64(dwb), odwb) <= TOL["f32"]
+
+
 def test_empty_batch():
     """B = 0: empty outputs from the data passes and zero weight gradients
     (every output element overwritten)."""

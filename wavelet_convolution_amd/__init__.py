@@ -11,7 +11,7 @@ _BINDING_NAMES = (
     "wtconv_fwd", "wtconv_bwd_data", "wtconv_bwd_weight",
     "wtconv_naive_fwd", "wtconv_naive_bwd_data", "wtconv_naive_bwd_weight",
     "wtconv_workspace_size", "wtconv_status_string", "load_library", "WTConvError",
-    "wtconv_peak_fma", "wtconv_peak_copy", "layout_of",
+    "wtconv_bwd", "wtconv_peak_fma", "wtconv_peak_copy", "layout_of",
 )
 
 _MODULE_NAMES = ("WTConv2d", "WTConvFunction", "wtconv")

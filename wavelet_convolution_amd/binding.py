@@ -19,7 +19,7 @@ _lib = None
 
 WTCONV_F32, WTCONV_BF16 = 0, 1
 WTCONV_NCHW, WTCONV_NHWC = 0, 1
-OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2
+OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT, OP_BWD = 0, 1, 2, 3
 
 
 class WTConvError(RuntimeError):
@@ -63,6 +63,8 @@ def load_library() -> ctypes.CDLL:
                 fn = getattr(lib, name)
                 fn.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]
                 fn.restype = ctypes.c_int
+            lib.wtconv_bwd.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]
+            lib.wtconv_bwd.restype = ctypes.c_int
             lib.wtconv_peak_fma.argtypes = [_V, ctypes.c_int32, ctypes.c_int32, _V]
             lib.wtconv_peak_fma.restype = ctypes.c_int
             lib.wtconv_peak_copy.argtypes = [_V, _V, _SZ, _V]
@@ -254,3 +256,32 @@ def wtconv_peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
         raise ValueError("dst is smaller than src")
     _check(load_library().wtconv_peak_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
     return 2 * n
+
+
+def wtconv_bwd(x, dy, w_base, w_lvl, scale, dx=None, out=None, ws=None, stream=None):
+    """(dx, (dW_base, dW_lvl, dscale)) in one call: a single pass over x and
+    dy where the library has one (L = 0 on its planned planes), else the two
+    backward calls on one workspace."""
+    lib = load_library()
+    levels, kb, k = _dims(w_base, w_lvl)
+    d = _desc(x, levels, kb, k)
+    _same_layout(x, dy)
+    _check_params(x, w_base, w_lvl, scale, levels, kb, k)
+    C = x.shape[1]
+    if dx is None:
+        dx = torch.empty_like(dy)
+    _same_layout(dy, dx)
+    if out is None:
+        dev = x.device
+        out = (torch.empty((C, kb, kb), dtype=torch.float32, device=dev),
+               torch.empty((levels, C, 4, k, k), dtype=torch.float32, device=dev),
+               torch.empty((levels, C, 4), dtype=torch.float32, device=dev))
+    dwb, dwl, dsc = out
+    _check_f32("dw_base", dwb, (C, kb, kb), x)
+    _check_f32("dw_lvl", dwl, (levels, C, 4, k, k), x)
+    _check_f32("dscale", dsc, (levels, C, 4), x)
+    if ws is None:
+        ws = _workspace(wtconv_workspace_size(x, levels, kb, k, OP_BWD), x.device)
+    _check(lib.wtconv_bwd(ctypes.byref(d), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(w_lvl), _ptr(scale), _ptr(dx),
+                          _ptr(dwb), _ptr(dwl), _ptr(dsc), _ws_ptr(ws), _ws_bytes(ws), _stream(stream)))
+    return dx, out

@@ -158,12 +158,28 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
+// The single-pass backward kernel covers this shape (planar, non-empty).
+bool single_pass_bwd(const wtconv_desc_t* d) {
+    return d->B > 0 && d->layout == WTCONV_NCHW &&
+           wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base) != (size_t)-1;
+}
+
+// Workspace of wtconv_bwd: the single-pass kernel's, else enough for the
+// two backward calls run one after the other on it.
+size_t bwd_workspace(const wtconv_desc_t* d) {
+    if (single_pass_bwd(d))
+        return wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base);
+    const size_t a = route(d, WTCONV_OP_BWD_DATA).need, b = route(d, WTCONV_OP_BWD_WEIGHT).need;
+    return a > b ? a : b;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
     if (check_desc(d) != WTCONV_OK) return (size_t)-1;
+    if (op == WTCONV_OP_BWD) return bwd_workspace(d);
     if (op != WTCONV_OP_FWD && op != WTCONV_OP_BWD_DATA && op != WTCONV_OP_BWD_WEIGHT) return (size_t)-1;
     return route(d, op).need;
 }
@@ -214,6 +230,34 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const v
                                      d->dtype == WTCONV_BF16, d->layout == WTCONV_NHWC, x, dy, w_lvl, scale,
                                      dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+wtconv_status_t wtconv_bwd(const wtconv_desc_t* d, const void* x, const void* dy, const float* w_base,
+                           const float* w_lvl, const float* scale, void* dx, float* dw_base, float* dw_lvl,
+                           float* dscale, void* ws, size_t ws_bytes, void* stream) {
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (d->B > 0 && (!x || !dy || !dx)) return WTCONV_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return WTCONV_ERR_INVALID_ARG;
+    if (overlap(dy, act_bytes(d), dx, act_bytes(d)) || overlap(x, act_bytes(d), dx, act_bytes(d)))
+        return WTCONV_ERR_INVALID_ARG;
+    if (!dw_base || !aligned16(dw_base)) return WTCONV_ERR_INVALID_ARG;
+    if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
+    if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
+    st = check_params(d, w_base, w_lvl, scale, true);
+    if (st != WTCONV_OK) return st;
+    const size_t need = bwd_workspace(d);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
+    if (single_pass_bwd(d)) {
+        const hipError_t err = wtc::bwd_single_pass_launch(d->B, d->C, d->H, d->W, d->k_base,
+                                                           d->dtype == WTCONV_BF16, x, dy, w_base, dx, dw_base,
+                                                           ws, (hipStream_t)stream);
+        return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+    }
+    // the two calls in stream order, one workspace
+    st = fused_data_pass(d, dy, w_base, w_lvl, scale, dx, ws, ws_bytes, stream, true);
+    if (st != WTCONV_OK) return st;
+    return wtconv_bwd_weight(d, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, ws_bytes, stream);
 }
 
 size_t wtconv_naive_workspace_size(const wtconv_desc_t* d, int32_t op) {

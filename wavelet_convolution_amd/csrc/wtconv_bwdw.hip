@@ -1283,6 +1283,90 @@ __global__ __launch_bounds__(P::NT) void dw_bwdw_kernel(const T* __restrict__ x,
     }
 }
 
+// Single-pass backward for L = 0: each plane of x and dy is read once and
+// gives both dx (the correlation of dy with the taps turned by 180 degrees)
+// and the base-tap sums of the weight gradient. As dw_bwdw_kernel, with dy
+// kept bordered in LDS (the dx windows read its zero border) and the turned
+// taps staged once per workgroup.
+template <class P, typename T>
+__global__ __launch_bounds__(P::NT) void dw_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy,
+                                                       const float* __restrict__ w_base, T* __restrict__ dx,
+                                                       float* __restrict__ part, int B, int C, int bpc) {
+    constexpr int H = P::H, W = P::W, KB = P::KB, NT = P::NT, RB = P::RB, NPB = P::NPW, NW = NT / 64;
+    constexpr int PB = P::PB, XO = P::XO, SX = P::SX, VA = P::VA, NQ = P::NQ, LPB = P::LPB;
+    constexpr int NIB = P::NIB, KB2 = KB * KB, KB2P = P::KB2P;
+    constexpr int XS = round_up(P::XSIZE, 4), PL = 2 * XS, RED = NW * 4 * KB2;
+    __shared__ __attribute__((aligned(16))) float lds[(NPB * PL > RED ? NPB * PL : RED) + KB2P];
+    float* const WR = lds + (NPB * PL > RED ? NPB * PL : RED);   // turned taps
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = blockIdx.x % C, chunk = blockIdx.x / C;
+    const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
+    for (int t = tid; t < KB2P; t += NT) WR[t] = t < KB2 ? w_base[(size_t)c * KB2 + KB2 - 1 - t] : 0.f;
+    {
+        float4* const z = reinterpret_cast<float4*>(lds);
+        for (int t = tid; t < NPB * PL / 4; t += NT) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float acc[KB2];
+#pragma unroll
+    for (int t = 0; t < KB2; ++t) acc[t] = 0.f;
+    for (int b = b0; b < b1; b += NPB) {
+        __syncthreads();   // the zeros and taps, or the previous step's reads, are done
+        for (int q = tid; q < NPB * NQ; q += NT) {
+            const int p = udiv(q, NQ), r = q - p * NQ, row = udiv(r, W / VA), col = (r - row * (W / VA)) * VA;
+            float* const X = lds + p * PL + (PB + row) * SX + XO + col;
+            float* const D = X + XS;
+            if (b + p < b1) {
+                const size_t off = ((size_t)(b + p) * C + c) * H * W + (size_t)row * W + col;
+                RawVec<T, VA> vx, vd;
+                load_raw<T, VA>(x + off, vx);
+                load_raw<T, VA>(dy + off, vd);
+                store_lds<T, VA>(X, vx);
+                store_lds<T, VA>(D, vd);
+            } else {
+                float zero[VA] = {};
+                store_vec<VA>(X, zero);
+                store_vec<VA>(D, zero);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < P::MB; ++it) {
+            const int item = tid + it * NT;
+            if (!((NPB * NIB) % NT == 0 || item < NPB * NIB)) continue;
+            const int p = NPB == 1 ? 0 : udiv(item, NIB), r = item - p * NIB;
+            const int rb = udiv(r, LPB), w = r - rb * LPB, h0 = rb * RB;
+            if (!(LPB == W || w < W)) continue;
+            const float* const Xw = lds + p * PL + XO - PB + h0 * SX + w;   // window origin, x
+            taps_col<KB, RB, SX, SX>(Xw, Xw + XS + PB * SX + PB, acc);      // dy interior rows h0..
+            if (b + p < b1) {
+                float y[RB];
+                conv_col<KB, RB, SX>(Xw + XS, WR, y);   // the same window over bordered dy
+                T* __restrict__ dst = dx + ((size_t)(b + p) * C + c) * H * W + (size_t)h0 * W + w;
+#pragma unroll
+                for (int o = 0; o < RB; ++o) {
+                    if constexpr (sizeof(T) == 2) dst[o * W] = narrow_bf16(y[o]);
+                    else dst[o * W] = y[o];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < KB2; ++t) acc[t] = row_sum(acc[t]);
+    __syncthreads();   // LDS becomes reduction scratch
+    float* const red = lds;   // [NW * 4 rows][KB2]
+    if ((lane & 15) == 0) {
+        const int wr = wave * 4 + (lane >> 4);
+#pragma unroll
+        for (int t = 0; t < KB2; ++t) red[wr * KB2 + t] = acc[t];
+    }
+    __syncthreads();
+    for (int t = tid; t < KB2; t += NT) {
+        float v = 0.f;
+        for (int wr = 0; wr < NW * 4; ++wr) v += red[wr * KB2 + t];
+        part[((size_t)chunk * C + c) * KB2 + t] = v;
+    }
+}
+
 // planes per chunk: about four workgroups per CU in all
 static int dw_bw_bpc(int B, int C) { return chunk_units(B, C, cu_count() * 4); }
 
@@ -1308,6 +1392,29 @@ static hipError_t dw_bw_launch(const void* x, const void* dy, const float* w_lvl
                        (const float*)nullptr, dw_base, (float*)nullptr, (float*)nullptr);
     return hipGetLastError();
 }
+
+template <class P, typename T>
+static hipError_t dw_bwd_launch(const void* x, const void* dy, const float* w_base, void* dx, float* dw_base,
+                                void* ws, int B, int C, hipStream_t stream) {
+    const int bpc = dw_bw_bpc(B, C), nch = cdiv(B, bpc);
+    float* part = (float*)ws;
+    hipLaunchKernelGGL((dw_bwd_kernel<P, T>), dim3((unsigned)(nch * C)), dim3(P::NT), 0, stream, (const T*)x,
+                       (const T*)dy, w_base, (T*)dx, part, B, C, bpc);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(P::KB, 1, 0)), 0, stream,
+                       (const float*)part, nch, 0, (const float*)nullptr, 0, C, 0, P::KB, 1, (const float*)nullptr,
+                       (const float*)nullptr, dw_base, (float*)nullptr, (float*)nullptr);
+    return hipGetLastError();
+}
+
+typedef hipError_t (*bwd1_fn)(const void* x, const void* dy, const float* w_base, void* dx, float* dw_base,
+                              void* ws, int B, int C, hipStream_t stream);
+struct Bwd1Entry {
+    int H, W, KB;
+    bwd1_fn fn[2];
+    size_t (*ws)(int B, int C);
+};
 
 typedef hipError_t (*bwdw_fn)(const void*, const void*, const float*, const float*, float*, float*, float*,
                               void*, int, int, hipStream_t);
@@ -1399,6 +1506,30 @@ static const BwEntry kBwEntries[] = {
     WTC_BW_DW(DB_56_k5), WTC_BW_DW(DB_56_k7), WTC_BW_DW(DB_28_k5), WTC_BW_DW(DB_28_k7), WTC_BW_DW(DB_14_k5),
     WTC_BW_DW(DB_14_k7),
 };
+
+#define WTC_BWD1(PLAN) {PLAN::H, PLAN::W, PLAN::KB, {dw_bwd_launch<PLAN, float>, dw_bwd_launch<PLAN, bf16_t>}, dw_bw_ws<PLAN>}
+static const Bwd1Entry kBwd1Entries[] = {
+    WTC_BWD1(DB_56_k5), WTC_BWD1(DB_56_k7), WTC_BWD1(DB_28_k5),
+    WTC_BWD1(DB_28_k7), WTC_BWD1(DB_14_k5), WTC_BWD1(DB_14_k7),
+};
+
+static const Bwd1Entry* find_bwd1(int H, int W, int KB) {
+    for (const Bwd1Entry& e : kBwd1Entries)
+        if (e.H == H && e.W == W && e.KB == KB) return &e;
+    return nullptr;
+}
+
+size_t bwd_single_pass_workspace_bytes(int B, int C, int H, int W, int L, int KB) {
+    const Bwd1Entry* e = L == 0 ? find_bwd1(H, W, KB) : nullptr;
+    return e ? e->ws(B, C) : (size_t)-1;
+}
+
+hipError_t bwd_single_pass_launch(int B, int C, int H, int W, int KB, bool bf16, const void* x, const void* dy,
+                                  const float* w_base, void* dx, float* dw_base, void* ws, hipStream_t stream) {
+    const Bwd1Entry* e = find_bwd1(H, W, KB);
+    if (!e) return hipErrorInvalidValue;
+    return e->fn[bf16 ? 1 : 0](x, dy, w_base, dx, dw_base, ws, B, C, stream);
+}
 
 static const BwEntry* find_bw(int H, int W, int L, int KB, int K) {
     for (const BwEntry& e : kBwEntries)

@@ -58,9 +58,12 @@ class WTConvFunction(torch.autograd.Function):
         x, w_base, w_lvl, scale = ctx.saved_tensors
         dy = dy.to(x.dtype).contiguous(memory_format=_order(x))
         dx = dwb = dwl = dsc = None
-        if ctx.needs_input_grad[0]:
+        if ctx.needs_input_grad[0] and any(ctx.needs_input_grad[1:]):
+            # both results: one call (a single pass over x and dy where the library has one)
+            dx, (dwb, dwl, dsc) = _b.wtconv_bwd(x, dy, w_base, w_lvl, scale)
+        elif ctx.needs_input_grad[0]:
             dx = _b.wtconv_bwd_data(dy, w_base, w_lvl, scale)
-        if any(ctx.needs_input_grad[1:]):
+        elif any(ctx.needs_input_grad[1:]):
             dwb, dwl, dsc = _b.wtconv_bwd_weight(x, dy, int(w_base.shape[-1]), w_lvl, scale)
         return dx, dwb, dwl, dsc
 
