@@ -187,7 +187,7 @@ wtconv_status_t wtconv_naive_bwd_weight(const wtconv_desc_t *desc, const void *x
 /* Static description of a status code. */
 const char *wtconv_status_string(wtconv_status_t status);
 
-/* Library version, e.g. "0.2.0". */
+/* Library version, e.g. "0.3.0". */
 const char *wtconv_version(void);
 
 /* Measurement probes (not operations of the layer). They measure on the

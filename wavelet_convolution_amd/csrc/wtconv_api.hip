@@ -329,6 +329,6 @@ const char* wtconv_status_string(wtconv_status_t s) {
     }
 }
 
-const char* wtconv_version(void) { return "0.2.0"; }
+const char* wtconv_version(void) { return "0.3.0"; }
 
 }  // extern "C"
