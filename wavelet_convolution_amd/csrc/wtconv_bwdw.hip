@@ -1435,7 +1435,9 @@ typedef BwPlan<16, 16, 4, 3, 7> BP_16_L4_k37;
 typedef BwPlan<64, 64, 4, 7, 5> BP_64_L4_k75;
 
 // split plans: fine tiles + coarse planes of LL_{L0} sums (no base taps)
-typedef TileBwPlan<128, 128, 1, 1, 5, 5, 16> TB_128_L1_k55;
+// 32-row tiles where the halo is 4 rows (one fine level): 10 % faster than
+// 16 at 128² L1; with two fine levels (8-row halo) 16 rows are 4-8 % faster
+typedef TileBwPlan<128, 128, 1, 1, 5, 5, 32> TB_128_L1_k55;
 typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16> TB_128_L2_k55;
 typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16> TB_128_L2of3_k55;
 typedef TileBwPlan<128, 128, 2, 4, 5, 5, 16> TB_128_L2of4_k55;
