@@ -101,21 +101,34 @@ def max_threads() -> int:
 
 
 def haar_dwt(X) -> np.ndarray:
-    """One orthonormal 2x2 Haar analysis step: [H, W] -> [4, H/2, W/2]."""
+    """One orthonormal 2x2 Haar analysis step: [H, W] -> [4, ceil(H/2), ceil(W/2)].
+
+    An odd last row or column is paired with a zero one (the odd-grid reading
+    the layer takes), so the bands are ceil-sized; that is also the size the C
+    routine writes."""
     X = _f64(X)
+    if X.ndim != 2 or X.shape[0] < 1 or X.shape[1] < 1:
+        raise ValueError(f"haar_dwt takes a non-empty 2-D plane, got shape {X.shape}")
     H, W = X.shape
-    out = np.zeros((4, H // 2, W // 2))
+    out = np.zeros((4, (H + 1) // 2, (W + 1) // 2))
     _load().wto_haar_dwt(_p(X), H, W, _p(out))
     return out
 
 
-def haar_iwt(bands) -> np.ndarray:
-    """Inverse of haar_dwt: [4, h, w] -> [2h, 2w]."""
+def haar_iwt(bands, shape=None) -> np.ndarray:
+    """Inverse of haar_dwt: [4, h, w] -> [2h, 2w], or the top-left
+    shape = (H, W) of it (H in {2h-1, 2h}, W in {2w-1, 2w}): the crop back to
+    an odd plane that haar_dwt analysed."""
     bands = _f64(bands)
+    if bands.ndim != 3 or bands.shape[0] != 4:
+        raise ValueError(f"haar_iwt takes [4, h, w] bands, got shape {bands.shape}")
     _, h, w = bands.shape
+    H, W = (2 * h, 2 * w) if shape is None else (int(shape[0]), int(shape[1]))
+    if not (2 * h - 1 <= H <= 2 * h and 2 * w - 1 <= W <= 2 * w):
+        raise ValueError(f"crop {H}x{W} does not fit bands of {h}x{w}")
     out = np.zeros((2 * h, 2 * w))
     _load().wto_haar_iwt(_p(bands), h, w, _p(out))
-    return out
+    return np.ascontiguousarray(out[:H, :W])
 
 
 def _fwd_like(fn_name, x, w_base, w_lvl, scale):

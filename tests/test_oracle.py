@@ -62,6 +62,37 @@ def test_haar_band_semantics_on_textbook_patterns():
             np.testing.assert_allclose(bands[t], expect, atol=1e-15)
 
 
+def test_haar_odd_plane_hand_worked_3x3():
+    """The level-1 bands of the hand-worked 3x3 plane (its last row and column
+    paired with zeros), as derived by hand in the odd-plane fixture, and the
+    cropped inverse giving the 3x3 plane back."""
+    with open(os.path.join(GOLDEN, "hand_worked_3x3_odd_l1.json")) as f:
+        g = json.load(f)
+    X = np.array(g["x"], float)
+    bands = oracle.haar_dwt(X)
+    assert bands.shape == (4, 2, 2)
+    np.testing.assert_array_equal(bands, np.array(g["haar_bands_l1"]["bands"], float))
+    np.testing.assert_array_equal(oracle.haar_iwt(bands, X.shape), X)
+
+
+@pytest.mark.parametrize("H", range(1, 10))
+def test_haar_odd_planes_match_zero_padded_embedding(H):
+    """For every plane size up to 9 x 9: the bands of an odd plane equal those
+    of the plane padded with a zero row / column to even size, the cropped
+    inverse restores the plane exactly, and energy is kept. (A buffer sized
+    H//2 x W//2 would fail on every odd size here.)"""
+    rng = np.random.default_rng(100 + H)
+    for W in range(1, 10):
+        X = rng.standard_normal((H, W))
+        E = np.zeros((H + H % 2, W + W % 2))
+        E[:H, :W] = X
+        bands = oracle.haar_dwt(X)
+        assert bands.shape == (4, (H + 1) // 2, (W + 1) // 2)
+        np.testing.assert_allclose(bands, oracle.haar_dwt(E), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(oracle.haar_iwt(bands, (H, W)), X, rtol=0, atol=1e-14)
+        assert abs(np.sum(bands ** 2) - np.sum(X ** 2)) <= 1e-12 * max(1.0, np.sum(X ** 2))
+
+
 # --------------------------------------------------------- golden (hand)
 
 def _golden():
