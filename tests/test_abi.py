@@ -157,23 +157,76 @@ def test_huge_channel_counts_leave_the_multi_image_kernels(lib):
         ctypes.byref(huge), 0) > 0
 
 
-def test_binding_checks_parameter_buffers():
-    """The library takes plain pointers, so the binding refuses parameter and
-    gradient buffers of the wrong shape, dtype or order before calling it."""
+def test_binding_refuses_host_tensors(monkeypatch):
+    """The library takes plain device pointers, so the binding refuses any CPU
+    tensor it would pass (activations, parameters, outputs, gradients,
+    workspace) before it even loads the library: a host pointer in a kernel
+    argument would be a GPU memory fault."""
     import torch
     from wavelet_convolution_amd import binding as wt
+
+    def no_library():
+        raise AssertionError("the library must not be reached with a host tensor")
+
+    monkeypatch.setattr(wt, "load_library", no_library)
     x = torch.zeros(1, 4, 8, 8)
     wb, wl, sc = torch.zeros(4, 5, 5), torch.zeros(1, 4, 4, 3, 3), torch.zeros(1, 4, 4)
-    bad = [(torch.zeros(3, 5, 5), wl, sc), (wb.double(), wl, sc), (wb, torch.zeros(1, 4, 4, 3, 3)[..., ::2, :], sc),
-           (wb, wl, torch.zeros(2, 4, 4))]
+    grads = (torch.zeros(4, 5, 5), torch.zeros(1, 4, 4, 3, 3), torch.zeros(1, 4, 4))
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    calls = [
+        lambda: wt.wtconv_fwd(x, wb, wl, sc),
+        lambda: wt.wtconv_fwd(x, wb, wl, sc, y=torch.zeros_like(x)),
+        lambda: wt.wtconv_fwd(x, wb, wl, sc, ws=ws),
+        lambda: wt.wtconv_bwd_data(x, wb, wl, sc, dx=torch.zeros_like(x)),
+        lambda: wt.wtconv_naive_fwd(x, wb, wl, sc),
+        lambda: wt.wtconv_bwd_weight(x, x, 5, wl, sc, out=grads),
+        lambda: wt.wtconv_bwd_weight(x, x, 5, wl, sc, ws=ws),
+        lambda: wt.wtconv_naive_bwd_weight(x, x, 5, wl, sc),
+        lambda: wt.wtconv_bwd(x, x, wb, wl, sc, dx=torch.zeros_like(x), out=grads, ws=ws),
+        lambda: wt.wtconv_peak_fma(torch.zeros(256), 1, 1),
+        lambda: wt.wtconv_peak_copy(torch.zeros(16), torch.zeros(16)),
+        lambda: wt.wtconv_fwd("not a tensor", wb, wl, sc),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="GPU|activations' GPU|cuda"):
+            call()
+
+
+@pytest.mark.gpu
+def test_binding_checks_buffers_on_the_gpu():
+    """On the GPU: parameter, output and gradient buffers of the wrong shape,
+    dtype, order or device are refused before the library is called, and so
+    is a host tensor among GPU ones (output, workspace, dy, gradient)."""
+    import torch
+    from wavelet_convolution_amd import binding as wt
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda")
+    x = torch.zeros(1, 4, 8, 8, device=dev)
+    wb, wl, sc = (torch.zeros(4, 5, 5, device=dev), torch.zeros(1, 4, 4, 3, 3, device=dev),
+                  torch.zeros(1, 4, 4, device=dev))
+    bad = [(torch.zeros(3, 5, 5, device=dev), wl, sc), (wb.double(), wl, sc),
+           (wb, torch.zeros(1, 4, 4, 3, 3, device=dev)[..., ::2, :], sc), (wb, wl, torch.zeros(2, 4, 4, device=dev)),
+           (wb.cpu(), wl, sc)]
     for args in bad:
         with pytest.raises(ValueError):
             wt.wtconv_fwd(x, *args)
+    grads = (torch.zeros(4, 5, 5, device=dev), torch.zeros(1, 4, 4, 3, 3, device=dev),
+             torch.zeros(1, 4, 4, device=dev))
     with pytest.raises(ValueError):
-        wt.wtconv_bwd_weight(x, x, 5, wl, sc, out=(torch.zeros(4, 5, 5), torch.zeros(1, 4, 4, 3, 3),
-                                                     torch.zeros(1, 4, 5)))
+        wt.wtconv_bwd_weight(x, x, 5, wl, sc, out=(grads[0], grads[1], torch.zeros(1, 4, 5, device=dev)))
     with pytest.raises(ValueError):
-        wt.wtconv_fwd(x, wb, wl, sc, y=torch.zeros(1, 4, 8, 8, dtype=torch.bfloat16))
+        wt.wtconv_bwd_weight(x, x, 5, wl, sc, out=(grads[0].cpu(), grads[1], grads[2]))
+    with pytest.raises(ValueError):
+        wt.wtconv_bwd_weight(x, x.cpu(), 5, wl, sc)
+    with pytest.raises(ValueError):
+        wt.wtconv_fwd(x, wb, wl, sc, y=torch.zeros(1, 4, 8, 8, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        wt.wtconv_fwd(x, wb, wl, sc, y=torch.zeros(1, 4, 8, 8))
+    with pytest.raises(ValueError):
+        wt.wtconv_fwd(x, wb, wl, sc, ws=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        wt.wtconv_bwd(x, x, wb, wl, sc, dx=torch.zeros(1, 4, 8, 8))
 
 
 def test_whole_backward_workspace(lib):

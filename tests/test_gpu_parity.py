@@ -354,7 +354,8 @@ def test_level_zero_fused_kernels(shape):
             assert rel_err(to_f64(dwb), odwb) <= TOL["f32"]
 
 
-@pytest.mark.parametrize("shape", [(3, 4, 56, 56, 0, 5, 5), (5, 3, 28, 28, 0, 7, 5), (17, 3, 14, 14, 0, 5, 5),
+@pytest.mark.parametrize("shape", [(3, 4, 56, 56, 0, 5, 5), (2, 3, 56, 56, 0, 7, 5), (5, 3, 28, 28, 0, 7, 5),
+                                   (4, 3, 28, 28, 0, 5, 5), (17, 3, 14, 14, 0, 5, 5), (5, 2, 14, 14, 0, 7, 3),
                                    (2, 3, 56, 56, 3, 5, 5), (2, 3, 13, 11, 2, 5, 3)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_whole_backward_equals_the_two_calls(shape):

@@ -1,8 +1,9 @@
 """Thin ctypes binding of libwtconv.so (argument marshalling only).
 
-Every function takes torch tensors on the GPU, checks nothing beyond what is
-needed to build the C descriptor, and calls the C-ABI entry point of the same
-name on the current stream. Validation and every step of the computation
+Every function takes torch tensors on the GPU, checks what the plain pointers
+of the C ABI cannot carry (device, shape, dtype and memory order of every
+tensor it passes), and calls the C-ABI entry point of the same name on the
+current stream. Validation and every step of the computation
 happen in the library. The library must exist: there is no fallback.
 """
 from __future__ import annotations
@@ -110,6 +111,26 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _require_gpu(act: torch.Tensor, **tensors) -> None:
+    """Every pointer handed to the library must be device memory on the
+    activation's GPU: a host pointer in a kernel argument is a memory fault,
+    so CPU tensors (or tensors on another device) are refused here, before
+    anything else is looked at."""
+    if not isinstance(act, torch.Tensor) or not act.is_cuda:
+        dev = act.device if isinstance(act, torch.Tensor) else type(act).__name__
+        raise ValueError(f"activations must be a GPU tensor, got one on {dev}")
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        for i, u in enumerate(t if isinstance(t, (tuple, list)) else (t,)):
+            if u is None:
+                continue
+            if not isinstance(u, torch.Tensor) or not u.is_cuda or u.device != act.device:
+                where = u.device if isinstance(u, torch.Tensor) else type(u).__name__
+                label = name if not isinstance(t, (tuple, list)) else f"{name}[{i}]"
+                raise ValueError(f"{label} must be a tensor on {act.device} (the activations' GPU), got {where}")
+
+
 def _check_f32(name: str, t, shape, like: torch.Tensor) -> None:
     """The library reads and writes parameter-shaped buffers through plain
     pointers: their shape, dtype, order and device are checked here."""
@@ -174,6 +195,7 @@ def _ws_ptr(ws: torch.Tensor | None) -> int:
 
 
 def _data_pass(name: str, naive: bool, op: int, act, w_base, w_lvl, scale, out, ws, stream):
+    _require_gpu(act, w_base=w_base, w_lvl=w_lvl, scale=scale, out=out, ws=ws)
     lib = load_library()
     levels, kb, k = _dims(w_base, w_lvl)
     d = _desc(act, levels, kb, k)
@@ -209,6 +231,7 @@ def wtconv_naive_bwd_data(dy, w_base, w_lvl, scale, dx=None, ws=None, stream=Non
 
 
 def _bwd_weight(name: str, naive: bool, x, dy, w_base_shape_kb, w_lvl, scale, out, ws, stream):
+    _require_gpu(x, dy=dy, w_lvl=w_lvl, scale=scale, out=out, ws=ws)
     lib = load_library()
     levels = int(w_lvl.shape[0])
     k = int(w_lvl.shape[-1])
@@ -245,12 +268,14 @@ def wtconv_naive_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stre
 
 def wtconv_peak_fma(out: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
     """Enqueue the FMA-rate probe; returns the flops it performs."""
+    _require_gpu(out)
     _check(load_library().wtconv_peak_fma(_ptr(out), int(blocks), int(iters), _stream(stream)))
     return 2 * 16 * int(iters) * 256 * int(blocks)
 
 
 def wtconv_peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
     """Enqueue the copy probe over src's bytes; returns the HBM bytes moved."""
+    _require_gpu(src, dst=dst)
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst is smaller than src")
@@ -262,6 +287,7 @@ def wtconv_bwd(x, dy, w_base, w_lvl, scale, dx=None, out=None, ws=None, stream=N
     """(dx, (dW_base, dW_lvl, dscale)) in one call: a single pass over x and
     dy where the library has one (L = 0 on its planned planes), else the two
     backward calls on one workspace."""
+    _require_gpu(x, dy=dy, w_base=w_base, w_lvl=w_lvl, scale=scale, dx=dx, out=out, ws=ws)
     lib = load_library()
     levels, kb, k = _dims(w_base, w_lvl)
     d = _desc(x, levels, kb, k)
