@@ -44,8 +44,17 @@ CONFIGS = {
     "depthwise56": WorkloadConfig("depthwise56", 64, 96, 56, 56, 0, 5, 5, "bf16"),
 }
 
-# the workload the headline images/s figure is quoted on
-HEADLINE = "stage1_56"
+# the workload the headline images/s figure is quoted on: the largest
+# single-GPU configuration (16 x 256 x 256², L4, 7x7 base, 5x5 levels)
+HEADLINE = "large256"
+
+# the bar workloads besides the headline (ConvNeXt stage shapes and the level
+# sweep), each timed briefly in the same run
+BAR_WORKLOADS = ("stage1_56", "stage2_28", "stage3_14", "sweep128_L1", "sweep128_L2", "sweep128_L3",
+                 "sweep128_L4", "sweep128_L5")
+
+# the drop-in block timed as context: a ConvNeXt-style block at the stage-1 shape
+BLOCK_WORKLOAD = "stage1_56"
 
 
 def get_config(name: str) -> WorkloadConfig:
