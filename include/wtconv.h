@@ -79,8 +79,14 @@ typedef enum {
     WTCONV_ERR_UNSUPPORTED_SHAPE = 2,  /* even or unsupported k, L out of
                                           range, or H*W above 2^30 */
     WTCONV_ERR_WORKSPACE = 3,          /* ws too small or misaligned */
-    WTCONV_ERR_LAUNCH = 4              /* the HIP runtime rejected a launch */
+    WTCONV_ERR_LAUNCH = 4,             /* the HIP runtime rejected a launch */
+    WTCONV_ERR_SCRATCH_LIMIT = 5       /* wtconv_bwd_weight_noalloc: the call needs
+                                          more than WTCONV_NOALLOC_SCRATCH_BYTES */
 } wtconv_status_t;
+
+/* Size of the static device scratch array of wtconv_bwd_weight_noalloc (one
+   per GPU the library runs on, held until the process ends). */
+#define WTCONV_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef enum {
     WTCONV_OP_FWD = 0,
@@ -147,6 +153,27 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t *desc, const void *x,
                                   const float *scale, float *dw_base,
                                   float *dw_lvl, float *dscale, void *ws,
                                   size_t ws_bytes, void *stream);
+
+/* Backward weight without allocation, for callers that cannot allocate
+   device memory (code under HIP graph capture, tight serving loops, harnesses
+   that forbid allocation): the same kernels, results and semantics as
+   wtconv_bwd_weight (bit for bit), with the scratch that call takes as a
+   workspace (per-chunk partial sums, the level-split planes, channels-last
+   copies) held in a static device array of WTCONV_NOALLOC_SCRATCH_BYTES
+   (64 MiB) instead. A call whose wtconv_workspace_size(desc,
+   WTCONV_OP_BWD_WEIGHT) exceeds that returns WTCONV_ERR_SCRATCH_LIMIT and
+   enqueues nothing (the stage-shape and 128x128 workloads fit; 16 x 256 x
+   256^2 at L = 4 does not). It calls no allocating routine; its first call on
+   a device looks up that device's copy of the array (hipGetSymbolAddress)
+   and keeps its address. Every call on one device shares that device's
+   array: calls that overlap on one GPU (on different streams, or from
+   different threads, without ordering) race on it and must not be made.
+   Nothing in the array needs to start at zero (every word read was written
+   earlier in the same call). */
+wtconv_status_t wtconv_bwd_weight_noalloc(const wtconv_desc_t *desc, const void *x,
+                                          const void *dy, const float *w_lvl,
+                                          const float *scale, float *dw_base,
+                                          float *dw_lvl, float *dscale, void *stream);
 
 /* Whole backward pass: dx (as wtconv_bwd_data) and the weight gradients (as
    wtconv_bwd_weight) in one call. For L = 0 on the planes its kernel covers

@@ -64,6 +64,8 @@ def load_library() -> ctypes.CDLL:
                 fn = getattr(lib, name)
                 fn.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]
                 fn.restype = ctypes.c_int
+            lib.wtconv_bwd_weight_noalloc.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V]
+            lib.wtconv_bwd_weight_noalloc.restype = ctypes.c_int
             lib.wtconv_bwd.argtypes = [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]
             lib.wtconv_bwd.restype = ctypes.c_int
             lib.wtconv_peak_fma.argtypes = [_V, ctypes.c_int32, ctypes.c_int32, _V]
@@ -260,6 +262,32 @@ def _bwd_weight(name: str, naive: bool, x, dy, w_base_shape_kb, w_lvl, scale, ou
 def wtconv_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stream=None):
     """(dW_base, dW_lvl, dscale) for kernels of size k_base (base) and w_lvl's."""
     return _bwd_weight("wtconv_bwd_weight", False, x, dy, k_base, w_lvl, scale, out, ws, stream)
+
+
+def wtconv_bwd_weight_noalloc(x, dy, k_base, w_lvl, scale, out=None, stream=None):
+    """As wtconv_bwd_weight, with the library's static scratch array instead
+    of a workspace (the C entry point allocates nothing; outputs are
+    allocated here when `out` is None). Raises WTConvError
+    (WTCONV_ERR_SCRATCH_LIMIT) when the call needs more than 64 MiB."""
+    _require_gpu(x, dy=dy, w_lvl=w_lvl, scale=scale, out=out)
+    lib = load_library()
+    levels, k, kb = int(w_lvl.shape[0]), int(w_lvl.shape[-1]), int(k_base)
+    d = _desc(x, levels, kb, k)
+    _same_layout(x, dy)
+    _check_params(x, None, w_lvl, scale, levels, kb, k)
+    C = x.shape[1]
+    if out is None:
+        dev = x.device
+        out = (torch.empty((C, kb, kb), dtype=torch.float32, device=dev),
+               torch.empty((levels, C, 4, k, k), dtype=torch.float32, device=dev),
+               torch.empty((levels, C, 4), dtype=torch.float32, device=dev))
+    dwb, dwl, dsc = out
+    _check_f32("dw_base", dwb, (C, kb, kb), x)
+    _check_f32("dw_lvl", dwl, (levels, C, 4, k, k), x)
+    _check_f32("dscale", dsc, (levels, C, 4), x)
+    _check(lib.wtconv_bwd_weight_noalloc(ctypes.byref(d), _ptr(x), _ptr(dy), _ptr(w_lvl), _ptr(scale), _ptr(dwb),
+                                         _ptr(dwl), _ptr(dsc), _stream(stream)))
+    return out
 
 
 def wtconv_naive_bwd_weight(x, dy, k_base, w_lvl, scale, out=None, ws=None, stream=None):

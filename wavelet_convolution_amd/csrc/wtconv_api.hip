@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/wtconv.h"
 #include "wtconv_plans.h"
 #include "wtconv_bwdw.h"
@@ -173,6 +175,84 @@ size_t bwd_workspace(const wtconv_desc_t* d) {
     return a > b ? a : b;
 }
 
+
+// Backward weight on a validated route. With `static_ws` set, the workspace
+// is the library's static scratch array (the no-allocation entry point): the
+// call's need is checked against its size first, then its device address is
+// looked up; `ws` and `ws_bytes` are ignored.
+wtconv_status_t bwd_weight_pass(const wtconv_desc_t* d, const void* x, const void* dy, const float* w_lvl,
+                                const float* scale, float* dw_base, float* dw_lvl, float* dscale, void* ws,
+                                size_t ws_bytes, void* stream, void* (*static_ws)(wtconv_status_t*)) {
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (d->B > 0 && (!x || !dy)) return WTCONV_ERR_INVALID_ARG;   // never read for an empty batch
+    if (!dw_base) return WTCONV_ERR_INVALID_ARG;
+    if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dw_base)) return WTCONV_ERR_INVALID_ARG;
+    if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
+    st = check_params(d, nullptr, w_lvl, scale, false);
+    if (st != WTCONV_OK) return st;
+    const Route r = route(d, WTCONV_OP_BWD_WEIGHT);
+    if (static_ws) {
+        if (r.need > ws_bytes) return WTCONV_ERR_SCRATCH_LIMIT;
+        ws = static_ws(&st);
+        if (st != WTCONV_OK) return st;
+    }
+    if (!ws_ok(r, ws, ws_bytes)) return WTCONV_ERR_WORKSPACE;
+    const bool bf16 = d->dtype == WTCONV_BF16;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t err;
+    if (r.bw) {
+        const void *kx = x, *kdy = dy;
+        if (r.copies) {   // planar copies of x and dy, after the kernels' partial sums
+            kx = copy_slot(r, d, ws, 0);
+            kdy = copy_slot(r, d, ws, 1);
+            err = wtc::nhwc_to_nchw(x, (void*)kx, d->B, d->C, d->H, d->W, bf16, s);
+            if (err == hipSuccess) err = wtc::nhwc_to_nchw(dy, (void*)kdy, d->B, d->C, d->H, d->W, bf16, s);
+            if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
+        }
+        err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, bf16, kx, kdy, w_lvl,
+                               scale, dw_base, dw_lvl, dscale, ws, s);
+    } else   // no fused plan for this shape (or an empty batch): the generic chain
+        err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                     d->dtype == WTCONV_BF16, d->layout == WTCONV_NHWC, x, dy, w_lvl, scale,
+                                     dw_base, dw_lvl, dscale, ws, s);
+    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+}
+
+// Scratch of the no-allocation entry point: one array per device, held
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory, so it is never passed to a kernel: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and that address is what the kernels get. Every call on a device
+// shares its array and leaves its contents behind; the weight-gradient
+// kernels overwrite every word they read (partial sums, level-split LL
+// planes, layout copies), so nothing in it has to start at zero. Calls that
+// overlap on one device race on the array.
+__device__ __align__(256) static unsigned char scratch[WTCONV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_device_ptr(wtconv_status_t* st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *st = WTCONV_ERR_LAUNCH;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            *st = WTCONV_ERR_LAUNCH;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *st = WTCONV_OK;
+    return g_scratch_ptr[dev];
+}
 }  // namespace
 
 extern "C" {
@@ -200,36 +280,16 @@ wtconv_status_t wtconv_bwd_weight(const wtconv_desc_t* d, const void* x, const v
                                   const float* w_lvl, const float* scale, float* dw_base,
                                   float* dw_lvl, float* dscale, void* ws, size_t ws_bytes,
                                   void* stream) {
-    wtconv_status_t st = check_desc(d);
-    if (st != WTCONV_OK) return st;
-    if (d->B > 0 && (!x || !dy)) return WTCONV_ERR_INVALID_ARG;   // never read for an empty batch
-    if (!dw_base) return WTCONV_ERR_INVALID_ARG;
-    if (d->levels > 0 && (!dw_lvl || !dscale)) return WTCONV_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(dy) || !aligned16(dw_base)) return WTCONV_ERR_INVALID_ARG;
-    if ((dw_lvl && !aligned16(dw_lvl)) || (dscale && !aligned16(dscale))) return WTCONV_ERR_INVALID_ARG;
-    st = check_params(d, nullptr, w_lvl, scale, false);
-    if (st != WTCONV_OK) return st;
-    const Route r = route(d, WTCONV_OP_BWD_WEIGHT);
-    if (!ws_ok(r, ws, ws_bytes)) return WTCONV_ERR_WORKSPACE;
-    const bool bf16 = d->dtype == WTCONV_BF16;
-    const hipStream_t s = (hipStream_t)stream;
-    hipError_t err;
-    if (r.bw) {
-        const void *kx = x, *kdy = dy;
-        if (r.copies) {   // planar copies of x and dy, after the kernels' partial sums
-            kx = copy_slot(r, d, ws, 0);
-            kdy = copy_slot(r, d, ws, 1);
-            err = wtc::nhwc_to_nchw(x, (void*)kx, d->B, d->C, d->H, d->W, bf16, s);
-            if (err == hipSuccess) err = wtc::nhwc_to_nchw(dy, (void*)kdy, d->B, d->C, d->H, d->W, bf16, s);
-            if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
-        }
-        err = wtc::bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, bf16, kx, kdy, w_lvl,
-                               scale, dw_base, dw_lvl, dscale, ws, s);
-    } else   // no fused plan for this shape (or an empty batch): the generic chain
-        err = wtc::naive_bwdw_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
-                                     d->dtype == WTCONV_BF16, d->layout == WTCONV_NHWC, x, dy, w_lvl, scale,
-                                     dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
-    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+    return bwd_weight_pass(d, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, ws_bytes, stream, nullptr);
+}
+
+wtconv_status_t wtconv_bwd_weight_noalloc(const wtconv_desc_t* d, const void* x, const void* dy,
+                                          const float* w_lvl, const float* scale, float* dw_base,
+                                          float* dw_lvl, float* dscale, void* stream) {
+    // the static scratch stands in for the workspace; bwd_weight_pass checks
+    // the call's need against its size before asking for its address
+    return bwd_weight_pass(d, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, nullptr, WTCONV_NOALLOC_SCRATCH_BYTES,
+                           stream, scratch_device_ptr);
 }
 
 wtconv_status_t wtconv_bwd(const wtconv_desc_t* d, const void* x, const void* dy, const float* w_base,
@@ -325,6 +385,9 @@ const char* wtconv_status_string(wtconv_status_t s) {
     case WTCONV_ERR_UNSUPPORTED_SHAPE: return "WTCONV_ERR_UNSUPPORTED_SHAPE: unsupported kernel size or levels, or a plane above 2^30 elements";
     case WTCONV_ERR_WORKSPACE: return "WTCONV_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
     case WTCONV_ERR_LAUNCH: return "WTCONV_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case WTCONV_ERR_SCRATCH_LIMIT:
+        return "WTCONV_ERR_SCRATCH_LIMIT: the call needs more scratch than the no-allocation entry point's "
+               "static buffer holds (WTCONV_NOALLOC_SCRATCH_BYTES, 64 MiB)";
     default: return "WTCONV: unknown status";
     }
 }
