@@ -14,6 +14,18 @@ def rel_err(got, ref) -> float:
     return float(np.abs(got - ref).max() / (denom if denom > 0 else 1.0))
 
 
+def elem_err(got, ref, floor: float = 1e-3) -> float:
+    """Elementwise max relative error with a floor: max_i |got_i - ref_i| /
+    max(|ref_i|, floor * max|ref|). Logged beside the normwise measure (it is
+    not the parity bar): an error confined to small elements shows up here."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.abs(ref).max()
+    if scale == 0:
+        return float(np.abs(got).max())
+    return float((np.abs(got - ref) / np.maximum(np.abs(ref), floor * scale)).max())
+
+
 def to_device(inp, device="cuda"):
     """(x, dy, w_base, w_lvl, scale) as torch tensors on the GPU."""
     import torch

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests._util import TOL, rel_err, to_device, to_f64
+from tests._util import TOL, elem_err, rel_err, to_device, to_f64
 from wavelet_convolution_amd.configs import CONFIGS
 from wavelet_convolution_amd.inputs import make_inputs
 
@@ -39,12 +39,15 @@ def test_full_size_sampled(name):
     xw, dyw = inp.act_f64("x"), inp.act_f64("dy")
     wbf, wlf, scf = inp.params_f64()
     worst = {"y": 0.0, "dx": 0.0, "dw_base": 0.0, "dw_lvl": 0.0, "dscale": 0.0}
+    worst_el = dict(worst)   # elementwise, floor 1e-3 max|o| (logged, not the bar)
     for b, c in _planes(cfg.B, cfg.C):
         pw = (wbf[c:c + 1], wlf[:, c:c + 1], scf[:, c:c + 1])
         oy = oracle.fwd(xw[b:b + 1, c:c + 1], *pw)
         odx = oracle.bwd_data(dyw[b:b + 1, c:c + 1], *pw)
-        ey, edx = rel_err(to_f64(y[b:b + 1, c:c + 1]), oy), rel_err(to_f64(dx[b:b + 1, c:c + 1]), odx)
+        gy, gdx = to_f64(y[b:b + 1, c:c + 1]), to_f64(dx[b:b + 1, c:c + 1])
+        ey, edx = rel_err(gy, oy), rel_err(gdx, odx)
         worst["y"], worst["dx"] = max(worst["y"], ey), max(worst["dx"], edx)
+        worst_el["y"], worst_el["dx"] = max(worst_el["y"], elem_err(gy, oy)), max(worst_el["dx"], elem_err(gdx, odx))
         assert ey <= tol and edx <= tol, (b, c, ey, edx)
     dwb, dwl, dsc = (to_f64(g) for g in grads)
     for c in sorted({0, cfg.C - 1, cfg.C // 2}):
@@ -56,7 +59,10 @@ def test_full_size_sampled(name):
                 continue
             e = rel_err(got, ref)
             worst[key] = max(worst[key], e)
+            worst_el[key] = max(worst_el[key], elem_err(got, ref))
             assert e <= TOL["f32"], (c, key, e)
     print(f"[fullsize] {name} max rel err: " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()), flush=True)
+    print(f"[fullsize] {name} elementwise (floor 1e-3 max|o|): "
+          + " ".join(f"{k} {v:.2e}" for k, v in worst_el.items()), flush=True)
     # properties that hold everywhere: finite outputs
     assert torch.isfinite(y.float()).all() and torch.isfinite(dx.float()).all()

@@ -31,38 +31,33 @@ namespace wtc {
 // column strip of dy-side values against its window of x-side values. Lanes
 // of a wavefront take consecutive columns: every load is a run of
 // consecutive LDS words across the wavefront, free of bank conflicts.
-#ifndef WTC_TAPS_AHEAD
-#define WTC_TAPS_AHEAD 1
-#endif
 template <int K, int R, int SU, int SV, int NA, typename VT>
 __device__ __forceinline__ void taps_col(const float* u, const VT* v, float (&acc)[NA]) {
     static_assert(NA >= K * K, "accumulator slot too small");
-    constexpr int NR = R + K - 1;       // window rows
-    constexpr int D = WTC_TAPS_AHEAD;   // rows requested ahead of their use
+    constexpr int NR = R + K - 1;   // window rows
     __builtin_amdgcn_sched_barrier(0);
     float vt[R];
 #pragma unroll
     for (int o = 0; o < R; ++o) vt[o] = widen(v[o * SV]);
-    // a ring of D + 1 window rows: row r + D is requested before row r's
-    // multiply-adds, so LDS latency hides behind D rows of them
+    // window rows double-buffered: row r + 1 is requested before row r's
+    // multiply-adds, so its LDS latency hides behind them (requesting two to
+    // five rows ahead measured no faster)
     const RowAddr<SU, NR> row(u);
-    float win[D + 1][K];
+    float win[2][K];
 #pragma unroll
-    for (int r = 0; r < D && r < NR; ++r)
-#pragma unroll
-        for (int n = 0; n < K; ++n) win[r][n] = row(r, n);
+    for (int n = 0; n < K; ++n) win[0][n] = row(0, n);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        if (r + D < NR) {
+        if (r + 1 < NR) {
 #pragma unroll
-            for (int n = 0; n < K; ++n) win[(r + D) % (D + 1)][n] = row(r + D, n);
+            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = row(r + 1, n);
         }
 #pragma unroll
         for (int o = 0; o < R; ++o) {
             const int m = r - o;
             if (m < 0 || m >= K) continue;
 #pragma unroll
-            for (int n = 0; n < K; ++n) acc[m * K + n] = __builtin_fmaf(vt[o], win[r % (D + 1)][n], acc[m * K + n]);
+            for (int n = 0; n < K; ++n) acc[m * K + n] = __builtin_fmaf(vt[o], win[r & 1][n], acc[m * K + n]);
         }
     }
     pin_regs(acc);
@@ -697,7 +692,11 @@ __global__ __launch_bounds__(1024) void bwdw_finalize(const float* __restrict__ 
                                                       float* __restrict__ dw_base,
                                                       float* __restrict__ dw_lvl,
                                                       float* __restrict__ dscale) {
-    __shared__ float WG[4 * 5 * 49];   // w_lvl * G per level tap
+    // w_lvl * G per level tap, sized for every shape the ABI accepts (the
+    // host rejects L > 5 and kernels above 15 before any launch)
+    constexpr int kMaxLevels = 5, kMaxK = 15;
+    __shared__ float WG[4 * kMaxLevels * kMaxK * kMaxK];
+    if (L > kMaxLevels || K > kMaxK) return;
     const int c = blockIdx.x, tid = threadIdx.x;
     const int kb2 = KB * KB, k2 = K * K, taps = kb2 + 4 * L * k2;
     const int TA = kb2 + 4 * LA * k2, TB = taps - TA;
@@ -1425,9 +1424,8 @@ struct BwEntry {
     size_t (*ws)(int B, int C);
 };
 
+// whole-plane plans of the small test shapes
 typedef BwPlan<32, 32, 2, 5, 5> BP_32_L2_k55;
-typedef BwPlan<56, 56, 3, 5, 5> BP_56_L3_k55;
-typedef BwPlan<28, 28, 2, 5, 5, 2, 4> BP_28_L2_k55;
 typedef BwPlan<14, 14, 1, 5, 5, 1, 8> BP_14_L1_k55;
 typedef BwPlan<32, 32, 3, 7, 5> BP_32_L3_k75;
 typedef BwPlan<24, 40, 3, 3, 3> BP_24x40_L3_k33;
@@ -1452,22 +1450,13 @@ typedef BwPlan<64, 64, 2, 1, 5> CB_64_L2_k5;
 typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8> TB_64_L2of4_k33;
 typedef BwPlan<16, 16, 2, 1, 3, 2, 8> CB_16_L2_k3;
 typedef TileBwPlan<64, 64, 1, 2, 5, 5, 16> TB_64_L1of2_k55;
-typedef BwPlan<32, 32, 1, 1, 5, 1, 4> CB_32_L1_k5b;
 
-// whole planes split by level (fine: base + level 1; coarse: the rest)
+// whole planes split by level (fine: base + level 1; coarse: the rest, on
+// the level-1 LL planes, several planes per step)
 typedef BwPlan<56, 56, 1, 5, 5, 3> WP_56_L1of3_k55;
-#ifndef WTC_CB28_NPB
-#define WTC_CB28_NPB 4
-#endif
-typedef BwPlan<28, 28, 2, 1, 5, 2, WTC_CB28_NPB> CB_28_L2_k5;
-#ifndef WTC_BW28_NPB
-#define WTC_BW28_NPB 2
-#endif
-#ifndef WTC_BW14C_NPB
-#define WTC_BW14C_NPB 8
-#endif
-typedef BwPlan<28, 28, 1, 5, 5, 2, WTC_BW28_NPB> WP_28_L1of2_k55;
-typedef BwPlan<14, 14, 1, 1, 5, 1, WTC_BW14C_NPB> CB_14_L1_k5;
+typedef BwPlan<28, 28, 2, 1, 5, 2, 4> CB_28_L2_k5;
+typedef BwPlan<28, 28, 1, 5, 5, 2, 2> WP_28_L1of2_k55;
+typedef BwPlan<14, 14, 1, 1, 5, 1, 8> CB_14_L1_k5;
 
 typedef DwPlan<56, 56, 5, 256, 14, 1> DB_56_k5;
 typedef DwPlan<56, 56, 7, 256, 14, 1> DB_56_k7;
@@ -1487,26 +1476,14 @@ typedef DwPlan<14, 14, 7, 256, 14, 16> DB_14_k7;
     {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K,                                                   \
      {split_bw_launch<FPL, CPL, float>, split_bw_launch<FPL, CPL, bf16_t>}, split_bw_ws<FPL, CPL>}
 
-#ifndef WTC_BW56_SPLIT
-#define WTC_BW56_SPLIT 1
-#endif
-#ifndef WTC_BW28_SPLIT
-#define WTC_BW28_SPLIT 1
-#endif
 static const BwEntry kBwEntries[] = {
-#if WTC_BW56_SPLIT
-    WTC_BW_PLANESPLIT(WP_56_L1of3_k55, CB_28_L2_k5),
-#endif
-#if WTC_BW28_SPLIT
-    WTC_BW_PLANESPLIT(WP_28_L1of2_k55, CB_14_L1_k5),
-#endif
-    WTC_BW_WHOLE(BP_32_L2_k55), WTC_BW_WHOLE(BP_56_L3_k55),    WTC_BW_WHOLE(BP_28_L2_k55),
-    WTC_BW_WHOLE(BP_14_L1_k55), WTC_BW_WHOLE(BP_32_L3_k75),    WTC_BW_WHOLE(BP_24x40_L3_k33),
-    WTC_BW_WHOLE(BP_16_L4_k37), WTC_BW_WHOLE(BP_64_L4_k75),
+    WTC_BW_PLANESPLIT(WP_56_L1of3_k55, CB_28_L2_k5), WTC_BW_PLANESPLIT(WP_28_L1of2_k55, CB_14_L1_k5),
+    WTC_BW_WHOLE(BP_32_L2_k55), WTC_BW_WHOLE(BP_14_L1_k55),    WTC_BW_WHOLE(BP_32_L3_k75),
+    WTC_BW_WHOLE(BP_24x40_L3_k33), WTC_BW_WHOLE(BP_16_L4_k37), WTC_BW_WHOLE(BP_64_L4_k75),
     WTC_BW_SPLIT(TB_128_L1_k55, CB_32_L1_k5),      WTC_BW_SPLIT(TB_128_L2_k55, CB_32_L1_k5),
     WTC_BW_SPLIT(TB_128_L2of3_k55, CB_32_L1_k5),   WTC_BW_SPLIT(TB_128_L2of4_k55, CB_32_L2_k5),
     WTC_BW_SPLIT(TB_128_L2of5_k55, CB_32_L3_k5),   WTC_BW_SPLIT(TB_256_L2of4_k75, CB_64_L2_k5),
-    WTC_BW_SPLIT(TB_64_L2of4_k33, CB_16_L2_k3),    WTC_BW_SPLIT(TB_64_L1of2_k55, CB_32_L1_k5b),
+    WTC_BW_SPLIT(TB_64_L2of4_k33, CB_16_L2_k3),    WTC_BW_SPLIT(TB_64_L1of2_k55, CB_32_L1_k5),
     WTC_BW_DW(DB_56_k5), WTC_BW_DW(DB_56_k7), WTC_BW_DW(DB_28_k5), WTC_BW_DW(DB_28_k7), WTC_BW_DW(DB_14_k5),
     WTC_BW_DW(DB_14_k7),
 };

@@ -107,34 +107,16 @@ struct PlaneEntry {
 const PlaneEntry* find_plane_entry(int H, int W, int L, int KB, int K);
 
 // ------------------------------------------------------------ the plans
-// ConvNeXt-stage and sweep shapes first, then small shapes that exercise
-// other kernel sizes, odd tile counts and non-square planes.
+// Micro-tile plans of planes that no column-strip plan covers: small shapes
+// with other kernel sizes, odd tile counts and non-square planes.
 typedef PlanePlan<32, 32, 2, 5, 5, 64, 2, 2> PP_32_L2_k55;
-#ifndef WTC_PLAN_56
-#define WTC_PLAN_56 256, 1, 4
-#endif
-#ifndef WTC_PLAN_128
-#define WTC_PLAN_128 1024, 2, 2
-#endif
-typedef PlanePlan<56, 56, 3, 5, 5, WTC_PLAN_56> PP_56_L3_k55;
-typedef PlanePlan<28, 28, 2, 5, 5, 64, 2, 2> PP_28_L2_k55;
-typedef PlanePlan<14, 14, 1, 5, 5, 64, 1, 1> PP_14_L1_k55;
-typedef PlanePlan<128, 128, 1, 5, 5, WTC_PLAN_128> PP_128_L1_k55;
-typedef PlanePlan<128, 128, 2, 5, 5, WTC_PLAN_128> PP_128_L2_k55;
-typedef PlanePlan<128, 128, 3, 5, 5, WTC_PLAN_128> PP_128_L3_k55;
-typedef PlanePlan<128, 128, 4, 5, 5, WTC_PLAN_128> PP_128_L4_k55;
-typedef PlanePlan<128, 128, 5, 5, 5, WTC_PLAN_128> PP_128_L5_k55;
 typedef PlanePlan<32, 32, 3, 7, 5, 64, 2, 2> PP_32_L3_k75;
 typedef PlanePlan<24, 40, 3, 3, 3, 64, 2, 2> PP_24x40_L3_k33;
 typedef PlanePlan<16, 16, 4, 3, 7, 64, 1, 1> PP_16_L4_k37;
 typedef PlanePlan<64, 64, 4, 7, 5, 64, 4, 4> PP_64_L4_k75;
 
-// NT, TR, TC of the ConvNeXt stage-1 and 128x128 plans can be set at build
-// time (-DWTC_PLAN_56=...) for tuning sweeps.
 #define WTC_PLANE_ENTRIES(X)                                                                 \
-    X(PP_32_L2_k55), X(PP_56_L3_k55), X(PP_28_L2_k55), X(PP_14_L1_k55), X(PP_128_L1_k55),   \
-        X(PP_128_L2_k55), X(PP_128_L3_k55), X(PP_128_L4_k55), X(PP_128_L5_k55),            \
-        X(PP_32_L3_k75), X(PP_24x40_L3_k33), X(PP_16_L4_k37), X(PP_64_L4_k75)
+    X(PP_32_L2_k55), X(PP_32_L3_k75), X(PP_24x40_L3_k33), X(PP_16_L4_k37), X(PP_64_L4_k75)
 
 }  // namespace wtc
 
@@ -360,34 +342,19 @@ struct ColPlan {
 }  // namespace wtc
 
 namespace wtc {
-// column-strip plans (listed ahead of the tile plans of the same shape)
-#ifndef WTC_COLS
-#define WTC_COLS 1
-#endif
-#ifndef WTC_COL56_NT
-#define WTC_COL56_NT 512
-#endif
-#ifndef WTC_COL56_WMAX
-#define WTC_COL56_WMAX 8
-#endif
-typedef ColPlan<56, 56, 3, 5, 5, WTC_COL56_NT, 8, 7, WTC_COL56_WMAX> CP_56_L3_k55;
-// small planes: several images of one channel per workgroup
-#ifndef WTC_COL28
-#define WTC_COL28 256, 4, 14, 8, 2
-#endif
-#ifndef WTC_COL14
-#define WTC_COL14 256, 14, 7, 8, 8
-#endif
-typedef ColPlan<28, 28, 2, 5, 5, WTC_COL28> CP_28_L2_k55;
-typedef ColPlan<14, 14, 1, 5, 5, WTC_COL14> CP_14_L1_k55;
-#ifndef WTC_COL128
-#define WTC_COL128 1024, 16, 16
-#endif
-typedef ColPlan<128, 128, 1, 5, 5, WTC_COL128> CP_128_L1_k55;
-typedef ColPlan<128, 128, 2, 5, 5, WTC_COL128> CP_128_L2_k55;
-typedef ColPlan<128, 128, 3, 5, 5, WTC_COL128> CP_128_L3_k55;
-typedef ColPlan<128, 128, 4, 5, 5, WTC_COL128> CP_128_L4_k55;
-typedef ColPlan<128, 128, 5, 5, 5, WTC_COL128> CP_128_L5_k55;
+// Column-strip plans of the ConvNeXt stage planes and the 128x128 level
+// sweep. Measured choices: the 56x56 plan runs 8 waves per SIMD (64 VGPRs);
+// small planes put several images of one channel in a workgroup (28x28: two,
+// 14x14: eight) with strips packed across them; 128x128 uses 16-row base
+// and level strips on 1024 lanes.
+typedef ColPlan<56, 56, 3, 5, 5, 512, 8, 7, 8> CP_56_L3_k55;
+typedef ColPlan<28, 28, 2, 5, 5, 256, 4, 14, 8, 2> CP_28_L2_k55;
+typedef ColPlan<14, 14, 1, 5, 5, 256, 14, 7, 8, 8> CP_14_L1_k55;
+typedef ColPlan<128, 128, 1, 5, 5, 1024, 16, 16> CP_128_L1_k55;
+typedef ColPlan<128, 128, 2, 5, 5, 1024, 16, 16> CP_128_L2_k55;
+typedef ColPlan<128, 128, 3, 5, 5, 1024, 16, 16> CP_128_L3_k55;
+typedef ColPlan<128, 128, 4, 5, 5, 1024, 16, 16> CP_128_L4_k55;
+typedef ColPlan<128, 128, 5, 5, 5, 1024, 16, 16> CP_128_L5_k55;
 #define WTC_COL_ENTRIES(X)                                                                     \
     X(CP_56_L3_k55), X(CP_28_L2_k55), X(CP_14_L1_k55), X(CP_128_L1_k55), X(CP_128_L2_k55),     \
         X(CP_128_L3_k55), X(CP_128_L4_k55), X(CP_128_L5_k55)

@@ -612,15 +612,10 @@ static size_t split_ws(int B, int C) {
 typedef PlanePlan<64, 64, 2, 1, 5, 256, 2, 2> CP_64_L2_k5;
 typedef PlanePlan<16, 16, 2, 1, 3, 64, 1, 1> CP_16_L2_k3;
 typedef PlanePlan<32, 32, 1, 1, 5, 256, 1, 1> CP_32_L1_k5;
-// fine-pass plans
-#ifndef WTC_COLTILE
-#define WTC_COLTILE 1
-#endif
-typedef TilePlan<256, 256, 2, 4, 7, 5, 16, 256, 1, 4> FP_256_L2of4_k75;
-#ifndef WTC_CT256
-#define WTC_CT256 16, 512, 8, 8
-#endif
-typedef ColTilePlan<256, 256, 2, 4, 7, 5, WTC_CT256> CT_256_L2of4_k75;
+// fine-pass plans: column-strip tiles of 16 rows on 512 lanes at 256x256
+// (measured against 8- and 32-row tiles and 256 lanes); micro-tile fine
+// passes for the 64x64 test shapes
+typedef ColTilePlan<256, 256, 2, 4, 7, 5, 16, 512, 8, 8> CT_256_L2of4_k75;
 typedef TilePlan<64, 64, 2, 4, 3, 3, 8, 128, 1, 1> FP_64_L2of4_k33;
 typedef TilePlan<64, 64, 1, 2, 5, 5, 16, 128, 1, 2> FP_64_L1of2_k55;
 
@@ -637,11 +632,7 @@ typedef TilePlan<64, 64, 1, 2, 5, 5, 16, 128, 1, 2> FP_64_L1of2_k55;
      split_ws<FPL>}
 
 static const SplitEntry kSplitEntries[] = {
-#if WTC_COLTILE
     WTC_COLSPLIT_ENTRY(CT_256_L2of4_k75, CP_64_L2_k5),
-#else
-    WTC_SPLIT_ENTRY(FP_256_L2of4_k75, CP_64_L2_k5),
-#endif
     WTC_SPLIT_ENTRY(FP_64_L2of4_k33, CP_16_L2_k3),
     WTC_SPLIT_ENTRY(FP_64_L1of2_k55, CP_32_L1_k5),
 };
