@@ -29,6 +29,15 @@ def test_module_parameters_and_init():
         WTConv2d(4, 2, k_base=4)
 
 
+def test_module_optional_bias_and_base_scale():
+    m = WTConv2d(6, 3, k_base=7, k_level=5, bias=True, base_scale=True)
+    assert tuple(m.bias.shape) == (6,) and tuple(m.base_scale.shape) == (6,)
+    assert torch.equal(m.bias, torch.zeros(6)) and torch.equal(m.base_scale, torch.ones(6))
+    assert sum(p.numel() for p in m.parameters()) == 6 * (49 + 4 * 3 * (25 + 1)) + 2 * 6
+    plain = WTConv2d(6, 3)
+    assert plain.bias is None and plain.base_scale is None
+
+
 def test_module_refuses_cpu_tensors():
     m = WTConv2d(2, 1)
     with pytest.raises(RuntimeError, match="GPU"):
@@ -100,6 +109,44 @@ def test_module_matches_oracle(shape, dtype):
     assert rel_err(to_f64(x.grad), oracle.bwd_data(dyo, wbo, wlo, sco)) <= tol
     gb, gl, gs = oracle.bwd_weight(xo, dyo, wbo, wlo, sco)
     assert rel_err(to_f64(m.w_base.grad), gb) <= TOL["f32"]
+    assert rel_err(to_f64(m.w_lvl.grad), gl) <= TOL["f32"]
+    assert rel_err(to_f64(m.scale.grad), gs) <= TOL["f32"]
+
+
+@pytest.mark.gpu
+@torch_gpu
+def test_module_bias_and_base_scale_match_oracle():
+    """With the optional bias and base scale: y = layer(x; w_base * s_b) + b,
+    and the gradients of b (the sum of dy per channel), of s_b
+    (sum(dw_base_eff * w_base) per channel) and of w_base (dw_base_eff * s_b),
+    all from the oracle's gradients."""
+    B, C, H, W, L, kb, k = 2, 3, 32, 32, 2, 5, 5
+    inp = make_inputs(B, C, H, W, L, kb, k, dtype="f32", seed=21)
+    x, dy, wb, wl, sc = to_device(inp)
+    m = WTConv2d(C, L, kb, k, device="cuda", bias=True, base_scale=True)
+    rng = np.random.default_rng(5)
+    bias = rng.standard_normal(C)
+    bscale = rng.uniform(0.5, 1.5, C)
+    with torch.no_grad():
+        m.w_base.copy_(wb)
+        m.w_lvl.copy_(wl)
+        m.scale.copy_(sc)
+        m.bias.copy_(torch.from_numpy(bias))
+        m.base_scale.copy_(torch.from_numpy(bscale))
+    x.requires_grad_(True)
+    y = m(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xo, dyo = inp.act_f64("x"), inp.act_f64("dy")
+    wbo, wlo, sco = inp.params_f64()
+    wbe = wbo * bscale[:, None, None]
+    yo = oracle.fwd(xo, wbe, wlo, sco) + bias[None, :, None, None]
+    assert rel_err(to_f64(y), yo) <= TOL["f32"]
+    assert rel_err(to_f64(x.grad), oracle.bwd_data(dyo, wbe, wlo, sco)) <= TOL["f32"]
+    gbe, gl, gs = oracle.bwd_weight(xo, dyo, wbe, wlo, sco)
+    assert rel_err(to_f64(m.bias.grad), dyo.sum(axis=(0, 2, 3))) <= TOL["f32"]
+    assert rel_err(to_f64(m.base_scale.grad), (gbe * wbo).sum(axis=(1, 2))) <= TOL["f32"]
+    assert rel_err(to_f64(m.w_base.grad), gbe * bscale[:, None, None]) <= TOL["f32"]
     assert rel_err(to_f64(m.w_lvl.grad), gl) <= TOL["f32"]
     assert rel_err(to_f64(m.scale.grad), gs) <= TOL["f32"]
 

@@ -83,10 +83,20 @@ class WTConv2d(torch.nn.Module):
     Input and output: [B, C, H, W], fp32 or bf16, any H, W >= 1 ('same'
     zero padding, stride 1; an odd band grid is analysed with one extra zero
     row or column and its synthesis is cropped back).
+
+    Optional extras of a drop-in convolution layer, both off by default (the
+    layer the pages describe has neither): ``bias=True`` adds a learned
+    per-channel bias ``bias`` [C] to the output, ``base_scale=True`` a learned
+    per-channel factor ``base_scale`` [C] on the base convolution's result
+    (initialised to 1). The factor is applied by scaling the base kernel
+    before the call (``w_base * base_scale``, exact in the result up to fp32
+    rounding since the base convolution is linear in its kernel); the bias is
+    added to the library's output. Their gradients follow by autograd from
+    the library's ``dw_base`` and from the output gradient.
     """
 
     def __init__(self, channels: int, levels: int, k_base: int = 5, k_level: int = 5,
-                 device=None):
+                 device=None, bias: bool = False, base_scale: bool = False):
         super().__init__()
         if channels < 1 or levels < 0 or k_base % 2 == 0 or k_level % 2 == 0:
             raise ValueError("channels >= 1, levels >= 0 and odd kernel sizes are required")
@@ -95,6 +105,8 @@ class WTConv2d(torch.nn.Module):
         self.w_base = torch.nn.Parameter(torch.empty(channels, k_base, k_base, **f32))
         self.w_lvl = torch.nn.Parameter(torch.empty(levels, channels, 4, k_level, k_level, **f32))
         self.scale = torch.nn.Parameter(torch.ones(levels, channels, 4, **f32))
+        self.bias = torch.nn.Parameter(torch.zeros(channels, **f32)) if bias else None
+        self.base_scale = torch.nn.Parameter(torch.ones(channels, **f32)) if base_scale else None
         self.reset_parameters()
 
     def reset_parameters(self) -> None:
@@ -102,12 +114,23 @@ class WTConv2d(torch.nn.Module):
             self.w_base.uniform_(-1.0 / math.sqrt(self.k_base ** 2), 1.0 / math.sqrt(self.k_base ** 2))
             self.w_lvl.uniform_(-1.0 / math.sqrt(self.k_level ** 2), 1.0 / math.sqrt(self.k_level ** 2))
             self.scale.fill_(1.0)
+            if self.bias is not None:
+                self.bias.zero_()
+            if self.base_scale is not None:
+                self.base_scale.fill_(1.0)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.dim() != 4 or x.shape[1] != self.channels:
             raise ValueError(f"expected [B, {self.channels}, H, W], got {tuple(x.shape)}")
-        return WTConvFunction.apply(x, self.w_base, self.w_lvl, self.scale)
+        w_base = self.w_base
+        if self.base_scale is not None:
+            w_base = w_base * self.base_scale.view(-1, 1, 1)
+        y = WTConvFunction.apply(x, w_base, self.w_lvl, self.scale)
+        if self.bias is not None:
+            y = y + self.bias.view(1, -1, 1, 1).to(y.dtype)
+        return y
 
     def extra_repr(self) -> str:
         return (f"channels={self.channels}, levels={self.levels}, k_base={self.k_base}, "
-                f"k_level={self.k_level}")
+                f"k_level={self.k_level}, bias={self.bias is not None}, "
+                f"base_scale={self.base_scale is not None}")
