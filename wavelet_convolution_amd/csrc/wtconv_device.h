@@ -232,9 +232,10 @@ __device__ __forceinline__ lds_cfp opaque_lds(const float* p) {
 template <int S>
 struct RowBases {
     // rows per base: the farthest pair offset (GROUP-1 rows + 7 words) under
-    // 1 KB; rows too long for two in one group keep the compiler's addressing
+    // 1 KB. Rows longer than that get one base each (left to itself, the
+    // compiler makes a base per pair of loads there: three adds per row)
     static constexpr int GROUP = (1020 / 4 - 8) / S + 1;
-    static constexpr bool USE = GROUP >= 2;
+    static constexpr bool USE = GROUP >= 1;
 };
 template <int S, int NR>
 struct RowAddr {

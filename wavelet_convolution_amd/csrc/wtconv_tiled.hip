@@ -394,45 +394,62 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
         WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
     }
     {
-        // The region's x rows and their level-1 bands in one pass: an item
-        // owns region rows 2i, 2i+1 and VA columns from 2*j0 (band cells
-        // j0.. of band row i). Items on the column border, or on rows
-        // outside the plane, store zeros.
-        constexpr int NQ = P::NQ, IPR = P::IPR, CPI = P::CPI, VA = P::VA, MQ = cdiv(NQ, NT);
-        RawVec<T, VA> v0[MQ], v1[MQ];
+        // Border columns, written once: the x rows' columns outside the
+        // plane and the level-1 bands' zero border columns (nothing else
+        // writes them). Then the interior: an item owns region rows 2i, 2i+1
+        // and four columns from 4u (band cells 2u, 2u+1 of band row i); rows
+        // outside the plane load nothing and store zeros (the zero padding of
+        // every level's band grid).
+        constexpr int XB = SX - W, XB1 = S1 - W1;
+        static_assert(XB > 0 && XB1 > 0 && XO + W <= SX, "border columns");
+        for (int i = tid; i < P::XROWS * XB + 4 * P::rh(1) * XB1; i += NT) {
+            if (i < P::XROWS * XB) {
+                const int r = udiv(i, XB), q = i - r * XB;
+                A[r * SX + (q < XO ? q : q + W)] = 0.f;
+            } else {
+                const int j = i - P::XROWS * XB, rb = udiv(j, XB1), q = j - rb * XB1;   // rb = band * rh(1) + row
+                Bq[rb * S1 + (q < PK ? q : q + W1)] = 0.f;
+            }
+        }
+        constexpr int QW = W / 4, NQI = P::rh(1) * QW, MQ = cdiv(NQI, NT);
+        static_assert(W % 4 == 0 && PK % 2 == 0 && S1 % 2 == 0, "aligned 4-column items and band pairs");
+        const int rtop = r0 - G;   // plane row of region row 0 (negative on the first tile)
+        RawVec<T, 4> v0[MQ], v1[MQ];
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
-            const int ii = q / IPR, uu = q - ii * IPR, j0 = uu * CPI - PK, pr = r0 - G + 2 * ii;
-            if ((NQ % NT == 0 || q < NQ) && j0 >= 0 && j0 < W1 && pr >= 0 && pr < H) {
-                const T* s0 = src + (size_t)pr * W + 2 * j0;
-                load_raw<T, VA>(s0, v0[k]);
-                load_raw<T, VA>(s0 + W, v1[k]);
-            } else {
+            const int ii = udiv(q, QW), uu = q - ii * QW, pr = rtop + 2 * ii;
+            // every lane loads (rows outside the plane: its first words) and
+            // then selects zeros: no branch around the loads
+            const bool inside = (NQI % NT == 0 || q < NQI) && pr >= 0 && pr < H;
+            const T* s0 = src + (inside ? (uint32_t)(pr * W + 4 * uu) : 0u);
+            load_raw<T, 4>(s0, v0[k]);
+            load_raw<T, 4>(s0 + (inside ? W : 0), v1[k]);
 #pragma unroll
-                for (int e = 0; e < RawVec<T, VA>::N; ++e) v0[k].w[e] = v1[k].w[e] = 0u;
+            for (int e = 0; e < RawVec<T, 4>::N; ++e) {
+                v0[k].w[e] = inside ? v0[k].w[e] : 0u;
+                v1[k].w[e] = inside ? v1[k].w[e] : 0u;
             }
         }
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
-            if (!(NQ % NT == 0 || q < NQ)) continue;
-            const int ii = q / IPR, uu = q - ii * IPR, j0 = uu * CPI - PK;
-            float f0[VA], f1[VA];
-            widen_raw<T, VA>(v0[k], f0);
-            widen_raw<T, VA>(v1[k], f1);
-            const int xc = XO + 2 * j0, xr = 2 * ii - P::XR0;
-            if (xc >= 0 && xc + VA <= SX) {
-                if (xr >= 0 && xr < P::XROWS) store_vec<VA>(A + xr * SX + xc, f0);
-                if (xr + 1 >= 0 && xr + 1 < P::XROWS) store_vec<VA>(A + (xr + 1) * SX + xc, f1);
-            }
-            float b[4][CPI];
+            if (!(NQI % NT == 0 || q < NQI)) continue;
+            const int ii = udiv(q, QW), uu = q - ii * QW;
+            float f0[4], f1[4];
+            widen_raw<T, 4>(v0[k], f0);
+            widen_raw<T, 4>(v1[k], f1);
+            const int xr = 2 * ii - P::XR0;   // kept x rows: those the base convolution reads
+            float* const xo = A + xr * SX + XO + 4 * uu;
+            if (xr >= 0 && xr < P::XROWS) store_vec<4>(xo, f0);
+            if (xr + 1 >= 0 && xr + 1 < P::XROWS) store_vec<4>(xo + SX, f1);
+            float b[4][2];
 #pragma unroll
-            for (int m = 0; m < CPI; ++m)
+            for (int m = 0; m < 2; ++m)
                 haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], b[0][m], b[1][m], b[2][m], b[3][m]);
-            float* o = Bq + ii * S1 + uu * CPI;
+            float* const o = Bq + ii * S1 + PK + 2 * uu;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) store_vec<CPI>(o + s * BS1, b[s]);
+            for (int s = 0; s < 4; ++s) store_vec<2>(o + s * BS1, b[s]);
         }
     }
     __syncthreads();
@@ -453,18 +470,22 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     P::for_deep_levels([&](auto lc) {
         constexpr int l = decltype(lc)::value;
         constexpr int wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), Sp = P::su(l - 1);
-        constexpr int UO = P::uoff(l), UP = P::uoff(l - 1);
+        constexpr int UO = P::uoff(l), UP = P::uoff(l - 1), RL = P::rh(l), XBl = Sl - wl;
+        static_assert(Sp % 2 == 0 && PK % 2 == 0, "LL pairs read as aligned 64-bit words");
         float* Ul = A + UO;
         const float* LLp = (l == 2) ? (Bq + PK) : (A + UP + PK);
-        constexpr int GW = wl + 2 * PK, GN = P::rh(l) * GW;
-        for (int q = tid; q < GN; q += NT) {
-            const int i = q / GW, jj = q - i * GW, j = jj - PK;
-            float b[4] = {0.f, 0.f, 0.f, 0.f};
-            if (j >= 0 && j < wl) {
-                const float* x2 = LLp + 2 * i * Sp + 2 * j;
-                haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], b[0], b[1], b[2], b[3]);
-            }
-            const int o = i * Sl + jj;
+        // border columns, then the interior cells
+        for (int i = tid; i < 4 * RL * XBl; i += NT) {
+            const int rb = udiv(i, XBl), q = i - rb * XBl;
+            Ul[rb * Sl + (q < PK ? q : q + wl)] = 0.f;
+        }
+        for (int q = tid; q < RL * wl; q += NT) {
+            const int i = udiv(q, wl), j = q - i * wl;
+            const float2 t = *reinterpret_cast<const float2*>(LLp + 2 * i * Sp + 2 * j);
+            const float2 d = *reinterpret_cast<const float2*>(LLp + (2 * i + 1) * Sp + 2 * j);
+            float b[4];
+            haar4(t.x, t.y, d.x, d.y, b[0], b[1], b[2], b[3]);
+            const int o = i * Sl + PK + j;
 #pragma unroll
             for (int s = 0; s < 4; ++s) Ul[s * BSl + o] = b[s];
         }
@@ -513,9 +534,13 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     __syncthreads();
 
     // ---------------------------------------------------------------- P4
-    // y = base + closed-form synthesis of the fine levels + the coarse image
+    // y = base + closed-form synthesis of the fine levels + the coarse image.
+    // Stores and coarse reads use the tile's uniform bases plus 32-bit lane
+    // offsets (rows at constant offsets from one address).
     constexpr int CW = W >> L0;
-    const float* __restrict__ cpl = coarse ? coarse + (size_t)plane * (H >> L0) * CW : nullptr;
+    static_assert(RB % 2 == 0, "bf16 rows are narrowed in pairs");
+    const float* __restrict__ ctile = coarse ? coarse + ((size_t)plane * (H >> L0) + (r0 >> L0)) * CW : nullptr;
+    T* __restrict__ dtile = dst + (size_t)r0 * W;
 #pragma unroll
     for (int it = 0; it < MB; ++it) {
         const int item = tid + it * NT;
@@ -526,9 +551,14 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
         // coarser levels add to every row of level-l block p; level l splits
         // it into its two half-blocks as carry + a +- b.
         float carry[RB];
+        if (ctile) {
+            const float* const cp = ctile + (uint32_t)((h0 >> L0) * CW + (w >> L0));
 #pragma unroll
-        for (int p = 0; p < (RB >> L0); ++p)
-            carry[p] = cpl ? cpl[(size_t)(((r0 + h0) >> L0) + p) * CW + (w >> L0)] : 0.f;
+            for (int p = 0; p < (RB >> L0); ++p) carry[p] = cp[p * CW];
+        } else {
+#pragma unroll
+            for (int p = 0; p < (RB >> L0); ++p) carry[p] = 0.f;
+        }
         P::for_levels([&](auto lc) {
             constexpr int l = L0 + 1 - decltype(lc)::value;   // L0, ..., 1
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
@@ -546,20 +576,21 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
 #pragma unroll
             for (int q = 0; q < (RB >> (l - 1)); ++q) carry[q] = next[q];
         });
-        float y[RB];
-#pragma unroll
-        for (int o = 0; o < RB; ++o) y[o] = yb[it][o] + carry[o];
+        T* const out_col = dtile + (uint32_t)(h0 * W + w);
         if constexpr (sizeof(T) == 2) {
             // two rows per conversion: the low half to row o, the high half to o + 1
 #pragma unroll
             for (int o = 0; o < RB; o += 2) {
-                const uint32_t pr = narrow_bf16x2(y[o], y[o + 1]);
-                dst[(size_t)(r0 + h0 + o) * W + w] = (bf16_t)(pr & 0xffffu);
-                dst[(size_t)(r0 + h0 + o + 1) * W + w] = (bf16_t)(pr >> 16);
+                uint32_t pr = narrow_bf16x2(yb[it][o] + carry[o], yb[it][o + 1] + carry[o + 1]);
+                // opaque to the compiler, which would otherwise convert the
+                // high half again on its own instead of storing it directly
+                asm volatile("" : "+v"(pr));
+                out_col[o * W] = (bf16_t)(pr & 0xffffu);
+                out_col[(o + 1) * W] = (bf16_t)(pr >> 16);
             }
         } else {
 #pragma unroll
-            for (int o = 0; o < RB; ++o) dst[(size_t)(r0 + h0 + o) * W + w] = y[o];
+            for (int o = 0; o < RB; ++o) out_col[o * W] = yb[it][o] + carry[o];
         }
     }
 }
