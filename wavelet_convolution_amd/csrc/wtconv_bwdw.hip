@@ -31,9 +31,9 @@ namespace wtc {
 // column strip of dy-side values against its window of x-side values. Lanes
 // of a wavefront take consecutive columns: every load is a run of
 // consecutive LDS words across the wavefront, free of bank conflicts.
-template <int K, int R, int SU, int SV, int NA, typename VT>
+template <int K, int R, int SU, int SV, int NA, typename VT, int OFF = 0>
 __device__ __forceinline__ void taps_col(const float* u, const VT* v, float (&acc)[NA]) {
-    static_assert(NA >= K * K, "accumulator slot too small");
+    static_assert(OFF + K * K <= NA, "accumulator slot too small");
     constexpr int NR = R + K - 1;   // window rows
     __builtin_amdgcn_sched_barrier(0);
     float vt[R];
@@ -42,22 +42,27 @@ __device__ __forceinline__ void taps_col(const float* u, const VT* v, float (&ac
     // window rows double-buffered: row r + 1 is requested before row r's
     // multiply-adds, so its LDS latency hides behind them (requesting two to
     // five rows ahead measured no faster)
-    const RowAddr<SU, NR> row(u);
+    const RowAddr<SU, NR> rows(u);
     float win[2][K];
+    {
+        const lds_cfp r0 = rows.row(0);
 #pragma unroll
-    for (int n = 0; n < K; ++n) win[0][n] = row(0, n);
+        for (int n = 0; n < K; ++n) win[0][n] = r0[n];
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         if (r + 1 < NR) {
+            const lds_cfp rn = rows.row(r + 1);
 #pragma unroll
-            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = row(r + 1, n);
+            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = rn[n];
         }
 #pragma unroll
         for (int o = 0; o < R; ++o) {
             const int m = r - o;
             if (m < 0 || m >= K) continue;
 #pragma unroll
-            for (int n = 0; n < K; ++n) acc[m * K + n] = __builtin_fmaf(vt[o], win[r & 1][n], acc[m * K + n]);
+            for (int n = 0; n < K; ++n)
+                acc[OFF + m * K + n] = __builtin_fmaf(vt[o], win[r & 1][n], acc[OFF + m * K + n]);
         }
     }
     pin_regs(acc);
@@ -749,14 +754,22 @@ __global__ __launch_bounds__(1024) void bwdw_finalize(const float* __restrict__ 
 // One workgroup per (channel, chunk of (b, tile) units); the units of a chunk
 // follow each other down the plane, so the halo rows of consecutive tiles
 // are read from L2.
-template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_>
+//
+// NT threads in two groups of NT/2: group A sums the base taps, group B the
+// taps of the fine levels, each band of each level on NT/8 lanes (one or two
+// wavefronts). A lane keeps one accumulator array for the whole chunk: the
+// base taps (group A) or the taps of every fine level, level l at offset
+// (l-1) K² (group B).
+template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int NT_ = 512>
 struct TileBwPlan {
     static constexpr int H = H_, W = W_, L0 = L0_, LT = LT_, KB = KB_, K = K_, TH = TH_;
-    static constexpr int RB = pick_rows(TH, W, 256, KB);
     static constexpr int L = L0;   // levels handled here (role helpers below)
-    static constexpr int NT = 512, NW = 8;
+    static constexpr int NT = NT_, NW = NT / 64, GW = NW / 2;   // waves per group
+    static constexpr int GL = GW * 64, BL = GL / 4;              // lanes per group, per band
+    static_assert(NT == 512 || NT == 1024, "two groups of four or eight wavefronts");
+    static constexpr int RB = pick_rows(TH, W, GL, KB);
     static constexpr int PB = KB / 2, PK = K / 2, BLK = 1 << L0;
-    static_assert(L0 >= 1 && L0 <= 5 && L0 <= LT, "fine levels 1..L0");
+    static_assert(L0 >= 1 && L0 <= 2 && L0 <= LT, "fine levels: one or two (group B holds them all)");
     static_assert(H % (1 << LT) == 0 && W % (1 << LT) == 0, "plane must divide into 2^L blocks");
     static_assert(TH % BLK == 0 && H % TH == 0, "tile shapes");
     static constexpr int G0 = PB > (PK << L0) ? PB : (PK << L0);
@@ -785,9 +798,10 @@ struct TileBwPlan {
         return o;
     }
     static constexpr int UTOT = uoff(L0 + 1), VTOT = voff(L0 + 1);
-    static constexpr int NSLOT = 1 + (L0 >= 2 ? 1 : 0) + (L0 >= 4 ? 1 : 0);
-    static constexpr int SLOT0 = KB * KB > K * K ? KB * KB : K * K;
-    static constexpr int RED = NW * SLOT0 + NW * (NSLOT - 1) * K * K;
+    // accumulators per lane: base taps, or the taps of all fine levels
+    static constexpr int ACC = KB * KB > L0 * K * K ? KB * KB : L0 * K * K;
+    static constexpr int boff(int l) { return (l - 1) * K * K; }
+    static constexpr int RED = NW * ACC;
     static constexpr int DATA = XSIZE + DSIZE + UTOT + VTOT;
     static constexpr int LDS_FLOATS = DATA > RED ? DATA : RED;
     static_assert(LDS_FLOATS * 4 <= 160 * 1024, "tile does not fit in LDS");
@@ -795,15 +809,13 @@ struct TileBwPlan {
     static constexpr int NI = (TH / RB) * LPB;
     static constexpr int NTILE = H / TH;
     static constexpr int TAPS = KB * KB + 4 * L0 * K * K;
-    static constexpr int band_rows(int l) { return pick_rows(TH >> l, W >> l, 64, K); }
+    static constexpr int band_rows(int l) { return pick_rows(TH >> l, W >> l, BL, K); }
     static constexpr int WG_PER_CU = (160 * 1024) / (LDS_FLOATS * 4);
     static constexpr int WAVES_PER_EU_LDS = WG_PER_CU * NW / 4;
-    static constexpr int REGS = SLOT0 + (NSLOT - 1) * K * K + 64;
+    static constexpr int REGS = ACC + 64;
     static constexpr int WAVES_PER_EU_REG = 512 / (REGS <= 128 ? 128 : (REGS <= 168 ? 168 : 256));
     static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
     static constexpr int WAVES_PER_EU = WAVES_PER_EU_MIN < 1 ? 1 : WAVES_PER_EU_MIN;
-    static constexpr int group_of(int l) { return (l == 3 || l == 5) ? 0 : 1; }
-    static constexpr int slot_of(int l) { return l == 1 ? 0 : (l == 2 || l == 3) ? 1 : 2; }
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -816,13 +828,13 @@ struct TileBwPlan {
 };
 
 template <class P, typename T>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
+__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
 void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* __restrict__ part,
                       float* __restrict__ px, float* __restrict__ pdy, int B, int C, int upc) {
     constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, G = P::G, RH0 = P::RH0, W1 = W / 2;
     constexpr int RB = P::RB, NI = P::NI, LPB = P::LPB, XO = P::XO, SD = P::SD;
-    constexpr int NSLOT = P::NSLOT, SLOT0 = P::SLOT0;
+    constexpr int ACC = P::ACC, GW = P::GW, GL = P::GL, BL = P::BL;
     constexpr int VL = P::VL;
     constexpr int NVX = RH0 * W / VL, NVD = TH * W / VL;
     constexpr int NLX = cdiv(NVX, NT), NLD = cdiv(NVD, NT);
@@ -835,7 +847,10 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
     float* Vb = U + P::UTOT;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int grp = wave >> 2, band = wave & 3, gtid = tid & 255;
+    // group A (waves 0..GW-1): base taps; group B: band (wave - GW) & 3 of
+    // every fine level, lanes blane of the band's BL
+    const int grp = wave / GW, gtid = tid - grp * GL;
+    const int band = (wave - GW) & 3, blane = (((wave - GW) >> 2) << 6) + lane;
     const int c = blockIdx.x % C, chunk = blockIdx.x / C;
     const int nunits = B * P::NTILE;
     const int u0 = chunk * upc, u1 = min(nunits, u0 + upc);
@@ -856,14 +871,9 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
         }
     });
 
-    float acc0[SLOT0];
-    float accl[NSLOT > 1 ? NSLOT - 1 : 1][K * K];
+    float acc[ACC];
 #pragma unroll
-    for (int t = 0; t < SLOT0; ++t) acc0[t] = 0.f;
-#pragma unroll
-    for (int j = 0; j < (NSLOT > 1 ? NSLOT - 1 : 1); ++j)
-#pragma unroll
-        for (int t = 0; t < K * K; ++t) accl[j][t] = 0.f;
+    for (int t = 0; t < ACC; ++t) acc[t] = 0.f;
 
     RawVec<T, VL> vx[NLX], vd[NLD];
     auto issue_loads = [&](int u) {
@@ -966,7 +976,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
         });
         // the coarse pass's inputs: the tile's level-L0 LL sums of x and dy
         if (P::LT > L0) {
-            constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GL = G >> L0;
+            constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GLv = G >> L0;
             const float* LLu = U + P::uoff(L0) + PK;
             const float* LLv = Vb + P::voff(L0);
             float* pxo = px + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
@@ -974,71 +984,54 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             constexpr int SVL = P::sv(L0);
             for (int q = tid; q < hl * wl; q += NT) {
                 const int i = q / wl, j = q - i * wl;
-                pxo[q] = LLu[(GL + i) * Sl + j];
+                pxo[q] = LLu[(GLv + i) * Sl + j];
                 pdo[q] = LLv[i * SVL + j];
             }
         }
-        // ------------------- P3: all taps at once, base taps and one band per wavefront
+        // ------------------- P3: all taps at once: base taps (group A), one band per wavefront (group B)
         if (grp == 0) {
-            for (int item = gtid; item < NI; item += 256) {
+            for (int item = gtid; item < NI; item += GL) {
                 const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
-                if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + (G + h0 - PB) * SX + w, DY + h0 * SD + w, acc0);
+                if (LPB == W || w < W) taps_col<KB, RB, SX, SD>(X0 + (G + h0 - PB) * SX + w, DY + h0 * SD + w, acc);
             }
-        }
-        P::for_levels([&](auto lc) {
-            constexpr int l = decltype(lc)::value;
-            constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-            constexpr int Gl = G >> l;
-            constexpr int R = P::band_rows(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
-            if (grp == P::group_of(l)) {
+        } else {
+            P::for_levels([&](auto lc) {
+                constexpr int l = decltype(lc)::value;
+                constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
+                constexpr int Gl = G >> l, SVl = P::sv(l), OFF = P::boff(l);
+                constexpr int R = P::band_rows(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
                 const float* Us = U + P::uoff(l) + band * BSl;
                 const float* Vs = Vb + P::voff(l) + band * VSl;
-                constexpr int SVl = P::sv(l);
-                for (int item = lane; item < NIl; item += 64) {
+                for (int item = blane; item < NIl; item += BL) {
                     const int rs = item / LPl, j = item - rs * LPl;
                     if (!(LPl == wl || j < wl)) continue;
-                    if constexpr (P::slot_of(l) == 0)
-                        taps_col<K, R, Sl, SVl>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j, acc0);
-                    else
-                        taps_col<K, R, Sl, SVl>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j,
-                                                accl[P::slot_of(l) - 1]);
+                    taps_col<K, R, Sl, SVl, ACC, float, OFF>(Us + (Gl + R * rs - PK) * Sl + j,
+                                                              Vs + R * rs * SVl + j, acc);
                 }
-            }
-        });
+            });
+        }
         // the next unit's P0 overwrites x, dy, U and V: wait for every reader
         __syncthreads();
     }
 
 #pragma unroll
-    for (int t = 0; t < SLOT0; ++t) acc0[t] = wave_sum(acc0[t]);
-#pragma unroll
-    for (int j = 0; j < NSLOT - 1; ++j)
-#pragma unroll
-        for (int t = 0; t < K * K; ++t) accl[j][t] = wave_sum(accl[j][t]);
+    for (int t = 0; t < ACC; ++t) acc[t] = wave_sum(acc[t]);
     __syncthreads();
-    float* red0 = lds;
-    float* redl = lds + P::NW * SLOT0;
+    float* red = lds;   // [NW][ACC]
     if (lane == 0) {
 #pragma unroll
-        for (int t = 0; t < SLOT0; ++t) red0[wave * SLOT0 + t] = acc0[t];
-#pragma unroll
-        for (int j = 0; j < NSLOT - 1; ++j)
-#pragma unroll
-            for (int t = 0; t < K * K; ++t) redl[(wave * (NSLOT - 1) + j) * K * K + t] = accl[j][t];
+        for (int t = 0; t < ACC; ++t) red[wave * ACC + t] = acc[t];
     }
     __syncthreads();
     float* dst = part + ((size_t)chunk * C + c) * P::TAPS;
     for (int t = tid; t < P::TAPS; t += NT) {
-        float v;
+        float v = 0.f;
         if (t < KB * KB) {
-            v = red0[t];
-#pragma unroll
-            for (int w = 1; w < 4; ++w) v += red0[w * SLOT0 + t];
+            for (int w = 0; w < GW; ++w) v += red[w * ACC + t];   // group A, waves in order
         } else {
             const int r = t - KB * KB, ls = r / (K * K), tap = r - ls * (K * K);
             const int l = ls / 4 + 1, s = ls - (l - 1) * 4;
-            const int w = P::group_of(l) * 4 + s, slot = P::slot_of(l);
-            v = slot == 0 ? red0[w * SLOT0 + tap] : redl[(w * (NSLOT - 1) + slot - 1) * K * K + tap];
+            for (int j = 0; j < GW / 4; ++j) v += red[(GW + 4 * j + s) * ACC + (l - 1) * K * K + tap];
         }
         dst[t] = v;
     }
@@ -1444,7 +1437,9 @@ typedef BwPlan<32, 32, 1, 1, 5, 1, 4> CB_32_L1_k5;
 typedef BwPlan<32, 32, 2, 1, 5, 2, 4> CB_32_L2_k5;
 typedef BwPlan<32, 32, 3, 1, 5, 3, 4> CB_32_L3_k5;
 // 16-row tiles: the 8-row halo on each side costs 1.5 tiles of rows instead
-// of 3 with 8-row tiles (1.34 -> 1.06 ms at 16x256x256²)
+// of 3 with 8-row tiles (1.34 -> 1.06 ms at 16x256x256²). 1024 lanes (four
+// waves per SIMD under the one workgroup per CU that 114 KB of LDS allow, 8-
+// and 2-row strips) measured slower: 1.07 against 0.99 ms
 typedef TileBwPlan<256, 256, 2, 4, 7, 5, 16> TB_256_L2of4_k75;
 typedef BwPlan<64, 64, 2, 1, 5> CB_64_L2_k5;
 typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8> TB_64_L2of4_k33;

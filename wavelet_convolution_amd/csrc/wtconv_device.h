@@ -248,9 +248,10 @@ struct RowAddr {
             for (int g = 0; g < cdiv(NR, GR); ++g) rb[g] = opaque_lds(base + g * GR * S);
         }
     }
-    __device__ __forceinline__ float operator()(int r, int n) const {
-        if constexpr (RowBases<S>::USE) return rb[r / GR][(r % GR) * S + n];
-        else return p[r * S + n];
+    // the start of window row r (read its words with [n])
+    __device__ __forceinline__ lds_cfp row(int r) const {
+        if constexpr (RowBases<S>::USE) return rb[r / GR] + (r % GR) * S;
+        else return (lds_cfp)(p + r * S);
     }
 };
 
@@ -325,15 +326,19 @@ __device__ __forceinline__ void conv_col(const float* s, const float* w, float (
     // window rows double-buffered: row r+1 is requested before row r's
     // multiply-adds, so its LDS latency hides behind them
     constexpr int NR = R + K - 1;
-    const RowAddr<S, NR> row(s);
+    const RowAddr<S, NR> rows(s);
     float win[2][K];
+    {
+        const lds_cfp r0 = rows.row(0);
 #pragma unroll
-    for (int n = 0; n < K; ++n) win[0][n] = row(0, n);
+        for (int n = 0; n < K; ++n) win[0][n] = r0[n];
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         if (r + 1 < NR) {
+            const lds_cfp rn = rows.row(r + 1);
 #pragma unroll
-            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = row(r + 1, n);
+            for (int n = 0; n < K; ++n) win[(r + 1) & 1][n] = rn[n];
         }
 #pragma unroll
         for (int o = 0; o < R; ++o) {
