@@ -132,6 +132,31 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ p, RawVec<T, V>& 
     }
 }
 
+// V activations of one row from column c0, in their storage format: the
+// ones at columns >= IW, or all of them when !row_ok, are zero (the zero
+// padding of a plane to whole 2^L blocks). A whole vector inside the row is
+// one load when the row length keeps it aligned.
+template <typename T, int V, int IW>
+__device__ __forceinline__ void load_raw_guarded(const T* __restrict__ row, int c0, bool row_ok, RawVec<T, V>& r) {
+#pragma unroll
+    for (int i = 0; i < RawVec<T, V>::N; ++i) r.w[i] = 0u;
+    if (!row_ok || c0 >= IW) return;
+    if constexpr (IW % V == 0) {
+        load_raw<T, V>(row + c0, r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            if (c0 + i >= IW) break;
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t v = *reinterpret_cast<const uint16_t*>(row + c0 + i);
+                r.w[i / 2] |= (i % 2 == 0) ? v : (v << 16);
+            } else {
+                r.w[i] = __float_as_uint(row[c0 + i]);
+            }
+        }
+    }
+}
+
 // Widen to fp32 (exact for bf16).
 template <typename T, int V>
 __device__ __forceinline__ void widen_raw(const RawVec<T, V>& r, float (&f)[V]) {
@@ -201,6 +226,10 @@ __device__ __forceinline__ void store_row(bf16_t* __restrict__ p, const float (&
         *reinterpret_cast<uint32_t*>(p + i) = narrow_bf16x2(v[i], v[i + 1]);
     }
 }
+
+// Store one value in the storage format (bf16: rounded to nearest even).
+__device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_one(bf16_t* p, float v) { *p = narrow_bf16(v); }
 
 // Materialise values in registers at this point: an empty asm that reads and
 // writes each one. Compiler passes may otherwise sink a convolution's FMAs

@@ -49,11 +49,13 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     float* WL = WB + P::KB2P;          // level taps x scale x 4^-l, [L][4][K2P]
 
     constexpr bool BASE = SHIFT == 0;
+    constexpr int IH = P::IH, IW = P::IW;   // the plane in memory (zero-padded to H x W here)
+    static_assert(!P::PADDED || SHIFT == 0, "padded planes are whole planes");
     const int tid = threadIdx.x;
     const int plane = blockIdx.x;
     const int c = plane % C;
-    const T* __restrict__ src = in + ((size_t)plane * H * W << (2 * SHIFT));
-    TO* __restrict__ dst = out + (size_t)plane * H * W;
+    const T* __restrict__ src = in + ((size_t)plane * IH * IW << (2 * SHIFT));
+    TO* __restrict__ dst = out + (size_t)plane * IH * IW;
 
     // ---------------------------------------------------------------- P0
     // stage the taps: turned by 180 degrees for the transpose, and the level
@@ -70,11 +72,19 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     }
     zero_border<1, H, W, PB, SX>(A, tid, NT);
     zero_border<4, H1, W1, PK, S1>(Bq, tid, NT);
+    if constexpr (P::PADDED) {
+        // the padded rows and columns of x: zero (the plane's own pixels,
+        // stored below, are other cells)
+        for (int i = tid; i < H * W; i += NT) {
+            const int r = i / W, col = i - r * W;
+            if (r >= IH || col >= IW) A[(r + PB) * SX + col + PB] = 0.f;
+        }
+    }
     if constexpr (SHIFT == 0) {
         // every global load of the plane is issued before the first LDS
         // write, so the HBM latency is paid once per plane
-        constexpr int V = vec_elems<T>(W, H * W);
-        constexpr int NV = H * W / V;
+        constexpr int V = vec_elems<T>(IW, IH * IW);
+        constexpr int NV = IH * IW / V;
         constexpr int NL = cdiv(NV, NT);
         float v[NL][V];
 #pragma unroll
@@ -86,7 +96,7 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
         for (int k = 0; k < NL; ++k) {
             const int q = tid + k * NT;
             if (NV % NT == 0 || q < NV) {
-                const int e = q * V, r = e / W, col = e - r * W;
+                const int e = q * V, r = e / IW, col = e - r * IW;
 #pragma unroll
                 for (int i = 0; i < V; ++i) A[(r + PB) * SX + col + PB + i] = v[k][i];
             }
@@ -248,8 +258,18 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
                 row1[2 * q + 1] = yb[it][2 * r + 1][2 * q + 1] + (p0 - p1 - p2 + p3) + e;
             }
             const int h = 2 * (i0 + r), w0 = 2 * j0;
-            store_row<2 * TC>(dst + (size_t)h * W + w0, row0);
-            store_row<2 * TC>(dst + (size_t)(h + 1) * W + w0, row1);
+            if constexpr (!P::PADDED) {
+                store_row<2 * TC>(dst + (size_t)h * W + w0, row0);
+                store_row<2 * TC>(dst + (size_t)(h + 1) * W + w0, row1);
+            } else {
+                // the plane's own pixels only (the crop of the padded plane)
+#pragma unroll
+                for (int q = 0; q < 2 * TC; ++q) {
+                    if (w0 + q >= IW) continue;
+                    if (h < IH) store_one(dst + (size_t)h * IW + w0 + q, row0[q]);
+                    if (h + 1 < IH) store_one(dst + (size_t)(h + 1) * IW + w0 + q, row1[q]);
+                }
+            }
         }
     }
 }
@@ -619,6 +639,27 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             }
         }
     }
+}
+
+// Launchers of the whole-plane kernels: one workgroup per plane
+// (plane_kernel), or per channel and group of NPW images (col_kernel).
+template <class P, typename T, bool FLIP>
+hipError_t launch_plane(const void* in, const float* wb, const float* wl, const float* sc,
+                               void* out, int B, int C, hipStream_t stream) {
+    const unsigned planes = (unsigned)B * (unsigned)C;
+    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, 0, T>), dim3(planes), dim3(P::NT), 0, stream,
+                       (const T*)in, wb, wl, sc, (T*)out, C);
+    return hipGetLastError();
+}
+
+template <class P, typename T, bool FLIP>
+hipError_t launch_col(const void* in, const float* wb, const float* wl, const float* sc, void* out,
+                             int B, int C, hipStream_t stream) {
+    // one workgroup per channel and group of NPW images
+    const unsigned groups = (unsigned)cdiv(B, P::NPW) * (unsigned)C;
+    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(groups), dim3(P::NT), 0, stream, (const T*)in, wb, wl, sc,
+                       (T*)out, B, C);
+    return hipGetLastError();
 }
 
 }  // namespace wtc

@@ -42,9 +42,19 @@ constexpr Tile pick_tile(int h, int w, int nt) {
 // base convolution it is reused for the bordered subbands of levels 2..L.
 // Region B holds the four bordered level-1 subbands. Bordered planes have a
 // zero border of K/2 and an odd row stride.
-template <int H_, int W_, int L_, int KB_, int K_, int NT_, int TR_, int TC_>
+//
+// IH x IW (at most H x W) is the plane in memory. A smaller one is zero-padded
+// to H x W on chip (H, W multiples of 2^L) and only its own pixels are
+// written: for a plane that 2^L does not divide this is exactly the layer's
+// reading of odd band grids (each odd grid analysed with one extra zero row
+// or column, each synthesis cropped), since the padded rows and columns only
+// ever meet zeros and only feed outputs outside the plane.
+template <int H_, int W_, int L_, int KB_, int K_, int NT_, int TR_, int TC_, int IH_ = H_, int IW_ = W_>
 struct PlanePlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, NT = NT_, TR = TR_, TC = TC_;
+    static constexpr int IH = IH_, IW = IW_;
+    static constexpr bool PADDED = IH != H || IW != W;
+    static_assert(IH <= H && IW <= W && IH > H - (1 << L) && IW > W - (1 << L), "padding below one 2^L block");
     static constexpr int PB = KB / 2, PK = K / 2;
     static_assert(L >= 1, "the whole-plane kernel needs at least one level");
     static_assert(H % (1 << L) == 0 && W % (1 << L) == 0, "plane must divide into 2^L blocks");
@@ -73,13 +83,18 @@ struct PlanePlan {
 
     static constexpr Tile deep_tile(int l) { return pick_tile(H >> l, W >> l, NT); }
 
-    // occupancy the LDS footprint allows (waves per SIMD, at most 8): the
-    // register allocator is held to it so that registers never become the
-    // tighter limit
+    // occupancy the LDS footprint allows (waves per SIMD, at most 8). With a
+    // kernel above 5x5 it is also held to what the registers of one output
+    // tile need (its staged taps, the tile, a window row and about 40 more),
+    // so that the allocator is never asked for fewer registers than that
     static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
     static constexpr int WAVES_PER_EU_LDS = (WG_PER_CU * (NT / 64)) / 4;
+    static constexpr int KMAX = KB > K ? KB : K;
+    static constexpr int REGS = kpad4(KMAX) + MI * 4 * TR * TC + 2 * TC + KMAX + 40;
+    static constexpr int WAVES_PER_EU_REG = KMAX <= 5 ? 8 : 512 / round_up(REGS, 8);
+    static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
     static constexpr int WAVES_PER_EU =
-        WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > 8 ? 8 : WAVES_PER_EU_LDS);
+        WAVES_PER_EU_MIN < 1 ? 1 : (WAVES_PER_EU_MIN > 8 ? 8 : WAVES_PER_EU_MIN);
 
     // f(std::integral_constant<int, l>) for l = 2..L, unrolled at compile time
     template <class F>
@@ -97,7 +112,7 @@ typedef hipError_t (*plane_launch_fn)(const void* in, const float* w_base, const
                                       hipStream_t stream);
 
 struct PlaneEntry {
-    int H, W, L, KB, K;
+    int H, W, L, KB, K;   // the plane in memory (a padded plan's IH, IW)
     plane_launch_fn fn[2][2];  // [dtype: 0 fp32, 1 bf16][flip: 0 fwd, 1 bwd_data]
     int lds_bytes;
     int nt;
