@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """WTConv training-step benchmark on one MI355X.
 
-A step is one pass of the whole hot path over one batch: forward
-(wtconv_fwd), backward data (wtconv_bwd_data) and backward weight
-(wtconv_bwd_weight), each through the C-ABI, on synthetic seeded inputs
-already resident in HBM. The default workload is the largest single-GPU
+A step is one pass of the whole hot path over one batch, through the C-ABI,
+on synthetic seeded inputs already resident in HBM: the forward (wtconv_fwd)
+and the whole backward (wtconv_bwd: dx and every weight gradient in one call,
+the library's fused backward). With --two-call-bwd the backward is
+wtconv_bwd_data + wtconv_bwd_weight instead; the line reports that step's
+time too, measured in the same run. The default workload is the largest single-GPU
 configuration: B=16, C=256, 256x256, L=4, 7x7 base and 5x5 level kernels,
 bf16 activations, fp32 arithmetic.
 
@@ -38,7 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "WTConv fwd+bwd images/sec and achieved HBM TB/s (% of MI355X peak)"
 KERNEL_SOURCES = ("wtconv_device.h", "wtconv_plans.h", "wtconv_plane.h", "wtconv_fused.hip", "wtconv_tiled.hip",
-                  "wtconv_bwdw.hip", "wtconv_dw.h", "wtconv_dw.hip")
+                  "wtconv_bwdw.hip", "wtconv_bwdw_body.h", "wtconv_dw.h", "wtconv_dw.hip")
 # rotated inputs must exceed twice the 256 MB MALL
 ROTATION_BYTES = 512 << 20
 
@@ -211,25 +213,27 @@ class Workload:
         return mean, med
 
 
-def workload_summary(torch, wt, cfg, steps: int):
+def workload_summary(torch, wt, cfg, steps: int, single_pass: bool):
     """images/s, per-call times, step TFLOP/s and HBM rate of one bar
     workload (inputs drawn on the device, rotated above ROTATION_BYTES)."""
     from wavelet_convolution_amd import iomodel
 
     wl = Workload(torch, wt, cfg, default_sets(cfg), exact_first=False)
     for i in range(3):
-        wl.step(i)
-    ms = wl.time_steps(steps)
-    mean, _ = wl.call_times(steps)
+        wl.step(i, single_pass)
+    ms = wl.time_steps(steps, lambda i: wl.step(i, single_pass))
+    mean, _ = wl.call_times(steps, single_pass)
     model = iomodel.step_model(cfg.B, cfg.C, cfg.H, cfg.W, cfg.L, cfg.kb, cfg.k, cfg.dtype)
     dominant = max(mean, key=mean.get)
+    calls = 2 if dominant == "bwd" else 1
+    step_bytes = model.step_bytes_fused_bwd if single_pass else model.step_bytes
     out = {"images_per_s": round(cfg.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
            "kernel_ms": {k: round(v, 5) for k, v in mean.items()},
            "step_TFLOPs": round(3 * model.flops_per_call / (ms * 1e-3) / 1e12, 2),
            "dominant": dominant,
-           "dominant_frac_of_157TF": round(model.flops_per_call / (mean[dominant] * 1e-3) / 1e12
+           "dominant_frac_of_157TF": round(calls * model.flops_per_call / (mean[dominant] * 1e-3) / 1e12
                                            / iomodel.FP32_VECTOR_PEAK_TFLOPS, 4),
-           "hbm_TBs_vs_min_bytes": round(model.step_bytes / (ms * 1e-3) / 1e12, 4),
+           "hbm_TBs_vs_min_bytes": round(step_bytes / (ms * 1e-3) / 1e12, 4),
            "input_sets_rotated": len(wl.sets), "steps": steps}
     del wl
     torch.cuda.empty_cache()
@@ -402,9 +406,9 @@ def main() -> int:
                     help="replay a HIP graph of each step instead of launching it from Python (measured "
                          "slower on this path: 0.19 vs 0.18 ms per stage-1 step)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the FMA-rate and copy-rate probes")
-    ap.add_argument("--single-pass-bwd", action="store_true",
-                    help="run the backward as one wtconv_bwd call (a single pass over x and dy where the "
-                         "library has one)")
+    ap.add_argument("--two-call-bwd", action="store_true",
+                    help="run the backward as wtconv_bwd_data + wtconv_bwd_weight instead of one wtconv_bwd "
+                         "call")
     ap.add_argument("--channels-last", action="store_true",
                     help="channels-last activations (planar kernels on converted copies)")
     ap.add_argument("--no-context", action="store_true",
@@ -440,8 +444,10 @@ def main() -> int:
     wl = Workload(torch, wt, cfg, args.sets or default_sets(cfg), exact_first=True,
                   channels_last=args.channels_last)
 
+    single = not args.two_call_bwd
+
     def step(i):
-        wl.step(i, args.single_pass_bwd)
+        wl.step(i, single)
 
     for i in range(args.warmup):
         step(i)
@@ -475,13 +481,22 @@ def main() -> int:
     print(f"[bench] {ms_per_step:.4f} ms per step", file=sys.stderr, flush=True)
 
     # per-call durations: HIP events on the stream the kernels run on
-    dur, med = wl.call_times(args.steps, args.single_pass_bwd)
+    dur, med = wl.call_times(args.steps, single)
     dominant = max(dur, key=dur.get)
     calls = 2 if dominant == "bwd" else 1   # the whole backward does two calls' multiply-adds
     achieved = calls * model.flops_per_call / (dur[dominant] * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     # the stored counter summaries are of planar runs
-    traffic = None if (args.channels_last or args.single_pass_bwd) else read_traffic(cfg.name, dominant, src_hash)
+    traffic = None if args.channels_last else read_traffic(cfg.name, dominant, src_hash)
+
+    # the other backward form, same inputs and run
+    for i in range(2):
+        wl.step(i, not single)
+    other_ms = wl.time_steps(args.steps, lambda i: wl.step(i, not single))
+    other_mean, _ = wl.call_times(args.steps, not single)
+    other = {"backward": "wtconv_bwd_data + wtconv_bwd_weight" if single else "wtconv_bwd",
+             "ms_per_step": round(other_ms, 4), "images_per_s": round(cfg.B / (other_ms * 1e-3), 1),
+             "kernel_ms": {k: round(v, 5) for k, v in other_mean.items()}}
 
     naive = None
     if not args.no_naive:
@@ -523,7 +538,7 @@ def main() -> int:
               "rotated_footprint_MB": round(len(wl.sets) * 2 * cfg.N * (2 if cfg.dtype == "bf16" else 4) / 1e6, 1),
               "launch": "hip graph per step" if args.graph else "eager",
               "layout": "channels_last" if args.channels_last else "nchw",
-              "backward": "wtconv_bwd" if args.single_pass_bwd else "wtconv_bwd_data + wtconv_bwd_weight"}
+              "backward": "wtconv_bwd" if single else "wtconv_bwd_data + wtconv_bwd_weight"}
     del wl
     torch.cuda.empty_cache()
 
@@ -538,14 +553,15 @@ def main() -> int:
         for name in BAR_WORKLOADS:
             if name == cfg.name:
                 continue
-            workloads[name] = workload_summary(torch, wt, CONFIGS[name], max(10, args.steps))
+            workloads[name] = workload_summary(torch, wt, CONFIGS[name], max(10, args.steps), single)
             print(f"[bench] workload {name}: {workloads[name]['images_per_s']} images/s", file=sys.stderr,
                   flush=True)
 
     peaks = None if args.no_peaks else measure_peaks(torch, wt)
 
     step_s = ms_per_step * 1e-3
-    hbm_tbs = model.step_bytes / step_s / 1e12
+    min_bytes = model.step_bytes_fused_bwd if single else model.step_bytes
+    hbm_tbs = min_bytes / step_s / 1e12
     out = {
         "metric": METRIC,
         "value": round(cfg.B / step_s, 1),
@@ -562,7 +578,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": config,
-        "hbm": {"min_bytes_per_step": model.step_bytes, "achieved_TBs": round(hbm_tbs, 4),
+        "hbm": {"min_bytes_per_step": min_bytes, "achieved_TBs": round(hbm_tbs, 4),
                 "frac_of_8TBs": round(hbm_tbs / iomodel.HBM_PEAK_TBS, 4)},
         "kernel_ms": {k: round(v, 5) for k, v in dur.items()},
         "kernel_ms_median": {k: round(v, 5) for k, v in med.items()},
@@ -572,6 +588,7 @@ def main() -> int:
                      "traffic": traffic,
                      "flops_per_launch": calls * model.flops_per_call,
                      "unpacked_fma_ceiling_TFLOPs": iomodel.FP32_UNPACKED_FMA_TFLOPS},
+        "other_backward_form": other,
         "workloads": workloads,
         "naive_baseline": naive,
         "context": context,

@@ -39,6 +39,8 @@ def test_minimum_bytes_are_the_tensors_each_call_touches(name):
     assert m.bwd_data_bytes == 2 * act + params       # dy in, dx out
     assert m.bwd_weight_bytes == 2 * act + 2 * params  # x and dy in, gradients out
     assert m.step_bytes == 6 * act + 4 * params
+    # forward + one backward call: x read twice, dy once, y and dx written once
+    assert m.step_bytes_fused_bwd == 5 * act + 3 * params
 
 
 def test_stage1_figures():

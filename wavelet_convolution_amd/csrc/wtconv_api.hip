@@ -166,11 +166,37 @@ bool single_pass_bwd(const wtconv_desc_t* d) {
            wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base) != (size_t)-1;
 }
 
-// Workspace of wtconv_bwd: the single-pass kernel's, else enough for the
-// two backward calls run one after the other on it.
+// Shared-sums backward of a split plane: the weight-gradient plan leaves the
+// level-L0 LL sums of dy in its workspace and the data pass's coarse step
+// (which sums dy over the same 2^L0 blocks) reads those instead of dy.
+// Workspace: the weight pass's, then the data pass's coarse image.
+struct SharedSums {
+    const wtc::SplitEntry* se = nullptr;
+    size_t sums_offset = 0, data_offset = 0, need = 0;
+};
+SharedSums shared_sums_bwd(const wtconv_desc_t* d) {
+    SharedSums r;
+    if (d->B == 0 || d->layout != WTCONV_NCHW) return r;
+    const Route rd = route(d, WTCONV_OP_BWD_DATA), rw = route(d, WTCONV_OP_BWD_WEIGHT);
+    int l0 = -1;
+    size_t off = 0;
+    if (!rd.se || !rd.se->bwd_data_from_sums[0] || !rw.bw ||
+        !wtc::bwdw_dy_sums(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, &l0, &off) || l0 != rd.se->L0)
+        return r;
+    r.se = rd.se;
+    r.sums_offset = off;
+    r.data_offset = align256(rw.own);
+    r.need = r.data_offset + rd.own;
+    return r;
+}
+
+// Workspace of wtconv_bwd: the single-pass kernel's, the shared-sums pair's,
+// else enough for the two backward calls run one after the other on it.
 size_t bwd_workspace(const wtconv_desc_t* d) {
     if (single_pass_bwd(d))
         return wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base);
+    const SharedSums ss = shared_sums_bwd(d);
+    if (ss.se) return ss.need;
     const size_t a = route(d, WTCONV_OP_BWD_DATA).need, b = route(d, WTCONV_OP_BWD_WEIGHT).need;
     return a > b ? a : b;
 }
@@ -312,6 +338,17 @@ wtconv_status_t wtconv_bwd(const wtconv_desc_t* d, const void* x, const void* dy
         const hipError_t err = wtc::bwd_single_pass_launch(d->B, d->C, d->H, d->W, d->k_base,
                                                            d->dtype == WTCONV_BF16, x, dy, w_base, dx, dw_base,
                                                            ws, (hipStream_t)stream);
+        return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+    }
+    const SharedSums ss = shared_sums_bwd(d);
+    if (ss.se) {
+        // the weight gradient first (it leaves the dy sums), then the data
+        // pass with its coarse step on those sums
+        st = wtconv_bwd_weight(d, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, ss.data_offset, stream);
+        if (st != WTCONV_OK) return st;
+        const hipError_t err = ss.se->bwd_data_from_sums[d->dtype == WTCONV_BF16 ? 1 : 0](
+            dy, (const float*)((const char*)ws + ss.sums_offset), w_base, w_lvl, scale, dx,
+            (float*)((char*)ws + ss.data_offset), d->B, d->C, (hipStream_t)stream);
         return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
     }
     // the two calls in stream order, one workspace

@@ -10,6 +10,11 @@ namespace wtc {
 // plan covers this shape.
 size_t bwdw_workspace_bytes(int B, int C, int H, int W, int L, int KB, int K);
 
+// Whether the fused weight-gradient plan of this shape leaves, in its
+// workspace at byte `offset`, the fp32 planes [B][C][H >> l0][W >> l0] of
+// unnormalised level-l0 LL sums of dy (its coarse pass's input).
+bool bwdw_dy_sums(int B, int C, int H, int W, int L, int KB, int K, int* l0, size_t* offset);
+
 hipError_t bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16,
                        const void* x, const void* dy, const float* w_lvl, const float* scale,
                        float* dw_base, float* dw_lvl, float* dscale, void* ws,

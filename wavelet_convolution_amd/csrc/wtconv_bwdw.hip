@@ -416,6 +416,17 @@ static size_t split_bw_ws(int B, int C) {
     return n;
 }
 
+// byte offset of the dy sums (pdy) in the workspace split_bw_launch lays out
+template <class FP, class CP>
+static size_t split_bw_dy_sums_offset(int B, int C) {
+    static_assert(FP::LT > FP::L0, "the LL planes exist only with a coarse pass");
+    const int units = B * FP::NTILE;
+    const int nA = cdiv(units, chunk_units(units, C)), nB = cdiv(B, chunk_units(B, C));
+    return bw_align256((size_t)nA * C * FP::TAPS * sizeof(float)) +
+           bw_align256((size_t)nB * C * 4 * (FP::LT - FP::L0) * FP::K * FP::K * sizeof(float)) +
+           bw_align256((size_t)B * C * (FP::H >> FP::L0) * (FP::W >> FP::L0) * sizeof(float));
+}
+
 template <class FP, class CP, typename T>
 static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_lvl, const float* scale,
                                   float* dw_base, float* dw_lvl, float* dscale, void* ws, int B, int C,
@@ -707,6 +718,11 @@ typedef DwPlan<14, 14, 7, 256, 14, 16> DB_14_k7;
 #define WTC_BW_SPLIT(FPL, CPL)                                                                    \
     {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K,                                                   \
      {split_bw_launch<FPL, CPL, float>, split_bw_launch<FPL, CPL, bf16_t>}, split_bw_ws<FPL, CPL>}
+// ... and its dy sums, offered to the backward-data pass
+#define WTC_BW_SPLIT_SUMS(FPL, CPL)                                                               \
+    {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K,                                                   \
+     {split_bw_launch<FPL, CPL, float>, split_bw_launch<FPL, CPL, bf16_t>}, split_bw_ws<FPL, CPL>,  \
+     FPL::L0, split_bw_dy_sums_offset<FPL, CPL>}
 
 static const BwEntry kBwEntries[] = {
     WTC_BW_PLANESPLIT(WP_56_L1of3_k55, CB_28_L2_k5), WTC_BW_PLANESPLIT(WP_28_L1of2_k55, CB_14_L1_k5),
@@ -714,8 +730,8 @@ static const BwEntry kBwEntries[] = {
     WTC_BW_WHOLE(BP_24x40_L3_k33), WTC_BW_WHOLE(BP_16_L4_k37), WTC_BW_WHOLE(BP_64_L4_k75),
     WTC_BW_SPLIT(TB_128_L1_k55, CB_32_L1_k5),      WTC_BW_SPLIT(TB_128_L2_k55, CB_32_L1_k5),
     WTC_BW_SPLIT(TB_128_L2of3_k55, CB_32_L1_k5),   WTC_BW_SPLIT(TB_128_L2of4_k55, CB_32_L2_k5),
-    WTC_BW_SPLIT(TB_128_L2of5_k55, CB_32_L3_k5),   WTC_BW_SPLIT(TB_256_L2of4_k75, CB_64_L2_k5),
-    WTC_BW_SPLIT(TB_64_L2of4_k33, CB_16_L2_k3),    WTC_BW_SPLIT(TB_64_L1of2_k55, CB_32_L1_k5),
+    WTC_BW_SPLIT(TB_128_L2of5_k55, CB_32_L3_k5),   WTC_BW_SPLIT_SUMS(TB_256_L2of4_k75, CB_64_L2_k5),
+    WTC_BW_SPLIT_SUMS(TB_64_L2of4_k33, CB_16_L2_k3),    WTC_BW_SPLIT_SUMS(TB_64_L1of2_k55, CB_32_L1_k5),
     WTC_BW_DW(DB_56_k5), WTC_BW_DW(DB_56_k7), WTC_BW_DW(DB_28_k5), WTC_BW_DW(DB_28_k7), WTC_BW_DW(DB_14_k5),
     WTC_BW_DW(DB_14_k7),
 };
@@ -749,6 +765,14 @@ static const BwEntry* find_bw(int H, int W, int L, int KB, int K) {
     for (const BwEntry& e : kBwEntries)
         if (e.H == H && e.W == W && e.L == L && e.KB == KB && (L == 0 || e.K == K)) return &e;
     return L > 0 ? find_family_bw_entry(H, W, L, KB, K) : nullptr;
+}
+
+bool bwdw_dy_sums(int B, int C, int H, int W, int L, int KB, int K, int* l0, size_t* offset) {
+    const BwEntry* e = find_bw(H, W, L, KB, K);
+    if (!e || !e->dy_sums_offset) return false;
+    *l0 = e->l0;
+    *offset = e->dy_sums_offset(B, C);
+    return true;
 }
 
 size_t bwdw_workspace_bytes(int B, int C, int H, int W, int L, int KB, int K) {

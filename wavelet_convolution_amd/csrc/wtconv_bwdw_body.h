@@ -798,6 +798,10 @@ struct BwEntry {
     int H, W, L, KB, K;
     bwdw_fn fn[2];
     size_t (*ws)(int B, int C);
+    // plans that leave the fp32 planes [B][C][H >> l0][W >> l0] of level-l0
+    // LL sums of dy in their workspace: l0 and the planes' byte offset
+    int l0 = 0;
+    size_t (*dy_sums_offset)(int B, int C) = nullptr;
 };
 
 }  // namespace wtc

@@ -30,7 +30,10 @@
 #include "wtconv_plans.h"
 
 namespace wtc {
-template <class P, typename T, bool FLIP, int SHIFT, typename TO>
+// SUMS (with SHIFT > 0): `in` already holds the fp32 plane of 2^SHIFT x
+// 2^SHIFT block sums (as the weight-gradient pass leaves them), so it is
+// loaded as it is instead of being summed from the full-size activations.
+template <class P, typename T, bool FLIP, int SHIFT, typename TO, bool SUMS = false>
 __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU))) void plane_kernel(const T* __restrict__ in,
                                                       const float* __restrict__ w_base,
                                                       const float* __restrict__ w_lvl,
@@ -51,10 +54,11 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     constexpr bool BASE = SHIFT == 0;
     constexpr int IH = P::IH, IW = P::IW;   // the plane in memory (zero-padded to H x W here)
     static_assert(!P::PADDED || SHIFT == 0, "padded planes are whole planes");
+    static_assert(!SUMS || (SHIFT > 0 && sizeof(T) == 4), "block sums are fp32 planes of a coarse pass");
     const int tid = threadIdx.x;
     const int plane = blockIdx.x;
     const int c = plane % C;
-    const T* __restrict__ src = in + ((size_t)plane * IH * IW << (2 * SHIFT));
+    const T* __restrict__ src = in + ((size_t)plane * IH * IW << (SUMS ? 0 : 2 * SHIFT));
     TO* __restrict__ dst = out + (size_t)plane * IH * IW;
 
     // ---------------------------------------------------------------- P0
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
             if (r >= IH || col >= IW) A[(r + PB) * SX + col + PB] = 0.f;
         }
     }
-    if constexpr (SHIFT == 0) {
+    if constexpr (SHIFT == 0 || SUMS) {
         // every global load of the plane is issued before the first LDS
         // write, so the HBM latency is paid once per plane
         constexpr int V = vec_elems<T>(IW, IH * IW);
@@ -104,7 +108,11 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     } else {
         // P[i][j] = sum of the 2^SHIFT x 2^SHIFT block of x at (i, j): one
         // thread per block, 2^SHIFT-element row segments (lanes of a wave
-        // read consecutive segments of the same rows)
+        // read consecutive segments of the same rows). The sum runs in the
+        // order of the Haar analysis's LL chain, (a + b) + (c + d) per 2x2
+        // group, level by level: exactly the unnormalised LL band the
+        // weight-gradient pass computes, so that its sums can stand in for
+        // these bit for bit.
         constexpr int BS = 1 << SHIFT, WF = W << SHIFT;
         static_assert(BS * Act<T>::BYTES <= 16, "block row must fit one vector load");
         constexpr int NBLK = H * W, NL = cdiv(NBLK, NT);
@@ -113,15 +121,17 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
             const int q = tid + k * NT;
             if (NBLK % NT == 0 || q < NBLK) {
                 const int i = q / W, j = q - i * W;
-                float acc = 0.f;
+                float v[BS][BS];
 #pragma unroll
-                for (int u = 0; u < BS; ++u) {
-                    float v[BS];
-                    load_vec<T, BS>(src + (size_t)(i * BS + u) * WF + j * BS, v);
+                for (int u = 0; u < BS; ++u) load_vec<T, BS>(src + (size_t)(i * BS + u) * WF + j * BS, v[u]);
 #pragma unroll
-                    for (int t = 0; t < BS; ++t) acc += v[t];
-                }
-                A[(i + PB) * SX + j + PB] = acc;
+                for (int st = 1; st < BS; st *= 2)
+#pragma unroll
+                    for (int r = 0; r < BS; r += 2 * st)
+#pragma unroll
+                        for (int cc = 0; cc < BS; cc += 2 * st)
+                            v[r][cc] = (v[r][cc] + v[r][cc + st]) + (v[r + st][cc] + v[r + st][cc + st]);
+                A[(i + PB) * SX + j + PB] = v[0][0];
             }
         }
     }
@@ -274,11 +284,11 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     }
 }
 
-template <class P, typename T, bool FLIP, int SHIFT>
+template <class P, typename T, bool FLIP, int SHIFT, bool SUMS = false>
 hipError_t launch_coarse(const void* in, const float* wl, const float* sc, float* out, int B, int C,
                          hipStream_t stream) {
     const unsigned planes = (unsigned)B * (unsigned)C;
-    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, SHIFT, float>), dim3(planes), dim3(P::NT), 0, stream,
+    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, SHIFT, float, SUMS>), dim3(planes), dim3(P::NT), 0, stream,
                        (const T*)in, (const float*)nullptr, wl, sc, out, C);
     return hipGetLastError();
 }

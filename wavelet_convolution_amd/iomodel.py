@@ -58,6 +58,17 @@ class StepModel:
         return self.fwd_bytes + self.bwd_data_bytes + self.bwd_weight_bytes
 
     @property
+    def bwd_fused_bytes(self) -> int:
+        """One backward call for dx and every weight gradient: x and dy read
+        once, dx written once, the parameters read, the gradients written."""
+        return 3 * self.N * self.elem_bytes + 2 * self.param_bytes
+
+    @property
+    def step_bytes_fused_bwd(self) -> int:
+        """Forward plus the single-call backward: 5 N e + 3 P."""
+        return self.fwd_bytes + self.bwd_fused_bytes
+
+    @property
     def step_flops(self) -> float:
         return 3.0 * self.flops_per_call
 
