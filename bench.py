@@ -43,6 +43,8 @@ KERNEL_SOURCES = ("wtconv_device.h", "wtconv_plans.h", "wtconv_plane.h", "wtconv
                   "wtconv_bwdw.hip", "wtconv_bwdw_body.h", "wtconv_dw.h", "wtconv_dw.hip")
 # rotated inputs must exceed twice the 256 MB MALL
 ROTATION_BYTES = 512 << 20
+# default warm-up before the timed steps
+WARMUP_SECONDS = 0.3
 
 
 def kernel_source_hash() -> str:
@@ -396,8 +398,9 @@ def measure_peaks(torch, wt, reps: int = 5):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed warm-up steps (default: as many as fill {WARMUP_SECONDS} s)")
     ap.add_argument("--workload", default=None, help="workload name (default: the headline large-plane shape)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -449,9 +452,20 @@ def main() -> int:
     def step(i):
         wl.step(i, single)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # Warm-up: W untimed steps. By default W is what fills WARMUP_SECONDS
+    # (the clocks take tens of milliseconds to settle; a block timed right
+    # after a few steps runs about 5 % slow on the small workloads).
+    if args.warmup is None:
+        t0, args.warmup = time.perf_counter(), 0
+        while time.perf_counter() - t0 < WARMUP_SECONDS or args.warmup < 10:
+            for i in range(10):
+                step(args.warmup + i)
+            args.warmup += 10
+            torch.cuda.synchronize()
+    else:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
 
     # Optionally one HIP graph per input set holding the step's kernel
     # launches (the library allocates and memsets nothing, so the captured
@@ -489,8 +503,8 @@ def main() -> int:
     # the stored counter summaries are of planar runs
     traffic = None if args.channels_last else read_traffic(cfg.name, dominant, src_hash)
 
-    # the other backward form, same inputs and run
-    for i in range(2):
+    # the other backward form, same inputs and run, as warm
+    for i in range(min(args.warmup, 100)):
         wl.step(i, not single)
     other_ms = wl.time_steps(args.steps, lambda i: wl.step(i, not single))
     other_mean, _ = wl.call_times(args.steps, not single)

@@ -357,14 +357,19 @@ def test_level_zero_fused_kernels(shape):
 @pytest.mark.parametrize("shape", [(3, 4, 56, 56, 0, 5, 5), (2, 3, 56, 56, 0, 7, 5), (5, 3, 28, 28, 0, 7, 5),
                                    (4, 3, 28, 28, 0, 5, 5), (17, 3, 14, 14, 0, 5, 5), (5, 2, 14, 14, 0, 7, 3),
                                    (2, 3, 56, 56, 3, 5, 5), (2, 3, 13, 11, 2, 5, 3),
+                                   # whole planes: the weight gradient's second stage in the data kernel's launch
+                                   (11, 3, 14, 14, 1, 5, 5), (3, 2, 28, 28, 2, 5, 5), (2, 3, 128, 128, 3, 5, 5),
+                                   (2, 2, 56, 56, 2, 7, 3), (3, 2, 7, 7, 2, 5, 7),
                                    # split planes: the data pass's coarse step reads the weight pass's dy sums
                                    (2, 3, 64, 64, 4, 3, 3), (3, 2, 64, 64, 2, 5, 5), (1, 2, 256, 256, 4, 7, 5)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_whole_backward_equals_the_two_calls(shape):
     """wtconv_bwd (a single pass over x and dy at L = 0 on planned planes;
     on split planes the weight pass first and the data pass's coarse step on
-    its dy sums; the two calls elsewhere) equals wtconv_bwd_data +
-    wtconv_bwd_weight bit for bit, and the oracle within the bars."""
+    its dy sums; on whole planes the weight pass first and its second stage
+    in the data kernel's launch; the two calls elsewhere) equals
+    wtconv_bwd_data + wtconv_bwd_weight bit for bit, and the oracle within
+    the bars."""
     _say(f"[parity] whole backward {shape}")
     kb = shape[5]
     for dtype in ("f32", "bf16"):

@@ -117,9 +117,11 @@ void* copy_slot(const Route& r, const wtconv_desc_t* d, void* ws, int i) {
     return (char*)ws + align256(r.own) + (size_t)i * align256(act_bytes(d));
 }
 
+// fin: a deferred weight-gradient second stage for a whole-plane kernel to
+// run as extra workgroups (null: none; the caller checked it fits)
 wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const float* w_base,
                                 const float* w_lvl, const float* scale, void* out, void* ws,
-                                size_t ws_bytes, void* stream, bool flip) {
+                                size_t ws_bytes, void* stream, bool flip, const wtc::FinalizeArgs* fin = nullptr) {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
     if (d->B == 0) return check_params(d, w_base, w_lvl, scale, true);   // empty batch: nothing to write
@@ -153,7 +155,7 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     if (r.de)   // L = 0: the plain depthwise correlation
         err = r.de->fn[dt][flip ? 1 : 0](kin, w_base, kout, d->B, d->C, s);
     else if (r.pe)   // the whole plane fits one workgroup: one kernel, no workspace of its own
-        err = r.pe->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, d->B, d->C, s);
+        err = r.pe->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, d->B, d->C, s, fin);
     else        // coarse pass on the LL band at level L0, then the fine tiles
         err = r.se->fn[dt][flip ? 1 : 0](kin, w_base, w_lvl, scale, kout, (float*)ws, d->B, d->C, s);
     if (err == hipSuccess && r.copies) err = wtc::nchw_to_nhwc(kout, out, d->B, d->C, d->H, d->W, dt == 1, s);
@@ -350,6 +352,26 @@ wtconv_status_t wtconv_bwd(const wtconv_desc_t* d, const void* x, const void* dy
             dy, (const float*)((const char*)ws + ss.sums_offset), w_base, w_lvl, scale, dx,
             (float*)((char*)ws + ss.data_offset), d->B, d->C, (hipStream_t)stream);
         return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
+    }
+    // A whole-plane data kernel: the weight gradient first, its second stage
+    // then rides in the data kernel's launch as extra workgroups (one launch
+    // fewer; the same sums in the same order).
+    const Route rd = route(d, WTCONV_OP_BWD_DATA), rw = route(d, WTCONV_OP_BWD_WEIGHT);
+    if (rd.pe && !rd.copies && rw.bw && !rw.copies && d->B > 0) {
+        wtc::FinalizeArgs fin{};
+        hipError_t err = wtc::bwdw_launch_deferred(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                                   d->dtype == WTCONV_BF16, x, dy, w_lvl, scale, dw_base, dw_lvl,
+                                                   dscale, ws, (hipStream_t)stream, &fin);
+        if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
+        const size_t scratch = (size_t)4 * fin.L * fin.K * fin.K * sizeof(float);
+        if (fin.C > 0 && scratch > (size_t)rd.pe->lds_bytes) {
+            // its scratch would not fit the data kernel's LDS: launch it on its own
+            err = wtc::launch_finalize(fin, (hipStream_t)stream);
+            if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
+            fin.C = 0;
+        }
+        return fused_data_pass(d, dy, w_base, w_lvl, scale, dx, ws, ws_bytes, stream, true,
+                               fin.C > 0 ? &fin : nullptr);
     }
     // the two calls in stream order, one workspace
     st = fused_data_pass(d, dy, w_base, w_lvl, scale, dx, ws, ws_bytes, stream, true);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "wtconv_device.h"
+
 namespace wtc {
 
 // Workspace bytes for the per-chunk partial sums, or (size_t)-1 if no fused
@@ -19,6 +21,17 @@ hipError_t bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf
                        const void* x, const void* dy, const float* w_lvl, const float* scale,
                        float* dw_base, float* dw_lvl, float* dscale, void* ws,
                        hipStream_t stream);
+
+// As bwdw_launch, but the second stage (the fixed-order chunk sum) is not
+// launched: its arguments go to *fin (fin->C = 0 when the plan has none), for
+// a later kernel of the same stream to run (finalize_channel per channel).
+hipError_t bwdw_launch_deferred(int B, int C, int H, int W, int L, int KB, int K, bool bf16,
+                                const void* x, const void* dy, const float* w_lvl, const float* scale,
+                                float* dw_base, float* dw_lvl, float* dscale, void* ws,
+                                hipStream_t stream, FinalizeArgs* fin);
+
+// Launch a (deferred) second stage on its own.
+hipError_t launch_finalize(const FinalizeArgs& f, hipStream_t stream);
 
 // Single-pass backward (dx and the weight gradient from one read of x and dy),
 // planned for L = 0 only: its workspace bytes, or (size_t)-1 without a plan.

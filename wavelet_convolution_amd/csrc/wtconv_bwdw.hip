@@ -26,70 +26,30 @@
 
 namespace wtc {
 
-// Stage 2: fixed-order sum over chunks, then scale and normalisation. Taps
-// [0, TA) (base, levels 1..LA) come from partA, the rest (levels LA+1..L)
-// from partB when the plane was split.
-__global__ __launch_bounds__(1024) void bwdw_finalize(const float* __restrict__ partA, int nA, int LA,
-                                                      const float* __restrict__ partB, int nB, int C,
-                                                      int L, int KB, int K,
-                                                      const float* __restrict__ w_lvl,
-                                                      const float* __restrict__ scale,
-                                                      float* __restrict__ dw_base,
-                                                      float* __restrict__ dw_lvl,
-                                                      float* __restrict__ dscale) {
+// Stage 2 as its own kernel: one workgroup per channel.
+__global__ __launch_bounds__(1024) void bwdw_finalize(FinalizeArgs f) {
     // w_lvl * G per level tap, sized for every shape the ABI accepts (the
     // host rejects L > 5 and kernels above 15 before any launch)
     constexpr int kMaxLevels = 5, kMaxK = 15;
     __shared__ float WG[4 * kMaxLevels * kMaxK * kMaxK];
-    if (L > kMaxLevels || K > kMaxK) return;
-    const int c = blockIdx.x, tid = threadIdx.x;
-    const int kb2 = KB * KB, k2 = K * K, taps = kb2 + 4 * L * k2;
-    const int TA = kb2 + 4 * LA * k2, TB = taps - TA;
-    // one tap per thread (blockDim covers every tap): the partial sums, the
-    // scale and the level tap are all requested before any is used
-    for (int t = tid; t < taps; t += blockDim.x) {
-        float sc = 1.f, wv = 0.f;
-        size_t pi = 0;
-        int tap = 0;
-        if (t >= kb2) {
-            const int r = t - kb2, ls = r / k2, l = ls / 4, s = ls - 4 * l;
-            tap = r - ls * k2;
-            pi = ((size_t)l * C + c) * 4 + s;
-            sc = scale[pi];
-            wv = w_lvl[pi * k2 + tap];
-        }
-        float a = 0.f;   // the sum stays in chunk order
-        if (t < TA) {
-#pragma unroll 8
-            for (int ch = 0; ch < nA; ++ch) a += partA[((size_t)ch * C + c) * TA + t];
-        } else {
-#pragma unroll 8
-            for (int ch = 0; ch < nB; ++ch) a += partB[((size_t)ch * C + c) * TB + (t - TA)];
-        }
-        if (t < kb2) {
-            dw_base[(size_t)c * kb2 + t] = a;
-        } else {
-            const int l = (t - kb2) / (4 * k2);   // 0-based level
-            a *= 1.0f / (float)(1 << (2 * (l + 1)));
-            dw_lvl[pi * k2 + tap] = sc * a;
-            WG[t - kb2] = wv * a;
-        }
-    }
-    __syncthreads();
-    for (int ls = tid; ls < 4 * L; ls += blockDim.x) {
-        const int l = ls / 4, s = ls - 4 * l;
-        float a = 0.f;
-        for (int tap = 0; tap < k2; ++tap) a += WG[ls * k2 + tap];
-        dscale[((size_t)l * C + c) * 4 + s] = a;
-    }
+    if (f.L > kMaxLevels || f.K > kMaxK) return;
+    finalize_channel(f, blockIdx.x, threadIdx.x, blockDim.x, WG);
 }
 
+// Where the calling thread has asked for it (bwdw_launch_deferred), the
+// second stage is not launched but handed back, for a later kernel of the
+// same stream to run as extra workgroups.
+static thread_local FinalizeArgs* g_defer = nullptr;
 
 hipError_t launch_bwdw_finalize(const float* partA, int nA, int LA, const float* partB, int nB, int C, int L, int KB,
                                 int K, const float* w_lvl, const float* scale, float* dw_base, float* dw_lvl,
                                 float* dscale, hipStream_t stream) {
-    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(KB, K, L)), 0, stream, partA, nA, LA,
-                       partB, nB, C, L, KB, K, w_lvl, scale, dw_base, dw_lvl, dscale);
+    const FinalizeArgs f{partA, nA, LA, partB, nB, C, L, KB, K, w_lvl, scale, dw_base, dw_lvl, dscale};
+    if (g_defer) {
+        *g_defer = f;
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)C), dim3(finalize_threads(KB, K, L)), 0, stream, f);
     return hipGetLastError();
 }
 
@@ -778,6 +738,22 @@ bool bwdw_dy_sums(int B, int C, int H, int W, int L, int KB, int K, int* l0, siz
 size_t bwdw_workspace_bytes(int B, int C, int H, int W, int L, int KB, int K) {
     const BwEntry* e = find_bw(H, W, L, KB, K);
     return e ? e->ws(B, C) : (size_t)-1;
+}
+
+hipError_t launch_finalize(const FinalizeArgs& f, hipStream_t stream) {
+    hipLaunchKernelGGL(bwdw_finalize, dim3((unsigned)f.C), dim3(finalize_threads(f.KB, f.K, f.L)), 0, stream, f);
+    return hipGetLastError();
+}
+
+hipError_t bwdw_launch_deferred(int B, int C, int H, int W, int L, int KB, int K, bool bf16, const void* x,
+                                const void* dy, const float* w_lvl, const float* scale, float* dw_base,
+                                float* dw_lvl, float* dscale, void* ws, hipStream_t stream, FinalizeArgs* fin) {
+    fin->C = 0;
+    g_defer = fin;
+    const hipError_t err =
+        bwdw_launch(B, C, H, W, L, KB, K, bf16, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, stream);
+    g_defer = nullptr;
+    return err;
 }
 
 hipError_t bwdw_launch(int B, int C, int H, int W, int L, int KB, int K, bool bf16, const void* x,

@@ -417,6 +417,65 @@ __device__ __forceinline__ void zero_border(float* base, int tid, int nt) {
     }
 }
 
+// The weight gradient's second stage for one channel c: the fixed-order sum
+// of the per-chunk partial tap sums, then scale and normalisation. Taps
+// [0, TA) (base, levels 1..LA) come from partA, the rest (levels LA+1..L)
+// from partB when the plane was split. WG holds 4 L K^2 floats. Run by one
+// workgroup (nthreads lanes, tid its lane); c < C.
+struct FinalizeArgs {
+    const float* partA;
+    int nA, LA;
+    const float* partB;
+    int nB, C, L, KB, K;
+    const float* w_lvl;
+    const float* scale;
+    float* dw_base;
+    float* dw_lvl;
+    float* dscale;
+};
+
+__device__ __forceinline__ void finalize_channel(const FinalizeArgs& f, int c, int tid, int nthreads, float* WG) {
+    const int kb2 = f.KB * f.KB, k2 = f.K * f.K, taps = kb2 + 4 * f.L * k2;
+    const int TA = kb2 + 4 * f.LA * k2, TB = taps - TA, C = f.C;
+    // one tap per lane: the partial sums, the scale and the level tap are
+    // all requested before any is used
+    for (int t = tid; t < taps; t += nthreads) {
+        float sc = 1.f, wv = 0.f;
+        size_t pi = 0;
+        int tap = 0;
+        if (t >= kb2) {
+            const int r = t - kb2, ls = r / k2, l = ls / 4, s = ls - 4 * l;
+            tap = r - ls * k2;
+            pi = ((size_t)l * C + c) * 4 + s;
+            sc = f.scale[pi];
+            wv = f.w_lvl[pi * k2 + tap];
+        }
+        float a = 0.f;   // the sum stays in chunk order
+        if (t < TA) {
+#pragma unroll 8
+            for (int ch = 0; ch < f.nA; ++ch) a += f.partA[((size_t)ch * C + c) * TA + t];
+        } else {
+#pragma unroll 8
+            for (int ch = 0; ch < f.nB; ++ch) a += f.partB[((size_t)ch * C + c) * TB + (t - TA)];
+        }
+        if (t < kb2) {
+            f.dw_base[(size_t)c * kb2 + t] = a;
+        } else {
+            const int l = (t - kb2) / (4 * k2);   // 0-based level
+            a *= 1.0f / (float)(1 << (2 * (l + 1)));
+            f.dw_lvl[pi * k2 + tap] = sc * a;
+            WG[t - kb2] = wv * a;
+        }
+    }
+    __syncthreads();
+    for (int ls = tid; ls < 4 * f.L; ls += nthreads) {
+        const int l = ls / 4, s = ls - 4 * l;
+        float a = 0.f;
+        for (int tap = 0; tap < k2; ++tap) a += WG[ls * k2 + tap];
+        f.dscale[((size_t)l * C + c) * 4 + s] = a;
+    }
+}
+
 // Butterfly of one 2x2 block (a b / c d), unnormalised: the four Haar bands
 // times 2 (the 1/2 factors are folded into the convolution weights).
 __device__ __forceinline__ void haar4(float a, float b, float c, float d, float& ll, float& b1,

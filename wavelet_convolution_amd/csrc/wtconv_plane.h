@@ -33,12 +33,16 @@ namespace wtc {
 // SUMS (with SHIFT > 0): `in` already holds the fp32 plane of 2^SHIFT x
 // 2^SHIFT block sums (as the weight-gradient pass leaves them), so it is
 // loaded as it is instead of being summed from the full-size activations.
+//
+// Workgroups from `nplanes` on run a deferred weight-gradient second stage
+// (fin.C channels) instead: see FinalizeArgs.
 template <class P, typename T, bool FLIP, int SHIFT, typename TO, bool SUMS = false>
 __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU))) void plane_kernel(const T* __restrict__ in,
                                                       const float* __restrict__ w_base,
                                                       const float* __restrict__ w_lvl,
                                                       const float* __restrict__ scale,
-                                                      TO* __restrict__ out, int C) {
+                                                      TO* __restrict__ out, int C,
+                                                      unsigned nplanes, FinalizeArgs fin) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT;
     constexpr int TR = P::TR, TC = P::TC, PB = P::PB, PK = P::PK;
     constexpr int SX = P::SX, H1 = H / 2, W1 = W / 2;
@@ -46,6 +50,10 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     constexpr int NI = P::NI, MI = P::MI, TPR = W1 / TC;
 
     __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
+    if (blockIdx.x >= nplanes) {   // a deferred second stage of the weight gradient
+        finalize_channel(fin, (int)(blockIdx.x - nplanes), threadIdx.x, P::NT, lds);
+        return;
+    }
     float* A = lds;               // x (bordered), later U_2..U_L and Z'_2..Z'_L
     float* Bq = lds + P::ASIZE;   // U_1 (4 bordered bands)
     float* WB = lds + P::LDS_FLOATS;   // base taps (turned for FLIP), padded to KB2P
@@ -289,7 +297,7 @@ hipError_t launch_coarse(const void* in, const float* wl, const float* sc, float
                          hipStream_t stream) {
     const unsigned planes = (unsigned)B * (unsigned)C;
     hipLaunchKernelGGL((plane_kernel<P, T, FLIP, SHIFT, float, SUMS>), dim3(planes), dim3(P::NT), 0, stream,
-                       (const T*)in, (const float*)nullptr, wl, sc, out, C);
+                       (const T*)in, (const float*)nullptr, wl, sc, out, C, planes, FinalizeArgs{});
     return hipGetLastError();
 }
 
@@ -301,10 +309,12 @@ namespace wtc {
 // ColPlan). Same phases and LDS regions as plane_kernel; P3 convolves every
 // level (level 1 included) into registers and writes the results over their
 // own subbands, P4 synthesises each output column strip in closed form.
+// Workgroups from cdiv(B, NPW) * C on run a deferred weight-gradient second
+// stage (fin.C channels) instead: see FinalizeArgs.
 template <class P, typename T, bool FLIP>
 __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
 void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, const float* __restrict__ w_lvl,
-                const float* __restrict__ scale, T* __restrict__ out, int B, int C) {
+                const float* __restrict__ scale, T* __restrict__ out, int B, int C, FinalizeArgs fin) {
     constexpr int H = P::H, W = P::W, L = P::L, KB = P::KB, K = P::K, NT = P::NT, RB = P::RB;
     constexpr int PB = P::PB, PK = P::PK, SX = P::SX, H1 = H / 2, W1 = W / 2;
     constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
@@ -316,6 +326,13 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     float* WL = WB + KB2P;
 
     const int tid = threadIdx.x;
+    {
+        const unsigned ndata = (unsigned)cdiv(B, NPW) * (unsigned)C;
+        if (blockIdx.x >= ndata) {   // a deferred second stage of the weight gradient
+            finalize_channel(fin, (int)(blockIdx.x - ndata), tid, NT, lds);
+            return;
+        }
+    }
     // this workgroup: channel c of images g*NPW .. g*NPW + NPW-1 (those < B)
     const int c = blockIdx.x % C, g = blockIdx.x / C;
     auto live = [&](int p) { return NPW == 1 || g * NPW + p < B; };
@@ -653,22 +670,25 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
 
 // Launchers of the whole-plane kernels: one workgroup per plane
 // (plane_kernel), or per channel and group of NPW images (col_kernel).
+// A non-null `fin` with fin->C > 0 adds fin->C workgroups that run that
+// deferred weight-gradient second stage (its scratch fits the kernel's LDS:
+// the caller checks PlaneEntry::lds_bytes).
 template <class P, typename T, bool FLIP>
 hipError_t launch_plane(const void* in, const float* wb, const float* wl, const float* sc,
-                               void* out, int B, int C, hipStream_t stream) {
-    const unsigned planes = (unsigned)B * (unsigned)C;
-    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, 0, T>), dim3(planes), dim3(P::NT), 0, stream,
-                       (const T*)in, wb, wl, sc, (T*)out, C);
+                               void* out, int B, int C, hipStream_t stream, const FinalizeArgs* fin) {
+    const unsigned planes = (unsigned)B * (unsigned)C, extra = fin ? (unsigned)fin->C : 0u;
+    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, 0, T>), dim3(planes + extra), dim3(P::NT), 0, stream,
+                       (const T*)in, wb, wl, sc, (T*)out, C, planes, fin ? *fin : FinalizeArgs{});
     return hipGetLastError();
 }
 
 template <class P, typename T, bool FLIP>
 hipError_t launch_col(const void* in, const float* wb, const float* wl, const float* sc, void* out,
-                             int B, int C, hipStream_t stream) {
+                             int B, int C, hipStream_t stream, const FinalizeArgs* fin) {
     // one workgroup per channel and group of NPW images
-    const unsigned groups = (unsigned)cdiv(B, P::NPW) * (unsigned)C;
-    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(groups), dim3(P::NT), 0, stream, (const T*)in, wb, wl, sc,
-                       (T*)out, B, C);
+    const unsigned groups = (unsigned)cdiv(B, P::NPW) * (unsigned)C, extra = fin ? (unsigned)fin->C : 0u;
+    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(groups + extra), dim3(P::NT), 0, stream, (const T*)in, wb, wl,
+                       sc, (T*)out, B, C, fin ? *fin : FinalizeArgs{});
     return hipGetLastError();
 }
 

@@ -107,9 +107,11 @@ struct PlanePlan {
     }
 };
 
+// fin: an optional deferred weight-gradient second stage run as extra
+// workgroups of the same launch (null: none)
 typedef hipError_t (*plane_launch_fn)(const void* in, const float* w_base, const float* w_lvl,
                                       const float* scale, void* out, int B, int C,
-                                      hipStream_t stream);
+                                      hipStream_t stream, const FinalizeArgs* fin);
 
 struct PlaneEntry {
     int H, W, L, KB, K;   // the plane in memory (a padded plan's IH, IW)
