@@ -418,6 +418,9 @@ def main() -> int:
                     help="skip the context lines: torch's depthwise convolution and the ConvNeXt-style block")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the brief timing of the other bar workloads")
+    ap.add_argument("--no-other-form", action="store_true",
+                    help="skip the timing of the other backward form (for profiled runs: only the measured "
+                         "form's kernels then run)")
     ap.add_argument("--sets", type=int, default=None,
                     help="rotated input sets (default: enough that x and dy of all sets exceed 512 MiB)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -504,13 +507,15 @@ def main() -> int:
     traffic = None if args.channels_last else read_traffic(cfg.name, dominant, src_hash)
 
     # the other backward form, same inputs and run, as warm
-    for i in range(min(args.warmup, 100)):
-        wl.step(i, not single)
-    other_ms = wl.time_steps(args.steps, lambda i: wl.step(i, not single))
-    other_mean, _ = wl.call_times(args.steps, not single)
-    other = {"backward": "wtconv_bwd_data + wtconv_bwd_weight" if single else "wtconv_bwd",
-             "ms_per_step": round(other_ms, 4), "images_per_s": round(cfg.B / (other_ms * 1e-3), 1),
-             "kernel_ms": {k: round(v, 5) for k, v in other_mean.items()}}
+    other = None
+    if not args.no_other_form:
+        for i in range(min(args.warmup, 100)):
+            wl.step(i, not single)
+        other_ms = wl.time_steps(args.steps, lambda i: wl.step(i, not single))
+        other_mean, _ = wl.call_times(args.steps, not single)
+        other = {"backward": "wtconv_bwd_data + wtconv_bwd_weight" if single else "wtconv_bwd",
+                 "ms_per_step": round(other_ms, 4), "images_per_s": round(cfg.B / (other_ms * 1e-3), 1),
+                 "kernel_ms": {k: round(v, 5) for k, v in other_mean.items()}}
 
     naive = None
     if not args.no_naive:
