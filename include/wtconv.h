@@ -176,13 +176,23 @@ wtconv_status_t wtconv_bwd_weight_noalloc(const wtconv_desc_t *desc, const void 
                                           float *dw_lvl, float *dscale, void *stream);
 
 /* Whole backward pass: dx (as wtconv_bwd_data) and the weight gradients (as
-   wtconv_bwd_weight) in one call. For L = 0 on the planes its kernel covers
-   (56x56, 28x28, 14x14; k_base 5 or 7; planar layout) it is a single pass
-   that reads x and dy once, the fused backward the I/O model counts at
-   5*N*e instead of 6*N*e bytes per step. Other shapes run the two backward
-   calls in stream order on one workspace. Results equal those of the two
-   calls bit for bit (the same multiply-adds in the same order). x and dy
-   must not overlap dx. Workspace:
+   wtconv_bwd_weight) in one call. Results equal those of the two calls bit
+   for bit (the same multiply-adds in the same order); what the call saves
+   depends on the shape (planar layout in each case):
+   - L = 0 on the planes its kernel covers (56x56, 28x28, 14x14; k_base 5 or
+     7): a single pass that reads x and dy once, the fused backward the I/O
+     model counts at 5*N*e instead of 6*N*e bytes per step;
+   - planes split into fine tiles and a coarse level-L0 image (256x256 at
+     L = 4 with kernels 7 and 5, and the 64x64 test plans): the weight pass
+     runs first and leaves the 2^L0-block sums of dy in the workspace; the
+     backward-data pass then takes its coarse levels from those sums instead
+     of reading dy a second time for them;
+   - whole-plane data kernels (the stage planes, 128x128, the family of
+     planes of 56, 28, 14 and 7 pixels): the weight pass runs first and the
+     fixed-order second stage of its reduction runs as extra workgroups of
+     the backward-data launch (one launch fewer);
+   - other shapes: the two backward calls in stream order on one workspace.
+   x and dy must not overlap dx. Workspace:
    wtconv_workspace_size(desc, WTCONV_OP_BWD). */
 wtconv_status_t wtconv_bwd(const wtconv_desc_t *desc, const void *x,
                            const void *dy, const float *w_base,
