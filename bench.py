@@ -222,8 +222,12 @@ def workload_summary(torch, wt, cfg, steps: int, single_pass: bool):
     from wavelet_convolution_amd import iomodel
 
     wl = Workload(torch, wt, cfg, default_sets(cfg), exact_first=False)
-    for i in range(3):
-        wl.step(i, single_pass)
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < WARMUP_SECONDS or n < 10:   # the same warm-up as the main line
+        for i in range(10):
+            wl.step(n + i, single_pass)
+        n += 10
+        torch.cuda.synchronize()
     ms = wl.time_steps(steps, lambda i: wl.step(i, single_pass))
     mean, _ = wl.call_times(steps, single_pass)
     model = iomodel.step_model(cfg.B, cfg.C, cfg.H, cfg.W, cfg.L, cfg.kb, cfg.k, cfg.dtype)
