@@ -282,7 +282,8 @@ void tile_kernel(const T* __restrict__ in, const float* __restrict__ w_base,
 // and one closed-form pass synthesises every output, adding the coarse
 // image. The region's rows are all plane rows (zeros outside the plane), so
 // only the band columns carry a zero border.
-template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int NT_, int RB_, int RL_, int WMAX_ = 4>
+template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int NT_, int RB_, int RL_, int WMAX_ = 4,
+          bool MF_ = false>
 struct ColTilePlan {
     static constexpr int H = H_, W = W_, L0 = L0_, LT = LT_, KB = KB_, K = K_, TH = TH_, NT = NT_;
     static constexpr int RB = RB_, RL = RL_;
@@ -322,7 +323,32 @@ struct ColTilePlan {
     static constexpr int LDS_FLOATS = (ASIZE + BSIZE + 3) / 4 * 4;
     static constexpr int KB2P = kpad4(KB), K2P = kpad4(K);
     static constexpr int WFLOATS = KB2P + 4 * L0 * K2P;
-    static_assert((LDS_FLOATS + WFLOATS) * 4 <= 160 * 1024, "tile does not fit in LDS");
+    // Base convolution on the matrix cores (bf16 activations; see P1 of
+    // coltile_kernel). The x rows the base convolution reads stay in their
+    // bf16 form, x column c at row position XOM + c, rows SXB apart (a
+    // multiple of 8 elements: 16-byte operand reads; 4 dwords of stagger per
+    // row spreads 8 consecutive rows over all banks), in region A, which is
+    // then sized for them rather than for fp32 rows. The banded tap rows (ZL
+    // entries, three bf16 parts of each tap, two copies shifted by one entry
+    // so that every lane's 8 entries start 4-byte aligned) follow the taps.
+    static constexpr bool MF = MF_;
+    static constexpr int XOM = 4, SXB = W + 24, ZL = 48, ZOFF = 15 + (XOM - PB), ZCOPIES = 2;
+    static constexpr int ZFLOATS = ZCOPIES * 3 * KB * ZL / 2;
+    template <typename T>
+    static constexpr bool mf() { return MF && sizeof(T) == 2; }
+    static constexpr int XSIZE_MF = (XROWS * SXB / 2 + 3) / 4 * 4;
+    template <typename T>
+    static constexpr int asize() { return mf<T>() ? (XSIZE_MF > UDEEP ? XSIZE_MF : UDEEP) : ASIZE; }
+    // floats of LDS per workgroup: regions A and B, the taps, the banded taps
+    template <typename T>
+    static constexpr int lds_floats() {
+        return (asize<T>() + BSIZE + 3) / 4 * 4 + WFLOATS + (mf<T>() ? ZFLOATS : 0);
+    }
+    static_assert(!MF || (TH % 16 == 0 && W % 16 == 0 && PB <= XOM && PB + XOM <= 16 && SXB % 8 == 0 &&
+                          ZOFF + KB <= ZL && ((TH / 16) * (W / 16)) % (NT / 64) == 0),
+                  "matrix-core base convolution: 16 x 16 output blocks, whole blocks per wavefront");
+    static_assert(lds_floats<float>() * 4 <= 160 * 1024 && lds_floats<bf16_t>() * 4 <= 160 * 1024,
+                  "tile does not fit in LDS");
     static constexpr int LPB = strip_lanes(W);
     static constexpr int NIB = (TH / RB) * LPB;
     static constexpr int MB = cdiv(NIB, NT);
@@ -331,10 +357,12 @@ struct ColTilePlan {
     static constexpr int IPR = ((W >> 1) + 2 * PK) / CPI;
     static constexpr int NQ = rh(1) * IPR;
     static constexpr int NTILE = H / TH;
-    static constexpr int WG_PER_CU = (160 * 1024) / ((LDS_FLOATS + WFLOATS) * 4);
-    static constexpr int WAVES_PER_EU_LDS = (WG_PER_CU * (NT / 64)) / 4;
-    static constexpr int WAVES_PER_EU =
-        WAVES_PER_EU_LDS < 1 ? 1 : (WAVES_PER_EU_LDS > WMAX_ ? WMAX_ : WAVES_PER_EU_LDS);
+    // occupancy the LDS footprint allows, at most WMAX waves per SIMD
+    template <typename T>
+    static constexpr int waves_per_eu() {
+        const int wg = (160 * 1024) / (lds_floats<T>() * 4), w = (wg * (NT / 64)) / 4;
+        return w < 1 ? 1 : (w > WMAX_ ? WMAX_ : w);
+    }
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -355,7 +383,7 @@ struct ColTilePlan {
 };
 
 template <class P, typename T, bool FLIP>
-__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU)))
+__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::template waves_per_eu<T>())))
 void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, const float* __restrict__ w_lvl,
                     const float* __restrict__ scale, const float* __restrict__ coarse, T* __restrict__ out, int C) {
     constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH, RB = P::RB;
@@ -364,11 +392,16 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     constexpr int NIB = P::NIB, MB = P::MB, LPB = P::LPB;
     constexpr int KB2P = P::KB2P, K2P = P::K2P;
 
-    __shared__ __attribute__((aligned(16))) float lds[P::LDS_FLOATS + P::WFLOATS];
+    // matrix-core base convolution: bf16 activations of a plan that asks for it
+    constexpr bool MF = P::template mf<T>();
+    constexpr int AS = P::template asize<T>();
+    __shared__ __attribute__((aligned(16))) float lds[P::template lds_floats<T>()];
     float* A = lds;               // x rows, later the bands of levels 2..L0
-    float* Bq = lds + P::ASIZE;   // level-1 bands
-    float* WB = lds + P::LDS_FLOATS;
+    float* Bq = lds + AS;         // level-1 bands
+    float* WB = lds + (AS + P::BSIZE + 3) / 4 * 4;
     float* WL = WB + KB2P;
+    uint16_t* const XS = reinterpret_cast<uint16_t*>(A);                        // bf16 x rows (MF)
+    uint16_t* const ZC = reinterpret_cast<uint16_t*>(WL + 4 * L0 * K2P);        // banded taps (MF)
 
     const int tid = threadIdx.x;
     const int lid = xcd_local_index();
@@ -385,8 +418,39 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     };
 
     // ---------------------------------------------------------------- P0
-    for (int t = tid; t < KB2P; t += NT)
-        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
+    if constexpr (MF) {
+        // Banded tap rows: entry e of row (part p, tap row i) is part p of
+        // tap (i, e - ZOFF), zero outside the row; copy cp holds entries
+        // cp, cp + 1, .. of each row from its position 0. The three parts
+        // are the bf16 rounding of the tap, of what that leaves, and of what
+        // remains then: their sum is the fp32 tap exactly, and each product
+        // with a bf16 x is exact in fp32. One thread per (tap row, entry).
+        constexpr int ZL = P::ZL, NC = P::ZCOPIES, NE = ZL + NC - 1;
+        for (int t = tid; t < KB * NE; t += NT) {
+            const int i = udiv(t, NE), e = t - i * NE, j = e - P::ZOFF;
+            float v = 0.f;
+            if (j >= 0 && j < KB) {
+                const int tap = i * KB + j;
+                v = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - tap : tap)];
+            }
+            bf16_t part[3];
+            part[0] = narrow_bf16(v);
+            v -= widen(part[0]);
+            part[1] = narrow_bf16(v);
+            part[2] = narrow_bf16(v - widen(part[1]));
+#pragma unroll
+            for (int cp = 0; cp < NC; ++cp) {
+                const int pos = e - cp;
+                if (pos >= 0 && pos < ZL) {
+#pragma unroll
+                    for (int pt = 0; pt < 3; ++pt) ZC[((cp * 3 + pt) * KB + i) * ZL + pos] = part[pt];
+                }
+            }
+        }
+    } else {
+        for (int t = tid; t < KB2P; t += NT)
+            WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
+    }
     for (int t = tid; t < 4 * L0 * K2P; t += NT) {
         const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
         const size_t pi = ((size_t)l * C + c) * 4 + s;
@@ -400,12 +464,17 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
         // and four columns from 4u (band cells 2u, 2u+1 of band row i); rows
         // outside the plane load nothing and store zeros (the zero padding of
         // every level's band grid).
-        constexpr int XB = SX - W, XB1 = S1 - W1;
+        // (bf16 x rows: border columns written as 32-bit words, pairs of entries)
+        constexpr int XB = MF ? (P::SXB - W) / 2 : SX - W, XB1 = S1 - W1;
         static_assert(XB > 0 && XB1 > 0 && XO + W <= SX, "border columns");
+        static_assert(!MF || (P::XOM % 2 == 0 && (P::SXB - W) % 2 == 0), "bf16 border pairs");
         for (int i = tid; i < P::XROWS * XB + 4 * P::rh(1) * XB1; i += NT) {
             if (i < P::XROWS * XB) {
                 const int r = udiv(i, XB), q = i - r * XB;
-                A[r * SX + (q < XO ? q : q + W)] = 0.f;
+                if constexpr (MF)
+                    reinterpret_cast<uint32_t*>(XS)[(r * P::SXB + (2 * q < P::XOM ? 2 * q : 2 * q + W)) / 2] = 0u;
+                else
+                    A[r * SX + (q < XO ? q : q + W)] = 0.f;
             } else {
                 const int j = i - P::XROWS * XB, rb = udiv(j, XB1), q = j - rb * XB1;   // rb = band * rh(1) + row
                 Bq[rb * S1 + (q < PK ? q : q + W1)] = 0.f;
@@ -440,9 +509,17 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
             widen_raw<T, 4>(v0[k], f0);
             widen_raw<T, 4>(v1[k], f1);
             const int xr = 2 * ii - P::XR0;   // kept x rows: those the base convolution reads
-            float* const xo = A + xr * SX + XO + 4 * uu;
-            if (xr >= 0 && xr < P::XROWS) store_vec<4>(xo, f0);
-            if (xr + 1 >= 0 && xr + 1 < P::XROWS) store_vec<4>(xo + SX, f1);
+            if constexpr (MF) {
+                // as loaded: four bf16 per row, one 64-bit store
+                uint2* const xo = reinterpret_cast<uint2*>(XS + xr * P::SXB + P::XOM + 4 * uu);
+                if (xr >= 0 && xr < P::XROWS) *xo = make_uint2(v0[k].w[0], v0[k].w[1]);
+                if (xr + 1 >= 0 && xr + 1 < P::XROWS)
+                    *reinterpret_cast<uint2*>(XS + (xr + 1) * P::SXB + P::XOM + 4 * uu) = make_uint2(v1[k].w[0], v1[k].w[1]);
+            } else {
+                float* const xo = A + xr * SX + XO + 4 * uu;
+                if (xr >= 0 && xr < P::XROWS) store_vec<4>(xo, f0);
+                if (xr + 1 >= 0 && xr + 1 < P::XROWS) store_vec<4>(xo + SX, f1);
+            }
             float b[4][2];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
@@ -455,13 +532,57 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     __syncthreads();
 
     // ---------------------------------------------------------------- P1
-    float yb[MB][RB];
+    // matrix-core form: 16 x 16 output blocks, NBW per wavefront
+    constexpr int NWV = NT / 64, NBC = W / 16, NBW = MF ? (TH / 16) * NBC / NWV : 1;
+    const int lane = tid & 63, wv = tid >> 6, mn = lane & 15, mq = lane >> 4;
+    float yb[MF ? NBW : MB][MF ? 4 : RB];
+    if constexpr (MF) {
+        // Output block (h0, w0): y[h0+m][w0+n] = sum over tap rows i and tap
+        // parts of sum_k X_i[m][k] T_i[k][n], with X_i[m][k] = x[h0+m+i-PB]
+        // [w0-XOM+k] (32 consecutive x columns of one row) and T_i[k][n] =
+        // part of tap (i, k-n-(XOM-PB)) where that lies in the row, else 0:
+        // one 16x16x32 bf16 matrix product each, fp32 accumulation. Lane l
+        // holds X row m = l%16, columns 8(l/16)..+7; T column n = l%16, rows
+        // 8(l/16)..+7 (banded-table entries 8(l/16)-n+15..+7); result rows
+        // 4(l/16)..+3 of column n.
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        constexpr int ZL = P::ZL, SXB = P::SXB;
+        const int e0 = 8 * mq - mn + 15, cp = e0 & 1, ea = e0 - cp;
+        f32x4 acc[NBW];
 #pragma unroll
-    for (int it = 0; it < MB; ++it) {
-        const int item = tid + it * NT;
-        if (NIB % NT == 0 || item < NIB) {
-            const int rb = item / LPB, w = item - rb * LPB;
-            if (LPB == W || w < W) conv_col<KB, RB, SX>(A + XO - PB + (rb * RB) * SX + w, WB, yb[it]);
+        for (int bb = 0; bb < NBW; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            bf16x8 tb[3];
+#pragma unroll
+            for (int part = 0; part < 3; ++part) {
+                // 4-byte aligned entries: four 32-bit reads
+                const uint32_t* zp = reinterpret_cast<const uint32_t*>(ZC + ((cp * 3 + part) * KB + i) * ZL + ea);
+                tb[part] = __builtin_bit_cast(bf16x8, make_uint4(zp[0], zp[1], zp[2], zp[3]));
+            }
+#pragma unroll
+            for (int bb = 0; bb < NBW; ++bb) {
+                const int blk = wv + bb * NWV, rbk = blk / NBC, cbk = blk - rbk * NBC;
+                const uint4 xv = *reinterpret_cast<const uint4*>(XS + (16 * rbk + mn + i) * SXB + 16 * cbk + 8 * mq);
+                const bf16x8 xa = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+                for (int part = 0; part < 3; ++part)
+                    acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, tb[part], acc[bb], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb)
+#pragma unroll
+            for (int o = 0; o < 4; ++o) yb[bb][o] = acc[bb][o];
+    } else {
+#pragma unroll
+        for (int it = 0; it < MB; ++it) {
+            const int item = tid + it * NT;
+            if (NIB % NT == 0 || item < NIB) {
+                const int rb = item / LPB, w = item - rb * LPB;
+                if (LPB == W || w < W) conv_col<KB, RB, SX>(A + XO - PB + (rb * RB) * SX + w, WB, yb[it]);
+            }
         }
     }
     __syncthreads();   // x is dead: levels 2..L0 go over it
@@ -541,32 +662,30 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     static_assert(RB % 2 == 0, "bf16 rows are narrowed in pairs");
     const float* __restrict__ ctile = coarse ? coarse + ((size_t)plane * (H >> L0) + (r0 >> L0)) * CW : nullptr;
     T* __restrict__ dtile = dst + (size_t)r0 * W;
-#pragma unroll
-    for (int it = 0; it < MB; ++it) {
-        const int item = tid + it * NT;
-        if (!(NIB % NT == 0 || item < NIB)) continue;
-        const int rb = item / LPB, w = item - rb * LPB, h0 = rb * RB;
-        if (!(LPB == W || w < W)) continue;
+    // one strip of R output rows from h0 in column w, base results yv
+    auto synth_store = [&](auto rc, const int h0, const int w, const float* yv) {
+        constexpr int RS = decltype(rc)::value;
+        static_assert(RS % (1 << L0) == 0 && RS % 2 == 0, "strips of whole 2^L0 blocks, rows in pairs");
         // From the coarse image down to level 1, carry[p] is what the
         // coarser levels add to every row of level-l block p; level l splits
         // it into its two half-blocks as carry + a +- b.
-        float carry[RB];
+        float carry[RS];
         if (ctile) {
             const float* const cp = ctile + (uint32_t)((h0 >> L0) * CW + (w >> L0));
 #pragma unroll
-            for (int p = 0; p < (RB >> L0); ++p) carry[p] = cp[p * CW];
+            for (int p = 0; p < (RS >> L0); ++p) carry[p] = cp[p * CW];
         } else {
 #pragma unroll
-            for (int p = 0; p < (RB >> L0); ++p) carry[p] = 0.f;
+            for (int p = 0; p < (RS >> L0); ++p) carry[p] = 0.f;
         }
         P::for_levels([&](auto lc) {
             constexpr int l = L0 + 1 - decltype(lc)::value;   // L0, ..., 1
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
             const float* Zl = ubase(std::integral_constant<int, l>{}) + ((G >> l) + (h0 >> l)) * Sl + PK + (w >> l);
             const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
-            float next[RB >> (l - 1)];
+            float next[RS >> (l - 1)];
 #pragma unroll
-            for (int p = 0; p < (RB >> l); ++p) {
+            for (int p = 0; p < (RS >> l); ++p) {
                 const float* z = Zl + p * Sl;
                 const float a = __builtin_fmaf(sw, z[2 * BSl], z[0]) + carry[p];
                 const float b = __builtin_fmaf(sw, z[3 * BSl], z[BSl]);
@@ -574,14 +693,14 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
                 next[2 * p + 1] = a - b;
             }
 #pragma unroll
-            for (int q = 0; q < (RB >> (l - 1)); ++q) carry[q] = next[q];
+            for (int q = 0; q < (RS >> (l - 1)); ++q) carry[q] = next[q];
         });
         T* const out_col = dtile + (uint32_t)(h0 * W + w);
         if constexpr (sizeof(T) == 2) {
             // two rows per conversion: the low half to row o, the high half to o + 1
 #pragma unroll
-            for (int o = 0; o < RB; o += 2) {
-                uint32_t pr = narrow_bf16x2(yb[it][o] + carry[o], yb[it][o + 1] + carry[o + 1]);
+            for (int o = 0; o < RS; o += 2) {
+                uint32_t pr = narrow_bf16x2(yv[o] + carry[o], yv[o + 1] + carry[o + 1]);
                 // opaque to the compiler, which would otherwise convert the
                 // high half again on its own instead of storing it directly
                 asm volatile("" : "+v"(pr));
@@ -590,7 +709,24 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
             }
         } else {
 #pragma unroll
-            for (int o = 0; o < RB; ++o) out_col[o * W] = yb[it][o] + carry[o];
+            for (int o = 0; o < RS; ++o) out_col[o * W] = yv[o] + carry[o];
+        }
+    };
+    if constexpr (MF) {
+        // the matrix-core blocks: rows 4(l/16)..+3 of column l%16 of each block
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int blk = wv + bb * NWV, rbk = blk / NBC, cbk = blk - rbk * NBC;
+            synth_store(std::integral_constant<int, 4>{}, 16 * rbk + 4 * mq, 16 * cbk + mn, yb[bb]);
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < MB; ++it) {
+            const int item = tid + it * NT;
+            if (!(NIB % NT == 0 || item < NIB)) continue;
+            const int rb = item / LPB, w = item - rb * LPB;
+            if (!(LPB == W || w < W)) continue;
+            synth_store(std::integral_constant<int, RB>{}, rb * RB, w, yb[it]);
         }
     }
 }
@@ -667,7 +803,7 @@ typedef PlanePlan<32, 32, 1, 1, 5, 256, 1, 1> CP_32_L1_k5;
 // fine-pass plans: column-strip tiles of 16 rows on 512 lanes at 256x256
 // (measured against 8- and 32-row tiles and 256 lanes); micro-tile fine
 // passes for the 64x64 test shapes
-typedef ColTilePlan<256, 256, 2, 4, 7, 5, 16, 512, 8, 8> CT_256_L2of4_k75;
+typedef ColTilePlan<256, 256, 2, 4, 7, 5, 16, 512, 8, 8, 6, true> CT_256_L2of4_k75;
 typedef TilePlan<64, 64, 2, 4, 3, 3, 8, 128, 1, 1> FP_64_L2of4_k33;
 typedef TilePlan<64, 64, 1, 2, 5, 5, 16, 128, 1, 2> FP_64_L1of2_k55;
 
