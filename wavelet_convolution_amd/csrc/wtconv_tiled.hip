@@ -328,12 +328,16 @@ struct ColTilePlan {
     // bf16 form, x column c at row position XOM + c, rows SXB apart (a
     // multiple of 8 elements: 16-byte operand reads; 4 dwords of stagger per
     // row spreads 8 consecutive rows over all banks), in region A, which is
-    // then sized for them rather than for fp32 rows. The banded tap rows (ZL
-    // entries, three bf16 parts of each tap, two copies shifted by one entry
-    // so that every lane's 8 entries start 4-byte aligned) follow the taps.
+    // then sized for them rather than for fp32 rows. The banded tap rows
+    // follow the taps, as 32-bit words of overlapping entry pairs (word w =
+    // entries w and w + 1; ZL words per row, three bf16 parts of each tap):
+    // a lane's 8 entries from any e are the words e, e+2, e+4, e+6.
+    // Half of the wavefronts run the matrix products while the other half
+    // runs the level-1 convolution (MFW blocks per matrix wavefront).
     static constexpr bool MF = MF_;
-    static constexpr int XOM = 4, SXB = W + 24, ZL = 48, ZOFF = 15 + (XOM - PB), ZCOPIES = 2;
-    static constexpr int ZFLOATS = ZCOPIES * 3 * KB * ZL / 2;
+    static constexpr int XOM = 4, SXB = W + 24, ZL = 48, ZOFF = 15 + (XOM - PB);
+    static constexpr int ZFLOATS = 3 * KB * ZL;
+    static constexpr int NW = NT / 64, MFW = MF ? (TH / 16) * (W / 16) / (NW / 2) : 1;
     template <typename T>
     static constexpr bool mf() { return MF && sizeof(T) == 2; }
     static constexpr int XSIZE_MF = (XROWS * SXB / 2 + 3) / 4 * 4;
@@ -345,7 +349,7 @@ struct ColTilePlan {
         return (asize<T>() + BSIZE + 3) / 4 * 4 + WFLOATS + (mf<T>() ? ZFLOATS : 0);
     }
     static_assert(!MF || (TH % 16 == 0 && W % 16 == 0 && PB <= XOM && PB + XOM <= 16 && SXB % 8 == 0 &&
-                          ZOFF + KB <= ZL && ((TH / 16) * (W / 16)) % (NT / 64) == 0),
+                          ZOFF + KB <= ZL && NW % 2 == 0 && ((TH / 16) * (W / 16)) % (NW / 2) == 0),
                   "matrix-core base convolution: 16 x 16 output blocks, whole blocks per wavefront");
     static_assert(lds_floats<float>() * 4 <= 160 * 1024 && lds_floats<bf16_t>() * 4 <= 160 * 1024,
                   "tile does not fit in LDS");
@@ -354,6 +358,10 @@ struct ColTilePlan {
     static constexpr int MB = cdiv(NIB, NT);
     static constexpr int lpl(int l) { return strip_lanes(W >> l); }
     static constexpr int nil(int l) { return 4 * (hout(l) / rl(l)) * lpl(l); }
+    // threads of the level convolutions: all of them, or (matrix-core form)
+    // the upper half for level 1 and the lower half for level 2
+    static constexpr int lvl_t0(int l, bool mf) { return mf && l == 1 ? NT / 2 : 0; }
+    static constexpr int lvl_nt(int l, bool mf) { return mf ? NT / 2 : NT; }
     static constexpr int IPR = ((W >> 1) + 2 * PK) / CPI;
     static constexpr int NQ = rh(1) * IPR;
     static constexpr int NTILE = H / TH;
@@ -420,32 +428,31 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     // ---------------------------------------------------------------- P0
     if constexpr (MF) {
         // Banded tap rows: entry e of row (part p, tap row i) is part p of
-        // tap (i, e - ZOFF), zero outside the row; copy cp holds entries
-        // cp, cp + 1, .. of each row from its position 0. The three parts
-        // are the bf16 rounding of the tap, of what that leaves, and of what
-        // remains then: their sum is the fp32 tap exactly, and each product
-        // with a bf16 x is exact in fp32. One thread per (tap row, entry).
-        constexpr int ZL = P::ZL, NC = P::ZCOPIES, NE = ZL + NC - 1;
-        for (int t = tid; t < KB * NE; t += NT) {
-            const int i = udiv(t, NE), e = t - i * NE, j = e - P::ZOFF;
-            float v = 0.f;
-            if (j >= 0 && j < KB) {
-                const int tap = i * KB + j;
-                v = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - tap : tap)];
-            }
-            bf16_t part[3];
-            part[0] = narrow_bf16(v);
-            v -= widen(part[0]);
-            part[1] = narrow_bf16(v);
-            part[2] = narrow_bf16(v - widen(part[1]));
+        // tap (i, e - ZOFF), zero outside the row, stored as words of entry
+        // pairs (e, e + 1). The three parts are the bf16 rounding of the tap,
+        // of what that leaves, and of what remains then: their sum is the
+        // fp32 tap exactly, and each product with a bf16 x is exact in fp32.
+        // One thread per (tap row, word).
+        constexpr int ZL = P::ZL;
+        for (int t = tid; t < KB * ZL; t += NT) {
+            const int i = udiv(t, ZL), w = t - i * ZL;
+            bf16_t part[2][3];
 #pragma unroll
-            for (int cp = 0; cp < NC; ++cp) {
-                const int pos = e - cp;
-                if (pos >= 0 && pos < ZL) {
-#pragma unroll
-                    for (int pt = 0; pt < 3; ++pt) ZC[((cp * 3 + pt) * KB + i) * ZL + pos] = part[pt];
+            for (int h = 0; h < 2; ++h) {
+                const int j = w + h - P::ZOFF;
+                float v = 0.f;
+                if (j >= 0 && j < KB) {
+                    const int tap = i * KB + j;
+                    v = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - tap : tap)];
                 }
+                part[h][0] = narrow_bf16(v);
+                v -= widen(part[h][0]);
+                part[h][1] = narrow_bf16(v);
+                part[h][2] = narrow_bf16(v - widen(part[h][1]));
             }
+            uint32_t* const zw = reinterpret_cast<uint32_t*>(ZC);
+#pragma unroll
+            for (int pt = 0; pt < 3; ++pt) zw[(pt * KB + i) * ZL + w] = (uint32_t)part[0][pt] | ((uint32_t)part[1][pt] << 16);
         }
     } else {
         for (int t = tid; t < KB2P; t += NT)
@@ -532,49 +539,79 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     __syncthreads();
 
     // ---------------------------------------------------------------- P1
-    // matrix-core form: 16 x 16 output blocks, NBW per wavefront
-    constexpr int NWV = NT / 64, NBC = W / 16, NBW = MF ? (TH / 16) * NBC / NWV : 1;
+    // matrix-core form: 16 x 16 output blocks, MFW on each of the lower half
+    // of the wavefronts; the upper half convolves level 1 meanwhile
+    constexpr int NWV = NT / 64, NBC = W / 16, NBW = P::MFW;
     const int lane = tid & 63, wv = tid >> 6, mn = lane & 15, mq = lane >> 4;
     float yb[MF ? NBW : MB][MF ? 4 : RB];
-    if constexpr (MF) {
-        // Output block (h0, w0): y[h0+m][w0+n] = sum over tap rows i and tap
-        // parts of sum_k X_i[m][k] T_i[k][n], with X_i[m][k] = x[h0+m+i-PB]
-        // [w0-XOM+k] (32 consecutive x columns of one row) and T_i[k][n] =
-        // part of tap (i, k-n-(XOM-PB)) where that lies in the row, else 0:
-        // one 16x16x32 bf16 matrix product each, fp32 accumulation. Lane l
-        // holds X row m = l%16, columns 8(l/16)..+7; T column n = l%16, rows
-        // 8(l/16)..+7 (banded-table entries 8(l/16)-n+15..+7); result rows
-        // 4(l/16)..+3 of column n.
-        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-        typedef float f32x4 __attribute__((ext_vector_type(4)));
-        constexpr int ZL = P::ZL, SXB = P::SXB;
-        const int e0 = 8 * mq - mn + 15, cp = e0 & 1, ea = e0 - cp;
-        f32x4 acc[NBW];
+    // level convolutions: strips of rl(l) output rows x 1 column of one band,
+    // on threads lvl_t0 .. lvl_t0 + lvl_nt
+    auto level_items = [&](auto lc, auto&& f) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int wl = W >> l, R = P::rl(l), NS = P::hout(l) / R, LP = P::lpl(l), NIl = P::nil(l);
+        constexpr int T0 = P::lvl_t0(l, MF), TN = P::lvl_nt(l, MF);
+        const int lt = tid - T0;
+        if (lt < 0 || lt >= TN) return;
 #pragma unroll
-        for (int bb = 0; bb < NBW; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-            bf16x8 tb[3];
-#pragma unroll
-            for (int part = 0; part < 3; ++part) {
-                // 4-byte aligned entries: four 32-bit reads
-                const uint32_t* zp = reinterpret_cast<const uint32_t*>(ZC + ((cp * 3 + part) * KB + i) * ZL + ea);
-                tb[part] = __builtin_bit_cast(bf16x8, make_uint4(zp[0], zp[1], zp[2], zp[3]));
-            }
-#pragma unroll
-            for (int bb = 0; bb < NBW; ++bb) {
-                const int blk = wv + bb * NWV, rbk = blk / NBC, cbk = blk - rbk * NBC;
-                const uint4 xv = *reinterpret_cast<const uint4*>(XS + (16 * rbk + mn + i) * SXB + 16 * cbk + 8 * mq);
-                const bf16x8 xa = __builtin_bit_cast(bf16x8, xv);
-#pragma unroll
-                for (int part = 0; part < 3; ++part)
-                    acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, tb[part], acc[bb], 0, 0, 0);
+        for (int it = 0; it < cdiv(NIl, TN); ++it) {
+            const int item = lt + it * TN;
+            if (NIl % TN == 0 || item < NIl) {
+                const int s = item / (NS * LP), rem = item - s * (NS * LP);
+                const int rs = rem / LP, j = rem - rs * LP;
+                if (LP == wl || j < wl) f(it, s, (G >> l) + rs * R, j);
             }
         }
+    };
+    float z1[cdiv(P::nil(1), P::lvl_nt(1, MF))][P::rl(1)];
+    auto level1_conv = [&]() {
+        level_items(std::integral_constant<int, 1>{}, [&](int it, int s, int row, int j) {
+            conv_col<K, P::rl(1), S1>(Bq + s * BS1 + (row - PK) * S1 + j, WL + s * K2P, z1[it]);
+        });
+    };
+    if constexpr (MF) {
+        if (wv < NWV / 2) {
+            // Output block (h0, w0): y[h0+m][w0+n] = sum over tap rows i and
+            // tap parts of sum_k X_i[m][k] T_i[k][n], with X_i[m][k] =
+            // x[h0+m+i-PB][w0-XOM+k] (32 consecutive x columns of one row) and
+            // T_i[k][n] = part of tap (i, k-n-(XOM-PB)) where that lies in the
+            // row, else 0: one 16x16x32 bf16 matrix product each, fp32
+            // accumulation. Lane l holds X row m = l%16, columns 8(l/16)..+7;
+            // T column n = l%16, rows 8(l/16)..+7 (banded-table entries
+            // 8(l/16)-n+15..+7); result rows 4(l/16)..+3 of column n.
+            typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            constexpr int ZL = P::ZL, SXB = P::SXB;
+            const int e0 = 8 * mq - mn + 15;
+            const uint32_t* const zw = reinterpret_cast<const uint32_t*>(ZC) + e0;
+            f32x4 acc[NBW];
 #pragma unroll
-        for (int bb = 0; bb < NBW; ++bb)
+            for (int bb = 0; bb < NBW; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int o = 0; o < 4; ++o) yb[bb][o] = acc[bb][o];
+            for (int i = 0; i < KB; ++i) {
+                bf16x8 tb[3];
+#pragma unroll
+                for (int part = 0; part < 3; ++part) {
+                    const uint32_t* zp = zw + (part * KB + i) * ZL;
+                    tb[part] = __builtin_bit_cast(bf16x8, make_uint4(zp[0], zp[2], zp[4], zp[6]));
+                }
+#pragma unroll
+                for (int bb = 0; bb < NBW; ++bb) {
+                    const int blk = wv + bb * (NWV / 2), rbk = blk / NBC, cbk = blk - rbk * NBC;
+                    const uint4 xv =
+                        *reinterpret_cast<const uint4*>(XS + (16 * rbk + mn + i) * SXB + 16 * cbk + 8 * mq);
+                    const bf16x8 xa = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+                    for (int part = 0; part < 3; ++part)
+                        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, tb[part], acc[bb], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int bb = 0; bb < NBW; ++bb)
+#pragma unroll
+                for (int o = 0; o < 4; ++o) yb[bb][o] = acc[bb][o];
+        } else {
+            level1_conv();
+        }
     } else {
 #pragma unroll
         for (int it = 0; it < MB; ++it) {
@@ -614,26 +651,11 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     });
 
     // ---------------------------------------------------------------- P3
-    // every fine level: strips of rl(l) output rows x 1 column of one band
-    auto level_items = [&](auto lc, auto&& f) {
-        constexpr int l = decltype(lc)::value;
-        constexpr int wl = W >> l, R = P::rl(l), NS = P::hout(l) / R, LP = P::lpl(l), NIl = P::nil(l);
-#pragma unroll
-        for (int it = 0; it < cdiv(NIl, NT); ++it) {
-            const int item = tid + it * NT;
-            if (NIl % NT == 0 || item < NIl) {
-                const int s = item / (NS * LP), rem = item - s * (NS * LP);
-                const int rs = rem / LP, j = rem - rs * LP;
-                if (LP == wl || j < wl) f(it, s, (G >> l) + rs * R, j);
-            }
-        }
-    };
-    float z1[cdiv(P::nil(1), NT)][P::rl(1)];
-    float z2[L0 >= 2 ? cdiv(P::nil(L0 >= 2 ? 2 : 1), NT) : 1][P::rl(L0 >= 2 ? 2 : 1)];
+    // every fine level into registers (level 1 already, in the matrix-core
+    // form), then written over its own bands
+    float z2[L0 >= 2 ? cdiv(P::nil(L0 >= 2 ? 2 : 1), P::lvl_nt(2, MF)) : 1][P::rl(L0 >= 2 ? 2 : 1)];
     static_assert(L0 <= 2, "fine levels: one or two");
-    level_items(std::integral_constant<int, 1>{}, [&](int it, int s, int row, int j) {
-        conv_col<K, P::rl(1), S1>(Bq + s * BS1 + (row - PK) * S1 + j, WL + s * K2P, z1[it]);
-    });
+    if constexpr (!MF) level1_conv();
     if constexpr (L0 >= 2) {
         constexpr int S2 = P::su(2), BS2 = P::bandsz(2), U2 = P::uoff(2);
         level_items(std::integral_constant<int, 2>{}, [&](int it, int s, int row, int j) {
@@ -714,10 +736,12 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     };
     if constexpr (MF) {
         // the matrix-core blocks: rows 4(l/16)..+3 of column l%16 of each block
+        if (wv < NWV / 2) {
 #pragma unroll
-        for (int bb = 0; bb < NBW; ++bb) {
-            const int blk = wv + bb * NWV, rbk = blk / NBC, cbk = blk - rbk * NBC;
-            synth_store(std::integral_constant<int, 4>{}, 16 * rbk + 4 * mq, 16 * cbk + mn, yb[bb]);
+            for (int bb = 0; bb < NBW; ++bb) {
+                const int blk = wv + bb * (NWV / 2), rbk = blk / NBC, cbk = blk - rbk * NBC;
+                synth_store(std::integral_constant<int, 4>{}, 16 * rbk + 4 * mq, 16 * cbk + mn, yb[bb]);
+            }
         }
     } else {
 #pragma unroll
