@@ -69,7 +69,7 @@ hipError_t launch_bwdw_finalize(const float* partA, int nA, int LA, const float*
 // wavefronts). A lane keeps one accumulator array for the whole chunk: the
 // base taps (group A) or the taps of every fine level, level l at offset
 // (l-1) K² (group B).
-template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int NT_ = 512>
+template <int H_, int W_, int L0_, int LT_, int KB_, int K_, int TH_, int NT_ = 512, bool MF_ = false>
 struct TileBwPlan {
     static constexpr int H = H_, W = W_, L0 = L0_, LT = LT_, KB = KB_, K = K_, TH = TH_;
     static constexpr int L = L0;   // levels handled here (role helpers below)
@@ -125,6 +125,26 @@ struct TileBwPlan {
     static constexpr int WAVES_PER_EU_REG = 512 / (REGS <= 128 ? 128 : (REGS <= 168 ? 168 : 256));
     static constexpr int WAVES_PER_EU_MIN = WAVES_PER_EU_LDS < WAVES_PER_EU_REG ? WAVES_PER_EU_LDS : WAVES_PER_EU_REG;
     static constexpr int WAVES_PER_EU = WAVES_PER_EU_MIN < 1 ? 1 : WAVES_PER_EU_MIN;
+
+    // Matrix-core form for bf16 activations (tile_bwdw_mf_kernel): the base
+    // taps as 16x16x32 bf16 matrix products, every wavefront one pair of dy
+    // rows; the level taps on all wavefronts (each band on NT/4 lanes). LDS:
+    // the x rows the base taps read as bf16 (XRM rows, SXBM apart), dy as
+    // words of overlapping bf16 pairs (word DOFF + c = dy[c], dy[c+1]; SDP
+    // words a row; zero outside the plane), then the level bands U and V.
+    static constexpr bool MF = MF_;
+    static constexpr int XRM = TH + 2 * PB, SXBM = W + 8, DOFF = 8, SDP = W + 48, BLM = NT / 4;
+    static constexpr int ACCM = L0 * K * K;
+    static constexpr int XSM = (XRM * SXBM / 2 + 3) / 4 * 4, DPM = TH * SDP;
+    static constexpr int DATAM = XSM + DPM + UTOT + VTOT, REDM = NW * (256 + ACCM);
+    static constexpr int MF_FLOATS = DATAM > REDM ? DATAM : REDM;
+    static constexpr int band_rows_mf(int l) { return pick_rows(TH >> l, W >> l, BLM, K); }
+    static_assert(!MF || (TH / 2 == NW && W % 32 == 0 && KB <= 7 && 7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
+                          MF_FLOATS * 4 <= 160 * 1024),
+                  "matrix-core weight gradient: one dy row pair per wavefront, 32-column chunks, taps up to 7x7");
+    static constexpr int WAVES_PER_EU_MF = ((160 * 1024) / (MF_FLOATS * 4)) * NW / 4 < 1
+                                               ? 1
+                                               : ((160 * 1024) / (MF_FLOATS * 4)) * NW / 4;
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -346,6 +366,259 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
     }
 }
 
+// Matrix-core weight gradient of the fine tiles (bf16 activations): the same
+// units, outputs and second stage as tile_bwdw_kernel, the base taps as
+// bf16 matrix products (the products of bf16 values are exact in fp32).
+// For the dy row pair (h, h+1) and a chunk of 32 x columns w0..w0+31:
+//   D[m][n] += sum_k X[m][k] Y[k][n],  X[m][k] = x[h-PB+m][w0+k],
+//   Y[k][n] = dy[h + n/8][w0 + k - n%8 + PB],
+// so D[i][j] (n < 8) collects tap (i, j) from dy row h and D[i+1][8+j] tap
+// (i, j) from dy row h+1: G[i][j] = sum over wavefronts of D[i][j] + D[i+1][8+j]
+// (rows m >= 8 and columns n%8 >= KB are not taps; their lanes read valid
+// LDS words whose products are discarded). Lane l holds X row l%16 (row 7 for
+// l%16 > 7), columns 8(l/16)..+7, and Y column l%16, rows 8(l/16)..+7 (dy
+// words at a lane-dependent column: the pair words make any start 4-byte
+// aligned); D rows 4(l/16)..+3 of column l%16.
+// The level taps run on every wavefront: band wave%4 of each fine level, on
+// the lanes of waves band and band + 4.
+template <class P>
+__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU_MF)))
+void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, float* __restrict__ part,
+                         float* __restrict__ px, float* __restrict__ pdy, int B, int C, int upc) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH, NW = P::NW;
+    constexpr int PB = P::PB, PK = P::PK, G = P::G, RH0 = P::RH0, W1 = W / 2;
+    constexpr int XRM = P::XRM, SXBM = P::SXBM, DOFF = P::DOFF, SDP = P::SDP, BLM = P::BLM, ACCM = P::ACCM;
+    constexpr int QW = W / 4;                       // 4-column items per row
+    constexpr int NQX = (RH0 / 2) * QW, NQD = (TH / 2) * QW;
+    constexpr int MQX = cdiv(NQX, NT), MQD = cdiv(NQD, NT);
+    static_assert(W % 4 == 0 && NQD % NT == 0, "whole dy items per thread");
+
+    __shared__ __attribute__((aligned(16))) float lds[P::MF_FLOATS];
+    uint16_t* const XS = reinterpret_cast<uint16_t*>(lds);
+    uint32_t* const DP = reinterpret_cast<uint32_t*>(lds + P::XSM);
+    uint16_t* const DP16 = reinterpret_cast<uint16_t*>(DP);
+    float* const U = lds + P::XSM + P::DPM;
+    float* const Vb = U + P::UTOT;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int band = wave & 3, blane = ((wave >> 2) << 6) + lane;
+    const int c = blockIdx.x % C, chunk = blockIdx.x / C;
+    const int nunits = B * P::NTILE;
+    const int u0 = chunk * upc, u1 = min(nunits, u0 + upc);
+
+    // once: every dy pair word zero (the interior halves are rewritten per
+    // unit, the words outside the plane stay zero); the band border columns
+    for (int i = tid; i < TH * SDP; i += NT) DP[i] = 0u;
+    P::for_levels([&](auto lc) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
+        float* Ul = U + P::uoff(l);
+        for (int i = tid; i < 4 * rl * (Sl - wl); i += NT) {
+            const int b = i / (rl * (Sl - wl)), j = i - b * (rl * (Sl - wl));
+            const int r = j / (Sl - wl), q = j - r * (Sl - wl);
+            Ul[b * BSl + r * Sl + (q < PK ? q : q + wl)] = 0.f;
+        }
+    });
+
+    float acc[ACCM];
+#pragma unroll
+    for (int t = 0; t < ACCM; ++t) acc[t] = 0.f;
+    f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
+
+    // x: region rows 2ii, 2ii+1 (plane rows r0-G+2ii..), four columns from
+    // 4uu; dy: tile rows 2ii, 2ii+1. Rows outside the plane load as zeros.
+    RawVec<bf16_t, 4> vx0[MQX], vx1[MQX], vd0[MQD], vd1[MQD];
+    auto issue_loads = [&](int u) {
+        const int b = u / P::NTILE, r0 = (u - b * P::NTILE) * TH;
+        const size_t plane = (size_t)b * C + c;
+        const bf16_t* __restrict__ xs = x + plane * H * W;
+        const bf16_t* __restrict__ ds = dy + plane * H * W + (size_t)r0 * W;
+#pragma unroll
+        for (int k = 0; k < MQX; ++k) {
+            const int q = tid + k * NT;
+            const int ii = udiv(q, QW), uu = q - ii * QW, pr = r0 - G + 2 * ii;
+            const bool inside = (NQX % NT == 0 || q < NQX) && pr >= 0 && pr < H;
+            const bf16_t* s0 = xs + (inside ? (uint32_t)(pr * W + 4 * uu) : 0u);
+            load_raw<bf16_t, 4>(s0, vx0[k]);
+            load_raw<bf16_t, 4>(s0 + (inside ? W : 0), vx1[k]);
+#pragma unroll
+            for (int e = 0; e < RawVec<bf16_t, 4>::N; ++e) {
+                vx0[k].w[e] = inside ? vx0[k].w[e] : 0u;
+                vx1[k].w[e] = inside ? vx1[k].w[e] : 0u;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < MQD; ++k) {
+            const int q = tid + k * NT;
+            const int ii = udiv(q, QW), uu = q - ii * QW;
+            load_raw<bf16_t, 4>(ds + (uint32_t)(2 * ii * W + 4 * uu), vd0[k]);
+            load_raw<bf16_t, 4>(ds + (uint32_t)((2 * ii + 1) * W + 4 * uu), vd1[k]);
+        }
+    };
+    if (u0 < u1) issue_loads(u0);
+
+    for (int u = u0; u < u1; ++u) {
+        const int b = u / P::NTILE, r0 = (u - b * P::NTILE) * TH;
+        const size_t plane = (size_t)b * C + c;
+        // ------------------------------------------------ P0: stream in
+        {
+            constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1);
+#pragma unroll
+            for (int k = 0; k < MQX; ++k) {
+                const int q = tid + k * NT;
+                if (!(NQX % NT == 0 || q < NQX)) continue;
+                const int ii = udiv(q, QW), uu = q - ii * QW;
+                // the x rows the base taps read, as loaded
+                const int xr = 2 * ii - (G - PB);
+                if (xr >= 0 && xr < XRM)
+                    *reinterpret_cast<uint2*>(XS + xr * SXBM + 4 * uu) = make_uint2(vx0[k].w[0], vx0[k].w[1]);
+                if (xr + 1 >= 0 && xr + 1 < XRM)
+                    *reinterpret_cast<uint2*>(XS + (xr + 1) * SXBM + 4 * uu) = make_uint2(vx1[k].w[0], vx1[k].w[1]);
+                float f0[4], f1[4];
+                widen_raw<bf16_t, 4>(vx0[k], f0);
+                widen_raw<bf16_t, 4>(vx1[k], f1);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    float bb[4];
+                    haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[0], bb[1], bb[2], bb[3]);
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb) U[sb * BS1 + ii * S1 + PK + 2 * uu + m] = bb[sb];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < MQD; ++k) {
+                const int q = tid + k * NT;
+                const int ii = udiv(q, QW), uu = q - ii * QW;
+                // pair words: c..c+2 whole, c+3's low half, c-1's high half
+#pragma unroll
+                for (int rs = 0; rs < 2; ++rs) {
+                    const uint32_t w0 = rs ? vd1[k].w[0] : vd0[k].w[0], w1 = rs ? vd1[k].w[1] : vd0[k].w[1];
+                    const int wb = (2 * ii + rs) * SDP + DOFF + 4 * uu;
+                    *reinterpret_cast<uint2*>(DP + wb) = make_uint2(w0, __builtin_amdgcn_alignbit(w1, w0, 16));
+                    DP[wb + 2] = w1;
+                    DP16[2 * (wb + 3)] = (uint16_t)(w1 >> 16);
+                    DP16[2 * (wb - 1) + 1] = (uint16_t)(w0 & 0xffffu);
+                }
+                float f0[4], f1[4];
+                widen_raw<bf16_t, 4>(vd0[k], f0);
+                widen_raw<bf16_t, 4>(vd1[k], f1);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    float bb[4];
+                    haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[0], bb[1], bb[2], bb[3]);
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb) Vb[sb * VS1 + ii * SV1 + 2 * uu + m] = bb[sb];
+                }
+            }
+        }
+        __syncthreads();
+        if (u + 1 < u1) issue_loads(u + 1);
+        // ----------------------------------------- P2: levels 2..L0 analysis
+        P::for_levels([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            if constexpr (l >= 2) {
+                constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
+                constexpr int Sp = P::su(l - 1), SVp = P::sv(l - 1), SVl = P::sv(l);
+                const float* LLu = U + P::uoff(l - 1) + PK;
+                const float* LLv = Vb + P::voff(l - 1);
+                float* Ul = U + P::uoff(l);
+                float* Vl = Vb + P::voff(l);
+                for (int q = tid; q < rl * wl; q += NT) {
+                    const int i = q / wl, j = q - i * wl;
+                    const float* x2 = LLu + 2 * i * Sp + 2 * j;
+                    float uu[4];
+                    haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], uu[0], uu[1], uu[2], uu[3]);
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb) Ul[sb * BSl + i * Sl + PK + j] = uu[sb];
+                }
+                for (int q = tid; q < (TH >> l) * wl; q += NT) {
+                    const int i = q / wl, j = q - i * wl;
+                    const float* d2 = LLv + 2 * i * SVp + 2 * j;
+                    float vv[4];
+                    haar4(d2[0], d2[1], d2[SVp], d2[SVp + 1], vv[0], vv[1], vv[2], vv[3]);
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb) Vl[sb * VSl + i * SVl + j] = vv[sb];
+                }
+                __syncthreads();
+            }
+        });
+        // the coarse pass's inputs: the tile's level-L0 LL sums of x and dy
+        if (P::LT > L0) {
+            constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GLv = G >> L0;
+            const float* LLu = U + P::uoff(L0) + PK;
+            const float* LLv = Vb + P::voff(L0);
+            float* pxo = px + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            float* pdo = pdy + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            constexpr int SVL = P::sv(L0);
+            for (int q = tid; q < hl * wl; q += NT) {
+                const int i = q / wl, j = q - i * wl;
+                pxo[q] = LLu[(GLv + i) * Sl + j];
+                pdo[q] = LLv[i * SVL + j];
+            }
+        }
+        // ------------------- P3: base taps on the matrix cores, then the level taps
+        {
+            const int m = lane & 15, qq = lane >> 4;
+            const uint16_t* xa = XS + (2 * wave + (m < 8 ? m : 7)) * SXBM + 8 * qq;
+            const uint32_t* ya = DP + (2 * wave + (m >> 3)) * SDP + DOFF + 8 * qq - (m & 7) + PB;
+#pragma unroll
+            for (int ch = 0; ch < W / 32; ++ch) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xa + 32 * ch));
+                const uint32_t* yp = ya + 32 * ch;
+                const bf16x8 bm = __builtin_bit_cast(bf16x8, make_uint4(yp[0], yp[2], yp[4], yp[6]));
+                dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, dacc, 0, 0, 0);
+            }
+        }
+        P::for_levels([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
+            constexpr int Gl = G >> l, SVl = P::sv(l), OFF = P::boff(l);
+            constexpr int R = P::band_rows_mf(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
+            const float* Us = U + P::uoff(l) + band * BSl;
+            const float* Vs = Vb + P::voff(l) + band * VSl;
+            for (int item = blane; item < NIl; item += BLM) {
+                const int rs = item / LPl, j = item - rs * LPl;
+                if (!(LPl == wl || j < wl)) continue;
+                taps_col<K, R, Sl, SVl, ACCM, float, OFF>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j,
+                                                          acc);
+            }
+        });
+        // the next unit's P0 overwrites every region: wait for every reader
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int t = 0; t < ACCM; ++t) acc[t] = wave_sum(acc[t]);
+    __syncthreads();
+    float* red = lds;                // [NW][ACCM] level taps per wavefront
+    float* redD = lds + NW * ACCM;   // [NW][16][16] matrix-core sums per wavefront
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < ACCM; ++t) red[wave * ACCM + t] = acc[t];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) redD[wave * 256 + (4 * (lane >> 4) + jj) * 16 + (lane & 15)] = dacc[jj];
+    __syncthreads();
+    float* dst = part + ((size_t)chunk * C + c) * P::TAPS;
+    for (int t = tid; t < P::TAPS; t += NT) {
+        float v = 0.f;
+        if (t < KB * KB) {
+            const int i = t / KB, j = t - i * KB;
+            for (int w = 0; w < NW; ++w) {   // wavefronts in order, dy row h then h + 1
+                v += redD[w * 256 + i * 16 + j];
+                v += redD[w * 256 + (i + 1) * 16 + 8 + j];
+            }
+        } else {
+            const int r = t - KB * KB, ls = r / (K * K), tap = r - ls * (K * K);
+            const int l = ls / 4 + 1, sb = ls - (l - 1) * 4;
+            for (int h = 0; h < NW / 4; ++h) v += red[(sb + 4 * h) * ACCM + (l - 1) * K * K + tap];
+        }
+        dst[t] = v;
+    }
+}
+
 // ------------------------------------------------------------ registry
 
 // Compute units of the current device (queried once per device).
@@ -407,8 +680,12 @@ static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_
         cur += bw_align256(pl);
         pdy = (float*)cur;
     }
-    hipLaunchKernelGGL((tile_bwdw_kernel<FP, T>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
-                       (const T*)x, (const T*)dy, partA, px, pdy, B, C, upc);
+    if constexpr (FP::MF && sizeof(T) == 2)
+        hipLaunchKernelGGL((tile_bwdw_mf_kernel<FP>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
+                           (const bf16_t*)x, (const bf16_t*)dy, partA, px, pdy, B, C, upc);
+    else
+        hipLaunchKernelGGL((tile_bwdw_kernel<FP, T>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
+                           (const T*)x, (const T*)dy, partA, px, pdy, B, C, upc);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if constexpr (FP::LT > FP::L0) {
@@ -648,7 +925,7 @@ typedef BwPlan<32, 32, 3, 1, 5, 3, 4> CB_32_L3_k5;
 // of 3 with 8-row tiles (1.34 -> 1.06 ms at 16x256x256²). 1024 lanes (four
 // waves per SIMD under the one workgroup per CU that 114 KB of LDS allow, 8-
 // and 2-row strips) measured slower: 1.07 against 0.99 ms
-typedef TileBwPlan<256, 256, 2, 4, 7, 5, 16> TB_256_L2of4_k75;
+typedef TileBwPlan<256, 256, 2, 4, 7, 5, 16, 512, true> TB_256_L2of4_k75;
 typedef BwPlan<64, 64, 2, 1, 5> CB_64_L2_k5;
 typedef TileBwPlan<64, 64, 2, 4, 3, 3, 8> TB_64_L2of4_k33;
 typedef BwPlan<16, 16, 2, 1, 3, 2, 8> CB_16_L2_k3;
