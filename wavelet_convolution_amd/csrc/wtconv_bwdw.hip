@@ -92,9 +92,12 @@ struct TileBwPlan {
     static constexpr int SD = round_up(W, 4);
     static constexpr int DSIZE = TH * SD;
     static constexpr int rh(int l) { return RH0 >> l; }
-    static constexpr int su(int l) { return odd_stride((W >> l) + 2 * PK); }
+    // band row strides: odd (scalar analysis stores of consecutive rows in
+    // different banks), or even in the matrix-core form, whose analysis
+    // stores cell pairs as 64-bit words
+    static constexpr int su(int l) { return MF_ ? round_up((W >> l) + 2 * PK, 2) : odd_stride((W >> l) + 2 * PK); }
     static constexpr int bandsz(int l) { return rh(l) * su(l); }
-    static constexpr int sv(int l) { return odd_stride(W >> l); }
+    static constexpr int sv(int l) { return MF_ ? round_up(W >> l, 2) : odd_stride(W >> l); }
     static constexpr int vsz(int l) { return (TH >> l) * sv(l); }
     static constexpr int uoff(int l) {
         int o = 0;
@@ -139,7 +142,8 @@ struct TileBwPlan {
     static constexpr int DATAM = XSM + DPM + UTOT + VTOT, REDM = NW * (256 + ACCM);
     static constexpr int MF_FLOATS = DATAM > REDM ? DATAM : REDM;
     static constexpr int band_rows_mf(int l) { return pick_rows(TH >> l, W >> l, BLM, K); }
-    static_assert(!MF || (TH / 2 == NW && W % 32 == 0 && KB <= 7 && 7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
+    static_assert(!MF || (TH / 2 == NW && W % 32 == 0 && KB <= 7 && PK % 2 == 0 && DOFF % 4 == 0 && SDP % 4 == 0 &&
+                          7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
                           MF_FLOATS * 4 <= 160 * 1024),
                   "matrix-core weight gradient: one dy row pair per wavefront, 32-column chunks, taps up to 7x7");
     static constexpr int WAVES_PER_EU_MF = ((160 * 1024) / (MF_FLOATS * 4)) * NW / 4 < 1
@@ -398,7 +402,6 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
     __shared__ __attribute__((aligned(16))) float lds[P::MF_FLOATS];
     uint16_t* const XS = reinterpret_cast<uint16_t*>(lds);
     uint32_t* const DP = reinterpret_cast<uint32_t*>(lds + P::XSM);
-    uint16_t* const DP16 = reinterpret_cast<uint16_t*>(DP);
     float* const U = lds + P::XSM + P::DPM;
     float* const Vb = U + P::UTOT;
 
@@ -479,38 +482,42 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 float f0[4], f1[4];
                 widen_raw<bf16_t, 4>(vx0[k], f0);
                 widen_raw<bf16_t, 4>(vx1[k], f1);
+                float bb[2][4];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    float bb[4];
-                    haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[0], bb[1], bb[2], bb[3]);
+                for (int m = 0; m < 2; ++m)
+                    haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[m][0], bb[m][1], bb[m][2], bb[m][3]);
 #pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) U[sb * BS1 + ii * S1 + PK + 2 * uu + m] = bb[sb];
-                }
+                for (int sb = 0; sb < 4; ++sb)
+                    *reinterpret_cast<float2*>(U + sb * BS1 + ii * S1 + PK + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
             }
 #pragma unroll
             for (int k = 0; k < MQD; ++k) {
                 const int q = tid + k * NT;
                 const int ii = udiv(q, QW), uu = q - ii * QW;
-                // pair words: c..c+2 whole, c+3's low half, c-1's high half
+                // pair words c..c+3 as one 16-byte store; the last needs the
+                // next item's first value (the next lane: a row's items are
+                // one wavefront), zero past the plane; the word before
+                // column 0 holds (0, dy[0])
+                static_assert(QW == 64 && NQD % 64 == 0, "one wavefront per dy row pair");
 #pragma unroll
                 for (int rs = 0; rs < 2; ++rs) {
                     const uint32_t w0 = rs ? vd1[k].w[0] : vd0[k].w[0], w1 = rs ? vd1[k].w[1] : vd0[k].w[1];
+                    const uint32_t nx = (uint32_t)__shfl_down((int)w0, 1, 64);
+                    const uint32_t w3 = (w1 >> 16) | (uu + 1 < QW ? (nx << 16) : 0u);
                     const int wb = (2 * ii + rs) * SDP + DOFF + 4 * uu;
-                    *reinterpret_cast<uint2*>(DP + wb) = make_uint2(w0, __builtin_amdgcn_alignbit(w1, w0, 16));
-                    DP[wb + 2] = w1;
-                    DP16[2 * (wb + 3)] = (uint16_t)(w1 >> 16);
-                    DP16[2 * (wb - 1) + 1] = (uint16_t)(w0 & 0xffffu);
+                    *reinterpret_cast<uint4*>(DP + wb) = make_uint4(w0, __builtin_amdgcn_alignbit(w1, w0, 16), w1, w3);
+                    if (uu == 0) DP[wb - 1] = w0 << 16;
                 }
                 float f0[4], f1[4];
                 widen_raw<bf16_t, 4>(vd0[k], f0);
                 widen_raw<bf16_t, 4>(vd1[k], f1);
+                float bb[2][4];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    float bb[4];
-                    haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[0], bb[1], bb[2], bb[3]);
+                for (int m = 0; m < 2; ++m)
+                    haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[m][0], bb[m][1], bb[m][2], bb[m][3]);
 #pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) Vb[sb * VS1 + ii * SV1 + 2 * uu + m] = bb[sb];
-                }
+                for (int sb = 0; sb < 4; ++sb)
+                    *reinterpret_cast<float2*>(Vb + sb * VS1 + ii * SV1 + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
             }
         }
         __syncthreads();
