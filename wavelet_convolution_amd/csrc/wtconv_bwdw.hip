@@ -136,19 +136,23 @@ struct TileBwPlan {
     // words of overlapping bf16 pairs (word DOFF + c = dy[c], dy[c+1]; SDP
     // words a row; zero outside the plane), then the level bands U and V.
     static constexpr bool MF = MF_;
-    static constexpr int XRM = TH + 2 * PB, SXBM = W + 8, DOFF = 8, SDP = W + 48, BLM = NT / 4;
+    // NTM threads (four wavefronts per SIMD under the one workgroup per CU
+    // that the LDS allows); WPR wavefronts per dy row pair, each taking
+    // W / 32 / WPR column chunks
+    static constexpr int NTM = 1024, NWM = NTM / 64, WPR = NWM / (TH / 2);
+    static constexpr int XRM = TH + 2 * PB, SXBM = W + 8, DOFF = 8, SDP = W + 48, BLM = NTM / 4;
     static constexpr int ACCM = L0 * K * K;
     static constexpr int XSM = (XRM * SXBM / 2 + 3) / 4 * 4, DPM = TH * SDP;
-    static constexpr int DATAM = XSM + DPM + UTOT + VTOT, REDM = NW * (256 + ACCM);
+    static constexpr int DATAM = XSM + DPM + UTOT + VTOT, REDM = NWM * (256 + ACCM);
     static constexpr int MF_FLOATS = DATAM > REDM ? DATAM : REDM;
     static constexpr int band_rows_mf(int l) { return pick_rows(TH >> l, W >> l, BLM, K); }
-    static_assert(!MF || (TH / 2 == NW && W % 32 == 0 && KB <= 7 && PK % 2 == 0 && DOFF % 4 == 0 && SDP % 4 == 0 &&
+    static_assert(!MF || (NWM % (TH / 2) == 0 && (W / 32) % WPR == 0 && KB <= 7 && PK % 2 == 0 && DOFF % 4 == 0 && SDP % 4 == 0 &&
                           7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
                           MF_FLOATS * 4 <= 160 * 1024),
                   "matrix-core weight gradient: one dy row pair per wavefront, 32-column chunks, taps up to 7x7");
-    static constexpr int WAVES_PER_EU_MF = ((160 * 1024) / (MF_FLOATS * 4)) * NW / 4 < 1
+    static constexpr int WAVES_PER_EU_MF = ((160 * 1024) / (MF_FLOATS * 4)) * NWM / 4 < 1
                                                ? 1
-                                               : ((160 * 1024) / (MF_FLOATS * 4)) * NW / 4;
+                                               : ((160 * 1024) / (MF_FLOATS * 4)) * NWM / 4;
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -386,18 +390,18 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 // The level taps run on every wavefront: band wave%4 of each fine level, on
 // the lanes of waves band and band + 4.
 template <class P>
-__global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU_MF)))
+__global__ __launch_bounds__(P::NTM) __attribute__((amdgpu_waves_per_eu(P::WAVES_PER_EU_MF)))
 void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, float* __restrict__ part,
                          float* __restrict__ px, float* __restrict__ pdy, int B, int C, int upc) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH, NW = P::NW;
-    constexpr int PB = P::PB, PK = P::PK, G = P::G, RH0 = P::RH0, W1 = W / 2;
+    constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NTM, TH = P::TH, NW = P::NWM;
+    constexpr int PB = P::PB, PK = P::PK, G = P::G, RH0 = P::RH0, WPR = P::WPR;
     constexpr int XRM = P::XRM, SXBM = P::SXBM, DOFF = P::DOFF, SDP = P::SDP, BLM = P::BLM, ACCM = P::ACCM;
     constexpr int QW = W / 4;                       // 4-column items per row
     constexpr int NQX = (RH0 / 2) * QW, NQD = (TH / 2) * QW;
     constexpr int MQX = cdiv(NQX, NT), MQD = cdiv(NQD, NT);
-    static_assert(W % 4 == 0 && NQD % NT == 0, "whole dy items per thread");
+    static_assert(W % 4 == 0 && (NQD % NT == 0 || NQD < NT), "whole dy items per thread");
 
     __shared__ __attribute__((aligned(16))) float lds[P::MF_FLOATS];
     uint16_t* const XS = reinterpret_cast<uint16_t*>(lds);
@@ -455,6 +459,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 #pragma unroll
         for (int k = 0; k < MQD; ++k) {
             const int q = tid + k * NT;
+            if (!(NQD % NT == 0 || q < NQD)) continue;
             const int ii = udiv(q, QW), uu = q - ii * QW;
             load_raw<bf16_t, 4>(ds + (uint32_t)(2 * ii * W + 4 * uu), vd0[k]);
             load_raw<bf16_t, 4>(ds + (uint32_t)((2 * ii + 1) * W + 4 * uu), vd1[k]);
@@ -493,6 +498,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 #pragma unroll
             for (int k = 0; k < MQD; ++k) {
                 const int q = tid + k * NT;
+                if (!(NQD % NT == 0 || q < NQD)) continue;
                 const int ii = udiv(q, QW), uu = q - ii * QW;
                 // pair words c..c+3 as one 16-byte store; the last needs the
                 // next item's first value (the next lane: a row's items are
@@ -567,11 +573,11 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
         }
         // ------------------- P3: base taps on the matrix cores, then the level taps
         {
-            const int m = lane & 15, qq = lane >> 4;
-            const uint16_t* xa = XS + (2 * wave + (m < 8 ? m : 7)) * SXBM + 8 * qq;
-            const uint32_t* ya = DP + (2 * wave + (m >> 3)) * SDP + DOFF + 8 * qq - (m & 7) + PB;
+            const int m = lane & 15, qq = lane >> 4, rp = wave / WPR, c0 = (wave - rp * WPR) * (W / 32 / WPR);
+            const uint16_t* xa = XS + (2 * rp + (m < 8 ? m : 7)) * SXBM + 8 * qq + 32 * c0;
+            const uint32_t* ya = DP + (2 * rp + (m >> 3)) * SDP + DOFF + 8 * qq - (m & 7) + PB + 32 * c0;
 #pragma unroll
-            for (int ch = 0; ch < W / 32; ++ch) {
+            for (int ch = 0; ch < W / 32 / WPR; ++ch) {
                 const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xa + 32 * ch));
                 const uint32_t* yp = ya + 32 * ch;
                 const bf16x8 bm = __builtin_bit_cast(bf16x8, make_uint4(yp[0], yp[2], yp[4], yp[6]));
@@ -688,7 +694,7 @@ static hipError_t split_bw_launch(const void* x, const void* dy, const float* w_
         pdy = (float*)cur;
     }
     if constexpr (FP::MF && sizeof(T) == 2)
-        hipLaunchKernelGGL((tile_bwdw_mf_kernel<FP>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
+        hipLaunchKernelGGL((tile_bwdw_mf_kernel<FP>), dim3((unsigned)(nA * C)), dim3(FP::NTM), 0, stream,
                            (const bf16_t*)x, (const bf16_t*)dy, partA, px, pdy, B, C, upc);
     else
         hipLaunchKernelGGL((tile_bwdw_kernel<FP, T>), dim3((unsigned)(nA * C)), dim3(FP::NT), 0, stream,
