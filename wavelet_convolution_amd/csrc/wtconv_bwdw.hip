@@ -136,17 +136,19 @@ struct TileBwPlan {
     // words of overlapping bf16 pairs (word DOFF + c = dy[c], dy[c+1]; SDP
     // words a row; zero outside the plane), then the level bands U and V.
     static constexpr bool MF = MF_;
-    // NTM threads (four wavefronts per SIMD under the one workgroup per CU
-    // that the LDS allows); WPR wavefronts per dy row pair, each taking
-    // W / 32 / WPR column chunks
-    static constexpr int NTM = 1024, NWM = NTM / 64, WPR = NWM / (TH / 2);
+    // NTM threads; WPR wavefronts per dy row pair, each taking W / 32 / WPR
+    // column chunks. The level-2 bands take the place of the x rows and dy
+    // pair words once the matrix products are done (two workgroups per CU).
+    static constexpr int NTM = 512, NWM = NTM / 64, WPR = NWM / (TH / 2);
     static constexpr int XRM = TH + 2 * PB, SXBM = W + 8, DOFF = 8, SDP = W + 48, BLM = NTM / 4;
     static constexpr int ACCM = L0 * K * K;
     static constexpr int XSM = (XRM * SXBM / 2 + 3) / 4 * 4, DPM = TH * SDP;
-    static constexpr int DATAM = XSM + DPM + UTOT + VTOT, REDM = NWM * (256 + ACCM);
+    static constexpr int U2M = 4 * bandsz(2), V2M = 4 * vsz(2), U1M = 4 * bandsz(1), V1M = 4 * vsz(1);
+    static constexpr int AM = XSM + DPM > U2M + V2M ? XSM + DPM : U2M + V2M;   // x rows + dy words, then level 2
+    static constexpr int DATAM = AM + U1M + V1M, REDM = NWM * (256 + ACCM);
     static constexpr int MF_FLOATS = DATAM > REDM ? DATAM : REDM;
     static constexpr int band_rows_mf(int l) { return pick_rows(TH >> l, W >> l, BLM, K); }
-    static_assert(!MF || (NWM % (TH / 2) == 0 && (W / 32) % WPR == 0 && KB <= 7 && PK % 2 == 0 && DOFF % 4 == 0 && SDP % 4 == 0 &&
+    static_assert(!MF || (L0 == 2 && NWM % (TH / 2) == 0 && (W / 32) % WPR == 0 && KB <= 7 && PK % 2 == 0 && DOFF % 4 == 0 && SDP % 4 == 0 &&
                           7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
                           MF_FLOATS * 4 <= 160 * 1024),
                   "matrix-core weight gradient: one dy row pair per wavefront, 32-column chunks, taps up to 7x7");
@@ -406,8 +408,19 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
     __shared__ __attribute__((aligned(16))) float lds[P::MF_FLOATS];
     uint16_t* const XS = reinterpret_cast<uint16_t*>(lds);
     uint32_t* const DP = reinterpret_cast<uint32_t*>(lds + P::XSM);
-    float* const U = lds + P::XSM + P::DPM;
-    float* const Vb = U + P::UTOT;
+    float* const U2 = lds;              // level 2 over the x rows and dy words
+    float* const V2 = lds + P::U2M;
+    float* const U1 = lds + P::AM;
+    float* const V1 = U1 + P::U1M;
+    // band l of x (bordered) and of dy
+    auto ub = [&](auto lc) -> float* {
+        if constexpr (decltype(lc)::value == 1) return U1;
+        else return U2;
+    };
+    auto vb = [&](auto lc) -> float* {
+        if constexpr (decltype(lc)::value == 1) return V1;
+        else return V2;
+    };
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int band = wave & 3, blane = ((wave >> 2) << 6) + lane;
@@ -415,19 +428,15 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
     const int nunits = B * P::NTILE;
     const int u0 = chunk * upc, u1 = min(nunits, u0 + upc);
 
-    // once: every dy pair word zero (the interior halves are rewritten per
-    // unit, the words outside the plane stay zero); the band border columns
-    for (int i = tid; i < TH * SDP; i += NT) DP[i] = 0u;
-    P::for_levels([&](auto lc) {
-        constexpr int l = decltype(lc)::value;
-        constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l);
-        float* Ul = U + P::uoff(l);
+    // once: the level-1 band border columns (nothing else writes them)
+    {
+        constexpr int rl = P::rh(1), wl = W >> 1, Sl = P::su(1), BSl = P::bandsz(1);
         for (int i = tid; i < 4 * rl * (Sl - wl); i += NT) {
             const int b = i / (rl * (Sl - wl)), j = i - b * (rl * (Sl - wl));
             const int r = j / (Sl - wl), q = j - r * (Sl - wl);
-            Ul[b * BSl + r * Sl + (q < PK ? q : q + wl)] = 0.f;
+            U1[b * BSl + r * Sl + (q < PK ? q : q + wl)] = 0.f;
         }
-    });
+    }
 
     float acc[ACCM];
 #pragma unroll
@@ -473,6 +482,12 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
         // ------------------------------------------------ P0: stream in
         {
             constexpr int S1 = P::su(1), BS1 = P::bandsz(1), VS1 = P::vsz(1), SV1 = P::sv(1);
+            // dy pair words outside the plane (level 2 used this space)
+            constexpr int ZW = SDP - W - 1;   // words 0..DOFF-2 and DOFF+W..SDP-1 of each row
+            for (int i = tid; i < TH * ZW; i += NT) {
+                const int r = udiv(i, ZW), q = i - r * ZW;
+                DP[r * SDP + (q < DOFF - 1 ? q : q + W + 1)] = 0u;
+            }
 #pragma unroll
             for (int k = 0; k < MQX; ++k) {
                 const int q = tid + k * NT;
@@ -493,7 +508,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                     haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[m][0], bb[m][1], bb[m][2], bb[m][3]);
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
-                    *reinterpret_cast<float2*>(U + sb * BS1 + ii * S1 + PK + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
+                    *reinterpret_cast<float2*>(U1 + sb * BS1 + ii * S1 + PK + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
             }
 #pragma unroll
             for (int k = 0; k < MQD; ++k) {
@@ -504,7 +519,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 // next item's first value (the next lane: a row's items are
                 // one wavefront), zero past the plane; the word before
                 // column 0 holds (0, dy[0])
-                static_assert(QW == 64 && NQD % 64 == 0, "one wavefront per dy row pair");
+                static_assert(QW == 64, "one wavefront per dy row pair");
 #pragma unroll
                 for (int rs = 0; rs < 2; ++rs) {
                     const uint32_t w0 = rs ? vd1[k].w[0] : vd0[k].w[0], w1 = rs ? vd1[k].w[1] : vd0[k].w[1];
@@ -523,55 +538,28 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                     haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], bb[m][0], bb[m][1], bb[m][2], bb[m][3]);
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
-                    *reinterpret_cast<float2*>(Vb + sb * VS1 + ii * SV1 + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
+                    *reinterpret_cast<float2*>(V1 + sb * VS1 + ii * SV1 + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
             }
         }
         __syncthreads();
         if (u + 1 < u1) issue_loads(u + 1);
-        // ----------------------------------------- P2: levels 2..L0 analysis
-        P::for_levels([&](auto lc) {
+
+        // level taps of level l: band `band` on the lanes of its wavefronts
+        auto level_taps = [&](auto lc) {
             constexpr int l = decltype(lc)::value;
-            if constexpr (l >= 2) {
-                constexpr int rl = P::rh(l), wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-                constexpr int Sp = P::su(l - 1), SVp = P::sv(l - 1), SVl = P::sv(l);
-                const float* LLu = U + P::uoff(l - 1) + PK;
-                const float* LLv = Vb + P::voff(l - 1);
-                float* Ul = U + P::uoff(l);
-                float* Vl = Vb + P::voff(l);
-                for (int q = tid; q < rl * wl; q += NT) {
-                    const int i = q / wl, j = q - i * wl;
-                    const float* x2 = LLu + 2 * i * Sp + 2 * j;
-                    float uu[4];
-                    haar4(x2[0], x2[1], x2[Sp], x2[Sp + 1], uu[0], uu[1], uu[2], uu[3]);
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) Ul[sb * BSl + i * Sl + PK + j] = uu[sb];
-                }
-                for (int q = tid; q < (TH >> l) * wl; q += NT) {
-                    const int i = q / wl, j = q - i * wl;
-                    const float* d2 = LLv + 2 * i * SVp + 2 * j;
-                    float vv[4];
-                    haar4(d2[0], d2[1], d2[SVp], d2[SVp + 1], vv[0], vv[1], vv[2], vv[3]);
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb) Vl[sb * VSl + i * SVl + j] = vv[sb];
-                }
-                __syncthreads();
+            constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
+            constexpr int Gl = G >> l, SVl = P::sv(l), OFF = P::boff(l);
+            constexpr int R = P::band_rows_mf(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
+            const float* Us = ub(lc) + band * BSl;
+            const float* Vs = vb(lc) + band * VSl;
+            for (int item = blane; item < NIl; item += BLM) {
+                const int rs = item / LPl, j = item - rs * LPl;
+                if (!(LPl == wl || j < wl)) continue;
+                taps_col<K, R, Sl, SVl, ACCM, float, OFF>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j,
+                                                          acc);
             }
-        });
-        // the coarse pass's inputs: the tile's level-L0 LL sums of x and dy
-        if (P::LT > L0) {
-            constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GLv = G >> L0;
-            const float* LLu = U + P::uoff(L0) + PK;
-            const float* LLv = Vb + P::voff(L0);
-            float* pxo = px + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
-            float* pdo = pdy + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
-            constexpr int SVL = P::sv(L0);
-            for (int q = tid; q < hl * wl; q += NT) {
-                const int i = q / wl, j = q - i * wl;
-                pxo[q] = LLu[(GLv + i) * Sl + j];
-                pdo[q] = LLv[i * SVL + j];
-            }
-        }
-        // ------------------- P3: base taps on the matrix cores, then the level taps
+        };
+        // ------------------- P1: base taps on the matrix cores, level-1 taps
         {
             const int m = lane & 15, qq = lane >> 4, rp = wave / WPR, c0 = (wave - rp * WPR) * (W / 32 / WPR);
             const uint16_t* xa = XS + (2 * rp + (m < 8 ? m : 7)) * SXBM + 8 * qq + 32 * c0;
@@ -584,20 +572,53 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, dacc, 0, 0, 0);
             }
         }
-        P::for_levels([&](auto lc) {
-            constexpr int l = decltype(lc)::value;
-            constexpr int hl = TH >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), VSl = P::vsz(l);
-            constexpr int Gl = G >> l, SVl = P::sv(l), OFF = P::boff(l);
-            constexpr int R = P::band_rows_mf(l), LPl = strip_lanes(wl), NIl = (hl / R) * LPl;
-            const float* Us = U + P::uoff(l) + band * BSl;
-            const float* Vs = Vb + P::voff(l) + band * VSl;
-            for (int item = blane; item < NIl; item += BLM) {
-                const int rs = item / LPl, j = item - rs * LPl;
-                if (!(LPl == wl || j < wl)) continue;
-                taps_col<K, R, Sl, SVl, ACCM, float, OFF>(Us + (Gl + R * rs - PK) * Sl + j, Vs + R * rs * SVl + j,
-                                                          acc);
+        level_taps(std::integral_constant<int, 1>{});
+        __syncthreads();   // the x rows and dy words are dead: level 2 goes over them
+        // ----------------------------------------- P2: level 2 analysis
+        {
+            constexpr int rl = P::rh(2), wl = W >> 2, Sl = P::su(2), BSl = P::bandsz(2), VSl = P::vsz(2);
+            constexpr int Sp = P::su(1), SVp = P::sv(1), SVl = P::sv(2), XB2 = Sl - wl;
+            const float* LLu = U1 + PK;
+            // border columns, then the interior cells
+            for (int i = tid; i < 4 * rl * XB2; i += NT) {
+                const int rb = udiv(i, XB2), q = i - rb * XB2;
+                U2[rb * Sl + (q < PK ? q : q + wl)] = 0.f;
             }
-        });
+            for (int q = tid; q < rl * wl; q += NT) {
+                const int i = q / wl, j = q - i * wl;
+                const float2 t0 = *reinterpret_cast<const float2*>(LLu + 2 * i * Sp + 2 * j);
+                const float2 t1 = *reinterpret_cast<const float2*>(LLu + (2 * i + 1) * Sp + 2 * j);
+                float uu[4];
+                haar4(t0.x, t0.y, t1.x, t1.y, uu[0], uu[1], uu[2], uu[3]);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) U2[sb * BSl + i * Sl + PK + j] = uu[sb];
+            }
+            for (int q = tid; q < (TH >> 2) * wl; q += NT) {
+                const int i = q / wl, j = q - i * wl;
+                const float2 t0 = *reinterpret_cast<const float2*>(V1 + 2 * i * SVp + 2 * j);
+                const float2 t1 = *reinterpret_cast<const float2*>(V1 + (2 * i + 1) * SVp + 2 * j);
+                float vv[4];
+                haar4(t0.x, t0.y, t1.x, t1.y, vv[0], vv[1], vv[2], vv[3]);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) V2[sb * VSl + i * SVl + j] = vv[sb];
+            }
+        }
+        __syncthreads();
+        // the coarse pass's inputs: the tile's level-2 LL sums of x and dy
+        if (P::LT > L0) {
+            constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GLv = G >> L0;
+            const float* LLu = U2 + PK;
+            float* pxo = px + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            float* pdo = pdy + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
+            constexpr int SVL = P::sv(L0);
+            for (int q = tid; q < hl * wl; q += NT) {
+                const int i = q / wl, j = q - i * wl;
+                pxo[q] = LLu[(GLv + i) * Sl + j];
+                pdo[q] = V2[i * SVL + j];
+            }
+        }
+        // ------------------------------------------------ P3: level-2 taps
+        level_taps(std::integral_constant<int, 2>{});
         // the next unit's P0 overwrites every region: wait for every reader
         __syncthreads();
     }
