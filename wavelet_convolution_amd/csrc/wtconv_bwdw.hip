@@ -152,9 +152,10 @@ struct TileBwPlan {
                           7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
                           MF_FLOATS * 4 <= 160 * 1024),
                   "matrix-core weight gradient: one dy row pair per wavefront, 32-column chunks, taps up to 7x7");
-    static constexpr int WAVES_PER_EU_MF = ((160 * 1024) / (MF_FLOATS * 4)) * NWM / 4 < 1
-                                               ? 1
-                                               : ((160 * 1024) / (MF_FLOATS * 4)) * NWM / 4;
+    // occupancy the LDS allows, at most four waves per SIMD: the level-tap
+    // accumulators and strips need up to 128 registers
+    static constexpr int WPE_LDS = ((160 * 1024) / (MF_FLOATS * 4)) * NWM / 4;
+    static constexpr int WAVES_PER_EU_MF = WPE_LDS < 1 ? 1 : (WPE_LDS > 4 ? 4 : WPE_LDS);
 
     template <class F>
     __device__ static __forceinline__ void for_levels(F&& f) {
@@ -519,7 +520,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 // next item's first value (the next lane: a row's items are
                 // one wavefront), zero past the plane; the word before
                 // column 0 holds (0, dy[0])
-                static_assert(QW == 64, "one wavefront per dy row pair");
+                static_assert(64 % QW == 0, "a dy row's items on consecutive lanes of one wavefront");
 #pragma unroll
                 for (int rs = 0; rs < 2; ++rs) {
                     const uint32_t w0 = rs ? vd1[k].w[0] : vd0[k].w[0], w1 = rs ? vd1[k].w[1] : vd0[k].w[1];
@@ -947,6 +948,8 @@ typedef BwPlan<64, 64, 4, 7, 5> BP_64_L4_k75;
 // split plans: fine tiles + coarse planes of LL_{L0} sums (no base taps)
 // 32-row tiles where the halo is 4 rows (one fine level): 10 % faster than
 // 16 at 128² L1; with two fine levels (8-row halo) 16 rows are 4-8 % faster
+// (the matrix-core weight gradient measured slower at 128x128: 0.204 against
+// about 0.19 ms per call at L = 2, 5x5 base taps being a smaller share)
 typedef TileBwPlan<128, 128, 1, 1, 5, 5, 32> TB_128_L1_k55;
 typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16> TB_128_L2_k55;
 typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16> TB_128_L2of3_k55;
