@@ -949,7 +949,7 @@ typedef BwPlan<64, 64, 4, 7, 5> BP_64_L4_k75;
 // 32-row tiles where the halo is 4 rows (one fine level): 10 % faster than
 // 16 at 128² L1; with two fine levels (8-row halo) 16 rows are 4-8 % faster
 // (the matrix-core weight gradient measured slower at 128x128: 0.204 against
-// about 0.19 ms per call at L = 2, 5x5 base taps being a smaller share)
+// about 0.18 ms per call at L = 2, 5x5 base taps being a smaller share)
 typedef TileBwPlan<128, 128, 1, 1, 5, 5, 32> TB_128_L1_k55;
 typedef TileBwPlan<128, 128, 2, 2, 5, 5, 16> TB_128_L2_k55;
 typedef TileBwPlan<128, 128, 2, 3, 5, 5, 16> TB_128_L2of3_k55;
