@@ -40,7 +40,7 @@ constexpr bool col_fits(int h, int L, int kb, int k) {
     const ColShape cs = col_shape(h);
     if (h % cs.rb != 0 || !(cs.rb % (1 << L) == 0 || (cs.rb & (cs.rb - 1)) == 0)) return false;
     const int pb = kb / 2, pk = k / 2, vl = lds_vec(h), va = vl >= 4 ? 4 : 2, cpi = va / 2;
-    const int xo = round_up(pb, 4), sx = round_up(xo + h + pb, 4);
+    const int xo = round_up(pb, va), sx = round_up(xo + h + pb, va);
     return (h / 2) % cpi == 0 && pk % cpi == 0 && (xo - 2 * pk) % va == 0 && xo <= 2 * pk && pb <= 2 * pk &&
            xo + h + 2 * pk >= sx;
 }

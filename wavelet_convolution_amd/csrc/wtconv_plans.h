@@ -223,16 +223,18 @@ struct ColPlan {
     static_assert(H % RB == 0, "base strips must divide the plane");
     static_assert(RB % (1 << L) == 0 || (RB & (RB - 1)) == 0, "base strips: a multiple of 2^L rows or a power of two");
     static_assert(NT % 64 == 0 && NT <= 1024, "whole wavefronts");
-    // x rows: interior from column XO (a multiple of 4, at least KB/2), row
-    // stride a multiple of 4: streamed rows take aligned 128-bit stores
-    static constexpr int VL = lds_vec(W);
-    static constexpr int XO = round_up(PB, 4);
-    static constexpr int SX = round_up(XO + W + PB, 4);
-    static constexpr int XSIZE = (H + 2 * PB) * SX;
     // level-1 analysis items: 2 x rows by VA columns (VA / 2 Haar blocks),
     // over the bordered level-1 grid; the items on the border write the
     // zeros of the band border and of the x border
+    static constexpr int VL = lds_vec(W);
     static constexpr int VA = VL >= 4 ? 4 : 2;
+    // x rows: interior from column XO (a multiple of VA, at least KB/2), row
+    // stride a multiple of VA: streamed rows take aligned VA-wide stores
+    // (128-bit, or 64-bit on planes whose rows take pairs: there the
+    // narrower border saves LDS, 14x14: a sixth workgroup per CU)
+    static constexpr int XO = round_up(PB, VA);
+    static constexpr int SX = round_up(XO + W + PB, VA);
+    static constexpr int XSIZE = (H + 2 * PB) * SX;
     static constexpr int CPI = VA / 2;
     static constexpr int rl(int l) { return RL < (H >> l) ? RL : (H >> l); }
     // band rows: level-1 cell pairs are stored as aligned 64-bit words
