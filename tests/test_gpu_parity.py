@@ -47,8 +47,12 @@ SMALL = [
     # then full-width fine tiles with a halo)
     (2, 3, 64, 64, 4, 3, 3),
     (2, 3, 64, 64, 2, 5, 5),
-    # the large-plane column tiles (7x7 base, coarse pass on the level-2 sums)
+    # the large-plane column tiles (7x7 base, coarse pass on the level-2 sums;
+    # bf16: the matrix-core fine pass and weight gradient), and a batch whose
+    # tiles split into several weight-gradient chunks per channel, the last
+    # one partial
     (1, 2, 256, 256, 4, 7, 5),
+    (3, 5, 256, 256, 4, 7, 5),
     # batches that leave the last multi-plane step of a weight-gradient chunk
     # partly empty (the whole-plane plans take several planes per step)
     (11, 2, 14, 14, 1, 5, 5),
@@ -361,7 +365,8 @@ def test_level_zero_fused_kernels(shape):
                                    (11, 3, 14, 14, 1, 5, 5), (3, 2, 28, 28, 2, 5, 5), (2, 3, 128, 128, 3, 5, 5),
                                    (2, 2, 56, 56, 2, 7, 3), (3, 2, 7, 7, 2, 5, 7),
                                    # split planes: the data pass's coarse step reads the weight pass's dy sums
-                                   (2, 3, 64, 64, 4, 3, 3), (3, 2, 64, 64, 2, 5, 5), (1, 2, 256, 256, 4, 7, 5)],
+                                   (2, 3, 64, 64, 4, 3, 3), (3, 2, 64, 64, 2, 5, 5), (1, 2, 256, 256, 4, 7, 5),
+                                   (3, 5, 256, 256, 4, 7, 5)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_whole_backward_equals_the_two_calls(shape):
     """wtconv_bwd (a single pass over x and dy at L = 0 on planned planes;
