@@ -344,9 +344,13 @@ struct ColTilePlan {
     template <typename T>
     static constexpr int asize() { return mf<T>() ? (XSIZE_MF > UDEEP ? XSIZE_MF : UDEEP) : ASIZE; }
     // floats of LDS per workgroup: regions A and B, the taps, the banded taps
+    // words of a channel's tap image: what the kernel keeps in LDS from its
+    // base taps on (base taps, level taps, banded rows in the matrix-core form)
+    template <typename T>
+    static constexpr int tapw() { return WFLOATS + (mf<T>() ? ZFLOATS : 0); }
     template <typename T>
     static constexpr int lds_floats() {
-        return (asize<T>() + BSIZE + 3) / 4 * 4 + WFLOATS + (mf<T>() ? ZFLOATS : 0);
+        return (asize<T>() + BSIZE + 3) / 4 * 4 + tapw<T>();
     }
     static_assert(!MF || (TH % 16 == 0 && W % 16 == 0 && PB <= XOM && PB + XOM <= 16 && SXB % 8 == 0 &&
                           ZOFF + KB <= ZL && NW % 2 == 0 && ((TH / 16) * (W / 16)) % (NW / 2) == 0),
@@ -390,10 +394,64 @@ struct ColTilePlan {
     }
 };
 
+// A channel's tap image for coltile_kernel, the words that kernel keeps in
+// LDS from its base taps on: base taps (turned 180 degrees for the backward
+// data pass), level taps with the band scale and 4^-l folded in, and in the
+// matrix-core form the banded tap rows. Every tile of every plane of a
+// channel reads the same image, so it is built once per call, a workgroup
+// per channel, and the fine kernel copies it in with one 16-byte load per
+// lane instead of rebuilding it per tile.
+template <class P, typename T, bool FLIP>
+__global__ __launch_bounds__(256) void coltile_taps_kernel(const float* __restrict__ w_base,
+                                                           const float* __restrict__ w_lvl,
+                                                           const float* __restrict__ scale, float* __restrict__ taps,
+                                                           int C) {
+    constexpr int KB = P::KB, K = P::K, L0 = P::L0, KB2P = P::KB2P, K2P = P::K2P, NT = 256;
+    const int c = blockIdx.x, tid = threadIdx.x;
+    float* const WB = taps + (size_t)c * P::template tapw<T>();
+    float* const WL = WB + KB2P;
+    for (int t = tid; t < KB2P; t += NT)
+        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
+    for (int t = tid; t < 4 * L0 * K2P; t += NT) {
+        const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
+        const size_t pi = ((size_t)l * C + c) * 4 + s;
+        const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
+        WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
+    }
+    if constexpr (P::template mf<T>()) {
+        // Banded tap rows: entry e of row (part p, tap row i) is part p of
+        // tap (i, e - ZOFF), zero outside the row, stored as words of entry
+        // pairs (e, e + 1). The three parts are the bf16 rounding of the tap,
+        // of what that leaves, and of what remains then: their sum is the
+        // fp32 tap exactly, and each product with a bf16 x is exact in fp32.
+        constexpr int ZL = P::ZL;
+        uint32_t* const zw = reinterpret_cast<uint32_t*>(WL + 4 * L0 * K2P);
+        for (int t = tid; t < KB * ZL; t += NT) {
+            const int i = t / ZL, w = t - i * ZL;
+            bf16_t part[2][3];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j = w + h - P::ZOFF;
+                float v = 0.f;
+                if (j >= 0 && j < KB) {
+                    const int tap = i * KB + j;
+                    v = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - tap : tap)];
+                }
+                part[h][0] = narrow_bf16(v);
+                v -= widen(part[h][0]);
+                part[h][1] = narrow_bf16(v);
+                part[h][2] = narrow_bf16(v - widen(part[h][1]));
+            }
+#pragma unroll
+            for (int pt = 0; pt < 3; ++pt) zw[(pt * KB + i) * ZL + w] = (uint32_t)part[0][pt] | ((uint32_t)part[1][pt] << 16);
+        }
+    }
+}
+
 template <class P, typename T, bool FLIP>
 __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::template waves_per_eu<T>())))
-void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, const float* __restrict__ w_lvl,
-                    const float* __restrict__ scale, const float* __restrict__ coarse, T* __restrict__ out, int C) {
+void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, const float* __restrict__ coarse,
+                    T* __restrict__ out, int C) {
     constexpr int H = P::H, W = P::W, L0 = P::L0, KB = P::KB, K = P::K, NT = P::NT, TH = P::TH, RB = P::RB;
     constexpr int PB = P::PB, PK = P::PK, G = P::G, SX = P::SX, XO = P::XO, W1 = W / 2;
     constexpr int S1 = P::su(1), BS1 = P::bandsz(1);
@@ -426,44 +484,14 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     };
 
     // ---------------------------------------------------------------- P0
-    if constexpr (MF) {
-        // Banded tap rows: entry e of row (part p, tap row i) is part p of
-        // tap (i, e - ZOFF), zero outside the row, stored as words of entry
-        // pairs (e, e + 1). The three parts are the bf16 rounding of the tap,
-        // of what that leaves, and of what remains then: their sum is the
-        // fp32 tap exactly, and each product with a bf16 x is exact in fp32.
-        // One thread per (tap row, word).
-        constexpr int ZL = P::ZL;
-        for (int t = tid; t < KB * ZL; t += NT) {
-            const int i = udiv(t, ZL), w = t - i * ZL;
-            bf16_t part[2][3];
+    // The channel's tap image (coltile_taps_kernel), loaded first and stored
+    // to LDS once the x loads are in flight.
+    constexpr int TW4 = P::template tapw<T>() / 4, MT = cdiv(TW4, NT);
+    static_assert(P::template tapw<T>() % 4 == 0, "tap image of whole 16-byte words");
+    const uint4* __restrict__ timg = reinterpret_cast<const uint4*>(taps) + (size_t)c * TW4;
+    uint4 tv[MT];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int j = w + h - P::ZOFF;
-                float v = 0.f;
-                if (j >= 0 && j < KB) {
-                    const int tap = i * KB + j;
-                    v = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - tap : tap)];
-                }
-                part[h][0] = narrow_bf16(v);
-                v -= widen(part[h][0]);
-                part[h][1] = narrow_bf16(v);
-                part[h][2] = narrow_bf16(v - widen(part[h][1]));
-            }
-            uint32_t* const zw = reinterpret_cast<uint32_t*>(ZC);
-#pragma unroll
-            for (int pt = 0; pt < 3; ++pt) zw[(pt * KB + i) * ZL + w] = (uint32_t)part[0][pt] | ((uint32_t)part[1][pt] << 16);
-        }
-    } else {
-        for (int t = tid; t < KB2P; t += NT)
-            WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
-    }
-    for (int t = tid; t < 4 * L0 * K2P; t += NT) {
-        const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
-        const size_t pi = ((size_t)l * C + c) * 4 + s;
-        const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
-        WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
-    }
+    for (int k = 0; k < MT; ++k) tv[k] = timg[min(tid + k * NT, TW4 - 1)];
     {
         // Border columns, written once: the x rows' columns outside the
         // plane and the level-1 bands' zero border columns (nothing else
@@ -507,6 +535,9 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
                 v1[k].w[e] = inside ? v1[k].w[e] : 0u;
             }
         }
+#pragma unroll
+        for (int k = 0; k < MT; ++k)
+            if (TW4 % NT == 0 || tid + k * NT < TW4) reinterpret_cast<uint4*>(WB)[tid + k * NT] = tv[k];
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
@@ -755,11 +786,32 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ w_base, 
     }
 }
 
+// Workspace of a column-tile plan: the coarse image (fp32 per plane at level
+// L0, where levels above L0 exist), then the channels' tap images.
+static size_t align_up256(size_t n) { return (n + 255) / 256 * 256; }
+template <class FP>
+static size_t coarse_bytes(int B, int C) {
+    if (FP::LT == FP::L0) return 0;
+    return (size_t)B * C * (FP::H >> FP::L0) * (FP::W >> FP::L0) * sizeof(float);
+}
+template <class FP>
+static size_t colsplit_ws(int B, int C) {
+    constexpr int TW = FP::template tapw<bf16_t>() > FP::template tapw<float>() ? FP::template tapw<bf16_t>()
+                                                                                 : FP::template tapw<float>();
+    return align_up256(coarse_bytes<FP>(B, C)) + (size_t)C * TW * sizeof(float);
+}
+template <class FP>
+static float* colsplit_taps(float* ws, int B, int C) {
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up256(coarse_bytes<FP>(B, C)));
+}
+
 template <class FP, class CP, typename T, bool FLIP>
 static hipError_t launch_colsplit(const void* in, const float* wb, const float* wl, const float* sc, void* out,
                                   float* ws, int B, int C, hipStream_t stream) {
     constexpr int L0 = FP::L0, LT = FP::LT;
     const unsigned planes = (unsigned)B * (unsigned)C;
+    float* const taps = colsplit_taps<FP>(ws, B, C);
+    hipLaunchKernelGGL((coltile_taps_kernel<FP, T, FLIP>), dim3(C), dim3(256), 0, stream, wb, wl, sc, taps, C);
     float* coarse = nullptr;
     if constexpr (LT > L0) {
         coarse = ws;
@@ -769,7 +821,7 @@ static hipError_t launch_colsplit(const void* in, const float* wb, const float* 
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL((coltile_kernel<FP, T, FLIP>), dim3(planes * FP::NTILE), dim3(FP::NT), 0, stream,
-                       (const T*)in, wb, wl, sc, (const float*)coarse, (T*)out, C);
+                       (const T*)in, (const float*)taps, (const float*)coarse, (T*)out, C);
     return hipGetLastError();
 }
 
@@ -782,12 +834,17 @@ static hipError_t launch_split_sums(const void* in, const float* sums, const flo
     static_assert(FP::LT > L0, "a coarse pass to feed");
     const unsigned planes = (unsigned)B * (unsigned)C;
     const size_t lvl = (size_t)C * 4 * FP::K * FP::K;
+    float* taps = nullptr;
+    if constexpr (COLS) {
+        taps = colsplit_taps<FP>(ws, B, C);
+        hipLaunchKernelGGL((coltile_taps_kernel<FP, T, true>), dim3(C), dim3(256), 0, stream, wb, wl, sc, taps, C);
+    }
     hipError_t err = launch_coarse<CP, float, true, L0, true>(sums, wl + L0 * lvl, sc + (size_t)L0 * C * 4, ws, B, C,
                                                              stream);
     if (err != hipSuccess) return err;
     if constexpr (COLS)
         hipLaunchKernelGGL((coltile_kernel<FP, T, true>), dim3(planes * FP::NTILE), dim3(FP::NT), 0, stream,
-                           (const T*)in, wb, wl, sc, (const float*)ws, (T*)out, C);
+                           (const T*)in, (const float*)taps, (const float*)ws, (T*)out, C);
     else
         hipLaunchKernelGGL((tile_kernel<FP, T, true>), dim3(planes * FP::NTILE), dim3(FP::NT), 0, stream,
                            (const T*)in, wb, wl, sc, (const float*)ws, (T*)out, C);
@@ -842,7 +899,7 @@ typedef TilePlan<64, 64, 1, 2, 5, 5, 16, 128, 1, 2> FP_64_L1of2_k55;
     {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K, FPL::L0,                                       \
      {{launch_colsplit<FPL, CPL, float, false>, launch_colsplit<FPL, CPL, float, true>},      \
       {launch_colsplit<FPL, CPL, bf16_t, false>, launch_colsplit<FPL, CPL, bf16_t, true>}},   \
-     split_ws<FPL>,                                                                           \
+     colsplit_ws<FPL>,                                                                         \
      {launch_split_sums<FPL, CPL, float, true>, launch_split_sums<FPL, CPL, bf16_t, true>}}
 
 static const SplitEntry kSplitEntries[] = {
