@@ -361,14 +361,41 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     };
 
     // ---------------------------------------------------------------- P0
-    for (int t = tid; t < KB2P; t += NT)
-        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)] : 0.f;
-    for (int t = tid; t < 4 * L * K2P; t += NT) {
-        const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2, s = ls & 3;
-        const size_t pi = ((size_t)l * C + c) * 4 + s;
-        const float f = scale[pi] * (1.0f / (float)(1 << (2 * (l + 1))));
-        WL[t] = tap < K * K ? w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)] * f : 0.f;
+    // The taps' loads go out first and the x loads right after them; the
+    // taps (level taps with the band scale and 4^-l folded in) are staged
+    // once both are in flight, so the two round trips overlap. Every lane
+    // loads (past the end: the last tap again) and stores only its own.
+    constexpr int MWB = cdiv(KB2P, NT), NWL = 4 * L * K2P, MWL = cdiv(NWL, NT);
+    float wbv[MWB], wlv[MWL], scv[MWL];
+#pragma unroll
+    for (int k = 0; k < MWB; ++k) {
+        const int t = min(tid + k * NT, KB * KB - 1);
+        wbv[k] = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)];
     }
+#pragma unroll
+    for (int k = 0; k < MWL; ++k) {
+        const int t = min(tid + k * NT, NWL - 1);
+        const int ls = t / K2P, tap = min(t - ls * K2P, K * K - 1), l = ls >> 2, s = ls & 3;
+        const size_t pi = ((size_t)l * C + c) * 4 + s;
+        scv[k] = scale[pi];
+        wlv[k] = w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)];
+    }
+    auto stage_taps = [&]() {
+#pragma unroll
+        for (int k = 0; k < MWB; ++k) {
+            const int t = tid + k * NT;
+            if (t < KB2P) WB[t] = t < KB * KB ? wbv[k] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < MWL; ++k) {
+            const int t = tid + k * NT;
+            if (t < NWL) {
+                const int ls = t / K2P, tap = t - ls * K2P, l = ls >> 2;
+                const float f = scv[k] * (1.0f / (float)(1 << (2 * (l + 1))));
+                WL[t] = tap < K * K ? wlv[k] * f : 0.f;
+            }
+        }
+    };
     {
         // The whole bordered x plane and the bordered level-1 bands in one
         // pass. An item owns x rows 2i, 2i+1 and VA columns from 2*j0 (one
@@ -410,6 +437,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
                 r1[k].w[e] = inside ? r1[k].w[e] : 0u;
             }
         }
+        stage_taps();
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int qa = tid + k * NT;
