@@ -492,6 +492,12 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     uint4 tv[MT];
 #pragma unroll
     for (int k = 0; k < MT; ++k) tv[k] = timg[min(tid + k * NT, TW4 - 1)];
+    // The coarse image's values under this thread's output strips (what the
+    // levels above L0 add, constant on 2^L0 blocks): loaded with the x rows,
+    // used by the synthesis at the end.
+    constexpr int CW = W >> L0, NSTRIP = MF ? P::MFW : P::MB, RSTRIP = MF ? 4 : RB;
+    const float* __restrict__ ctile = coarse ? coarse + ((size_t)plane * (H >> L0) + (r0 >> L0)) * CW : nullptr;
+    float cpre[NSTRIP][RSTRIP >> L0];
     {
         // Border columns, written once: the x rows' columns outside the
         // plane and the level-1 bands' zero border columns (nothing else
@@ -533,6 +539,29 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
             for (int e = 0; e < RawVec<T, 4>::N; ++e) {
                 v0[k].w[e] = inside ? v0[k].w[e] : 0u;
                 v1[k].w[e] = inside ? v1[k].w[e] : 0u;
+            }
+        }
+        {
+            const int lane = tid & 63, wv = tid >> 6;
+            auto cload = [&](int s, int h0, int w) {
+#pragma unroll
+                for (int p = 0; p < (RSTRIP >> L0); ++p)
+                    cpre[s][p] = ctile ? ctile[(uint32_t)(((h0 >> L0) + p) * CW + (w >> L0))] : 0.f;
+            };
+            if constexpr (MF) {
+                if (wv < P::NW / 2) {
+#pragma unroll
+                    for (int bb = 0; bb < NSTRIP; ++bb) {
+                        const int blk = wv + bb * (P::NW / 2), rbk = blk / (W / 16), cbk = blk - rbk * (W / 16);
+                        cload(bb, 16 * rbk + 4 * (lane >> 4), 16 * cbk + (lane & 15));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int it = 0; it < NSTRIP; ++it) {
+                    const int item = min(tid + it * NT, NIB - 1), rb = item / LPB, w = min(item - rb * LPB, W - 1);
+                    cload(it, rb * RB, w);
+                }
             }
         }
 #pragma unroll
@@ -711,26 +740,19 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     // y = base + closed-form synthesis of the fine levels + the coarse image.
     // Stores and coarse reads use the tile's uniform bases plus 32-bit lane
     // offsets (rows at constant offsets from one address).
-    constexpr int CW = W >> L0;
     static_assert(RB % 2 == 0, "bf16 rows are narrowed in pairs");
-    const float* __restrict__ ctile = coarse ? coarse + ((size_t)plane * (H >> L0) + (r0 >> L0)) * CW : nullptr;
     T* __restrict__ dtile = dst + (size_t)r0 * W;
-    // one strip of R output rows from h0 in column w, base results yv
-    auto synth_store = [&](auto rc, const int h0, const int w, const float* yv) {
+    // one strip of R output rows from h0 in column w, base results yv, the
+    // coarse image's values cv (loaded at the start)
+    auto synth_store = [&](auto rc, const int h0, const int w, const float* yv, const float* cv) {
         constexpr int RS = decltype(rc)::value;
         static_assert(RS % (1 << L0) == 0 && RS % 2 == 0, "strips of whole 2^L0 blocks, rows in pairs");
         // From the coarse image down to level 1, carry[p] is what the
         // coarser levels add to every row of level-l block p; level l splits
         // it into its two half-blocks as carry + a +- b.
         float carry[RS];
-        if (ctile) {
-            const float* const cp = ctile + (uint32_t)((h0 >> L0) * CW + (w >> L0));
 #pragma unroll
-            for (int p = 0; p < (RS >> L0); ++p) carry[p] = cp[p * CW];
-        } else {
-#pragma unroll
-            for (int p = 0; p < (RS >> L0); ++p) carry[p] = 0.f;
-        }
+        for (int p = 0; p < (RS >> L0); ++p) carry[p] = cv[p];
         P::for_levels([&](auto lc) {
             constexpr int l = L0 + 1 - decltype(lc)::value;   // L0, ..., 1
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
@@ -771,7 +793,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb) {
                 const int blk = wv + bb * (NWV / 2), rbk = blk / NBC, cbk = blk - rbk * NBC;
-                synth_store(std::integral_constant<int, 4>{}, 16 * rbk + 4 * mq, 16 * cbk + mn, yb[bb]);
+                synth_store(std::integral_constant<int, 4>{}, 16 * rbk + 4 * mq, 16 * cbk + mn, yb[bb], cpre[bb]);
             }
         }
     } else {
@@ -781,7 +803,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
             if (!(NIB % NT == 0 || item < NIB)) continue;
             const int rb = item / LPB, w = item - rb * LPB;
             if (!(LPB == W || w < W)) continue;
-            synth_store(std::integral_constant<int, RB>{}, rb * RB, w, yb[it]);
+            synth_store(std::integral_constant<int, RB>{}, rb * RB, w, yb[it], cpre[it]);
         }
     }
 }
