@@ -460,11 +460,8 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             const bf16_t* s0 = xs + (inside ? (uint32_t)(pr * W + 4 * uu) : 0u);
             load_raw<bf16_t, 4>(s0, vx0[k]);
             load_raw<bf16_t, 4>(s0 + (inside ? W : 0), vx1[k]);
-#pragma unroll
-            for (int e = 0; e < RawVec<bf16_t, 4>::N; ++e) {
-                vx0[k].w[e] = inside ? vx0[k].w[e] : 0u;
-                vx1[k].w[e] = inside ? vx1[k].w[e] : 0u;
-            }
+            // (the rows outside the plane are zeroed where they are used: a
+            // select here would wait for the loads and undo the prefetch)
         }
 #pragma unroll
         for (int k = 0; k < MQD; ++k) {
@@ -493,7 +490,14 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             for (int k = 0; k < MQX; ++k) {
                 const int q = tid + k * NT;
                 if (!(NQX % NT == 0 || q < NQX)) continue;
-                const int ii = udiv(q, QW), uu = q - ii * QW;
+                const int ii = udiv(q, QW), uu = q - ii * QW, pr = r0 - G + 2 * ii;
+                if (pr < 0 || pr >= H) {   // rows outside the plane: zeros
+#pragma unroll
+                    for (int e = 0; e < RawVec<bf16_t, 4>::N; ++e) {
+                        vx0[k].w[e] = 0u;
+                        vx1[k].w[e] = 0u;
+                    }
+                }
                 // the x rows the base taps read, as loaded
                 const int xr = 2 * ii - (G - PB);
                 if (xr >= 0 && xr < XRM)
