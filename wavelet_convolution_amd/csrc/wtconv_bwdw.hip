@@ -446,7 +446,16 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 
     // x: region rows 2ii, 2ii+1 (plane rows r0-G+2ii..), four columns from
     // 4uu; dy: tile rows 2ii, 2ii+1. Rows outside the plane load as zeros.
-    RawVec<bf16_t, 4> vx0[MQX], vx1[MQX], vd0[MQD], vd1[MQD];
+    // Held as 64-bit words until they are used: a 64-bit value keeps its
+    // aligned register pair, where two 32-bit halves may be moved apart
+    // right after the load, which waits for it and undoes the prefetch.
+    uint64_t lx0[MQX], lx1[MQX], ld0[MQD], ld1[MQD];
+    auto raw4 = [](uint64_t v) {
+        RawVec<bf16_t, 4> r;
+        r.w[0] = (uint32_t)v;
+        r.w[1] = (uint32_t)(v >> 32);
+        return r;
+    };
     auto issue_loads = [&](int u) {
         const int b = u / P::NTILE, r0 = (u - b * P::NTILE) * TH;
         const size_t plane = (size_t)b * C + c;
@@ -458,8 +467,8 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             const int ii = udiv(q, QW), uu = q - ii * QW, pr = r0 - G + 2 * ii;
             const bool inside = (NQX % NT == 0 || q < NQX) && pr >= 0 && pr < H;
             const bf16_t* s0 = xs + (inside ? (uint32_t)(pr * W + 4 * uu) : 0u);
-            load_raw<bf16_t, 4>(s0, vx0[k]);
-            load_raw<bf16_t, 4>(s0 + (inside ? W : 0), vx1[k]);
+            lx0[k] = *reinterpret_cast<const uint64_t*>(s0);
+            lx1[k] = *reinterpret_cast<const uint64_t*>(s0 + (inside ? W : 0));
             // (the rows outside the plane are zeroed where they are used: a
             // select here would wait for the loads and undo the prefetch)
         }
@@ -468,8 +477,8 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             const int q = tid + k * NT;
             if (!(NQD % NT == 0 || q < NQD)) continue;
             const int ii = udiv(q, QW), uu = q - ii * QW;
-            load_raw<bf16_t, 4>(ds + (uint32_t)(2 * ii * W + 4 * uu), vd0[k]);
-            load_raw<bf16_t, 4>(ds + (uint32_t)((2 * ii + 1) * W + 4 * uu), vd1[k]);
+            ld0[k] = *reinterpret_cast<const uint64_t*>(ds + (uint32_t)(2 * ii * W + 4 * uu));
+            ld1[k] = *reinterpret_cast<const uint64_t*>(ds + (uint32_t)((2 * ii + 1) * W + 4 * uu));
         }
     };
     if (u0 < u1) issue_loads(u0);
@@ -491,22 +500,23 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 const int q = tid + k * NT;
                 if (!(NQX % NT == 0 || q < NQX)) continue;
                 const int ii = udiv(q, QW), uu = q - ii * QW, pr = r0 - G + 2 * ii;
+                RawVec<bf16_t, 4> vx0 = raw4(lx0[k]), vx1 = raw4(lx1[k]);
                 if (pr < 0 || pr >= H) {   // rows outside the plane: zeros
 #pragma unroll
                     for (int e = 0; e < RawVec<bf16_t, 4>::N; ++e) {
-                        vx0[k].w[e] = 0u;
-                        vx1[k].w[e] = 0u;
+                        vx0.w[e] = 0u;
+                        vx1.w[e] = 0u;
                     }
                 }
                 // the x rows the base taps read, as loaded
                 const int xr = 2 * ii - (G - PB);
                 if (xr >= 0 && xr < XRM)
-                    *reinterpret_cast<uint2*>(XS + xr * SXBM + 4 * uu) = make_uint2(vx0[k].w[0], vx0[k].w[1]);
+                    *reinterpret_cast<uint2*>(XS + xr * SXBM + 4 * uu) = make_uint2(vx0.w[0], vx0.w[1]);
                 if (xr + 1 >= 0 && xr + 1 < XRM)
-                    *reinterpret_cast<uint2*>(XS + (xr + 1) * SXBM + 4 * uu) = make_uint2(vx1[k].w[0], vx1[k].w[1]);
+                    *reinterpret_cast<uint2*>(XS + (xr + 1) * SXBM + 4 * uu) = make_uint2(vx1.w[0], vx1.w[1]);
                 float f0[4], f1[4];
-                widen_raw<bf16_t, 4>(vx0[k], f0);
-                widen_raw<bf16_t, 4>(vx1[k], f1);
+                widen_raw<bf16_t, 4>(vx0, f0);
+                widen_raw<bf16_t, 4>(vx1, f1);
                 float bb[2][4];
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
@@ -520,6 +530,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 const int q = tid + k * NT;
                 if (!(NQD % NT == 0 || q < NQD)) continue;
                 const int ii = udiv(q, QW), uu = q - ii * QW;
+                const RawVec<bf16_t, 4> vd0 = raw4(ld0[k]), vd1 = raw4(ld1[k]);
                 // pair words c..c+3 as one 16-byte store; the last needs the
                 // next item's first value (the next lane: a row's items are
                 // one wavefront), zero past the plane; the word before
@@ -527,7 +538,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 static_assert(64 % QW == 0, "a dy row's items on consecutive lanes of one wavefront");
 #pragma unroll
                 for (int rs = 0; rs < 2; ++rs) {
-                    const uint32_t w0 = rs ? vd1[k].w[0] : vd0[k].w[0], w1 = rs ? vd1[k].w[1] : vd0[k].w[1];
+                    const uint32_t w0 = rs ? vd1.w[0] : vd0.w[0], w1 = rs ? vd1.w[1] : vd0.w[1];
                     const uint32_t nx = (uint32_t)__shfl_down((int)w0, 1, 64);
                     const uint32_t w3 = (w1 >> 16) | (uu + 1 < QW ? (nx << 16) : 0u);
                     const int wb = (2 * ii + rs) * SDP + DOFF + 4 * uu;
@@ -535,8 +546,8 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                     if (uu == 0) DP[wb - 1] = w0 << 16;
                 }
                 float f0[4], f1[4];
-                widen_raw<bf16_t, 4>(vd0[k], f0);
-                widen_raw<bf16_t, 4>(vd1[k], f1);
+                widen_raw<bf16_t, 4>(vd0, f0);
+                widen_raw<bf16_t, 4>(vd1, f1);
                 float bb[2][4];
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
