@@ -470,6 +470,9 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     uint16_t* const ZC = reinterpret_cast<uint16_t*>(WL + 4 * L0 * K2P);        // banded taps (MF)
 
     const int tid = threadIdx.x;
+    // the wavefront index as a scalar: row indices derived from it (P0's
+    // items are a wavefront per row pair on 256-wide planes) stay uniform
+    const int wvu = __builtin_amdgcn_readfirstlane(tid >> 6), lane_ = tid & 63;
     const int lid = xcd_local_index();
     const int plane = lid / P::NTILE, tile = lid - plane * P::NTILE;
     const int c = plane % C;
@@ -496,7 +499,8 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     // levels above L0 add, constant on 2^L0 blocks): loaded with the x rows,
     // used by the synthesis at the end.
     constexpr int CW = W >> L0, NSTRIP = MF ? P::MFW : P::MB, RSTRIP = MF ? 4 : RB;
-    const float* __restrict__ ctile = coarse ? coarse + ((size_t)plane * (H >> L0) + (r0 >> L0)) * CW : nullptr;
+    // (a plan with no levels above L0 has no coarse image: zeros)
+    const float* __restrict__ ctile = P::LT > L0 ? coarse + ((size_t)plane * (H >> L0) + (r0 >> L0)) * CW : nullptr;
     float cpre[NSTRIP][RSTRIP >> L0];
     {
         // Border columns, written once: the x rows' columns outside the
@@ -528,7 +532,8 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
-            const int ii = udiv(q, QW), uu = q - ii * QW, pr = rtop + 2 * ii;
+            const int ii = QW == 64 ? wvu + k * (NT / 64) : udiv(q, QW), uu = QW == 64 ? lane_ : q - ii * QW;
+            const int pr = rtop + 2 * ii;
             // every lane loads (rows outside the plane: its first words) and
             // then selects zeros: no branch around the loads
             const bool inside = (NQI % NT == 0 || q < NQI) && pr >= 0 && pr < H;
@@ -542,11 +547,11 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
             }
         }
         {
-            const int lane = tid & 63, wv = tid >> 6;
+            const int lane = lane_, wv = wvu;
             auto cload = [&](int s, int h0, int w) {
 #pragma unroll
                 for (int p = 0; p < (RSTRIP >> L0); ++p)
-                    cpre[s][p] = ctile ? ctile[(uint32_t)(((h0 >> L0) + p) * CW + (w >> L0))] : 0.f;
+                    cpre[s][p] = P::LT > L0 ? ctile[(uint32_t)(((h0 >> L0) + p) * CW + (w >> L0))] : 0.f;
             };
             if constexpr (MF) {
                 if (wv < P::NW / 2) {
@@ -571,7 +576,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
         for (int k = 0; k < MQ; ++k) {
             const int q = tid + k * NT;
             if (!(NQI % NT == 0 || q < NQI)) continue;
-            const int ii = udiv(q, QW), uu = q - ii * QW;
+            const int ii = QW == 64 ? wvu + k * (NT / 64) : udiv(q, QW), uu = QW == 64 ? lane_ : q - ii * QW;
             float f0[4], f1[4];
             widen_raw<T, 4>(v0[k], f0);
             widen_raw<T, 4>(v1[k], f1);
@@ -602,7 +607,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     // matrix-core form: 16 x 16 output blocks, MFW on each of the lower half
     // of the wavefronts; the upper half convolves level 1 meanwhile
     constexpr int NWV = NT / 64, NBC = W / 16, NBW = P::MFW;
-    const int lane = tid & 63, wv = tid >> 6, mn = lane & 15, mq = lane >> 4;
+    const int lane = lane_, wv = wvu, mn = lane & 15, mq = lane >> 4;
     float yb[MF ? NBW : MB][MF ? 4 : RB];
     // level convolutions: strips of rl(l) output rows x 1 column of one band,
     // on threads lvl_t0 .. lvl_t0 + lvl_nt
