@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace wtc {
 
 typedef uint16_t bf16_t;
@@ -19,6 +21,17 @@ constexpr int odd_stride(int w) { return (w % 2 == 0) ? w + 1 : w; }
 
 // a / b for a >= 0 and b > 0, in unsigned arithmetic: no sign fix-up
 __device__ __forceinline__ int udiv(int a, int b) { return (int)((unsigned)a / (unsigned)b); }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): an
+// unrolled loop whose index is a compile-time constant in the body
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }

@@ -615,15 +615,28 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
         constexpr int l = decltype(lc)::value;
         constexpr int wl = W >> l, R = P::rl(l), NS = P::hout(l) / R, LP = P::lpl(l), NIl = P::nil(l);
         constexpr int T0 = P::lvl_t0(l, MF), TN = P::lvl_nt(l, MF);
-        const int lt = tid - T0;
-        if (lt < 0 || lt >= TN) return;
+        if constexpr (LP % 64 == 0 && TN % 64 == 0 && T0 % 64 == 0 && NIl % TN == 0) {
+            // a wavefront's 64 items share band and strip row: those stay
+            // scalar, the column is the lane's
+            if (wvu < T0 / 64 || wvu >= (T0 + TN) / 64) return;
 #pragma unroll
-        for (int it = 0; it < cdiv(NIl, TN); ++it) {
-            const int item = lt + it * TN;
-            if (NIl % TN == 0 || item < NIl) {
-                const int s = item / (NS * LP), rem = item - s * (NS * LP);
-                const int rs = rem / LP, j = rem - rs * LP;
+            for (int it = 0; it < NIl / TN; ++it) {
+                const int wb = (wvu - T0 / 64) * 64 + it * TN;
+                const int s = wb / (NS * LP), rem = wb - s * (NS * LP);
+                const int rs = rem / LP, j = rem - rs * LP + lane_;
                 if (LP == wl || j < wl) f(it, s, (G >> l) + rs * R, j);
+            }
+        } else {
+            const int lt = tid - T0;
+            if (lt < 0 || lt >= TN) return;
+#pragma unroll
+            for (int it = 0; it < cdiv(NIl, TN); ++it) {
+                const int item = lt + it * TN;
+                if (NIl % TN == 0 || item < NIl) {
+                    const int s = item / (NS * LP), rem = item - s * (NS * LP);
+                    const int rs = rem / LP, j = rem - rs * LP;
+                    if (LP == wl || j < wl) f(it, s, (G >> l) + rs * R, j);
+                }
             }
         }
     };
@@ -703,7 +716,8 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
             Ul[rb * Sl + (q < PK ? q : q + wl)] = 0.f;
         }
         for (int q = tid; q < RL * wl; q += NT) {
-            const int i = udiv(q, wl), j = q - i * wl;
+            // (64-wide bands: a wavefront per band row, the row a scalar)
+            const int i = wl == 64 ? wvu + (q - tid) / 64 : udiv(q, wl), j = wl == 64 ? lane_ : q - i * wl;
             const float2 t = *reinterpret_cast<const float2*>(LLp + 2 * i * Sp + 2 * j);
             const float2 d = *reinterpret_cast<const float2*>(LLp + (2 * i + 1) * Sp + 2 * j);
             float b[4];
@@ -747,10 +761,12 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     // offsets (rows at constant offsets from one address).
     static_assert(RB % 2 == 0, "bf16 rows are narrowed in pairs");
     T* __restrict__ dtile = dst + (size_t)r0 * W;
-    // one strip of R output rows from h0 in column w, base results yv, the
-    // coarse image's values cv (loaded at the start)
-    auto synth_store = [&](auto rc, const int h0, const int w, const float* yv, const float* cv) {
-        constexpr int RS = decltype(rc)::value;
+    // one strip of R output rows from h0 in column w + CO, base results yv,
+    // the coarse image's values cv (loaded at the start); CO, a constant
+    // multiple of 64, folds into the addresses' immediate offsets
+    auto synth_store = [&](auto rc, auto co, const int h0, const int w, const float* yv, const float* cv) {
+        constexpr int RS = decltype(rc)::value, CO = decltype(co)::value;
+        static_assert(CO % 64 == 0 && L0 <= 6, "column offsets that leave every level's parity alone");
         static_assert(RS % (1 << L0) == 0 && RS % 2 == 0, "strips of whole 2^L0 blocks, rows in pairs");
         // From the coarse image down to level 1, carry[p] is what the
         // coarser levels add to every row of level-l block p; level l splits
@@ -761,7 +777,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
         P::for_levels([&](auto lc) {
             constexpr int l = L0 + 1 - decltype(lc)::value;   // L0, ..., 1
             constexpr int Sl = P::su(l), BSl = P::bandsz(l);
-            const float* Zl = ubase(std::integral_constant<int, l>{}) + ((G >> l) + (h0 >> l)) * Sl + PK + (w >> l);
+            const float* Zl = ubase(std::integral_constant<int, l>{}) + ((G >> l) + (h0 >> l)) * Sl + PK + (w >> l) + (CO >> l);
             const float sw = ((w >> (l - 1)) & 1) ? -1.f : 1.f;
             float next[RS >> (l - 1)];
 #pragma unroll
@@ -775,7 +791,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
 #pragma unroll
             for (int q = 0; q < (RS >> (l - 1)); ++q) carry[q] = next[q];
         });
-        T* const out_col = dtile + (uint32_t)(h0 * W + w);
+        T* const out_col = dtile + (uint32_t)(h0 * W + w) + CO;
         if constexpr (sizeof(T) == 2) {
             // two rows per conversion: the low half to row o, the high half to o + 1
 #pragma unroll
@@ -795,10 +811,20 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
     if constexpr (MF) {
         // the matrix-core blocks: rows 4(l/16)..+3 of column l%16 of each block
         if (wv < NWV / 2) {
+            if constexpr (TH == 16 && (16 * (NWV / 2)) % 64 == 0) {
+                // one row of blocks: block bb sits 16 (NWV / 2) bb columns on
+                static_for<NBW>([&](auto bc) {
+                    constexpr int bb = decltype(bc)::value;
+                    synth_store(std::integral_constant<int, 4>{}, std::integral_constant<int, 16 * (NWV / 2) * bb>{},
+                                4 * mq, 16 * wv + mn, yb[bb], cpre[bb]);
+                });
+            } else {
 #pragma unroll
-            for (int bb = 0; bb < NBW; ++bb) {
-                const int blk = wv + bb * (NWV / 2), rbk = blk / NBC, cbk = blk - rbk * NBC;
-                synth_store(std::integral_constant<int, 4>{}, 16 * rbk + 4 * mq, 16 * cbk + mn, yb[bb], cpre[bb]);
+                for (int bb = 0; bb < NBW; ++bb) {
+                    const int blk = wv + bb * (NWV / 2), rbk = blk / NBC, cbk = blk - rbk * NBC;
+                    synth_store(std::integral_constant<int, 4>{}, std::integral_constant<int, 0>{}, 16 * rbk + 4 * mq,
+                                16 * cbk + mn, yb[bb], cpre[bb]);
+                }
             }
         }
     } else {
@@ -808,7 +834,7 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
             if (!(NIB % NT == 0 || item < NIB)) continue;
             const int rb = item / LPB, w = item - rb * LPB;
             if (!(LPB == W || w < W)) continue;
-            synth_store(std::integral_constant<int, RB>{}, rb * RB, w, yb[it], cpre[it]);
+            synth_store(std::integral_constant<int, RB>{}, std::integral_constant<int, 0>{}, rb * RB, w, yb[it], cpre[it]);
         }
     }
 }
