@@ -259,7 +259,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
                 store_lds<T, VL>(DY + rr * SD + col, vd[k]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (u + 1 < u1) issue_loads(u + 1);
         // ----------------------------------------- P1: level 1 analysis
         {
@@ -284,7 +284,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
                 for (int s = 0; s < 4; ++s) Vb[s * VS1 + i * SV1 + j] = vv[s];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ----------------------------------------- P2: levels 2..L0 analysis
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
@@ -311,7 +311,7 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
 #pragma unroll
                     for (int s = 0; s < 4; ++s) Vl[s * VSl + i * SVl + j] = vv[s];
                 }
-                __syncthreads();
+                lds_barrier();
             }
         });
         // the coarse pass's inputs: the tile's level-L0 LL sums of x and dy
@@ -351,7 +351,10 @@ void tile_bwdw_kernel(const T* __restrict__ x, const T* __restrict__ dy, float* 
             });
         }
         // the next unit's P0 overwrites x, dy, U and V: wait for every reader
-        __syncthreads();
+        // (the loop's barriers order LDS only: the LL sums this unit wrote to
+        // global memory are read by a later kernel, and the next unit's
+        // loads stay in flight)
+        lds_barrier();
     }
 
 #pragma unroll
@@ -557,7 +560,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                     *reinterpret_cast<float2*>(V1 + sb * VS1 + ii * SV1 + 2 * uu) = make_float2(bb[0][sb], bb[1][sb]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (u + 1 < u1) issue_loads(u + 1);
 
         // level taps of level l: band `band` on the lanes of its wavefronts
@@ -589,7 +592,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             }
         }
         level_taps(std::integral_constant<int, 1>{});
-        __syncthreads();   // the x rows and dy words are dead: level 2 goes over them
+        lds_barrier();   // the x rows and dy words are dead: level 2 goes over them
         // ----------------------------------------- P2: level 2 analysis
         {
             constexpr int rl = P::rh(2), wl = W >> 2, Sl = P::su(2), BSl = P::bandsz(2), VSl = P::vsz(2);
@@ -619,7 +622,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 for (int sb = 0; sb < 4; ++sb) V2[sb * VSl + i * SVl + j] = vv[sb];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // the coarse pass's inputs: the tile's level-2 LL sums of x and dy
         if (P::LT > L0) {
             constexpr int hl = TH >> L0, wl = W >> L0, Sl = P::su(L0), GLv = G >> L0;
@@ -636,7 +639,10 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
         // ------------------------------------------------ P3: level-2 taps
         level_taps(std::integral_constant<int, 2>{});
         // the next unit's P0 overwrites every region: wait for every reader
-        __syncthreads();
+        // (the loop's barriers order LDS only: the LL sums this unit wrote to
+        // global memory are read by a later kernel, and the next unit's
+        // loads stay in flight)
+        lds_barrier();
     }
 
 #pragma unroll

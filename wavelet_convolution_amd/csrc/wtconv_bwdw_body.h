@@ -455,7 +455,7 @@ __device__ __forceinline__ void bwdw_body(const T* __restrict__ x, const T* __re
     for (int b = b0; b < b1; b += NPB) {
         if (!P::PREFETCH) issue_loads(b);
         // the previous step's taps read x, dy and the bands: all done first
-        if (b > b0) __syncthreads();
+        if (b > b0) lds_barrier();   // (LDS only: the next step's loads stay in flight)
         // ------------------------------------ P0: stream in and analyse
         if (tid < NPB * NA) {
             float xv[2][CW], dv[2][CW];
@@ -546,7 +546,9 @@ __device__ __forceinline__ void bwdw_body(const T* __restrict__ x, const T* __re
                 }
             }
         }
-        __syncthreads();
+        // (LDS only: the LL sums written to global memory above are read by
+        // a later pass, and the next step's loads stay in flight)
+        lds_barrier();
         // ------------------- P3: all taps at once, base taps and one band per wavefront
         if (BASE && grp == 0) {
             if constexpr (P::BASE_PAIR) {

@@ -22,6 +22,18 @@ constexpr int odd_stride(int w) { return (w % 2 == 0) ? w + 1 : w; }
 // a / b for a >= 0 and b > 0, in unsigned arithmetic: no sign fix-up
 __device__ __forceinline__ int udiv(int a, int b) { return (int)((unsigned)a / (unsigned)b); }
 
+// A workgroup barrier that orders LDS only: each wavefront waits for its
+// own LDS operations, not for its global loads and stores, so a prefetch
+// in flight stays in flight across it (a full barrier waits for every
+// outstanding vector memory operation, and loads and stores share one
+// counter). For barriers where no wavefront reads what another wrote to
+// global memory before it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): an
 // unrolled loop whose index is a compile-time constant in the body
 template <class F, int... I>
