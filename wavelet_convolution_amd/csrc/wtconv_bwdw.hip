@@ -426,7 +426,8 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
         else return V2;
     };
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // (the wavefront index as a scalar: row indices derived from it stay uniform)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int band = wave & 3, blane = ((wave >> 2) << 6) + lane;
     const int c = blockIdx.x % C, chunk = blockIdx.x / C;
     const int nunits = B * P::NTILE;
@@ -467,7 +468,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
 #pragma unroll
         for (int k = 0; k < MQX; ++k) {
             const int q = tid + k * NT;
-            const int ii = udiv(q, QW), uu = q - ii * QW, pr = r0 - G + 2 * ii;
+            const int ii = QW == 64 ? wave + k * (NT / 64) : udiv(q, QW), uu = QW == 64 ? lane : q - ii * QW, pr = r0 - G + 2 * ii;
             const bool inside = (NQX % NT == 0 || q < NQX) && pr >= 0 && pr < H;
             const bf16_t* s0 = xs + (inside ? (uint32_t)(pr * W + 4 * uu) : 0u);
             lx0[k] = *reinterpret_cast<const uint64_t*>(s0);
@@ -479,7 +480,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
         for (int k = 0; k < MQD; ++k) {
             const int q = tid + k * NT;
             if (!(NQD % NT == 0 || q < NQD)) continue;
-            const int ii = udiv(q, QW), uu = q - ii * QW;
+            const int ii = QW == 64 ? wave + k * (NT / 64) : udiv(q, QW), uu = QW == 64 ? lane : q - ii * QW;
             ld0[k] = *reinterpret_cast<const uint64_t*>(ds + (uint32_t)(2 * ii * W + 4 * uu));
             ld1[k] = *reinterpret_cast<const uint64_t*>(ds + (uint32_t)((2 * ii + 1) * W + 4 * uu));
         }
@@ -502,7 +503,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             for (int k = 0; k < MQX; ++k) {
                 const int q = tid + k * NT;
                 if (!(NQX % NT == 0 || q < NQX)) continue;
-                const int ii = udiv(q, QW), uu = q - ii * QW, pr = r0 - G + 2 * ii;
+                const int ii = QW == 64 ? wave + k * (NT / 64) : udiv(q, QW), uu = QW == 64 ? lane : q - ii * QW, pr = r0 - G + 2 * ii;
                 RawVec<bf16_t, 4> vx0 = raw4(lx0[k]), vx1 = raw4(lx1[k]);
                 if (pr < 0 || pr >= H) {   // rows outside the plane: zeros
 #pragma unroll
@@ -532,7 +533,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             for (int k = 0; k < MQD; ++k) {
                 const int q = tid + k * NT;
                 if (!(NQD % NT == 0 || q < NQD)) continue;
-                const int ii = udiv(q, QW), uu = q - ii * QW;
+                const int ii = QW == 64 ? wave + k * (NT / 64) : udiv(q, QW), uu = QW == 64 ? lane : q - ii * QW;
                 const RawVec<bf16_t, 4> vd0 = raw4(ld0[k]), vd1 = raw4(ld1[k]);
                 // pair words c..c+3 as one 16-byte store; the last needs the
                 // next item's first value (the next lane: a row's items are
@@ -604,7 +605,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 U2[rb * Sl + (q < PK ? q : q + wl)] = 0.f;
             }
             for (int q = tid; q < rl * wl; q += NT) {
-                const int i = q / wl, j = q - i * wl;
+                const int i = wl == 64 ? wave + (q - tid) / 64 : q / wl, j = wl == 64 ? lane : q - i * wl;
                 const float2 t0 = *reinterpret_cast<const float2*>(LLu + 2 * i * Sp + 2 * j);
                 const float2 t1 = *reinterpret_cast<const float2*>(LLu + (2 * i + 1) * Sp + 2 * j);
                 float uu[4];
@@ -613,7 +614,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
                 for (int sb = 0; sb < 4; ++sb) U2[sb * BSl + i * Sl + PK + j] = uu[sb];
             }
             for (int q = tid; q < (TH >> 2) * wl; q += NT) {
-                const int i = q / wl, j = q - i * wl;
+                const int i = wl == 64 ? wave + (q - tid) / 64 : q / wl, j = wl == 64 ? lane : q - i * wl;
                 const float2 t0 = *reinterpret_cast<const float2*>(V1 + 2 * i * SVp + 2 * j);
                 const float2 t1 = *reinterpret_cast<const float2*>(V1 + (2 * i + 1) * SVp + 2 * j);
                 float vv[4];
@@ -631,7 +632,7 @@ void tile_bwdw_mf_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict_
             float* pdo = pdy + plane * (H >> L0) * wl + (size_t)(r0 >> L0) * wl;
             constexpr int SVL = P::sv(L0);
             for (int q = tid; q < hl * wl; q += NT) {
-                const int i = q / wl, j = q - i * wl;
+                const int i = wl == 64 ? wave + (q - tid) / 64 : q / wl, j = wl == 64 ? lane : q - i * wl;
                 pxo[q] = LLu[(GLv + i) * Sl + j];
                 pdo[q] = V2[i * SVL + j];
             }
