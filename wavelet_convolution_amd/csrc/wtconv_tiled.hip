@@ -640,7 +640,14 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
             }
         }
     };
-    float z1[cdiv(P::nil(1), P::lvl_nt(1, MF))][P::rl(1)];
+    // Matrix-core form on a band of whole 64-lane pairs of columns: a level-1
+    // item is two adjacent output columns of one band (conv_tile with two
+    // columns reads each window row once for both: half the LDS reads of two
+    // one-column strips), one item per upper-half thread, the band scalar.
+    constexpr bool L1P = MF && (W1 / 2) % 64 == 0 && 4 * (W1 / 2) == NT / 2 && P::hout(1) == P::rl(1);
+    float z1[cdiv(P::nil(1), P::lvl_nt(1, MF))][P::rl(1)];   // (unused with L1P)
+    float z1p[L1P ? P::rl(1) : 1][2];
+    const int p_s = wvu - NT / 128, p_j = 2 * lane_;   // band, first column (upper half, L1P)
     auto level1_conv = [&]() {
         level_items(std::integral_constant<int, 1>{}, [&](int it, int s, int row, int j) {
             conv_col<K, P::rl(1), S1>(Bq + s * BS1 + (row - PK) * S1 + j, WL + s * K2P, z1[it]);
@@ -688,7 +695,10 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
 #pragma unroll
                 for (int o = 0; o < 4; ++o) yb[bb][o] = acc[bb][o];
         } else {
-            level1_conv();
+            if constexpr (L1P)
+                conv_tile<K, P::rl(1), 2, S1>(Bq + p_s * BS1 + ((G >> 1) - PK) * S1 + p_j, WL + p_s * K2P, z1p);
+            else
+                level1_conv();
         }
     } else {
 #pragma unroll
@@ -742,10 +752,19 @@ void coltile_kernel(const T* __restrict__ in, const float* __restrict__ taps, co
         });
     }
     __syncthreads();
-    level_items(std::integral_constant<int, 1>{}, [&](int it, int s, int row, int j) {
+    if constexpr (L1P) {
+        if (wvu >= NT / 128) {
 #pragma unroll
-        for (int o = 0; o < P::rl(1); ++o) Bq[s * BS1 + (row + o) * S1 + PK + j] = z1[it][o];
-    });
+            for (int o = 0; o < P::rl(1); ++o)
+                *reinterpret_cast<float2*>(Bq + p_s * BS1 + ((G >> 1) + o) * S1 + PK + p_j) =
+                    make_float2(z1p[o][0], z1p[o][1]);
+        }
+    } else {
+        level_items(std::integral_constant<int, 1>{}, [&](int it, int s, int row, int j) {
+#pragma unroll
+            for (int o = 0; o < P::rl(1); ++o) Bq[s * BS1 + (row + o) * S1 + PK + j] = z1[it][o];
+        });
+    }
     if constexpr (L0 >= 2) {
         constexpr int S2 = P::su(2), BS2 = P::bandsz(2), U2 = P::uoff(2);
         level_items(std::integral_constant<int, 2>{}, [&](int it, int s, int row, int j) {
