@@ -147,7 +147,12 @@ struct TileBwPlan {
     static constexpr int AM = XSM + DPM > U2M + V2M ? XSM + DPM : U2M + V2M;   // x rows + dy words, then level 2
     static constexpr int DATAM = AM + U1M + V1M, REDM = NWM * (256 + ACCM);
     static constexpr int MF_FLOATS = DATAM > REDM ? DATAM : REDM;
-    static constexpr int band_rows_mf(int l) { return pick_rows(TH >> l, W >> l, BLM, K); }
+    // (level 2 in four-row strips on half the lanes rather than two-row
+    // strips on all: fewer LDS reads per multiply-add, and the waves wait on
+    // LDS instruction issue more than on multiply-adds)
+    static constexpr int band_rows_mf(int l) {
+        return l == 2 && (TH >> 2) % 4 == 0 ? 4 : pick_rows(TH >> l, W >> l, BLM, K);
+    }
     static_assert(!MF || (L0 == 2 && NWM % (TH / 2) == 0 && (W / 32) % WPR == 0 && KB <= 7 && PK % 2 == 0 && DOFF % 4 == 0 && SDP % 4 == 0 &&
                           7 - PB <= DOFF && DOFF + PB + W < SDP && SXBM % 8 == 0 &&
                           MF_FLOATS * 4 <= 160 * 1024),
