@@ -345,12 +345,24 @@ wtconv_status_t wtconv_bwd(const wtconv_desc_t* d, const void* x, const void* dy
     const SharedSums ss = shared_sums_bwd(d);
     if (ss.se) {
         // the weight gradient first (it leaves the dy sums), then the data
-        // pass with its coarse step on those sums
-        st = wtconv_bwd_weight(d, x, dy, w_lvl, scale, dw_base, dw_lvl, dscale, ws, ss.data_offset, stream);
-        if (st != WTCONV_OK) return st;
-        const hipError_t err = ss.se->bwd_data_from_sums[d->dtype == WTCONV_BF16 ? 1 : 0](
+        // pass with its coarse step on those sums; the weight gradient's
+        // second stage rides in that coarse step's launch as extra
+        // workgroups (one launch fewer; the same sums in the same order)
+        wtc::FinalizeArgs fin{};
+        hipError_t err = wtc::bwdw_launch_deferred(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level,
+                                                   d->dtype == WTCONV_BF16, x, dy, w_lvl, scale, dw_base, dw_lvl,
+                                                   dscale, ws, (hipStream_t)stream, &fin);
+        if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
+        const size_t scratch = (size_t)4 * fin.L * fin.K * fin.K * sizeof(float);
+        if (fin.C > 0 && scratch > ss.se->coarse_lds_bytes) {
+            // its scratch would not fit the coarse kernel's LDS: launch it on its own
+            err = wtc::launch_finalize(fin, (hipStream_t)stream);
+            if (err != hipSuccess) return WTCONV_ERR_LAUNCH;
+            fin.C = 0;
+        }
+        err = ss.se->bwd_data_from_sums[d->dtype == WTCONV_BF16 ? 1 : 0](
             dy, (const float*)((const char*)ws + ss.sums_offset), w_base, w_lvl, scale, dx,
-            (float*)((char*)ws + ss.data_offset), d->B, d->C, (hipStream_t)stream);
+            (float*)((char*)ws + ss.data_offset), d->B, d->C, (hipStream_t)stream, fin.C > 0 ? &fin : nullptr);
         return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
     }
     // A whole-plane data kernel: the weight gradient first, its second stage

@@ -292,12 +292,14 @@ __global__ __launch_bounds__(P::NT) __attribute__((amdgpu_waves_per_eu(P::WAVES_
     }
 }
 
+// fin: a weight-gradient second stage to run as extra workgroups (its
+// channels after the planes), or null
 template <class P, typename T, bool FLIP, int SHIFT, bool SUMS = false>
 hipError_t launch_coarse(const void* in, const float* wl, const float* sc, float* out, int B, int C,
-                         hipStream_t stream) {
-    const unsigned planes = (unsigned)B * (unsigned)C;
-    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, SHIFT, float, SUMS>), dim3(planes), dim3(P::NT), 0, stream,
-                       (const T*)in, (const float*)nullptr, wl, sc, out, C, planes, FinalizeArgs{});
+                         hipStream_t stream, const FinalizeArgs* fin = nullptr) {
+    const unsigned planes = (unsigned)B * (unsigned)C, extra = fin ? (unsigned)fin->C : 0u;
+    hipLaunchKernelGGL((plane_kernel<P, T, FLIP, SHIFT, float, SUMS>), dim3(planes + extra), dim3(P::NT), 0, stream,
+                       (const T*)in, (const float*)nullptr, wl, sc, out, C, planes, fin ? *fin : FinalizeArgs{});
     return hipGetLastError();
 }
 

@@ -901,7 +901,8 @@ static hipError_t launch_colsplit(const void* in, const float* wb, const float* 
 // split_sums_fn), then the fine pass as usual.
 template <class FP, class CP, typename T, bool COLS>
 static hipError_t launch_split_sums(const void* in, const float* sums, const float* wb, const float* wl,
-                                    const float* sc, void* out, float* ws, int B, int C, hipStream_t stream) {
+                                    const float* sc, void* out, float* ws, int B, int C, hipStream_t stream,
+                                    const FinalizeArgs* fin) {
     constexpr int L0 = FP::L0;
     static_assert(FP::LT > L0, "a coarse pass to feed");
     const unsigned planes = (unsigned)B * (unsigned)C;
@@ -912,7 +913,7 @@ static hipError_t launch_split_sums(const void* in, const float* sums, const flo
         hipLaunchKernelGGL((coltile_taps_kernel<FP, T, true>), dim3(C), dim3(256), 0, stream, wb, wl, sc, taps, C);
     }
     hipError_t err = launch_coarse<CP, float, true, L0, true>(sums, wl + L0 * lvl, sc + (size_t)L0 * C * 4, ws, B, C,
-                                                             stream);
+                                                             stream, fin);
     if (err != hipSuccess) return err;
     if constexpr (COLS)
         hipLaunchKernelGGL((coltile_kernel<FP, T, true>), dim3(planes * FP::NTILE), dim3(FP::NT), 0, stream,
@@ -965,14 +966,16 @@ typedef TilePlan<64, 64, 1, 2, 5, 5, 16, 128, 1, 2> FP_64_L1of2_k55;
      {{launch_split<FPL, CPL, float, false>, launch_split<FPL, CPL, float, true>},            \
       {launch_split<FPL, CPL, bf16_t, false>, launch_split<FPL, CPL, bf16_t, true>}},         \
      split_ws<FPL>,                                                                           \
-     {launch_split_sums<FPL, CPL, float, false>, launch_split_sums<FPL, CPL, bf16_t, false>}}
+     {launch_split_sums<FPL, CPL, float, false>, launch_split_sums<FPL, CPL, bf16_t, false>},  \
+     (CPL::LDS_FLOATS + CPL::WFLOATS) * sizeof(float)}
 
 #define WTC_COLSPLIT_ENTRY(FPL, CPL)                                                           \
     {FPL::H, FPL::W, FPL::LT, FPL::KB, FPL::K, FPL::L0,                                       \
      {{launch_colsplit<FPL, CPL, float, false>, launch_colsplit<FPL, CPL, float, true>},      \
       {launch_colsplit<FPL, CPL, bf16_t, false>, launch_colsplit<FPL, CPL, bf16_t, true>}},   \
      colsplit_ws<FPL>,                                                                         \
-     {launch_split_sums<FPL, CPL, float, true>, launch_split_sums<FPL, CPL, bf16_t, true>}}
+     {launch_split_sums<FPL, CPL, float, true>, launch_split_sums<FPL, CPL, bf16_t, true>},    \
+     (CPL::LDS_FLOATS + CPL::WFLOATS) * sizeof(float)}
 
 static const SplitEntry kSplitEntries[] = {
     WTC_COLSPLIT_ENTRY(CT_256_L2of4_k75, CP_64_L2_k5),
