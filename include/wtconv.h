@@ -186,7 +186,8 @@ wtconv_status_t wtconv_bwd_weight_noalloc(const wtconv_desc_t *desc, const void 
      L = 4 with kernels 7 and 5, and the 64x64 test plans): the weight pass
      runs first and leaves the 2^L0-block sums of dy in the workspace; the
      backward-data pass then takes its coarse levels from those sums instead
-     of reading dy a second time for them;
+     of reading dy a second time for them, and the weight pass's fixed-order
+     second stage runs as extra workgroups of that coarse step's launch;
    - whole-plane data kernels (the stage planes, 128x128, the family of
      planes of 56, 28, 14 and 7 pixels): the weight pass runs first and the
      fixed-order second stage of its reduction runs as extra workgroups of
