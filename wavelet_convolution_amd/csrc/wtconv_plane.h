@@ -468,8 +468,49 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     }
     __syncthreads();
 
+    // the level convolutions: strips of rl(l) rows x 1 column of one band,
+    // into registers; level l's strips on threads T0.. (level 1 with CONC1:
+    // the threads that the base strips leave idle, in P1), else all threads
+    auto level_conv = [&](auto lc, auto& z) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
+        constexpr int T0 = (l == 1 && P::CONC1) ? P::NBL : 0, NTH = NT - T0;
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NPW * NIl, NTH);
+#pragma unroll
+        for (int it = 0; it < MIl; ++it) {
+            const int ia = tid - T0 + it * NTH;
+            if ((T0 == 0 || tid >= T0) && ((NPW * NIl) % NTH == 0 || ia < NPW * NIl)) {
+                int item;
+                float* const Ul = ubase(lc, split(ia, NIl, item));
+                const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
+                const int rs = udiv(rem, LP), j = rem - rs * LP;
+                if (LP == wl || j < wl)
+                    conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z[it]);
+            }
+        }
+    };
+    auto level_store = [&](auto lc, auto& z) {
+        constexpr int l = decltype(lc)::value;
+        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
+        constexpr int T0 = (l == 1 && P::CONC1) ? P::NBL : 0, NTH = NT - T0;
+        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NPW * NIl, NTH);
+#pragma unroll
+        for (int it = 0; it < MIl; ++it) {
+            const int ia = tid - T0 + it * NTH;
+            if ((T0 == 0 || tid >= T0) && ((NPW * NIl) % NTH == 0 || ia < NPW * NIl)) {
+                int item;
+                float* const Ul = ubase(lc, split(ia, NIl, item));
+                const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
+                const int rs = udiv(rem, LP), j = rem - rs * LP;
+                if (!(LP == wl || j < wl)) continue;
+#pragma unroll
+                for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = z[it][o];
+            }
+        }
+    };
     // ---------------------------------------------------------------- P1
     float yb[MB][RB];
+    float z1[cdiv(NPW * P::nil(1), P::CONC1 ? NT - P::NBL : NT)][P::rl(1)];
 #pragma unroll
     for (int it = 0; it < MB; ++it) {
         const int item = tid + it * NT;
@@ -481,6 +522,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             if (LPB == W || w < W) conv_col<KB, RB, SX>(X0 + (rb * RB) * SX + w, WB, yb[it]);
         }
     }
+    if constexpr (P::CONC1) level_conv(std::integral_constant<int, 1>{}, z1);
     __syncthreads();
 
     // ---------------------------------------------------------------- P2
@@ -510,42 +552,6 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     });
 
     // ---------------------------------------------------------------- P3
-    // every level: strips of rl(l) rows x 1 column of one band, into registers
-    auto level_conv = [&](auto lc, auto& z) {
-        constexpr int l = decltype(lc)::value;
-        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
-        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NPW * NIl, NT);
-#pragma unroll
-        for (int it = 0; it < MIl; ++it) {
-            const int ia = tid + it * NT;
-            if ((NPW * NIl) % NT == 0 || ia < NPW * NIl) {
-                int item;
-                float* const Ul = ubase(lc, split(ia, NIl, item));
-                const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
-                const int rs = udiv(rem, LP), j = rem - rs * LP;
-                if (LP == wl || j < wl)
-                    conv_col<K, R, Sl>(Ul + s * BSl + (rs * R) * Sl + j, WL + ((l - 1) * 4 + s) * K2P, z[it]);
-            }
-        }
-    };
-    auto level_store = [&](auto lc, auto& z) {
-        constexpr int l = decltype(lc)::value;
-        constexpr int hl = H >> l, wl = W >> l, Sl = P::su(l), BSl = P::bandsz(l), R = P::rl(l);
-        constexpr int NS = hl / R, LP = P::lpl(l), NIl = P::nil(l), MIl = cdiv(NPW * NIl, NT);
-#pragma unroll
-        for (int it = 0; it < MIl; ++it) {
-            const int ia = tid + it * NT;
-            if ((NPW * NIl) % NT == 0 || ia < NPW * NIl) {
-                int item;
-                float* const Ul = ubase(lc, split(ia, NIl, item));
-                const int s = udiv(item, NS * LP), rem = item - s * (NS * LP);
-                const int rs = udiv(rem, LP), j = rem - rs * LP;
-                if (!(LP == wl || j < wl)) continue;
-#pragma unroll
-                for (int o = 0; o < R; ++o) Ul[s * BSl + (PK + rs * R + o) * Sl + PK + j] = z[it][o];
-            }
-        }
-    };
     // one level-2..L strip per thread when they all fit (fewer live registers)
     auto deep_conv = [&](auto lc, float (&zd)[P::RLD]) {
         constexpr int l = decltype(lc)::value;
@@ -581,9 +587,9 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             }
         }
     };
-    // results of all levels stay in registers across one barrier
-    float z1[cdiv(NPW * P::nil(1), NT)][P::rl(1)];
-    level_conv(std::integral_constant<int, 1>{}, z1);
+    // results of all levels stay in registers across one barrier (with
+    // CONC1, level 1's were made in P1, and P1's barrier is that barrier)
+    if constexpr (!P::CONC1) level_conv(std::integral_constant<int, 1>{}, z1);
     if constexpr (P::DSHARE) {
         float zd[P::RLD];
         P::for_deep_levels([&](auto lc) { deep_conv(lc, zd); });
@@ -599,7 +605,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         if constexpr (L >= 3) level_conv(std::integral_constant<int, 3>{}, z3);
         if constexpr (L >= 4) level_conv(std::integral_constant<int, 4>{}, z4);
         if constexpr (L >= 5) level_conv(std::integral_constant<int, 5>{}, z5);
-        __syncthreads();
+        if constexpr (!P::CONC1) __syncthreads();
         level_store(std::integral_constant<int, 1>{}, z1);
         if constexpr (L >= 2) level_store(std::integral_constant<int, 2>{}, z2);
         if constexpr (L >= 3) level_store(std::integral_constant<int, 3>{}, z3);

@@ -280,14 +280,33 @@ struct ColPlan {
     static constexpr int lpl(int l) { return lay(l).lp; }
     static constexpr int nil(int l) { return 4 * ((H >> l) / rl(l)) * lpl(l); }
     // levels 2..L share one register strip per thread when all their strip
-    // slots fit the workgroup: level l takes threads [doff(l), doff(l) + nil(l))
-    static constexpr int doff(int l) {
+    // slots fit the workgroup: level l takes threads [doff(l), doff(l) + nil(l)),
+    // from the first whole wavefront after level 1's strips when one round
+    // of those leaves room for them all (the deep strips then fall on
+    // wavefronts that level 1 leaves idle), else from thread 0
+    static constexpr int ddeep(int l) {
         int o = 0;
         for (int q = 2; q < l; ++q) o += NPW * nil(q);
         return o;
     }
+    static constexpr int DBASE =
+        (NPW * nil(1) <= NT && round_up(NPW * nil(1), 64) + ddeep(L + 1) <= NT) ? round_up(NPW * nil(1), 64) : 0;
+    static constexpr int doff(int l) { return DBASE + ddeep(l); }
     static constexpr bool DSHARE = L >= 2 && doff(L + 1) <= NT;
     static constexpr int RLD = L >= 2 ? rl(2) : 1;
+    // Level 1 beside the base convolution. With one level nothing overwrites
+    // x before the synthesis, so when one round of base strips leaves whole
+    // wavefronts idle (threads from NBL on), the level-1 strips run there in
+    // the same phase, if that shortens the busiest wavefront's multiply-adds
+    // (14x14: 350 on every wavefront instead of 525 on the base ones and 175
+    // on the others).
+    static constexpr int NBL = round_up(NPW * NIB, 64);
+    static constexpr int conc1_cost() {
+        const int base = RB * KB * KB, lv = cdiv(NPW * nil(1), NT - NBL) * rl(1) * K * K;
+        return base > lv ? base : lv;
+    }
+    static constexpr bool CONC1 = L == 1 && MB == 1 && NT - NBL >= 64 &&
+                                  conc1_cost() < RB * KB * KB + cdiv(NPW * nil(1), NT) * rl(1) * K * K;
     // occupancy the LDS footprint allows, at most WMAX waves per SIMD (a
     // plan whose registers need more than 512 / WMAX lowers WMAX)
     // planes of a workgroup lie PL floats apart: a multiple of 4 (128-bit
