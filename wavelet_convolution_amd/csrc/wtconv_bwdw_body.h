@@ -322,6 +322,43 @@ struct BwPlan {
     static constexpr int LPB = BASE_PAIR ? pair_lanes(W, KB) : strip_lanes(W);
     static constexpr int NI = (H / RB) * LPB;
     static constexpr int TAPS = KB * KB + 4 * L * K * K;
+    // Order of the one-column base strips over the lanes: plane-major
+    // (strip s = plane s / (H/RB), row block s % (H/RB)), or row-block-major
+    // with the planes of each group of four taken 0, 2, 1, 3, so that the
+    // strips sharing a 32-lane LDS pass come from planes two apart rather
+    // than from neighbouring row blocks of one plane (14x14: row blocks 7 x 20
+    // floats apart share two banks, planes two pitches apart none). The
+    // order with fewer bank conflicts on the x rows is taken.
+    template <typename T>
+    static constexpr int base_conflicts(bool rbmajor) {
+        const int ps = pstride<T>(), n = NPB * NI;
+        int cost = 0;
+        for (int h0 = 0; h0 < n; h0 += 32) {
+            int cnt[32] = {};
+            int worst = 0;
+            for (int t = h0; t < h0 + 32 && t < n; ++t) {
+                int pl, rb;
+                const int w = t % LPB;
+                if (rbmajor) {
+                    const int st = t / LPB, q = st % NPB;
+                    rb = st / NPB;
+                    pl = (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1);
+                } else {
+                    pl = t / NI;
+                    rb = (t - pl * NI) / LPB;
+                }
+                if (w >= W) continue;
+                const int b = (pl * ps + rb * RB * SX + w) % 32;
+                if (++cnt[b] > worst) worst = cnt[b];
+            }
+            cost += worst;
+        }
+        return cost;
+    }
+    template <typename T>
+    static constexpr bool base_rbmajor() {
+        return !BASE_PAIR && !COARSE && NPB % 4 == 0 && base_conflicts<T>(true) < base_conflicts<T>(false);
+    }
     // Analysis lanes: each owns 2 rows x CW columns of x and dy. The lanes
     // of one 2^L x 2^L block form a group of GS = BR x BC (BR row pairs,
     // BC column slices, row pair fastest) inside one wavefront.
@@ -565,7 +602,15 @@ __device__ __forceinline__ void bwdw_body(const T* __restrict__ x, const T* __re
                 }
             } else {
                 for (int item = gtid; item < NPB * NI; item += 256) {
-                    const int pl = item / NI, r = item - pl * NI;
+                    int pl, r;
+                    if constexpr (P::template base_rbmajor<T>()) {
+                        const int st = item / LPB, rbs = st / NPB, q = st - rbs * NPB;
+                        pl = (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1);
+                        r = rbs * LPB + (item - st * LPB);
+                    } else {
+                        pl = item / NI;
+                        r = item - pl * NI;
+                    }
                     const int rb = r / LPB, w = r - rb * LPB, h0 = rb * RB;
                     if (LPB == W || w < W)
                         taps_col<KB, RB, SX, SD>(Xp(pl) + XO - PB + h0 * SX + w, DYp(pl) + h0 * SD + w, acc0);
