@@ -410,7 +410,15 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         // by the border).
         constexpr bool ZF = P::ZFILL;
         constexpr int CPI = P::CPI, VA = P::VA;
-        constexpr int NQ = ZF ? P::NQI : P::NQ, IPR = ZF ? P::IPRI : P::IPR;
+        // QPOW2: items on the power-of-two grid, NQ cells per plane of IPR
+        // per row, the cells past the plane's rows or items idle
+        constexpr bool QP = P::QPOW2;
+        constexpr int NQ = QP ? P::NQP : ZF ? P::NQI : P::NQ, IPR = QP ? P::IPRP : ZF ? P::IPRI : P::IPR;
+        auto cell = [&](int q, int& ri, int& uq) {
+            ri = udiv(q, IPR);
+            uq = q - ri * IPR;
+            return !QP || (ri < H1 && uq < P::IPRI);
+        };
         constexpr int R0 = ZF ? PK : 0, U0 = ZF ? PK / CPI : 0;
         constexpr int NQA = NPW * NQ, MQ = cdiv(NQA, NT);
         if constexpr (ZF) {
@@ -425,8 +433,10 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             const int qa = tid + k * NT;
             int q;
             const int p = split(qa < NQA ? qa : 0, NQ, q);
-            const int ri = udiv(q, IPR), ii = ri + R0, uu = q - ri * IPR + U0, i = ii - PK, j0 = uu * CPI - PK;
-            const bool inside = (NQA % NT == 0 || qa < NQA) && live(p) &&
+            int ri, uq;
+            const bool real = cell(q, ri, uq);
+            const int ii = ri + R0, uu = uq + U0, i = ii - PK, j0 = uu * CPI - PK;
+            const bool inside = (NQA % NT == 0 || qa < NQA) && live(p) && real &&
                                 (ZF || (i >= 0 && i < H1 && j0 >= 0 && j0 < W1));
             // every lane loads (border items the plane's first words) and
             // then selects zeros: no branch, so the registers stay registers
@@ -448,7 +458,9 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             const int p = split(qa, NQ, q);
             float* const A = Ap(p);
             float* const Bq = A + P::ASIZE;
-            const int ri = udiv(q, IPR), ii = ri + R0, uu = q - ri * IPR + U0, i = ii - PK, j0 = uu * CPI - PK;
+            int ri, uq;
+            if (!cell(q, ri, uq)) continue;
+            const int ii = ri + R0, uu = uq + U0, i = ii - PK, j0 = uu * CPI - PK;
             float f0[VA], f1[VA];
             widen_raw<T, VA>(r0[k], f0);
             widen_raw<T, VA>(r1[k], f1);

@@ -258,6 +258,13 @@ struct ColPlan {
     static constexpr int IPRI = (W >> 1) / CPI;
     static constexpr int NQI = (H >> 1) * IPRI;
     static constexpr bool ZFILL = cdiv(NPW * NQI, NT) < cdiv(NPW * NQ, NT) && NQ >= 2 * NQI;
+    // Interior items on a power-of-two grid (pow2(H/2) rows of pow2(IPRI)
+    // items per plane, the extra cells idle) where that takes no more
+    // rounds per thread: plane, row and item then come from shifts and
+    // masks instead of divisions by constants (14x14: 8 x 8 cells for 7 x 7
+    // items, 512 of them on 256 threads as 392 were)
+    static constexpr int IPRP = strip_lanes(IPRI < 32 ? IPRI : 32), NQP = strip_lanes((H >> 1) < 32 ? H >> 1 : 32) * IPRP;
+    static constexpr bool QPOW2 = ZFILL && IPRI <= 32 && (H >> 1) <= 32 && cdiv(NPW * NQP, NT) == cdiv(NPW * NQI, NT);
     static_assert((W >> 1) % CPI == 0, "interior items tile the level-1 rows");
     static_assert(VL % 2 == 0, "rows of whole Haar blocks");
     static_assert(PK % CPI == 0 && (XO - 2 * PK) % VA == 0 && PB <= 2 * PK && XO + W + 2 * PK >= SX,
