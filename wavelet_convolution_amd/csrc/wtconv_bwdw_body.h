@@ -427,11 +427,21 @@ __device__ __forceinline__ void bwdw_body(const T* __restrict__ x, const T* __re
     const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
 
     // borders stay zero for the whole chunk: nothing writes them
-    for (int p = 0; p < NPB; ++p) {
-        if constexpr (!P::COARSE) zero_border<1, H, W, PB, SX, XO>(Xp(p), tid, NT);
+    if constexpr (NPB > 1) {
+        // several planes per step: their whole regions cleared with a few
+        // 128-bit stores per thread (a border loop per plane and band costs
+        // more: 14x14, eight planes, about a fifth of the multiply-adds);
+        // the barrier keeps these stores ahead of the first stream-in
+        constexpr int NZ = NPB * PS;
+        float4* const z = reinterpret_cast<float4*>(lds);
+        for (int t = tid; t < NZ / 4; t += NT) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < NZ % 4) lds[NZ / 4 * 4 + tid] = 0.f;
+        __syncthreads();
+    } else {
+        if constexpr (!P::COARSE) zero_border<1, H, W, PB, SX, XO>(Xp(0), tid, NT);
         P::for_levels([&](auto lc) {
             constexpr int l = decltype(lc)::value;
-            zero_border<4, (H >> l), (W >> l), PK, P::su(l)>(Up(p) + P::uoff(l), tid, NT);
+            zero_border<4, (H >> l), (W >> l), PK, P::su(l)>(Up(0) + P::uoff(l), tid, NT);
         });
     }
 
