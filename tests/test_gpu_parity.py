@@ -366,28 +366,44 @@ def test_level_zero_fused_kernels(shape):
                                    (2, 2, 56, 56, 2, 7, 3), (3, 2, 7, 7, 2, 5, 7),
                                    # split planes: the data pass's coarse step reads the weight pass's dy sums
                                    (2, 3, 64, 64, 4, 3, 3), (3, 2, 64, 64, 2, 5, 5), (1, 2, 256, 256, 4, 7, 5),
-                                   (3, 5, 256, 256, 4, 7, 5)],
+                                   (3, 5, 256, 256, 4, 7, 5),
+                                   # one-level single pass (14x14, 5x5): one image per chunk with three
+                                   # idle planes per step; chunks of several steps, the last one partial
+                                   (30, 200, 14, 14, 1, 5, 5), (64, 384, 14, 14, 1, 5, 5)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_whole_backward_equals_the_two_calls(shape):
-    """wtconv_bwd (a single pass over x and dy at L = 0 on planned planes;
-    on split planes the weight pass first and the data pass's coarse step on
-    its dy sums; on whole planes the weight pass first and its second stage
-    in the data kernel's launch; the two calls elsewhere) equals
-    wtconv_bwd_data + wtconv_bwd_weight bit for bit, and the oracle within
-    the bars."""
+    """wtconv_bwd (a single pass over x and dy at L = 0 on planned planes
+    and at L = 1 on the 14x14 plane with 5x5 kernels; on split planes the
+    weight pass first and the data pass's coarse step on its dy sums; on
+    whole planes the weight pass first and its second stage in the data
+    kernel's launch; the two calls elsewhere) equals wtconv_bwd_data +
+    wtconv_bwd_weight bit for bit, except that the one-level single pass
+    groups the tap products differently (its weight gradients agree with
+    the two calls to fp32 rounding, its dx bit for bit); every form matches
+    the oracle within the bars and repeats bit for bit."""
     _say(f"[parity] whole backward {shape}")
     kb = shape[5]
+    one_level_pass = shape[2:] == (14, 14, 1, 5, 5)
     for dtype in ("f32", "bf16"):
         inp = make_inputs(*shape, dtype=dtype, seed=43)
         x, dy, wb, wl, sc = to_device(inp)
         dx, (dwb, dwl, dsc) = wt.wtconv_bwd(x, dy, wb, wl, sc)
         dx2 = wt.wtconv_bwd_data(dy, wb, wl, sc)
         dwb2, dwl2, dsc2 = wt.wtconv_bwd_weight(x, dy, kb, wl, sc)
+        dx3, (dwb3, dwl3, dsc3) = wt.wtconv_bwd(x, dy, wb, wl, sc)
         torch.cuda.synchronize()
-        for a, b in ((dx, dx2), (dwb, dwb2), (dwl, dwl2), (dsc, dsc2)):
-            assert torch.equal(a, b)
-        _, odx, (odwb, _, _) = _oracle_all(inp)
+        assert torch.equal(dx, dx2)
+        for a, b, c in ((dwb, dwb2, dwb3), (dwl, dwl2, dwl3), (dsc, dsc2, dsc3)):
+            assert torch.equal(a, c)   # deterministic
+            if one_level_pass:
+                assert rel_err(to_f64(a), to_f64(b)) <= 1e-5
+            else:
+                assert torch.equal(a, b)
+        assert torch.equal(dx, dx3)
+        _, odx, (odwb, odwl, odsc) = _oracle_all(inp)
         assert rel_err(to_f64(dx), odx) <= TOL[dtype] and rel_err(to_f64(dwb), odwb) <= TOL["f32"]
+        if shape[4] > 0:
+            assert rel_err(to_f64(dwl), odwl) <= TOL["f32"] and rel_err(to_f64(dsc), odsc) <= TOL["f32"]
 
 
 def test_empty_batch():

@@ -10,6 +10,7 @@
 
 #include "../../include/wtconv.h"
 #include "wtconv_plans.h"
+#include "wtconv_bwd1.h"
 #include "wtconv_bwdw.h"
 #include "wtconv_dw.h"
 #include "wtconv_layout.h"
@@ -162,10 +163,16 @@ wtconv_status_t fused_data_pass(const wtconv_desc_t* d, const void* in, const fl
     return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
 }
 
-// The single-pass backward kernel covers this shape (planar, non-empty).
+// Workspace of the single-pass backward kernel for this shape (L = 0: the
+// depthwise one; L = 1: the one-level whole-plane one), or (size_t)-1.
+size_t single_pass_ws(const wtconv_desc_t* d) {
+    if (d->levels == 0) return wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, 0, d->k_base);
+    return wtc::bwd1_level_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level);
+}
+
+// A single-pass backward kernel covers this shape (planar, non-empty).
 bool single_pass_bwd(const wtconv_desc_t* d) {
-    return d->B > 0 && d->layout == WTCONV_NCHW &&
-           wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base) != (size_t)-1;
+    return d->B > 0 && d->layout == WTCONV_NCHW && single_pass_ws(d) != (size_t)-1;
 }
 
 // Shared-sums backward of a split plane: the weight-gradient plan leaves the
@@ -195,8 +202,7 @@ SharedSums shared_sums_bwd(const wtconv_desc_t* d) {
 // Workspace of wtconv_bwd: the single-pass kernel's, the shared-sums pair's,
 // else enough for the two backward calls run one after the other on it.
 size_t bwd_workspace(const wtconv_desc_t* d) {
-    if (single_pass_bwd(d))
-        return wtc::bwd_single_pass_workspace_bytes(d->B, d->C, d->H, d->W, d->levels, d->k_base);
+    if (single_pass_bwd(d)) return single_pass_ws(d);
     const SharedSums ss = shared_sums_bwd(d);
     if (ss.se) return ss.need;
     const size_t a = route(d, WTCONV_OP_BWD_DATA).need, b = route(d, WTCONV_OP_BWD_WEIGHT).need;
@@ -337,9 +343,13 @@ wtconv_status_t wtconv_bwd(const wtconv_desc_t* d, const void* x, const void* dy
     const size_t need = bwd_workspace(d);
     if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return WTCONV_ERR_WORKSPACE;
     if (single_pass_bwd(d)) {
-        const hipError_t err = wtc::bwd_single_pass_launch(d->B, d->C, d->H, d->W, d->k_base,
-                                                           d->dtype == WTCONV_BF16, x, dy, w_base, dx, dw_base,
-                                                           ws, (hipStream_t)stream);
+        const bool bf16 = d->dtype == WTCONV_BF16;
+        const hipError_t err =
+            d->levels == 0
+                ? wtc::bwd_single_pass_launch(d->B, d->C, d->H, d->W, d->k_base, bf16, x, dy, w_base, dx, dw_base, ws,
+                                              (hipStream_t)stream)
+                : wtc::bwd1_level_launch(d->B, d->C, d->H, d->W, d->levels, d->k_base, d->k_level, bf16, x, dy,
+                                         w_base, w_lvl, scale, dx, dw_base, dw_lvl, dscale, ws, (hipStream_t)stream);
         return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_LAUNCH;
     }
     const SharedSums ss = shared_sums_bwd(d);
