@@ -177,11 +177,18 @@ wtconv_status_t wtconv_bwd_weight_noalloc(const wtconv_desc_t *desc, const void 
 
 /* Whole backward pass: dx (as wtconv_bwd_data) and the weight gradients (as
    wtconv_bwd_weight) in one call. Results equal those of the two calls bit
-   for bit (the same multiply-adds in the same order); what the call saves
-   depends on the shape (planar layout in each case):
+   for bit (the same multiply-adds in the same order), except where noted
+   for the one-level single pass; what the call saves depends on the shape
+   (planar layout in each case):
    - L = 0 on the planes its kernel covers (56x56, 28x28, 14x14; k_base 5 or
      7): a single pass that reads x and dy once, the fused backward the I/O
      model counts at 5*N*e instead of 6*N*e bytes per step;
+   - L = 1 on 14x14 planes with 5x5 kernels: a single pass that reads x and
+     dy once and computes dx and every weight gradient's partial sums in one
+     kernel (then the weight gradient's fixed-order second stage); dx equals
+     the two calls' bit for bit, the weight gradients group their products
+     differently and agree with the two calls' to fp32 rounding (both are
+     deterministic);
    - planes split into fine tiles and a coarse level-L0 image (256x256 at
      L = 4 with kernels 7 and 5, and the 64x64 test plans): the weight pass
      runs first and leaves the 2^L0-block sums of dy in the workspace; the
