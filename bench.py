@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "WTConv fwd+bwd images/sec and achieved HBM TB/s (% of MI355X peak)"
 KERNEL_SOURCES = ("wtconv_device.h", "wtconv_plans.h", "wtconv_plane.h", "wtconv_fused.hip", "wtconv_tiled.h",
                   "wtconv_tiled.hip", "wtconv_bwdw.h", "wtconv_bwdw.hip", "wtconv_bwdw_body.h", "wtconv_dw.h",
-                  "wtconv_dw.hip", "wtconv_api.hip")
+                  "wtconv_dw.hip", "wtconv_api.hip", "wtconv_bwd1.h", "wtconv_bwd1.hip", "wtconv_family.h")
 # rotated inputs must exceed twice the 256 MB MALL
 ROTATION_BYTES = 512 << 20
 # default warm-up before the timed steps
