@@ -112,6 +112,28 @@ typedef struct {
    must be 256-byte aligned. */
 size_t wtconv_workspace_size(const wtconv_desc_t *desc, int32_t op);
 
+/* How a call of `op` (wtconv_op_t) runs for `desc`, so that a caller can
+   tell a shape the fused kernels cover from one that takes the generic
+   chain (same results, many times slower):
+   - WTCONV_ROUTE_GENERIC: the one-kernel-per-step chain (no fused kernel
+     for this shape, or an empty batch, for which nothing is launched but
+     the zeroing of the weight gradients);
+   - WTCONV_ROUTE_FUSED: fused kernels on the activations as they are;
+   - WTCONV_ROUTE_FUSED_COPIES: fused kernels on planar copies of
+     channels-last activations in the workspace;
+   - WTCONV_ROUTE_SINGLE_PASS (WTCONV_OP_BWD only): one kernel reads x and
+     dy once for dx and every weight gradient.
+   For WTCONV_OP_BWD a shape reports FUSED (or FUSED_COPIES) when both of
+   its backward passes are fused, else GENERIC. Returns -1 if the
+   descriptor or op is invalid. No device call is made. */
+typedef enum {
+    WTCONV_ROUTE_GENERIC = 0,
+    WTCONV_ROUTE_FUSED = 1,
+    WTCONV_ROUTE_FUSED_COPIES = 2,
+    WTCONV_ROUTE_SINGLE_PASS = 3
+} wtconv_route_t;
+int32_t wtconv_route(const wtconv_desc_t *desc, int32_t op);
+
 /* Forward: y = WTConv(x). One fused pass: reads x once, writes y once.
    Workspace: wtconv_workspace_size(desc, WTCONV_OP_FWD) bytes (0 for planes
    that fit one workgroup's LDS; ws may then be NULL).

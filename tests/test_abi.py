@@ -246,3 +246,28 @@ def test_whole_backward_workspace(lib):
     # dx overlapping dy is refused before anything launches
     assert lib.wtconv_bwd(ctypes.byref(d), ok, ctypes.c_void_p(1 << 24), ok, ok, ok, ctypes.c_void_p(1 << 24), ok,
                           ok, ok, ctypes.c_void_p(1 << 28), 1 << 30, None) == 1
+
+
+def test_route_query(lib):
+    """wtconv_route tells the fused routes from the generic chain without a
+    device call: the bench workloads are fused (one kernel for the whole
+    backward at 14x14, L = 1 and at L = 0), channels-last calls of planned
+    shapes run the fused kernels on planar copies, an unplanned shape takes
+    the generic chain, and an invalid descriptor or op reports -1."""
+    from wavelet_convolution_amd.binding import WTConvDesc
+    from wavelet_convolution_amd.configs import CONFIGS
+    for cfg in CONFIGS.values():
+        d = WTConvDesc(cfg.B, cfg.C, cfg.H, cfg.W, cfg.L, cfg.kb, cfg.k, 1 if cfg.dtype == "bf16" else 0, 0)
+        routes = [lib.wtconv_route(ctypes.byref(d), op) for op in (0, 1, 2, 3)]
+        single = cfg.L == 0 or (cfg.H, cfg.W, cfg.L, cfg.kb, cfg.k) == (14, 14, 1, 5, 5)
+        assert routes == [1, 1, 1, 3 if single else 1], (cfg.name, routes)
+    d = WTConvDesc(64, 96, 56, 56, 3, 5, 5, 1, 1)   # channels last
+    assert [lib.wtconv_route(ctypes.byref(d), op) for op in (0, 1, 2, 3)] == [2, 2, 2, 2]
+    d = WTConvDesc(2, 3, 30, 30, 2, 5, 5, 1, 0)     # no fused kernel for 30x30
+    assert [lib.wtconv_route(ctypes.byref(d), op) for op in (0, 1, 2, 3)] == [0, 0, 0, 0]
+    d = WTConvDesc(0, 3, 56, 56, 3, 5, 5, 1, 0)     # empty batch
+    assert lib.wtconv_route(ctypes.byref(d), 3) == 0
+    d = WTConvDesc(2, 3, 56, 56, 3, 4, 5, 1, 0)     # even kernel: invalid
+    assert lib.wtconv_route(ctypes.byref(d), 0) == -1
+    d = WTConvDesc(2, 3, 56, 56, 3, 5, 5, 1, 0)
+    assert lib.wtconv_route(ctypes.byref(d), 7) == -1

@@ -40,6 +40,12 @@ def test_family_routes_to_fused_kernels(lib, member):
         fused = lib.wtconv_workspace_size(ctypes.byref(d), 2)
         naive = lib.wtconv_naive_workspace_size(ctypes.byref(d), 2)
         assert 0 < fused < naive, (member, dtype, fused, naive)
+        # the route query says the same: fused data passes and weight
+        # gradient; the whole backward fused (one kernel for one-level 14x14
+        # planes with 5x5 kernels)
+        routes = [lib.wtconv_route(ctypes.byref(d), op) for op in (0, 1, 2, 3)]
+        single = (h, L, kb, k) == (14, 1, 5, 5)
+        assert routes == [1, 1, 1, 3 if single else 1], (member, dtype, routes)
 
 
 torch = pytest.importorskip("torch")

@@ -54,6 +54,8 @@ def load_library() -> ctypes.CDLL:
             lib = ctypes.CDLL(_LIB_PATH)
             lib.wtconv_workspace_size.argtypes = [_P, ctypes.c_int32]
             lib.wtconv_workspace_size.restype = _SZ
+            lib.wtconv_route.argtypes = [_P, ctypes.c_int32]
+            lib.wtconv_route.restype = ctypes.c_int32
             lib.wtconv_naive_workspace_size.argtypes = [_P, ctypes.c_int32]
             lib.wtconv_naive_workspace_size.restype = _SZ
             for name in ("wtconv_fwd", "wtconv_bwd_data", "wtconv_naive_fwd", "wtconv_naive_bwd_data"):
@@ -174,6 +176,23 @@ def wtconv_workspace_size(act: torch.Tensor, levels: int, k_base: int, k_level: 
     if n == ctypes.c_size_t(-1).value:
         raise WTConvError(2, wtconv_status_string(2))
     return int(n)
+
+
+ROUTES = {0: "generic", 1: "fused", 2: "fused_copies", 3: "single_pass"}
+
+
+def wtconv_route(act: torch.Tensor, levels: int, k_base: int, k_level: int, op: int) -> str:
+    """How the library runs `op` for this activation tensor's shape, dtype
+    and layout: "generic" (the one-kernel-per-step chain), "fused",
+    "fused_copies" (fused kernels on planar copies of channels-last
+    activations) or "single_pass" (wtconv_bwd: one kernel for dx and every
+    weight gradient). Makes no device call."""
+    lib = load_library()
+    d = _desc(act, levels, k_base, k_level)
+    r = lib.wtconv_route(ctypes.byref(d), int(op))
+    if r < 0:
+        raise WTConvError(2, wtconv_status_string(2))
+    return ROUTES[r]
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor | None:

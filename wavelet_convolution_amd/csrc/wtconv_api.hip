@@ -298,6 +298,22 @@ size_t wtconv_workspace_size(const wtconv_desc_t* d, int32_t op) {
     return route(d, op).need;
 }
 
+int32_t wtconv_route(const wtconv_desc_t* d, int32_t op) {
+    if (check_desc(d) != WTCONV_OK) return -1;
+    if (op != WTCONV_OP_FWD && op != WTCONV_OP_BWD_DATA && op != WTCONV_OP_BWD_WEIGHT && op != WTCONV_OP_BWD)
+        return -1;
+    if (op == WTCONV_OP_BWD && single_pass_bwd(d)) return WTCONV_ROUTE_SINGLE_PASS;
+    auto one = [&](int o) -> int32_t {
+        const Route r = route(d, o);
+        const bool fused = o == WTCONV_OP_BWD_WEIGHT ? r.bw : (r.de || r.pe || r.se);
+        if (!fused) return WTCONV_ROUTE_GENERIC;
+        return r.copies ? WTCONV_ROUTE_FUSED_COPIES : WTCONV_ROUTE_FUSED;
+    };
+    if (op != WTCONV_OP_BWD) return one(op);
+    const int32_t a = one(WTCONV_OP_BWD_DATA), b = one(WTCONV_OP_BWD_WEIGHT);
+    return (a == WTCONV_ROUTE_GENERIC || b == WTCONV_ROUTE_GENERIC) ? (int32_t)WTCONV_ROUTE_GENERIC : a;
+}
+
 wtconv_status_t wtconv_fwd(const wtconv_desc_t* d, const void* x, const float* w_base,
                            const float* w_lvl, const float* scale, void* y, void* ws,
                            size_t ws_bytes, void* stream) {
