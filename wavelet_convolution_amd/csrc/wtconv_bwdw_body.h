@@ -236,14 +236,59 @@ struct BwPlan {
     static constexpr int XSIZE = COARSE ? 0 : (H + 2 * PB) * SX;
     static constexpr int SD = round_up(W, 4);
     static constexpr int DSIZE = COARSE ? 0 : H * SD;
+    static constexpr int band_rows(int l) {
+        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K, NPB) : pick_rows(H >> l, W >> l, 64, K, NPB);
+    }
     // band rows: even strides where column pairs are read (8-byte aligned
     // pairs), odd ones elsewhere (the analysis stores of lanes on
-    // consecutive rows then fall into different banks)
-    static constexpr int su(int l) {
-        return level_pair(l) ? round_up((W >> l) + 2 * PK, 2) : odd_stride((W >> l) + 2 * PK);
+    // consecutive rows then fall into different banks). Where one 32-lane
+    // pass of the one-column level strips holds several row strips of one
+    // plane (28x28: level 1 in two 7-row strips), the stride is the first
+    // from there with the fewest bank conflicts between them (28x28: 19
+    // floats put the second strip 5 banks on, over 9 of the first strip's
+    // 14; 25 put it 15 on, clear of them).
+    static constexpr int row_conflicts(int l, int S) {
+        const int hl = H >> l, wl = W >> l, R = band_rows(l), LP = strip_lanes(wl), NI = (hl / R) * LP;
+        // lanes of one plane only (planes are placed apart by best_pitch)
+        int cost = 0;
+        for (int h0 = 0; h0 < NPB * NI; h0 += 32) {
+            int worst = 0;
+            for (int pl = 0; pl < NPB; ++pl) {
+                int cnt[32] = {};
+                for (int t = h0; t < h0 + 32 && t < NPB * NI; ++t) {
+                    const int tp = t / NI, r = t - tp * NI, rs = r / LP, j = r - rs * LP;
+                    if (tp != pl || j >= wl) continue;
+                    const int b = (rs * R * S + j) % 32;
+                    if (++cnt[b] > worst) worst = cnt[b];
+                }
+            }
+            cost += worst;
+        }
+        return cost;
     }
+    static constexpr int level_stride(int l, int base) {
+        if (level_pair(l) || l > L) return base;
+        int best = base, best_cost = row_conflicts(l, base);
+        for (int S = base + 2; S < base + 32; S += 2)
+            if (row_conflicts(l, S) < best_cost) {
+                best_cost = row_conflicts(l, S);
+                best = S;
+            }
+        return best;
+    }
+    static constexpr int su_calc(int l) {
+        return l > L ? 1
+                     : level_pair(l) ? round_up((W >> l) + 2 * PK, 2) : level_stride(l, odd_stride((W >> l) + 2 * PK));
+    }
+    static constexpr int sv_calc(int l) {
+        return l > L ? 1 : level_pair(l) ? round_up(W >> l, 2) : level_stride(l, odd_stride(W >> l));
+    }
+    // computed once per plan (each is a search)
+    static constexpr int SU[6] = {1, su_calc(1), su_calc(2), su_calc(3), su_calc(4), su_calc(5)};
+    static constexpr int SV[6] = {1, sv_calc(1), sv_calc(2), sv_calc(3), sv_calc(4), sv_calc(5)};
+    static constexpr int su(int l) { return SU[l]; }
     static constexpr int bandsz(int l) { return ((H >> l) + 2 * PK) * su(l); }
-    static constexpr int sv(int l) { return level_pair(l) ? round_up(W >> l, 2) : odd_stride(W >> l); }
+    static constexpr int sv(int l) { return SV[l]; }
     static constexpr int vsz(int l) { return (H >> l) * sv(l); }
     static constexpr int uoff(int l) {
         int o = 0;
@@ -268,9 +313,6 @@ struct BwPlan {
     // bf16 (only the base taps read it): half the region
     template <typename T>
     static constexpr int dsize() { return sizeof(T) == 2 ? DSIZE / 2 : DSIZE; }
-    static constexpr int band_rows(int l) {
-        return level_pair(l) ? pick_rows2(H >> l, W >> l, 64, K, NPB) : pick_rows(H >> l, W >> l, 64, K, NPB);
-    }
     // Bank conflicts of the level taps of a step at plane pitch ps: the
     // lanes of a pass may hold strips of several planes (narrow bands, NPB
     // planes per step). Cost: over the passes of U and V reads, the largest
