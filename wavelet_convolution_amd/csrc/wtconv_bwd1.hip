@@ -112,9 +112,9 @@ void bwd1_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float*
 
     // One register array serves the role of each wavefront (a wavefront's
     // role never changes): dx's base rows, its two level-1 strips, or the
-    // tap sums that accumulate over the chunk. Separate arrays would all be
-    // live across a step (the compiler cannot tell the roles apart) and
-    // spill at this occupancy.
+    // tap sums that accumulate over the chunk. No two roles share a
+    // wavefront, so they need no registers of their own (separate arrays
+    // spilled at this occupancy).
     static_assert(RB <= Q::KK && 2 * R1 <= Q::KK, "role registers");
     float acc[Q::KK];
 #pragma unroll
