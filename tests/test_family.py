@@ -6,7 +6,8 @@ multiple of 2^L, which is the odd-grid reading of the layer.
 
 CPU: every member is routed to fused kernels (the data passes need no
 workspace, the weight gradient less than the generic chain's). GPU: every
-member's forward, backward data and weight gradients against the oracle."""
+member's forward, backward data and weight gradients against the oracle, by
+the three calls and by the whole backward in one call."""
 import ctypes
 import os
 
@@ -70,13 +71,16 @@ def test_family_matches_oracle(member):
         y = wt.wtconv_fwd(x, wb, wl, sc)
         dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
         gb, gl, gs = wt.wtconv_bwd_weight(x, dy, kb, wl, sc)
+        dx1, (gb1, gl1, gs1) = wt.wtconv_bwd(x, dy, wb, wl, sc)   # the whole backward in one call
         torch.cuda.synchronize()
         xo, dyo = inp.act_f64("x"), inp.act_f64("dy")
         pw = inp.params_f64()
         tol = TOL[dtype]
         assert rel_err(to_f64(y), oracle.fwd(xo, *pw)) <= tol
-        assert rel_err(to_f64(dx), oracle.bwd_data(dyo, *pw)) <= tol
+        odx = oracle.bwd_data(dyo, *pw)
+        assert rel_err(to_f64(dx), odx) <= tol and rel_err(to_f64(dx1), odx) <= tol
         ob, ol, os_ = oracle.bwd_weight(xo, dyo, *pw)
-        assert rel_err(to_f64(gb), ob) <= TOL["f32"]
-        assert rel_err(to_f64(gl), ol) <= TOL["f32"]
-        assert rel_err(to_f64(gs), os_) <= TOL["f32"]
+        for got in ((gb, gl, gs), (gb1, gl1, gs1)):
+            assert rel_err(to_f64(got[0]), ob) <= TOL["f32"]
+            assert rel_err(to_f64(got[1]), ol) <= TOL["f32"]
+            assert rel_err(to_f64(got[2]), os_) <= TOL["f32"]
