@@ -464,6 +464,46 @@ def test_graph_replay_matches_eager(shape):
         (x.float() * 2).sum().item()   # eager work between replays
 
 
+@pytest.mark.parametrize("shape", [(24, 16, 14, 14, 1, 5, 5), (4, 3, 56, 56, 3, 5, 5), (2, 3, 64, 64, 4, 3, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_graph_replay_whole_backward(shape):
+    """wtconv_bwd captured in a HIP graph (the one-level single pass with its
+    second-stage launch, the weight pass with its second stage in the data
+    kernel's launch, the split plane's shared dy sums): every replay, with
+    eager work between replays, equals the eager result bit for bit."""
+    _say(f"[parity] graph replay of the whole backward {shape}")
+    B, C, H, W, L, kb, k = shape
+    inp = make_inputs(*shape, dtype="bf16", seed=29)
+    x, dy, wb, wl, sc = to_device(inp)
+    ws = torch.empty(wt.wtconv_workspace_size(x, L, kb, k, 3) + 256, dtype=torch.uint8, device="cuda")
+    dx = torch.empty_like(x)
+    gr = (torch.empty(C, kb, kb, device="cuda"), torch.empty(tuple(wl.shape), device="cuda"),
+          torch.empty(tuple(sc.shape), device="cuda"))
+
+    def step():
+        wt.wtconv_bwd(x, dy, wb, wl, sc, dx=dx, out=gr, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (dx, *gr)]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in (dx, *gr):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip((dx, *gr), eager):
+            assert torch.equal(t, e), f"replay {r}"
+        (x.float() * 2).sum().item()   # eager work between replays
+
+
 def test_measurement_probes():
     """The copy probe copies exactly; the FMA probe writes finite values to
     every lane's slot; bad arguments are refused before any launch."""

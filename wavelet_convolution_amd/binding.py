@@ -332,8 +332,9 @@ def wtconv_peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
 
 def wtconv_bwd(x, dy, w_base, w_lvl, scale, dx=None, out=None, ws=None, stream=None):
     """(dx, (dW_base, dW_lvl, dscale)) in one call: a single pass over x and
-    dy where the library has one (L = 0 on its planned planes), else the two
-    backward calls on one workspace."""
+    dy where the library has one (L = 0 on its planned planes, L = 1 on
+    14x14 planes with 5x5 kernels), else the library's other fused backward
+    forms or the two backward calls on one workspace."""
     _require_gpu(x, dy=dy, w_base=w_base, w_lvl=w_lvl, scale=scale, dx=dx, out=out, ws=ws)
     lib = load_library()
     levels, kb, k = _dims(w_base, w_lvl)
