@@ -77,21 +77,6 @@ void bwd1_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float*
     const int c = blockIdx.x % C, chunk = blockIdx.x / C;
     const int b0 = chunk * bpc, b1 = min(B, b0 + bpc);
 
-    // the taps as the column kernel stages them for the backward-data pass
-    for (int t = tid; t < KB2P; t += 256)
-        WB[t] = t < KB * KB ? w_base[(size_t)c * KB * KB + (KB * KB - 1 - t)] : 0.f;
-    for (int t = tid; t < 4 * K2P; t += 256) {
-        const int s = t / K2P, tap = t - s * K2P;
-        const size_t pi = (size_t)c * 4 + s;
-        const float f = scale[pi] * (1.0f / 4.0f);
-        WL[t] = tap < K * K ? w_lvl[pi * K * K + (K * K - 1 - tap)] * f : 0.f;
-    }
-    // every plane region cleared once: no step writes a border cell
-    {
-        float4* const z = reinterpret_cast<float4*>(lds);
-        for (int t = tid; t < NPW * PLF / 4; t += 256) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
     // this thread's stream-in cell: plane cp, level-1 position (ci, cj)
     const int cp = tid / NG, ci = (tid % NG) / GC, cj = tid % GC;
     const bool creal = ci < H1 && cj < W1;
@@ -108,7 +93,23 @@ void bwd1_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float*
             for (int i = 0; i < RawVec<T, 2>::N; ++i) vx[0].w[i] = vx[1].w[i] = vd[0].w[i] = vd[1].w[i] = 0u;
         }
     };
+    // The first step's loads go out first, the taps' right after them; the
+    // taps are staged (as the column kernel stages them for the
+    // backward-data pass) once both are in flight, so the two global round
+    // trips overlap. Every plane region is cleared once in between: no step
+    // writes a border cell.
     issue(b0);
+    static_assert(KB * KB <= 256 && 4 * P::K2P <= 256, "one tap of each kind per thread");
+    const float wb = w_base[(size_t)c * KB * KB + (KB * KB - 1 - min(tid, KB * KB - 1))];
+    const int ts = min(tid, 4 * K2P - 1) / K2P, ttap = min(tid, 4 * K2P - 1) - ts * K2P;
+    const float sc = scale[(size_t)c * 4 + ts];
+    const float wl = w_lvl[((size_t)c * 4 + ts) * K * K + (K * K - 1 - min(ttap, K * K - 1))];
+    {
+        float4* const z = reinterpret_cast<float4*>(lds);
+        for (int t = tid; t < NPW * PLF / 4; t += 256) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < KB2P) WB[tid] = tid < KB * KB ? wb : 0.f;
+    if (tid < 4 * K2P) WL[tid] = ttap < K * K ? wl * (sc * (1.0f / 4.0f)) : 0.f;
 
     // One register array serves the role of each wavefront (a wavefront's
     // role never changes): dx's base rows, its two level-1 strips, or the
