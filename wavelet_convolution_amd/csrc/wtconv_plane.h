@@ -328,23 +328,21 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     float* WL = WB + KB2P;
 
     const int tid = threadIdx.x;
-    {
-        const unsigned ndata = (unsigned)cdiv(B, NPW) * (unsigned)C;
-        if (blockIdx.x >= ndata) {   // a deferred second stage of the weight gradient
-            finalize_channel(fin, (int)(blockIdx.x - ndata), tid, NT, lds);
-            return;
-        }
+    constexpr bool PERS = P::template persist<T>();
+    // Groups: channel c of images g*NPW .. g*NPW + NPW-1 (those < B), group
+    // index g*C + c. One workgroup per group, or (PERSIST) the launch's
+    // first ndata workgroups, each taking every ndata-th group from its own
+    // index with the next group's loads in flight during the current one.
+    const unsigned ngroups = (unsigned)cdiv(B, NPW) * (unsigned)C;
+    const unsigned ndata = PERS ? gridDim.x - (unsigned)fin.C : ngroups;
+    if (blockIdx.x >= ndata) {   // a deferred second stage of the weight gradient
+        finalize_channel(fin, (int)(blockIdx.x - ndata), tid, NT, lds);
+        return;
     }
-    // this workgroup: channel c of images g*NPW .. g*NPW + NPW-1 (those < B)
-    const int c = blockIdx.x % C, g = blockIdx.x / C;
-    auto live = [&](int p) { return NPW == 1 || g * NPW + p < B; };
-    // The workgroup's first plane, a uniform base; plane p lies p*C*H*W
+    // A group's first plane is a uniform base; plane p lies p*C*H*W
     // elements further on. The host routes shapes whose NPW*C*H*W reaches
     // 2^32 elsewhere, so per-lane offsets stay 32-bit and the loads and
     // stores take the scalar-base, vector-offset form.
-    const size_t g0 = ((size_t)g * NPW * C + c) * H * W;
-    const T* __restrict__ in_g = in + g0;
-    T* __restrict__ out_g = out + g0;
     auto plane_rel = [&](int p) -> uint32_t { return NPW == 1 ? 0u : (uint32_t)p * ((uint32_t)C * (H * W)); };
     // plane p of an item index over all NPW planes, and the index within it
     auto split = [&](int item, int n, int& r) {
@@ -352,6 +350,93 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         r = item - p * n;
         return p;
     };
+
+    // P0's loads. The taps' loads (of channel cc) go out first and the x
+    // loads (of group gg, channel cc) right after them; the taps (level taps
+    // with the band scale and 4^-l folded in) are staged once both are in
+    // flight, so the two round trips overlap. Every lane loads (past the
+    // end: the last tap again) and stores only its own.
+    constexpr int MWB = cdiv(KB2P, NT), NWL = 4 * L * K2P, MWL = cdiv(NWL, NT);
+    float wbv[MWB], wlv[MWL], scv[MWL];
+    auto load_taps = [&](int cc) {
+#pragma unroll
+        for (int k = 0; k < MWB; ++k) {
+            const int t = min(tid + k * NT, KB * KB - 1);
+            wbv[k] = w_base[(size_t)cc * KB * KB + (FLIP ? KB * KB - 1 - t : t)];
+        }
+#pragma unroll
+        for (int k = 0; k < MWL; ++k) {
+            const int t = min(tid + k * NT, NWL - 1);
+            const int ls = t / K2P, tap = min(t - ls * K2P, K * K - 1), l = ls >> 2, s = ls & 3;
+            const size_t pi = ((size_t)l * C + cc) * 4 + s;
+            scv[k] = scale[pi];
+            wlv[k] = w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)];
+        }
+    };
+    // The whole bordered x plane and the bordered level-1 bands in one pass.
+    // An item owns x rows 2i, 2i+1 and VA columns from 2*j0 (one or two Haar
+    // blocks, band cells j0.. of row i): inside the plane it loads them,
+    // stores them widened and stores their four bands; on the border it
+    // stores zeros to both (the padding of the base convolution and of the
+    // level-1 convolutions). With ZFILL the regions are zeroed first and the
+    // items cover the interior cells only (row ii, item uu of the bordered
+    // grid, offset by the border).
+    constexpr bool ZF = P::ZFILL;
+    constexpr int CPI = P::CPI, VA = P::VA;
+    // QPOW2: items on the power-of-two grid, NQ cells per plane of IPR
+    // per row, the cells past the plane's rows or items idle
+    constexpr bool QP = P::QPOW2;
+    constexpr int NQ = QP ? P::NQP : ZF ? P::NQI : P::NQ, IPR = QP ? P::IPRP : ZF ? P::IPRI : P::IPR;
+    auto cell = [&](int q, int& ri, int& uq) {
+        ri = udiv(q, IPR);
+        uq = q - ri * IPR;
+        return !QP || (ri < H1 && uq < P::IPRI);
+    };
+    constexpr int R0 = ZF ? PK : 0, U0 = ZF ? PK / CPI : 0;
+    constexpr int NQA = NPW * NQ, MQ = cdiv(NQA, NT);
+    static_assert(!PERS || (!ZF && NPW == 1), "persistent plans: one plane per group, bordered items");
+    RawVec<T, VA> r0[MQ], r1[MQ];
+    auto load_x = [&](int gg, int cc) {
+        const T* __restrict__ in_gg = in + ((size_t)gg * NPW * C + cc) * H * W;
+#pragma unroll
+        for (int k = 0; k < MQ; ++k) {
+            const int qa = tid + k * NT;
+            int q;
+            const int p = split(qa < NQA ? qa : 0, NQ, q);
+            int ri, uq;
+            const bool real = cell(q, ri, uq);
+            const int ii = ri + R0, uu = uq + U0, i = ii - PK, j0 = uu * CPI - PK;
+            const bool inside = (NQA % NT == 0 || qa < NQA) && (NPW == 1 || gg * NPW + p < B) && real &&
+                                (ZF || (i >= 0 && i < H1 && j0 >= 0 && j0 < W1));
+            // every lane loads (border items the plane's first words) and
+            // then selects zeros: no branch, so the registers stay registers
+            const T* s0 = in_gg + (inside ? plane_rel(p) + (uint32_t)((2 * i) * W + 2 * j0) : 0u);
+            load_raw<T, VA>(s0, r0[k]);
+            load_raw<T, VA>(s0 + (inside ? W : 0), r1[k]);
+#pragma unroll
+            for (int e = 0; e < RawVec<T, VA>::N; ++e) {
+                r0[k].w[e] = inside ? r0[k].w[e] : 0u;
+                r1[k].w[e] = inside ? r1[k].w[e] : 0u;
+            }
+        }
+    };
+    if constexpr (PERS) {
+        load_taps((int)(blockIdx.x % C));
+        load_x((int)(blockIdx.x / C), (int)(blockIdx.x % C));
+    }
+
+    for (unsigned grp = blockIdx.x;;) {
+    // The thread index anew for each group: an empty asm makes it opaque, so
+    // the compiler cannot hoist the group's address arithmetic out of the
+    // loop, where it would stay live across every group and spill.
+    int tid = (int)threadIdx.x;
+    if constexpr (PERS) asm volatile("" : "+v"(tid));
+    // this group: channel c of images g*NPW .. g*NPW + NPW-1 (those < B)
+    const int c = grp % C, g = grp / C;
+    auto live = [&](int p) { return NPW == 1 || g * NPW + p < B; };
+    T* __restrict__ out_g = out + ((size_t)g * NPW * C + c) * H * W;
+    // the previous group's reads of LDS are done before this one's stores
+    if (PERS && grp != blockIdx.x) __syncthreads();
     // plane p's regions: x (A), level-1 bands (B); U_l (and then Z'_l) of
     // level l >= 2 in region A
     auto Ap = [&](int p) { return lds + p * PL; };
@@ -363,25 +448,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     };
 
     // ---------------------------------------------------------------- P0
-    // The taps' loads go out first and the x loads right after them; the
-    // taps (level taps with the band scale and 4^-l folded in) are staged
-    // once both are in flight, so the two round trips overlap. Every lane
-    // loads (past the end: the last tap again) and stores only its own.
-    constexpr int MWB = cdiv(KB2P, NT), NWL = 4 * L * K2P, MWL = cdiv(NWL, NT);
-    float wbv[MWB], wlv[MWL], scv[MWL];
-#pragma unroll
-    for (int k = 0; k < MWB; ++k) {
-        const int t = min(tid + k * NT, KB * KB - 1);
-        wbv[k] = w_base[(size_t)c * KB * KB + (FLIP ? KB * KB - 1 - t : t)];
-    }
-#pragma unroll
-    for (int k = 0; k < MWL; ++k) {
-        const int t = min(tid + k * NT, NWL - 1);
-        const int ls = t / K2P, tap = min(t - ls * K2P, K * K - 1), l = ls >> 2, s = ls & 3;
-        const size_t pi = ((size_t)l * C + c) * 4 + s;
-        scv[k] = scale[pi];
-        wlv[k] = w_lvl[pi * K * K + (FLIP ? K * K - 1 - tap : tap)];
-    }
+    if constexpr (!PERS) load_taps(c);
     auto stage_taps = [&]() {
 #pragma unroll
         for (int k = 0; k < MWB; ++k) {
@@ -399,56 +466,13 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         }
     };
     {
-        // The whole bordered x plane and the bordered level-1 bands in one
-        // pass. An item owns x rows 2i, 2i+1 and VA columns from 2*j0 (one
-        // or two Haar blocks, band cells j0.. of row i): inside the plane it
-        // loads them, stores them widened and stores their four bands; on
-        // the border it stores zeros to both (the padding of the base
-        // convolution and of the level-1 convolutions).
-        // With ZFILL the regions are zeroed first and the items cover the
-        // interior cells only (row ii, item uu of the bordered grid, offset
-        // by the border).
-        constexpr bool ZF = P::ZFILL;
-        constexpr int CPI = P::CPI, VA = P::VA;
-        // QPOW2: items on the power-of-two grid, NQ cells per plane of IPR
-        // per row, the cells past the plane's rows or items idle
-        constexpr bool QP = P::QPOW2;
-        constexpr int NQ = QP ? P::NQP : ZF ? P::NQI : P::NQ, IPR = QP ? P::IPRP : ZF ? P::IPRI : P::IPR;
-        auto cell = [&](int q, int& ri, int& uq) {
-            ri = udiv(q, IPR);
-            uq = q - ri * IPR;
-            return !QP || (ri < H1 && uq < P::IPRI);
-        };
-        constexpr int R0 = ZF ? PK : 0, U0 = ZF ? PK / CPI : 0;
-        constexpr int NQA = NPW * NQ, MQ = cdiv(NQA, NT);
         if constexpr (ZF) {
             static_assert((NPW * PL) % 4 == 0, "planes span whole 128-bit words");
             float4* const z = reinterpret_cast<float4*>(lds);
             for (int t = tid; t < NPW * PL / 4; t += NT) z[t] = make_float4(0.f, 0.f, 0.f, 0.f);
             __syncthreads();
         }
-        RawVec<T, VA> r0[MQ], r1[MQ];
-#pragma unroll
-        for (int k = 0; k < MQ; ++k) {
-            const int qa = tid + k * NT;
-            int q;
-            const int p = split(qa < NQA ? qa : 0, NQ, q);
-            int ri, uq;
-            const bool real = cell(q, ri, uq);
-            const int ii = ri + R0, uu = uq + U0, i = ii - PK, j0 = uu * CPI - PK;
-            const bool inside = (NQA % NT == 0 || qa < NQA) && live(p) && real &&
-                                (ZF || (i >= 0 && i < H1 && j0 >= 0 && j0 < W1));
-            // every lane loads (border items the plane's first words) and
-            // then selects zeros: no branch, so the registers stay registers
-            const T* s0 = in_g + (inside ? plane_rel(p) + (uint32_t)((2 * i) * W + 2 * j0) : 0u);
-            load_raw<T, VA>(s0, r0[k]);
-            load_raw<T, VA>(s0 + (inside ? W : 0), r1[k]);
-#pragma unroll
-            for (int e = 0; e < RawVec<T, VA>::N; ++e) {
-                r0[k].w[e] = inside ? r0[k].w[e] : 0u;
-                r1[k].w[e] = inside ? r1[k].w[e] : 0u;
-            }
-        }
+        if constexpr (!PERS) load_x(g, c);
         stage_taps();
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
@@ -476,6 +500,13 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             float* o = Bq + ii * S1 + uu * CPI;
 #pragma unroll
             for (int s = 0; s < 4; ++s) store_vec<CPI>(o + s * BS1, b[s]);
+        }
+        if constexpr (PERS) {   // the next group's loads fly during this one
+            const unsigned nx = grp + ndata;
+            if (nx < ngroups) {
+                load_taps((int)(nx % C));
+                load_x((int)(nx / C), (int)(nx % C));
+            }
         }
     }
     __syncthreads();
@@ -714,6 +745,12 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             }
         }
     }
+    // one group per workgroup: no loop at all (the same code as a kernel
+    // without one); persistent: the next of this workgroup's groups
+    if constexpr (!PERS) break;
+    grp += ndata;
+    if (grp >= ngroups) break;
+    }  // groups
 }
 
 // Launchers of the whole-plane kernels: one workgroup per plane
@@ -733,9 +770,15 @@ hipError_t launch_plane(const void* in, const float* wb, const float* wl, const 
 template <class P, typename T, bool FLIP>
 hipError_t launch_col(const void* in, const float* wb, const float* wl, const float* sc, void* out,
                              int B, int C, hipStream_t stream, const FinalizeArgs* fin) {
-    // one workgroup per channel and group of NPW images
+    // one workgroup per channel and group of NPW images, or (PERSIST) as
+    // many as the chip holds at once, each looping over its share
     const unsigned groups = (unsigned)cdiv(B, P::NPW) * (unsigned)C, extra = fin ? (unsigned)fin->C : 0u;
-    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(groups + extra), dim3(P::NT), 0, stream, (const T*)in, wb, wl,
+    unsigned nwg = groups;
+    if constexpr (P::template persist<T>()) {
+        const unsigned slots = (unsigned)cu_count() * (unsigned)(P::WG_PER_CU > 0 ? P::WG_PER_CU : 1);
+        nwg = groups < slots ? groups : slots;
+    }
+    hipLaunchKernelGGL((col_kernel<P, T, FLIP>), dim3(nwg + extra), dim3(P::NT), 0, stream, (const T*)in, wb, wl,
                        sc, (T*)out, B, C, fin ? *fin : FinalizeArgs{});
     return hipGetLastError();
 }

@@ -10,6 +10,9 @@
 
 namespace wtc {
 
+// Compute units of the current device (queried once per device).
+int cu_count();
+
 struct Tile {
     int r, c;
 };
@@ -211,9 +214,19 @@ constexpr BandLayout band_layout(int hl, int wl, int pk, int r, bool even) {
 // level l, either whole 2^l-row blocks per strip (RB a multiple of 2^l) or a
 // strip inside one block whose row bit l-1 is constant (RB a power of two
 // below 2^l): RB is a multiple of 2^L or a power of two.
-template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_, int WMAX_ = 8, int NPW_ = 1>
+template <int H_, int W_, int L_, int KB_, int K_, int NT_, int RB_, int RL_, int WMAX_ = 8, int NPW_ = 1,
+          bool PERSIST_ = false>
 struct ColPlan {
     static constexpr int H = H_, W = W_, L = L_, KB = KB_, K = K_, NT = NT_, RB = RB_, RL = RL_;
+    // persistent workgroups: as many as fit the chip at once, each taking
+    // every such-many-th plane with the next plane's x rows and taps loaded
+    // during the current one (planes whose LDS admits one workgroup per CU
+    // otherwise expose each plane's load latency). For bf16 activations
+    // only: fp32 ones take twice the prefetch registers (128x128 L3: a
+    // spill).
+    static constexpr bool PERSIST = PERSIST_;
+    template <typename T>
+    static constexpr bool persist() { return PERSIST && sizeof(T) == 2; }
     // planes per workgroup: NPW planes of one channel (consecutive images)
     // share the staged taps, and every phase packs its strips of all of
     // them onto the lanes (small planes otherwise leave lanes idle)
@@ -395,9 +408,12 @@ namespace wtc {
 typedef ColPlan<56, 56, 3, 5, 5, 512, 8, 7, 8> CP_56_L3_k55;
 typedef ColPlan<28, 28, 2, 5, 5, 256, 4, 14, 8, 2> CP_28_L2_k55;
 typedef ColPlan<14, 14, 1, 5, 5, 256, 14, 7, 8, 8> CP_14_L1_k55;
-typedef ColPlan<128, 128, 1, 5, 5, 1024, 16, 16> CP_128_L1_k55;
+// Persistent at L = 1 and 3 (128x128 level sweep, bf16: forward 140 -> 127
+// and 169 -> 157 us per call on one box); at L = 2, 4 and 5 the prefetch
+// registers spill (20-28 bytes) and it measured no faster.
+typedef ColPlan<128, 128, 1, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L1_k55;
 typedef ColPlan<128, 128, 2, 5, 5, 1024, 16, 16> CP_128_L2_k55;
-typedef ColPlan<128, 128, 3, 5, 5, 1024, 16, 16> CP_128_L3_k55;
+typedef ColPlan<128, 128, 3, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L3_k55;
 typedef ColPlan<128, 128, 4, 5, 5, 1024, 16, 16> CP_128_L4_k55;
 typedef ColPlan<128, 128, 5, 5, 5, 1024, 16, 16> CP_128_L5_k55;
 #define WTC_COL_ENTRIES(X)                                                                     \
