@@ -395,9 +395,31 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
     constexpr int R0 = ZF ? PK : 0, U0 = ZF ? PK / CPI : 0;
     constexpr int NQA = NPW * NQ, MQ = cdiv(NQA, NT);
     static_assert(!PERS || (!ZF && NPW == 1), "persistent plans: one plane per group, bordered items");
-    RawVec<T, VA> r0[MQ], r1[MQ];
+    // Persistent plans load (and prefetch) the interior items only, on a
+    // power-of-two grid of H/2 rows of IPN items, in MQN whole rounds; their
+    // border items store zeros each plane (no registers held for them).
+    constexpr int IPN = (W >> 1) / CPI, NQN = (H >> 1) * IPN, MQN = cdiv(NQN, NT);
+    static_assert(!PERS || (NQN % NT == 0 && (IPN & (IPN - 1)) == 0), "whole rounds of interior items");
+    constexpr int MQL = PERS ? MQN : MQ;   // rounds of loaded items
+    RawVec<T, VA> r0[MQL], r1[MQL];
     auto load_x = [&](int gg, int cc) {
         const T* __restrict__ in_gg = in + ((size_t)gg * NPW * C + cc) * H * W;
+        if constexpr (PERS) {
+            const bool live_gg = NPW == 1 || gg * NPW < B;
+#pragma unroll
+            for (int k = 0; k < MQN; ++k) {
+                const int q = tid + k * NT, i = q / IPN, j0 = (q - (q / IPN) * IPN) * CPI;
+                const T* s0 = in_gg + (live_gg ? (uint32_t)((2 * i) * W + 2 * j0) : 0u);
+                load_raw<T, VA>(s0, r0[k]);
+                load_raw<T, VA>(s0 + W, r1[k]);
+#pragma unroll
+                for (int e = 0; e < RawVec<T, VA>::N; ++e) {
+                    r0[k].w[e] = live_gg ? r0[k].w[e] : 0u;
+                    r1[k].w[e] = live_gg ? r1[k].w[e] : 0u;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int qa = tid + k * NT;
@@ -474,6 +496,52 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
         }
         if constexpr (!PERS) load_x(g, c);
         stage_taps();
+        // one item's stores: its two x rows, widened, and its four band cells
+        auto store_item = [&](float* A, int ii, int uu, const float (&f0)[VA], const float (&f1)[VA]) {
+            float* const Bq = A + P::ASIZE;
+            const int i = ii - PK, j0 = uu * CPI - PK;
+            const int xr = PB + 2 * i, xc = XO + 2 * j0;
+            if (xc >= 0 && xc + VA <= SX) {
+                if (xr >= 0 && xr < H + 2 * PB) store_vec<VA>(A + xr * SX + xc, f0);
+                if (xr + 1 >= 0 && xr + 1 < H + 2 * PB) store_vec<VA>(A + (xr + 1) * SX + xc, f1);
+            }
+            float b[4][CPI];
+#pragma unroll
+            for (int m = 0; m < CPI; ++m)
+                haar4(f0[2 * m], f0[2 * m + 1], f1[2 * m], f1[2 * m + 1], b[0][m], b[1][m], b[2][m], b[3][m]);
+            float* o = Bq + ii * S1 + uu * CPI;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) store_vec<CPI>(o + s * BS1, b[s]);
+        };
+        if constexpr (PERS) {
+            // the interior items from the prefetched registers ...
+#pragma unroll
+            for (int k = 0; k < MQN; ++k) {
+                const int q = tid + k * NT, ri = q / IPN, uq = q - ri * IPN;
+                float f0[VA], f1[VA];
+                widen_raw<T, VA>(r0[k], f0);
+                widen_raw<T, VA>(r1[k], f1);
+                store_item(Ap(0), ri + PK, uq + PK / CPI, f0, f1);
+            }
+            // ... and zeros for the border items: the PK top and bottom rows of
+            // the bordered grid, then its PK / CPI items at each side of the
+            // interior rows
+            constexpr int UB = PK / CPI, NTB = 2 * PK * P::IPR, NBD = NTB + (H >> 1) * 2 * UB;
+            for (int t = tid; t < NBD; t += NT) {
+                int ii, uu;
+                if (t < NTB) {
+                    const int r = t / P::IPR;
+                    ii = r < PK ? r : r + (H >> 1);
+                    uu = t - r * P::IPR;
+                } else {
+                    const int t2 = t - NTB, r = t2 / (2 * UB), sd = t2 - r * (2 * UB);
+                    ii = PK + r;
+                    uu = sd < UB ? sd : sd + IPN;
+                }
+                float z[VA] = {};
+                store_item(Ap(0), ii, uu, z, z);
+            }
+        } else {
 #pragma unroll
         for (int k = 0; k < MQ; ++k) {
             const int qa = tid + k * NT;
@@ -500,6 +568,7 @@ void col_kernel(const T* __restrict__ in, const float* __restrict__ w_base, cons
             float* o = Bq + ii * S1 + uu * CPI;
 #pragma unroll
             for (int s = 0; s < 4; ++s) store_vec<CPI>(o + s * BS1, b[s]);
+        }
         }
         if constexpr (PERS) {   // the next group's loads fly during this one
             const unsigned nx = grp + ndata;

@@ -408,14 +408,16 @@ namespace wtc {
 typedef ColPlan<56, 56, 3, 5, 5, 512, 8, 7, 8> CP_56_L3_k55;
 typedef ColPlan<28, 28, 2, 5, 5, 256, 4, 14, 8, 2> CP_28_L2_k55;
 typedef ColPlan<14, 14, 1, 5, 5, 256, 14, 7, 8, 8> CP_14_L1_k55;
-// Persistent at L = 1 and 3 (128x128 level sweep, bf16: forward 140 -> 127
-// and 169 -> 157 us per call on one box); at L = 2, 4 and 5 the prefetch
-// registers spill (20-28 bytes) and it measured no faster.
+// Persistent (bf16 activations), against one workgroup per plane on one
+// box: level-sweep step 0.488 -> 0.455, 0.536 -> 0.506 and 0.548 -> 0.539
+// ms at L = 2, 4, 5 (L = 5 keeps a 12-byte spill and still gains); at L = 1
+// and 3 0.398 -> 0.377 and 0.525 -> 0.505 ms with every stream-in item
+// prefetched, a further 1 % with the interior items only.
 typedef ColPlan<128, 128, 1, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L1_k55;
-typedef ColPlan<128, 128, 2, 5, 5, 1024, 16, 16> CP_128_L2_k55;
+typedef ColPlan<128, 128, 2, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L2_k55;
 typedef ColPlan<128, 128, 3, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L3_k55;
-typedef ColPlan<128, 128, 4, 5, 5, 1024, 16, 16> CP_128_L4_k55;
-typedef ColPlan<128, 128, 5, 5, 5, 1024, 16, 16> CP_128_L5_k55;
+typedef ColPlan<128, 128, 4, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L4_k55;
+typedef ColPlan<128, 128, 5, 5, 5, 1024, 16, 16, 8, 1, true> CP_128_L5_k55;
 #define WTC_COL_ENTRIES(X)                                                                     \
     X(CP_56_L3_k55), X(CP_28_L2_k55), X(CP_14_L1_k55), X(CP_128_L1_k55), X(CP_128_L2_k55),     \
         X(CP_128_L3_k55), X(CP_128_L4_k55), X(CP_128_L5_k55)
