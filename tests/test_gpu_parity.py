@@ -504,6 +504,27 @@ def test_graph_replay_whole_backward(shape):
         (x.float() * 2).sum().item()   # eager work between replays
 
 
+@pytest.mark.parametrize("L", [2, 4])
+def test_persistent_column_kernel_uneven_share(L):
+    """The 128x128 column kernel with persistent workgroups (one per CU,
+    every 256th plane each, the next plane's loads in flight): 300 planes,
+    so some workgroups take two planes and the rest one; y, dx and the
+    whole backward against the oracle, bf16 activations."""
+    B, C, H, W, kb, k = 3, 100, 128, 128, 5, 5
+    _say(f"[parity] persistent column kernel {B}x{C}x{H}x{W} L{L}")
+    inp = make_inputs(B, C, H, W, L, kb, k, dtype="bf16", seed=31 + L)
+    x, dy, wb, wl, sc = to_device(inp)
+    y = wt.wtconv_fwd(x, wb, wl, sc)
+    dx = wt.wtconv_bwd_data(dy, wb, wl, sc)
+    dx1, (gb, gl, gs) = wt.wtconv_bwd(x, dy, wb, wl, sc)
+    torch.cuda.synchronize()
+    oy, odx, (ob, ol, os_) = _oracle_all(inp)
+    assert rel_err(to_f64(y), oy) <= TOL["bf16"]
+    assert rel_err(to_f64(dx), odx) <= TOL["bf16"] and torch.equal(dx, dx1)
+    for g, o in ((gb, ob), (gl, ol), (gs, os_)):
+        assert rel_err(to_f64(g), o) <= TOL["f32"]
+
+
 def test_measurement_probes():
     """The copy probe copies exactly; the FMA probe writes finite values to
     every lane's slot; bad arguments are refused before any launch."""
